@@ -1,0 +1,190 @@
+"""Seeded synthetic inputs for the rotated low-bit linear layer.
+
+This module only draws inputs: activations shaped like diffusion-transformer
+tokens, weights, the random signs and permutation of the RPBH rotation, the
+dense PCA basis of the DiRotQ path and its calibration sample.  It holds none
+of the layer's arithmetic (no rotation, quantization or GEMM), so the product
+path and the CPU oracle can both take their inputs from it.
+
+Workloads (token counts include the two classifier-free-guidance branches
+stacked into one batch):
+
+  tiny   256 x 1152 -> 1152, fp32 input, RPBH block 128, INT4
+  pixart 8192 x 1152 -> 4608, bf16, dense PCA basis, top 32 kept bf16, INT4
+  flux_up   9216 x 3072 -> 12288, bf16, RPBH block 256, INT4
+  flux_down 9216 x 12288 -> 3072, bf16 (GELU-shaped), RPBH block 512, INT4
+  video  32760 x 1536 -> 8960, bf16, RPBH block 256, Lloyd-Max A4 / W2
+
+Random streams: numpy PCG64 seeded from SeedSequence(1000 + i) for workload
+i, with spawned child streams for X, W, sign, perm and the calibration
+sample, so every tensor is reproducible on its own.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+import math
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    index: int
+    T: int
+    K: int
+    N: int
+    rot: str            # "rpbh" | "dense"
+    block: int          # RPBH block (0 for dense)
+    r: int              # top-r kept in bf16 (dense only)
+    quant: str          # "int4" | "lloydmax"
+    xdtype: str         # "f32" | "bf16"
+    ydtype: str         # "f32" | "bf16"
+    x_kind: str         # distribution recipe of X
+    a_bits: int = 4
+    w_bits: int = 4
+
+    @property
+    def Kq(self) -> int:
+        return self.K - self.r
+
+    @property
+    def b_eff(self) -> int:
+        return self.block if self.rot == "rpbh" else 1
+
+    def ops(self) -> int:
+        """Algorithmic GEMM operations 2*T*Kq*N (multiply-add counted as 2)."""
+        return 2 * self.T * self.Kq * self.N
+
+    def with_shape(self, T=None, K=None, N=None, block=None) -> "Workload":
+        return replace(self, T=self.T if T is None else T, K=self.K if K is None else K,
+                       N=self.N if N is None else N,
+                       block=self.block if block is None else block)
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 0, 256, 1152, 1152, "rpbh", 128, 0, "int4", "f32", "f32",
+                     "gauss_outlier8x50"),
+    "pixart": Workload("pixart", 1, 8192, 1152, 4608, "dense", 0, 32, "int4", "bf16", "bf16",
+                       "gauss_t4rows_outlier16x30"),
+    "flux_up": Workload("flux_up", 2, 9216, 3072, 12288, "rpbh", 256, 0, "int4", "bf16", "bf16",
+                        "gauss_outlier16x30"),
+    "flux_down": Workload("flux_down", 3, 9216, 12288, 3072, "rpbh", 512, 0, "int4", "bf16",
+                          "bf16", "gelu"),
+    "video": Workload("video", 4, 32760, 1536, 8960, "rpbh", 256, 0, "lloydmax", "bf16", "bf16",
+                      "gauss", a_bits=4, w_bits=2),
+}
+
+
+def _streams(w: Workload, seed_offset: int = 0):
+    ss = np.random.SeedSequence(1000 + w.index + seed_offset)
+    kids = ss.spawn(6)
+    names = ("x", "w", "sign", "perm", "calib", "extra")
+    return {n: np.random.Generator(np.random.PCG64(k)) for n, k in zip(names, kids)}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (nearest, ties to even) and return the bit patterns
+    as uint16.  Only used to produce bf16 inputs."""
+    x = np.ascontiguousarray(x, np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lower = u & 0xFFFF
+    upper = u >> 16
+    up = (lower > 0x8000) | ((lower == 0x8000) & ((upper & 1) == 1))
+    return (upper + up.astype(np.uint64)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(h, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _gelu_erf(z: np.ndarray) -> np.ndarray:
+    from scipy.special import erf
+    return 0.5 * z * (1.0 + erf(z / math.sqrt(2.0)))
+
+
+def _draw_x(w: Workload, g: np.random.Generator, T: int, K: int, outlier_cols=None):
+    """fp32 activations [T][K] for the workload's recipe."""
+    kind = w.x_kind
+    if kind == "gelu":
+        z = g.standard_normal((T, K), dtype=np.float32)
+        return _gelu_erf(z.astype(np.float64)).astype(np.float32)
+    x = g.standard_normal((T, K), dtype=np.float32)
+    if kind.startswith("gauss_t4rows"):
+        # a random eighth of the rows are heavy-tailed Student-t (df = 4)
+        nt = T // 8
+        rows = g.choice(T, size=nt, replace=False) if nt > 0 else np.zeros(0, np.int64)
+        x[rows] = g.standard_t(4.0, size=(nt, K)).astype(np.float32)
+    if "outlier" in kind:
+        spec = kind.split("outlier")[1]           # e.g. "16x30"
+        cnt, mag = (int(v) for v in spec.split("x"))
+        cnt = min(cnt, K)
+        cols = outlier_cols if outlier_cols is not None else g.choice(K, size=cnt, replace=False)
+        x[:, cols] *= np.float32(mag)
+    return x
+
+
+def make_inputs(w: Workload, seed_offset: int = 0) -> dict:
+    """All inputs of one workload instance.
+
+    Returns dict with:
+      X     np.float32 [T][K] (fp32 workloads) or np.uint16 bf16 bits [T][K]
+      Xf    np.float32 [T][K]: X widened to fp32 (for reporting only)
+      W     np.float32 [N][K] ~ N(0, 0.02^2)
+      sign  np.int8 [K] in {-1, +1}          (RPBH)
+      perm  np.int32 [K], a uniform permutation (RPBH)
+      R     np.float32 [K][K] dense PCA basis (dense), columns by descending
+            variance of a separate 4096-row calibration sample
+    """
+    s = _streams(w, seed_offset)
+    T, K, N = w.T, w.K, w.N
+    # outlier channels are a property of the layer: the calibration sample of
+    # the dense path shares them with the runtime tokens
+    cols = None
+    if "outlier" in w.x_kind:
+        spec = w.x_kind.split("outlier")[1]
+        cnt = min(int(spec.split("x")[0]), K)
+        cols = s["extra"].choice(K, size=cnt, replace=False)
+    xf = _draw_x(w, s["x"], T, K, cols)
+    out = {"workload": w}
+    if w.xdtype == "bf16":
+        out["X"] = f32_to_bf16_bits(xf)
+        out["Xf"] = bf16_bits_to_f32(out["X"])
+    else:
+        out["X"] = xf
+        out["Xf"] = xf
+    out["W"] = (s["w"].standard_normal((N, K), dtype=np.float32) * np.float32(0.02)).astype(np.float32)
+    if w.rot == "rpbh":
+        out["sign"] = np.where(s["sign"].integers(0, 2, size=K) == 1, 1, -1).astype(np.int8)
+        out["perm"] = s["perm"].permutation(K).astype(np.int32)
+        out["R"] = None
+    else:
+        out["sign"] = None
+        out["perm"] = None
+        out["R"] = pca_basis(_draw_x(w, s["calib"], 4096, K, cols))
+    return out
+
+
+def pca_basis(calib: np.ndarray) -> np.ndarray:
+    """Dense orthogonal basis from a calibration sample (stand-in for the
+    calibration step that produces the rotation): eigenvectors of the centered
+    covariance, fp64, ordered by descending eigenvalue (ties by index), each
+    column's largest-magnitude entry made positive, stored as fp32 [K][K]
+    with column j = component j."""
+    c = calib.astype(np.float64)
+    c = c - c.mean(axis=0, keepdims=True)
+    cov = c.T @ c / max(1, c.shape[0] - 1)
+    evals, evecs = np.linalg.eigh(cov)
+    order = np.lexsort((np.arange(evals.size), -evals))
+    V = evecs[:, order]
+    idx = np.argmax(np.abs(V), axis=0)
+    sgn = np.sign(V[idx, np.arange(V.shape[1])])
+    sgn[sgn == 0] = 1.0
+    return np.ascontiguousarray((V * sgn).astype(np.float32))
+
+
+def random_rpbh(K: int, seed: int):
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    sign = np.where(g.integers(0, 2, size=K) == 1, 1, -1).astype(np.int8)
+    perm = g.permutation(K).astype(np.int32)
+    return sign, perm

@@ -1,0 +1,98 @@
+"""Layer-level properties of the oracle's dequantized output.
+
+Y-hat is the fp64 value of the codes and scales ("TR-DQ" section 3.1:
+per-token x per-channel scales; Eq.(9): the rotation cancels between the
+activations and the folded weights).  It must approximate the unquantized
+X . W^T to within 4-bit quantization noise; a dropped factor (the 1/b of the
+unnormalized Hadamard, a scale) or a transposed operand would fail these.
+The claim that rotation tames outlier channels ("TR-DQ" section 3.2, Fig. 2;
+"OrbitQuant" abstract) is checked as a property on synthetic outliers.
+"""
+import numpy as np
+import pytest
+
+from oracle import oracle as orc
+from rotated_w4a4_quantized_amd import datagen
+
+
+def snr_db(y, ref):
+    return 10 * np.log10(np.sum(ref ** 2) / np.sum((y - ref) ** 2))
+
+
+def _int4_layer(inp, w, rot_sign=None, rot_perm=None, b=None):
+    X, Xf, W = inp["X"], inp["Xf"], inp["W"]
+    T, K = Xf.shape
+    xd = 0 if w.xdtype == "f32" else 1
+    if w.rot == "rpbh":
+        sign = inp["sign"] if rot_sign is None else rot_sign
+        perm = inp["perm"] if rot_perm is None else rot_perm
+        bb = w.block if b is None else b
+        a = orc.act_rows(X, xd, K, np.arange(T), rot_kind=0, b=bb, sign=sign, perm=perm)
+        wt = orc.weight_rows(W, rot_kind=0, b=bb, sign=sign, perm=perm)
+        acc = orc.int_gemm(a["codes"], K, wt["codes"], K)
+        return orc.yhat_int4(a["scale"][:, None], wt["scale"][None, :], acc, bb)
+    a = orc.act_rows(X, xd, K, np.arange(T), rot_kind=1, R=inp["R"], r=w.r)
+    wt = orc.weight_rows(W, rot_kind=1, R=inp["R"])
+    acc = orc.int_gemm(a["codes"], w.Kq, wt["codes"], K, koff=w.r)
+    ta, nw = np.meshgrid(np.arange(T), np.arange(W.shape[0]), indexing="ij")
+    lr = orc.lowrank_pairs(a["top"], w.r, wt["codes"], K, ta.ravel(), nw.ravel()).reshape(acc.shape)
+    return orc.yhat_int4(a["scale"][:, None], wt["scale"][None, :], acc, 1, lr=lr)
+
+
+def test_int4_rpbh_layer_snr_and_outliers():
+    w = datagen.WORKLOADS["tiny"].with_shape(T=64, N=96)
+    inp = datagen.make_inputs(w)
+    ref = inp["Xf"].astype(np.float64) @ inp["W"].astype(np.float64).T
+    y = _int4_layer(inp, w)
+    s_rot = snr_db(y, ref)
+    K = w.K
+    y0 = _int4_layer(inp, w, rot_sign=np.ones(K, np.int8),
+                     rot_perm=np.arange(K, dtype=np.int32), b=1)
+    s_id = snr_db(y0, ref)
+    print(f"tiny INT4 SNR: RPBH {s_rot:.1f} dB, no rotation {s_id:.1f} dB")
+    assert s_rot > 12.0
+    assert s_rot > s_id + 2.0
+
+
+def test_int4_dense_layer_snr():
+    w = datagen.WORKLOADS["pixart"].with_shape(T=64, N=80)
+    inp = datagen.make_inputs(w)
+    ref = inp["Xf"].astype(np.float64) @ inp["W"].astype(np.float64).T
+    y = _int4_layer(inp, w)
+    s = snr_db(y, ref)
+    print(f"pixart INT4 + top-32 bf16 SNR: {s:.1f} dB")
+    assert s > 12.0
+
+
+def test_codebook_layer_snr():
+    w = datagen.WORKLOADS["video"].with_shape(T=64, N=72)
+    inp = datagen.make_inputs(w)
+    K = w.K
+    a_lv, w_lv = orc.codebook_bf16(16), orc.codebook_bf16(4)
+    a = orc.act_rows(inp["X"], 1, K, np.arange(w.T), rot_kind=0, b=w.block, sign=inp["sign"],
+                     perm=inp["perm"], q_kind=1, levels=a_lv)
+    wt = orc.weight_rows(inp["W"], rot_kind=0, b=w.block, sign=inp["sign"], perm=inp["perm"],
+                         q_kind=1, levels=w_lv)
+    ta, nw = np.meshgrid(np.arange(w.T), np.arange(w.N), indexing="ij")
+    dot = orc.codebook_dot_pairs(a["codes"], wt["codes"], K, a_lv, w_lv, ta.ravel(), nw.ravel())
+    y = orc.yhat_codebook(a["scale"][ta.ravel()], wt["scale"][nw.ravel()], dot, w.block)
+    ref = (inp["Xf"].astype(np.float64) @ inp["W"].astype(np.float64).T).ravel()
+    s = snr_db(y, ref)
+    print(f"video W2A4 Lloyd-Max SNR: {s:.1f} dB")
+    # 2-bit weights: about 9 dB of weight noise dominates
+    assert s > 6.0
+
+
+def test_rotated_coordinates_follow_one_marginal():
+    # OrbitQuant: after RPBH the normalized coordinates concentrate around one
+    # fixed marginal whatever the input (here N(0,1)); reported as a KS distance
+    from scipy.stats import kstest
+    w = datagen.WORKLOADS["video"].with_shape(T=32)
+    inp = datagen.make_inputs(w)
+    a = orc.act_rows(inp["X"], 1, w.K, np.arange(32), rot_kind=0, b=w.block, sign=inp["sign"],
+                     perm=inp["perm"], want_u=True, q_kind=1, levels=orc.codebook_bf16(16))
+    u = a["u"].astype(np.float64)
+    v = (u * np.sqrt(w.K) / np.linalg.norm(u, axis=1, keepdims=True)).ravel()
+    ks = kstest(v, "norm").statistic
+    print(f"KS distance of normalized RPBH coordinates to N(0,1): {ks:.4f}")
+    assert ks < 0.02
