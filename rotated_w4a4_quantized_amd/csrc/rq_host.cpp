@@ -1,0 +1,331 @@
+// rq_host.cpp -- host half of librq: error state, descriptor validation,
+// the offline weight pack (fold + quantize + blob) and the Lloyd-Max
+// codebook.  No GPU calls in this file.
+//
+// Compiled with -ffp-contract=off: every a*b+c below is two roundings unless
+// std::fma is written out, so the fold and the quantizers are reproducible.
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "rq_internal.h"
+
+namespace rq {
+
+static thread_local std::string g_err;
+
+rq_status fail(rq_status st, const std::string &msg) {
+    g_err = msg;
+    return st;
+}
+void clear_error() { g_err.clear(); }
+
+rq_status check_rotation(const rq_rotation *rot, bool need_tables) {
+    if (!rot) return fail(RQ_ERR_NULL, "rotation descriptor is NULL");
+    const int K = rot->K;
+    if (K < 32 || K > 16384 || K % 32 != 0)
+        return fail(RQ_ERR_SHAPE, "K must satisfy 32 <= K <= 16384 and K % 32 == 0, got " +
+                                      std::to_string(K));
+    if (rot->kind == RQ_ROT_RPBH) {
+        const int b = rot->block;
+        if (!is_pow2(b) || b < 2 || b > 1024)
+            return fail(RQ_ERR_SHAPE, "RPBH block must be a power of two in [2, 1024], got " +
+                                          std::to_string(b));
+        if (K % b != 0)
+            return fail(RQ_ERR_SHAPE, "RPBH block " + std::to_string(b) + " does not divide K " +
+                                          std::to_string(K));
+        if (rot->r != 0) return fail(RQ_ERR_SHAPE, "RPBH takes r == 0");
+        if (need_tables && (!rot->sign || !rot->perm))
+            return fail(RQ_ERR_NULL, "RPBH needs sign and perm tables");
+    } else if (rot->kind == RQ_ROT_DENSE) {
+        if (rot->r < 0 || rot->r >= K || rot->r % 32 != 0)
+            return fail(RQ_ERR_SHAPE, "DENSE r must satisfy 0 <= r < K and r % 32 == 0, got " +
+                                          std::to_string(rot->r));
+        if (need_tables && !rot->R) return fail(RQ_ERR_NULL, "DENSE needs the basis R");
+    } else {
+        return fail(RQ_ERR_UNSUPPORTED, "unknown rotation kind " + std::to_string(rot->kind));
+    }
+    return RQ_OK;
+}
+
+rq_status check_quant(const rq_rotation *rot, const rq_quant *q) {
+    if (!q) return fail(RQ_ERR_NULL, "quantizer descriptor is NULL");
+    if (q->a_bits != 4) return fail(RQ_ERR_UNSUPPORTED, "a_bits must be 4");
+    if (q->kind == RQ_Q_INT4_SYM) {
+        if (q->w_bits != 4) return fail(RQ_ERR_UNSUPPORTED, "INT4_SYM needs w_bits == 4");
+    } else if (q->kind == RQ_Q_LLOYDMAX) {
+        if (q->w_bits != 2 && q->w_bits != 4)
+            return fail(RQ_ERR_UNSUPPORTED, "LLOYDMAX needs w_bits 2 or 4");
+        if (rot->kind != RQ_ROT_RPBH)
+            return fail(RQ_ERR_UNSUPPORTED, "LLOYDMAX is built for the RPBH rotation only");
+        const int La = 1 << q->a_bits, Lw = 1 << q->w_bits;
+        for (int i = 0; i + 1 < La; ++i)
+            if (!(q->a_levels[i] < q->a_levels[i + 1]))
+                return fail(RQ_ERR_SHAPE, "a_levels must be strictly ascending");
+        for (int i = 0; i + 1 < Lw; ++i)
+            if (!(q->w_levels[i] < q->w_levels[i + 1]))
+                return fail(RQ_ERR_SHAPE, "w_levels must be strictly ascending");
+        for (int i = 0; i < La; ++i) {
+            uint32_t bits;
+            std::memcpy(&bits, &q->a_levels[i], 4);
+            if ((bits & 0xFFFFu) != 0 || !std::isfinite(q->a_levels[i]))
+                return fail(RQ_ERR_SHAPE, "a_levels must be finite bf16 values");
+        }
+        for (int i = 0; i < Lw; ++i) {
+            uint32_t bits;
+            std::memcpy(&bits, &q->w_levels[i], 4);
+            if ((bits & 0xFFFFu) != 0 || !std::isfinite(q->w_levels[i]))
+                return fail(RQ_ERR_SHAPE, "w_levels must be finite bf16 values");
+        }
+    } else {
+        return fail(RQ_ERR_UNSUPPORTED, "unknown quantizer kind " + std::to_string(q->kind));
+    }
+    return RQ_OK;
+}
+
+// ---------------------------------------------------------------------------
+// weight fold (fp64) -- the transposed rotation of TR-DQ Eq.(9) applied to
+// each output row of W stored [N][K]: v = w R.
+// ---------------------------------------------------------------------------
+
+// Sign/permutation gather, then the Sylvester butterflies of every block in
+// ascending stage order, all in fp64.
+static void fold_rpbh(const double *w, int K, int b, const int8_t *sign, const int32_t *perm,
+                      double *v) {
+    for (int j = 0; j < K; ++j) v[j] = sign[j] < 0 ? -w[perm[j]] : w[perm[j]];
+    for (int base = 0; base < K; base += b)
+        for (int h = 1; h < b; h <<= 1)
+            for (int s = 0; s < b; s += 2 * h)
+                for (int i = base + s; i < base + s + h; ++i) {
+                    const double lo = v[i], hi = v[i + h];
+                    v[i] = lo + hi;
+                    v[i + h] = lo - hi;
+                }
+}
+
+// Dense: v[j] = fp64 fma chain over k ascending of w[k] * R[k][j], from +0.
+static void fold_dense(const double *w, int K, const float *R, double *v) {
+    std::fill(v, v + K, 0.0);
+    for (int k = 0; k < K; ++k) {
+        const float *Rk = R + (size_t)k * K;
+        const double wk = w[k];
+        for (int j = 0; j < K; ++j) v[j] = std::fma(wk, (double)Rk[j], v[j]);
+    }
+}
+
+static inline double bf16_bits_to_double(uint16_t h) {
+    uint32_t bits = (uint32_t)h << 16;
+    float f;
+    std::memcpy(&f, &bits, 4);
+    return (double)f;
+}
+
+static int64_t blob_layout(const rq_rotation *rot, const rq_quant *q, int32_t N,
+                           int32_t *row_bytes, int64_t *scale_off, int64_t *codes_off) {
+    const int K = rot->K;
+    const int rb = (q->kind == RQ_Q_INT4_SYM || q->w_bits == 4) ? K / 2 : K / 4;
+    const int64_t so = (int64_t)sizeof(rq_weight_header);
+    const int64_t co = so + (((int64_t)N * 4 + 255) / 256) * 256;
+    *row_bytes = rb;
+    *scale_off = so;
+    *codes_off = co;
+    return co + (((int64_t)N * rb + 255) / 256) * 256;
+}
+
+}  // namespace rq
+
+using namespace rq;
+
+extern "C" {
+
+int32_t rq_version(void) { return 100; }
+
+const char *rq_last_error(void) { return g_err.c_str(); }
+
+rq_status rq_packed_weight_bytes(const rq_rotation *rot, const rq_quant *q, int32_t N,
+                                 size_t *bytes) {
+    clear_error();
+    rq_status st = check_rotation(rot, false);
+    if (st != RQ_OK) return st;
+    if ((st = check_quant(rot, q)) != RQ_OK) return st;
+    if (!bytes) return fail(RQ_ERR_NULL, "bytes is NULL");
+    if (N < 1 || N > (1 << 20)) return fail(RQ_ERR_SHAPE, "N must be in [1, 2^20]");
+    int32_t rb;
+    int64_t so, co;
+    *bytes = (size_t)blob_layout(rot, q, N, &rb, &so, &co);
+    return RQ_OK;
+}
+
+rq_status rq_pack_weights(const rq_rotation *rot, const rq_quant *q, const void *W,
+                          int32_t w_dtype, int32_t N, void *blob, size_t blob_bytes) {
+    clear_error();
+    rq_status st = check_rotation(rot, true);
+    if (st != RQ_OK) return st;
+    if ((st = check_quant(rot, q)) != RQ_OK) return st;
+    if (!W || !blob) return fail(RQ_ERR_NULL, "W and blob must not be NULL");
+    if (w_dtype != RQ_F32 && w_dtype != RQ_BF16)
+        return fail(RQ_ERR_DTYPE, "W must be RQ_F32 or RQ_BF16");
+    if (N < 1 || N > (1 << 20)) return fail(RQ_ERR_SHAPE, "N must be in [1, 2^20]");
+    const int K = rot->K;
+    if (rot->kind == RQ_ROT_RPBH) {
+        std::vector<char> seen(K, 0);
+        for (int j = 0; j < K; ++j) {
+            const int p = rot->perm[j];
+            if (p < 0 || p >= K || seen[p]) return fail(RQ_ERR_SHAPE, "perm is not a permutation");
+            seen[p] = 1;
+            if (rot->sign[j] != 1 && rot->sign[j] != -1)
+                return fail(RQ_ERR_SHAPE, "sign entries must be -1 or +1");
+        }
+    }
+    int32_t rb;
+    int64_t so, co;
+    const int64_t total = blob_layout(rot, q, N, &rb, &so, &co);
+    if ((int64_t)blob_bytes < total)
+        return fail(RQ_ERR_SHAPE, "blob_bytes " + std::to_string(blob_bytes) + " < required " +
+                                      std::to_string(total));
+
+    uint8_t *out = static_cast<uint8_t *>(blob);
+    std::memset(out, 0, (size_t)total);
+    rq_weight_header hdr;
+    std::memset(&hdr, 0, sizeof hdr);
+    hdr.magic = RQ_WEIGHT_MAGIC;
+    hdr.version = RQ_WEIGHT_VERSION;
+    hdr.format = q->kind;
+    hdr.K = K;
+    hdr.N = N;
+    hdr.r = rot->kind == RQ_ROT_DENSE ? rot->r : 0;
+    hdr.b_div = rot->kind == RQ_ROT_RPBH ? rot->block : 1;
+    hdr.a_bits = q->a_bits;
+    hdr.w_bits = q->w_bits;
+    hdr.row_bytes = rb;
+    hdr.scale_offset = so;
+    hdr.codes_offset = co;
+    hdr.total_bytes = total;
+    if (q->kind == RQ_Q_LLOYDMAX) {
+        std::memcpy(hdr.a_levels, q->a_levels, sizeof hdr.a_levels);
+        std::memcpy(hdr.w_levels, q->w_levels, sizeof hdr.w_levels);
+    }
+    std::memcpy(out, &hdr, sizeof hdr);
+    float *scales = reinterpret_cast<float *>(out + so);
+    uint8_t *codes = out + co;
+
+    // midpoints of adjacent weight levels (exact for bf16 levels)
+    const int Lw = 1 << q->w_bits;
+    double wth[15];
+    for (int i = 0; i + 1 < Lw; ++i)
+        wth[i] = ((double)q->w_levels[i] + (double)q->w_levels[i + 1]) / 2.0;
+
+    auto work = [&](int n0, int n1) {
+        std::vector<double> w(K), v(K);
+        for (int n = n0; n < n1; ++n) {
+            if (w_dtype == RQ_F32) {
+                const float *src = static_cast<const float *>(W) + (size_t)n * K;
+                for (int k = 0; k < K; ++k) w[k] = (double)src[k];
+            } else {
+                const uint16_t *src = static_cast<const uint16_t *>(W) + (size_t)n * K;
+                for (int k = 0; k < K; ++k) w[k] = bf16_bits_to_double(src[k]);
+            }
+            if (rot->kind == RQ_ROT_RPBH)
+                fold_rpbh(w.data(), K, rot->block, rot->sign, rot->perm, v.data());
+            else
+                fold_dense(w.data(), K, rot->R, v.data());
+            uint8_t *row = codes + (size_t)n * rb;
+            if (q->kind == RQ_Q_INT4_SYM) {
+                double amax = 0.0;
+                for (int k = 0; k < K; ++k) amax = std::max(amax, std::fabs(v[k]));
+                if (amax == 0.0) {
+                    scales[n] = 0.0f;
+                    continue;  // codes already zero
+                }
+                const double inv = 7.0 / amax;
+                for (int k = 0; k < K; k += 2) {
+                    int c[2];
+                    for (int e = 0; e < 2; ++e) {
+                        double t = std::nearbyint(v[k + e] * inv);
+                        t = std::min(7.0, std::max(-7.0, t));
+                        c[e] = (int)t;
+                    }
+                    row[k / 2] = (uint8_t)((c[0] & 0xF) | ((c[1] & 0xF) << 4));
+                }
+                scales[n] = (float)(amax / 7.0);
+            } else {
+                double ss = 0.0;
+                for (int k = 0; k < K; ++k) ss += v[k] * v[k];
+                const double nrm = std::sqrt(ss);
+                if (nrm == 0.0) {
+                    scales[n] = 0.0f;
+                    continue;
+                }
+                const double g = std::sqrt((double)K) / nrm;
+                const int per_byte = 8 / q->w_bits;
+                for (int k = 0; k < K; ++k) {
+                    const double x = v[k] * g;
+                    int idx = 0;
+                    for (int i = 0; i + 1 < Lw; ++i) idx += (x > wth[i]) ? 1 : 0;
+                    row[k / per_byte] |= (uint8_t)(idx << ((k % per_byte) * q->w_bits));
+                }
+                scales[n] = (float)(nrm / std::sqrt((double)K));
+            }
+        }
+    };
+    unsigned nt = std::max(1u, std::min(32u, std::thread::hardware_concurrency()));
+    nt = std::min<unsigned>(nt, (unsigned)N);
+    std::vector<std::thread> pool;
+    const int chunk = (N + (int)nt - 1) / (int)nt;
+    for (unsigned t = 0; t < nt; ++t) {
+        const int n0 = (int)t * chunk, n1 = std::min(N, n0 + chunk);
+        if (n0 < n1) pool.emplace_back(work, n0, n1);
+    }
+    for (auto &th : pool) th.join();
+    return RQ_OK;
+}
+
+// Lloyd's iteration for N(0,1) in fp64, then bf16 rounding of the levels.
+rq_status rq_lloydmax_gaussian(int32_t L, float *levels) {
+    clear_error();
+    if (!levels) return fail(RQ_ERR_NULL, "levels is NULL");
+    if (L != 2 && L != 4 && L != 8 && L != 16)
+        return fail(RQ_ERR_SHAPE, "L must be 2, 4, 8 or 16");
+    const double inv_sqrt2 = 0.70710678118654752440;
+    const double inv_sqrt2pi = 0.39894228040143267794;
+    auto pdf = [&](double t) { return std::isinf(t) ? 0.0 : inv_sqrt2pi * std::exp(-0.5 * t * t); };
+    // upper-tail mass Q(t) = P(Z > t) through erfc (accurate in the tails)
+    auto upper = [&](double t) {
+        if (std::isinf(t)) return t > 0 ? 0.0 : 1.0;
+        return 0.5 * std::erfc(t * inv_sqrt2);
+    };
+    auto cell_mass = [&](double a, double b) {
+        if (a >= 0) return upper(a) - upper(b);
+        if (b <= 0) return upper(-b) - upper(-a);
+        return 1.0 - upper(-a) - upper(b);
+    };
+    std::vector<double> c(L), t(L + 1), nc(L);
+    const double span = 1.0 + 0.25 * std::log2((double)L);
+    for (int i = 0; i < L; ++i) c[i] = -span + 2.0 * span * (i + 0.5) / L;
+    for (int it = 0; it < 200000; ++it) {
+        t[0] = -INFINITY;
+        t[L] = INFINITY;
+        for (int i = 1; i < L; ++i) t[i] = (c[i - 1] + c[i]) / 2.0;
+        double delta = 0.0;
+        for (int i = 0; i < L; ++i) {
+            nc[i] = (pdf(t[i]) - pdf(t[i + 1])) / cell_mass(t[i], t[i + 1]);
+            delta = std::max(delta, std::fabs(nc[i] - c[i]));
+        }
+        c.swap(nc);
+        if (delta < 1e-15) break;
+    }
+    for (int i = 0; i < L; ++i) {
+        // nearest bf16 (8 significant bits), ties to even, straight from fp64
+        int e;
+        const double m = std::frexp(c[i], &e);      // c = m 2^e, 0.5 <= |m| < 1
+        const double q = std::nearbyint(m * 256.0);  // exact scaling; RNE mode
+        levels[i] = (float)std::ldexp(q, e - 8);
+    }
+    return RQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// rq_internal.h -- declarations shared by librq's translation units.
+#pragma once
+
+#include <cstdint>
+#include <cstddef>
+#include <string>
+
+#include "../../include/rq.h"
+
+namespace rq {
+
+// Thread-local error state behind rq_last_error().
+rq_status fail(rq_status st, const std::string &msg);
+void clear_error();
+
+// Shape/descriptor checks shared by pack and runtime entry points.
+rq_status check_rotation(const rq_rotation *rot, bool need_tables);
+rq_status check_quant(const rq_rotation *rot, const rq_quant *q);
+
+inline bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+inline int ilog2(int64_t v) { int l = 0; while ((int64_t(1) << l) < v) ++l; return l; }
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Kernel launchers (rq_rotate.hip, rq_gemm.hip).  Arguments are validated
+// by the caller; these only launch.  They return a hipError_t as int.
+int launch_rpbh_int4(const void *X, int x_bf16, int64_t T, int K, int block,
+                     const int8_t *sign, const int32_t *perm, uint8_t *codes,
+                     float *scale, void *stream);
+int launch_rpbh_lloydmax(const void *X, int x_bf16, int64_t T, int K, int block,
+                         const int8_t *sign, const int32_t *perm, const float *thresholds,
+                         int n_thresholds, uint8_t *codes, float *sigma, void *stream);
+int launch_dense_rotate(const void *X, int x_bf16, int64_t T, int K, const float *R,
+                        float *U, void *stream);
+int launch_dense_quant(const float *U, int64_t T, int K, int r, uint8_t *codes,
+                       float *scale, uint16_t *top, void *stream);
+int launch_gemm_w4a4(const uint8_t *codes, const float *scale, const uint16_t *top,
+                     int64_t T, const rq_weight_header *hdr, const void *blob,
+                     const float *bias, void *Y, int y_dtype, void *stream);
+int launch_gemm_codebook(const uint8_t *codes, const float *sigma, int64_t T,
+                         const rq_weight_header *hdr, const void *blob,
+                         const float *bias, void *Y, int y_dtype, void *stream);
+
+}  // namespace rq

@@ -1,0 +1,316 @@
+"""Thin ctypes binding of librq (include/rq.h): argument marshalling only.
+
+Every computation runs inside librq's gfx950 kernels (or, for the offline
+weight pack, in librq's host code).  This module converts numpy / torch
+arguments into the C structs and raw pointers of the C ABI, passes the
+current HIP stream, and raises RQError on any non-OK status.  There is no
+fallback: if librq.so is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librq.so")
+
+RQ_OK = 0
+RQ_F32, RQ_BF16, RQ_I32 = 0, 1, 2
+RQ_ROT_RPBH, RQ_ROT_DENSE = 0, 1
+RQ_Q_INT4_SYM, RQ_Q_LLOYDMAX = 0, 1
+RQ_WEIGHT_MAGIC = 0x31575152
+STATUS_NAMES = {0: "RQ_OK", -1: "RQ_ERR_NULL", -2: "RQ_ERR_SHAPE", -3: "RQ_ERR_DTYPE",
+                -4: "RQ_ERR_ALIGN", -5: "RQ_ERR_FORMAT", -6: "RQ_ERR_UNSUPPORTED",
+                -7: "RQ_ERR_HIP"}
+
+
+class RQError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class c_rotation(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("K", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("r", ctypes.c_int32), ("sign", ctypes.c_void_p), ("perm", ctypes.c_void_p),
+                ("R", ctypes.c_void_p)]
+
+
+class c_quant(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("a_bits", ctypes.c_int32), ("w_bits", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("a_levels", ctypes.c_float * 16),
+                ("w_levels", ctypes.c_float * 16)]
+
+
+class c_weight_header(ctypes.Structure):
+    _fields_ = [("magic", ctypes.c_uint32), ("version", ctypes.c_uint32),
+                ("format", ctypes.c_int32), ("K", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("r", ctypes.c_int32), ("b_div", ctypes.c_int32), ("a_bits", ctypes.c_int32),
+                ("w_bits", ctypes.c_int32), ("row_bytes", ctypes.c_int32),
+                ("scale_offset", ctypes.c_int64), ("codes_offset", ctypes.c_int64),
+                ("total_bytes", ctypes.c_int64), ("a_levels", ctypes.c_float * 16),
+                ("w_levels", ctypes.c_float * 16), ("reserved", ctypes.c_uint8 * 64)]
+
+
+assert ctypes.sizeof(c_weight_header) == 256
+
+# every symbol include/rq.h declares
+EXPORTS = ("rq_version", "rq_last_error", "rq_lloydmax_gaussian", "rq_packed_weight_bytes",
+           "rq_pack_weights", "rq_rotate_quant_workspace_bytes", "rq_rotate_quant",
+           "rq_w4a4_linear")
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load librq.so (built in-tree); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise FileNotFoundError(
+            f"{LIB_PATH} is missing: build it with `python -m rotated_w4a4_quantized_amd.build` "
+            "(there is no fallback path)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    L.rq_version.restype = I32
+    L.rq_last_error.restype = ctypes.c_char_p
+    L.rq_lloydmax_gaussian.argtypes = [I32, P]
+    L.rq_packed_weight_bytes.argtypes = [P, P, I32, ctypes.POINTER(SZ)]
+    L.rq_pack_weights.argtypes = [P, P, P, I32, I32, P, SZ]
+    L.rq_rotate_quant_workspace_bytes.argtypes = [P, P, I64, ctypes.POINTER(SZ)]
+    L.rq_rotate_quant.argtypes = [P, P, P, I32, I64, P, P, P, P, SZ, P]
+    L.rq_w4a4_linear.argtypes = [P, P, P, P, P, I64, P, P, I32, P]
+    for name in ("rq_lloydmax_gaussian", "rq_packed_weight_bytes", "rq_pack_weights",
+                 "rq_rotate_quant_workspace_bytes", "rq_rotate_quant", "rq_w4a4_linear"):
+        getattr(L, name).restype = I32
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != RQ_OK:
+        raise RQError(status, load().rq_last_error().decode())
+
+
+def _np_ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"]
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _t_ptr(t):
+    if t is None:
+        return None
+    assert t.is_contiguous(), "device buffers must be contiguous"
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ---------------------------------------------------------------------------
+# descriptors
+# ---------------------------------------------------------------------------
+
+@dataclass
+class Rotation:
+    """Host description of a rotation (numpy arrays)."""
+    kind: int
+    K: int
+    block: int = 0
+    r: int = 0
+    sign: Optional[np.ndarray] = None
+    perm: Optional[np.ndarray] = None
+    R: Optional[np.ndarray] = None
+
+    @staticmethod
+    def rpbh(sign, perm, block):
+        sign = np.ascontiguousarray(sign, np.int8)
+        perm = np.ascontiguousarray(perm, np.int32)
+        return Rotation(RQ_ROT_RPBH, int(sign.size), int(block), 0, sign, perm, None)
+
+    @staticmethod
+    def dense(R, r):
+        R = np.ascontiguousarray(R, np.float32)
+        return Rotation(RQ_ROT_DENSE, int(R.shape[0]), 0, int(r), None, None, R)
+
+    def c_host(self) -> c_rotation:
+        return c_rotation(self.kind, self.K, self.block, self.r,
+                          None if self.sign is None else self.sign.ctypes.data,
+                          None if self.perm is None else self.perm.ctypes.data,
+                          None if self.R is None else self.R.ctypes.data)
+
+    def to_device(self, device="cuda") -> "DeviceRotation":
+        import torch
+        d = DeviceRotation(self)
+        if self.sign is not None:
+            d.sign = torch.from_numpy(self.sign).to(device)
+            d.perm = torch.from_numpy(self.perm).to(device)
+        if self.R is not None:
+            d.R = torch.from_numpy(self.R).to(device)
+        return d
+
+
+@dataclass
+class DeviceRotation:
+    host: Rotation
+    sign: object = None
+    perm: object = None
+    R: object = None
+
+    def c_dev(self) -> c_rotation:
+        h = self.host
+        return c_rotation(h.kind, h.K, h.block, h.r,
+                          None if self.sign is None else self.sign.data_ptr(),
+                          None if self.perm is None else self.perm.data_ptr(),
+                          None if self.R is None else self.R.data_ptr())
+
+
+@dataclass
+class Quant:
+    kind: int = RQ_Q_INT4_SYM
+    a_bits: int = 4
+    w_bits: int = 4
+    a_levels: Optional[np.ndarray] = None
+    w_levels: Optional[np.ndarray] = None
+
+    @staticmethod
+    def int4():
+        return Quant(RQ_Q_INT4_SYM, 4, 4)
+
+    @staticmethod
+    def lloydmax(a_levels, w_levels):
+        a = np.ascontiguousarray(a_levels, np.float32)
+        w = np.ascontiguousarray(w_levels, np.float32)
+        return Quant(RQ_Q_LLOYDMAX, 4, int(np.log2(w.size)), a, w)
+
+    def c(self) -> c_quant:
+        q = c_quant(self.kind, self.a_bits, self.w_bits, 0)
+        if self.a_levels is not None:
+            for i, v in enumerate(self.a_levels):
+                q.a_levels[i] = float(v)
+        if self.w_levels is not None:
+            for i, v in enumerate(self.w_levels):
+                q.w_levels[i] = float(v)
+        return q
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+def version() -> int:
+    return load().rq_version()
+
+
+def lloydmax_gaussian(L: int) -> np.ndarray:
+    out = np.zeros(L, np.float32)
+    _check(load().rq_lloydmax_gaussian(L, _np_ptr(out)))
+    return out
+
+
+def packed_weight_bytes(rot: Rotation, q: Quant, N: int) -> int:
+    n = ctypes.c_size_t(0)
+    cr, cq = rot.c_host(), q.c()
+    _check(load().rq_packed_weight_bytes(ctypes.byref(cr), ctypes.byref(cq), N, ctypes.byref(n)))
+    return n.value
+
+
+@dataclass
+class PackedWeights:
+    blob: np.ndarray                      # uint8, host
+    header: c_weight_header = field(default=None)
+
+    @property
+    def N(self):
+        return self.header.N
+
+    @property
+    def K(self):
+        return self.header.K
+
+    def scales(self) -> np.ndarray:
+        h = self.header
+        return self.blob[h.scale_offset:h.scale_offset + 4 * h.N].view(np.float32)
+
+    def codes(self) -> np.ndarray:
+        h = self.header
+        return self.blob[h.codes_offset:h.codes_offset + h.N * h.row_bytes].reshape(h.N, h.row_bytes)
+
+    def to_device(self, device="cuda") -> "DeviceWeights":
+        import torch
+        return DeviceWeights(self.header, torch.from_numpy(self.blob).to(device))
+
+
+@dataclass
+class DeviceWeights:
+    header: c_weight_header
+    blob: object                          # torch uint8 tensor on the GPU
+
+    @property
+    def N(self):
+        return self.header.N
+
+
+def pack_weights(rot: Rotation, q: Quant, W: np.ndarray) -> PackedWeights:
+    """Offline fold + quantize + pack (librq host code)."""
+    if W.dtype == np.float32:
+        wdt = RQ_F32
+    elif W.dtype == np.uint16:
+        wdt = RQ_BF16
+    else:
+        raise TypeError("W must be float32 or bf16 bit patterns (uint16)")
+    W = np.ascontiguousarray(W)
+    N = int(W.shape[0])
+    nbytes = packed_weight_bytes(rot, q, N)
+    blob = np.zeros(nbytes, np.uint8)
+    cr, cq = rot.c_host(), q.c()
+    _check(load().rq_pack_weights(ctypes.byref(cr), ctypes.byref(cq), _np_ptr(W), wdt, N,
+                                  _np_ptr(blob), nbytes))
+    hdr = c_weight_header.from_buffer_copy(blob[:256].tobytes())
+    return PackedWeights(blob, hdr)
+
+
+def rotate_quant_workspace_bytes(rot: Rotation, q: Quant, T: int) -> int:
+    n = ctypes.c_size_t(0)
+    cr, cq = rot.c_host(), q.c()
+    _check(load().rq_rotate_quant_workspace_bytes(ctypes.byref(cr), ctypes.byref(cq), T,
+                                                  ctypes.byref(n)))
+    return n.value
+
+
+def dtype_code(t) -> int:
+    import torch
+    return {torch.float32: RQ_F32, torch.bfloat16: RQ_BF16, torch.int16: RQ_BF16,
+            torch.uint16: RQ_BF16, torch.int32: RQ_I32}[t.dtype]
+
+
+def rotate_quant(drot: DeviceRotation, q: Quant, X, codes, scale, top=None, workspace=None,
+                 stream=None):
+    """Launch the activation kernels on `stream` (default: torch's current)."""
+    cr, cq = drot.c_dev(), q.c()
+    T = int(X.shape[0])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().rq_rotate_quant(ctypes.byref(cr), ctypes.byref(cq), _t_ptr(X), dtype_code(X), T,
+                                  _t_ptr(codes), _t_ptr(scale), _t_ptr(top), _t_ptr(workspace),
+                                  ws_bytes, _stream(stream)))
+
+
+def w4a4_linear(dw: DeviceWeights, codes, scale, Y, top=None, bias=None, T=None, stream=None):
+    """Launch the low-bit GEMM; Y dtype picks the output (f32, bf16, raw int32)."""
+    T = int(codes.shape[0]) if T is None else T
+    _check(load().rq_w4a4_linear(ctypes.byref(dw.header), _t_ptr(dw.blob), _t_ptr(codes),
+                                 _t_ptr(scale), _t_ptr(top), T, _t_ptr(bias), _t_ptr(Y),
+                                 dtype_code(Y), _stream(stream)))

@@ -1,0 +1,201 @@
+"""C-ABI checks that need no GPU: librq loads, exports every symbol that
+include/rq.h declares, rejects bad arguments before touching the GPU, and its
+host-side weight pack (fold in fp64 + quantize + pack) and Lloyd-Max codebook
+match the oracle bit for bit.
+
+Weight pack: "DiRotQ" abstract (inverse rotation fused into the weights
+offline), "OrbitQuant" abstract (rotation absorbed into the weight rows,
+same normalized-basis quantizer), "TR-DQ" Eq.(9) and section 3.1
+(per-output-channel weight quantization).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import oracle as orc
+from rotated_w4a4_quantized_amd import datagen, rq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "rq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = rq.load()
+    declared = header_functions()
+    assert declared, "no declarations parsed"
+    assert sorted(rq.EXPORTS) == declared
+    for name in declared:
+        assert hasattr(L, name), name
+    assert rq.version() >= 100
+
+
+def test_struct_sizes_match_header():
+    assert ctypes.sizeof(rq.c_weight_header) == 256
+    assert ctypes.sizeof(rq.c_quant) == 16 + 128
+    assert ctypes.sizeof(rq.c_rotation) == 16 + 24
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def _rq_call(rot: rq.c_rotation, q: rq.c_quant, X=1 << 20, xdt=rq.RQ_BF16, T=4, codes=1 << 20,
+             scale=1 << 20, top=None, ws=None, wsb=0):
+    L = rq.load()
+    return L.rq_rotate_quant(ctypes.byref(rot), ctypes.byref(q), ctypes.c_void_p(X), xdt, T,
+                             ctypes.c_void_p(codes), ctypes.c_void_p(scale),
+                             None if top is None else ctypes.c_void_p(top),
+                             None if ws is None else ctypes.c_void_p(ws), wsb, None)
+
+
+def _rpbh(K=256, b=64):
+    # pointer values only: every call below is rejected (or returns for T == 0)
+    # before any pointer is dereferenced or any HIP call is made
+    return rq.c_rotation(rq.RQ_ROT_RPBH, K, b, 0, 1 << 20, 1 << 21, None)
+
+
+def test_rotate_quant_validation_errors():
+    q = rq.Quant.int4().c()
+    assert _rq_call(rq.c_rotation(rq.RQ_ROT_RPBH, 100, 4, 0, 1 << 20, 1 << 21, None), q) == -2
+    assert _rq_call(rq.c_rotation(rq.RQ_ROT_RPBH, 256, 48, 0, 1 << 20, 1 << 21, None), q) == -2
+    assert _rq_call(rq.c_rotation(rq.RQ_ROT_RPBH, 256, 512, 0, 1 << 20, 1 << 21, None), q) == -2
+    assert _rq_call(rq.c_rotation(rq.RQ_ROT_RPBH, 32768, 64, 0, 1 << 20, 1 << 21, None), q) == -2
+    assert _rq_call(rq.c_rotation(rq.RQ_ROT_RPBH, 256, 64, 0, None, 1 << 21, None), q) == -1
+    assert _rq_call(rq.c_rotation(7, 256, 64, 0, 1 << 20, 1 << 21, None), q) == -6
+    assert _rq_call(_rpbh(), q, xdt=5) == -3
+    assert _rq_call(_rpbh(), q, T=-1) == -2
+    assert _rq_call(_rpbh(), q, X=0) == -1
+    assert _rq_call(_rpbh(), q, codes=(1 << 20) + 8) == -4
+    assert "aligned" in rq.load().rq_last_error().decode()
+    # dense: r must be a multiple of 32 below K; workspace required; top required
+    dense = rq.c_rotation(rq.RQ_ROT_DENSE, 256, 0, 16, None, None, 1 << 22)
+    assert _rq_call(dense, q) == -2
+    dense = rq.c_rotation(rq.RQ_ROT_DENSE, 256, 0, 32, None, None, 1 << 22)
+    assert _rq_call(dense, q, top=None) == -1
+    assert _rq_call(dense, q, top=1 << 23, ws=None) == -2
+    # a bad quantizer
+    bad = rq.Quant(kind=rq.RQ_Q_INT4_SYM, a_bits=4, w_bits=2).c()
+    assert _rq_call(_rpbh(), bad) == -6
+    lm = rq.Quant.lloydmax(np.arange(16, dtype=np.float32)[::-1], np.arange(4, dtype=np.float32)).c()
+    assert _rq_call(_rpbh(), lm) == -2      # levels not ascending
+    lm = rq.Quant.lloydmax(np.linspace(-2, 2, 16).astype(np.float32), np.arange(4, dtype=np.float32)).c()
+    assert _rq_call(_rpbh(), lm) == -2      # levels not bf16-representable
+
+
+def test_empty_token_batch_is_a_no_op():
+    # T == 0 returns before any pointer is read or any kernel launched
+    assert _rq_call(_rpbh(), rq.Quant.int4().c(), T=0, X=0, codes=0, scale=0) == 0
+    hdr = _small_header()
+    L = rq.load()
+    assert L.rq_w4a4_linear(ctypes.byref(hdr), None, None, None, None, 0, None, None,
+                            rq.RQ_F32, None) == 0
+
+
+def _small_header():
+    w = datagen.WORKLOADS["tiny"].with_shape(T=8, K=256, N=64, block=64)
+    inp = datagen.make_inputs(w)
+    pw = rq.pack_weights(rq.Rotation.rpbh(inp["sign"], inp["perm"], 64), rq.Quant.int4(), inp["W"])
+    return pw.header
+
+
+def test_linear_validation_errors():
+    L = rq.load()
+    hdr = _small_header()
+    args = lambda h, ydt=rq.RQ_F32, Y=1 << 24: (ctypes.byref(h), ctypes.c_void_p(1 << 20),
+                                                ctypes.c_void_p(1 << 21), ctypes.c_void_p(1 << 22),
+                                                None, 4, None, ctypes.c_void_p(Y), ydt, None)
+    bad = rq.c_weight_header.from_buffer_copy(bytes(hdr))
+    bad.magic = 0
+    assert L.rq_w4a4_linear(*args(bad)) == -5
+    bad = rq.c_weight_header.from_buffer_copy(bytes(hdr))
+    bad.version = 9
+    assert L.rq_w4a4_linear(*args(bad)) == -5
+    bad = rq.c_weight_header.from_buffer_copy(bytes(hdr))
+    bad.row_bytes += 1
+    assert L.rq_w4a4_linear(*args(bad)) == -5
+    assert L.rq_w4a4_linear(*args(hdr, ydt=9)) == -3
+    assert L.rq_w4a4_linear(*args(hdr, Y=(1 << 24) + 4)) == -4
+    assert L.rq_w4a4_linear(None, None, None, None, None, 1, None, None, 0, None) == -1
+
+
+def test_lloydmax_codebook_matches_oracle():
+    for L in (2, 4, 8, 16):
+        assert np.array_equal(rq.lloydmax_gaussian(L), orc.codebook_bf16(L)), L
+    with pytest.raises(rq.RQError):
+        rq.lloydmax_gaussian(5)
+
+
+def _oracle_weights(w, inp, q_kind=0, levels=None):
+    if w.rot == "rpbh":
+        return orc.weight_rows(inp["W"], rot_kind=0, b=w.block, sign=inp["sign"], perm=inp["perm"],
+                               q_kind=q_kind, levels=levels)
+    return orc.weight_rows(inp["W"], rot_kind=1, R=inp["R"], q_kind=q_kind, levels=levels)
+
+
+@pytest.mark.parametrize("name,shape", [("tiny", dict(N=96)),
+                                        ("flux_up", dict(K=1024, N=70, block=256)),
+                                        ("flux_down", dict(K=2048, N=33, block=512)),
+                                        ("pixart", dict(K=256, N=40)),
+                                        ("tiny", dict(K=64, N=10, block=2))])
+def test_pack_int4_matches_oracle(name, shape):
+    w = datagen.WORKLOADS[name].with_shape(T=4, **shape)
+    inp = datagen.make_inputs(w)
+    rot = (rq.Rotation.rpbh(inp["sign"], inp["perm"], w.block) if w.rot == "rpbh"
+           else rq.Rotation.dense(inp["R"], w.r))
+    pw = rq.pack_weights(rot, rq.Quant.int4(), inp["W"])
+    ref = _oracle_weights(w, inp)
+    assert np.array_equal(pw.codes(), ref["codes"])
+    assert np.array_equal(pw.scales().view(np.uint32), ref["scale"].view(np.uint32))
+    h = pw.header
+    assert (h.magic, h.K, h.N, h.r, h.b_div, h.row_bytes) == (
+        rq.RQ_WEIGHT_MAGIC, w.K, w.N, w.r, w.b_eff, w.K // 2)
+
+
+def test_pack_bf16_weights_and_zero_rows():
+    w = datagen.WORKLOADS["flux_up"].with_shape(T=4, K=512, N=16, block=128)
+    inp = datagen.make_inputs(w)
+    Wb = datagen.f32_to_bf16_bits(inp["W"])
+    Wb[3] = 0
+    inp2 = dict(inp, W=datagen.bf16_bits_to_f32(Wb))
+    pw = rq.pack_weights(rq.Rotation.rpbh(inp["sign"], inp["perm"], 128), rq.Quant.int4(), Wb)
+    ref = _oracle_weights(w, inp2)
+    assert np.array_equal(pw.codes(), ref["codes"])
+    assert np.array_equal(pw.scales(), ref["scale"])
+    assert pw.scales()[3] == 0 and not pw.codes()[3].any()
+
+
+def test_pack_lloydmax_matches_oracle():
+    w = datagen.WORKLOADS["video"].with_shape(T=4, K=512, N=24, block=256)
+    inp = datagen.make_inputs(w)
+    a_lv, w_lv = rq.lloydmax_gaussian(16), rq.lloydmax_gaussian(4)
+    pw = rq.pack_weights(rq.Rotation.rpbh(inp["sign"], inp["perm"], 256),
+                         rq.Quant.lloydmax(a_lv, w_lv), inp["W"])
+    ref = _oracle_weights(w, inp, q_kind=1, levels=orc.codebook_bf16(4))
+    assert np.array_equal(pw.codes(), ref["codes"])
+    assert np.array_equal(pw.scales(), ref["scale"])
+    assert pw.header.row_bytes == w.K // 4 and pw.header.b_div == 256
+    assert np.array_equal(np.array(pw.header.a_levels[:16], np.float32), a_lv)
+
+
+def test_pack_rejects_bad_tables():
+    sign, perm = datagen.random_rpbh(256, 1)
+    perm = perm.copy()
+    perm[0] = perm[1]
+    W = np.zeros((4, 256), np.float32)
+    with pytest.raises(rq.RQError, match="permutation"):
+        rq.pack_weights(rq.Rotation.rpbh(sign, perm, 64), rq.Quant.int4(), W)
+    sign2 = sign.copy()
+    sign2[5] = 0
+    with pytest.raises(rq.RQError, match="sign"):
+        rq.pack_weights(rq.Rotation.rpbh(sign2, np.arange(256, dtype=np.int32), 64), rq.Quant.int4(), W)
+    with pytest.raises(TypeError):
+        rq.pack_weights(rq.Rotation.rpbh(sign, np.arange(256, dtype=np.int32), 64), rq.Quant.int4(),
+                        W.astype(np.float64))

@@ -1,0 +1,196 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle, on the
+same seeded inputs.  Integer results bit-exact, floats within the stated
+tolerance (tests/_layer.py).
+
+Small shapes span several 128 x 128 GEMM tiles with ragged token and output
+tails; the full workloads (tiny 256x1152->1152 fp32, pixart 8192x1152->4608
+dense, flux_up 9216x3072->12288, flux_down 9216x12288->3072, video
+32760x1536->8960 Lloyd-Max W2A4) run in the launch configuration bench.py
+times, with every code and scale compared and the outputs compared at
+sampled (token, channel) pairs.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from rotated_w4a4_quantized_amd import datagen
+from tests import _layer as H
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check_act(w, L, act, rows=None):
+    codes = L.codes.cpu().numpy()
+    scale = L.scale.cpu().numpy()
+    if rows is not None:
+        codes, scale = codes[rows], scale[rows]
+    assert np.array_equal(scale.view(np.uint32), act["scale"].view(np.uint32)), \
+        f"scale mismatch in {int(np.sum(scale != act['scale']))} tokens"
+    bad = np.nonzero(np.any(codes != act["codes"], axis=1))[0]
+    assert bad.size == 0, f"codes differ in {bad.size} tokens, first {bad[:5]}"
+    if w.r:
+        top = L.top.cpu().numpy().view(np.uint16)
+        if rows is not None:
+            top = top[rows]
+        assert np.array_equal(top, act["top"])
+
+
+SMALL = [
+    ("tiny", dict(T=300, N=200)),
+    ("tiny", dict(T=1, N=130, K=256, block=256)),
+    ("flux_up", dict(T=257, K=3072, N=384)),
+    ("flux_down", dict(T=131, K=12288, N=136)),
+    ("video", dict(T=190, N=264)),
+    ("pixart", dict(T=200, N=170)),
+    ("tiny", dict(T=70, K=1024, N=128, block=1024)),
+    ("tiny", dict(T=65, K=96, N=40, block=2)),
+    ("tiny", dict(T=33, K=32, N=7, block=8)),
+    ("flux_up", dict(T=40, K=16384, N=64, block=512)),
+]
+
+
+@pytest.mark.parametrize("name,shape", SMALL, ids=[f"{n}-{'-'.join(f'{k}{v}' for k, v in s.items())}"
+                                                   for n, s in SMALL])
+def test_small_full_parity(name, shape):
+    w = datagen.WORKLOADS[name].with_shape(**shape)
+    say(f"[parity small] {w}")
+    inp = datagen.make_inputs(w)
+    L = H.GpuLayer(w, inp, y_dtype="f32")
+    L.run()
+    torch.cuda.synchronize()
+    act = H.oracle_act(w, inp)
+    check_act(w, L, act)
+    wts = H.oracle_weights(w, inp)
+    assert np.array_equal(L.packed.codes(), wts["codes"])
+    ta, nw = np.meshgrid(np.arange(w.T), np.arange(w.N), indexing="ij")
+    ta, nw = ta.ravel(), nw.ravel()
+    yhat = H.oracle_yhat_pairs(w, act, wts, ta, nw)
+    y = L.Y.cpu().numpy().ravel()
+    err = H.rel_err(y, yhat)
+    say(f"  fp32 output max floored rel err {err:.3e}")
+    assert err <= H.REL_TOL
+    if w.quant == "int4":
+        acc = L.raw_acc().cpu().numpy().astype(np.int64)
+        import oracle.oracle as orc
+        ref = orc.int_gemm(act["codes"], w.Kq, wts["codes"], w.K, koff=w.r)
+        assert np.array_equal(acc, 256 * ref)
+    # bf16 output of the same kernels
+    Yb = torch.empty((w.T, w.N), dtype=torch.bfloat16, device="cuda")
+    L.linear(Yb)
+    dist, ok = H.bf16_check(H.to_np_bf16_bits(Yb).ravel(), yhat)
+    say(f"  bf16 output max ulp distance {dist}")
+    assert ok
+
+
+FULL = ["tiny", "flux_up", "flux_down", "video", "pixart"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_workload_parity(name):
+    w = datagen.WORKLOADS[name]
+    say(f"[parity full] {w}")
+    inp = datagen.make_inputs(w)
+    L = H.GpuLayer(w, inp)
+    L.run()
+    torch.cuda.synchronize()
+    g = np.random.default_rng(7)
+    # every code and scale for the RPBH paths; a token sample for the dense
+    # path, whose oracle rotation is a K x K fp32 chain per token
+    rows = None if w.rot == "rpbh" else np.sort(g.choice(w.T, 512, replace=False))
+    act = H.oracle_act(w, inp, rows)
+    check_act(w, L, act, rows)
+    wts = H.oracle_weights(w, inp)
+    assert np.array_equal(L.packed.codes(), wts["codes"])
+    # outputs at sampled pairs: 8192 random pairs plus two whole tokens and
+    # two whole channels
+    tok_pool = np.arange(w.T) if rows is None else rows
+    ta = g.choice(tok_pool, 8192)
+    nw = g.integers(0, w.N, 8192)
+    t2 = np.repeat(tok_pool[[0, -1]], w.N)
+    n2 = np.tile(np.arange(w.N), 2)
+    n3 = np.repeat(np.array([0, w.N - 1]), tok_pool.size)
+    t3 = np.tile(tok_pool, 2)
+    ta = np.concatenate([ta, t2, t3])
+    nw = np.concatenate([nw, n2, n3])
+    yhat = H.oracle_yhat_pairs(w, act, wts, ta, nw, act_rows=rows)
+    Y = L.Y
+    idx = torch.from_numpy(ta).to("cuda") * w.N + torch.from_numpy(nw).to("cuda")
+    ys = Y.view(-1)[idx]
+    if w.ydtype == "f32":
+        err = H.rel_err(ys.cpu().numpy(), yhat)
+        say(f"  fp32 max floored rel err {err:.3e}")
+        assert err <= H.REL_TOL
+    else:
+        dist, ok = H.bf16_check(H.to_np_bf16_bits(ys), yhat)
+        say(f"  bf16 max ulp distance {dist}")
+        assert ok
+        # and the fp32-output run of the same kernels meets the 1e-3 bound
+        Yf = torch.empty((w.T, w.N), dtype=torch.float32, device="cuda")
+        L.linear(Yf)
+        err = H.rel_err(Yf.view(-1)[idx].cpu().numpy(), yhat)
+        say(f"  fp32 max floored rel err {err:.3e}")
+        assert err <= H.REL_TOL
+
+
+def test_zero_tokens_and_determinism():
+    w = datagen.WORKLOADS["flux_up"].with_shape(T=300, K=3072, N=256)
+    inp = datagen.make_inputs(w)
+    Xz = inp["X"].copy()
+    Xz[[0, 17, 299]] = 0
+    inp = dict(inp, X=Xz, Xf=datagen.bf16_bits_to_f32(Xz))
+    L = H.GpuLayer(w, inp, y_dtype="f32")
+    L.run()
+    c1, s1, y1 = L.codes.clone(), L.scale.clone(), L.Y.clone()
+    L.run()
+    torch.cuda.synchronize()
+    assert torch.equal(c1, L.codes) and torch.equal(s1, L.scale) and torch.equal(y1, L.Y)
+    for t in (0, 17, 299):
+        assert float(L.scale[t]) == 0.0 and int(L.codes[t].abs().sum()) == 0
+        assert float(L.Y[t].abs().max()) == 0.0
+
+
+def test_outputs_stay_in_bounds():
+    # guard bands after every output buffer must be untouched
+    w = datagen.WORKLOADS["tiny"].with_shape(T=77, N=150)
+    inp = datagen.make_inputs(w)
+    L = H.GpuLayer(w, inp, y_dtype="f32")
+    G = 4096
+    codes = torch.full((w.T * w.K // 2 + G,), 0xA5, dtype=torch.uint8, device="cuda")
+    scale = torch.full((w.T + G,), 7.5, dtype=torch.float32, device="cuda")
+    Y = torch.full((w.T * w.N + G,), 3.25, dtype=torch.float32, device="cuda")
+    L.codes = codes[: w.T * w.K // 2].view(w.T, w.K // 2)
+    L.scale = scale[: w.T]
+    L.rotate_quant()
+    L.linear(Y[: w.T * w.N].view(w.T, w.N))
+    torch.cuda.synchronize()
+    assert bool((codes[w.T * w.K // 2:] == 0xA5).all())
+    assert bool((scale[w.T:] == 7.5).all())
+    assert bool((Y[w.T * w.N:] == 3.25).all())
+
+
+def test_runs_on_a_side_stream():
+    w = datagen.WORKLOADS["tiny"].with_shape(T=128, N=128)
+    inp = datagen.make_inputs(w)
+    L = H.GpuLayer(w, inp, y_dtype="f32")
+    L.run()
+    ref = L.Y.clone()
+    L.Y.zero_()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        L.run()
+    s.synchronize()
+    assert torch.equal(ref, L.Y)
