@@ -1,0 +1,214 @@
+// rq_gemm_codebook.hip -- codebook GEMM of the Lloyd-Max variant for gfx950.
+//
+// "OrbitQuant" abstract: tokens and weight rows are quantized in a
+// normalized rotated basis with fixed Lloyd-Max codebooks; the output is
+//   Y[t][n] = sigma[t] tau[n] / b * sum_k a_levels[ia[t][k]] w_levels[iw[n][k]]
+// 4-bit activation and 2-bit (or 4-bit) weight level indices are decoded to
+// bf16 through LDS look-up tables (one entry per packed byte), staged as bf16
+// tiles, and multiplied on bf16 MFMA (v_mfma_f32_32x32x16_bf16) with fp32
+// accumulation.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rq_internal.h"
+
+namespace rq {
+namespace {
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr int BM = 128, BN = 128;
+
+// Output element e of a 32x32 MFMA accumulator held by lane l:
+// column l % 32, row 8 * (e / 4) + 4 * (l / 32) + e % 4.
+__device__ inline int acc_row(int e, int lane) { return 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); }
+
+
+__device__ inline uint16_t f32_to_bf16_rne(float x) {
+    const uint32_t b = __float_as_uint(x);
+    const uint32_t lower = b & 0xFFFFu, upper = b >> 16;
+    return (uint16_t)(upper + ((lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) ? 1u : 0u));
+}
+
+__device__ inline __bf16 bits_to_bf16(uint16_t h) {
+    return __builtin_bit_cast(__bf16, h);
+}
+
+// ---------------------------------------------------------------------------
+// Codebook GEMM (W2A4 / W4A4 Lloyd-Max)
+// ---------------------------------------------------------------------------
+struct CodebookArgs {
+    const uint8_t *A;      // activation indices, 4-bit, [T][K/2]
+    const uint8_t *B;      // weight indices, w_bits, [N][ldb]
+    const float *sigma;    // [T]
+    const float *tau;      // [N]
+    const float *bias;
+    const float *a_levels; // device, inside the blob header (16)
+    const float *w_levels; // device (16)
+    void *Y;
+    int64_t T;
+    int N, K, ldb, w_bits, ydt;
+    float post;            // 1 / b_div
+};
+
+constexpr int CBK = 64;                // k per stage
+constexpr int CLDS = CBK * 2 + 16;     // bf16 tile row stride in bytes (padded)
+
+__global__ void __launch_bounds__(256)
+gemm_codebook_kernel(CodebookArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t As[BM * CLDS];
+    __shared__ __attribute__((aligned(16))) uint8_t Bs[BN * CLDS];
+    __shared__ uint32_t lutA[256];   // packed byte of two 4-bit indices -> two bf16
+    __shared__ uint2 lutB[256];      // packed byte of four 2-bit indices -> four bf16
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t m0 = (int64_t)blockIdx.y * BM;
+    const int n0 = blockIdx.x * BN;
+    const int li = lane & 31, lg = lane >> 5;
+    {
+        const uint32_t lo = __float_as_uint(a.a_levels[tid & 15]) >> 16;
+        const uint32_t hi = __float_as_uint(a.a_levels[tid >> 4]) >> 16;
+        lutA[tid] = lo | (hi << 16);
+        if (a.w_bits == 2) {
+            uint32_t h[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = __float_as_uint(a.w_levels[(tid >> (2 * e)) & 3]) >> 16;
+            lutB[tid] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        } else {
+            lutB[tid] = make_uint2(0, 0);
+        }
+    }
+    __syncthreads();
+    v16f acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    for (int k0 = 0; k0 < a.K; k0 += CBK) {
+        // A: 128 rows x 32 bytes; thread -> row tid / 2, 16 bytes at (tid & 1) * 16
+        {
+            const int row = tid >> 1, cb = (tid & 1) * 16;
+            int64_t ar = m0 + row;
+            if (ar >= a.T) ar = a.T - 1;
+            const uint4 v = *reinterpret_cast<const uint4 *>(a.A + ar * (a.K / 2) + k0 / 2 + cb);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            uint32_t d[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int by = 0; by < 4; ++by) d[4 * q + by] = lutA[(w[q] >> (8 * by)) & 0xFFu];
+            uint4 *dst = reinterpret_cast<uint4 *>(As + row * CLDS + cb * 4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dst[q] = make_uint4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]);
+        }
+        // B: 128 rows x 64 k
+        if (a.w_bits == 2) {
+            const int row = tid >> 1, cb = (tid & 1) * 8;   // 8 bytes = 32 k
+            int br = n0 + row;
+            if (br >= a.N) br = a.N - 1;
+            const uint2 v = *reinterpret_cast<const uint2 *>(a.B + (int64_t)br * a.ldb + k0 / 4 + cb);
+            const uint32_t w[2] = {v.x, v.y};
+            uint2 d[8];
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int by = 0; by < 4; ++by) d[4 * q + by] = lutB[(w[q] >> (8 * by)) & 0xFFu];
+            uint4 *dst = reinterpret_cast<uint4 *>(Bs + row * CLDS + cb * 8);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dst[q] = make_uint4(d[2 * q].x, d[2 * q].y, d[2 * q + 1].x, d[2 * q + 1].y);
+        } else {
+            const int row = tid >> 1, cb = (tid & 1) * 16;  // 16 bytes = 32 k (4-bit weights)
+            int br = n0 + row;
+            if (br >= a.N) br = a.N - 1;
+            const uint4 v = *reinterpret_cast<const uint4 *>(a.B + (int64_t)br * a.ldb + k0 / 2 + cb);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            uint32_t d[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int by = 0; by < 4; ++by) {
+                    const uint32_t bt = (w[q] >> (8 * by)) & 0xFFu;
+                    const uint32_t lo = __float_as_uint(a.w_levels[bt & 15]) >> 16;
+                    const uint32_t hi = __float_as_uint(a.w_levels[bt >> 4]) >> 16;
+                    d[4 * q + by] = lo | (hi << 16);
+                }
+            uint4 *dst = reinterpret_cast<uint4 *>(Bs + row * CLDS + cb * 4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dst[q] = make_uint4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < CBK / 16; ++ks) {
+            v8bf fa[2], fb[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                fa[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4 *>(
+                                                     As + (wm * 64 + i * 32 + li) * CLDS + (ks * 16 + 8 * lg) * 2));
+                fb[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4 *>(
+                                                     Bs + (wn * 64 + i * 32 + li) * CLDS + (ks * 16 + 8 * lg) * 2));
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = n0 + wn * 64 + j * 32 + li;
+            if (col >= a.N) continue;
+            const float tn = a.tau[col] * a.post;
+            const float bn = a.bias ? a.bias[col] : 0.0f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t row = m0 + wm * 64 + i * 32 + acc_row(e, lane);
+                if (row >= a.T) continue;
+                const float y = acc[i][j][e] * (a.sigma[row] * tn) + bn;
+                const int64_t o = row * a.N + col;
+                if (a.ydt == RQ_F32)
+                    static_cast<float *>(a.Y)[o] = y;
+                else
+                    static_cast<uint16_t *>(a.Y)[o] = f32_to_bf16_rne(y);
+            }
+        }
+    }
+}
+
+}  // namespace
+
+int launch_gemm_codebook(const uint8_t *codes, const float *sigma, int64_t T,
+                         const rq_weight_header *hdr, const void *blob, const float *bias,
+                         void *Y, int y_dtype, void *stream) {
+    CodebookArgs a;
+    const uint8_t *base = static_cast<const uint8_t *>(blob);
+    a.A = codes;
+    a.B = base + hdr->codes_offset;
+    a.sigma = sigma;
+    a.tau = reinterpret_cast<const float *>(base + hdr->scale_offset);
+    a.bias = bias;
+    a.a_levels = reinterpret_cast<const float *>(base + offsetof(rq_weight_header, a_levels));
+    a.w_levels = reinterpret_cast<const float *>(base + offsetof(rq_weight_header, w_levels));
+    a.Y = Y;
+    a.T = T;
+    a.N = hdr->N;
+    a.K = hdr->K;
+    a.ldb = hdr->row_bytes;
+    a.w_bits = hdr->w_bits;
+    a.ydt = y_dtype;
+    a.post = 1.0f / (float)hdr->b_div;
+    dim3 grid((hdr->N + BN - 1) / BN, (unsigned)((T + BM - 1) / BM));
+    hipLaunchKernelGGL(gemm_codebook_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream), a);
+    return (int)hipGetLastError();
+}
+
+}  // namespace rq
