@@ -1,0 +1,481 @@
+// rq_rpbh.hip -- runtime activation path for gfx950 with the randomized
+// permuted block-Hadamard (RPBH) rotation, then per-token 4-bit
+// quantization: symmetric INT4, or the Lloyd-Max codebook on the
+// norm-normalized token.
+//
+// Rotation ("OrbitQuant" abstract; block structure "TR-DQ" Eq.(8)):
+//   y[j] = sign[j] * x[perm[j]]; then on every b-block the unnormalized
+//   Sylvester transform by radix-2 fp32 butterflies (lo, hi) -> (lo + hi,
+//   lo - hi), stages h = 1, 2, ..., b/2 in that order.  Inside one stage the
+//   butterflies are independent, so any schedule that keeps the stage order
+//   and evaluates lo + hi and lo - hi in fp32 gives the same bits.
+//
+// Work decomposition.  A token is owned by K/32 threads, 32 coordinates
+// each; a workgroup holds `tpw` tokens.  Per token:
+//   staging  the row is read from HBM one iteration ahead (coalesced 16-byte
+//            loads into registers), the sign of the coordinate each source
+//            element will land on is applied with one XOR per 32-bit word,
+//            and the row is written to LDS in its natural order;
+//   gather   each thread reads its 32 permuted inputs from LDS;
+//   pass 0   stages on bits 0..4 of the block index, in registers;
+//   pass p   one LDS exchange, then up to four more stages in registers; the
+//            register set of every pass after the first also carries index
+//            bit 0, so the final values of each nibble pair sit in one thread;
+//   stat     per-token absmax (and for the codebook the exact integer-grid
+//            squared norm) by shuffles and one LDS atomic per lane group;
+//   codes    nibbles are packed from registers, regrouped through LDS inside
+//            the wave into 16 contiguous bytes per thread, and stored with
+//            one 16-byte store.
+// Two workgroup barriers per token (three for the codebook).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rq_internal.h"
+
+namespace rq {
+namespace {
+
+constexpr int kE = 32;   // coordinates per thread
+constexpr int kMaxTpw = 16;
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS
+// operations, not for its global loads and stores (a __syncthreads() would
+// also drain the next token's prefetch and the code stores in flight).
+__device__ inline void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int L>
+struct Plan {
+    static constexpr int NP = L <= 5 ? 1 : 1 + (L - 5 + 3) / 4;
+    __host__ __device__ static constexpr int lo(int p) { return p == 0 ? 0 : 5 + 4 * (p - 1); }
+    __host__ __device__ static constexpr int hi(int p) {
+        return p == 0 ? (L < 5 ? L : 5) : (5 + 4 * p < L ? 5 + 4 * p : L);
+    }
+    // index bit carried by register bit k in pass p
+    __host__ __device__ static constexpr int vbit(int p, int k) {
+        return p == 0 ? k : (k < 5 - (hi(p) - lo(p)) ? k : lo(p) + k - (5 - (hi(p) - lo(p))));
+    }
+    __host__ __device__ static constexpr int roff(int p, int r) {
+        int o = 0;
+        for (int k = 0; k < 5; ++k)
+            if ((r >> k) & 1) o |= 1 << vbit(p, k);
+        return o;
+    }
+    __host__ __device__ static constexpr bool isv(int p, int pos) {
+        for (int k = 0; k < 5; ++k)
+            if (vbit(p, k) == pos) return true;
+        return false;
+    }
+    __host__ __device__ static constexpr int rbit(int p, int s) {
+        for (int k = 0; k < 5; ++k)
+            if (vbit(p, k) == s) return k;
+        return -1;
+    }
+};
+
+// First coordinate of thread tt's set in pass P (the set is base + roff(P, r)).
+template <int L, int P>
+__device__ inline int pbase(int tt) {
+    if constexpr (P == 0) {
+        return kE * tt;
+    } else {
+        const int c = tt >> (L - 5);
+        int f = tt & ((1 << (L - 5)) - 1);
+        int i = 0;
+#pragma unroll
+        for (int pos = 0; pos < L; ++pos) {
+            if (Plan<L>::isv(P, pos)) continue;
+            i |= (f & 1) << pos;
+            f >>= 1;
+        }
+        return (c << L) + i;
+    }
+}
+
+template <int L, int P>
+__device__ inline void stages(float (&v)[kE]) {
+#pragma unroll
+    for (int s = Plan<L>::lo(P); s < Plan<L>::hi(P); ++s) {
+        const int kb = Plan<L>::rbit(P, s);
+#pragma unroll
+        for (int r = 0; r < kE; ++r) {
+            if (r & (1 << kb)) continue;
+            const float lo = v[r], hi = v[r | (1 << kb)];
+            v[r] = lo + hi;
+            v[r | (1 << kb)] = lo - hi;
+        }
+    }
+}
+
+// LDS slot of coordinate j in the exchange buffer: j with its low five bits
+// XORed with a rotation of the bits above them, so that both the pass-0
+// layout (lanes differ in bits 5..9) and the pass-1 layout (lanes differ in
+// bits nx..4 and in the block bits L..L+nx-1) hit 32 distinct banks.
+template <int L>
+__device__ inline int xslot(int j) {
+    constexpr int nx = L <= 9 ? 10 - L : 0;
+    constexpr int hb = L - 5 < 5 ? L - 5 : 5;
+    const int g = ((j >> L) & ((1 << nx) - 1)) | (((j >> 5) & ((1 << hb) - 1)) << nx);
+    return j ^ (g & 31);
+}
+
+template <int L, int P>
+__device__ inline void put(float *us, int tt, const float (&v)[kE]) {
+    const int b = pbase<L, P>(tt);
+#pragma unroll
+    for (int r = 0; r < kE; ++r) us[xslot<L>(b + Plan<L>::roff(P, r))] = v[r];
+}
+template <int L, int P>
+__device__ inline void get(const float *us, int tt, float (&v)[kE]) {
+    const int b = pbase<L, P>(tt);
+#pragma unroll
+    for (int r = 0; r < kE; ++r) v[r] = us[xslot<L>(b + Plan<L>::roff(P, r))];
+}
+
+// 16-byte chunk slot of code chunk ch (chunk = 32 coordinates): the low three
+// bits XORed with the RPBH block index bits, so the byte writes of one
+// instruction (lanes of several blocks) spread over the banks.  Bijective on
+// every aligned group of eight chunks (the XORed bits sit above the output
+// bits); the code buffer is padded to a multiple of eight chunks.
+template <int L>
+__device__ inline int cslot(int ch) {
+    constexpr int s = L - 5 > 0 ? L - 5 : 1;
+    return ch ^ ((ch >> s) & 7);
+}
+
+struct RpbhArgs {
+    const void *X;
+    int64_t T;
+    int K;
+    int tpt;              // threads per token (K / 32)
+    int tpw;              // tokens per workgroup
+    const int8_t *sign;
+    const int32_t *perm;
+    uint8_t *codes;
+    float *scale;
+    float th[15];         // codebook thresholds (Lloyd-Max)
+};
+
+template <bool BF16>
+struct Src {
+    // 32-bit words of input a thread stages per token, in 16-byte chunks
+    static constexpr int WORDS = BF16 ? 16 : 32;
+    static constexpr int CHUNKS = WORDS / 4;
+    static constexpr int ELEMS_PER_CHUNK = BF16 ? 8 : 4;
+    static constexpr int XB = BF16 ? 2 : 4;
+};
+
+__device__ inline uint32_t bf16_sign_mask(bool neg, int half) {
+    return neg ? (half ? 0x80000000u : 0x00008000u) : 0u;
+}
+
+template <int L, bool BF16, int QK>
+__global__ void __launch_bounds__(512)
+rpbh_quant_kernel(RpbhArgs a) {
+    using S = Src<BF16>;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    __shared__ unsigned red_max[2][kMaxTpw];
+    __shared__ unsigned long long red_sum[2][kMaxTpw];
+    const int K = a.K;
+    const int tid = threadIdx.x;
+    const int tl = tid / a.tpt;
+    const int tt = tid - tl * a.tpt;
+    uint8_t *xs = smem + (size_t)tl * K * S::XB;
+    float *us = reinterpret_cast<float *>(smem + (size_t)a.tpw * K * S::XB) + (size_t)tl * K;
+    const int cs_bytes = ((K / 2 + 127) / 128) * 128;
+    uint8_t *cs = smem + (size_t)a.tpw * K * (S::XB + 4) + (size_t)tl * cs_bytes;
+
+    // ---- prologue: gather offsets, source-side sign masks -----------------
+    int gofs[kE];
+#pragma unroll
+    for (int r = 0; r < kE; ++r) gofs[r] = a.perm[kE * tt + r] * S::XB;
+    {
+        int *inv = reinterpret_cast<int *>(us);
+#pragma unroll
+        for (int r = 0; r < kE; ++r) inv[a.perm[kE * tt + r]] = kE * tt + r;
+    }
+    __syncthreads();
+    uint32_t smask[S::WORDS];
+    {
+        const int *inv = reinterpret_cast<const int *>(us);
+#pragma unroll
+        for (int q = 0; q < S::CHUNKS; ++q) {
+            const int e0 = S::ELEMS_PER_CHUNK * (tt + q * a.tpt);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                if constexpr (BF16) {
+                    const int e = e0 + 2 * w;
+                    smask[4 * q + w] = bf16_sign_mask(a.sign[inv[e]] < 0, 0) |
+                                       bf16_sign_mask(a.sign[inv[e + 1]] < 0, 1);
+                } else {
+                    smask[4 * q + w] = a.sign[inv[e0 + w]] < 0 ? 0x80000000u : 0u;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    const int64_t stride = (int64_t)gridDim.x * a.tpw;
+    int64_t base = (int64_t)blockIdx.x * a.tpw;
+    uint4 pre[S::CHUNKS];
+    auto fetch = [&](int64_t b) {
+        int64_t tok = b + tl;
+        if (tok >= a.T) tok = a.T - 1;
+        const uint8_t *row = static_cast<const uint8_t *>(a.X) + tok * (int64_t)K * S::XB;
+#pragma unroll
+        for (int q = 0; q < S::CHUNKS; ++q)
+            pre[q] = *reinterpret_cast<const uint4 *>(row + (size_t)16 * (tt + q * a.tpt));
+    };
+    auto stage = [&]() {
+#pragma unroll
+        for (int q = 0; q < S::CHUNKS; ++q) {
+            uint4 w = pre[q];
+            w.x ^= smask[4 * q];
+            w.y ^= smask[4 * q + 1];
+            w.z ^= smask[4 * q + 2];
+            w.w ^= smask[4 * q + 3];
+            *reinterpret_cast<uint4 *>(xs + (size_t)16 * (tt + q * a.tpt)) = w;
+        }
+    };
+    if (base < a.T) {
+        fetch(base);
+        stage();
+        if (base + stride < a.T) fetch(base + stride);
+    }
+    __syncthreads();
+
+    // lane groups of one token for the shuffle reductions
+    int grp = 64;
+    while (a.tpt % grp) grp >>= 1;
+
+    int it = 0;
+    for (; base < a.T; base += stride, ++it) {
+        const int64_t tok = base + tl;
+        const bool valid = tok < a.T;
+        if (tt == 0) {
+            red_max[it & 1][tl] = 0u;
+            if constexpr (QK == 1) red_sum[it & 1][tl] = 0ull;
+        }
+        float v[kE];
+#pragma unroll
+        for (int r = 0; r < kE; ++r) {
+            if constexpr (BF16)
+                v[r] = __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t *>(xs + gofs[r])) << 16);
+            else
+                v[r] = *reinterpret_cast<const float *>(xs + gofs[r]);
+        }
+        stages<L, 0>(v);
+        if constexpr (Plan<L>::NP > 1) put<L, 0>(us, tt, v);
+        lds_barrier();  // B1: every gather of this token is done
+        const bool more = base + stride < a.T;
+        if (more) {
+            stage();                                        // next token -> LDS
+            if (base + 2 * stride < a.T) fetch(base + 2 * stride);
+        }
+        if constexpr (Plan<L>::NP > 1) {
+            get<L, 1>(us, tt, v);
+            stages<L, 1>(v);
+        }
+        if constexpr (Plan<L>::NP > 2) {
+            put<L, 1>(us, tt, v);
+            lds_barrier();
+            get<L, 2>(us, tt, v);
+            stages<L, 2>(v);
+        }
+        static_assert(Plan<L>::NP <= 3, "block too large");
+        constexpr int PL = Plan<L>::NP - 1;
+
+        float m = 0.0f;
+#pragma unroll
+        for (int r = 0; r < kE; ++r) m = fmaxf(m, fabsf(v[r]));
+        for (int off = 1; off < grp; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+        if ((tid & (grp - 1)) == 0) atomicMax(&red_max[it & 1][tl], __float_as_uint(m));
+        lds_barrier();  // B2: statistic complete, next token staged
+        const float amax = __uint_as_float(red_max[it & 1][tl]);
+
+        uint32_t nib[kE];
+        float sc = 0.0f;
+        if constexpr (QK == 0) {
+            // q = rne(fl32(u * inv)) lands in [-7, 7]: |u * inv| <= fl32(7 (1 + 2^-24)) = 7,
+            // so no clamp is needed.  Adding 1.5 * 2^23 rounds to an integer
+            // (nearest-even) and leaves q in the low bits, two's complement.
+            const float inv = amax > 0.0f ? 7.0f / amax : 0.0f;
+#pragma unroll
+            for (int r = 0; r < kE; ++r) {
+                const float mq = v[r] * inv;
+                nib[r] = __float_as_uint(mq + 12582912.0f) & 0xFu;
+            }
+            sc = amax > 0.0f ? amax / 7.0f : 0.0f;
+        } else {
+            // exact squared norm on the grid 2^(2E - 36), E = ilogb(max |u|)
+            const int E = amax > 0.0f ? ilogbf(amax) : 0;
+            unsigned long long s = 0;
+            if (amax > 0.0f) {
+#pragma unroll
+                for (int r = 0; r < kE; ++r) {
+                    const double sq = (double)v[r] * (double)v[r];
+                    s += (unsigned long long)rint(ldexp(sq, 36 - 2 * E));
+                }
+            }
+            for (int off = 1; off < grp; off <<= 1) s += __shfl_xor(s, off, 64);
+            if ((tid & (grp - 1)) == 0 && s) atomicAdd(&red_sum[it & 1][tl], s);
+            lds_barrier();  // B3
+            const unsigned long long S = red_sum[it & 1][tl];
+            if (amax > 0.0f) {
+                const double d = ldexp((double)S, 2 * E - 36);
+                const float g = (float)sqrt((double)K / d);
+                sc = (float)sqrt(d / (double)K);
+#pragma unroll
+                for (int r = 0; r < kE; ++r) {
+                    const float x = v[r] * g;
+                    uint32_t idx = 0;
+#pragma unroll
+                    for (int i = 0; i < 15; ++i) idx += (x > a.th[i]) ? 1u : 0u;
+                    nib[r] = idx;
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < kE; ++r) nib[r] = 0u;
+            }
+        }
+
+        // pack: register bit 0 carries index bit 0, so registers (2m, 2m + 1)
+        // hold a nibble pair
+        uint8_t *crow = a.codes + tok * (int64_t)(K / 2);
+        if constexpr (Plan<L>::NP == 1) {
+            uint32_t w[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t x = 0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x |= nib[8 * q + e] << (4 * e);
+                w[q] = x;
+            }
+            if (valid) *reinterpret_cast<uint4 *>(crow + 16 * tt) = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+            const int b = pbase<L, PL>(tt);
+#pragma unroll
+            for (int mm = 0; mm < kE / 2; ++mm) {
+                const int q = (b + Plan<L>::roff(PL, 2 * mm)) >> 1;
+                cs[(cslot<L>(q >> 4) << 4) | (q & 15)] = (uint8_t)(nib[2 * mm] | (nib[2 * mm + 1] << 4));
+            }
+            // the 16 bytes this thread stores were written by lanes of its own
+            // wave (its RPBH block): order the LDS writes before the read
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const uint4 w = *reinterpret_cast<const uint4 *>(cs + 16 * cslot<L>(tt));
+            if (valid) *reinterpret_cast<uint4 *>(crow + 16 * tt) = w;
+        }
+        if (valid && tt == 0) a.scale[tok] = sc;
+    }
+}
+
+int g_num_cus = 0;
+
+int num_cus() {
+    if (g_num_cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            g_num_cus = n;
+        else
+            g_num_cus = 256;
+    }
+    return g_num_cus;
+}
+
+template <int L, bool BF16, int QK>
+hipError_t launch_L(RpbhArgs a, hipStream_t s) {
+    const int xb = BF16 ? 2 : 4;
+    const size_t per_tok = (size_t)a.K * (xb + 4) + ((a.K / 2 + 127) / 128) * 128;
+    // tokens per workgroup: <= 512 threads, <= 78 KB of LDS (two workgroups
+    // per CU), then the candidate whose last round of tokens is fullest
+    const int cus = num_cus();
+    int best_tpw = 1;
+    double best_eff = -1.0;
+    for (int tpw = 1; tpw <= kMaxTpw; tpw *= 2) {
+        if (tpw * a.tpt > 512 || tpw * per_tok > 78 * 1024) break;
+        const int64_t units = (a.T + tpw - 1) / tpw;
+        const int64_t slots = (int64_t)cus * 2;
+        const int64_t rounds = (units + slots - 1) / slots;
+        const double eff = (double)units / (double)(rounds * slots) + 0.02 * tpw;  // prefer fuller WGs
+        if (eff > best_eff) {
+            best_eff = eff;
+            best_tpw = tpw;
+        }
+    }
+    a.tpw = best_tpw;
+    const size_t lds = per_tok * best_tpw;
+    const int64_t units = (a.T + best_tpw - 1) / best_tpw;
+    const int grid = (int)(units < (int64_t)cus * 2 ? units : (int64_t)cus * 2);
+    auto kern = rpbh_quant_kernel<L, BF16, QK>;
+    // raise the dynamic-LDS limit once per instantiation (the call is not free)
+    static size_t lds_set = 0;
+    if (lds > 64 * 1024 && lds > lds_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        lds_set = lds;
+    }
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(a.tpw * a.tpt), lds, s, a);
+    return hipGetLastError();
+}
+
+template <bool BF16, int QK>
+hipError_t dispatch(int L, RpbhArgs a, hipStream_t s) {
+    switch (L) {
+        case 1: return launch_L<1, BF16, QK>(a, s);
+        case 2: return launch_L<2, BF16, QK>(a, s);
+        case 3: return launch_L<3, BF16, QK>(a, s);
+        case 4: return launch_L<4, BF16, QK>(a, s);
+        case 5: return launch_L<5, BF16, QK>(a, s);
+        case 6: return launch_L<6, BF16, QK>(a, s);
+        case 7: return launch_L<7, BF16, QK>(a, s);
+        case 8: return launch_L<8, BF16, QK>(a, s);
+        case 9: return launch_L<9, BF16, QK>(a, s);
+        case 10: return launch_L<10, BF16, QK>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+RpbhArgs make_args(const void *X, int64_t T, int K, const int8_t *sign, const int32_t *perm,
+                   uint8_t *codes, float *scale) {
+    RpbhArgs a;
+    a.X = X;
+    a.T = T;
+    a.K = K;
+    a.tpt = K / kE;
+    a.tpw = 1;
+    a.sign = sign;
+    a.perm = perm;
+    a.codes = codes;
+    a.scale = scale;
+    for (int i = 0; i < 15; ++i) a.th[i] = 0.0f;
+    return a;
+}
+
+}  // namespace
+
+int launch_rpbh_int4(const void *X, int x_bf16, int64_t T, int K, int block, const int8_t *sign,
+                     const int32_t *perm, uint8_t *codes, float *scale, void *stream) {
+    RpbhArgs a = make_args(X, T, K, sign, perm, codes, scale);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int L = ilog2(block);
+    return (int)(x_bf16 ? dispatch<true, 0>(L, a, s) : dispatch<false, 0>(L, a, s));
+}
+
+int launch_rpbh_lloydmax(const void *X, int x_bf16, int64_t T, int K, int block,
+                         const int8_t *sign, const int32_t *perm, const float *thresholds,
+                         int n_thresholds, uint8_t *codes, float *sigma, void *stream) {
+    if (n_thresholds != 15) return (int)hipErrorInvalidValue;
+    RpbhArgs a = make_args(X, T, K, sign, perm, codes, sigma);
+    for (int i = 0; i < 15; ++i) a.th[i] = thresholds[i];
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int L = ilog2(block);
+    return (int)(x_bf16 ? dispatch<true, 1>(L, a, s) : dispatch<false, 1>(L, a, s));
+}
+
+}  // namespace rq
