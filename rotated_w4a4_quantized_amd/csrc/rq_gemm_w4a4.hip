@@ -31,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "rq_internal.h"
 
 namespace rq {
@@ -42,7 +44,6 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kStageBytes = 64;  // bytes of packed codes per row per stage (128 k)
-constexpr int kRowStride = 80;   // padded LDS row stride
 
 struct W4A4Args {
     const uint8_t *A;      // activation codes [T][lda]
@@ -64,6 +65,12 @@ struct W4A4Args {
     float post_lr;         // 1 / 256
 };
 
+// Workgroup barrier ordering LDS only: waits for this wave's LDS traffic,
+// not for global loads in flight (the next stages' prefetch).
+__device__ inline void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ inline v4i widen(uint32_t w0, uint32_t w1) {
     const uint32_t M = 0xF0F0F0F0u;
     v4i r;
@@ -79,19 +86,30 @@ __device__ inline uint32_t bf16_rne_bits(float x) {
     return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;   // finite x
 }
 
-template <int BT_, int BN_, int WT_, int WN_>
+template <int BT_, int BN_, int WT_, int WN_, int NBUF_>
 struct Cfg {
     static constexpr int BT = BT_, BN = BN_, WT = WT_, WN = WN_;
+    static constexpr int NBUF = NBUF_;        // LDS stage buffers (prefetch distance NBUF - 1)
     static constexpr int NW = WT * WN;
     static constexpr int NTH = 64 * NW;
     static constexpr int FT = BT / WT / 32;   // token fragments per wave
     static constexpr int FN = BN / WN / 32;   // channel fragments per wave
-    static constexpr int ROWS = BT + BN;
-    static constexpr int CHUNKS = ROWS * (kStageBytes / 16);
-    static constexpr int CPT = (CHUNKS + NTH - 1) / NTH;
-    static constexpr int LDS_STAGE = ROWS * kRowStride;
+    static constexpr int ROWS = BT + BN;      // token rows, then weight rows
+    static constexpr int LDS_STAGE = ROWS * kStageBytes;
+    static constexpr int NQ = ROWS / 16;      // 1 KB direct-to-LDS loads per stage
+    static constexpr int IPW = NQ / NW;       // ... issued by each wave
     static_assert(BT % (32 * WT) == 0 && BN % (32 * WN) == 0, "tile shape");
+    static_assert(IPW * NW == NQ, "load split");
 };
+
+// LDS rows hold 64 bytes of packed nibbles; 16-byte chunk c of row r sits at
+// c ^ ((r >> 1) & 3), which keeps the 16-byte accesses of eight consecutive
+// lanes on distinct bank groups.
+__device__ inline int row_slot(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4); }
+
+// Source of K-tail chunks: sixteen zero bytes in global memory, so that the
+// direct-to-LDS loads need no branch.
+__device__ __attribute__((aligned(16))) uint8_t g_zero16[16];
 
 // Tile id for workgroup `bid`: contiguous id ranges per XCD, then grouped
 // ordering (GM token tiles x all channel tiles per group).
@@ -109,10 +127,10 @@ __device__ inline void tile_of(int bid, int nblk, int tiles_t, int tiles_n, int 
     tn = in / gsize;
 }
 
-template <class C, bool HAS_LR>
+template <class C, bool HAS_LR, bool TAIL>
 __global__ void __launch_bounds__(C::NTH, 2)
 gemm_w4a4_kernel(W4A4Args a) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::LDS_STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[C::NBUF * C::LDS_STAGE];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wt = wave / C::WN, wn = wave % C::WN;
@@ -122,43 +140,45 @@ gemm_w4a4_kernel(W4A4Args a) {
     const int64_t t0 = (int64_t)tile_t * C::BT;
     const int n0 = tile_n * C::BN;
 
-    // global source of every 16-byte chunk this thread stages
-    const uint8_t *src[C::CPT];
-    int dst[C::CPT];
-    bool live[C::CPT];
+    // Loads: every stage is NQ direct-to-LDS instructions of 1 KB (16 rows x
+    // 64 bytes); lane l of instruction q fills physical chunk l & 3 of row
+    // 16 q + l / 4, i.e. logical chunk (l & 3) ^ ((row >> 1) & 3).
+    const uint8_t *gsrc[C::IPW];
+    int col[C::IPW];
 #pragma unroll
-    for (int h = 0; h < C::CPT; ++h) {
-        const int c = tid + C::NTH * h;
-        live[h] = c < C::CHUNKS;
-        const int row = c >> 2, col = (c & 3) * 16;
-        dst[h] = row * kRowStride + col;
+    for (int i = 0; i < C::IPW; ++i) {
+        const int q = wave * C::IPW + i;
+        const int row = 16 * q + (lane >> 2);
+        const int ch = (lane & 3) ^ ((row >> 1) & 3);
+        col[i] = 16 * ch;
         if (row < C::BT) {
             int64_t t = t0 + row;
             if (t >= a.T) t = a.T - 1;
-            src[h] = a.A + t * a.lda + col;
+            gsrc[i] = a.A + t * a.lda + col[i];
         } else {
             int n = n0 + row - C::BT;
             if (n >= a.N) n = a.N - 1;
-            src[h] = a.B + (int64_t)n * a.ldb + a.koff + col;
+            gsrc[i] = a.B + (int64_t)n * a.ldb + a.koff + col[i];
         }
     }
     const int nstage = (a.lda + kStageBytes - 1) / kStageBytes;
-    uint4 pre[C::CPT];
-    auto fetch = [&](int s) {
+    auto issue = [&](int s, int buf) {
         const int kb = s * kStageBytes;
 #pragma unroll
-        for (int h = 0; h < C::CPT; ++h) {
-            const int col = (dst[h] % kRowStride);
-            if (live[h] && kb + col < a.lda)
-                pre[h] = *reinterpret_cast<const uint4 *>(src[h] + kb);
-            else
-                pre[h] = make_uint4(0u, 0u, 0u, 0u);
+        for (int i = 0; i < C::IPW; ++i) {
+            const uint8_t *p = gsrc[i] + kb;
+            if (TAIL && kb + col[i] >= a.lda) p = g_zero16;
+            __builtin_amdgcn_global_load_lds(
+                (const void *)p,
+                (__attribute__((address_space(3))) void *)(lds + buf * C::LDS_STAGE +
+                                                          (wave * C::IPW + i) * 1024),
+                16, 0, 0);
         }
     };
-    auto stash = [&](int buf) {
-#pragma unroll
-        for (int h = 0; h < C::CPT; ++h)
-            if (live[h]) *reinterpret_cast<uint4 *>(lds + buf * C::LDS_STAGE + dst[h]) = pre[h];
+    // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding)
+    auto wait_vm = [](auto nc) {
+        constexpr int n = decltype(nc)::value;
+        __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
     };
 
     v16i acc[C::FN][C::FT];
@@ -169,34 +189,56 @@ gemm_w4a4_kernel(W4A4Args a) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
-    fetch(0);
-    stash(0);
-    __syncthreads();
-    // LDS row offsets of this lane's fragments (token rows first, then channels)
-    const int rowT = (wt * C::FT * 32 + li) * kRowStride + 32 * lg;
-    const int rowN = (C::BT + wn * C::FN * 32 + li) * kRowStride + 32 * lg;
+    // NBUF LDS buffers: stage s is multiplied while stages s + 1 .. s + D
+    // (D = NBUF - 1) are in flight; before the barrier that ends step s only
+    // stage s + 1 must have landed, i.e. at most (pending - 1) stages of IPW
+    // loads each may remain outstanding
+    constexpr int D = C::NBUF - 1;
+    auto wait_pending = [&](int pending) {
+        // pending: stages in flight after stage s + 1 (0 .. D - 1)
+        if constexpr (D >= 4) if (pending >= 3) { wait_vm(std::integral_constant<int, 3 * C::IPW>()); return; }
+        if constexpr (D >= 3) if (pending == 2) { wait_vm(std::integral_constant<int, 2 * C::IPW>()); return; }
+        if constexpr (D >= 2) if (pending == 1) { wait_vm(std::integral_constant<int, C::IPW>()); return; }
+        wait_vm(std::integral_constant<int, 0>());
+    };
+    for (int p = 0; p < D && p < nstage; ++p) issue(p, p);
+    wait_pending((nstage < D ? nstage : D) - 1);
+    lds_barrier();
+    const int rT0 = wt * C::FT * 32 + li;
+    const int rN0 = C::BT + wn * C::FN * 32 + li;
+    int toff[2], noff[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        toff[h] = row_slot(rT0, 2 * lg + h);
+        noff[h] = row_slot(rN0, 2 * lg + h);
+    }
+    int buf = 0;
     for (int s = 0; s < nstage; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < nstage) fetch(s + 1);
+        if (s + D < nstage) issue(s + D, buf == 0 ? D : buf - 1);
         const uint8_t *L = lds + buf * C::LDS_STAGE;
+        // fragments of both half-stages are read up front so the second
+        // half's LDS latency hides under the first half's MFMAs
+        uint4 fn_[2][C::FN], ft_[2][C::FT];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-            uint4 fn_[C::FN], ft_[C::FT];
 #pragma unroll
             for (int i = 0; i < C::FN; ++i)
-                fn_[i] = *reinterpret_cast<const uint4 *>(L + rowN + i * 32 * kRowStride + 16 * half);
+                fn_[half][i] = *reinterpret_cast<const uint4 *>(L + noff[half] + i * 32 * 64);
 #pragma unroll
             for (int j = 0; j < C::FT; ++j)
-                ft_[j] = *reinterpret_cast<const uint4 *>(L + rowT + j * 32 * kRowStride + 16 * half);
+                ft_[half][j] = *reinterpret_cast<const uint4 *>(L + toff[half] + j * 32 * 64);
+        }
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
+        for (int half = 0; half < 2; ++half) {
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
                 v4i xn[C::FN], xt[C::FT];
 #pragma unroll
                 for (int i = 0; i < C::FN; ++i)
-                    xn[i] = ks ? widen(fn_[i].z, fn_[i].w) : widen(fn_[i].x, fn_[i].y);
+                    xn[i] = k ? widen(fn_[half][i].z, fn_[half][i].w) : widen(fn_[half][i].x, fn_[half][i].y);
 #pragma unroll
                 for (int j = 0; j < C::FT; ++j)
-                    xt[j] = ks ? widen(ft_[j].z, ft_[j].w) : widen(ft_[j].x, ft_[j].y);
+                    xt[j] = k ? widen(ft_[half][j].z, ft_[half][j].w) : widen(ft_[half][j].x, ft_[half][j].y);
 #pragma unroll
                 for (int i = 0; i < C::FN; ++i)
 #pragma unroll
@@ -204,8 +246,13 @@ gemm_w4a4_kernel(W4A4Args a) {
                         acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xn[i], xt[j], acc[i][j], 0, 0, 0);
             }
         }
-        if (s + 1 < nstage) stash(buf ^ 1);
-        __syncthreads();
+        // stage s + 1 has landed; stages s + 2 .. may still be in flight
+        {
+            const int last = (s + D < nstage ? s + D : nstage - 1);   // newest stage issued
+            wait_pending(last - (s + 1) > 0 ? last - (s + 1) : 0);
+        }
+        lds_barrier();
+        buf = buf == D ? 0 : buf + 1;
     }
 
     // low-rank term (DENSE weights): lr[n][t] = sum_{j < r} qw[n][j] * bf16(top[t][j])
@@ -247,7 +294,48 @@ gemm_w4a4_kernel(W4A4Args a) {
         }
     }
 
-    // epilogue: lane owns token t = ... + li and channels n = ... + 8 q + 4 lg + (0..3)
+    // Epilogue for a full tile with bf16 output: the scaled tile is staged
+    // in LDS (free after the last barrier) and written back as 256-byte row
+    // segments -- the accumulator layout alone would give every store
+    // instruction 32 separate 16-byte pieces in 32 different rows.
+    constexpr int kOutStride = C::BN * 2 + 16;   // bytes per staged output row
+    if constexpr (!HAS_LR && C::BT * kOutStride <= C::NBUF * C::LDS_STAGE) {
+        if (a.ydt == RQ_BF16 && t0 + C::BT <= a.T && n0 + C::BN <= a.N && (a.N % 8) == 0 &&
+            a.bias == nullptr) {
+#pragma unroll
+            for (int j = 0; j < C::FT; ++j) {
+                const int tl = wt * C::FT * 32 + j * 32 + li;
+                const float sat = a.sa[t0 + tl] * a.post;
+#pragma unroll
+                for (int i = 0; i < C::FN; ++i) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int nl = wn * C::FN * 32 + i * 32 + 8 * q + 4 * lg;
+                        const float4 sw4 = *reinterpret_cast<const float4 *>(a.sw + n0 + nl);
+                        const float y0 = (float)acc[i][j][4 * q + 0] * (sat * sw4.x);
+                        const float y1 = (float)acc[i][j][4 * q + 1] * (sat * sw4.y);
+                        const float y2 = (float)acc[i][j][4 * q + 2] * (sat * sw4.z);
+                        const float y3 = (float)acc[i][j][4 * q + 3] * (sat * sw4.w);
+                        *reinterpret_cast<uint2 *>(lds + tl * kOutStride + 2 * nl) =
+                            make_uint2(bf16_rne_bits(y0) | (bf16_rne_bits(y1) << 16),
+                                       bf16_rne_bits(y2) | (bf16_rne_bits(y3) << 16));
+                    }
+                }
+            }
+            lds_barrier();
+            constexpr int kChunksPerRow = C::BN * 2 / 16;
+            constexpr int kChunks = C::BT * kChunksPerRow;
+#pragma unroll 4
+            for (int c = tid; c < kChunks; c += C::NTH) {
+                const int row = c / kChunksPerRow, cc = c % kChunksPerRow;
+                const uint4 v = *reinterpret_cast<const uint4 *>(lds + row * kOutStride + 16 * cc);
+                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.Y) + (t0 + row) * a.N + n0 + 8 * cc) = v;
+            }
+            return;
+        }
+    }
+
+    // general epilogue: lane owns token t = ... + li and channels n = ... + 8 q + 4 lg + (0..3)
     const bool vec_ok = (a.N % 4) == 0;
 #pragma unroll
     for (int j = 0; j < C::FT; ++j) {
@@ -308,12 +396,18 @@ hipError_t launch_cfg(W4A4Args a, hipStream_t s) {
     a.tiles_t = (int)((a.T + C::BT - 1) / C::BT);
     a.tiles_n = (a.N + C::BN - 1) / C::BN;
     const int nblk = a.tiles_t * a.tiles_n;
-    hipLaunchKernelGGL((gemm_w4a4_kernel<C, HAS_LR>), dim3(nblk), dim3(C::NTH), 0, s, a);
+    if (a.lda % kStageBytes)
+        hipLaunchKernelGGL((gemm_w4a4_kernel<C, HAS_LR, true>), dim3(nblk), dim3(C::NTH), 0, s, a);
+    else
+        hipLaunchKernelGGL((gemm_w4a4_kernel<C, HAS_LR, false>), dim3(nblk), dim3(C::NTH), 0, s, a);
     return hipGetLastError();
 }
 
-using CfgBig = Cfg<256, 128, 4, 1>;    // 256 tokens x 128 channels, waves 4 x 1 (64 x 128 each)
-using CfgMid = Cfg<128, 128, 2, 2>;    // 128 x 128, waves 2 x 2 (64 x 64 each)
+// Two workgroups per CU (2 waves per SIMD): one workgroup's barrier waits and
+// epilogue overlap the other's MFMAs.  (A 256 x 256 tile with one 8-wave
+// workgroup per CU stages fewer bytes per MFMA but measured slower.)
+using CfgBig = Cfg<256, 128, 4, 1, 3>;    // 4 waves of 64 x 128, two workgroups per CU
+using CfgMid = Cfg<128, 128, 2, 2, 3>;    // 4 waves of 64 x 64
 
 }  // namespace
 
@@ -341,13 +435,7 @@ int launch_gemm_w4a4(const uint8_t *codes, const float *scale, const uint16_t *t
     hipStream_t s = static_cast<hipStream_t>(stream);
     // the low-rank term needs registers for its own accumulators: mid tile
     if (a.r > 0) return (int)launch_cfg<CfgMid, true>(a, s);
-    // 512 workgroup slots (256 CUs x 2): pick the tile that leaves the
-    // smaller idle fraction in the last round of tiles
-    const int64_t big = ((T + 255) / 256) * ((hdr->N + 127) / 128);
-    const int64_t mid = ((T + 127) / 128) * ((hdr->N + 127) / 128);
-    const double eff_big = (double)big / (double)(((big + 511) / 512) * 512);
-    const double eff_mid = (double)mid / (double)(((mid + 511) / 512) * 512) * 0.92;
-    if (T >= 256 && eff_big >= eff_mid) return (int)launch_cfg<CfgBig, false>(a, s);
+    if (T >= 256) return (int)launch_cfg<CfgBig, false>(a, s);
     return (int)launch_cfg<CfgMid, false>(a, s);
 }
 

@@ -109,41 +109,39 @@ __device__ inline void stages(float (&v)[kE]) {
     }
 }
 
-// LDS slot of coordinate j in the exchange buffer: j with its low five bits
-// XORed with a rotation of the bits above them, so that both the pass-0
-// layout (lanes differ in bits 5..9) and the pass-1 layout (lanes differ in
-// bits nx..4 and in the block bits L..L+nx-1) hit 32 distinct banks.
+// Exchange buffer layout: coordinate j lives at j + (j >> 5) + (j >> L)
+// (one pad slot per 32 coordinates and one per block).  In every pass a
+// thread's coordinates are base | roff(r) with disjoint bit fields, so the
+// slot splits into a per-thread base plus a per-register constant (an
+// immediate offset of the LDS instruction), and the pads spread the lanes of
+// one instruction over the banks: pass 0 lanes differ in bits 5..9, pass-1
+// lanes in the fixed low bits and the block bits.
 template <int L>
-__device__ inline int xslot(int j) {
-    constexpr int nx = L <= 9 ? 10 - L : 0;
-    constexpr int hb = L - 5 < 5 ? L - 5 : 5;
-    const int g = ((j >> L) & ((1 << nx) - 1)) | (((j >> 5) & ((1 << hb) - 1)) << nx);
-    return j ^ (g & 31);
-}
+__device__ inline int xbase(int b) { return b + (b >> 5) + (b >> L); }
+__host__ __device__ constexpr int xoff(int o) { return o + (o >> 5); }
+template <int L>
+__host__ __device__ constexpr int xwords(int K) { return (K + K / 32 + K / (1 << L) + 1 + 3) & ~3; }
 
 template <int L, int P>
 __device__ inline void put(float *us, int tt, const float (&v)[kE]) {
-    const int b = pbase<L, P>(tt);
+    float *p = us + xbase<L>(pbase<L, P>(tt));
 #pragma unroll
-    for (int r = 0; r < kE; ++r) us[xslot<L>(b + Plan<L>::roff(P, r))] = v[r];
+    for (int r = 0; r < kE; ++r) p[xoff(Plan<L>::roff(P, r))] = v[r];
 }
 template <int L, int P>
 __device__ inline void get(const float *us, int tt, float (&v)[kE]) {
-    const int b = pbase<L, P>(tt);
+    const float *p = us + xbase<L>(pbase<L, P>(tt));
 #pragma unroll
-    for (int r = 0; r < kE; ++r) v[r] = us[xslot<L>(b + Plan<L>::roff(P, r))];
+    for (int r = 0; r < kE; ++r) v[r] = p[xoff(Plan<L>::roff(P, r))];
 }
 
-// 16-byte chunk slot of code chunk ch (chunk = 32 coordinates): the low three
-// bits XORed with the RPBH block index bits, so the byte writes of one
-// instruction (lanes of several blocks) spread over the banks.  Bijective on
-// every aligned group of eight chunks (the XORed bits sit above the output
-// bits); the code buffer is padded to a multiple of eight chunks.
+// Code staging layout: code byte q at q + 16 (q >> (L - 1)), i.e. 16 pad
+// bytes after every block (b / 2 bytes), which spreads the byte writes of one
+// instruction over the banks and keeps every 16-byte chunk aligned.
 template <int L>
-__device__ inline int cslot(int ch) {
-    constexpr int s = L - 5 > 0 ? L - 5 : 1;
-    return ch ^ ((ch >> s) & 7);
-}
+__host__ __device__ constexpr int cpad(int q) { return q + 16 * (q >> (L - 1)); }
+template <int L>
+__host__ __device__ constexpr int cbytes(int K) { return L <= 5 ? 0 : K / 2 + 16 * (K >> L) + 16; }
 
 struct RpbhArgs {
     const void *X;
@@ -183,9 +181,10 @@ rpbh_quant_kernel(RpbhArgs a) {
     const int tl = tid / a.tpt;
     const int tt = tid - tl * a.tpt;
     uint8_t *xs = smem + (size_t)tl * K * S::XB;
-    float *us = reinterpret_cast<float *>(smem + (size_t)a.tpw * K * S::XB) + (size_t)tl * K;
-    const int cs_bytes = ((K / 2 + 127) / 128) * 128;
-    uint8_t *cs = smem + (size_t)a.tpw * K * (S::XB + 4) + (size_t)tl * cs_bytes;
+    const int xw = xwords<L>(K);
+    const int cb = (cbytes<L>(K) + 15) & ~15;
+    float *us = reinterpret_cast<float *>(smem + (size_t)a.tpw * K * S::XB) + (size_t)tl * xw;
+    uint8_t *cs = smem + (size_t)a.tpw * (K * S::XB + 4 * xw) + (size_t)tl * cb;
 
     // ---- prologue: gather offsets, source-side sign masks -----------------
     int gofs[kE];
@@ -305,7 +304,7 @@ rpbh_quant_kernel(RpbhArgs a) {
 #pragma unroll
             for (int r = 0; r < kE; ++r) {
                 const float mq = v[r] * inv;
-                nib[r] = __float_as_uint(mq + 12582912.0f) & 0xFu;
+                nib[r] = __float_as_uint(mq + 12582912.0f);   // code in bits 0..3
             }
             sc = amax > 0.0f ? amax / 7.0f : 0.0f;
         } else {
@@ -350,23 +349,21 @@ rpbh_quant_kernel(RpbhArgs a) {
             for (int q = 0; q < 4; ++q) {
                 uint32_t x = 0;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x |= nib[8 * q + e] << (4 * e);
+                for (int e = 0; e < 8; ++e) x |= (nib[8 * q + e] & 0xFu) << (4 * e);
                 w[q] = x;
             }
             if (valid) *reinterpret_cast<uint4 *>(crow + 16 * tt) = make_uint4(w[0], w[1], w[2], w[3]);
         } else {
-            const int b = pbase<L, PL>(tt);
+            uint8_t *p = cs + cpad<L>(pbase<L, PL>(tt) >> 1);
 #pragma unroll
-            for (int mm = 0; mm < kE / 2; ++mm) {
-                const int q = (b + Plan<L>::roff(PL, 2 * mm)) >> 1;
-                cs[(cslot<L>(q >> 4) << 4) | (q & 15)] = (uint8_t)(nib[2 * mm] | (nib[2 * mm + 1] << 4));
-            }
+            for (int mm = 0; mm < kE / 2; ++mm)
+                p[Plan<L>::roff(PL, 2 * mm) >> 1] = (uint8_t)((nib[2 * mm] & 0xFu) | (nib[2 * mm + 1] << 4));
             // the 16 bytes this thread stores were written by lanes of its own
             // wave (its RPBH block): order the LDS writes before the read
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            const uint4 w = *reinterpret_cast<const uint4 *>(cs + 16 * cslot<L>(tt));
+            const uint4 w = *reinterpret_cast<const uint4 *>(cs + cpad<L>(16 * tt));
             if (valid) *reinterpret_cast<uint4 *>(crow + 16 * tt) = w;
         }
         if (valid && tt == 0) a.scale[tok] = sc;
@@ -390,7 +387,8 @@ int num_cus() {
 template <int L, bool BF16, int QK>
 hipError_t launch_L(RpbhArgs a, hipStream_t s) {
     const int xb = BF16 ? 2 : 4;
-    const size_t per_tok = (size_t)a.K * (xb + 4) + ((a.K / 2 + 127) / 128) * 128;
+    const size_t per_tok = (size_t)a.K * xb + 4 * (size_t)xwords<L>(a.K) +
+                           (size_t)((cbytes<L>(a.K) + 15) & ~15);
     // tokens per workgroup: <= 512 threads, <= 78 KB of LDS (two workgroups
     // per CU), then the candidate whose last round of tokens is fullest
     const int cus = num_cus();
