@@ -61,8 +61,8 @@ def source_hash(name: str) -> str:
 
 def profiled_traffic(kernel_file: str, summary: str):
     """HBM bytes per launch from a committed rocprofv3 counter summary, or
-    None when that summary is missing or was taken on a different kernel
-    source."""
+    None when the summary is missing or was taken on a different kernel
+    source (the summary stores a hash of the source file)."""
     path = os.path.join(ROOT, "profiles", summary)
     if not os.path.exists(path):
         return None
@@ -73,6 +73,88 @@ def profiled_traffic(kernel_file: str, summary: str):
     if data.get("source_sha256_16") != source_hash(kernel_file):
         return None
     return data.get("hbm_bytes_per_launch")
+
+
+# kernels summarized from rocprofv3 runs: (summary file, kernel source, name match)
+PMC_KERNELS = {
+    "gemm": ("rq_gemm_w4a4.hip", "gemm_w4a4_kernel"),
+    "gemm_codebook": ("rq_gemm_codebook.hip", "gemm_codebook_kernel"),
+    "rotate": ("rq_rpbh.hip", "rpbh_quant_kernel"),
+    "dense": ("rq_dense.hip", "dense_rotate_kernel"),
+}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def _read_pmc(d):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def summarize_pmc(fetch_dir, write_dir, workload, copy_bytes, command):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
+    dispatch) into per-launch HBM bytes, each counter scaled by what it reads
+    for the plain device-to-device copy of copy_bytes in the same run."""
+    out = {}
+    per = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals = {}
+        for r in _read_pmc(d):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        copy = [v for k, v in vals.items() if COPY_KERNEL in k]
+        big = max((x for lst in copy for x in lst), default=0.0)
+        factor = copy_bytes / (big * 1024.0) if big > 0 else None
+        per[counter] = (vals, factor, big)
+    for key, (src, match) in PMC_KERNELS.items():
+        fetch_vals = [x for k, lst in per["FETCH_SIZE"][0].items() if match in k for x in lst]
+        write_vals = [x for k, lst in per["WRITE_SIZE"][0].items() if match in k for x in lst]
+        if not fetch_vals or not write_vals:
+            continue
+        ff, wf = per["FETCH_SIZE"][1], per["WRITE_SIZE"][1]
+        fetch = sum(fetch_vals) / len(fetch_vals) * 1024.0 * (ff or 1.0)
+        write = sum(write_vals) / len(write_vals) * 1024.0 * (wf or 1.0)
+        data = {
+            "kernel": match, "workload": workload, "dispatches": len(fetch_vals),
+            "fetch_kib_per_dispatch_raw": round(sum(fetch_vals) / len(fetch_vals), 1),
+            "write_kib_per_dispatch_raw": round(sum(write_vals) / len(write_vals), 1),
+            "copy_calibration": {"bytes": copy_bytes,
+                                 "fetch_kib_raw": per["FETCH_SIZE"][2],
+                                 "write_kib_raw": per["WRITE_SIZE"][2],
+                                 "fetch_factor": ff, "write_factor": wf},
+            "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
+            "hbm_bytes_per_launch": round(fetch + write),
+            "source_sha256_16": source_hash(src),
+            "command": command,
+        }
+        name = f"{key}_{workload}_counters.json"
+        json.dump(data, open(os.path.join(ROOT, "profiles", name), "w"), indent=1)
+        out[name] = data
+    return out
+
+
+def summarize_stats(stats_csv, workload, command):
+    """Short text summary of a rocprofv3 --kernel-trace --stats csv."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# rocprofv3 kernel statistics, workload {workload}", "",
+             "Command (from the repository root on the GPU host):", "", "    " + command, "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share (%) |",
+             "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("rq::(anonymous namespace)::", "").replace("|", "/")
+        if len(name) > 110:
+            name = name[:107] + "..."
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | "
+                     f"{float(r['MinNs'])/1e3:.2f} | {float(r['MaxNs'])/1e3:.2f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    path = os.path.join(ROOT, "profiles", f"kernel_stats_{workload}.md")
+    open(path, "w").write("\n".join(lines) + "\n")
+    return path
 
 
 def rotate_bytes(w) -> int:
@@ -130,7 +212,23 @@ def main():
     ap.add_argument("--ring", type=int, default=2, help="independent layer instances cycled")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="after timing, run a plain device copy of BYTES (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="offline: summarize two rocprofv3 --pmc runs into profiles/")
+    ap.add_argument("--summarize-stats", metavar="STATS_CSV",
+                    help="offline: summarize a rocprofv3 --stats csv into profiles/")
+    ap.add_argument("--command", default="", help="command recorded in the summaries")
     args = ap.parse_args()
+
+    if args.summarize_pmc or args.summarize_stats:
+        if args.summarize_pmc:
+            res = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
+                                args.copy_calibration, args.command)
+            print(json.dumps({k: v["hbm_bytes_per_launch"] for k, v in res.items()}))
+        if args.summarize_stats:
+            print(summarize_stats(args.summarize_stats, args.workload, args.command))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -140,7 +238,7 @@ def main():
 
     import torch
     from rotated_w4a4_quantized_amd import datagen, rq
-    from tests import _layer as H
+    from rotated_w4a4_quantized_amd.layer import QuantLinear
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     rq.load()
@@ -153,7 +251,7 @@ def main():
         layers = []
         for w in wls:
             inp = datagen.make_inputs(w, seed_offset=100 * i)
-            layers.append(H.GpuLayer(w, inp))
+            layers.append(QuantLinear(w, inp))
             log(f"[bench] instance {i} layer {w.name}: T={w.T} K={w.K} N={w.N} ready")
         ring.append(layers)
     torch.cuda.synchronize()
@@ -196,6 +294,15 @@ def main():
     gemm_ms = np.array([[evs[i][j][1].elapsed_time(evs[i][j][2]) for j in range(nl)]
                         for i in range(args.steps)])
 
+    if args.copy_calibration:
+        n = args.copy_calibration
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     ops = [w.ops() for w in wls]
     value = sum(ops) / (ms_step * 1e-3) / 1e12
     layers = []
@@ -217,7 +324,8 @@ def main():
     peak = PEAK_BF16_TFLOPS if is_codebook else PEAK_INT8_TOPS
     gemm_mean_ms = float(np.mean(gemm_ms))
     achieved = float(np.mean(ops)) / (gemm_mean_ms * 1e-3) / 1e12
-    traffic = profiled_traffic("rq_gemm.hip", f"gemm_{args.workload}_counters.json")
+    traffic = profiled_traffic("rq_gemm_codebook.hip" if is_codebook else "rq_gemm_w4a4.hip",
+                               f"{'gemm_codebook' if is_codebook else 'gemm'}_{args.workload}_counters.json")
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
                 "unit": "TFLOP/s" if is_codebook else "TOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic,
@@ -227,7 +335,7 @@ def main():
     rot_gbs = rot_bytes / (rot_mean_ms * 1e-3) / 1e9
     roofline_rot = {"bound": "hbm", "achieved": round(rot_gbs, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(rot_gbs / PEAK_HBM_GBS, 4),
-                    "traffic": profiled_traffic("rq_rotate.hip",
+                    "traffic": profiled_traffic("rq_rpbh.hip",
                                                 f"rotate_{args.workload}_counters.json"),
                     "kernel": "rotate_quant"}
 

@@ -12,75 +12,11 @@ from __future__ import annotations
 import numpy as np
 
 from oracle import oracle as orc
-from rotated_w4a4_quantized_amd import datagen, rq
+from rotated_w4a4_quantized_amd import datagen, rq  # noqa: F401
+from rotated_w4a4_quantized_amd.layer import (QuantLinear as GpuLayer, device_x,  # noqa: F401
+                                              quant_for, rotation_for, torch_mod)
 
 REL_TOL = 1e-3
-
-
-def torch_mod():
-    import torch
-    return torch
-
-
-def device_x(inp, device):
-    torch = torch_mod()
-    X = inp["X"]
-    if X.dtype == np.uint16:
-        return torch.from_numpy(X.view(np.int16)).to(device)
-    return torch.from_numpy(X).to(device)
-
-
-def rotation_for(w, inp) -> rq.Rotation:
-    if w.rot == "rpbh":
-        return rq.Rotation.rpbh(inp["sign"], inp["perm"], w.block)
-    return rq.Rotation.dense(inp["R"], w.r)
-
-
-def quant_for(w) -> rq.Quant:
-    if w.quant == "int4":
-        return rq.Quant.int4()
-    return rq.Quant.lloydmax(rq.lloydmax_gaussian(16), rq.lloydmax_gaussian(1 << w.w_bits))
-
-
-class GpuLayer:
-    """Device state of one layer instance: rotation, packed weights, buffers."""
-
-    def __init__(self, w: datagen.Workload, inp: dict, device="cuda", y_dtype=None):
-        torch = torch_mod()
-        self.w, self.inp, self.device = w, inp, device
-        self.rot = rotation_for(w, inp)
-        self.q = quant_for(w)
-        self.packed = rq.pack_weights(self.rot, self.q, inp["W"])
-        self.dw = self.packed.to_device(device)
-        self.drot = self.rot.to_device(device)
-        self.X = device_x(inp, device)
-        T = w.T
-        ncode = (w.Kq // 2)
-        self.codes = torch.empty((T, ncode), dtype=torch.uint8, device=device)
-        self.scale = torch.empty((T,), dtype=torch.float32, device=device)
-        self.top = torch.empty((T, w.r), dtype=torch.int16, device=device) if w.r else None
-        wsb = rq.rotate_quant_workspace_bytes(self.rot, self.q, T)
-        self.ws = torch.empty((max(wsb, 16) // 4,), dtype=torch.float32, device=device) if wsb else None
-        ydt = {"f32": torch.float32, "bf16": torch.bfloat16}[y_dtype or w.ydtype]
-        self.Y = torch.empty((T, w.N), dtype=ydt, device=device)
-
-    def rotate_quant(self, stream=None):
-        rq.rotate_quant(self.drot, self.q, self.X, self.codes, self.scale, self.top, self.ws,
-                        stream=stream)
-
-    def linear(self, Y=None, stream=None):
-        rq.w4a4_linear(self.dw, self.codes, self.scale, self.Y if Y is None else Y, top=self.top,
-                       stream=stream)
-
-    def run(self):
-        self.rotate_quant()
-        self.linear()
-
-    def raw_acc(self):
-        torch = torch_mod()
-        acc = torch.empty((self.w.T, self.w.N), dtype=torch.int32, device=self.device)
-        self.linear(acc)
-        return acc
 
 
 def oracle_act(w, inp, rows=None):
