@@ -119,7 +119,7 @@ typedef struct rq_quant {
 } rq_quant;
 
 #define RQ_WEIGHT_MAGIC 0x31575152u /* "RQW1" */
-#define RQ_WEIGHT_VERSION 1u
+#define RQ_WEIGHT_VERSION 2u
 
 /*
  * Header at the start of every packed-weight blob (256 bytes).  The blob is
@@ -138,6 +138,14 @@ typedef struct rq_quant {
  *                 the lowest bits
  *   total_bytes   size of the whole blob
  *   a_levels, w_levels  the LLOYDMAX decode levels (zeros for INT4)
+ *   INT4 only, the GEMM's private copy of the codes of the quantized
+ *   coordinates k in [r, K) (zeros for LLOYDMAX):
+ *   wsum_offset   byte offset of int32 [N]: sum over k in [r, K) of q_w[n][k]
+ *   mma_offset    byte offset of the FP6 matrix-core fragments,
+ *                 [mma_ntiles][mma_stages][3][64][16] bytes: 32 output rows
+ *                 by 128 coordinates per 3 KB tile, zero-padded past N and K
+ *   mma_stages    ceil((K - r) / 128)
+ *   mma_ntiles    ceil(N / 32)
  */
 typedef struct rq_weight_header {
     uint32_t magic;
@@ -155,7 +163,11 @@ typedef struct rq_weight_header {
     int64_t total_bytes;
     float a_levels[16];
     float w_levels[16];
-    uint8_t reserved[256 - 64 - 128];
+    int64_t wsum_offset;
+    int64_t mma_offset;
+    int32_t mma_stages;
+    int32_t mma_ntiles;
+    uint8_t reserved[256 - 64 - 128 - 24];
 } rq_weight_header;
 
 /* Library version (major * 10000 + minor * 100 + patch). */
@@ -273,7 +285,7 @@ rq_status rq_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void 
  *   T       tokens, 0 <= T < 2^31
  *   bias    device fp32 [N] or NULL
  *   Y       device [T][N], dtype y_dtype: RQ_F32, RQ_BF16 (nearest-even), or
- *           RQ_I32 = the raw INT4 accumulators acc * 256 (INT4 formats only;
+ *           RQ_I32 = the exact INT4 accumulators acc (INT4 formats only;
  *           the low-rank term and bias are left out)
  *   stream  hipStream_t
  * Errors: RQ_ERR_NULL, RQ_ERR_FORMAT, RQ_ERR_SHAPE, RQ_ERR_DTYPE,

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -35,7 +36,25 @@ rq_status check_header(const rq_weight_header *hdr) {
         return fail(RQ_ERR_SHAPE, "the codebook GEMM needs K % 64 == 0");
     if (hdr->scale_offset % 16 != 0 || hdr->codes_offset % 16 != 0)
         return fail(RQ_ERR_FORMAT, "weight header offsets are not 16-byte aligned");
+    if (hdr->format == RQ_Q_INT4_SYM) {
+        if (hdr->mma_stages != (hdr->K - hdr->r + 127) / 128 || hdr->mma_ntiles != (hdr->N + 31) / 32)
+            return fail(RQ_ERR_FORMAT, "weight header FP6 tile counts are inconsistent");
+        if (hdr->wsum_offset % 16 != 0 || hdr->mma_offset % 16 != 0 || hdr->wsum_offset <= 0 ||
+            hdr->mma_offset + (int64_t)hdr->mma_ntiles * hdr->mma_stages * 3 * 1024 > hdr->total_bytes)
+            return fail(RQ_ERR_FORMAT, "weight header FP6 section offsets are inconsistent");
+    }
     return RQ_OK;
+}
+
+// Which matrix cores run the INT4 GEMM: FP6 (default; exact, twice the int8
+// rate on gfx950) or, with RQ_W4A4_MFMA=int8 in the environment, the int8
+// kernel that widens the nibbles in registers.  Read once per process.
+bool use_int8_gemm() {
+    static const bool v = [] {
+        const char *e = std::getenv("RQ_W4A4_MFMA");
+        return e && std::strcmp(e, "int8") == 0;
+    }();
+    return v;
 }
 
 }  // namespace
@@ -112,9 +131,13 @@ rq_status rq_w4a4_linear(const rq_weight_header *hdr, const void *blob, const ui
     if (!aligned16(blob) || !aligned16(codes) || !aligned16(scale) || !aligned16(Y) ||
         (top && !aligned16(top)) || (bias && !aligned16(bias)))
         return fail(RQ_ERR_ALIGN, "device buffers must be 16-byte aligned");
-    if (hdr->format == RQ_Q_INT4_SYM)
-        return hip_status(launch_gemm_w4a4(codes, scale, top, T, hdr, blob, bias, Y, y_dtype, stream),
-                          "w4a4 gemm launch");
+    if (hdr->format == RQ_Q_INT4_SYM) {
+        if (use_int8_gemm())
+            return hip_status(launch_gemm_w4a4(codes, scale, top, T, hdr, blob, bias, Y, y_dtype, stream),
+                              "w4a4 int8 gemm launch");
+        return hip_status(launch_gemm_fp6(codes, scale, top, T, hdr, blob, bias, Y, y_dtype, stream),
+                          "w4a4 fp6 gemm launch");
+    }
     return hip_status(launch_gemm_codebook(codes, scale, T, hdr, blob, bias, Y, y_dtype, stream),
                       "codebook gemm launch");
 }

@@ -7,6 +7,10 @@
 //   RPBH:  Y = s_a[t] s_w[n] acc / b
 //   DENSE: Y = s_w[n] (lr[t][n] + s_a[t] acc),  lr = sum_{j<r} bf16(u)[t][j] qw[n][j]
 //
+// This is the int8 baseline of the INT4 GEMM (selected with
+// RQ_W4A4_MFMA=int8); the default runs on the FP6 matrix cores
+// (rq_gemm_fp6.hip) at twice the rate.
+//
 // Widening: gfx950 has no 4-bit MFMA.  For a packed word p (eight nibbles,
 // low nibble = even k), (p << 4) & 0xF0F0F0F0 holds 16 q for the even k and
 // p & 0xF0F0F0F0 holds 16 q for the odd k, as int8 lanes.  Both operands
@@ -61,8 +65,7 @@ struct W4A4Args {
     int r;                 // low-rank width (multiple of 32) or 0
     int ydt;               // rq_dtype
     int tiles_t, tiles_n;
-    float post;            // 1 / (256 * b_div)
-    float post_lr;         // 1 / 256
+    float post;            // 1 / b_div
 };
 
 // Workgroup barrier ordering LDS only: waits for this wave's LDS traffic,
@@ -86,8 +89,9 @@ __device__ inline uint32_t bf16_rne_bits(float x) {
     return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;   // finite x
 }
 
-template <int BT_, int BN_, int WT_, int WN_, int NBUF_>
+template <int BT_, int BN_, int WT_, int WN_, int NBUF_, int OCC_ = 2>
 struct Cfg {
+    static constexpr int OCC = OCC_;          // workgroups per CU the register budget is sized for
     static constexpr int BT = BT_, BN = BN_, WT = WT_, WN = WN_;
     static constexpr int NBUF = NBUF_;        // LDS stage buffers (prefetch distance NBUF - 1)
     static constexpr int NW = WT * WN;
@@ -98,6 +102,8 @@ struct Cfg {
     static constexpr int LDS_STAGE = ROWS * kStageBytes;
     static constexpr int NQ = ROWS / 16;      // 1 KB direct-to-LDS loads per stage
     static constexpr int IPW = NQ / NW;       // ... issued by each wave
+    static constexpr int OUT_STRIDE = BN * 2 + 16;            // bytes per staged bf16 output row
+    static constexpr int LDS_BYTES = NBUF * LDS_STAGE > BT * OUT_STRIDE ? NBUF * LDS_STAGE : BT * OUT_STRIDE;
     static_assert(BT % (32 * WT) == 0 && BN % (32 * WN) == 0, "tile shape");
     static_assert(IPW * NW == NQ, "load split");
 };
@@ -106,6 +112,26 @@ struct Cfg {
 // c ^ ((r >> 1) & 3), which keeps the 16-byte accesses of eight consecutive
 // lanes on distinct bank groups.
 __device__ inline int row_slot(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4); }
+
+// One direct-to-LDS load of 16 bytes per lane (global_load_lds_dwordx4): lane
+// l's bytes land at LDS offset lds_addr + 16 l.  Written as inline asm so that
+// the compiler does not see an LDS store it cannot tell apart from the
+// fragment reads -- it would otherwise wait for every load in flight (the
+// prefetched stages too) before each read.  Completion is tracked by hand
+// with s_waitcnt vmcnt.  M0 holds the LDS address (saved and restored; one
+// wait state between the M0 write and the load); the load has no VGPR result.
+__device__ inline void dma16(const void *gptr, uint32_t lds_addr) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(gptr), "s"(lds_addr)
+        : "memory");
+}
 
 // Source of K-tail chunks: sixteen zero bytes in global memory, so that the
 // direct-to-LDS loads need no branch.
@@ -128,9 +154,9 @@ __device__ inline void tile_of(int bid, int nblk, int tiles_t, int tiles_n, int 
 }
 
 template <class C, bool HAS_LR, bool TAIL>
-__global__ void __launch_bounds__(C::NTH, 2)
+__global__ void __launch_bounds__(C::NTH, C::OCC)
 gemm_w4a4_kernel(W4A4Args a) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[C::NBUF * C::LDS_STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_BYTES];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wt = wave / C::WN, wn = wave % C::WN;
@@ -162,17 +188,15 @@ gemm_w4a4_kernel(W4A4Args a) {
         }
     }
     const int nstage = (a.lda + kStageBytes - 1) / kStageBytes;
+    // LDS byte offset of the buffer (the low half of its flat address), wave-uniform
+    const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
     auto issue = [&](int s, int buf) {
         const int kb = s * kStageBytes;
 #pragma unroll
         for (int i = 0; i < C::IPW; ++i) {
             const uint8_t *p = gsrc[i] + kb;
             if (TAIL && kb + col[i] >= a.lda) p = g_zero16;
-            __builtin_amdgcn_global_load_lds(
-                (const void *)p,
-                (__attribute__((address_space(3))) void *)(lds + buf * C::LDS_STAGE +
-                                                          (wave * C::IPW + i) * 1024),
-                16, 0, 0);
+            dma16(p, __builtin_amdgcn_readfirstlane(lds_base + buf * C::LDS_STAGE + (wave * C::IPW + i) * 1024));
         }
     };
     // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding)
@@ -298,8 +322,8 @@ gemm_w4a4_kernel(W4A4Args a) {
     // in LDS (free after the last barrier) and written back as 256-byte row
     // segments -- the accumulator layout alone would give every store
     // instruction 32 separate 16-byte pieces in 32 different rows.
-    constexpr int kOutStride = C::BN * 2 + 16;   // bytes per staged output row
-    if constexpr (!HAS_LR && C::BT * kOutStride <= C::NBUF * C::LDS_STAGE) {
+    constexpr int kOutStride = C::OUT_STRIDE;
+    if constexpr (!HAS_LR) {
         if (a.ydt == RQ_BF16 && t0 + C::BT <= a.T && n0 + C::BN <= a.N && (a.N % 8) == 0 &&
             a.bias == nullptr) {
 #pragma unroll
@@ -312,10 +336,10 @@ gemm_w4a4_kernel(W4A4Args a) {
                     for (int q = 0; q < 4; ++q) {
                         const int nl = wn * C::FN * 32 + i * 32 + 8 * q + 4 * lg;
                         const float4 sw4 = *reinterpret_cast<const float4 *>(a.sw + n0 + nl);
-                        const float y0 = (float)acc[i][j][4 * q + 0] * (sat * sw4.x);
-                        const float y1 = (float)acc[i][j][4 * q + 1] * (sat * sw4.y);
-                        const float y2 = (float)acc[i][j][4 * q + 2] * (sat * sw4.z);
-                        const float y3 = (float)acc[i][j][4 * q + 3] * (sat * sw4.w);
+                        const float y0 = (float)(acc[i][j][4 * q + 0] >> 8) * (sat * sw4.x);
+                        const float y1 = (float)(acc[i][j][4 * q + 1] >> 8) * (sat * sw4.y);
+                        const float y2 = (float)(acc[i][j][4 * q + 2] >> 8) * (sat * sw4.z);
+                        const float y3 = (float)(acc[i][j][4 * q + 3] >> 8) * (sat * sw4.w);
                         *reinterpret_cast<uint2 *>(lds + tl * kOutStride + 2 * nl) =
                             make_uint2(bf16_rne_bits(y0) | (bf16_rne_bits(y1) << 16),
                                        bf16_rne_bits(y2) | (bf16_rne_bits(y3) << 16));
@@ -353,12 +377,12 @@ gemm_w4a4_kernel(W4A4Args a) {
                 float y[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    iv[e] = acc[i][j][4 * q + e];
+                    iv[e] = acc[i][j][4 * q + e] >> 8;   // the MFMA returned 256 acc
                     const int n = nb + e < a.N ? nb + e : a.N - 1;
                     const float swn = a.sw[n];
                     const float bn = a.bias ? a.bias[n] : 0.0f;
                     if constexpr (has_lr)
-                        y[e] = swn * (lr[i][j][4 * q + e] + sat * ((float)iv[e] * a.post_lr)) + bn;
+                        y[e] = swn * (lr[i][j][4 * q + e] + sat * (float)iv[e]) + bn;
                     else
                         y[e] = ((float)iv[e] * a.post) * (sat * swn) + bn;
                 }
@@ -430,8 +454,7 @@ int launch_gemm_w4a4(const uint8_t *codes, const float *scale, const uint16_t *t
     a.ldb = hdr->row_bytes;
     a.koff = hdr->r / 2;
     a.ydt = y_dtype;
-    a.post = 1.0f / (256.0f * (float)hdr->b_div);
-    a.post_lr = 1.0f / 256.0f;
+    a.post = 1.0f / (float)hdr->b_div;
     hipStream_t s = static_cast<hipStream_t>(stream);
     // the low-rank term needs registers for its own accumulators: mid tile
     if (a.r > 0) return (int)launch_cfg<CfgMid, true>(a, s);

@@ -124,16 +124,73 @@ static inline double bf16_bits_to_double(uint16_t h) {
     return (double)f;
 }
 
-static int64_t blob_layout(const rq_rotation *rot, const rq_quant *q, int32_t N,
-                           int32_t *row_bytes, int64_t *scale_off, int64_t *codes_off) {
+struct BlobLayout {
+    int32_t row_bytes;
+    int64_t scale_off, codes_off, wsum_off, mma_off, total;
+    int32_t mma_stages, mma_ntiles;
+};
+
+static inline int64_t round256(int64_t v) { return (v + 255) / 256 * 256; }
+
+static BlobLayout blob_layout(const rq_rotation *rot, const rq_quant *q, int32_t N) {
     const int K = rot->K;
-    const int rb = (q->kind == RQ_Q_INT4_SYM || q->w_bits == 4) ? K / 2 : K / 4;
-    const int64_t so = (int64_t)sizeof(rq_weight_header);
-    const int64_t co = so + (((int64_t)N * 4 + 255) / 256) * 256;
-    *row_bytes = rb;
-    *scale_off = so;
-    *codes_off = co;
-    return co + (((int64_t)N * rb + 255) / 256) * 256;
+    const int r = rot->kind == RQ_ROT_DENSE ? rot->r : 0;
+    BlobLayout L;
+    L.row_bytes = (q->kind == RQ_Q_INT4_SYM || q->w_bits == 4) ? K / 2 : K / 4;
+    L.scale_off = (int64_t)sizeof(rq_weight_header);
+    L.codes_off = L.scale_off + round256((int64_t)N * 4);
+    const int64_t end = L.codes_off + round256((int64_t)N * L.row_bytes);
+    if (q->kind == RQ_Q_INT4_SYM) {
+        L.mma_stages = (K - r + 127) / 128;
+        L.mma_ntiles = (N + 31) / 32;
+        L.wsum_off = end;
+        L.mma_off = L.wsum_off + round256((int64_t)N * 4);
+        L.total = L.mma_off + (int64_t)L.mma_ntiles * L.mma_stages * 3 * 1024;
+    } else {
+        L.mma_stages = L.mma_ntiles = 0;
+        L.wsum_off = L.mma_off = 0;
+        L.total = end;
+    }
+    return L;
+}
+
+// FP6 (E2M3) fragments of the GEMM's matrix cores.  A weight code q in
+// [-7, 7] is stored sign-magnitude, (q < 0) << 5 | |q|, which E2M3 decodes as
+// the subnormal q / 8.  Tile (nt, s) covers rows 32 nt .. 32 nt + 31 and the
+// quantized coordinates 128 s .. 128 s + 127; lane l (row 32 nt + l % 32,
+// half h = l / 32) holds two 24-byte fragments, for k-steps ks = 0, 1, over
+// coordinates 128 s + 64 ks + 32 h + (0..31).  Within a fragment, 6-bit field
+// f holds coordinate offset kFieldOrder[f % 16] + 16 (f / 16): the order in
+// which the GEMM spreads activation nibbles into fields without per-element
+// shifts (rq_gemm_fp6.hip).  The lane's 48 bytes go out as three 16-byte
+// parts, part-major: [part][lane][16].
+static const int kFieldOrder[16] = {0, 1, 3, 4, 6, 7, 9, 10, 12, 13, 15, 8, 2, 11, 5, 14};
+
+static void pack_mma_tile(const uint8_t *codes, int32_t N, int row_bytes, int r, int Kq,
+                          int nt, int s, uint8_t *tile /* 3 KB */) {
+    for (int l = 0; l < 64; ++l) {
+        const int n = 32 * nt + (l % 32), h = l / 32;
+        uint32_t dw[12] = {0};
+        for (int ks = 0; ks < 2; ++ks) {
+            const int kbase = 128 * s + 64 * ks + 32 * h;
+            for (int f = 0; f < 32; ++f) {
+                const int k = kbase + kFieldOrder[f % 16] + 16 * (f / 16);
+                int qv = 0;
+                if (n < N && k < Kq) {
+                    const int kk = r + k;
+                    const uint8_t byte = codes[(size_t)n * row_bytes + kk / 2];
+                    const int nib = (kk & 1) ? (byte >> 4) : (byte & 15);
+                    qv = nib >= 8 ? nib - 16 : nib;
+                }
+                const uint32_t code = (qv < 0 ? 32u : 0u) | (uint32_t)(qv < 0 ? -qv : qv);
+                const int w = (6 * f) / 32, o = (6 * f) % 32;   // field f at bits [6f, 6f + 6)
+                dw[6 * ks + w] |= code << o;
+                if (o > 26) dw[6 * ks + w + 1] |= code >> (32 - o);   // straddles two dwords
+            }
+        }
+        for (int part = 0; part < 3; ++part)
+            std::memcpy(tile + (part * 64 + l) * 16, &dw[4 * part], 16);
+    }
 }
 
 }  // namespace rq
@@ -154,9 +211,7 @@ rq_status rq_packed_weight_bytes(const rq_rotation *rot, const rq_quant *q, int3
     if ((st = check_quant(rot, q)) != RQ_OK) return st;
     if (!bytes) return fail(RQ_ERR_NULL, "bytes is NULL");
     if (N < 1 || N > (1 << 20)) return fail(RQ_ERR_SHAPE, "N must be in [1, 2^20]");
-    int32_t rb;
-    int64_t so, co;
-    *bytes = (size_t)blob_layout(rot, q, N, &rb, &so, &co);
+    *bytes = (size_t)blob_layout(rot, q, N).total;
     return RQ_OK;
 }
 
@@ -181,9 +236,9 @@ rq_status rq_pack_weights(const rq_rotation *rot, const rq_quant *q, const void 
                 return fail(RQ_ERR_SHAPE, "sign entries must be -1 or +1");
         }
     }
-    int32_t rb;
-    int64_t so, co;
-    const int64_t total = blob_layout(rot, q, N, &rb, &so, &co);
+    const BlobLayout BL = blob_layout(rot, q, N);
+    const int32_t rb = BL.row_bytes;
+    const int64_t so = BL.scale_off, co = BL.codes_off, total = BL.total;
     if ((int64_t)blob_bytes < total)
         return fail(RQ_ERR_SHAPE, "blob_bytes " + std::to_string(blob_bytes) + " < required " +
                                       std::to_string(total));
@@ -205,6 +260,10 @@ rq_status rq_pack_weights(const rq_rotation *rot, const rq_quant *q, const void 
     hdr.scale_offset = so;
     hdr.codes_offset = co;
     hdr.total_bytes = total;
+    hdr.wsum_offset = BL.wsum_off;
+    hdr.mma_offset = BL.mma_off;
+    hdr.mma_stages = BL.mma_stages;
+    hdr.mma_ntiles = BL.mma_ntiles;
     if (q->kind == RQ_Q_LLOYDMAX) {
         std::memcpy(hdr.a_levels, q->a_levels, sizeof hdr.a_levels);
         std::memcpy(hdr.w_levels, q->w_levels, sizeof hdr.w_levels);
@@ -281,6 +340,36 @@ rq_status rq_pack_weights(const rq_rotation *rot, const rq_quant *q, const void 
         if (n0 < n1) pool.emplace_back(work, n0, n1);
     }
     for (auto &th : pool) th.join();
+    if (q->kind == RQ_Q_INT4_SYM) {
+        // the GEMM's copy of the quantized coordinates [r, K): row sums and
+        // FP6 fragments (see pack_mma_tile)
+        const int r = hdr.r, Kq = K - r;
+        int32_t *wsum = reinterpret_cast<int32_t *>(out + BL.wsum_off);
+        for (int n = 0; n < N; ++n) {
+            int32_t sum = 0;
+            for (int k = r; k < K; ++k) {
+                const uint8_t byte = codes[(size_t)n * rb + k / 2];
+                const int nib = (k & 1) ? (byte >> 4) : (byte & 15);
+                sum += nib >= 8 ? nib - 16 : nib;
+            }
+            wsum[n] = sum;
+        }
+        const int ntiles = BL.mma_ntiles, S = BL.mma_stages;
+        auto tiles = [&](int t0, int t1) {
+            for (int tile = t0; tile < t1; ++tile)
+                for (int s = 0; s < S; ++s)
+                    pack_mma_tile(codes, N, rb, r, Kq, tile, s,
+                                  out + BL.mma_off + ((int64_t)tile * S + s) * 3 * 1024);
+        };
+        std::vector<std::thread> tp;
+        const unsigned nth = std::max(1u, std::min<unsigned>(nt, (unsigned)ntiles));
+        const int tchunk = (ntiles + (int)nth - 1) / (int)nth;
+        for (unsigned t = 0; t < nth; ++t) {
+            const int a0 = (int)t * tchunk, a1 = std::min(ntiles, a0 + tchunk);
+            if (a0 < a1) tp.emplace_back(tiles, a0, a1);
+        }
+        for (auto &th : tp) th.join();
+    }
     return RQ_OK;
 }
 

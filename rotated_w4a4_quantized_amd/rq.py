@@ -53,7 +53,9 @@ class c_weight_header(ctypes.Structure):
                 ("w_bits", ctypes.c_int32), ("row_bytes", ctypes.c_int32),
                 ("scale_offset", ctypes.c_int64), ("codes_offset", ctypes.c_int64),
                 ("total_bytes", ctypes.c_int64), ("a_levels", ctypes.c_float * 16),
-                ("w_levels", ctypes.c_float * 16), ("reserved", ctypes.c_uint8 * 64)]
+                ("w_levels", ctypes.c_float * 16), ("wsum_offset", ctypes.c_int64),
+                ("mma_offset", ctypes.c_int64), ("mma_stages", ctypes.c_int32),
+                ("mma_ntiles", ctypes.c_int32), ("reserved", ctypes.c_uint8 * 40)]
 
 
 assert ctypes.sizeof(c_weight_header) == 256
@@ -248,6 +250,17 @@ class PackedWeights:
     def codes(self) -> np.ndarray:
         h = self.header
         return self.blob[h.codes_offset:h.codes_offset + h.N * h.row_bytes].reshape(h.N, h.row_bytes)
+
+    def wsum(self) -> np.ndarray:
+        """INT4: per-channel sums of the quantized weight codes (int32 [N])."""
+        h = self.header
+        return self.blob[h.wsum_offset:h.wsum_offset + 4 * h.N].view(np.int32)
+
+    def mma_tiles(self) -> np.ndarray:
+        """INT4: the GEMM's FP6 fragments, uint8 [ntiles][stages][3][64][16]."""
+        h = self.header
+        n = h.mma_ntiles * h.mma_stages * 3 * 1024
+        return self.blob[h.mma_offset:h.mma_offset + n].reshape(h.mma_ntiles, h.mma_stages, 3, 64, 16)
 
     def to_device(self, device="cuda") -> "DeviceWeights":
         import torch

@@ -159,6 +159,68 @@ def test_pack_int4_matches_oracle(name, shape):
         rq.RQ_WEIGHT_MAGIC, w.K, w.N, w.r, w.b_eff, w.K // 2)
 
 
+# E2M3 (OCP MX FP6): sign, 2 exponent bits with bias 1, 3 mantissa bits
+def _e2m3_value(code):
+    code = np.asarray(code, np.int64)
+    sgn = np.where(code & 32, -1.0, 1.0)
+    e, m = (code >> 3) & 3, code & 7
+    mag = np.where(e == 0, m / 8.0, np.ldexp(1.0 + m / 8.0, (e - 1).astype(np.int32)))
+    return sgn * mag
+
+
+def _decode_fp6_fragments(tiles, N, Kq):
+    """Rebuild q_w[n][k] (k over the quantized coordinates) from the GEMM's
+    FP6 fragments as rq.h documents them: tile (nt, s), lane l -> row
+    32 nt + l % 32, half h = l // 32; 48 bytes = [part][16], fragment ks at
+    bytes 24 ks; field f at bits 6 f holds coordinate
+    128 s + 64 ks + 32 h + order[f % 16] + 16 (f // 16), scaled by 2^3."""
+    order = [0, 1, 3, 4, 6, 7, 9, 10, 12, 13, 15, 8, 2, 11, 5, 14]
+    nt_, S = tiles.shape[:2]
+    out = np.zeros((nt_ * 32, S * 128), np.int64)
+    lane_bytes = tiles.transpose(0, 1, 3, 2, 4).reshape(nt_, S, 64, 48)
+    for ks in range(2):
+        frag = lane_bytes[..., 24 * ks:24 * ks + 24].astype(np.uint64)
+        bits = np.zeros(frag.shape[:-1], dtype=object)
+        for b in range(24):
+            bits = bits + (frag[..., b].astype(object) << (8 * b))
+        for f in range(32):
+            code = np.vectorize(lambda v: (v >> (6 * f)) & 63, otypes=[np.int64])(bits)
+            val = _e2m3_value(code) * 8
+            assert np.all(val == np.round(val))
+            k_in = order[f % 16] + 16 * (f // 16)
+            for l in range(64):
+                rows = 32 * np.arange(nt_) + l % 32
+                ks_ = 128 * np.arange(S) + 64 * ks + 32 * (l // 32) + k_in
+                out[np.ix_(rows, ks_)] = val[:, :, l].astype(np.int64)
+    return out[:N, :Kq], out
+
+
+def _unpack_nibbles(codes):
+    lo = (codes & 15).astype(np.int64)
+    hi = (codes >> 4).astype(np.int64)
+    q = np.stack([lo, hi], -1).reshape(codes.shape[0], -1)
+    return np.where(q >= 8, q - 16, q)
+
+
+@pytest.mark.parametrize("name,shape", [("tiny", dict(K=256, N=40, block=64)),
+                                        ("pixart", dict(K=224, N=33)),
+                                        ("flux_up", dict(K=160, N=70, block=32))])
+def test_pack_int4_fp6_fragments(name, shape):
+    w = datagen.WORKLOADS[name].with_shape(T=4, **shape)
+    inp = datagen.make_inputs(w)
+    rot = (rq.Rotation.rpbh(inp["sign"], inp["perm"], w.block) if w.rot == "rpbh"
+           else rq.Rotation.dense(inp["R"], w.r))
+    pw = rq.pack_weights(rot, rq.Quant.int4(), inp["W"])
+    h = pw.header
+    Kq = w.K - w.r
+    assert h.mma_stages == -(-Kq // 128) and h.mma_ntiles == -(-w.N // 32)
+    qw = _unpack_nibbles(_oracle_weights(w, inp)["codes"])[:, w.r:]
+    got, padded = _decode_fp6_fragments(pw.mma_tiles(), w.N, Kq)
+    assert np.array_equal(got, qw)
+    assert not padded[w.N:].any() and not padded[:, Kq:].any()   # zero padding
+    assert np.array_equal(pw.wsum(), qw.sum(axis=1))
+
+
 def test_pack_bf16_weights_and_zero_rows():
     w = datagen.WORKLOADS["flux_up"].with_shape(T=4, K=512, N=16, block=128)
     inp = datagen.make_inputs(w)
