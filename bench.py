@@ -37,6 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
+PEAK_FP6_TOPS = 10100.0      # MI355X dense fp6/fp4 MFMA, TOP/s (the INT4 GEMM's matrix cores)
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 
@@ -77,7 +78,8 @@ def profiled_traffic(kernel_file: str, summary: str):
 
 # kernels summarized from rocprofv3 runs: (summary file, kernel source, name match)
 PMC_KERNELS = {
-    "gemm": ("rq_gemm_w4a4.hip", "gemm_w4a4_kernel"),
+    "gemm": ("rq_gemm_fp6.hip", "gemm_fp6_mma_kernel"),
+    "gemm_int8": ("rq_gemm_w4a4.hip", "gemm_w4a4_kernel"),
     "gemm_codebook": ("rq_gemm_codebook.hip", "gemm_codebook_kernel"),
     "rotate": ("rq_rpbh.hip", "rpbh_quant_kernel"),
     "dense": ("rq_dense.hip", "dense_rotate_kernel"),
@@ -242,6 +244,7 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     rq.load()
+    int8_gemm = os.environ.get("RQ_W4A4_MFMA") == "int8"
     names = WORKLOADS[args.workload]
     wls = [datagen.WORKLOADS[n] for n in names]
 
@@ -251,7 +254,9 @@ def main():
         layers = []
         for w in wls:
             inp = datagen.make_inputs(w, seed_offset=100 * i)
-            layers.append(QuantLinear(w, inp))
+            # RPBH INT4 layers hand the GEMM its codes in the matrix-core layout
+            mode = "mma" if (w.rot == "rpbh" and w.quant == "int4" and not int8_gemm) else "canonical"
+            layers.append(QuantLinear(w, inp, codes=mode))
             log(f"[bench] instance {i} layer {w.name}: T={w.T} K={w.K} N={w.N} ready")
         ring.append(layers)
     torch.cuda.synchronize()
@@ -321,15 +326,19 @@ def main():
         log(f"[bench] {json.dumps(layers[-1])}")
 
     is_codebook = all(w.quant == "lloydmax" for w in wls)
-    peak = PEAK_BF16_TFLOPS if is_codebook else PEAK_INT8_TOPS
+    if is_codebook:
+        peak, gsrc, gkey, gname = PEAK_BF16_TFLOPS, "rq_gemm_codebook.hip", "gemm_codebook", "gemm_codebook_kernel"
+    elif int8_gemm:
+        peak, gsrc, gkey, gname = PEAK_INT8_TOPS, "rq_gemm_w4a4.hip", "gemm_int8", "gemm_w4a4_kernel"
+    else:
+        # the INT4 GEMM computes on the FP6 matrix cores: its own dtype's peak
+        peak, gsrc, gkey, gname = PEAK_FP6_TOPS, "rq_gemm_fp6.hip", "gemm", "gemm_fp6_mma_kernel"
     gemm_mean_ms = float(np.mean(gemm_ms))
     achieved = float(np.mean(ops)) / (gemm_mean_ms * 1e-3) / 1e12
-    traffic = profiled_traffic("rq_gemm_codebook.hip" if is_codebook else "rq_gemm_w4a4.hip",
-                               f"{'gemm_codebook' if is_codebook else 'gemm'}_{args.workload}_counters.json")
+    traffic = profiled_traffic(gsrc, f"{gkey}_{args.workload}_counters.json")
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
                 "unit": "TFLOP/s" if is_codebook else "TOP/s",
-                "frac": round(achieved / peak, 4), "traffic": traffic,
-                "kernel": "gemm_codebook_kernel" if is_codebook else "gemm_w4a4_kernel"}
+                "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": gname}
     rot_mean_ms = float(np.mean(rot_ms))
     rot_bytes = float(np.mean([rotate_bytes(w) for w in wls]))
     rot_gbs = rot_bytes / (rot_mean_ms * 1e-3) / 1e9
@@ -356,7 +365,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if is_codebook else "i8",
+        "dtype": "bf16" if is_codebook else ("i8" if int8_gemm else "fp6"),
         "data": "synthetic",
         "config": {"workload": args.workload, "layers": [
             {"name": w.name, "T": w.T, "K": w.K, "N": w.N, "rotation": w.rot, "block": w.block,

@@ -228,6 +228,13 @@ rq_status rq_rotate_quant_workspace_bytes(const rq_rotation *rot, const rq_quant
                                           int64_t T, size_t *bytes);
 
 /*
+ * Bytes of a codes_mma buffer for T tokens (rq_rotate_quant's optional
+ * output, rq_w4a4_linear's optional input): T * ceil((K - r) / 128) * 96.
+ * Errors: RQ_ERR_NULL, RQ_ERR_SHAPE, RQ_ERR_UNSUPPORTED.
+ */
+rq_status rq_codes_mma_bytes(const rq_rotation *rot, int64_t T, size_t *bytes);
+
+/*
  * Runtime activation path: rotate and quantize T tokens.
  * ("OrbitQuant" abstract: only a forward rotation of the activations
  * remains at runtime; TR-DQ section 3.2: quantization parameters are
@@ -251,9 +258,17 @@ rq_status rq_rotate_quant_workspace_bytes(const rq_rotation *rot, const rq_quant
  *           16-byte aligned
  *   T       tokens, 0 <= T < 2^31
  *   codes   device uint8 [T][(K - r) / 2]: INT4 nibbles (two's complement,
- *           low nibble = even coordinate) or LLOYDMAX 4-bit indices, same packing
+ *           low nibble = even coordinate) or LLOYDMAX 4-bit indices, same
+ *           packing.  May be NULL for RPBH INT4_SYM when codes_mma is given.
  *   scale   device fp32 [T]: s (INT4) or sigma (LLOYDMAX)
  *   top     device bf16 [T][r] for DENSE with r > 0, else NULL
+ *   codes_mma  RPBH INT4_SYM only, optional: device buffer of
+ *           rq_codes_mma_bytes() receiving the same codes in the low-bit
+ *           GEMM's matrix-core layout.  Per token, one 96-byte block per 128
+ *           coordinates; coordinate c of the block is carried as the 6-bit
+ *           E2M3 value (q + 8) / 8 in one of four 24-byte fragments (the
+ *           placement is fixed; rq_w4a4_linear is its only reader).  Bytes
+ *           for coordinates past K are left unwritten.  NULL: not written.
  *   workspace, workspace_bytes  device scratch of at least
  *           rq_rotate_quant_workspace_bytes() (NULL/0 when that is 0)
  *   stream  hipStream_t
@@ -262,8 +277,8 @@ rq_status rq_rotate_quant_workspace_bytes(const rq_rotation *rot, const rq_quant
  */
 rq_status rq_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void *X,
                           int32_t x_dtype, int64_t T, uint8_t *codes, float *scale,
-                          uint16_t *top, void *workspace, size_t workspace_bytes,
-                          void *stream);
+                          uint16_t *top, uint8_t *codes_mma, void *workspace,
+                          size_t workspace_bytes, void *stream);
 
 /*
  * Runtime low-bit GEMM with the per-token x per-channel rescale
@@ -278,10 +293,19 @@ rq_status rq_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void 
  *   LLOYDMAX: Y = sigma[t] tau[n] / b_div * sum_k a_levels[idx_a] * w_levels[idx_w]
  *          (bf16 products, fp32 accumulation)
  *   + bias[n] when bias is not NULL.
+ * INT4 weights run on the FP6 (E2M3) matrix cores: activation codes become
+ * q + 8, weight codes q, both exact in E2M3, and the per-channel sum of the
+ * weight codes (in the blob) removes the offset; every partial sum is an
+ * integer below 2^24, so the fp32 accumulation is exact.  With
+ * RQ_W4A4_MFMA=int8 in the environment the int8 matrix cores run instead
+ * (codes must then be given).
  * Arguments:
  *   hdr     host pointer to the blob's header (its first 256 bytes)
  *   blob    device copy of the whole blob, 16-byte aligned
  *   codes, scale, top  as written by rq_rotate_quant (device)
+ *   codes_mma  optional (INT4 weights with r == 0): the codes_mma output of
+ *           rq_rotate_quant for the same tokens; when given it is read
+ *           instead of codes (which may then be NULL)
  *   T       tokens, 0 <= T < 2^31
  *   bias    device fp32 [N] or NULL
  *   Y       device [T][N], dtype y_dtype: RQ_F32, RQ_BF16 (nearest-even), or
@@ -292,8 +316,8 @@ rq_status rq_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void 
  *         RQ_ERR_ALIGN, RQ_ERR_UNSUPPORTED, RQ_ERR_HIP.
  */
 rq_status rq_w4a4_linear(const rq_weight_header *hdr, const void *blob, const uint8_t *codes,
-                         const float *scale, const uint16_t *top, int64_t T,
-                         const float *bias, void *Y, int32_t y_dtype, void *stream);
+                         const float *scale, const uint16_t *top, const uint8_t *codes_mma,
+                         int64_t T, const float *bias, void *Y, int32_t y_dtype, void *stream);
 
 #ifdef __cplusplus
 }

@@ -73,9 +73,20 @@ rq_status rq_rotate_quant_workspace_bytes(const rq_rotation *rot, const rq_quant
     return RQ_OK;
 }
 
+rq_status rq_codes_mma_bytes(const rq_rotation *rot, int64_t T, size_t *bytes) {
+    clear_error();
+    rq_status st = check_rotation(rot, false);
+    if (st != RQ_OK) return st;
+    if (!bytes) return fail(RQ_ERR_NULL, "bytes is NULL");
+    if (T < 0 || T >= (int64_t(1) << 31)) return fail(RQ_ERR_SHAPE, "T out of range");
+    *bytes = (size_t)T * (size_t)mma_row_bytes(rot->K - rot->r);
+    return RQ_OK;
+}
+
 rq_status rq_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void *X,
                           int32_t x_dtype, int64_t T, uint8_t *codes, float *scale,
-                          uint16_t *top, void *workspace, size_t workspace_bytes, void *stream) {
+                          uint16_t *top, uint8_t *codes_mma, void *workspace,
+                          size_t workspace_bytes, void *stream) {
     clear_error();
     rq_status st = check_rotation(rot, true);
     if (st != RQ_OK) return st;
@@ -83,18 +94,24 @@ rq_status rq_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void 
     if (x_dtype != RQ_F32 && x_dtype != RQ_BF16)
         return fail(RQ_ERR_DTYPE, "X must be RQ_F32 or RQ_BF16");
     if (T < 0 || T >= (int64_t(1) << 31)) return fail(RQ_ERR_SHAPE, "T out of range");
-    if (T == 0) return RQ_OK;
-    if (!X || !codes || !scale) return fail(RQ_ERR_NULL, "X, codes and scale must not be NULL");
     const int K = rot->K;
     const bool dense = rot->kind == RQ_ROT_DENSE;
+    if (codes_mma && (dense || q->kind != RQ_Q_INT4_SYM))
+        return fail(RQ_ERR_UNSUPPORTED, "codes_mma is written for RPBH with INT4_SYM only");
+    if (T == 0) return RQ_OK;
+    if (!X || !scale || (!codes && !codes_mma))
+        return fail(RQ_ERR_NULL, "X, scale and at least one of codes / codes_mma must not be NULL");
+    if (dense && !codes) return fail(RQ_ERR_NULL, "DENSE needs codes");
+    if (q->kind != RQ_Q_INT4_SYM && !codes) return fail(RQ_ERR_NULL, "LLOYDMAX needs codes");
     if (dense && rot->r > 0 && !top) return fail(RQ_ERR_NULL, "DENSE with r > 0 needs top");
-    if (!aligned16(X) || !aligned16(codes) || !aligned16(scale) || (top && !aligned16(top)))
+    if (!aligned16(X) || (codes && !aligned16(codes)) || !aligned16(scale) ||
+        (top && !aligned16(top)) || (codes_mma && !aligned16(codes_mma)))
         return fail(RQ_ERR_ALIGN, "device buffers must be 16-byte aligned");
     const int xb = x_dtype == RQ_BF16 ? 1 : 0;
     if (!dense) {
         if (q->kind == RQ_Q_INT4_SYM)
             return hip_status(launch_rpbh_int4(X, xb, T, K, rot->block, rot->sign, rot->perm, codes,
-                                               scale, stream),
+                                               codes_mma, scale, stream),
                               "rotate_quant launch");
         float th[15];
         const int La = 1 << q->a_bits;
@@ -115,8 +132,8 @@ rq_status rq_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void 
 }
 
 rq_status rq_w4a4_linear(const rq_weight_header *hdr, const void *blob, const uint8_t *codes,
-                         const float *scale, const uint16_t *top, int64_t T, const float *bias,
-                         void *Y, int32_t y_dtype, void *stream) {
+                         const float *scale, const uint16_t *top, const uint8_t *codes_mma,
+                         int64_t T, const float *bias, void *Y, int32_t y_dtype, void *stream) {
     clear_error();
     rq_status st = check_header(hdr);
     if (st != RQ_OK) return st;
@@ -124,18 +141,25 @@ rq_status rq_w4a4_linear(const rq_weight_header *hdr, const void *blob, const ui
         return fail(RQ_ERR_DTYPE, "Y must be RQ_F32, RQ_BF16 or RQ_I32");
     if (y_dtype == RQ_I32 && hdr->format != RQ_Q_INT4_SYM)
         return fail(RQ_ERR_UNSUPPORTED, "raw accumulators exist for INT4 weights only");
+    if (codes_mma && (hdr->format != RQ_Q_INT4_SYM || hdr->r != 0))
+        return fail(RQ_ERR_UNSUPPORTED, "codes_mma is read for INT4 weights with r == 0 only");
     if (T < 0 || T >= (int64_t(1) << 31)) return fail(RQ_ERR_SHAPE, "T out of range");
     if (T == 0) return RQ_OK;
-    if (!blob || !codes || !scale || !Y) return fail(RQ_ERR_NULL, "blob, codes, scale and Y must not be NULL");
+    const bool int8 = hdr->format == RQ_Q_INT4_SYM && use_int8_gemm();
+    if (!blob || !scale || !Y || (!codes && !codes_mma) || (int8 && !codes))
+        return fail(RQ_ERR_NULL, "blob, scale, Y and the activation codes must not be NULL");
+    if (hdr->format != RQ_Q_INT4_SYM && !codes) return fail(RQ_ERR_NULL, "LLOYDMAX needs codes");
     if (hdr->r > 0 && !top) return fail(RQ_ERR_NULL, "weights with r > 0 need top");
-    if (!aligned16(blob) || !aligned16(codes) || !aligned16(scale) || !aligned16(Y) ||
-        (top && !aligned16(top)) || (bias && !aligned16(bias)))
+    if (!aligned16(blob) || (codes && !aligned16(codes)) || !aligned16(scale) || !aligned16(Y) ||
+        (top && !aligned16(top)) || (bias && !aligned16(bias)) ||
+        (codes_mma && !aligned16(codes_mma)))
         return fail(RQ_ERR_ALIGN, "device buffers must be 16-byte aligned");
     if (hdr->format == RQ_Q_INT4_SYM) {
-        if (use_int8_gemm())
+        if (int8)
             return hip_status(launch_gemm_w4a4(codes, scale, top, T, hdr, blob, bias, Y, y_dtype, stream),
                               "w4a4 int8 gemm launch");
-        return hip_status(launch_gemm_fp6(codes, scale, top, T, hdr, blob, bias, Y, y_dtype, stream),
+        return hip_status(launch_gemm_fp6(codes_mma ? nullptr : codes, codes_mma, scale, top, T, hdr,
+                                          blob, bias, Y, y_dtype, stream),
                           "w4a4 fp6 gemm launch");
     }
     return hip_status(launch_gemm_codebook(codes, scale, T, hdr, blob, bias, Y, y_dtype, stream),

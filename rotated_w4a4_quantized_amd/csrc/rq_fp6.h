@@ -1,0 +1,64 @@
+// rq_fp6.h -- device helpers shared by the kernels that produce and consume
+// INT4 codes in the GEMM's FP6 (E2M3) matrix-core layout.
+//
+// An E2M3 element (sign, 2 exponent bits with bias 1, 3 mantissa bits) whose
+// 6-bit code is an unsigned u < 16 decodes to u / 8 (codes 0..7 are the
+// subnormals m / 8, codes 8..15 have exponent 1 and decode to (8 + m) / 8).
+// An activation code q in [-7, 7] is carried as u = q + 8: the two's-
+// complement nibble with its top bit flipped.  Weights are carried
+// sign-magnitude ((q < 0) << 5 | |q|, i.e. q / 8), so with both block scales
+// at 2^3 the matrix core sums (qa + 8) qw exactly.
+//
+// "Codes in MMA layout" (rq_rotate_quant's codes_mma output): per token row,
+// one 96-byte block per 128 quantized coordinates (stage s, coordinates
+// 128 s .. 128 s + 127).  The block holds four 24-byte fragments, one per
+// (k-step ks, half h) over coordinates 128 s + 64 ks + 32 h + (0..31); the
+// fragments of half h are the twelve dwords f[0..11] (ks 0: f[0..5], ks 1:
+// f[6..11]) and dword f[d] sits at byte 32 (d / 4) + 16 h + 4 (d % 4) of the
+// block, so each 16-byte piece of the block is one direct-to-LDS load slot of
+// the GEMM.  Within a fragment, 6-bit field e at bits [6 e, 6 e + 6) holds
+// coordinate offset kFp6Order[e % 16] + 16 (e / 16) (to_fp6 below).
+#pragma once
+
+#include <stdint.h>
+
+namespace rq {
+
+constexpr int kMmaStageBytes = 96;   // MMA-layout bytes per 128 coordinates per row
+
+// 16 canonical nibble codes (a: offsets 0..7, b: offsets 8..15 of a group of
+// coordinates; low nibble = even offset) -> sixteen 6-bit fields holding
+// q + 8, in three dwords.  Field e takes offset
+// {0,1,3,4,6,7,9,10,12,13,15,8,2,11,5,14}[e]: with that order each field is
+// a nibble of a or b shifted by 0 or 2 bits, so three masks per output dword
+// do the spreading.
+__device__ __forceinline__ void to_fp6(uint32_t a, uint32_t b, uint32_t &d0, uint32_t &d1,
+                                       uint32_t &d2) {
+    a ^= 0x88888888u;
+    b ^= 0x88888888u;
+    const uint32_t a2 = a << 2, b2 = b << 2;
+    d0 = (a & 0x0F00F00Fu) | (a2 & 0xC03C03C0u);
+    d1 = (a >> 30) | (b & 0xF00F00F0u) | (b2 & 0x03C03C00u);
+    d2 = (a & 0x00F00F00u) | (b2 & 0x3C03C03Cu);
+}
+
+// Stores the 32 canonical codes of chunk c (coordinates 32 c .. 32 c + 31,
+// sixteen bytes w) of one token into that token's MMA-layout row.
+__device__ __forceinline__ void store_chunk_mma(uint8_t *row, int c, uint4 w) {
+    uint32_t d[6];
+    to_fp6(w.x, w.y, d[0], d[1], d[2]);
+    to_fp6(w.z, w.w, d[3], d[4], d[5]);
+    const int s = c >> 2, ks = (c >> 1) & 1, h = c & 1;
+    uint8_t *blk = row + s * kMmaStageBytes + 16 * h;
+    if (ks == 0) {
+        // dwords f[0..3] -> piece 0, f[4..5] -> first half of piece 1
+        *reinterpret_cast<uint4 *>(blk) = make_uint4(d[0], d[1], d[2], d[3]);
+        *reinterpret_cast<uint2 *>(blk + 32) = make_uint2(d[4], d[5]);
+    } else {
+        // dwords f[6..7] -> second half of piece 1, f[8..11] -> piece 2
+        *reinterpret_cast<uint2 *>(blk + 40) = make_uint2(d[0], d[1]);
+        *reinterpret_cast<uint4 *>(blk + 64) = make_uint4(d[2], d[3], d[4], d[5]);
+    }
+}
+
+}  // namespace rq

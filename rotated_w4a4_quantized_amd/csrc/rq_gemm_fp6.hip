@@ -47,6 +47,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "rq_fp6.h"
 #include "rq_internal.h"
 
 namespace rq {
@@ -60,7 +61,9 @@ constexpr int kActStageBytes = 64;      // nibble bytes per token row per stage
 constexpr uint32_t kScale2p3 = 130u * 0x01010101u;   // E8M0 2^3 in every byte
 
 struct Fp6Args {
-    const uint8_t *A;      // activation codes [T][lda]
+    const uint8_t *A;      // activation codes [T][lda] (canonical nibbles)
+    const uint8_t *Amma;   // activation codes in FP6 fragment layout [T][ldm], or null
+    int64_t ldm;           // bytes per MMA-layout activation row
     const uint8_t *Bmma;   // weight fragments [ntiles][S][3][64][16]
     const uint8_t *Bcan;   // canonical weight codes [N][ldb] (low-rank part)
     const float *sa;       // [T]
@@ -83,20 +86,6 @@ struct Fp6Args {
 
 __device__ inline void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// 16 canonical nibble codes (a: k 0..7, b: k 8..15 of a group) -> sixteen
-// 6-bit fields holding q + 8, in three dwords.  Field f takes canonical
-// offset {0,1,3,4,6,7,9,10,12,13,15,8,2,11,5,14}[f]: with that order each
-// field is a nibble of a or b shifted by 0 or 2 bits, so three masks per
-// output dword do the spreading.
-__device__ inline void to_fp6(uint32_t a, uint32_t b, uint32_t &d0, uint32_t &d1, uint32_t &d2) {
-    a ^= 0x88888888u;
-    b ^= 0x88888888u;
-    const uint32_t a2 = a << 2, b2 = b << 2;
-    d0 = (a & 0x0F00F00Fu) | (a2 & 0xC03C03C0u);
-    d1 = (a >> 30) | (b & 0xF00F00F0u) | (b2 & 0x03C03C00u);
-    d2 = (a & 0x00F00F00u) | (b2 & 0x3C03C03Cu);
 }
 
 __device__ inline uint32_t bf16_rne_bits(float x) {
@@ -279,10 +268,13 @@ gemm_fp6_kernel(Fp6Args a) {
     const uint32_t woff = lane * 16;
     const int nstage = a.S;
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-    auto issue = [&](int s, int buf) {
+    // loads d0 .. d1 - 1 of this wave's IPW loads for stage s into buffer buf
+    // (activation loads first, then weight loads)
+    auto issue_range = [&](int s, int buf, int d0, int d1) {
         const uint32_t lb = lds_base + buf * C::LDS_STAGE;
 #pragma unroll
         for (int i = 0; i < C::NA; ++i) {
+            if (i < d0 || i >= d1) continue;
             const uint32_t dst = __builtin_amdgcn_readfirstlane(lb + (wave * C::NA + i) * 1024);
             if constexpr (TAIL) {
                 // a chunk past the end of the row reads sixteen zero bytes
@@ -292,11 +284,12 @@ gemm_fp6_kernel(Fp6Args a) {
                                        : abase + aoff[i] + (int64_t)s * kActStageBytes;
                 dma16_v(p, dst);
             } else {
-                dma16_s(abase + (int64_t)s * kActStageBytes, aoff[i], dst);
+                dma16_s(uniform_ptr(abase + (int64_t)s * kActStageBytes), aoff[i], dst);
             }
         }
 #pragma unroll
         for (int i = 0; i < C::NB; ++i) {
+            if (C::NA + i < d0 || C::NA + i >= d1) continue;
             const int q = wave * C::NB + i;
             int nt = n0 / 32 + q / 3;
             if (nt >= a.ntiles) nt = a.ntiles - 1;
@@ -304,16 +297,11 @@ gemm_fp6_kernel(Fp6Args a) {
             dma16_s(src, woff, __builtin_amdgcn_readfirstlane(lb + C::ACT_STAGE + q * 1024));
         }
     };
+    auto issue = [&](int s, int buf) { issue_range(s, buf, 0, C::IPW); };
     // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding)
     auto wait_vm = [](auto nc) {
         constexpr int n = decltype(nc)::value;
         __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
-    };
-    constexpr int D = C::NBUF - 1;
-    auto wait_pending = [&](int pending) {
-        if constexpr (D >= 3) if (pending >= 2) { wait_vm(std::integral_constant<int, 2 * C::IPW>()); return; }
-        if constexpr (D >= 2) if (pending >= 1) { wait_vm(std::integral_constant<int, C::IPW>()); return; }
-        wait_vm(std::integral_constant<int, 0>());
     };
 
     v16f acc[C::FN][C::FT];
@@ -324,57 +312,113 @@ gemm_fp6_kernel(Fp6Args a) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    for (int p = 0; p < D && p < nstage; ++p) issue(p, p);
-    wait_pending((nstage < D ? nstage : D) - 1);
-    lds_barrier();
-
-    int buf = 0;
-    for (int s = 0; s < nstage; ++s) {
-        if (s + D < nstage) issue(s + D, buf == 0 ? D : buf - 1);
-        const uint8_t *L = lds + buf * C::LDS_STAGE;
-        const uint8_t *LW = L + C::ACT_STAGE + wn * C::FN * 3 * 1024 + lane * 16;
-        const uint8_t *LA = L + wt * C::FT * 2 * 1024 + lane * 16;
-        // k-step 0 uses weight parts 0 and 1.xy, k-step 1 parts 1.zw and 2
-        uint4 w0[C::FN], w1[C::FN];
+    // Fragments of one stage: part 0 and 1 of every weight fragment plus the
+    // k-step-0 activation chunks (R0), part 2 plus the k-step-1 chunks (R1).
+    // k-step 0 multiplies parts 0 and 1.xy, k-step 1 parts 1.zw and 2.
+    struct R0t { uint4 w0[C::FN], w1[C::FN], a[C::FT]; };
+    struct R1t { uint4 w2[C::FN], a[C::FT]; };
+    const uint8_t *LWb = lds + C::ACT_STAGE + wn * C::FN * 3 * 1024 + lane * 16;
+    const uint8_t *LAb = lds + wt * C::FT * 2 * 1024 + lane * 16;
+    auto read_r0 = [&](int b, R0t &r) {
+#pragma unroll
+        for (int j = 0; j < C::FT; ++j)
+            r.a[j] = *reinterpret_cast<const uint4 *>(LAb + b * C::LDS_STAGE + (j * 2 + 0) * 1024);
 #pragma unroll
         for (int i = 0; i < C::FN; ++i) {
-            w0[i] = *reinterpret_cast<const uint4 *>(LW + (i * 3 + 0) * 1024);
-            w1[i] = *reinterpret_cast<const uint4 *>(LW + (i * 3 + 1) * 1024);
+            r.w0[i] = *reinterpret_cast<const uint4 *>(LWb + b * C::LDS_STAGE + (i * 3 + 0) * 1024);
+            r.w1[i] = *reinterpret_cast<const uint4 *>(LWb + b * C::LDS_STAGE + (i * 3 + 1) * 1024);
         }
+    };
+    auto read_r1 = [&](int b, R1t &r) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            v8i bt[C::FT];
+        for (int j = 0; j < C::FT; ++j)
+            r.a[j] = *reinterpret_cast<const uint4 *>(LAb + b * C::LDS_STAGE + (j * 2 + 1) * 1024);
 #pragma unroll
-            for (int j = 0; j < C::FT; ++j) {
-                const uint4 an = *reinterpret_cast<const uint4 *>(LA + (j * 2 + ks) * 1024);
-                uint32_t d0, d1, d2, d3, d4, d5;
-                to_fp6(an.x, an.y, d0, d1, d2);
-                to_fp6(an.z, an.w, d3, d4, d5);
-                bt[j] = v8i{(int)d0, (int)d1, (int)d2, (int)d3, (int)d4, (int)d5, 0, 0};
-            }
+        for (int i = 0; i < C::FN; ++i)
+            r.w2[i] = *reinterpret_cast<const uint4 *>(LWb + b * C::LDS_STAGE + (i * 3 + 2) * 1024);
+    };
+    auto convert = [&](const uint4 (&an)[C::FT], v8i (&bt)[C::FT]) {
 #pragma unroll
-            for (int i = 0; i < C::FN; ++i) {
-                v8i wa;
-                if (ks == 0) {
-                    wa = v8i{(int)w0[i].x, (int)w0[i].y, (int)w0[i].z, (int)w0[i].w,
-                             (int)w1[i].x, (int)w1[i].y, 0, 0};
-                } else {
-                    const uint4 w2 = *reinterpret_cast<const uint4 *>(LW + (i * 3 + 2) * 1024);
-                    wa = v8i{(int)w1[i].z, (int)w1[i].w, (int)w2.x, (int)w2.y, (int)w2.z, (int)w2.w, 0, 0};
-                }
-#pragma unroll
-                for (int j = 0; j < C::FT; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        wa, bt[j], acc[i][j], 2, 2, 0, (int)kScale2p3, 0, (int)kScale2p3);
-            }
+        for (int j = 0; j < C::FT; ++j) {
+            uint32_t d0, d1, d2, d3, d4, d5;
+            to_fp6(an[j].x, an[j].y, d0, d1, d2);
+            to_fp6(an[j].z, an[j].w, d3, d4, d5);
+            bt[j] = v8i{(int)d0, (int)d1, (int)d2, (int)d3, (int)d4, (int)d5, 0, 0};
         }
-        {
-            const int last = (s + D < nstage ? s + D : nstage - 1);   // newest stage issued
-            wait_pending(last - (s + 1) > 0 ? last - (s + 1) : 0);
+    };
+    auto mfma_row = [&](int i, const v8i &wa, const v8i (&bt)[C::FT]) {
+#pragma unroll
+        for (int j = 0; j < C::FT; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                wa, bt[j], acc[i][j], 2, 2, 0, (int)kScale2p3, 0, (int)kScale2p3);
+    };
+
+    // Software pipeline over the NBUF = 3 LDS buffers, stage s in buffer
+    // s % 3.  Per stage: k-step 0 MFMAs; wait until stage s + 1 has landed
+    // and every wave is done reading buffer s % 3 (one barrier); read all
+    // fragments of stage s + 1 while the k-step 1 MFMAs run, and start the
+    // loads of stage s + 3 into buffer s % 3 between them.  So three stages
+    // of global loads are in flight and the LDS reads of a stage overlap the
+    // previous stage's MFMAs.
+    static_assert(C::NBUF == 3, "pipeline written for three buffers");
+    const int npre = nstage < 3 ? nstage : 3;
+    for (int p = 0; p < npre; ++p) issue(p, p);
+    if (npre == 3) wait_vm(std::integral_constant<int, 2 * C::IPW>());
+    else if (npre == 2) wait_vm(std::integral_constant<int, C::IPW>());
+    else wait_vm(std::integral_constant<int, 0>());
+    lds_barrier();
+    R0t r0;
+    R1t r1;
+    read_r0(0, r0);
+    read_r1(0, r1);
+
+    // One stage.  PF: issue the loads of stage s + 3; WAIT_IPW: at the
+    // mid-stage wait, this wave's loads of stage s + 2 may still be in
+    // flight.  Both compile-time, so the body is one basic block.
+    int b = 0;
+    auto stage = [&](int s, auto pf_c, auto wait_c) {
+        constexpr bool PF = decltype(pf_c)::value;
+        constexpr bool WAIT_IPW = decltype(wait_c)::value;
+        const int bn = b == 2 ? 0 : b + 1;
+        v8i bt0[C::FT], bt1[C::FT];
+        convert(r0.a, bt0);
+        // k-step 0
+#pragma unroll
+        for (int i = 0; i < C::FN; ++i) {
+            const v8i wa = v8i{(int)r0.w0[i].x, (int)r0.w0[i].y, (int)r0.w0[i].z, (int)r0.w0[i].w,
+                               (int)r0.w1[i].x, (int)r0.w1[i].y, 0, 0};
+            mfma_row(i, wa, bt0);
         }
+        convert(r1.a, bt1);
+        // stage s + 1 has landed (own loads, then every wave's), and every
+        // wave's reads of buffer b are complete
+        if constexpr (WAIT_IPW) wait_vm(std::integral_constant<int, C::IPW>());
+        else wait_vm(std::integral_constant<int, 0>());
         lds_barrier();
-        buf = buf == D ? 0 : buf + 1;
-    }
+        R0t r0n;
+        R1t r1n;
+        read_r0(bn, r0n);   // the last stage reads a stale buffer; never used
+        read_r1(bn, r1n);
+        // k-step 1, with the loads of stage s + 3 (into buffer b) between its MFMAs
+#pragma unroll
+        for (int i = 0; i < C::FN; ++i) {
+            const v8i wa = v8i{(int)r0.w1[i].z, (int)r0.w1[i].w, (int)r1.w2[i].x, (int)r1.w2[i].y,
+                               (int)r1.w2[i].z, (int)r1.w2[i].w, 0, 0};
+            mfma_row(i, wa, bt1);
+            if constexpr (PF) issue_range(s + 3, b, (i * C::IPW) / C::FN, ((i + 1) * C::IPW) / C::FN);
+        }
+        r0 = r0n;
+        r1 = r1n;
+        b = bn;
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    for (int s = 0; s + 3 < nstage; ++s) stage(s, T_{}, T_{});
+    // the last three stages: no further loads; at the wait of stage S - 3
+    // the loads of stage S - 1 may still be in flight
+    if (nstage >= 3) stage(nstage - 3, F_{}, T_{});
+    if (nstage >= 2) stage(nstage - 2, F_{}, F_{});
+    stage(nstage - 1, F_{}, F_{});
 
     // low-rank term (DENSE weights): lr[n][t] = sum_{j < r} qw[n][j] * bf16(top[t][j])
     v16f lr[HAS_LR ? C::FN : 1][HAS_LR ? C::FT : 1];
@@ -482,6 +526,253 @@ gemm_fp6_kernel(Fp6Args a) {
     });
 }
 
+// ---------------------------------------------------------------------------
+// The same GEMM on activations that rq_rotate_quant already wrote in the FP6
+// fragment layout (rq_fp6.h): no conversion, so the main loop is MFMAs, LDS
+// fragment reads and direct-to-LDS loads only (on gfx950 VALU work does not
+// overlap the FP6 matrix core, so every VALU instruction in the loop costs
+// MFMA time).  Both operands stream through LDS as [32 rows][3 pieces][64
+// lanes][16 B] per 128-coordinate stage; a lane's three pieces are the
+// twelve dwords of its k-step-0 and k-step-1 fragments, so the MFMA operands
+// are plain sub-ranges of the loaded registers.
+// ---------------------------------------------------------------------------
+template <int BT_, int BN_, int WT_, int WN_>
+struct MmaCfg {
+    static constexpr int BT = BT_, BN = BN_, WT = WT_, WN = WN_;
+    static constexpr int NW = WT * WN;
+    static constexpr int NTH = 64 * NW;
+    static constexpr int FT = BT / WT / 32;
+    static constexpr int FN = BN / WN / 32;
+    static constexpr int ACT_STAGE = BT / 32 * 3 * 1024;
+    static constexpr int W_STAGE = BN / 32 * 3 * 1024;
+    static constexpr int LDS_STAGE = ACT_STAGE + W_STAGE;
+    static constexpr int NA = BT / 32 * 3 / NW;   // activation loads per wave per stage
+    static constexpr int NB = BN / 32 * 3 / NW;   // weight loads per wave per stage
+    static constexpr int IPW = NA + NB;
+    static constexpr int OUT_STRIDE = BN * 2 + 16;
+    static constexpr int LDS_BYTES =
+        3 * LDS_STAGE > BT * OUT_STRIDE ? 3 * LDS_STAGE : BT * OUT_STRIDE;
+    static_assert(NA * NW == BT / 32 * 3 && NB * NW == BN / 32 * 3, "load split");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+};
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// one lane's three 16-byte pieces of a 32-row fragment pair
+struct Frag {
+    v4i p[3];
+};
+__device__ __forceinline__ v8i frag_k0(const Frag &f) {
+    const v8i lo = __builtin_shufflevector(f.p[0], f.p[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_shufflevector(lo, lo, 0, 1, 2, 3, 4, 5, -1, -1);
+}
+__device__ __forceinline__ v8i frag_k1(const Frag &f) {
+    const v8i hi = __builtin_shufflevector(f.p[1], f.p[2], 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_shufflevector(hi, hi, 2, 3, 4, 5, 6, 7, -1, -1);
+}
+// An empty asm that "redefines" the fragment: code that uses the result
+// cannot be scheduled above the asm, and the asm stays below the barrier
+// before it (volatile asm keeps its order).
+__device__ __forceinline__ void pin(Frag &f) {
+    asm volatile("" : "+v"(f.p[0]), "+v"(f.p[1]), "+v"(f.p[2]));
+}
+
+template <class C>
+__global__ void __launch_bounds__(C::NTH, 1)
+gemm_fp6_mma_kernel(Fp6Args a) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_BYTES];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wt = wave / C::WN, wn = wave % C::WN;
+    const int li = lane & 31, lg = lane >> 5;
+    int tile_t, tile_n;
+    tile_of(blockIdx.x, gridDim.x, a.tiles_t, a.tiles_n, tile_t, tile_n);
+    const int64_t t0 = (int64_t)tile_t * C::BT;
+    const int n0 = tile_n * C::BN;
+    const int nstage = a.S;
+
+    // Direct-to-LDS loads of this wave per stage: NA activation loads, then
+    // NB weight loads.  Activation load q = wave NA + i fills piece
+    // q % 3 of token fragment q / 3: lane l brings bytes 32 (q % 3) + 16 (l / 32)
+    // of the stage block of token t0 + 32 (q / 3) + l % 32 (rows past T read
+    // row T - 1, whose outputs are never stored).  Weight load q = wave NB + i
+    // copies piece q % 3 of weight tile n0 / 32 + q / 3 (1 KB, contiguous).
+    uint32_t aoff[C::NA];
+#pragma unroll
+    for (int i = 0; i < C::NA; ++i) {
+        const int q = wave * C::NA + i;
+        int64_t t = t0 + 32 * (q / 3) + li;
+        if (t >= a.T) t = a.T - 1;
+        aoff[i] = (uint32_t)((t - t0) * a.ldm + 16 * lg);
+    }
+    const uint8_t *abase = uniform_ptr(a.Amma + t0 * a.ldm);
+    const uint32_t woff = lane * 16;
+    const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+    auto issue = [&](int s, int buf) {
+        const uint32_t lb = lds_base + buf * C::LDS_STAGE;
+#pragma unroll
+        for (int i = 0; i < C::NA; ++i) {
+            const int q = wave * C::NA + i;
+            dma16_s(uniform_ptr(abase + (int64_t)s * kMmaStageBytes + 32 * (q % 3)), aoff[i],
+                    __builtin_amdgcn_readfirstlane(lb + q * 1024));
+        }
+#pragma unroll
+        for (int i = 0; i < C::NB; ++i) {
+            const int q = wave * C::NB + i;
+            int nt = n0 / 32 + q / 3;
+            if (nt >= a.ntiles) nt = a.ntiles - 1;
+            const uint8_t *src = uniform_ptr(a.Bmma + (((int64_t)nt * a.S + s) * 3 + q % 3) * 1024);
+            dma16_s(src, woff, __builtin_amdgcn_readfirstlane(lb + C::ACT_STAGE + q * 1024));
+        }
+    };
+    auto wait_vm = [](auto nc) {
+        constexpr int n = decltype(nc)::value;
+        __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+    };
+
+    v16f acc[C::FN][C::FT];
+#pragma unroll
+    for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FT; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    const uint8_t *LA = lds + wt * C::FT * 3 * 1024 + lane * 16;
+    const uint8_t *LW = lds + C::ACT_STAGE + wn * C::FN * 3 * 1024 + lane * 16;
+    auto rd = [](const uint8_t *p) {
+        Frag f;
+#pragma unroll
+        for (int part = 0; part < 3; ++part) f.p[part] = *reinterpret_cast<const v4i *>(p + part * 1024);
+        return f;
+    };
+    auto rd_act = [&](int buf, int j) { return rd(LA + buf * C::LDS_STAGE + j * 3 * 1024); };
+    auto rd_w = [&](int buf, int i) { return rd(LW + buf * C::LDS_STAGE + i * 3 * 1024); };
+    // the eight MFMAs of weight fragment i: both k-steps, all token fragments
+    auto mfma_frag = [&](auto ic, const Frag &w, const Frag (&act)[C::FT]) {
+        constexpr int i = decltype(ic)::value;
+        const v8i w0 = frag_k0(w), w1 = frag_k1(w);
+#pragma unroll
+        for (int j = 0; j < C::FT; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                w0, frag_k0(act[j]), acc[i][j], 2, 2, 0, (int)kScale2p3, 0, (int)kScale2p3);
+#pragma unroll
+        for (int j = 0; j < C::FT; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                w1, frag_k1(act[j]), acc[i][j], 2, 2, 0, (int)kScale2p3, 0, (int)kScale2p3);
+    };
+
+    // Three LDS buffers, stage s in buffer s % 3.  Within a stage the weight
+    // fragments are consumed one at a time with the next one's LDS read in
+    // flight; once every read of stage s has landed in registers, one
+    // barrier (also covering: this wave's loads of stage s + 1 complete)
+    // lets all waves read stage s + 1 -- issued before the last fragment's
+    // MFMAs, so their latency hides behind them -- and frees buffer s % 3
+    // for the loads of stage s + 3.
+    static_assert(C::FN == 4, "pipeline written for four weight fragments per wave");
+    const int npre = nstage < 3 ? nstage : 3;
+    for (int p = 0; p < npre; ++p) issue(p, p);
+    if (npre == 3) wait_vm(std::integral_constant<int, 2 * C::IPW>());
+    else if (npre == 2) wait_vm(std::integral_constant<int, C::IPW>());
+    else wait_vm(std::integral_constant<int, 0>());
+    lds_barrier();
+    Frag A[C::FT], W0, W1;
+#pragma unroll
+    for (int j = 0; j < C::FT; ++j) A[j] = rd_act(0, j);
+    W0 = rd_w(0, 0);
+    W1 = rd_w(0, 1);
+
+    int b = 0;
+    auto stage = [&](int s, auto pf_c, auto wait_c) {
+        constexpr bool PF = decltype(pf_c)::value;
+        constexpr bool WAIT_IPW = decltype(wait_c)::value;
+        const int bn = b == 2 ? 0 : b + 1;
+        const Frag W2 = rd_w(b, 2);
+        mfma_frag(std::integral_constant<int, 0>(), W0, A);
+        Frag W3 = rd_w(b, 3);
+        mfma_frag(std::integral_constant<int, 1>(), W1, A);
+        mfma_frag(std::integral_constant<int, 2>(), W2, A);
+        if constexpr (WAIT_IPW) wait_vm(std::integral_constant<int, C::IPW>());
+        else wait_vm(std::integral_constant<int, 0>());
+        lds_barrier();
+        pin(W3);
+        Frag An[C::FT];
+#pragma unroll
+        for (int j = 0; j < C::FT; ++j) An[j] = rd_act(bn, j);   // stale after the last stage; unused
+        const Frag W0n = rd_w(bn, 0), W1n = rd_w(bn, 1);
+        mfma_frag(std::integral_constant<int, 3>(), W3, A);
+        if constexpr (PF) issue(s + 3, b);
+#pragma unroll
+        for (int j = 0; j < C::FT; ++j) A[j] = An[j];
+        W0 = W0n;
+        W1 = W1n;
+        b = bn;
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    for (int s = 0; s + 3 < nstage; ++s) stage(s, T_{}, T_{});
+    if (nstage >= 3) stage(nstage - 3, F_{}, T_{});
+    if (nstage >= 2) stage(nstage - 2, F_{}, F_{});
+    stage(nstage - 1, F_{}, F_{});
+
+    // epilogue: full bf16 tiles staged through LDS (free after the last
+    // barrier once this wave's reads have landed), else the general path
+    constexpr int kOutStride = C::OUT_STRIDE;
+    if (a.ydt == RQ_BF16 && t0 + C::BT <= a.T && n0 + C::BN <= a.N && (a.N % 8) == 0 &&
+        a.bias == nullptr) {
+        lds_barrier();
+        static_for<C::FN>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            static_for<4>([&](auto qc) {
+                constexpr int q = decltype(qc)::value;
+                const int nl = wn * C::FN * 32 + i * 32 + 8 * q + 4 * lg;
+                const float4 sw4 = *reinterpret_cast<const float4 *>(a.sw + n0 + nl);
+                const int4 ws4 = *reinterpret_cast<const int4 *>(a.wsum + n0 + nl);
+                const float o0 = (float)(8 * ws4.x), o1 = (float)(8 * ws4.y);
+                const float o2 = (float)(8 * ws4.z), o3 = (float)(8 * ws4.w);
+                static_for<C::FT>([&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    const int tl = wt * C::FT * 32 + j * 32 + li;
+                    const float sat = a.sa[t0 + tl] * a.post;
+                    const float y0 = (acc[i][j][4 * q + 0] - o0) * (sat * sw4.x);
+                    const float y1 = (acc[i][j][4 * q + 1] - o1) * (sat * sw4.y);
+                    const float y2 = (acc[i][j][4 * q + 2] - o2) * (sat * sw4.z);
+                    const float y3 = (acc[i][j][4 * q + 3] - o3) * (sat * sw4.w);
+                    *reinterpret_cast<uint2 *>(lds + tl * kOutStride + 2 * nl) =
+                        make_uint2(bf16_rne_bits(y0) | (bf16_rne_bits(y1) << 16),
+                                   bf16_rne_bits(y2) | (bf16_rne_bits(y3) << 16));
+                });
+            });
+        });
+        lds_barrier();
+        constexpr int kChunksPerRow = C::BN * 2 / 16;
+        constexpr int kChunks = C::BT * kChunksPerRow;
+        for (int c = tid; c < kChunks; c += C::NTH) {
+            const int row = c / kChunksPerRow, cc = c % kChunksPerRow;
+            const uint4 v = *reinterpret_cast<const uint4 *>(lds + row * kOutStride + 16 * cc);
+            *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.Y) + (t0 + row) * a.N + n0 + 8 * cc) = v;
+        }
+        return;
+    }
+    static_for<C::FT>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        const int64_t t = t0 + wt * C::FT * 32 + j * 32 + li;
+        const bool t_ok = t < a.T;
+        const float sat = a.sa[t_ok ? t : a.T - 1];
+        static_for<C::FN>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            static_for<4>([&](auto qc) {
+                constexpr int q = decltype(qc)::value;
+                const int nb = n0 + wn * C::FN * 32 + i * 32 + 8 * q + 4 * lg;
+                const float lr4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                if (t_ok && nb < a.N)
+                    store4<false>(a, t, nb, sat, acc[i][j][4 * q + 0], acc[i][j][4 * q + 1],
+                                  acc[i][j][4 * q + 2], acc[i][j][4 * q + 3], lr4);
+            });
+        });
+    });
+}
+
 template <class C, bool HAS_LR>
 hipError_t launch_cfg(Fp6Args a, hipStream_t s) {
     a.tiles_t = (int)((a.T + C::BT - 1) / C::BT);
@@ -503,12 +794,14 @@ using CfgMid = Cfg<128, 128, 2, 2, 3, 2>;
 
 }  // namespace
 
-int launch_gemm_fp6(const uint8_t *codes, const float *scale, const uint16_t *top, int64_t T,
-                    const rq_weight_header *hdr, const void *blob, const float *bias, void *Y,
-                    int y_dtype, void *stream) {
+int launch_gemm_fp6(const uint8_t *codes, const uint8_t *codes_mma, const float *scale,
+                    const uint16_t *top, int64_t T, const rq_weight_header *hdr, const void *blob,
+                    const float *bias, void *Y, int y_dtype, void *stream) {
     Fp6Args a;
     const uint8_t *base = static_cast<const uint8_t *>(blob);
     a.A = codes;
+    a.Amma = codes_mma;
+    a.ldm = mma_row_bytes(hdr->K - hdr->r);
     a.Bmma = base + hdr->mma_offset;
     a.Bcan = base + hdr->codes_offset;
     a.sa = scale;
@@ -527,6 +820,14 @@ int launch_gemm_fp6(const uint8_t *codes, const float *scale, const uint16_t *to
     a.ydt = y_dtype;
     a.post = 1.0f / (float)hdr->b_div;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (codes_mma) {
+        // activations already in the FP6 fragment layout (RPBH, r == 0)
+        using C = MmaCfg<256, 256, 2, 2>;
+        a.tiles_t = (int)((T + C::BT - 1) / C::BT);
+        a.tiles_n = (a.N + C::BN - 1) / C::BN;
+        hipLaunchKernelGGL((gemm_fp6_mma_kernel<C>), dim3(a.tiles_t * a.tiles_n), dim3(C::NTH), 0, s, a);
+        return (int)hipGetLastError();
+    }
     if (a.r > 0) return (int)launch_cfg<CfgMid, true>(a, s);
     if (T >= 256 && hdr->N >= 256) return (int)launch_cfg<CfgBig, false>(a, s);
     return (int)launch_cfg<CfgMid, false>(a, s);

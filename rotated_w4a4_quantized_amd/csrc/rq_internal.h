@@ -20,12 +20,14 @@ rq_status check_quant(const rq_rotation *rot, const rq_quant *q);
 inline bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 inline int ilog2(int64_t v) { int l = 0; while ((int64_t(1) << l) < v) ++l; return l; }
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// bytes per token row of codes in the GEMM's FP6 fragment layout
+inline int64_t mma_row_bytes(int Kq) { return (int64_t)((Kq + 127) / 128) * 96; }
 
 // Kernel launchers (rq_rpbh.hip, rq_dense.hip, rq_gemm_*.hip).  Arguments are validated
 // by the caller; these only launch.  They return a hipError_t as int.
 int launch_rpbh_int4(const void *X, int x_bf16, int64_t T, int K, int block,
                      const int8_t *sign, const int32_t *perm, uint8_t *codes,
-                     float *scale, void *stream);
+                     uint8_t *codes_mma, float *scale, void *stream);
 int launch_rpbh_lloydmax(const void *X, int x_bf16, int64_t T, int K, int block,
                          const int8_t *sign, const int32_t *perm, const float *thresholds,
                          int n_thresholds, uint8_t *codes, float *sigma, void *stream);
@@ -36,9 +38,9 @@ int launch_dense_quant(const float *U, int64_t T, int K, int r, uint8_t *codes,
 int launch_gemm_w4a4(const uint8_t *codes, const float *scale, const uint16_t *top,
                      int64_t T, const rq_weight_header *hdr, const void *blob,
                      const float *bias, void *Y, int y_dtype, void *stream);
-int launch_gemm_fp6(const uint8_t *codes, const float *scale, const uint16_t *top,
-                    int64_t T, const rq_weight_header *hdr, const void *blob,
-                    const float *bias, void *Y, int y_dtype, void *stream);
+int launch_gemm_fp6(const uint8_t *codes, const uint8_t *codes_mma, const float *scale,
+                    const uint16_t *top, int64_t T, const rq_weight_header *hdr,
+                    const void *blob, const float *bias, void *Y, int y_dtype, void *stream);
 int launch_gemm_codebook(const uint8_t *codes, const float *sigma, int64_t T,
                          const rq_weight_header *hdr, const void *blob,
                          const float *bias, void *Y, int y_dtype, void *stream);

@@ -25,12 +25,14 @@
 //            squared norm) by shuffles and one LDS atomic per lane group;
 //   codes    nibbles are packed from registers, regrouped through LDS inside
 //            the wave into 16 contiguous bytes per thread, and stored with
-//            one 16-byte store.
+//            one 16-byte store (canonical layout) and/or spread into the
+//            GEMM's FP6 fragment layout (rq_fp6.h) with two stores.
 // Two workgroup barriers per token (three for the codebook).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "rq_fp6.h"
 #include "rq_internal.h"
 
 namespace rq {
@@ -151,7 +153,9 @@ struct RpbhArgs {
     int tpw;              // tokens per workgroup
     const int8_t *sign;
     const int32_t *perm;
-    uint8_t *codes;
+    uint8_t *codes;       // canonical [T][K/2], or null
+    uint8_t *codes_mma;   // FP6 fragment layout [T][mma_ld], or null (INT4 only)
+    int64_t mma_ld;       // bytes per MMA-layout row
     float *scale;
     float th[15];         // codebook thresholds (Lloyd-Max)
 };
@@ -342,7 +346,7 @@ rpbh_quant_kernel(RpbhArgs a) {
 
         // pack: register bit 0 carries index bit 0, so registers (2m, 2m + 1)
         // hold a nibble pair
-        uint8_t *crow = a.codes + tok * (int64_t)(K / 2);
+        uint4 chunk;
         if constexpr (Plan<L>::NP == 1) {
             uint32_t w[4];
 #pragma unroll
@@ -352,7 +356,7 @@ rpbh_quant_kernel(RpbhArgs a) {
                 for (int e = 0; e < 8; ++e) x |= (nib[8 * q + e] & 0xFu) << (4 * e);
                 w[q] = x;
             }
-            if (valid) *reinterpret_cast<uint4 *>(crow + 16 * tt) = make_uint4(w[0], w[1], w[2], w[3]);
+            chunk = make_uint4(w[0], w[1], w[2], w[3]);
         } else {
             uint8_t *p = cs + cpad<L>(pbase<L, PL>(tt) >> 1);
 #pragma unroll
@@ -363,10 +367,14 @@ rpbh_quant_kernel(RpbhArgs a) {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            const uint4 w = *reinterpret_cast<const uint4 *>(cs + cpad<L>(16 * tt));
-            if (valid) *reinterpret_cast<uint4 *>(crow + 16 * tt) = w;
+            chunk = *reinterpret_cast<const uint4 *>(cs + cpad<L>(16 * tt));
         }
-        if (valid && tt == 0) a.scale[tok] = sc;
+        if (valid) {
+            if (a.codes) *reinterpret_cast<uint4 *>(a.codes + tok * (int64_t)(K / 2) + 16 * tt) = chunk;
+            if constexpr (QK == 0)
+                if (a.codes_mma) store_chunk_mma(a.codes_mma + tok * a.mma_ld, tt, chunk);
+            if (tt == 0) a.scale[tok] = sc;
+        }
     }
 }
 
@@ -440,7 +448,7 @@ hipError_t dispatch(int L, RpbhArgs a, hipStream_t s) {
 }
 
 RpbhArgs make_args(const void *X, int64_t T, int K, const int8_t *sign, const int32_t *perm,
-                   uint8_t *codes, float *scale) {
+                   uint8_t *codes, uint8_t *codes_mma, float *scale) {
     RpbhArgs a;
     a.X = X;
     a.T = T;
@@ -450,6 +458,8 @@ RpbhArgs make_args(const void *X, int64_t T, int K, const int8_t *sign, const in
     a.sign = sign;
     a.perm = perm;
     a.codes = codes;
+    a.codes_mma = codes_mma;
+    a.mma_ld = (int64_t)((K + 127) / 128) * kMmaStageBytes;
     a.scale = scale;
     for (int i = 0; i < 15; ++i) a.th[i] = 0.0f;
     return a;
@@ -458,8 +468,9 @@ RpbhArgs make_args(const void *X, int64_t T, int K, const int8_t *sign, const in
 }  // namespace
 
 int launch_rpbh_int4(const void *X, int x_bf16, int64_t T, int K, int block, const int8_t *sign,
-                     const int32_t *perm, uint8_t *codes, float *scale, void *stream) {
-    RpbhArgs a = make_args(X, T, K, sign, perm, codes, scale);
+                     const int32_t *perm, uint8_t *codes, uint8_t *codes_mma, float *scale,
+                     void *stream) {
+    RpbhArgs a = make_args(X, T, K, sign, perm, codes, codes_mma, scale);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int L = ilog2(block);
     return (int)(x_bf16 ? dispatch<true, 0>(L, a, s) : dispatch<false, 0>(L, a, s));
@@ -469,7 +480,7 @@ int launch_rpbh_lloydmax(const void *X, int x_bf16, int64_t T, int K, int block,
                          const int8_t *sign, const int32_t *perm, const float *thresholds,
                          int n_thresholds, uint8_t *codes, float *sigma, void *stream) {
     if (n_thresholds != 15) return (int)hipErrorInvalidValue;
-    RpbhArgs a = make_args(X, T, K, sign, perm, codes, sigma);
+    RpbhArgs a = make_args(X, T, K, sign, perm, codes, nullptr, sigma);
     for (int i = 0; i < 15; ++i) a.th[i] = thresholds[i];
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int L = ilog2(block);

@@ -37,9 +37,14 @@ def quant_for(w) -> rq.Quant:
 
 class QuantLinear:
     """Device state of one layer instance (w: a datagen.Workload, inp: its
-    inputs): rotation, packed weights, buffers."""
+    inputs): rotation, packed weights, buffers.
 
-    def __init__(self, w, inp: dict, device="cuda", y_dtype=None):
+    codes: which activation-code layouts rq_rotate_quant writes and
+    rq_w4a4_linear reads -- "canonical" (nibbles), "mma" (the GEMM's FP6
+    fragment layout only; RPBH INT4 layers) or "both" (writes both, the GEMM
+    reads the MMA copy)."""
+
+    def __init__(self, w, inp: dict, device="cuda", y_dtype=None, codes="canonical"):
         torch = torch_mod()
         self.w, self.inp, self.device = w, inp, device
         self.rot = rotation_for(w, inp)
@@ -50,7 +55,15 @@ class QuantLinear:
         self.X = device_x(inp, device)
         T = w.T
         ncode = (w.Kq // 2)
-        self.codes = torch.empty((T, ncode), dtype=torch.uint8, device=device)
+        mma_ok = w.rot == "rpbh" and w.quant == "int4"
+        if codes not in ("canonical", "mma", "both") or (codes != "canonical" and not mma_ok):
+            raise ValueError(f"codes={codes!r} is not available for {w.name}")
+        self.codes = (torch.empty((T, ncode), dtype=torch.uint8, device=device)
+                      if codes != "mma" else None)
+        self.codes_mma = None
+        if codes != "canonical":
+            nb = rq.codes_mma_bytes(self.rot, T)
+            self.codes_mma = torch.empty((T, nb // max(T, 1)), dtype=torch.uint8, device=device)
         self.scale = torch.empty((T,), dtype=torch.float32, device=device)
         self.top = torch.empty((T, w.r), dtype=torch.int16, device=device) if w.r else None
         wsb = rq.rotate_quant_workspace_bytes(self.rot, self.q, T)
@@ -60,20 +73,21 @@ class QuantLinear:
 
     def rotate_quant(self, stream=None):
         rq.rotate_quant(self.drot, self.q, self.X, self.codes, self.scale, self.top, self.ws,
-                        stream=stream)
+                        stream=stream, codes_mma=self.codes_mma)
 
-    def linear(self, Y=None, stream=None):
+    def linear(self, Y=None, stream=None, use_mma=True):
         rq.w4a4_linear(self.dw, self.codes, self.scale, self.Y if Y is None else Y, top=self.top,
-                       stream=stream)
+                       stream=stream, T=self.w.T,
+                       codes_mma=self.codes_mma if use_mma else None)
 
     def run(self):
         self.rotate_quant()
         self.linear()
 
-    def raw_acc(self):
+    def raw_acc(self, use_mma=True):
         torch = torch_mod()
         acc = torch.empty((self.w.T, self.w.N), dtype=torch.int32, device=self.device)
-        self.linear(acc)
+        self.linear(acc, use_mma=use_mma)
         return acc
 
 

@@ -62,8 +62,8 @@ assert ctypes.sizeof(c_weight_header) == 256
 
 # every symbol include/rq.h declares
 EXPORTS = ("rq_version", "rq_last_error", "rq_lloydmax_gaussian", "rq_packed_weight_bytes",
-           "rq_pack_weights", "rq_rotate_quant_workspace_bytes", "rq_rotate_quant",
-           "rq_w4a4_linear")
+           "rq_pack_weights", "rq_rotate_quant_workspace_bytes", "rq_codes_mma_bytes",
+           "rq_rotate_quant", "rq_w4a4_linear")
 
 _lib = None
 
@@ -85,10 +85,12 @@ def load() -> ctypes.CDLL:
     L.rq_packed_weight_bytes.argtypes = [P, P, I32, ctypes.POINTER(SZ)]
     L.rq_pack_weights.argtypes = [P, P, P, I32, I32, P, SZ]
     L.rq_rotate_quant_workspace_bytes.argtypes = [P, P, I64, ctypes.POINTER(SZ)]
-    L.rq_rotate_quant.argtypes = [P, P, P, I32, I64, P, P, P, P, SZ, P]
-    L.rq_w4a4_linear.argtypes = [P, P, P, P, P, I64, P, P, I32, P]
+    L.rq_codes_mma_bytes.argtypes = [P, I64, ctypes.POINTER(SZ)]
+    L.rq_rotate_quant.argtypes = [P, P, P, I32, I64, P, P, P, P, P, SZ, P]
+    L.rq_w4a4_linear.argtypes = [P, P, P, P, P, P, I64, P, P, I32, P]
     for name in ("rq_lloydmax_gaussian", "rq_packed_weight_bytes", "rq_pack_weights",
-                 "rq_rotate_quant_workspace_bytes", "rq_rotate_quant", "rq_w4a4_linear"):
+                 "rq_rotate_quant_workspace_bytes", "rq_codes_mma_bytes", "rq_rotate_quant",
+                 "rq_w4a4_linear"):
         getattr(L, name).restype = I32
     _lib = L
     return L
@@ -310,20 +312,31 @@ def dtype_code(t) -> int:
             torch.uint16: RQ_BF16, torch.int32: RQ_I32}[t.dtype]
 
 
+def codes_mma_bytes(rot: Rotation, T: int) -> int:
+    n = ctypes.c_size_t(0)
+    cr = rot.c_host()
+    _check(load().rq_codes_mma_bytes(ctypes.byref(cr), T, ctypes.byref(n)))
+    return n.value
+
+
 def rotate_quant(drot: DeviceRotation, q: Quant, X, codes, scale, top=None, workspace=None,
-                 stream=None):
-    """Launch the activation kernels on `stream` (default: torch's current)."""
+                 stream=None, codes_mma=None):
+    """Launch the activation kernels on `stream` (default: torch's current).
+    codes and/or codes_mma (the GEMM's FP6 fragment layout) receive the codes."""
     cr, cq = drot.c_dev(), q.c()
     T = int(X.shape[0])
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().rq_rotate_quant(ctypes.byref(cr), ctypes.byref(cq), _t_ptr(X), dtype_code(X), T,
-                                  _t_ptr(codes), _t_ptr(scale), _t_ptr(top), _t_ptr(workspace),
-                                  ws_bytes, _stream(stream)))
+                                  _t_ptr(codes), _t_ptr(scale), _t_ptr(top), _t_ptr(codes_mma),
+                                  _t_ptr(workspace), ws_bytes, _stream(stream)))
 
 
-def w4a4_linear(dw: DeviceWeights, codes, scale, Y, top=None, bias=None, T=None, stream=None):
-    """Launch the low-bit GEMM; Y dtype picks the output (f32, bf16, raw int32)."""
-    T = int(codes.shape[0]) if T is None else T
+def w4a4_linear(dw: DeviceWeights, codes, scale, Y, top=None, bias=None, T=None, stream=None,
+                codes_mma=None):
+    """Launch the low-bit GEMM; Y dtype picks the output (f32, bf16, raw int32).
+    When codes_mma is given it is read instead of codes (which may be None)."""
+    if T is None:
+        T = int((codes if codes is not None else codes_mma).shape[0])
     _check(load().rq_w4a4_linear(ctypes.byref(dw.header), _t_ptr(dw.blob), _t_ptr(codes),
-                                 _t_ptr(scale), _t_ptr(top), T, _t_ptr(bias), _t_ptr(Y),
-                                 dtype_code(Y), _stream(stream)))
+                                 _t_ptr(scale), _t_ptr(top), _t_ptr(codes_mma), T, _t_ptr(bias),
+                                 _t_ptr(Y), dtype_code(Y), _stream(stream)))

@@ -85,3 +85,55 @@ def bf16_check(y_bits, yhat):
 def to_np_bf16_bits(t):
     torch = torch_mod()
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+FP6_ORDER = np.array([0, 1, 3, 4, 6, 7, 9, 10, 12, 13, 15, 8, 2, 11, 5, 14])
+
+
+def decode_codes_mma(buf, Kq):
+    """INT4 codes [T][Kq] (int8) from rq_rotate_quant's codes_mma output, read
+    as rq.h documents it: per token one 96-byte block per 128 coordinates;
+    half h of a block is the dwords f[0..11], f[d] at byte 32 (d // 4) +
+    16 h + 4 (d % 4); k-step ks is f[6 ks .. 6 ks + 5], 6-bit field e holding
+    (q + 8) for coordinate 128 s + 64 ks + 32 h + order[e % 16] + 16 (e // 16).
+    Also returns whether every field of a coordinate below Kq had its two
+    top bits clear."""
+    buf = np.ascontiguousarray(buf, np.uint8)
+    T = buf.shape[0]
+    S = -(-Kq // 128)
+    blk = buf.reshape(T, S, 96).view(np.uint32).reshape(T, S, 3, 2, 4)   # [piece][h][dword]
+    f = blk.transpose(0, 1, 3, 2, 4).reshape(T, S, 2, 12).astype(np.uint64)  # [h][f0..f11]
+    q = np.zeros((T, S, 2, 2, 32), np.int16)   # [s][ks][h][field]
+    top = np.zeros((T, S, 2, 2, 32), bool)
+    for ks in range(2):
+        d = f[:, :, :, 6 * ks:6 * ks + 6]
+        for e in range(32):
+            w, off = divmod(6 * e, 32)
+            v = d[..., w] >> np.uint64(off)
+            if off > 26:
+                v = v | (d[..., w + 1] << np.uint64(32 - off))
+            v = (v & np.uint64(63)).astype(np.int16)
+            top[:, :, ks, :, e] = (v & 48) != 0
+            q[:, :, ks, :, e] = (v & 15) - 8
+    k_of = np.zeros((2, 2, 32), np.int64)
+    for ks in range(2):
+        for h in range(2):
+            for e in range(32):
+                k_of[ks, h, e] = 64 * ks + 32 * h + FP6_ORDER[e % 16] + 16 * (e // 16)
+    out = np.zeros((T, S * 128), np.int16)
+    tops = np.zeros((T, S * 128), bool)
+    for s_ in range(S):
+        out[:, 128 * s_ + k_of.reshape(-1)] = q[:, s_].reshape(T, -1)
+        tops[:, 128 * s_ + k_of.reshape(-1)] = top[:, s_].reshape(T, -1)
+    # fields past Kq are never written: only the real coordinates count
+    return out[:, :Kq], not tops[:, :Kq].any()
+
+
+def unpack_codes(codes):
+    """Canonical nibbles [T][Kq/2] -> INT4 codes [T][Kq]."""
+    codes = np.asarray(codes, np.uint8)
+    lo = (codes & 15).astype(np.int16)
+    hi = (codes >> 4).astype(np.int16)
+    q = np.stack([lo, hi], -1).reshape(codes.shape[0], -1)
+    return np.where(q >= 8, q - 16, q)
+

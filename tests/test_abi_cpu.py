@@ -48,11 +48,13 @@ def _status(fn, *args):
 
 
 def _rq_call(rot: rq.c_rotation, q: rq.c_quant, X=1 << 20, xdt=rq.RQ_BF16, T=4, codes=1 << 20,
-             scale=1 << 20, top=None, ws=None, wsb=0):
+             scale=1 << 20, top=None, ws=None, wsb=0, mma=None):
     L = rq.load()
     return L.rq_rotate_quant(ctypes.byref(rot), ctypes.byref(q), ctypes.c_void_p(X), xdt, T,
-                             ctypes.c_void_p(codes), ctypes.c_void_p(scale),
+                             None if codes is None else ctypes.c_void_p(codes),
+                             ctypes.c_void_p(scale),
                              None if top is None else ctypes.c_void_p(top),
+                             None if mma is None else ctypes.c_void_p(mma),
                              None if ws is None else ctypes.c_void_p(ws), wsb, None)
 
 
@@ -88,6 +90,26 @@ def test_rotate_quant_validation_errors():
     assert _rq_call(_rpbh(), lm) == -2      # levels not ascending
     lm = rq.Quant.lloydmax(np.linspace(-2, 2, 16).astype(np.float32), np.arange(4, dtype=np.float32)).c()
     assert _rq_call(_rpbh(), lm) == -2      # levels not bf16-representable
+    # the MMA-layout copy of the codes: RPBH INT4 only, aligned, one of the two outputs
+    assert _rq_call(_rpbh(), q, codes=None, mma=None) == -1
+    assert _rq_call(_rpbh(), q, codes=None, mma=(1 << 22) + 8) == -4
+    dense = rq.c_rotation(rq.RQ_ROT_DENSE, 256, 0, 32, None, None, 1 << 22)
+    assert _rq_call(dense, q, top=1 << 23, ws=1 << 24, wsb=1 << 30, mma=1 << 22) == -6
+    lm = rq.Quant.lloydmax(rq.lloydmax_gaussian(16), rq.lloydmax_gaussian(4)).c()
+    assert _rq_call(_rpbh(), lm, mma=1 << 22) == -6
+
+
+def test_codes_mma_bytes():
+    def nbytes(rot, T):
+        n = ctypes.c_size_t(0)
+        assert rq.load().rq_codes_mma_bytes(ctypes.byref(rot), T, ctypes.byref(n)) == 0
+        return n.value
+    assert nbytes(_rpbh(256, 64), 4) == 4 * 2 * 96
+    assert nbytes(_rpbh(96, 32), 3) == 3 * 1 * 96
+    assert nbytes(_rpbh(12288, 512), 2) == 2 * 96 * 96
+    assert nbytes(rq.c_rotation(rq.RQ_ROT_DENSE, 1152, 0, 32, None, None, 1 << 22), 5) == 5 * 9 * 96
+    n = ctypes.c_size_t(0)
+    assert rq.load().rq_codes_mma_bytes(ctypes.byref(_rpbh(100, 4)), 1, ctypes.byref(n)) == -2
 
 
 def test_empty_token_batch_is_a_no_op():
@@ -95,7 +117,7 @@ def test_empty_token_batch_is_a_no_op():
     assert _rq_call(_rpbh(), rq.Quant.int4().c(), T=0, X=0, codes=0, scale=0) == 0
     hdr = _small_header()
     L = rq.load()
-    assert L.rq_w4a4_linear(ctypes.byref(hdr), None, None, None, None, 0, None, None,
+    assert L.rq_w4a4_linear(ctypes.byref(hdr), None, None, None, None, None, 0, None, None,
                             rq.RQ_F32, None) == 0
 
 
@@ -109,9 +131,11 @@ def _small_header():
 def test_linear_validation_errors():
     L = rq.load()
     hdr = _small_header()
-    args = lambda h, ydt=rq.RQ_F32, Y=1 << 24: (ctypes.byref(h), ctypes.c_void_p(1 << 20),
-                                                ctypes.c_void_p(1 << 21), ctypes.c_void_p(1 << 22),
-                                                None, 4, None, ctypes.c_void_p(Y), ydt, None)
+    def args(h, ydt=rq.RQ_F32, Y=1 << 24, codes=1 << 21, mma=None):
+        return (ctypes.byref(h), ctypes.c_void_p(1 << 20),
+                None if codes is None else ctypes.c_void_p(codes), ctypes.c_void_p(1 << 22),
+                None, None if mma is None else ctypes.c_void_p(mma), 4, None, ctypes.c_void_p(Y),
+                ydt, None)
     bad = rq.c_weight_header.from_buffer_copy(bytes(hdr))
     bad.magic = 0
     assert L.rq_w4a4_linear(*args(bad)) == -5
@@ -123,7 +147,14 @@ def test_linear_validation_errors():
     assert L.rq_w4a4_linear(*args(bad)) == -5
     assert L.rq_w4a4_linear(*args(hdr, ydt=9)) == -3
     assert L.rq_w4a4_linear(*args(hdr, Y=(1 << 24) + 4)) == -4
-    assert L.rq_w4a4_linear(None, None, None, None, None, 1, None, None, 0, None) == -1
+    assert L.rq_w4a4_linear(None, None, None, None, None, None, 1, None, None, 0, None) == -1
+    assert L.rq_w4a4_linear(*args(hdr, codes=None)) == -1
+    assert L.rq_w4a4_linear(*args(hdr, codes=None, mma=(1 << 23) + 4)) == -4
+    # the MMA-layout codes are read for r == 0 only
+    w = datagen.WORKLOADS["pixart"].with_shape(T=4, K=256, N=40)
+    inp = datagen.make_inputs(w)
+    dh = rq.pack_weights(rq.Rotation.dense(inp["R"], w.r), rq.Quant.int4(), inp["W"]).header
+    assert L.rq_w4a4_linear(*args(dh, mma=1 << 23)) == -6
 
 
 def test_lloydmax_codebook_matches_oracle():

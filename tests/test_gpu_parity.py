@@ -33,6 +33,12 @@ def say(msg):
     sys.stdout.flush()
 
 
+def mma_mode(w):
+    """Layer mode for the parity runs: RPBH INT4 layers write both code
+    layouts and the GEMM reads the MMA copy."""
+    return "both" if (w.rot == "rpbh" and w.quant == "int4") else "canonical"
+
+
 def check_act(w, L, act, rows=None):
     codes = L.codes.cpu().numpy()
     scale = L.scale.cpu().numpy()
@@ -42,6 +48,15 @@ def check_act(w, L, act, rows=None):
         f"scale mismatch in {int(np.sum(scale != act['scale']))} tokens"
     bad = np.nonzero(np.any(codes != act["codes"], axis=1))[0]
     assert bad.size == 0, f"codes differ in {bad.size} tokens, first {bad[:5]}"
+    if L.codes_mma is not None:
+        mma = L.codes_mma.cpu().numpy()
+        if rows is not None:
+            mma = mma[rows]
+        dec, top_clear = H.decode_codes_mma(mma, w.Kq)
+        assert top_clear, "a codes_mma field has its top bits set"
+        ref = H.unpack_codes(act["codes"])
+        bad = np.nonzero(np.any(dec != ref, axis=1))[0]
+        assert bad.size == 0, f"codes_mma differs in {bad.size} tokens, first {bad[:5]}"
     if w.r:
         top = L.top.cpu().numpy().view(np.uint16)
         if rows is not None:
@@ -69,7 +84,7 @@ def test_small_full_parity(name, shape):
     w = datagen.WORKLOADS[name].with_shape(**shape)
     say(f"[parity small] {w}")
     inp = datagen.make_inputs(w)
-    L = H.GpuLayer(w, inp, y_dtype="f32")
+    L = H.GpuLayer(w, inp, y_dtype="f32", codes=mma_mode(w))
     L.run()
     torch.cuda.synchronize()
     act = H.oracle_act(w, inp)
@@ -84,10 +99,19 @@ def test_small_full_parity(name, shape):
     say(f"  fp32 output max floored rel err {err:.3e}")
     assert err <= H.REL_TOL
     if w.quant == "int4":
-        acc = L.raw_acc().cpu().numpy().astype(np.int64)
         import oracle.oracle as orc
         ref = orc.int_gemm(act["codes"], w.Kq, wts["codes"], w.K, koff=w.r)
+        acc = L.raw_acc().cpu().numpy().astype(np.int64)
         assert np.array_equal(acc, ref)
+        if L.codes_mma is not None:
+            # the same accumulators from the canonical codes (converted in the GEMM)
+            acc = L.raw_acc(use_mma=False).cpu().numpy().astype(np.int64)
+            assert np.array_equal(acc, ref)
+            Yc = torch.empty((w.T, w.N), dtype=torch.float32, device="cuda")
+            L.linear(Yc, use_mma=False)
+            err = H.rel_err(Yc.cpu().numpy().ravel(), yhat)
+            say(f"  fp32 output (canonical-code GEMM) max floored rel err {err:.3e}")
+            assert err <= H.REL_TOL
     # bf16 output of the same kernels
     Yb = torch.empty((w.T, w.N), dtype=torch.bfloat16, device="cuda")
     L.linear(Yb)
@@ -104,7 +128,7 @@ def test_full_workload_parity(name):
     w = datagen.WORKLOADS[name]
     say(f"[parity full] {w}")
     inp = datagen.make_inputs(w)
-    L = H.GpuLayer(w, inp)
+    L = H.GpuLayer(w, inp, codes=mma_mode(w))
     L.run()
     torch.cuda.synchronize()
     g = np.random.default_rng(7)
@@ -180,6 +204,19 @@ def test_outputs_stay_in_bounds():
     assert bool((codes[w.T * w.K // 2:] == 0xA5).all())
     assert bool((scale[w.T:] == 7.5).all())
     assert bool((Y[w.T * w.N:] == 3.25).all())
+    # the MMA-layout codes and the GEMM that reads them (K = 1152: a ragged
+    # last 128-coordinate block)
+    M = H.GpuLayer(w, inp, y_dtype="f32", codes="mma")
+    nb = M.codes_mma.numel()
+    mma = torch.full((nb + G,), 0x5A, dtype=torch.uint8, device="cuda")
+    Y2 = torch.full((w.T * w.N + G,), 3.25, dtype=torch.float32, device="cuda")
+    M.codes_mma = mma[:nb].view(w.T, nb // w.T)
+    M.rotate_quant()
+    M.linear(Y2[: w.T * w.N].view(w.T, w.N))
+    torch.cuda.synchronize()
+    assert bool((mma[nb:] == 0x5A).all())
+    assert bool((Y2[w.T * w.N:] == 3.25).all())
+    assert torch.equal(Y2[: w.T * w.N], Y[: w.T * w.N])
 
 
 def test_runs_on_a_side_stream():
@@ -194,3 +231,20 @@ def test_runs_on_a_side_stream():
         L.run()
     s.synchronize()
     assert torch.equal(ref, L.Y)
+
+
+def test_mma_codes_only_path():
+    # the bench configuration: rq_rotate_quant writes only the MMA-layout
+    # codes and the GEMM reads them; compared with a canonical-code run
+    w = datagen.WORKLOADS["flux_down"].with_shape(T=300, K=2048, N=520, block=512)
+    inp = datagen.make_inputs(w)
+    A = H.GpuLayer(w, inp, y_dtype="f32", codes="mma")
+    B = H.GpuLayer(w, inp, y_dtype="f32", codes="canonical")
+    A.run()
+    B.run()
+    accA = A.raw_acc().cpu().numpy()
+    accB = B.raw_acc().cpu().numpy()
+    torch.cuda.synchronize()
+    assert A.codes is None and np.array_equal(accA, accB)
+    assert torch.equal(A.scale, B.scale) and torch.equal(A.Y, B.Y)
+
