@@ -229,7 +229,8 @@ rq_status rq_rotate_quant_workspace_bytes(const rq_rotation *rot, const rq_quant
 
 /*
  * Bytes of a codes_mma buffer for T tokens (rq_rotate_quant's optional
- * output, rq_w4a4_linear's optional input): T * ceil((K - r) / 128) * 96.
+ * output, rq_w4a4_linear's optional input):
+ * ceil(T / 32) * ceil((K - r) / 128) * 3072.
  * Errors: RQ_ERR_NULL, RQ_ERR_SHAPE, RQ_ERR_UNSUPPORTED.
  */
 rq_status rq_codes_mma_bytes(const rq_rotation *rot, int64_t T, size_t *bytes);
@@ -264,11 +265,18 @@ rq_status rq_codes_mma_bytes(const rq_rotation *rot, int64_t T, size_t *bytes);
  *   top     device bf16 [T][r] for DENSE with r > 0, else NULL
  *   codes_mma  RPBH INT4_SYM only, optional: device buffer of
  *           rq_codes_mma_bytes() receiving the same codes in the low-bit
- *           GEMM's matrix-core layout.  Per token, one 96-byte block per 128
- *           coordinates; coordinate c of the block is carried as the 6-bit
- *           E2M3 value (q + 8) / 8 in one of four 24-byte fragments (the
- *           placement is fixed; rq_w4a4_linear is its only reader).  Bytes
- *           for coordinates past K are left unwritten.  NULL: not written.
+ *           GEMM's matrix-core layout (NULL: not written).  Tokens come in
+ *           tiles of 32 and coordinates in stages of 128; the buffer is
+ *           [tile][stage][piece 0..2][lane 0..63][16 bytes], 3 KB per tile
+ *           and stage.  Token t of a tile owns lanes t and t + 32 (half h);
+ *           its twelve dwords f[0..11] for half h of a stage are dword d % 4
+ *           of its lane in piece d / 4.  f[0..5] and f[6..11] are the 192-bit
+ *           fragments of coordinates 128 s + 64 ks + 32 h + (0..31) for
+ *           ks = 0, 1; bits [6 e, 6 e + 6) of a fragment hold the E2M3 code
+ *           q + 8 (value (q + 8) / 8, top two bits clear) of coordinate offset
+ *           {0,1,3,4,6,7,9,10,12,13,15,8,2,11,5,14}[e % 16] + 16 (e / 16).
+ *           Bytes of tokens past T and coordinates past K - r are left
+ *           unwritten.
  *   workspace, workspace_bytes  device scratch of at least
  *           rq_rotate_quant_workspace_bytes() (NULL/0 when that is 0)
  *   stream  hipStream_t

@@ -79,7 +79,7 @@ rq_status rq_codes_mma_bytes(const rq_rotation *rot, int64_t T, size_t *bytes) {
     if (st != RQ_OK) return st;
     if (!bytes) return fail(RQ_ERR_NULL, "bytes is NULL");
     if (T < 0 || T >= (int64_t(1) << 31)) return fail(RQ_ERR_SHAPE, "T out of range");
-    *bytes = (size_t)T * (size_t)mma_row_bytes(rot->K - rot->r);
+    *bytes = (size_t)mma_codes_bytes(T, rot->K - rot->r);
     return RQ_OK;
 }
 

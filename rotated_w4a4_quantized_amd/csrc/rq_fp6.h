@@ -9,22 +9,26 @@
 // sign-magnitude ((q < 0) << 5 | |q|, i.e. q / 8), so with both block scales
 // at 2^3 the matrix core sums (qa + 8) qw exactly.
 //
-// "Codes in MMA layout" (rq_rotate_quant's codes_mma output): per token row,
-// one 96-byte block per 128 quantized coordinates (stage s, coordinates
-// 128 s .. 128 s + 127).  The block holds four 24-byte fragments, one per
-// (k-step ks, half h) over coordinates 128 s + 64 ks + 32 h + (0..31); the
-// fragments of half h are the twelve dwords f[0..11] (ks 0: f[0..5], ks 1:
-// f[6..11]) and dword f[d] sits at byte 32 (d / 4) + 16 h + 4 (d % 4) of the
-// block, so each 16-byte piece of the block is one direct-to-LDS load slot of
-// the GEMM.  Within a fragment, 6-bit field e at bits [6 e, 6 e + 6) holds
-// coordinate offset kFp6Order[e % 16] + 16 (e / 16) (to_fp6 below).
+// "Codes in MMA layout" (rq_rotate_quant's codes_mma output): tokens in
+// tiles of 32, and per tile one 3 KB block per 128 quantized coordinates
+// (stage s, coordinates 128 s .. 128 s + 127), laid out
+// [tile][stage][piece 0..2][lane 0..63][16 bytes] -- the layout of the
+// weight blob's FP6 section, so that every 1 KB piece is one contiguous
+// direct-to-LDS load of the GEMM.  Token t of the tile sits in lanes t and
+// t + 32 (half h = 0, 1).  Half h of a token's stage holds four 24-byte
+// fragments, one per (k-step ks, half h) over coordinates
+// 128 s + 64 ks + 32 h + (0..31), as twelve dwords f[0..11] (ks 0: f[0..5],
+// ks 1: f[6..11]); dword f[d] is dword d % 4 of the 16 bytes of lane
+// t + 32 h in piece d / 4.  Within a fragment, 6-bit field e at bits
+// [6 e, 6 e + 6) holds coordinate offset kFp6Order[e % 16] + 16 (e / 16)
+// (to_fp6 below).
 #pragma once
 
 #include <stdint.h>
 
 namespace rq {
 
-constexpr int kMmaStageBytes = 96;   // MMA-layout bytes per 128 coordinates per row
+constexpr int kMmaTileStageBytes = 3 * 1024;   // per 32 tokens per 128 coordinates
 
 // 16 canonical nibble codes (a: offsets 0..7, b: offsets 8..15 of a group of
 // coordinates; low nibble = even offset) -> sixteen 6-bit fields holding
@@ -43,21 +47,21 @@ __device__ __forceinline__ void to_fp6(uint32_t a, uint32_t b, uint32_t &d0, uin
 }
 
 // Stores the 32 canonical codes of chunk c (coordinates 32 c .. 32 c + 31,
-// sixteen bytes w) of one token into that token's MMA-layout row.
-__device__ __forceinline__ void store_chunk_mma(uint8_t *row, int c, uint4 w) {
+// sixteen bytes w) of token t into the MMA-layout buffer of S stages.
+__device__ __forceinline__ void store_chunk_mma(uint8_t *mma, int64_t t, int S, int c, uint4 w) {
     uint32_t d[6];
     to_fp6(w.x, w.y, d[0], d[1], d[2]);
     to_fp6(w.z, w.w, d[3], d[4], d[5]);
     const int s = c >> 2, ks = (c >> 1) & 1, h = c & 1;
-    uint8_t *blk = row + s * kMmaStageBytes + 16 * h;
+    uint8_t *blk = mma + ((t >> 5) * S + s) * (int64_t)kMmaTileStageBytes + (((int)t & 31) + 32 * h) * 16;
     if (ks == 0) {
         // dwords f[0..3] -> piece 0, f[4..5] -> first half of piece 1
         *reinterpret_cast<uint4 *>(blk) = make_uint4(d[0], d[1], d[2], d[3]);
-        *reinterpret_cast<uint2 *>(blk + 32) = make_uint2(d[4], d[5]);
+        *reinterpret_cast<uint2 *>(blk + 1024) = make_uint2(d[4], d[5]);
     } else {
         // dwords f[6..7] -> second half of piece 1, f[8..11] -> piece 2
-        *reinterpret_cast<uint2 *>(blk + 40) = make_uint2(d[0], d[1]);
-        *reinterpret_cast<uint4 *>(blk + 64) = make_uint4(d[2], d[3], d[4], d[5]);
+        *reinterpret_cast<uint2 *>(blk + 1024 + 8) = make_uint2(d[0], d[1]);
+        *reinterpret_cast<uint4 *>(blk + 2048) = make_uint4(d[2], d[3], d[4], d[5]);
     }
 }
 

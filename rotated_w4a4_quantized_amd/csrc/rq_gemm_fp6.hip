@@ -62,8 +62,7 @@ constexpr uint32_t kScale2p3 = 130u * 0x01010101u;   // E8M0 2^3 in every byte
 
 struct Fp6Args {
     const uint8_t *A;      // activation codes [T][lda] (canonical nibbles)
-    const uint8_t *Amma;   // activation codes in FP6 fragment layout [T][ldm], or null
-    int64_t ldm;           // bytes per MMA-layout activation row
+    const uint8_t *Amma;   // activation codes in FP6 fragment layout (rq_fp6.h), or null
     const uint8_t *Bmma;   // weight fragments [ntiles][S][3][64][16]
     const uint8_t *Bcan;   // canonical weight codes [N][ldb] (low-rank part)
     const float *sa;       // [T]
@@ -592,29 +591,23 @@ gemm_fp6_mma_kernel(Fp6Args a) {
     const int nstage = a.S;
 
     // Direct-to-LDS loads of this wave per stage: NA activation loads, then
-    // NB weight loads.  Activation load q = wave NA + i fills piece
-    // q % 3 of token fragment q / 3: lane l brings bytes 32 (q % 3) + 16 (l / 32)
-    // of the stage block of token t0 + 32 (q / 3) + l % 32 (rows past T read
-    // row T - 1, whose outputs are never stored).  Weight load q = wave NB + i
-    // copies piece q % 3 of weight tile n0 / 32 + q / 3 (1 KB, contiguous).
-    uint32_t aoff[C::NA];
-#pragma unroll
-    for (int i = 0; i < C::NA; ++i) {
-        const int q = wave * C::NA + i;
-        int64_t t = t0 + 32 * (q / 3) + li;
-        if (t >= a.T) t = a.T - 1;
-        aoff[i] = (uint32_t)((t - t0) * a.ldm + 16 * lg);
-    }
-    const uint8_t *abase = uniform_ptr(a.Amma + t0 * a.ldm);
-    const uint32_t woff = lane * 16;
+    // NB weight loads, each one contiguous 1 KB piece: activation load
+    // q = wave NA + i copies piece q % 3 of token tile t0 / 32 + q / 3 (tiles
+    // past the last token are clamped to it; their outputs are never
+    // stored), weight load q = wave NB + i piece q % 3 of weight tile
+    // n0 / 32 + q / 3.
+    const int atiles = (int)((a.T + 31) / 32);
+    const uint32_t loff = lane * 16;
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
     auto issue = [&](int s, int buf) {
         const uint32_t lb = lds_base + buf * C::LDS_STAGE;
 #pragma unroll
         for (int i = 0; i < C::NA; ++i) {
             const int q = wave * C::NA + i;
-            dma16_s(uniform_ptr(abase + (int64_t)s * kMmaStageBytes + 32 * (q % 3)), aoff[i],
-                    __builtin_amdgcn_readfirstlane(lb + q * 1024));
+            int tt = (int)(t0 / 32) + q / 3;
+            if (tt >= atiles) tt = atiles - 1;
+            const uint8_t *src = uniform_ptr(a.Amma + (((int64_t)tt * a.S + s) * 3 + q % 3) * 1024);
+            dma16_s(src, loff, __builtin_amdgcn_readfirstlane(lb + q * 1024));
         }
 #pragma unroll
         for (int i = 0; i < C::NB; ++i) {
@@ -622,7 +615,7 @@ gemm_fp6_mma_kernel(Fp6Args a) {
             int nt = n0 / 32 + q / 3;
             if (nt >= a.ntiles) nt = a.ntiles - 1;
             const uint8_t *src = uniform_ptr(a.Bmma + (((int64_t)nt * a.S + s) * 3 + q % 3) * 1024);
-            dma16_s(src, woff, __builtin_amdgcn_readfirstlane(lb + C::ACT_STAGE + q * 1024));
+            dma16_s(src, loff, __builtin_amdgcn_readfirstlane(lb + C::ACT_STAGE + q * 1024));
         }
     };
     auto wait_vm = [](auto nc) {
@@ -801,7 +794,6 @@ int launch_gemm_fp6(const uint8_t *codes, const uint8_t *codes_mma, const float 
     const uint8_t *base = static_cast<const uint8_t *>(blob);
     a.A = codes;
     a.Amma = codes_mma;
-    a.ldm = mma_row_bytes(hdr->K - hdr->r);
     a.Bmma = base + hdr->mma_offset;
     a.Bcan = base + hdr->codes_offset;
     a.sa = scale;

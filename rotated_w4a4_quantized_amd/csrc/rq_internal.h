@@ -20,8 +20,11 @@ rq_status check_quant(const rq_rotation *rot, const rq_quant *q);
 inline bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 inline int ilog2(int64_t v) { int l = 0; while ((int64_t(1) << l) < v) ++l; return l; }
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-// bytes per token row of codes in the GEMM's FP6 fragment layout
-inline int64_t mma_row_bytes(int Kq) { return (int64_t)((Kq + 127) / 128) * 96; }
+// bytes of codes in the GEMM's FP6 fragment layout for T tokens: 3 KB per 32
+// tokens per 128 quantized coordinates
+inline int64_t mma_codes_bytes(int64_t T, int Kq) {
+    return ((T + 31) / 32) * (int64_t)((Kq + 127) / 128) * 3 * 1024;
+}
 
 // Kernel launchers (rq_rpbh.hip, rq_dense.hip, rq_gemm_*.hip).  Arguments are validated
 // by the caller; these only launch.  They return a hipError_t as int.

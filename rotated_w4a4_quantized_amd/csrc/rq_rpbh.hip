@@ -154,8 +154,8 @@ struct RpbhArgs {
     const int8_t *sign;
     const int32_t *perm;
     uint8_t *codes;       // canonical [T][K/2], or null
-    uint8_t *codes_mma;   // FP6 fragment layout [T][mma_ld], or null (INT4 only)
-    int64_t mma_ld;       // bytes per MMA-layout row
+    uint8_t *codes_mma;   // FP6 fragment layout (rq_fp6.h), or null (INT4 only)
+    int mma_stages;       // 128-coordinate stages of the MMA layout
     float *scale;
     float th[15];         // codebook thresholds (Lloyd-Max)
 };
@@ -220,8 +220,13 @@ rpbh_quant_kernel(RpbhArgs a) {
     }
     __syncthreads();
 
+    // Workgroup b runs on XCD b % 8: number the workgroups XCD-major so that
+    // each XCD works on a contiguous range of tokens, whose 32-token tiles of
+    // the MMA-layout codes are then written from one L2.
+    int vb = blockIdx.x;
+    if (gridDim.x % 8 == 0) vb = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
     const int64_t stride = (int64_t)gridDim.x * a.tpw;
-    int64_t base = (int64_t)blockIdx.x * a.tpw;
+    int64_t base = (int64_t)vb * a.tpw;
     uint4 pre[S::CHUNKS];
     auto fetch = [&](int64_t b) {
         int64_t tok = b + tl;
@@ -372,7 +377,7 @@ rpbh_quant_kernel(RpbhArgs a) {
         if (valid) {
             if (a.codes) *reinterpret_cast<uint4 *>(a.codes + tok * (int64_t)(K / 2) + 16 * tt) = chunk;
             if constexpr (QK == 0)
-                if (a.codes_mma) store_chunk_mma(a.codes_mma + tok * a.mma_ld, tt, chunk);
+                if (a.codes_mma) store_chunk_mma(a.codes_mma, tok, a.mma_stages, tt, chunk);
             if (tt == 0) a.scale[tok] = sc;
         }
     }
@@ -459,7 +464,7 @@ RpbhArgs make_args(const void *X, int64_t T, int K, const int8_t *sign, const in
     a.perm = perm;
     a.codes = codes;
     a.codes_mma = codes_mma;
-    a.mma_ld = (int64_t)((K + 127) / 128) * kMmaStageBytes;
+    a.mma_stages = (K + 127) / 128;
     a.scale = scale;
     for (int i = 0; i < 15; ++i) a.th[i] = 0.0f;
     return a;

@@ -63,7 +63,7 @@ class QuantLinear:
         self.codes_mma = None
         if codes != "canonical":
             nb = rq.codes_mma_bytes(self.rot, T)
-            self.codes_mma = torch.empty((T, nb // max(T, 1)), dtype=torch.uint8, device=device)
+            self.codes_mma = torch.empty((max(nb, 16),), dtype=torch.uint8, device=device)
         self.scale = torch.empty((T,), dtype=torch.float32, device=device)
         self.top = torch.empty((T, w.r), dtype=torch.int16, device=device) if w.r else None
         wsb = rq.rotate_quant_workspace_bytes(self.rot, self.q, T)

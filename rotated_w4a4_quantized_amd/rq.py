@@ -336,7 +336,9 @@ def w4a4_linear(dw: DeviceWeights, codes, scale, Y, top=None, bias=None, T=None,
     """Launch the low-bit GEMM; Y dtype picks the output (f32, bf16, raw int32).
     When codes_mma is given it is read instead of codes (which may be None)."""
     if T is None:
-        T = int((codes if codes is not None else codes_mma).shape[0])
+        if codes is None:
+            raise ValueError("T must be given when codes is None")
+        T = int(codes.shape[0])
     _check(load().rq_w4a4_linear(ctypes.byref(dw.header), _t_ptr(dw.blob), _t_ptr(codes),
                                  _t_ptr(scale), _t_ptr(top), _t_ptr(codes_mma), T, _t_ptr(bias),
                                  _t_ptr(Y), dtype_code(Y), _stream(stream)))

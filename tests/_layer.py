@@ -90,21 +90,23 @@ def to_np_bf16_bits(t):
 FP6_ORDER = np.array([0, 1, 3, 4, 6, 7, 9, 10, 12, 13, 15, 8, 2, 11, 5, 14])
 
 
-def decode_codes_mma(buf, Kq):
-    """INT4 codes [T][Kq] (int8) from rq_rotate_quant's codes_mma output, read
-    as rq.h documents it: per token one 96-byte block per 128 coordinates;
-    half h of a block is the dwords f[0..11], f[d] at byte 32 (d // 4) +
-    16 h + 4 (d % 4); k-step ks is f[6 ks .. 6 ks + 5], 6-bit field e holding
+def decode_codes_mma(buf, T, Kq):
+    """INT4 codes [T][Kq] (int16) from rq_rotate_quant's codes_mma output, read
+    as rq.h documents it: [token tile of 32][stage of 128 coordinates]
+    [piece 0..2][lane 0..63][16 bytes]; token t of a tile owns lanes t and
+    t + 32 (half h); its dwords f[0..11] of half h are dword d % 4 of its lane
+    in piece d // 4; k-step ks is f[6 ks .. 6 ks + 5], 6-bit field e holding
     (q + 8) for coordinate 128 s + 64 ks + 32 h + order[e % 16] + 16 (e // 16).
-    Also returns whether every field of a coordinate below Kq had its two
-    top bits clear."""
-    buf = np.ascontiguousarray(buf, np.uint8)
-    T = buf.shape[0]
+    Also returns whether every field of a real coordinate (token below T,
+    coordinate below Kq) had its two top bits clear."""
     S = -(-Kq // 128)
-    blk = buf.reshape(T, S, 96).view(np.uint32).reshape(T, S, 3, 2, 4)   # [piece][h][dword]
-    f = blk.transpose(0, 1, 3, 2, 4).reshape(T, S, 2, 12).astype(np.uint64)  # [h][f0..f11]
-    q = np.zeros((T, S, 2, 2, 32), np.int16)   # [s][ks][h][field]
-    top = np.zeros((T, S, 2, 2, 32), bool)
+    NT = -(-T // 32)
+    buf = np.ascontiguousarray(buf, np.uint8)[:NT * S * 3 * 1024]
+    blk = buf.view(np.uint32).reshape(NT, S, 3, 2, 32, 4)        # [tile][s][piece][h][t][dword]
+    f = blk.transpose(0, 4, 1, 3, 2, 5).reshape(NT * 32, S, 2, 12).astype(np.uint64)  # [tok][s][h][f]
+    Tp = NT * 32
+    q = np.zeros((Tp, S, 2, 2, 32), np.int16)   # [tok][s][ks][h][field]
+    top = np.zeros((Tp, S, 2, 2, 32), bool)
     for ks in range(2):
         d = f[:, :, :, 6 * ks:6 * ks + 6]
         for e in range(32):
@@ -120,13 +122,13 @@ def decode_codes_mma(buf, Kq):
         for h in range(2):
             for e in range(32):
                 k_of[ks, h, e] = 64 * ks + 32 * h + FP6_ORDER[e % 16] + 16 * (e // 16)
-    out = np.zeros((T, S * 128), np.int16)
-    tops = np.zeros((T, S * 128), bool)
+    out = np.zeros((Tp, S * 128), np.int16)
+    tops = np.zeros((Tp, S * 128), bool)
     for s_ in range(S):
-        out[:, 128 * s_ + k_of.reshape(-1)] = q[:, s_].reshape(T, -1)
-        tops[:, 128 * s_ + k_of.reshape(-1)] = top[:, s_].reshape(T, -1)
-    # fields past Kq are never written: only the real coordinates count
-    return out[:, :Kq], not tops[:, :Kq].any()
+        out[:, 128 * s_ + k_of.reshape(-1)] = q[:, s_].reshape(Tp, -1)
+        tops[:, 128 * s_ + k_of.reshape(-1)] = top[:, s_].reshape(Tp, -1)
+    # only real tokens and coordinates are ever written
+    return out[:T, :Kq], not tops[:T, :Kq].any()
 
 
 def unpack_codes(codes):

@@ -104,10 +104,12 @@ def test_codes_mma_bytes():
         n = ctypes.c_size_t(0)
         assert rq.load().rq_codes_mma_bytes(ctypes.byref(rot), T, ctypes.byref(n)) == 0
         return n.value
-    assert nbytes(_rpbh(256, 64), 4) == 4 * 2 * 96
-    assert nbytes(_rpbh(96, 32), 3) == 3 * 1 * 96
-    assert nbytes(_rpbh(12288, 512), 2) == 2 * 96 * 96
-    assert nbytes(rq.c_rotation(rq.RQ_ROT_DENSE, 1152, 0, 32, None, None, 1 << 22), 5) == 5 * 9 * 96
+    # 3 KB per 32 tokens per 128 quantized coordinates
+    assert nbytes(_rpbh(256, 64), 4) == 1 * 2 * 3072
+    assert nbytes(_rpbh(96, 32), 33) == 2 * 1 * 3072
+    assert nbytes(_rpbh(12288, 512), 64) == 2 * 96 * 3072
+    assert nbytes(rq.c_rotation(rq.RQ_ROT_DENSE, 1152, 0, 32, None, None, 1 << 22), 5) == 1 * 9 * 3072
+    assert nbytes(_rpbh(256, 64), 0) == 0
     n = ctypes.c_size_t(0)
     assert rq.load().rq_codes_mma_bytes(ctypes.byref(_rpbh(100, 4)), 1, ctypes.byref(n)) == -2
 

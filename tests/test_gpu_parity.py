@@ -49,10 +49,9 @@ def check_act(w, L, act, rows=None):
     bad = np.nonzero(np.any(codes != act["codes"], axis=1))[0]
     assert bad.size == 0, f"codes differ in {bad.size} tokens, first {bad[:5]}"
     if L.codes_mma is not None:
-        mma = L.codes_mma.cpu().numpy()
+        dec, top_clear = H.decode_codes_mma(L.codes_mma.cpu().numpy(), w.T, w.Kq)
         if rows is not None:
-            mma = mma[rows]
-        dec, top_clear = H.decode_codes_mma(mma, w.Kq)
+            dec = dec[rows]
         assert top_clear, "a codes_mma field has its top bits set"
         ref = H.unpack_codes(act["codes"])
         bad = np.nonzero(np.any(dec != ref, axis=1))[0]
@@ -210,7 +209,7 @@ def test_outputs_stay_in_bounds():
     nb = M.codes_mma.numel()
     mma = torch.full((nb + G,), 0x5A, dtype=torch.uint8, device="cuda")
     Y2 = torch.full((w.T * w.N + G,), 3.25, dtype=torch.float32, device="cuda")
-    M.codes_mma = mma[:nb].view(w.T, nb // w.T)
+    M.codes_mma = mma[:nb]
     M.rotate_quant()
     M.linear(Y2[: w.T * w.N].view(w.T, w.N))
     torch.cuda.synchronize()
