@@ -169,6 +169,20 @@ __device__ inline const uint8_t *uniform_ptr(const uint8_t *p) {
     return reinterpret_cast<const uint8_t *>((uintptr_t)(((uint64_t)hi << 32) | lo));
 }
 
+// The same load with M0 declared clobbered instead of saved and restored:
+// three instructions.  Every operand is wave-uniform by construction (kernel
+// arguments, the scalar wave index and loop counters), so the scalar
+// constraints need no readfirstlane.
+__device__ inline void dma16_m0(const void *sbase, uint32_t voff, uint32_t lds_addr) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(sbase), "s"(lds_addr)
+        : "memory", "m0");
+}
+
 // sixteen zero bytes: the source of activation chunks past the end of a row
 __device__ __attribute__((aligned(16))) uint8_t g_zero16_fp6[16];
 
@@ -581,7 +595,8 @@ __global__ void __launch_bounds__(C::NTH, 1)
 gemm_fp6_mma_kernel(Fp6Args a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_BYTES];
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar address math
     const int wt = wave / C::WN, wn = wave % C::WN;
     const int li = lane & 31, lg = lane >> 5;
     int tile_t, tile_n;
@@ -606,16 +621,14 @@ gemm_fp6_mma_kernel(Fp6Args a) {
             const int q = wave * C::NA + i;
             int tt = (int)(t0 / 32) + q / 3;
             if (tt >= atiles) tt = atiles - 1;
-            const uint8_t *src = uniform_ptr(a.Amma + (((int64_t)tt * a.S + s) * 3 + q % 3) * 1024);
-            dma16_s(src, loff, __builtin_amdgcn_readfirstlane(lb + q * 1024));
+            dma16_m0(a.Amma + (((int64_t)tt * a.S + s) * 3 + q % 3) * 1024, loff, lb + q * 1024);
         }
 #pragma unroll
         for (int i = 0; i < C::NB; ++i) {
             const int q = wave * C::NB + i;
             int nt = n0 / 32 + q / 3;
             if (nt >= a.ntiles) nt = a.ntiles - 1;
-            const uint8_t *src = uniform_ptr(a.Bmma + (((int64_t)nt * a.S + s) * 3 + q % 3) * 1024);
-            dma16_s(src, loff, __builtin_amdgcn_readfirstlane(lb + C::ACT_STAGE + q * 1024));
+            dma16_m0(a.Bmma + (((int64_t)nt * a.S + s) * 3 + q % 3) * 1024, loff, lb + C::ACT_STAGE + q * 1024);
         }
     };
     auto wait_vm = [](auto nc) {
