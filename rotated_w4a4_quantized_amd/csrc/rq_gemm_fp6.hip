@@ -563,13 +563,25 @@ struct MmaCfg {
     static constexpr int NB = BN / 32 * 3 / NW;   // weight loads per wave per stage
     static constexpr int IPW = NA + NB;
     static constexpr int OUT_STRIDE = BN * 2 + 16;
-    static constexpr int LDS_BYTES =
-        3 * LDS_STAGE > BT * OUT_STRIDE ? 3 * LDS_STAGE : BT * OUT_STRIDE;
+    // after the stage buffers / output staging: the epilogue's per-token
+    // scales, per-channel scales and code sums of the tile, 1 KB each
+    static constexpr int EPI_OFF = 3 * LDS_STAGE > BT * OUT_STRIDE ? 3 * LDS_STAGE : BT * OUT_STRIDE;
+    static constexpr int LDS_BYTES = EPI_OFF + 3 * 1024;
+    static_assert(BT == 256 && BN == 256, "one 1 KB direct-to-LDS load per epilogue array");
+    static_assert(NW >= 3, "three waves load the epilogue arrays");
     static_assert(NA * NW == BT / 32 * 3 && NB * NW == BN / 32 * 3, "load split");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// two floats -> packed bf16 (round to nearest even), one instruction
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+    const f2v v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
+}
 
 // one lane's three 16-byte pieces of a 32-row fragment pair
 struct Frag {
@@ -676,6 +688,17 @@ gemm_fp6_mma_kernel(Fp6Args a) {
     // MFMAs, so their latency hides behind them -- and frees buffer s % 3
     // for the loads of stage s + 3.
     static_assert(C::FN == 4, "pipeline written for four weight fragments per wave");
+    // Full bf16 tiles take the staged epilogue; its per-token and
+    // per-channel arrays are loaded to LDS ahead of the stage-0 loads (the
+    // prologue's wait covers them).
+    const bool fast = a.ydt == RQ_BF16 && t0 + C::BT <= a.T && n0 + C::BN <= a.N && (a.N % 8) == 0 &&
+                      a.bias == nullptr;
+    if (fast && wave < 3) {
+        const void *src = wave == 0   ? static_cast<const void *>(a.sa + t0)
+                          : wave == 1 ? static_cast<const void *>(a.sw + n0)
+                                      : static_cast<const void *>(a.wsum + n0);
+        dma16_m0(src, loff, lds_base + C::EPI_OFF + wave * 1024);
+    }
     const int npre = nstage < 3 ? nstage : 3;
     for (int p = 0; p < npre; ++p) issue(p, p);
     if (npre == 3) wait_vm(std::integral_constant<int, 2 * C::IPW>());
@@ -724,29 +747,32 @@ gemm_fp6_mma_kernel(Fp6Args a) {
     // epilogue: full bf16 tiles staged through LDS (free after the last
     // barrier once this wave's reads have landed), else the general path
     constexpr int kOutStride = C::OUT_STRIDE;
-    if (a.ydt == RQ_BF16 && t0 + C::BT <= a.T && n0 + C::BN <= a.N && (a.N % 8) == 0 &&
-        a.bias == nullptr) {
+    if (fast) {
         lds_barrier();
+        const float *e_sa = reinterpret_cast<const float *>(lds + C::EPI_OFF);
+        const float *e_sw = reinterpret_cast<const float *>(lds + C::EPI_OFF + 1024);
+        const int32_t *e_ws = reinterpret_cast<const int32_t *>(lds + C::EPI_OFF + 2048);
+        float sat[C::FT];
+#pragma unroll
+        for (int j = 0; j < C::FT; ++j) sat[j] = e_sa[wt * C::FT * 32 + j * 32 + li] * a.post;
         static_for<C::FN>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
             static_for<4>([&](auto qc) {
                 constexpr int q = decltype(qc)::value;
                 const int nl = wn * C::FN * 32 + i * 32 + 8 * q + 4 * lg;
-                const float4 sw4 = *reinterpret_cast<const float4 *>(a.sw + n0 + nl);
-                const int4 ws4 = *reinterpret_cast<const int4 *>(a.wsum + n0 + nl);
+                const float4 sw4 = *reinterpret_cast<const float4 *>(e_sw + nl);
+                const int4 ws4 = *reinterpret_cast<const int4 *>(e_ws + nl);
                 const float o0 = (float)(8 * ws4.x), o1 = (float)(8 * ws4.y);
                 const float o2 = (float)(8 * ws4.z), o3 = (float)(8 * ws4.w);
                 static_for<C::FT>([&](auto jc) {
                     constexpr int j = decltype(jc)::value;
                     const int tl = wt * C::FT * 32 + j * 32 + li;
-                    const float sat = a.sa[t0 + tl] * a.post;
-                    const float y0 = (acc[i][j][4 * q + 0] - o0) * (sat * sw4.x);
-                    const float y1 = (acc[i][j][4 * q + 1] - o1) * (sat * sw4.y);
-                    const float y2 = (acc[i][j][4 * q + 2] - o2) * (sat * sw4.z);
-                    const float y3 = (acc[i][j][4 * q + 3] - o3) * (sat * sw4.w);
+                    const float y0 = (acc[i][j][4 * q + 0] - o0) * (sat[j] * sw4.x);
+                    const float y1 = (acc[i][j][4 * q + 1] - o1) * (sat[j] * sw4.y);
+                    const float y2 = (acc[i][j][4 * q + 2] - o2) * (sat[j] * sw4.z);
+                    const float y3 = (acc[i][j][4 * q + 3] - o3) * (sat[j] * sw4.w);
                     *reinterpret_cast<uint2 *>(lds + tl * kOutStride + 2 * nl) =
-                        make_uint2(bf16_rne_bits(y0) | (bf16_rne_bits(y1) << 16),
-                                   bf16_rne_bits(y2) | (bf16_rne_bits(y3) << 16));
+                        make_uint2(bf16x2_rne(y0, y1), bf16x2_rne(y2, y3));
                 });
             });
         });

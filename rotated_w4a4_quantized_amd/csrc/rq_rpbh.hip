@@ -23,10 +23,15 @@
 //            bit 0, so the final values of each nibble pair sit in one thread;
 //   stat     per-token absmax (and for the codebook the exact integer-grid
 //            squared norm) by shuffles and one LDS atomic per lane group;
-//   codes    nibbles are packed from registers, regrouped through LDS inside
-//            the wave into 16 contiguous bytes per thread, and stored with
-//            one 16-byte store (canonical layout) and/or spread into the
-//            GEMM's FP6 fragment layout (rq_fp6.h) with two stores.
+//   codes    nibbles are packed from registers and regrouped through LDS
+//            into 16 contiguous bytes per 32 coordinates; the canonical
+//            layout is stored with one 16-byte store per thread.  For the
+//            GEMM's FP6 fragment layout (rq_fp6.h) a workgroup takes its
+//            tokens in groups of at least four consecutive ones, keeps the
+//            group's codes in LDS, and once the group is complete spreads
+//            them so that the four tokens' 16-byte slots of one piece -- 64
+//            contiguous bytes -- come from four adjacent lanes: whole-request
+//            stores instead of sixteen-byte writes to scattered lines.
 // Two workgroup barriers per token (three for the codebook).
 
 #include <hip/hip_runtime.h>
@@ -143,7 +148,11 @@ __device__ inline void get(const float *us, int tt, float (&v)[kE]) {
 template <int L>
 __host__ __device__ constexpr int cpad(int q) { return q + 16 * (q >> (L - 1)); }
 template <int L>
-__host__ __device__ constexpr int cbytes(int K) { return L <= 5 ? 0 : K / 2 + 16 * (K >> L) + 16; }
+__host__ __device__ constexpr int cbytes(int K) { return L <= 5 ? K / 2 : K / 2 + 16 * (K >> L) + 16; }
+// byte offset of the 16-byte code chunk c (coordinates 32 c .. 32 c + 31)
+// in a token's staging slot
+template <int L>
+__host__ __device__ constexpr int chunk_off(int c) { return L <= 5 ? 16 * c : cpad<L>(16 * c); }
 
 struct RpbhArgs {
     const void *X;
@@ -156,6 +165,10 @@ struct RpbhArgs {
     uint8_t *codes;       // canonical [T][K/2], or null
     uint8_t *codes_mma;   // FP6 fragment layout (rq_fp6.h), or null (INT4 only)
     int mma_stages;       // 128-coordinate stages of the MMA layout
+    int grouped;          // MMA codes written per group (else per token)
+    int gsz_log2;         // tokens per group: a workgroup's unit of work
+    int ipg_log2;         // iterations per group (group size / tpw)
+    int64_t ngroups;
     float *scale;
     float th[15];         // codebook thresholds (Lloyd-Max)
 };
@@ -188,7 +201,8 @@ rpbh_quant_kernel(RpbhArgs a) {
     const int xw = xwords<L>(K);
     const int cb = (cbytes<L>(K) + 15) & ~15;
     float *us = reinterpret_cast<float *>(smem + (size_t)a.tpw * K * S::XB) + (size_t)tl * xw;
-    uint8_t *cs = smem + (size_t)a.tpw * (K * S::XB + 4 * xw) + (size_t)tl * cb;
+    // code staging: one slot per token of the group
+    uint8_t *const cs0 = smem + (size_t)a.tpw * (K * S::XB + 4 * xw);
 
     // ---- prologue: gather offsets, source-side sign masks -----------------
     int gofs[kE];
@@ -225,8 +239,14 @@ rpbh_quant_kernel(RpbhArgs a) {
     // the MMA-layout codes are then written from one L2.
     int vb = blockIdx.x;
     if (gridDim.x % 8 == 0) vb = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
-    const int64_t stride = (int64_t)gridDim.x * a.tpw;
-    int64_t base = (int64_t)vb * a.tpw;
+    // Iteration k of this workgroup takes group vb + (k / ipg) * grid, and in
+    // it tokens (k % ipg) tpw .. (k % ipg) tpw + tpw - 1; -1 past the end.
+    const int ipg_mask = (1 << a.ipg_log2) - 1;
+    auto first_tok = [&](int k) -> int64_t {
+        const int64_t g = vb + (int64_t)(k >> a.ipg_log2) * gridDim.x;
+        return g < a.ngroups ? (g << a.gsz_log2) + (int64_t)(k & ipg_mask) * a.tpw : -1;
+    };
+    int64_t base = first_tok(0);
     uint4 pre[S::CHUNKS];
     auto fetch = [&](int64_t b) {
         int64_t tok = b + tl;
@@ -247,21 +267,46 @@ rpbh_quant_kernel(RpbhArgs a) {
             *reinterpret_cast<uint4 *>(xs + (size_t)16 * (tt + q * a.tpt)) = w;
         }
     };
-    if (base < a.T) {
+    if (base >= 0) {
         fetch(base);
         stage();
-        if (base + stride < a.T) fetch(base + stride);
+        const int64_t b1 = first_tok(1);
+        if (b1 >= 0) fetch(b1);
     }
     __syncthreads();
+
+    // MMA-layout codes of group g (complete in the slots, LDS writes ordered
+    // by a barrier): item i is (stage s, half h) = (i >> gsz_log2) and token
+    // j = i % group size, so four adjacent lanes write one 64-byte run.
+    auto flush = [&](int64_t g) {
+        const int items = a.mma_stages * 2 << a.gsz_log2;
+        const int nth = a.tpw * a.tpt;
+        const int nch = K / kE;
+        const int gmask = (1 << a.gsz_log2) - 1;
+        for (int i = tid; i < items; i += nth) {
+            const int j = i & gmask;
+            const int sh = i >> a.gsz_log2;
+            const int64_t t = (g << a.gsz_log2) + j;
+            if (t >= a.T) continue;
+            const uint8_t *slot = cs0 + (size_t)j * cb;
+            const int c0 = 2 * (sh & ~1) + (sh & 1), c1 = c0 + 2;
+            const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+            const uint4 w0 = c0 < nch ? *reinterpret_cast<const uint4 *>(slot + chunk_off<L>(c0)) : z;
+            const uint4 w1 = c1 < nch ? *reinterpret_cast<const uint4 *>(slot + chunk_off<L>(c1)) : z;
+            store_pair_mma(a.codes_mma, t, a.mma_stages, sh >> 1, sh & 1, w0, w1);
+        }
+    };
+    const bool grouped = QK == 0 && a.grouped;
 
     // lane groups of one token for the shuffle reductions
     int grp = 64;
     while (a.tpt % grp) grp >>= 1;
 
     int it = 0;
-    for (; base < a.T; base += stride, ++it) {
+    for (; base >= 0; ++it) {
         const int64_t tok = base + tl;
         const bool valid = tok < a.T;
+        uint8_t *const cs = cs0 + (size_t)(((it & ipg_mask) * a.tpw) + tl) * cb;
         if (tt == 0) {
             red_max[it & 1][tl] = 0u;
             if constexpr (QK == 1) red_sum[it & 1][tl] = 0ull;
@@ -277,11 +322,15 @@ rpbh_quant_kernel(RpbhArgs a) {
         stages<L, 0>(v);
         if constexpr (Plan<L>::NP > 1) put<L, 0>(us, tt, v);
         lds_barrier();  // B1: every gather of this token is done
-        const bool more = base + stride < a.T;
-        if (more) {
+        const int64_t next = first_tok(it + 1);
+        if (next >= 0) {
             stage();                                        // next token -> LDS
-            if (base + 2 * stride < a.T) fetch(base + 2 * stride);
+            const int64_t b2 = first_tok(it + 2);
+            if (b2 >= 0) fetch(b2);
         }
+        // the previous group is complete: its packs are ordered by B1
+        if (grouped && it > 0 && (it & ipg_mask) == 0)
+            flush(vb + (int64_t)((it - 1) >> a.ipg_log2) * gridDim.x);
         if constexpr (Plan<L>::NP > 1) {
             get<L, 1>(us, tt, v);
             stages<L, 1>(v);
@@ -351,7 +400,7 @@ rpbh_quant_kernel(RpbhArgs a) {
 
         // pack: register bit 0 carries index bit 0, so registers (2m, 2m + 1)
         // hold a nibble pair
-        uint4 chunk;
+        uint4 chunk = make_uint4(0u, 0u, 0u, 0u);
         if constexpr (Plan<L>::NP == 1) {
             uint32_t w[4];
 #pragma unroll
@@ -362,24 +411,32 @@ rpbh_quant_kernel(RpbhArgs a) {
                 w[q] = x;
             }
             chunk = make_uint4(w[0], w[1], w[2], w[3]);
+            if (grouped) *reinterpret_cast<uint4 *>(cs + 16 * tt) = chunk;
         } else {
             uint8_t *p = cs + cpad<L>(pbase<L, PL>(tt) >> 1);
 #pragma unroll
             for (int mm = 0; mm < kE / 2; ++mm)
                 p[Plan<L>::roff(PL, 2 * mm) >> 1] = (uint8_t)((nib[2 * mm] & 0xFu) | (nib[2 * mm + 1] << 4));
-            // the 16 bytes this thread stores were written by lanes of its own
-            // wave (its RPBH block): order the LDS writes before the read
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            chunk = *reinterpret_cast<const uint4 *>(cs + cpad<L>(16 * tt));
+            if (a.codes || (a.codes_mma && !grouped)) {
+                // the 16 bytes this thread stores were written by lanes of its
+                // own wave (its RPBH block): order the LDS writes before the read
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                chunk = *reinterpret_cast<const uint4 *>(cs + cpad<L>(16 * tt));
+            }
         }
         if (valid) {
             if (a.codes) *reinterpret_cast<uint4 *>(a.codes + tok * (int64_t)(K / 2) + 16 * tt) = chunk;
             if constexpr (QK == 0)
-                if (a.codes_mma) store_chunk_mma(a.codes_mma, tok, a.mma_stages, tt, chunk);
+                if (a.codes_mma && !grouped) store_chunk_mma(a.codes_mma, tok, a.mma_stages, tt, chunk);
             if (tt == 0) a.scale[tok] = sc;
         }
+        base = next;
+    }
+    if (grouped && it > 0) {
+        lds_barrier();
+        flush(vb + (int64_t)((it - 1) >> a.ipg_log2) * gridDim.x);
     }
 }
 
@@ -400,28 +457,50 @@ int num_cus() {
 template <int L, bool BF16, int QK>
 hipError_t launch_L(RpbhArgs a, hipStream_t s) {
     const int xb = BF16 ? 2 : 4;
-    const size_t per_tok = (size_t)a.K * xb + 4 * (size_t)xwords<L>(a.K) +
-                           (size_t)((cbytes<L>(a.K) + 15) & ~15);
-    // tokens per workgroup: <= 512 threads, <= 78 KB of LDS (two workgroups
-    // per CU), then the candidate whose last round of tokens is fullest
+    const size_t per_tok = (size_t)a.K * xb + 4 * (size_t)xwords<L>(a.K);
+    const size_t slot_bytes = (size_t)((cbytes<L>(a.K) + 15) & ~15);
+    // the dynamic LDS a workgroup may take (160 KB less the static arrays)
+    constexpr size_t kLdsMax = 159 * 1024;
+    // MMA-layout codes are written per group of >= 4 consecutive tokens when
+    // the group's code slots fit, else per token
+    const bool grouped = QK == 0 && a.codes_mma != nullptr && per_tok + 4 * slot_bytes <= kLdsMax;
+    a.grouped = grouped ? 1 : 0;
+    // per-token code staging: the regrouping exchange (blocks > 32), or the
+    // group's slots
+    const size_t slot = (L <= 5 && !grouped) ? 0 : slot_bytes;
+    auto group_of = [&](int tpw) { return grouped && tpw < 4 ? 4 : tpw; };
+    auto lds_of = [&](int tpw) { return per_tok * tpw + slot * group_of(tpw); };
+    // Tokens per workgroup: <= 512 threads and <= 159 KB of LDS; two
+    // workgroups per CU when each fits in 78 KB, else one.  Every workgroup
+    // stays resident and loops over groups, so the candidate with the fewest
+    // tokens on the busiest CU wins; ties go to more waves per CU, then to
+    // the larger workgroup (fewer barriers per token).
     const int cus = num_cus();
     int best_tpw = 1;
-    double best_eff = -1.0;
+    int64_t best_load = -1;
+    int best_waves = 0;
     for (int tpw = 1; tpw <= kMaxTpw; tpw *= 2) {
-        if (tpw * a.tpt > 512 || tpw * per_tok > 78 * 1024) break;
-        const int64_t units = (a.T + tpw - 1) / tpw;
-        const int64_t slots = (int64_t)cus * 2;
-        const int64_t rounds = (units + slots - 1) / slots;
-        const double eff = (double)units / (double)(rounds * slots) + 0.02 * tpw;  // prefer fuller WGs
-        if (eff > best_eff) {
-            best_eff = eff;
+        if (tpw > 1 && (tpw * a.tpt > 512 || lds_of(tpw) > kLdsMax)) break;
+        const int occ = lds_of(tpw) <= 78 * 1024 ? 2 : 1;
+        const int gs = group_of(tpw);
+        const int64_t groups = (a.T + gs - 1) / gs;
+        const int64_t wgs = (int64_t)cus * occ;
+        const int64_t load = (int64_t)occ * ((groups + wgs - 1) / wgs) * gs;
+        const int waves = occ * ((tpw * a.tpt + 63) / 64);
+        if (best_load < 0 || load < best_load || (load == best_load && waves >= best_waves)) {
+            best_load = load;
+            best_waves = waves;
             best_tpw = tpw;
         }
     }
     a.tpw = best_tpw;
-    const size_t lds = per_tok * best_tpw;
-    const int64_t units = (a.T + best_tpw - 1) / best_tpw;
-    const int grid = (int)(units < (int64_t)cus * 2 ? units : (int64_t)cus * 2);
+    const int gs = group_of(best_tpw);
+    a.gsz_log2 = ilog2(gs);
+    a.ipg_log2 = ilog2(gs / best_tpw);
+    a.ngroups = (a.T + gs - 1) / gs;
+    const size_t lds = lds_of(best_tpw);
+    const int64_t resident = (int64_t)cus * (lds <= 78 * 1024 ? 2 : 1);
+    const int grid = (int)(a.ngroups < resident ? a.ngroups : resident);
     auto kern = rpbh_quant_kernel<L, BF16, QK>;
     // raise the dynamic-LDS limit once per instantiation (the call is not free)
     static size_t lds_set = 0;
@@ -465,6 +544,9 @@ RpbhArgs make_args(const void *X, int64_t T, int K, const int8_t *sign, const in
     a.codes = codes;
     a.codes_mma = codes_mma;
     a.mma_stages = (K + 127) / 128;
+    a.grouped = 0;
+    a.gsz_log2 = a.ipg_log2 = 0;
+    a.ngroups = 0;
     a.scale = scale;
     for (int i = 0; i < 15; ++i) a.th[i] = 0.0f;
     return a;

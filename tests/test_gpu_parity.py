@@ -74,6 +74,9 @@ SMALL = [
     ("tiny", dict(T=65, K=96, N=40, block=2)),
     ("tiny", dict(T=33, K=32, N=7, block=8)),
     ("flux_up", dict(T=40, K=16384, N=64, block=512)),
+    # fp32 input at the largest K: the MMA codes are stored per token (a group
+    # of four tokens' code slots does not fit in LDS beside the row)
+    ("tiny", dict(T=37, K=16384, N=64, block=512)),
 ]
 
 
@@ -247,3 +250,21 @@ def test_mma_codes_only_path():
     assert A.codes is None and np.array_equal(accA, accB)
     assert torch.equal(A.scale, B.scale) and torch.equal(A.Y, B.Y)
 
+
+
+def test_mma_bf16_output_matches_converting_kernel():
+    # Full 256 x 256 tiles of the MMA-layout GEMM round bf16 outputs with the
+    # hardware conversion; the converting kernel rounds in software (nearest
+    # even).  Same accumulators and the same fp32 operations, so the bits
+    # must agree -- full tiles and the ragged edge alike.
+    w = datagen.WORKLOADS["flux_up"].with_shape(T=600, K=1024, N=800, block=256)
+    inp = datagen.make_inputs(w)
+    L = H.GpuLayer(w, inp, codes="both")
+    assert L.Y.dtype == torch.bfloat16
+    L.rotate_quant()
+    Ya = torch.empty_like(L.Y)
+    Yb = torch.empty_like(L.Y)
+    L.linear(Ya, use_mma=True)
+    L.linear(Yb, use_mma=False)
+    torch.cuda.synchronize()
+    assert torch.equal(Ya.view(torch.int16), Yb.view(torch.int16))
