@@ -68,10 +68,11 @@ __device__ __forceinline__ void store_chunk_mma(uint8_t *mma, int64_t t, int S, 
 // Stores the MMA-layout codes of token t for stage s and half h: the canonical
 // chunks c0 = 4 s + h (k-step 0) and c1 = 4 s + 2 + h (k-step 1), sixteen
 // bytes each, become the token's three 16-byte lane slots (lane t % 32 + 32 h)
-// of the stage block's pieces 0, 1 and 2.  Tokens t .. t + 3 of one tile
-// write one contiguous 64-byte run per piece.
+// of the stage block's pieces 0, 1 and 2 (only k-step 0's 24 bytes when has1
+// is false: chunk c1 lies past the last coordinate).  Tokens t .. t + 3 of
+// one tile write one contiguous 64-byte run per piece.
 __device__ __forceinline__ void store_pair_mma(uint8_t *mma, int64_t t, int S, int s, int h, uint4 w0,
-                                               uint4 w1) {
+                                               uint4 w1, bool has1) {
     uint32_t d[12];
     to_fp6(w0.x, w0.y, d[0], d[1], d[2]);
     to_fp6(w0.z, w0.w, d[3], d[4], d[5]);
@@ -79,6 +80,10 @@ __device__ __forceinline__ void store_pair_mma(uint8_t *mma, int64_t t, int S, i
     to_fp6(w1.z, w1.w, d[9], d[10], d[11]);
     uint8_t *blk = mma + ((t >> 5) * S + s) * (int64_t)kMmaTileStageBytes + (((int)t & 31) + 32 * h) * 16;
     *reinterpret_cast<uint4 *>(blk) = make_uint4(d[0], d[1], d[2], d[3]);
+    if (!has1) {
+        *reinterpret_cast<uint2 *>(blk + 1024) = make_uint2(d[4], d[5]);
+        return;
+    }
     *reinterpret_cast<uint4 *>(blk + 1024) = make_uint4(d[4], d[5], d[6], d[7]);
     *reinterpret_cast<uint4 *>(blk + 2048) = make_uint4(d[8], d[9], d[10], d[11]);
 }

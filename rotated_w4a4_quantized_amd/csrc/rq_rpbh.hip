@@ -289,11 +289,14 @@ rpbh_quant_kernel(RpbhArgs a) {
             const int64_t t = (g << a.gsz_log2) + j;
             if (t >= a.T) continue;
             const uint8_t *slot = cs0 + (size_t)j * cb;
+            // chunks c0 (k-step 0) and c1 (k-step 1); those past the last
+            // coordinate are not written
             const int c0 = 2 * (sh & ~1) + (sh & 1), c1 = c0 + 2;
-            const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-            const uint4 w0 = c0 < nch ? *reinterpret_cast<const uint4 *>(slot + chunk_off<L>(c0)) : z;
-            const uint4 w1 = c1 < nch ? *reinterpret_cast<const uint4 *>(slot + chunk_off<L>(c1)) : z;
-            store_pair_mma(a.codes_mma, t, a.mma_stages, sh >> 1, sh & 1, w0, w1);
+            if (c0 >= nch) continue;
+            const uint4 w0 = *reinterpret_cast<const uint4 *>(slot + chunk_off<L>(c0));
+            const uint4 w1 = c1 < nch ? *reinterpret_cast<const uint4 *>(slot + chunk_off<L>(c1))
+                                      : make_uint4(0u, 0u, 0u, 0u);
+            store_pair_mma(a.codes_mma, t, a.mma_stages, sh >> 1, sh & 1, w0, w1, c1 < nch);
         }
     };
     const bool grouped = QK == 0 && a.grouped;
