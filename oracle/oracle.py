@@ -8,7 +8,8 @@ in rq_oracle.c (plain C, no contraction), loaded here with ctypes.
 What each function computes is stated with the page passage it follows:
 
 * "TR-DQ: Time-Rotation Diffusion Quantization" section 3.1 -- linear layer
-  Y = X.W, uniform quantizer Eq.(1)-(2), per-token activation and
+  Y = X.W, uniform quantizer Eq.(1)-(3) (symmetric form, and the asymmetric
+  per-token form with a zero point), per-token activation and
   per-channel weight granularity; section 3.2 Eq.(8)-(9) -- block-diagonal
   rotation, runtime rotation of X with the transposed rotation folded into W.
 * "OrbitQuant" abstract -- RPBH rotation, normalized rotated basis, one
@@ -72,6 +73,7 @@ def _declare(L):
     L.orc_dense_row_f64.argtypes = [_P, _P, _I, _P]
     L.orc_quant_int4_row.argtypes = [_P, _I, _I, _P, _P]
     L.orc_quant_int4_wrow.argtypes = [_P, _I, _P, _P]
+    L.orc_quant_int4_asym_row.argtypes = [_P, _I, _P, _P, _P]
     L.orc_pack_nibbles.argtypes = [_P, _I, _P]
     L.orc_pack_crumbs.argtypes = [_P, _I, _P]
     L.orc_norm2_grid.argtypes = [_P, _I]
@@ -79,10 +81,11 @@ def _declare(L):
     L.orc_quant_lloydmax_row.argtypes = [_P, _I, _P, _I, _P, _P]
     L.orc_quant_lloydmax_wrow.argtypes = [_P, _I, _P, _I, _P, _P]
     L.orc_act_rows.argtypes = [_P, _I, _I, _P, _I64, _I, _I, _P, _P, _P, _I, _I,
-                               _P, _I, _P, _P, _P, _P]
+                               _P, _I, _P, _P, _P, _P, _P]
     L.orc_weight_rows.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _I, _P,
                                   _P, _P]
     L.orc_int_gemm_pairs.argtypes = [_P, _I, _P, _I, _I, _P, _P, _I64, _P]
+    L.orc_asym_gemm_pairs.argtypes = [_P, _I, _P, _P, _P, _I64, _P]
     L.orc_int_gemm.argtypes = [_P, _I, _I, _P, _I, _I, _I, _P]
     L.orc_lowrank_pairs.argtypes = [_P, _I, _P, _I, _P, _P, _I64, _P]
     L.orc_codebook_dot_pairs.argtypes = [_P, _P, _I, _P, _P, _P, _P, _I64, _P]
@@ -142,6 +145,16 @@ def quant_int4_row(u, r=0):
     s = np.zeros(1, np.float32)
     lib().orc_quant_int4_row(_ptr(u), u.size, r, _ptr(q), _ptr(s))
     return q, np.float32(s[0])
+
+
+def quant_int4_asym_row(u):
+    """Asymmetric per-token INT4 (TR-DQ Eq.(1)-(3)): unsigned codes, s, z."""
+    u = np.ascontiguousarray(u, np.float32)
+    q = np.empty(u.size, np.uint8)
+    s = np.zeros(1, np.float32)
+    z = np.zeros(1, np.float32)
+    lib().orc_quant_int4_asym_row(_ptr(u), u.size, _ptr(q), _ptr(s), _ptr(z))
+    return q, np.float32(s[0]), np.float32(z[0])
 
 
 def quant_int4_wrow(v):
@@ -283,7 +296,8 @@ def act_rows(X, xdtype, K, rows, *, rot_kind, b=0, sign=None, perm=None, R=None,
     """Activation side for the listed rows of X (see orc_act_rows).
 
     X: np.float32 [T][K] (xdtype 0) or np.uint16 bf16 bits [T][K] (xdtype 1).
-    Returns dict(codes, scale, top, u)."""
+    q_kind 2 (asymmetric INT4, r = 0) also returns the zero points.
+    Returns dict(codes, scale, zero, top, u)."""
     rows = np.ascontiguousarray(rows, np.int64)
     n = rows.size
     X = np.ascontiguousarray(X)
@@ -291,6 +305,7 @@ def act_rows(X, xdtype, K, rows, *, rot_kind, b=0, sign=None, perm=None, R=None,
     ncode = (Kq // 2) if q_kind == 0 else (K // 2)
     codes = np.zeros((n, ncode), np.uint8)
     scale = np.zeros(n, np.float32)
+    zero = np.zeros(n, np.float32) if q_kind == 2 else None
     top = np.zeros((n, r), np.uint16) if r > 0 else None
     u = np.zeros((n, K), np.float32) if want_u else None
     lv = None if levels is None else np.ascontiguousarray(levels, np.float32)
@@ -299,8 +314,8 @@ def act_rows(X, xdtype, K, rows, *, rot_kind, b=0, sign=None, perm=None, R=None,
                        _ptr(None if perm is None else np.ascontiguousarray(perm, np.int32)),
                        _ptr(None if R is None else np.ascontiguousarray(R, np.float32)),
                        r, q_kind, _ptr(lv), 0 if lv is None else lv.size,
-                       _ptr(codes), _ptr(scale), _ptr(top), _ptr(u))
-    return dict(codes=codes, scale=scale, top=top, u=u)
+                       _ptr(codes), _ptr(scale), _ptr(zero), _ptr(top), _ptr(u))
+    return dict(codes=codes, scale=scale, zero=zero, top=top, u=u)
 
 
 def weight_rows(W, *, rot_kind, b=0, sign=None, perm=None, R=None, q_kind=0, levels=None):
@@ -342,6 +357,17 @@ def int_gemm_pairs(codes_a, Kq, codes_w, Kw, ta, nw, koff=0):
     return acc
 
 
+def asym_gemm_pairs(codes_a, codes_w, K, ta, nw):
+    """acc[p] = sum_k ua[t_p][k] qw[n_p][k] (unsigned activation codes)."""
+    ta = np.ascontiguousarray(ta, np.int64)
+    nw = np.ascontiguousarray(nw, np.int64)
+    acc = np.zeros(ta.size, np.int64)
+    lib().orc_asym_gemm_pairs(_ptr(np.ascontiguousarray(codes_a, np.uint8)), K,
+                              _ptr(np.ascontiguousarray(codes_w, np.uint8)),
+                              _ptr(ta), _ptr(nw), ta.size, _ptr(acc))
+    return acc
+
+
 def lowrank_pairs(top, r, codes_w, Kw, ta, nw):
     ta = np.ascontiguousarray(ta, np.int64)
     nw = np.ascontiguousarray(nw, np.int64)
@@ -373,6 +399,14 @@ def yhat_int4(s_a, s_w, acc, b_eff, lr=None):
     if lr is None:
         return s_a * s_w * acc / float(b_eff)
     return s_w * (np.asarray(lr, np.float64) + s_a * acc) / float(b_eff)
+
+
+def yhat_int4_asym(s_a, z_a, s_w, acc_u, wsum, b):
+    """fp64 output with asymmetric activations ([TRDQ] 3.1: X ~ s (X_int - z)):
+    s_a s_w (sum_k ua qw - z sum_k qw) / b."""
+    return (np.asarray(s_a, np.float64) * np.asarray(s_w, np.float64) *
+            (np.asarray(acc_u, np.float64) -
+             np.asarray(z_a, np.float64) * np.asarray(wsum, np.float64)) / float(b))
 
 
 def yhat_codebook(sigma, tau, dot, b):

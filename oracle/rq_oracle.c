@@ -190,6 +190,55 @@ void orc_quant_int4_row(const float *u, int K, int r, int8_t *q, float *s_out)
     *s_out = s;
 }
 
+/*
+ * Per-token asymmetric INT4 of a rotated row ([TRDQ] section 3.1: Eq.(1)
+ * X_int = clamp(round(X / s) + z, 0, 2^b - 1), Eq.(2) s = (max X - min X) /
+ * (2^b - 1), Eq.(3) the zero point z), b = 4, over all K coordinates.
+ * Readings where the pages are open or garbled:
+ *   - Eq.(3) prints z = round(min X / s); with Eq.(1)'s "+ z" the minimum
+ *     must land on code 0, so z = -round(min X / s);
+ *   - z is kept in [0, 15] (it already is whenever min <= 0 <= max);
+ *   - one fp32 rounding per operation, the division by s taken as a
+ *     multiplication by its reciprocal computed directly:
+ *       lo = min u, hi = max u, d = fl32(hi - lo)
+ *       d == 0  ->  all codes 0, s = 0, z = 0
+ *       else    s = fl32(d / 15), inv = fl32(15 / d)
+ *               z = clamp(-rne(fl32(lo * inv)), 0, 15)
+ *               q[j] = clamp(rne(fl32(u[j] * inv)) + z, 0, 15)
+ * Codes are unsigned, 0..15.
+ */
+void orc_quant_int4_asym_row(const float *u, int K, uint8_t *q, float *s_out, float *z_out)
+{
+    float lo = u[0], hi = u[0];
+    for (int j = 1; j < K; j++) {
+        if (u[j] < lo) lo = u[j];
+        if (u[j] > hi) hi = u[j];
+    }
+    float d = hi - lo;
+    if (d == 0.0f) {
+        for (int j = 0; j < K; j++)
+            q[j] = 0;
+        *s_out = 0.0f;
+        *z_out = 0.0f;
+        return;
+    }
+    float s = d / 15.0f;
+    float inv = 15.0f / d;
+    float zl = lo * inv;
+    float z = -rintf(zl);
+    if (z < 0.0f) z = 0.0f;
+    if (z > 15.0f) z = 15.0f;
+    for (int j = 0; j < K; j++) {
+        float m = u[j] * inv;
+        float t = rintf(m) + z;   /* integers below 2^24: exact */
+        if (t < 0.0f) t = 0.0f;
+        if (t > 15.0f) t = 15.0f;
+        q[j] = (uint8_t)t;
+    }
+    *s_out = s;
+    *z_out = z;
+}
+
 /* Per-output-channel symmetric INT4 of a folded fp64 weight row (all K).
  *   amax == 0 -> codes 0, scale 0
  *   s_w = (float)(amax / 7), inv = 7 / amax (fp64), q = clamp(rne(v*inv)). */
@@ -359,6 +408,8 @@ static void widen_row(const void *X, int xdtype, size_t row, int K, float *out)
  *   q_kind   0: INT4 symmetric -> codes [nrows][(K-r)/2] nibbles, scale[nrows]
  *            1: Lloyd-Max (levels, L=16) -> codes [nrows][K/2] nibbles of the
  *               4-bit index, scale[nrows] = sigma
+ *            2: INT4 asymmetric (r = 0) -> codes [nrows][K/2] unsigned
+ *               nibbles, scale[nrows] = s, zero[nrows] = z
  *   top: bf16 [nrows][r] (dense only), may be NULL when r == 0.
  *   u_out: optional fp32 [nrows][K] copy of the rotated rows.
  * rows: indices into X (nrows of them).
@@ -367,7 +418,7 @@ void orc_act_rows(const void *X, int xdtype, int K, const int64_t *rows,
                   int64_t nrows, int rot_kind, int b, const int8_t *sign,
                   const int32_t *perm, const float *R, int r, int q_kind,
                   const float *levels, int L, uint8_t *codes, float *scale,
-                  uint16_t *top, float *u_out)
+                  float *zero, uint16_t *top, float *u_out)
 {
     int Kq = K - r;
 #pragma omp parallel
@@ -390,6 +441,11 @@ void orc_act_rows(const void *X, int xdtype, int K, const int64_t *rows,
                 orc_pack_nibbles(q, Kq, codes + (size_t)i * (Kq / 2));
                 for (int j = 0; j < r; j++)
                     top[(size_t)i * r + j] = orc_f32_to_bf16(u[j]);
+            } else if (q_kind == 2) {
+                orc_quant_int4_asym_row(u, K, ix, &scale[i], &zero[i]);
+                for (int j = 0; j < K / 2; j++)
+                    codes[(size_t)i * (K / 2) + j] =
+                        (uint8_t)((ix[2 * j] & 0x0Fu) | ((ix[2 * j + 1] & 0x0Fu) << 4));
             } else {
                 orc_quant_lloydmax_row(u, K, levels, L, ix, &scale[i]);
                 for (int j = 0; j < K / 2; j++)
@@ -472,6 +528,27 @@ void orc_int_gemm_pairs(const uint8_t *codes_a, int Kq, const uint8_t *codes_w,
         int64_t s = 0;
         for (int k = 0; k < Kq; k++)
             s += (int64_t)nib(ra, k) * (int64_t)nib(rw, koff + k);
+        acc[p] = s;
+    }
+}
+
+/*
+ * Asymmetric activations: acc[p] = sum_{k < K} ua[t_p][k] * qw[n_p][k] in
+ * int64, ua the unsigned activation codes (0..15), qw the signed weight
+ * codes.  The layer output subtracts z[t] * sum_k qw[n][k] (see oracle.py).
+ */
+void orc_asym_gemm_pairs(const uint8_t *codes_a, int K, const uint8_t *codes_w,
+                         const int64_t *ta, const int64_t *nw, int64_t npairs, int64_t *acc)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < npairs; p++) {
+        const uint8_t *ra = codes_a + (size_t)ta[p] * (K / 2);
+        const uint8_t *rw = codes_w + (size_t)nw[p] * (K / 2);
+        int64_t s = 0;
+        for (int k = 0; k < K; k++) {
+            int ua = (ra[k >> 1] >> ((k & 1) * 4)) & 0xF;
+            s += (int64_t)ua * (int64_t)nib(rw, k);
+        }
         acc[p] = s;
     }
 }

@@ -216,3 +216,100 @@ def test_codebook_weight_row():
     wh = v * (np.sqrt(K) / nrm)
     assert all(idx[k] == _nearest_level(wh[k], levels) for k in range(K))
     assert abs(float(tau) - nrm / np.sqrt(K)) <= 1e-7 * nrm / np.sqrt(K)
+
+
+# ---------------------------------------------------------------------------
+# asymmetric per-token INT4 ("TR-DQ" section 3.1, Eq.(1)-(3): codes
+# clamp(round(X / s) + z, 0, 15), s = (max - min) / 15, zero point z; the
+# sign of Eq.(3) read so that the minimum lands on code 0)
+# ---------------------------------------------------------------------------
+
+def asym_brute(u):
+    """Independent check of one row: s and 1/s correctly rounded from the fp32
+    range, z the nearest integer to -min/s (clamped to [0, 15]), every code
+    the level k in [0, 15] nearest to fl32(u inv) + z by exhaustive search
+    (ties to k - z even, i.e. nearest-even on the unshifted value)."""
+    lo, hi = np.float32(np.min(u)), np.float32(np.max(u))
+    d = np.float32(hi - lo)
+    inv = np.float32(15.0) / d
+    zl = np.float32(lo * inv)
+    f = Fraction(float(zl))
+    k0 = f.numerator // f.denominator                    # floor
+    k = k0 if (f - k0 < Fraction(1, 2) or (f - k0 == Fraction(1, 2) and k0 % 2 == 0)) else k0 + 1
+    z = min(max(-k, 0), 15)
+    codes = []
+    for x in u:
+        m = np.float32(np.float32(x) * inv)
+        best = None
+        for k in range(16):
+            dist = abs(Fraction(float(m)) + z - k)
+            if best is None or dist < best[0] or (dist == best[0] and (k - z) % 2 == 0):
+                best = (dist, k)
+        codes.append(best[1])
+    return np.array(codes), d, z
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_int4_asym_brute_force(seed):
+    g = np.random.default_rng(100 + seed)
+    K = 64
+    u = (g.standard_normal(K) * g.choice([1e-3, 1.0, 23.0]) + (0.3 if seed == 3 else 0.0)).astype(np.float32)
+    if seed == 4:   # plant values that scale to exact half-levels
+        u[0], u[1] = np.float32(-1.0), np.float32(2.0)
+        u[2:8] = np.float32(0.5)
+    q, s, z = orc.quant_int4_asym_row(u)
+    ref, d, zref = asym_brute(u)
+    assert is_nearest_f32(s, Fraction(float(d)) / 15)
+    assert z == zref
+    assert np.array_equal(q.astype(np.int64), ref)
+
+
+def test_int4_asym_hand_example():
+    # u = [-1, 0, 0.5, 2]: range 3, s = 0.2, 1/s = 5, z = -round(-5) = 5;
+    # levels round([-5, 0, 2.5, 10]) + 5 = [0, 5, 7 (2.5 -> 2, even), 15]
+    q, s, z = orc.quant_int4_asym_row(np.array([-1.0, 0.0, 0.5, 2.0], np.float32))
+    assert list(q) == [0, 5, 7, 15]
+    assert z == 5.0 and s == np.float32(3.0) / np.float32(15.0)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_int4_asym_extremes_and_error_bound(seed):
+    g = np.random.default_rng(200 + seed)
+    u = (g.standard_normal(4096) * 3.0).astype(np.float32)
+    q, s, z = orc.quant_int4_asym_row(u)
+    assert q.min() >= 0 and q.max() <= 15
+    assert q[np.argmin(u)] == 0          # min X lands on code 0 (0 is inside [min, max])
+    assert q[np.argmax(u)] >= 14          # max X on the top level (or one below at a tie)
+    err = np.abs(s * (q.astype(np.float64) - z) - u.astype(np.float64))
+    # nearest rounding: half a step, plus fp32 error of u * inv; the clamped
+    # top code may be one step off
+    bound = 0.5 * float(s) + 4e-7 * float(np.max(np.abs(u)))
+    assert np.mean(err <= bound) > 0.999
+    assert np.all(err <= 1.0001 * float(s))
+
+
+def test_int4_asym_degenerate_rows():
+    for u in (np.zeros(32, np.float32), np.full(32, 2.5, np.float32)):
+        q, s, z = orc.quant_int4_asym_row(u)
+        assert not q.any() and s == 0 and z == 0
+    # all-positive row: the zero point clamps to 0 and codes still span [0, 15]
+    u = np.linspace(1.0, 4.0, 64, dtype=np.float32)
+    q, s, z = orc.quant_int4_asym_row(u)
+    assert z == 0 and q.max() == 15
+
+
+def test_asym_gemm_and_output_identity():
+    g = np.random.default_rng(7)
+    T, N, K, b = 5, 6, 64, 32
+    ua = g.integers(0, 16, (T, K))
+    qw = g.integers(-7, 8, (N, K))
+    pa = orc.pack_nibbles((ua - 16 * (ua >= 8)).astype(np.int8))
+    pw = orc.pack_nibbles(qw.astype(np.int8))
+    ta, nw = np.repeat(np.arange(T), N), np.tile(np.arange(N), T)
+    acc = orc.asym_gemm_pairs(pa.reshape(T, K // 2), pw.reshape(N, K // 2), K, ta, nw)
+    assert np.array_equal(acc.reshape(T, N), ua @ qw.T)
+    s_a, z_a = g.random(T).astype(np.float32), g.integers(0, 16, T).astype(np.float32)
+    s_w = g.random(N).astype(np.float32)
+    y = orc.yhat_int4_asym(s_a[ta], z_a[ta], s_w[nw], acc, qw.sum(1)[nw], b)
+    direct = ((s_a[:, None] * (ua - z_a[:, None])) @ (s_w[:, None] * qw).T) / b
+    assert np.allclose(y.reshape(T, N), direct, rtol=1e-12, atol=1e-12)
