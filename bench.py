@@ -43,6 +43,7 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 
 WORKLOADS = {
     "flux": ["flux_up", "flux_down"],
+    "flux_asym": ["flux_up_asym", "flux_down_asym"],
     "flux_up": ["flux_up"],
     "flux_down": ["flux_down"],
     "tiny": ["tiny"],
@@ -164,6 +165,8 @@ def rotate_bytes(w) -> int:
     scales (and top) written."""
     xb = 4 if w.xdtype == "f32" else 2
     b = w.T * w.K * xb + w.T * (w.Kq // 2) + 4 * w.T
+    if w.quant == "int4_asym":
+        b += 4 * w.T   # zero points
     if w.r:
         b += 2 * w.T * w.r
     return b
@@ -255,7 +258,8 @@ def main():
         for w in wls:
             inp = datagen.make_inputs(w, seed_offset=100 * i)
             # RPBH INT4 layers hand the GEMM its codes in the matrix-core layout
-            mode = "mma" if (w.rot == "rpbh" and w.quant == "int4" and not int8_gemm) else "canonical"
+            mode = ("mma" if (w.rot == "rpbh" and w.quant in ("int4", "int4_asym") and not int8_gemm)
+                    else "canonical")
             layers.append(QuantLinear(w, inp, codes=mode))
             log(f"[bench] instance {i} layer {w.name}: T={w.T} K={w.K} N={w.N} ready")
         ring.append(layers)

@@ -78,7 +78,7 @@ typedef enum rq_dtype {
 } rq_dtype;
 
 typedef enum rq_rot_kind { RQ_ROT_RPBH = 0, RQ_ROT_DENSE = 1 } rq_rot_kind;
-typedef enum rq_q_kind { RQ_Q_INT4_SYM = 0, RQ_Q_LLOYDMAX = 1 } rq_q_kind;
+typedef enum rq_q_kind { RQ_Q_INT4_SYM = 0, RQ_Q_LLOYDMAX = 1, RQ_Q_INT4_ASYM = 2 } rq_q_kind;
 
 /*
  * Rotation descriptor.  Pointer members are host pointers for
@@ -103,9 +103,10 @@ typedef struct rq_rotation {
 
 /*
  * Quantizer descriptor (plain values, no pointers).
- *   kind      rq_q_kind
+ *   kind      rq_q_kind.  INT4_ASYM: activations per token with a zero point
+ *             (TR-DQ section 3.1 Eq.(1)-(3)), weights as INT4_SYM; RPBH only
  *   a_bits    4
- *   w_bits    INT4_SYM: 4;  LLOYDMAX: 2 or 4
+ *   w_bits    INT4_SYM, INT4_ASYM: 4;  LLOYDMAX: 2 or 4
  *   a_levels  LLOYDMAX: 2^a_bits strictly ascending, bf16-representable
  *   w_levels  LLOYDMAX: 2^w_bits strictly ascending, bf16-representable
  */
@@ -249,21 +250,28 @@ rq_status rq_codes_mma_bytes(const rq_rotation *rot, int64_t T, size_t *bytes);
  *          amax = max |u[j]|; s = fl32(amax / 7); inv = fl32(7 / amax)
  *          q[j] = clamp(rne(fl32(u[j] * inv)), -7, 7); amax == 0 -> 0, s = 0.
  *          DENSE also writes top[t][j] = bf16_rne(u[j]) for j < r.
+ *   INT4_ASYM (RPBH): lo = min u, hi = max u, d = fl32(hi - lo);
+ *          s = fl32(d / 15); inv = fl32(15 / d);
+ *          z = clamp(-rne(fl32(lo * inv)), 0, 15) (an integer);
+ *          q[j] = clamp(rne(fl32(u[j] * inv)) + z, 0, 15); d == 0 -> 0, s = z = 0.
  *   LLOYDMAX: d = |u|^2 on an exact integer grid (order independent),
  *          g = (float)sqrt(K / d); index[j] = number of midpoints of adjacent
  *          a_levels strictly below fl32(u[j] * g); sigma = (float)sqrt(d / K).
  * Arguments:
  *   rot     host descriptor with device sign/perm (RPBH) or R (DENSE)
- *   q       quantizer (INT4_SYM with RPBH or DENSE; LLOYDMAX with RPBH)
+ *   q       quantizer (INT4_SYM with RPBH or DENSE; INT4_ASYM and LLOYDMAX
+ *           with RPBH)
  *   X       device [T][K] tokens, row-major, dtype x_dtype (RQ_F32/RQ_BF16),
  *           16-byte aligned
  *   T       tokens, 0 <= T < 2^31
- *   codes   device uint8 [T][(K - r) / 2]: INT4 nibbles (two's complement,
- *           low nibble = even coordinate) or LLOYDMAX 4-bit indices, same
- *           packing.  May be NULL for RPBH INT4_SYM when codes_mma is given.
- *   scale   device fp32 [T]: s (INT4) or sigma (LLOYDMAX)
+ *   codes   device uint8 [T][(K - r) / 2]: INT4_SYM nibbles (two's complement,
+ *           low nibble = even coordinate), INT4_ASYM unsigned nibbles, or
+ *           LLOYDMAX 4-bit indices, same packing.  May be NULL for RPBH
+ *           INT4 when codes_mma is given.
+ *   scale   device fp32 [T]: s (INT4_SYM) or sigma (LLOYDMAX); INT4_ASYM:
+ *           fp32 [2][T], s[t] then the zero point z[t]
  *   top     device bf16 [T][r] for DENSE with r > 0, else NULL
- *   codes_mma  RPBH INT4_SYM only, optional: device buffer of
+ *   codes_mma  RPBH INT4 only, optional: device buffer of
  *           rq_codes_mma_bytes() receiving the same codes in the low-bit
  *           GEMM's matrix-core layout (NULL: not written).  Tokens come in
  *           tiles of 32 and coordinates in stages of 128; the buffer is
@@ -273,7 +281,8 @@ rq_status rq_codes_mma_bytes(const rq_rotation *rot, int64_t T, size_t *bytes);
  *           of its lane in piece d / 4.  f[0..5] and f[6..11] are the 192-bit
  *           fragments of coordinates 128 s + 64 ks + 32 h + (0..31) for
  *           ks = 0, 1; bits [6 e, 6 e + 6) of a fragment hold the E2M3 code
- *           q + 8 (value (q + 8) / 8, top two bits clear) of coordinate offset
+ *           u (value u / 8, top two bits clear; u = q + 8 for INT4_SYM, the
+ *           unsigned code for INT4_ASYM) of coordinate offset
  *           {0,1,3,4,6,7,9,10,12,13,15,8,2,11,5,14}[e % 16] + 16 (e / 16).
  *           Bytes of tokens past T and coordinates past K - r are left
  *           unwritten.
@@ -293,7 +302,8 @@ rq_status rq_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void 
  * (TR-DQ section 3.1: Y = X W with per-token activation and per-channel
  * weight scales; DiRotQ abstract: the top principal coefficients add a
  * higher-precision term).
- *   INT4:  acc[t][n] = sum_{k < K-r} q_a[t][k] * q_w[n][r + k]  (exact, int32)
+ *   INT4:  acc[t][n] = sum_{k < K-r} q_a[t][k] * q_w[n][r + k]  (exact, int32);
+ *          INT4_ASYM: q_a[t][k] = u_a[t][k] - z[t] (codes minus zero point)
  *          RPBH:  Y = s_a[t] s_w[n] acc / b_div
  *          DENSE: Y = s_w[n] (lr[t][n] + s_a[t] acc), with
  *                 lr = sum_{j < r} top[t][j] * q_w[n][j] (bf16 x int4 products,
@@ -306,11 +316,12 @@ rq_status rq_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void 
  * weight codes (in the blob) removes the offset; every partial sum is an
  * integer below 2^24, so the fp32 accumulation is exact.  With
  * RQ_W4A4_MFMA=int8 in the environment the int8 matrix cores run instead
- * (codes must then be given).
+ * (codes must then be given; INT4_SYM only).
  * Arguments:
  *   hdr     host pointer to the blob's header (its first 256 bytes)
  *   blob    device copy of the whole blob, 16-byte aligned
- *   codes, scale, top  as written by rq_rotate_quant (device)
+ *   codes, scale, top  as written by rq_rotate_quant (device); the weights'
+ *           format (INT4_SYM / INT4_ASYM) must match the activations' quantizer
  *   codes_mma  optional (INT4 weights with r == 0): the codes_mma output of
  *           rq_rotate_quant for the same tokens; when given it is read
  *           instead of codes (which may then be NULL)

@@ -225,9 +225,9 @@ void orc_quant_int4_asym_row(const float *u, int K, uint8_t *q, float *s_out, fl
     float s = d / 15.0f;
     float inv = 15.0f / d;
     float zl = lo * inv;
-    float z = -rintf(zl);
-    if (z < 0.0f) z = 0.0f;
-    if (z > 15.0f) z = 15.0f;
+    float zr = rintf(zl);
+    int zi = zr > 0.0f ? 0 : (zr < -15.0f ? 15 : -(int)zr);
+    float z = (float)zi;        /* an integer in [0, 15]; +0 for zero */
     for (int j = 0; j < K; j++) {
         float m = u[j] * inv;
         float t = rintf(m) + z;   /* integers below 2^24: exact */

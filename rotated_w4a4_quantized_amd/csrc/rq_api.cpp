@@ -25,18 +25,21 @@ rq_status check_header(const rq_weight_header *hdr) {
     if (hdr->version != RQ_WEIGHT_VERSION)
         return fail(RQ_ERR_FORMAT, "weight header version " + std::to_string(hdr->version) +
                                        " is not " + std::to_string(RQ_WEIGHT_VERSION));
-    if (hdr->format != RQ_Q_INT4_SYM && hdr->format != RQ_Q_LLOYDMAX)
+    if (hdr->format != RQ_Q_INT4_SYM && hdr->format != RQ_Q_LLOYDMAX && hdr->format != RQ_Q_INT4_ASYM)
         return fail(RQ_ERR_FORMAT, "unknown weight format");
+    const bool int4 = hdr->format != RQ_Q_LLOYDMAX;
     if (hdr->K < 32 || hdr->K > 16384 || hdr->K % 32 != 0 || hdr->N < 1 || hdr->N > (1 << 20) ||
         hdr->r < 0 || hdr->r >= hdr->K || hdr->r % 32 != 0 || hdr->b_div < 1)
         return fail(RQ_ERR_FORMAT, "weight header shape fields are inconsistent");
-    const int want_rb = (hdr->format == RQ_Q_INT4_SYM || hdr->w_bits == 4) ? hdr->K / 2 : hdr->K / 4;
+    const int want_rb = (int4 || hdr->w_bits == 4) ? hdr->K / 2 : hdr->K / 4;
     if (hdr->row_bytes != want_rb) return fail(RQ_ERR_FORMAT, "weight header row_bytes mismatch");
     if (hdr->format == RQ_Q_LLOYDMAX && hdr->K % 64 != 0)
         return fail(RQ_ERR_SHAPE, "the codebook GEMM needs K % 64 == 0");
     if (hdr->scale_offset % 16 != 0 || hdr->codes_offset % 16 != 0)
         return fail(RQ_ERR_FORMAT, "weight header offsets are not 16-byte aligned");
-    if (hdr->format == RQ_Q_INT4_SYM) {
+    if (hdr->format == RQ_Q_INT4_ASYM && hdr->r != 0)
+        return fail(RQ_ERR_FORMAT, "INT4_ASYM weights have r == 0 (RPBH)");
+    if (int4) {
         if (hdr->mma_stages != (hdr->K - hdr->r + 127) / 128 || hdr->mma_ntiles != (hdr->N + 31) / 32)
             return fail(RQ_ERR_FORMAT, "weight header FP6 tile counts are inconsistent");
         if (hdr->wsum_offset % 16 != 0 || hdr->mma_offset % 16 != 0 || hdr->wsum_offset <= 0 ||
@@ -96,22 +99,24 @@ rq_status rq_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void 
     if (T < 0 || T >= (int64_t(1) << 31)) return fail(RQ_ERR_SHAPE, "T out of range");
     const int K = rot->K;
     const bool dense = rot->kind == RQ_ROT_DENSE;
-    if (codes_mma && (dense || q->kind != RQ_Q_INT4_SYM))
-        return fail(RQ_ERR_UNSUPPORTED, "codes_mma is written for RPBH with INT4_SYM only");
+    const bool int4 = q->kind == RQ_Q_INT4_SYM || q->kind == RQ_Q_INT4_ASYM;
+    if (codes_mma && (dense || !int4))
+        return fail(RQ_ERR_UNSUPPORTED, "codes_mma is written for RPBH with INT4 only");
     if (T == 0) return RQ_OK;
     if (!X || !scale || (!codes && !codes_mma))
         return fail(RQ_ERR_NULL, "X, scale and at least one of codes / codes_mma must not be NULL");
     if (dense && !codes) return fail(RQ_ERR_NULL, "DENSE needs codes");
-    if (q->kind != RQ_Q_INT4_SYM && !codes) return fail(RQ_ERR_NULL, "LLOYDMAX needs codes");
+    if (!int4 && !codes) return fail(RQ_ERR_NULL, "LLOYDMAX needs codes");
     if (dense && rot->r > 0 && !top) return fail(RQ_ERR_NULL, "DENSE with r > 0 needs top");
     if (!aligned16(X) || (codes && !aligned16(codes)) || !aligned16(scale) ||
         (top && !aligned16(top)) || (codes_mma && !aligned16(codes_mma)))
         return fail(RQ_ERR_ALIGN, "device buffers must be 16-byte aligned");
     const int xb = x_dtype == RQ_BF16 ? 1 : 0;
     if (!dense) {
-        if (q->kind == RQ_Q_INT4_SYM)
+        if (int4)
             return hip_status(launch_rpbh_int4(X, xb, T, K, rot->block, rot->sign, rot->perm, codes,
-                                               codes_mma, scale, stream),
+                                               codes_mma, scale, q->kind == RQ_Q_INT4_ASYM ? 1 : 0,
+                                               stream),
                               "rotate_quant launch");
         float th[15];
         const int La = 1 << q->a_bits;
@@ -139,27 +144,32 @@ rq_status rq_w4a4_linear(const rq_weight_header *hdr, const void *blob, const ui
     if (st != RQ_OK) return st;
     if (y_dtype != RQ_F32 && y_dtype != RQ_BF16 && y_dtype != RQ_I32)
         return fail(RQ_ERR_DTYPE, "Y must be RQ_F32, RQ_BF16 or RQ_I32");
-    if (y_dtype == RQ_I32 && hdr->format != RQ_Q_INT4_SYM)
+    const bool int4 = hdr->format != RQ_Q_LLOYDMAX;
+    const bool asym = hdr->format == RQ_Q_INT4_ASYM;
+    if (y_dtype == RQ_I32 && !int4)
         return fail(RQ_ERR_UNSUPPORTED, "raw accumulators exist for INT4 weights only");
-    if (codes_mma && (hdr->format != RQ_Q_INT4_SYM || hdr->r != 0))
+    if (codes_mma && (!int4 || hdr->r != 0))
         return fail(RQ_ERR_UNSUPPORTED, "codes_mma is read for INT4 weights with r == 0 only");
+    if (asym && use_int8_gemm())
+        return fail(RQ_ERR_UNSUPPORTED, "the int8 GEMM (RQ_W4A4_MFMA=int8) takes INT4_SYM only");
     if (T < 0 || T >= (int64_t(1) << 31)) return fail(RQ_ERR_SHAPE, "T out of range");
     if (T == 0) return RQ_OK;
     const bool int8 = hdr->format == RQ_Q_INT4_SYM && use_int8_gemm();
     if (!blob || !scale || !Y || (!codes && !codes_mma) || (int8 && !codes))
         return fail(RQ_ERR_NULL, "blob, scale, Y and the activation codes must not be NULL");
-    if (hdr->format != RQ_Q_INT4_SYM && !codes) return fail(RQ_ERR_NULL, "LLOYDMAX needs codes");
+    if (!int4 && !codes) return fail(RQ_ERR_NULL, "LLOYDMAX needs codes");
     if (hdr->r > 0 && !top) return fail(RQ_ERR_NULL, "weights with r > 0 need top");
     if (!aligned16(blob) || (codes && !aligned16(codes)) || !aligned16(scale) || !aligned16(Y) ||
         (top && !aligned16(top)) || (bias && !aligned16(bias)) ||
         (codes_mma && !aligned16(codes_mma)))
         return fail(RQ_ERR_ALIGN, "device buffers must be 16-byte aligned");
-    if (hdr->format == RQ_Q_INT4_SYM) {
+    if (int4) {
         if (int8)
             return hip_status(launch_gemm_w4a4(codes, scale, top, T, hdr, blob, bias, Y, y_dtype, stream),
                               "w4a4 int8 gemm launch");
-        return hip_status(launch_gemm_fp6(codes_mma ? nullptr : codes, codes_mma, scale, top, T, hdr,
-                                          blob, bias, Y, y_dtype, stream),
+        return hip_status(launch_gemm_fp6(codes_mma ? nullptr : codes, codes_mma, scale,
+                                          asym ? scale + T : nullptr, top, T, hdr, blob, bias, Y,
+                                          y_dtype, stream),
                           "w4a4 fp6 gemm launch");
     }
     return hip_status(launch_gemm_codebook(codes, scale, T, hdr, blob, bias, Y, y_dtype, stream),

@@ -4,8 +4,9 @@
 // An E2M3 element (sign, 2 exponent bits with bias 1, 3 mantissa bits) whose
 // 6-bit code is an unsigned u < 16 decodes to u / 8 (codes 0..7 are the
 // subnormals m / 8, codes 8..15 have exponent 1 and decode to (8 + m) / 8).
-// An activation code q in [-7, 7] is carried as u = q + 8: the two's-
-// complement nibble with its top bit flipped.  Weights are carried
+// A symmetric activation code q in [-7, 7] is carried as u = q + 8: the two's-
+// complement nibble with its top bit flipped.  An asymmetric (zero-point)
+// code is already unsigned and is carried as itself.  Weights are carried
 // sign-magnitude ((q < 0) << 5 | |q|, i.e. q / 8), so with both block scales
 // at 2^3 the matrix core sums (qa + 8) qw exactly.
 //
@@ -31,15 +32,16 @@ namespace rq {
 constexpr int kMmaTileStageBytes = 3 * 1024;   // per 32 tokens per 128 coordinates
 
 // 16 canonical nibble codes (a: offsets 0..7, b: offsets 8..15 of a group of
-// coordinates; low nibble = even offset) -> sixteen 6-bit fields holding
-// q + 8, in three dwords.  Field e takes offset
+// coordinates; low nibble = even offset) -> sixteen 6-bit fields holding the
+// nibble XOR flip (flip = 0x88888888: q + 8 for signed codes; 0: unsigned
+// codes as they are), in three dwords.  Field e takes offset
 // {0,1,3,4,6,7,9,10,12,13,15,8,2,11,5,14}[e]: with that order each field is
 // a nibble of a or b shifted by 0 or 2 bits, so three masks per output dword
 // do the spreading.
 __device__ __forceinline__ void to_fp6(uint32_t a, uint32_t b, uint32_t &d0, uint32_t &d1,
-                                       uint32_t &d2) {
-    a ^= 0x88888888u;
-    b ^= 0x88888888u;
+                                       uint32_t &d2, uint32_t flip) {
+    a ^= flip;
+    b ^= flip;
     const uint32_t a2 = a << 2, b2 = b << 2;
     d0 = (a & 0x0F00F00Fu) | (a2 & 0xC03C03C0u);
     d1 = (a >> 30) | (b & 0xF00F00F0u) | (b2 & 0x03C03C00u);
@@ -48,10 +50,11 @@ __device__ __forceinline__ void to_fp6(uint32_t a, uint32_t b, uint32_t &d0, uin
 
 // Stores the 32 canonical codes of chunk c (coordinates 32 c .. 32 c + 31,
 // sixteen bytes w) of token t into the MMA-layout buffer of S stages.
-__device__ __forceinline__ void store_chunk_mma(uint8_t *mma, int64_t t, int S, int c, uint4 w) {
+__device__ __forceinline__ void store_chunk_mma(uint8_t *mma, int64_t t, int S, int c, uint4 w,
+                                                uint32_t flip) {
     uint32_t d[6];
-    to_fp6(w.x, w.y, d[0], d[1], d[2]);
-    to_fp6(w.z, w.w, d[3], d[4], d[5]);
+    to_fp6(w.x, w.y, d[0], d[1], d[2], flip);
+    to_fp6(w.z, w.w, d[3], d[4], d[5], flip);
     const int s = c >> 2, ks = (c >> 1) & 1, h = c & 1;
     uint8_t *blk = mma + ((t >> 5) * S + s) * (int64_t)kMmaTileStageBytes + (((int)t & 31) + 32 * h) * 16;
     if (ks == 0) {
@@ -72,12 +75,12 @@ __device__ __forceinline__ void store_chunk_mma(uint8_t *mma, int64_t t, int S, 
 // is false: chunk c1 lies past the last coordinate).  Tokens t .. t + 3 of
 // one tile write one contiguous 64-byte run per piece.
 __device__ __forceinline__ void store_pair_mma(uint8_t *mma, int64_t t, int S, int s, int h, uint4 w0,
-                                               uint4 w1, bool has1) {
+                                               uint4 w1, bool has1, uint32_t flip) {
     uint32_t d[12];
-    to_fp6(w0.x, w0.y, d[0], d[1], d[2]);
-    to_fp6(w0.z, w0.w, d[3], d[4], d[5]);
-    to_fp6(w1.x, w1.y, d[6], d[7], d[8]);
-    to_fp6(w1.z, w1.w, d[9], d[10], d[11]);
+    to_fp6(w0.x, w0.y, d[0], d[1], d[2], flip);
+    to_fp6(w0.z, w0.w, d[3], d[4], d[5], flip);
+    to_fp6(w1.x, w1.y, d[6], d[7], d[8], flip);
+    to_fp6(w1.z, w1.w, d[9], d[10], d[11], flip);
     uint8_t *blk = mma + ((t >> 5) * S + s) * (int64_t)kMmaTileStageBytes + (((int)t & 31) + 32 * h) * 16;
     *reinterpret_cast<uint4 *>(blk) = make_uint4(d[0], d[1], d[2], d[3]);
     if (!has1) {

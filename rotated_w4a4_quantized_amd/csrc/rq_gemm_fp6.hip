@@ -18,7 +18,9 @@
 //     i.e. subnormal q / 8.
 // With both E8M0 block scales at 2^3 the matrix core returns
 // sum_k (qa + 8) qw = acc + 8 wsum[n], where wsum[n] = sum_k qw[n][k] is
-// stored in the weight blob.  Every product and partial sum is an integer of
+// stored in the weight blob.  Asymmetric activations ("TR-DQ" section 3.1,
+// codes u in [0, 15] with a per-token zero point z) are carried as u itself,
+// and the epilogue removes z[t] wsum[n] instead of 8 wsum[n].  Every product and partial sum is an integer of
 // magnitude <= 15 * 7 * 16384 < 2^24, so the fp32 accumulation is exact in
 // any order, and acc is recovered exactly as a float.
 //
@@ -81,6 +83,8 @@ struct Fp6Args {
     int ydt;               // rq_dtype
     int tiles_t, tiles_n;
     float post;            // 1 / b_div
+    const float *za;       // asymmetric activations: zero point per token [T], else null
+    uint32_t flip;         // canonical nibble -> FP6 field: XOR 0x88888888 (signed) or 0
 };
 
 __device__ inline void lds_barrier() {
@@ -203,17 +207,19 @@ __device__ inline void tile_of(int bid, int nblk, int tiles_t, int tiles_n, int 
 }
 
 // Epilogue of four consecutive channels nb .. nb + 3 (those below N) of
-// token t: remove the offset-binary term, rescale, store as rq_dtype.
+// token t: remove the offset term zt wsum[n] (zt = 8, or the token's zero
+// point), rescale, store as rq_dtype.
 template <bool HAS_LR>
-__device__ __forceinline__ void store4(const Fp6Args &a, int64_t t, int nb, float sat, float c0,
-                                       float c1, float c2, float c3, const float (&lr4)[4]) {
+__device__ __forceinline__ void store4(const Fp6Args &a, int64_t t, int nb, float sat, float zt,
+                                       float c0, float c1, float c2, float c3,
+                                       const float (&lr4)[4]) {
     const float c[4] = {c0, c1, c2, c3};
     int32_t iv[4];
     float y[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int n = nb + e < a.N ? nb + e : a.N - 1;
-        const float accn = c[e] - (float)(8 * a.wsum[n]);   // exact: integers below 2^24
+        const float accn = c[e] - zt * (float)a.wsum[n];   // exact: integers below 2^24
         iv[e] = (int32_t)accn;
         const float swn = a.sw[n];
         const float bn = a.bias ? a.bias[n] : 0.0f;
@@ -354,8 +360,8 @@ gemm_fp6_kernel(Fp6Args a) {
 #pragma unroll
         for (int j = 0; j < C::FT; ++j) {
             uint32_t d0, d1, d2, d3, d4, d5;
-            to_fp6(an[j].x, an[j].y, d0, d1, d2);
-            to_fp6(an[j].z, an[j].w, d3, d4, d5);
+            to_fp6(an[j].x, an[j].y, d0, d1, d2, a.flip);
+            to_fp6(an[j].z, an[j].w, d3, d4, d5, a.flip);
             bt[j] = v8i{(int)d0, (int)d1, (int)d2, (int)d3, (int)d4, (int)d5, 0, 0};
         }
     };
@@ -486,16 +492,16 @@ gemm_fp6_kernel(Fp6Args a) {
                     const int nl = wn * C::FN * 32 + i * 32 + 8 * q + 4 * lg;
                     const float4 sw4 = *reinterpret_cast<const float4 *>(a.sw + n0 + nl);
                     const int4 ws4 = *reinterpret_cast<const int4 *>(a.wsum + n0 + nl);
-                    const float o0 = (float)(8 * ws4.x), o1 = (float)(8 * ws4.y);
-                    const float o2 = (float)(8 * ws4.z), o3 = (float)(8 * ws4.w);
+                    const float w0 = (float)ws4.x, w1 = (float)ws4.y, w2 = (float)ws4.z, w3 = (float)ws4.w;
                     static_for<C::FT>([&](auto jc) {
                         constexpr int j = decltype(jc)::value;
                         const int tl = wt * C::FT * 32 + j * 32 + li;
                         const float sat = a.sa[t0 + tl] * a.post;
-                        const float y0 = (acc[i][j][4 * q + 0] - o0) * (sat * sw4.x);
-                        const float y1 = (acc[i][j][4 * q + 1] - o1) * (sat * sw4.y);
-                        const float y2 = (acc[i][j][4 * q + 2] - o2) * (sat * sw4.z);
-                        const float y3 = (acc[i][j][4 * q + 3] - o3) * (sat * sw4.w);
+                        const float zt = a.za ? a.za[t0 + tl] : 8.0f;   // zt * w exact
+                        const float y0 = (acc[i][j][4 * q + 0] - zt * w0) * (sat * sw4.x);
+                        const float y1 = (acc[i][j][4 * q + 1] - zt * w1) * (sat * sw4.y);
+                        const float y2 = (acc[i][j][4 * q + 2] - zt * w2) * (sat * sw4.z);
+                        const float y3 = (acc[i][j][4 * q + 3] - zt * w3) * (sat * sw4.w);
                         *reinterpret_cast<uint2 *>(lds + tl * kOutStride + 2 * nl) =
                             make_uint2(bf16_rne_bits(y0) | (bf16_rne_bits(y1) << 16),
                                        bf16_rne_bits(y2) | (bf16_rne_bits(y3) << 16));
@@ -521,6 +527,7 @@ gemm_fp6_kernel(Fp6Args a) {
         const int64_t t = t0 + wt * C::FT * 32 + j * 32 + li;
         const bool t_ok = t < a.T;
         const float sat = a.sa[t_ok ? t : a.T - 1];
+        const float zt = a.za ? a.za[t_ok ? t : a.T - 1] : 8.0f;
         static_for<C::FN>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
             static_for<4>([&](auto qc) {
@@ -532,7 +539,7 @@ gemm_fp6_kernel(Fp6Args a) {
                     for (int e = 0; e < 4; ++e) lr4[e] = lr[i][j][4 * q + e];
                 }
                 if (t_ok && nb < a.N)
-                    store4<HAS_LR>(a, t, nb, sat, acc[i][j][4 * q + 0], acc[i][j][4 * q + 1],
+                    store4<HAS_LR>(a, t, nb, sat, zt, acc[i][j][4 * q + 0], acc[i][j][4 * q + 1],
                                    acc[i][j][4 * q + 2], acc[i][j][4 * q + 3], lr4);
             });
         });
@@ -564,11 +571,12 @@ struct MmaCfg {
     static constexpr int IPW = NA + NB;
     static constexpr int OUT_STRIDE = BN * 2 + 16;
     // after the stage buffers / output staging: the epilogue's per-token
-    // scales, per-channel scales and code sums of the tile, 1 KB each
+    // scales, per-channel scales, code sums and per-token zero points of the
+    // tile, 1 KB each
     static constexpr int EPI_OFF = 3 * LDS_STAGE > BT * OUT_STRIDE ? 3 * LDS_STAGE : BT * OUT_STRIDE;
-    static constexpr int LDS_BYTES = EPI_OFF + 3 * 1024;
+    static constexpr int LDS_BYTES = EPI_OFF + 4 * 1024;
     static_assert(BT == 256 && BN == 256, "one 1 KB direct-to-LDS load per epilogue array");
-    static_assert(NW >= 3, "three waves load the epilogue arrays");
+    static_assert(NW >= 4, "four waves load the epilogue arrays");
     static_assert(NA * NW == BT / 32 * 3 && NB * NW == BN / 32 * 3, "load split");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
@@ -693,10 +701,14 @@ gemm_fp6_mma_kernel(Fp6Args a) {
     // prologue's wait covers them).
     const bool fast = a.ydt == RQ_BF16 && t0 + C::BT <= a.T && n0 + C::BN <= a.N && (a.N % 8) == 0 &&
                       a.bias == nullptr;
-    if (fast && wave < 3) {
+    // zero points follow the scales ([2][T]): a 16-byte aligned start only
+    // when T % 4 == 0, else they are read from global memory at the end
+    const bool za_lds = a.za != nullptr && (reinterpret_cast<uintptr_t>(a.za) & 15) == 0;
+    if (fast && (wave < 3 || (wave == 3 && za_lds))) {
         const void *src = wave == 0   ? static_cast<const void *>(a.sa + t0)
                           : wave == 1 ? static_cast<const void *>(a.sw + n0)
-                                      : static_cast<const void *>(a.wsum + n0);
+                          : wave == 2 ? static_cast<const void *>(a.wsum + n0)
+                                      : static_cast<const void *>(a.za + t0);
         dma16_m0(src, loff, lds_base + C::EPI_OFF + wave * 1024);
     }
     const int npre = nstage < 3 ? nstage : 3;
@@ -752,9 +764,14 @@ gemm_fp6_mma_kernel(Fp6Args a) {
         const float *e_sa = reinterpret_cast<const float *>(lds + C::EPI_OFF);
         const float *e_sw = reinterpret_cast<const float *>(lds + C::EPI_OFF + 1024);
         const int32_t *e_ws = reinterpret_cast<const int32_t *>(lds + C::EPI_OFF + 2048);
-        float sat[C::FT];
+        const float *e_za = reinterpret_cast<const float *>(lds + C::EPI_OFF + 3072);
+        float sat[C::FT], zt[C::FT];
 #pragma unroll
-        for (int j = 0; j < C::FT; ++j) sat[j] = e_sa[wt * C::FT * 32 + j * 32 + li] * a.post;
+        for (int j = 0; j < C::FT; ++j) {
+            sat[j] = e_sa[wt * C::FT * 32 + j * 32 + li] * a.post;
+            const int tl = wt * C::FT * 32 + j * 32 + li;
+            zt[j] = !a.za ? 8.0f : za_lds ? e_za[tl] : a.za[t0 + tl];
+        }
         static_for<C::FN>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
             static_for<4>([&](auto qc) {
@@ -762,15 +779,15 @@ gemm_fp6_mma_kernel(Fp6Args a) {
                 const int nl = wn * C::FN * 32 + i * 32 + 8 * q + 4 * lg;
                 const float4 sw4 = *reinterpret_cast<const float4 *>(e_sw + nl);
                 const int4 ws4 = *reinterpret_cast<const int4 *>(e_ws + nl);
-                const float o0 = (float)(8 * ws4.x), o1 = (float)(8 * ws4.y);
-                const float o2 = (float)(8 * ws4.z), o3 = (float)(8 * ws4.w);
+                const float w0 = (float)ws4.x, w1 = (float)ws4.y, w2 = (float)ws4.z, w3 = (float)ws4.w;
                 static_for<C::FT>([&](auto jc) {
                     constexpr int j = decltype(jc)::value;
                     const int tl = wt * C::FT * 32 + j * 32 + li;
-                    const float y0 = (acc[i][j][4 * q + 0] - o0) * (sat[j] * sw4.x);
-                    const float y1 = (acc[i][j][4 * q + 1] - o1) * (sat[j] * sw4.y);
-                    const float y2 = (acc[i][j][4 * q + 2] - o2) * (sat[j] * sw4.z);
-                    const float y3 = (acc[i][j][4 * q + 3] - o3) * (sat[j] * sw4.w);
+                    // zt * w is an exact integer below 2^24
+                    const float y0 = (acc[i][j][4 * q + 0] - zt[j] * w0) * (sat[j] * sw4.x);
+                    const float y1 = (acc[i][j][4 * q + 1] - zt[j] * w1) * (sat[j] * sw4.y);
+                    const float y2 = (acc[i][j][4 * q + 2] - zt[j] * w2) * (sat[j] * sw4.z);
+                    const float y3 = (acc[i][j][4 * q + 3] - zt[j] * w3) * (sat[j] * sw4.w);
                     *reinterpret_cast<uint2 *>(lds + tl * kOutStride + 2 * nl) =
                         make_uint2(bf16x2_rne(y0, y1), bf16x2_rne(y2, y3));
                 });
@@ -791,6 +808,7 @@ gemm_fp6_mma_kernel(Fp6Args a) {
         const int64_t t = t0 + wt * C::FT * 32 + j * 32 + li;
         const bool t_ok = t < a.T;
         const float sat = a.sa[t_ok ? t : a.T - 1];
+        const float zt = a.za ? a.za[t_ok ? t : a.T - 1] : 8.0f;
         static_for<C::FN>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
             static_for<4>([&](auto qc) {
@@ -798,7 +816,7 @@ gemm_fp6_mma_kernel(Fp6Args a) {
                 const int nb = n0 + wn * C::FN * 32 + i * 32 + 8 * q + 4 * lg;
                 const float lr4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
                 if (t_ok && nb < a.N)
-                    store4<false>(a, t, nb, sat, acc[i][j][4 * q + 0], acc[i][j][4 * q + 1],
+                    store4<false>(a, t, nb, sat, zt, acc[i][j][4 * q + 0], acc[i][j][4 * q + 1],
                                   acc[i][j][4 * q + 2], acc[i][j][4 * q + 3], lr4);
             });
         });
@@ -827,9 +845,12 @@ using CfgMid = Cfg<128, 128, 2, 2, 3, 2>;
 }  // namespace
 
 int launch_gemm_fp6(const uint8_t *codes, const uint8_t *codes_mma, const float *scale,
-                    const uint16_t *top, int64_t T, const rq_weight_header *hdr, const void *blob,
-                    const float *bias, void *Y, int y_dtype, void *stream) {
+                    const float *zero, const uint16_t *top, int64_t T,
+                    const rq_weight_header *hdr, const void *blob, const float *bias, void *Y,
+                    int y_dtype, void *stream) {
     Fp6Args a;
+    a.za = zero;
+    a.flip = zero ? 0u : 0x88888888u;
     const uint8_t *base = static_cast<const uint8_t *>(blob);
     a.A = codes;
     a.Amma = codes_mma;

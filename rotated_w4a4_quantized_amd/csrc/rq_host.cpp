@@ -55,8 +55,10 @@ rq_status check_rotation(const rq_rotation *rot, bool need_tables) {
 rq_status check_quant(const rq_rotation *rot, const rq_quant *q) {
     if (!q) return fail(RQ_ERR_NULL, "quantizer descriptor is NULL");
     if (q->a_bits != 4) return fail(RQ_ERR_UNSUPPORTED, "a_bits must be 4");
-    if (q->kind == RQ_Q_INT4_SYM) {
-        if (q->w_bits != 4) return fail(RQ_ERR_UNSUPPORTED, "INT4_SYM needs w_bits == 4");
+    if (q->kind == RQ_Q_INT4_SYM || q->kind == RQ_Q_INT4_ASYM) {
+        if (q->w_bits != 4) return fail(RQ_ERR_UNSUPPORTED, "INT4 needs w_bits == 4");
+        if (q->kind == RQ_Q_INT4_ASYM && rot->kind != RQ_ROT_RPBH)
+            return fail(RQ_ERR_UNSUPPORTED, "INT4_ASYM is built for the RPBH rotation only");
     } else if (q->kind == RQ_Q_LLOYDMAX) {
         if (q->w_bits != 2 && q->w_bits != 4)
             return fail(RQ_ERR_UNSUPPORTED, "LLOYDMAX needs w_bits 2 or 4");
@@ -136,11 +138,11 @@ static BlobLayout blob_layout(const rq_rotation *rot, const rq_quant *q, int32_t
     const int K = rot->K;
     const int r = rot->kind == RQ_ROT_DENSE ? rot->r : 0;
     BlobLayout L;
-    L.row_bytes = (q->kind == RQ_Q_INT4_SYM || q->w_bits == 4) ? K / 2 : K / 4;
+    L.row_bytes = (q->kind != RQ_Q_LLOYDMAX || q->w_bits == 4) ? K / 2 : K / 4;
     L.scale_off = (int64_t)sizeof(rq_weight_header);
     L.codes_off = L.scale_off + round256((int64_t)N * 4);
     const int64_t end = L.codes_off + round256((int64_t)N * L.row_bytes);
-    if (q->kind == RQ_Q_INT4_SYM) {
+    if (q->kind != RQ_Q_LLOYDMAX) {   // INT4 weights (either activation quantizer)
         L.mma_stages = (K - r + 127) / 128;
         L.mma_ntiles = (N + 31) / 32;
         L.wsum_off = end;
@@ -293,7 +295,7 @@ rq_status rq_pack_weights(const rq_rotation *rot, const rq_quant *q, const void 
             else
                 fold_dense(w.data(), K, rot->R, v.data());
             uint8_t *row = codes + (size_t)n * rb;
-            if (q->kind == RQ_Q_INT4_SYM) {
+            if (q->kind != RQ_Q_LLOYDMAX) {   // symmetric INT4 weights (both INT4 kinds)
                 double amax = 0.0;
                 for (int k = 0; k < K; ++k) amax = std::max(amax, std::fabs(v[k]));
                 if (amax == 0.0) {
@@ -340,7 +342,7 @@ rq_status rq_pack_weights(const rq_rotation *rot, const rq_quant *q, const void 
         if (n0 < n1) pool.emplace_back(work, n0, n1);
     }
     for (auto &th : pool) th.join();
-    if (q->kind == RQ_Q_INT4_SYM) {
+    if (q->kind != RQ_Q_LLOYDMAX) {
         // the GEMM's copy of the quantized coordinates [r, K): row sums and
         // FP6 fragments (see pack_mma_tile)
         const int r = hdr.r, Kq = K - r;

@@ -28,9 +28,10 @@ inline int64_t mma_codes_bytes(int64_t T, int Kq) {
 
 // Kernel launchers (rq_rpbh.hip, rq_dense.hip, rq_gemm_*.hip).  Arguments are validated
 // by the caller; these only launch.  They return a hipError_t as int.
+// asym: per-token zero point (INT4_ASYM), written to scale[T .. 2T)
 int launch_rpbh_int4(const void *X, int x_bf16, int64_t T, int K, int block,
                      const int8_t *sign, const int32_t *perm, uint8_t *codes,
-                     uint8_t *codes_mma, float *scale, void *stream);
+                     uint8_t *codes_mma, float *scale, int asym, void *stream);
 int launch_rpbh_lloydmax(const void *X, int x_bf16, int64_t T, int K, int block,
                          const int8_t *sign, const int32_t *perm, const float *thresholds,
                          int n_thresholds, uint8_t *codes, float *sigma, void *stream);
@@ -41,9 +42,11 @@ int launch_dense_quant(const float *U, int64_t T, int K, int r, uint8_t *codes,
 int launch_gemm_w4a4(const uint8_t *codes, const float *scale, const uint16_t *top,
                      int64_t T, const rq_weight_header *hdr, const void *blob,
                      const float *bias, void *Y, int y_dtype, void *stream);
+// zero: per-token zero points of INT4_ASYM activations, or null (symmetric)
 int launch_gemm_fp6(const uint8_t *codes, const uint8_t *codes_mma, const float *scale,
-                    const uint16_t *top, int64_t T, const rq_weight_header *hdr,
-                    const void *blob, const float *bias, void *Y, int y_dtype, void *stream);
+                    const float *zero, const uint16_t *top, int64_t T,
+                    const rq_weight_header *hdr, const void *blob, const float *bias, void *Y,
+                    int y_dtype, void *stream);
 int launch_gemm_codebook(const uint8_t *codes, const float *sigma, int64_t T,
                          const rq_weight_header *hdr, const void *blob,
                          const float *bias, void *Y, int y_dtype, void *stream);

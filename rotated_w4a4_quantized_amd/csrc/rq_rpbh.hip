@@ -1,6 +1,7 @@
 // rq_rpbh.hip -- runtime activation path for gfx950 with the randomized
 // permuted block-Hadamard (RPBH) rotation, then per-token 4-bit
-// quantization: symmetric INT4, or the Lloyd-Max codebook on the
+// quantization: symmetric INT4, asymmetric INT4 with a zero point ("TR-DQ"
+// section 3.1, Eq.(1)-(3)), or the Lloyd-Max codebook on the
 // norm-normalized token.
 //
 // Rotation ("OrbitQuant" abstract; block structure "TR-DQ" Eq.(8)):
@@ -21,8 +22,9 @@
 //   pass p   one LDS exchange, then up to four more stages in registers; the
 //            register set of every pass after the first also carries index
 //            bit 0, so the final values of each nibble pair sit in one thread;
-//   stat     per-token absmax (and for the codebook the exact integer-grid
-//            squared norm) by shuffles and one LDS atomic per lane group;
+//   stat     per-token absmax (asymmetric: min and max; for the codebook
+//            also the exact integer-grid squared norm) by shuffles and one
+//            LDS atomic per lane group;
 //   codes    nibbles are packed from registers and regrouped through LDS
 //            into 16 contiguous bytes per 32 coordinates; the canonical
 //            layout is stored with one 16-byte store per thread.  For the
@@ -154,6 +156,16 @@ __host__ __device__ constexpr int cbytes(int K) { return L <= 5 ? K / 2 : K / 2 
 template <int L>
 __host__ __device__ constexpr int chunk_off(int c) { return L <= 5 ? 16 * c : cpad<L>(16 * c); }
 
+// Order-preserving 32-bit key of a float (for LDS atomic min / max over
+// values of either sign) and its inverse.
+__device__ inline unsigned fkey(float f) {
+    const unsigned b = __float_as_uint(f);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ inline float fkey_inv(unsigned k) {
+    return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
 struct RpbhArgs {
     const void *X;
     int64_t T;
@@ -169,7 +181,7 @@ struct RpbhArgs {
     int gsz_log2;         // tokens per group: a workgroup's unit of work
     int ipg_log2;         // iterations per group (group size / tpw)
     int64_t ngroups;
-    float *scale;
+    float *scale;         // s or sigma [T]; asymmetric INT4: s [T] then z [T]
     float th[15];         // codebook thresholds (Lloyd-Max)
 };
 
@@ -190,8 +202,11 @@ template <int L, bool BF16, int QK>
 __global__ void __launch_bounds__(512)
 rpbh_quant_kernel(RpbhArgs a) {
     using S = Src<BF16>;
+    // MMA-layout fields: symmetric codes carried as q + 8, unsigned as they are
+    constexpr uint32_t kFlip = QK == 2 ? 0u : 0x88888888u;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ unsigned red_max[2][kMaxTpw];
+    __shared__ unsigned red_min[2][kMaxTpw];   // asymmetric INT4 (keys)
     __shared__ unsigned long long red_sum[2][kMaxTpw];
     const int K = a.K;
     const int tid = threadIdx.x;
@@ -296,10 +311,10 @@ rpbh_quant_kernel(RpbhArgs a) {
             const uint4 w0 = *reinterpret_cast<const uint4 *>(slot + chunk_off<L>(c0));
             const uint4 w1 = c1 < nch ? *reinterpret_cast<const uint4 *>(slot + chunk_off<L>(c1))
                                       : make_uint4(0u, 0u, 0u, 0u);
-            store_pair_mma(a.codes_mma, t, a.mma_stages, sh >> 1, sh & 1, w0, w1, c1 < nch);
+            store_pair_mma(a.codes_mma, t, a.mma_stages, sh >> 1, sh & 1, w0, w1, c1 < nch, kFlip);
         }
     };
-    const bool grouped = QK == 0 && a.grouped;
+    const bool grouped = QK != 1 && a.grouped;
 
     // lane groups of one token for the shuffle reductions
     int grp = 64;
@@ -313,6 +328,7 @@ rpbh_quant_kernel(RpbhArgs a) {
         if (tt == 0) {
             red_max[it & 1][tl] = 0u;
             if constexpr (QK == 1) red_sum[it & 1][tl] = 0ull;
+            if constexpr (QK == 2) red_min[it & 1][tl] = 0xFFFFFFFFu;
         }
         float v[kE];
 #pragma unroll
@@ -347,17 +363,55 @@ rpbh_quant_kernel(RpbhArgs a) {
         static_assert(Plan<L>::NP <= 3, "block too large");
         constexpr int PL = Plan<L>::NP - 1;
 
-        float m = 0.0f;
+        if constexpr (QK == 2) {
+            float lo = v[0], hi = v[0];
 #pragma unroll
-        for (int r = 0; r < kE; ++r) m = fmaxf(m, fabsf(v[r]));
-        for (int off = 1; off < grp; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-        if ((tid & (grp - 1)) == 0) atomicMax(&red_max[it & 1][tl], __float_as_uint(m));
+            for (int r = 1; r < kE; ++r) {
+                lo = fminf(lo, v[r]);
+                hi = fmaxf(hi, v[r]);
+            }
+            for (int off = 1; off < grp; off <<= 1) {
+                lo = fminf(lo, __shfl_xor(lo, off, 64));
+                hi = fmaxf(hi, __shfl_xor(hi, off, 64));
+            }
+            if ((tid & (grp - 1)) == 0) {
+                atomicMin(&red_min[it & 1][tl], fkey(lo));
+                atomicMax(&red_max[it & 1][tl], fkey(hi));
+            }
+        } else {
+            float m = 0.0f;
+#pragma unroll
+            for (int r = 0; r < kE; ++r) m = fmaxf(m, fabsf(v[r]));
+            for (int off = 1; off < grp; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+            if ((tid & (grp - 1)) == 0) atomicMax(&red_max[it & 1][tl], __float_as_uint(m));
+        }
         lds_barrier();  // B2: statistic complete, next token staged
         const float amax = __uint_as_float(red_max[it & 1][tl]);
 
         uint32_t nib[kE];
-        float sc = 0.0f;
-        if constexpr (QK == 0) {
+        float sc = 0.0f, zp = 0.0f;
+        if constexpr (QK == 2) {
+            // s = fl32(d / 15), inv = fl32(15 / d), z = clamp(-rne(fl32(lo inv)), 0, 15),
+            // q = clamp(rne(fl32(u inv)) + z, 0, 15); the float sum is exact
+            // wherever the clamp does not bind
+            const float lo = fkey_inv(red_min[it & 1][tl]);
+            const float hi = fkey_inv(red_max[it & 1][tl]);
+            const float d = hi - lo;
+            if (d != 0.0f) {
+                const float inv = 15.0f / d;
+                sc = d / 15.0f;
+                const float zr = rintf(lo * inv);
+                zp = zr > 0.0f ? 0.0f : (zr < -15.0f ? 15.0f : -zr);
+#pragma unroll
+                for (int r = 0; r < kE; ++r) {
+                    const float t = fminf(fmaxf(rintf(v[r] * inv) + zp, 0.0f), 15.0f);
+                    nib[r] = (uint32_t)t;
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < kE; ++r) nib[r] = 0u;
+            }
+        } else if constexpr (QK == 0) {
             // q = rne(fl32(u * inv)) lands in [-7, 7]: |u * inv| <= fl32(7 (1 + 2^-24)) = 7,
             // so no clamp is needed.  Adding 1.5 * 2^23 rounds to an integer
             // (nearest-even) and leaves q in the low bits, two's complement.
@@ -432,8 +486,13 @@ rpbh_quant_kernel(RpbhArgs a) {
         if (valid) {
             if (a.codes) *reinterpret_cast<uint4 *>(a.codes + tok * (int64_t)(K / 2) + 16 * tt) = chunk;
             if constexpr (QK == 0)
-                if (a.codes_mma && !grouped) store_chunk_mma(a.codes_mma, tok, a.mma_stages, tt, chunk);
-            if (tt == 0) a.scale[tok] = sc;
+                if (a.codes_mma && !grouped) store_chunk_mma(a.codes_mma, tok, a.mma_stages, tt, chunk, kFlip);
+            if constexpr (QK == 2)
+                if (a.codes_mma && !grouped) store_chunk_mma(a.codes_mma, tok, a.mma_stages, tt, chunk, kFlip);
+            if (tt == 0) {
+                a.scale[tok] = sc;
+                if constexpr (QK == 2) a.scale[a.T + tok] = zp;
+            }
         }
         base = next;
     }
@@ -466,7 +525,7 @@ hipError_t launch_L(RpbhArgs a, hipStream_t s) {
     constexpr size_t kLdsMax = 159 * 1024;
     // MMA-layout codes are written per group of >= 4 consecutive tokens when
     // the group's code slots fit, else per token
-    const bool grouped = QK == 0 && a.codes_mma != nullptr && per_tok + 4 * slot_bytes <= kLdsMax;
+    const bool grouped = QK != 1 && a.codes_mma != nullptr && per_tok + 4 * slot_bytes <= kLdsMax;
     a.grouped = grouped ? 1 : 0;
     // per-token code staging: the regrouping exchange (blocks > 32), or the
     // group's slots
@@ -559,10 +618,11 @@ RpbhArgs make_args(const void *X, int64_t T, int K, const int8_t *sign, const in
 
 int launch_rpbh_int4(const void *X, int x_bf16, int64_t T, int K, int block, const int8_t *sign,
                      const int32_t *perm, uint8_t *codes, uint8_t *codes_mma, float *scale,
-                     void *stream) {
+                     int asym, void *stream) {
     RpbhArgs a = make_args(X, T, K, sign, perm, codes, codes_mma, scale);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int L = ilog2(block);
+    if (asym) return (int)(x_bf16 ? dispatch<true, 2>(L, a, s) : dispatch<false, 2>(L, a, s));
     return (int)(x_bf16 ? dispatch<true, 0>(L, a, s) : dispatch<false, 0>(L, a, s));
 }
 

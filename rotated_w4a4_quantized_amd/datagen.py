@@ -37,7 +37,7 @@ class Workload:
     rot: str            # "rpbh" | "dense"
     block: int          # RPBH block (0 for dense)
     r: int              # top-r kept in bf16 (dense only)
-    quant: str          # "int4" | "lloydmax"
+    quant: str          # "int4" | "int4_asym" | "lloydmax"
     xdtype: str         # "f32" | "bf16"
     ydtype: str         # "f32" | "bf16"
     x_kind: str         # distribution recipe of X
@@ -71,6 +71,12 @@ WORKLOADS = {
                         "gauss_outlier16x30"),
     "flux_down": Workload("flux_down", 3, 9216, 12288, 3072, "rpbh", 512, 0, "int4", "bf16",
                           "bf16", "gelu"),
+    # the FLUX layers with asymmetric per-token activations (zero point): same
+    # seeds, so the same X, W and rotation as flux_up / flux_down
+    "flux_up_asym": Workload("flux_up_asym", 2, 9216, 3072, 12288, "rpbh", 256, 0, "int4_asym",
+                             "bf16", "bf16", "gauss_outlier16x30"),
+    "flux_down_asym": Workload("flux_down_asym", 3, 9216, 12288, 3072, "rpbh", 512, 0, "int4_asym",
+                               "bf16", "bf16", "gelu"),
     "video": Workload("video", 4, 32760, 1536, 8960, "rpbh", 256, 0, "lloydmax", "bf16", "bf16",
                       "gauss", a_bits=4, w_bits=2),
 }

@@ -32,6 +32,8 @@ def rotation_for(w, inp) -> rq.Rotation:
 def quant_for(w) -> rq.Quant:
     if w.quant == "int4":
         return rq.Quant.int4()
+    if w.quant == "int4_asym":
+        return rq.Quant.int4_asym()
     return rq.Quant.lloydmax(rq.lloydmax_gaussian(16), rq.lloydmax_gaussian(1 << w.w_bits))
 
 
@@ -55,7 +57,7 @@ class QuantLinear:
         self.X = device_x(inp, device)
         T = w.T
         ncode = (w.Kq // 2)
-        mma_ok = w.rot == "rpbh" and w.quant == "int4"
+        mma_ok = w.rot == "rpbh" and w.quant in ("int4", "int4_asym")
         if codes not in ("canonical", "mma", "both") or (codes != "canonical" and not mma_ok):
             raise ValueError(f"codes={codes!r} is not available for {w.name}")
         self.codes = (torch.empty((T, ncode), dtype=torch.uint8, device=device)
@@ -64,7 +66,8 @@ class QuantLinear:
         if codes != "canonical":
             nb = rq.codes_mma_bytes(self.rot, T)
             self.codes_mma = torch.empty((max(nb, 16),), dtype=torch.uint8, device=device)
-        self.scale = torch.empty((T,), dtype=torch.float32, device=device)
+        # INT4_ASYM: s [T] then the zero points [T]
+        self.scale = torch.empty((self.q.scale_rows * T,), dtype=torch.float32, device=device)
         self.top = torch.empty((T, w.r), dtype=torch.int16, device=device) if w.r else None
         wsb = rq.rotate_quant_workspace_bytes(self.rot, self.q, T)
         self.ws = torch.empty((max(wsb, 16) // 4,), dtype=torch.float32, device=device) if wsb else None

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "librq.so")
 RQ_OK = 0
 RQ_F32, RQ_BF16, RQ_I32 = 0, 1, 2
 RQ_ROT_RPBH, RQ_ROT_DENSE = 0, 1
-RQ_Q_INT4_SYM, RQ_Q_LLOYDMAX = 0, 1
+RQ_Q_INT4_SYM, RQ_Q_LLOYDMAX, RQ_Q_INT4_ASYM = 0, 1, 2
 RQ_WEIGHT_MAGIC = 0x31575152
 STATUS_NAMES = {0: "RQ_OK", -1: "RQ_ERR_NULL", -2: "RQ_ERR_SHAPE", -3: "RQ_ERR_DTYPE",
                 -4: "RQ_ERR_ALIGN", -5: "RQ_ERR_FORMAT", -6: "RQ_ERR_UNSUPPORTED",
@@ -195,6 +195,16 @@ class Quant:
         return Quant(RQ_Q_INT4_SYM, 4, 4)
 
     @staticmethod
+    def int4_asym():
+        """Asymmetric per-token INT4 activations (zero point), INT4 weights."""
+        return Quant(RQ_Q_INT4_ASYM, 4, 4)
+
+    @property
+    def scale_rows(self) -> int:
+        """Rows of the fp32 scale output per token set: 2 (s, z) for INT4_ASYM."""
+        return 2 if self.kind == RQ_Q_INT4_ASYM else 1
+
+    @staticmethod
     def lloydmax(a_levels, w_levels):
         a = np.ascontiguousarray(a_levels, np.float32)
         w = np.ascontiguousarray(w_levels, np.float32)
@@ -322,7 +332,8 @@ def codes_mma_bytes(rot: Rotation, T: int) -> int:
 def rotate_quant(drot: DeviceRotation, q: Quant, X, codes, scale, top=None, workspace=None,
                  stream=None, codes_mma=None):
     """Launch the activation kernels on `stream` (default: torch's current).
-    codes and/or codes_mma (the GEMM's FP6 fragment layout) receive the codes."""
+    codes and/or codes_mma (the GEMM's FP6 fragment layout) receive the codes;
+    scale holds T floats, or 2T (s then z) for INT4_ASYM."""
     cr, cq = drot.c_dev(), q.c()
     T = int(X.shape[0])
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -26,6 +26,9 @@ def oracle_act(w, inp, rows=None):
         if w.quant == "int4":
             return orc.act_rows(inp["X"], xd, w.K, rows, rot_kind=0, b=w.block, sign=inp["sign"],
                                 perm=inp["perm"])
+        if w.quant == "int4_asym":
+            return orc.act_rows(inp["X"], xd, w.K, rows, rot_kind=0, b=w.block, sign=inp["sign"],
+                                perm=inp["perm"], q_kind=2)
         return orc.act_rows(inp["X"], xd, w.K, rows, rot_kind=0, b=w.block, sign=inp["sign"],
                             perm=inp["perm"], q_kind=1, levels=orc.codebook_bf16(16))
     return orc.act_rows(inp["X"], xd, w.K, rows, rot_kind=1, R=inp["R"], r=w.r)
@@ -33,7 +36,7 @@ def oracle_act(w, inp, rows=None):
 
 def oracle_weights(w, inp):
     if w.rot == "rpbh":
-        if w.quant == "int4":
+        if w.quant in ("int4", "int4_asym"):   # INT4 weights are symmetric either way
             return orc.weight_rows(inp["W"], rot_kind=0, b=w.block, sign=inp["sign"], perm=inp["perm"])
         return orc.weight_rows(inp["W"], rot_kind=0, b=w.block, sign=inp["sign"], perm=inp["perm"],
                                q_kind=1, levels=orc.codebook_bf16(1 << w.w_bits))
@@ -48,11 +51,28 @@ def oracle_yhat_pairs(w, act, wts, ta, nw, act_rows=None):
         dot = orc.codebook_dot_pairs(act["codes"], wts["codes"], w.K, orc.codebook_bf16(16),
                                      orc.codebook_bf16(1 << w.w_bits), ia, nw)
         return orc.yhat_codebook(act["scale"][ia], wts["scale"][nw], dot, w.block)
+    if w.quant == "int4_asym":
+        acc_u = orc.asym_gemm_pairs(act["codes"], wts["codes"], w.K, ia, nw)
+        wsum = wts["q"].astype(np.int64).sum(axis=1)
+        return orc.yhat_int4_asym(act["scale"][ia], act["zero"][ia], wts["scale"][nw], acc_u,
+                                  wsum[nw], w.b_eff)
     acc = orc.int_gemm_pairs(act["codes"], w.Kq, wts["codes"], w.K, ia, nw, koff=w.r)
     lr = None
     if w.r:
         lr = orc.lowrank_pairs(act["top"], w.r, wts["codes"], w.K, ia, nw)
     return orc.yhat_int4(act["scale"][ia], wts["scale"][nw], acc, w.b_eff, lr=lr)
+
+
+def oracle_raw_acc(w, act, wts):
+    """Exact int64 accumulators [T][N] that RQ_I32 output returns:
+    sum_k q_a q_w, with q_a = u - z for asymmetric activations."""
+    if w.quant == "int4_asym":
+        T, N = act["codes"].shape[0], wts["codes"].shape[0]
+        ta, nw = np.meshgrid(np.arange(T), np.arange(N), indexing="ij")
+        acc_u = orc.asym_gemm_pairs(act["codes"], wts["codes"], w.K, ta.ravel(), nw.ravel())
+        wsum = wts["q"].astype(np.int64).sum(axis=1)
+        return acc_u.reshape(T, N) - act["zero"].astype(np.int64)[:, None] * wsum[None, :]
+    return orc.int_gemm(act["codes"], w.Kq, wts["codes"], w.K, koff=w.r)
 
 
 def rel_err(y, yhat):

@@ -294,3 +294,25 @@ def test_pack_rejects_bad_tables():
     with pytest.raises(TypeError):
         rq.pack_weights(rq.Rotation.rpbh(sign, np.arange(256, dtype=np.int32), 64), rq.Quant.int4(),
                         W.astype(np.float64))
+
+
+def test_int4_asym_descriptor_and_blob():
+    # asymmetric activations take the RPBH rotation only; their weights are the
+    # symmetric INT4 weights, tagged with the activation quantizer
+    qa = rq.Quant.int4_asym().c()
+    dense = rq.c_rotation(rq.RQ_ROT_DENSE, 256, 0, 32, None, None, 1 << 22)
+    assert _rq_call(dense, qa, top=1 << 23, ws=1 << 24, wsb=1 << 30) == -6
+    assert _rq_call(_rpbh(), qa, T=0, X=0, codes=0, scale=0) == 0
+    assert _rq_call(_rpbh(), qa, codes=None, mma=None) == -1
+    w = datagen.WORKLOADS["flux_up_asym"].with_shape(T=4, K=512, N=40, block=128)
+    inp = datagen.make_inputs(w)
+    rot = rq.Rotation.rpbh(inp["sign"], inp["perm"], w.block)
+    pa = rq.pack_weights(rot, rq.Quant.int4_asym(), inp["W"])
+    ps = rq.pack_weights(rot, rq.Quant.int4(), inp["W"])
+    assert pa.header.format == rq.RQ_Q_INT4_ASYM and ps.header.format == rq.RQ_Q_INT4_SYM
+    assert np.array_equal(pa.codes(), ps.codes()) and np.array_equal(pa.scales(), ps.scales())
+    assert np.array_equal(pa.wsum(), ps.wsum()) and np.array_equal(pa.mma_tiles(), ps.mma_tiles())
+    n = ctypes.c_size_t(0)
+    rd = rq.Rotation.dense(np.eye(512, dtype=np.float32), 0)
+    assert rq.load().rq_packed_weight_bytes(ctypes.byref(rd.c_host()), ctypes.byref(qa), 40,
+                                            ctypes.byref(n)) == -6

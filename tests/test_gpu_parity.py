@@ -36,12 +36,20 @@ def say(msg):
 def mma_mode(w):
     """Layer mode for the parity runs: RPBH INT4 layers write both code
     layouts and the GEMM reads the MMA copy."""
-    return "both" if (w.rot == "rpbh" and w.quant == "int4") else "canonical"
+    return "both" if (w.rot == "rpbh" and w.quant in ("int4", "int4_asym")) else "canonical"
 
 
 def check_act(w, L, act, rows=None):
     codes = L.codes.cpu().numpy()
     scale = L.scale.cpu().numpy()
+    asym = w.quant == "int4_asym"
+    if asym:   # s [T] then the zero points [T]
+        zero = scale[w.T:]
+        scale = scale[:w.T]
+        if rows is not None:
+            zero = zero[rows]
+        assert np.array_equal(zero.view(np.uint32), act["zero"].view(np.uint32)), \
+            f"zero point mismatch in {int(np.sum(zero != act['zero']))} tokens"
     if rows is not None:
         codes, scale = codes[rows], scale[rows]
     assert np.array_equal(scale.view(np.uint32), act["scale"].view(np.uint32)), \
@@ -54,6 +62,8 @@ def check_act(w, L, act, rows=None):
             dec = dec[rows]
         assert top_clear, "a codes_mma field has its top bits set"
         ref = H.unpack_codes(act["codes"])
+        if asym:   # fields hold the unsigned codes: decoded as u - 8
+            ref = (ref & 15) - 8
         bad = np.nonzero(np.any(dec != ref, axis=1))[0]
         assert bad.size == 0, f"codes_mma differs in {bad.size} tokens, first {bad[:5]}"
     if w.r:
@@ -77,6 +87,10 @@ SMALL = [
     # fp32 input at the largest K: the MMA codes are stored per token (a group
     # of four tokens' code slots does not fit in LDS beside the row)
     ("tiny", dict(T=37, K=16384, N=64, block=512)),
+    # asymmetric per-token activations (zero point)
+    ("flux_up_asym", dict(T=257, K=3072, N=384)),
+    ("flux_down_asym", dict(T=131, K=12288, N=136)),
+    ("flux_up_asym", dict(T=33, K=96, N=40, block=2)),
 ]
 
 
@@ -100,9 +114,8 @@ def test_small_full_parity(name, shape):
     err = H.rel_err(y, yhat)
     say(f"  fp32 output max floored rel err {err:.3e}")
     assert err <= H.REL_TOL
-    if w.quant == "int4":
-        import oracle.oracle as orc
-        ref = orc.int_gemm(act["codes"], w.Kq, wts["codes"], w.K, koff=w.r)
+    if w.quant in ("int4", "int4_asym"):
+        ref = H.oracle_raw_acc(w, act, wts)
         acc = L.raw_acc().cpu().numpy().astype(np.int64)
         assert np.array_equal(acc, ref)
         if L.codes_mma is not None:
@@ -122,7 +135,7 @@ def test_small_full_parity(name, shape):
     assert ok
 
 
-FULL = ["tiny", "flux_up", "flux_down", "video", "pixart"]
+FULL = ["tiny", "flux_up", "flux_down", "video", "pixart", "flux_up_asym", "flux_down_asym"]
 
 
 @pytest.mark.parametrize("name", FULL)
