@@ -768,38 +768,57 @@ gemm_fp6_mma_kernel(Fp6Args a) {
         float sat[C::FT], zt[C::FT];
 #pragma unroll
         for (int j = 0; j < C::FT; ++j) {
-            sat[j] = e_sa[wt * C::FT * 32 + j * 32 + li] * a.post;
             const int tl = wt * C::FT * 32 + j * 32 + li;
+            sat[j] = e_sa[tl] * a.post;
             zt[j] = !a.za ? 8.0f : za_lds ? e_za[tl] : a.za[t0 + tl];
         }
-        static_for<C::FN>([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
-            static_for<4>([&](auto qc) {
-                constexpr int q = decltype(qc)::value;
-                const int nl = wn * C::FN * 32 + i * 32 + 8 * q + 4 * lg;
-                const float4 sw4 = *reinterpret_cast<const float4 *>(e_sw + nl);
-                const int4 ws4 = *reinterpret_cast<const int4 *>(e_ws + nl);
-                const float w0 = (float)ws4.x, w1 = (float)ws4.y, w2 = (float)ws4.z, w3 = (float)ws4.w;
-                static_for<C::FT>([&](auto jc) {
-                    constexpr int j = decltype(jc)::value;
-                    const int tl = wt * C::FT * 32 + j * 32 + li;
-                    // zt * w is an exact integer below 2^24
-                    const float y0 = (acc[i][j][4 * q + 0] - zt[j] * w0) * (sat[j] * sw4.x);
-                    const float y1 = (acc[i][j][4 * q + 1] - zt[j] * w1) * (sat[j] * sw4.y);
-                    const float y2 = (acc[i][j][4 * q + 2] - zt[j] * w2) * (sat[j] * sw4.z);
-                    const float y3 = (acc[i][j][4 * q + 3] - zt[j] * w3) * (sat[j] * sw4.w);
-                    *reinterpret_cast<uint2 *>(lds + tl * kOutStride + 2 * nl) =
-                        make_uint2(bf16x2_rne(y0, y1), bf16x2_rne(y2, y3));
+        // y = (acc - zt wsum[n]) (s_a post s_w): zt wsum is an exact integer
+        // below 2^24 (zt = 8 for symmetric codes: one offset per channel)
+        auto scale_tile = [&](auto asym_c) {
+            constexpr bool ASYM = decltype(asym_c)::value;
+            static_for<C::FN>([&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                static_for<4>([&](auto qc) {
+                    constexpr int q = decltype(qc)::value;
+                    const int nl = wn * C::FN * 32 + i * 32 + 8 * q + 4 * lg;
+                    const float4 sw4 = *reinterpret_cast<const float4 *>(e_sw + nl);
+                    const int4 ws4 = *reinterpret_cast<const int4 *>(e_ws + nl);
+                    const float w0 = (float)ws4.x, w1 = (float)ws4.y, w2 = (float)ws4.z, w3 = (float)ws4.w;
+                    const float o0 = 8.0f * w0, o1 = 8.0f * w1, o2 = 8.0f * w2, o3 = 8.0f * w3;
+                    static_for<C::FT>([&](auto jc) {
+                        constexpr int j = decltype(jc)::value;
+                        const int tl = wt * C::FT * 32 + j * 32 + li;
+                        const float y0 = (acc[i][j][4 * q + 0] - (ASYM ? zt[j] * w0 : o0)) * (sat[j] * sw4.x);
+                        const float y1 = (acc[i][j][4 * q + 1] - (ASYM ? zt[j] * w1 : o1)) * (sat[j] * sw4.y);
+                        const float y2 = (acc[i][j][4 * q + 2] - (ASYM ? zt[j] * w2 : o2)) * (sat[j] * sw4.z);
+                        const float y3 = (acc[i][j][4 * q + 3] - (ASYM ? zt[j] * w3 : o3)) * (sat[j] * sw4.w);
+                        *reinterpret_cast<uint2 *>(lds + tl * kOutStride + 2 * nl) =
+                            make_uint2(bf16x2_rne(y0, y1), bf16x2_rne(y2, y3));
+                    });
                 });
             });
-        });
+        };
+        if (a.za) scale_tile(std::true_type());
+        else scale_tile(std::false_type());
         lds_barrier();
         constexpr int kChunksPerRow = C::BN * 2 / 16;
         constexpr int kChunks = C::BT * kChunksPerRow;
-        for (int c = tid; c < kChunks; c += C::NTH) {
-            const int row = c / kChunksPerRow, cc = c % kChunksPerRow;
-            const uint4 v = *reinterpret_cast<const uint4 *>(lds + row * kOutStride + 16 * cc);
-            *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.Y) + (t0 + row) * a.N + n0 + 8 * cc) = v;
+        static_assert(kChunks % (8 * C::NTH) == 0, "whole batches of eight chunks per thread");
+        // eight LDS reads in flight, then their eight stores
+        for (int c0 = tid; c0 < kChunks; c0 += 8 * C::NTH) {
+            uint4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int c = c0 + u * C::NTH;
+                v[u] = *reinterpret_cast<const uint4 *>(lds + (c / kChunksPerRow) * kOutStride +
+                                                        16 * (c % kChunksPerRow));
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int c = c0 + u * C::NTH;
+                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.Y) + (t0 + c / kChunksPerRow) * a.N +
+                                           n0 + 8 * (c % kChunksPerRow)) = v[u];
+            }
         }
         return;
     }
