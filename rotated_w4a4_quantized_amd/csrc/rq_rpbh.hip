@@ -47,6 +47,14 @@ namespace {
 
 constexpr int kE = 32;   // coordinates per thread
 constexpr int kMaxTpw = 16;
+// Threads per workgroup: bf16 input up to twelve waves, three per SIMD (at
+// most 168 registers per lane, which the kernel fits); fp32 input stages
+// twice the words per thread and keeps the 256-register budget of eight.
+template <bool BF16>
+constexpr int kMaxThreads = BF16 ? 768 : 512;
+// relative time per token of a workgroup that shares its CU with others
+// (their LDS, memory and VALU phases overlap), against one alone on the CU
+constexpr double kOverlap = 0.75;
 
 // Workgroup barrier that orders LDS only: waits for this wave's LDS
 // operations, not for its global loads and stores (a __syncthreads() would
@@ -118,30 +126,58 @@ __device__ inline void stages(float (&v)[kE]) {
     }
 }
 
-// Exchange buffer layout: coordinate j lives at j + (j >> 5) + (j >> L)
-// (one pad slot per 32 coordinates and one per block).  In every pass a
+// Exchanges.  A block's 2^(L-5) threads are adjacent lanes of one wave, so
+// every exchange stays inside a wave and needs only wave-level ordering (LDS
+// operations of one wave complete in issue order).  It runs in two rounds:
+// round h moves the coordinates with index bit 0 = h, which sit in the
+// registers of parity h in every pass, so one round needs a buffer of half a
+// token.  Half-coordinate m = j >> 1 lives at hslot(m).  In every pass a
 // thread's coordinates are base | roff(r) with disjoint bit fields, so the
 // slot splits into a per-thread base plus a per-register constant (an
-// immediate offset of the LDS instruction), and the pads spread the lanes of
-// one instruction over the banks: pass 0 lanes differ in bits 5..9, pass-1
-// lanes in the fixed low bits and the block bits.
+// immediate offset of the LDS instruction).  The pads put the 64 lanes of one
+// instruction on distinct banks in both access patterns for b >= 512, with at
+// most a two-way conflict for b = 64..256 (checked for 32 and 64 four-byte
+// banks).
 template <int L>
-__device__ inline int xbase(int b) { return b + (b >> 5) + (b >> L); }
-__host__ __device__ constexpr int xoff(int o) { return o + (o >> 5); }
-template <int L>
-__host__ __device__ constexpr int xwords(int K) { return (K + K / 32 + K / (1 << L) + 1 + 3) & ~3; }
-
-template <int L, int P>
-__device__ inline void put(float *us, int tt, const float (&v)[kE]) {
-    float *p = us + xbase<L>(pbase<L, P>(tt));
-#pragma unroll
-    for (int r = 0; r < kE; ++r) p[xoff(Plan<L>::roff(P, r))] = v[r];
+__host__ __device__ constexpr int hslot(int m) {
+    return L == 6 ? m + 8 * (m >> 4) + (m >> 6) : L == 7 ? m + 4 * (m >> 4) + (m >> 7) : m + (m >> 4);
 }
-template <int L, int P>
-__device__ inline void get(const float *us, int tt, float (&v)[kE]) {
-    const float *p = us + xbase<L>(pbase<L, P>(tt));
+// exchange words per token (blocks up to 32 need none, but the prologue's
+// inverse-permutation scratch needs the staging plus these words to hold K ints)
+template <int L>
+__host__ __device__ constexpr int xwords(int K) {
+    return L <= 5 ? ((K / 2 + 3) & ~3) : ((hslot<L>(K / 2 - 1) + 1 + 3) & ~3);
+}
+
+template <int L, int P, int H>
+__device__ inline void put(float *us, int tt, const float (&v)[kE]) {
+    float *p = us + hslot<L>(pbase<L, P>(tt) >> 1);
 #pragma unroll
-    for (int r = 0; r < kE; ++r) v[r] = p[xoff(Plan<L>::roff(P, r))];
+    for (int r = H; r < kE; r += 2) p[hslot<L>(Plan<L>::roff(P, r) >> 1)] = v[r];
+}
+template <int L, int P, int H>
+__device__ inline void get(const float *us, int tt, float (&v)[kE]) {
+    const float *p = us + hslot<L>(pbase<L, P>(tt) >> 1);
+#pragma unroll
+    for (int r = H; r < kE; r += 2) v[r] = p[hslot<L>(Plan<L>::roff(P, r) >> 1)];
+}
+// orders this wave's LDS accesses at the compiler level (the hardware keeps
+// one wave's LDS operations in order)
+__device__ inline void wave_lds_order() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+// pass P -> pass P + 1; round 0's put may already have been issued
+template <int L, int P, bool PUT0>
+__device__ inline void exchange(float *us, int tt, float (&v)[kE]) {
+    if constexpr (PUT0) put<L, P, 0>(us, tt, v);
+    wave_lds_order();
+    get<L, P + 1, 0>(us, tt, v);
+    wave_lds_order();
+    put<L, P, 1>(us, tt, v);
+    wave_lds_order();
+    get<L, P + 1, 1>(us, tt, v);
 }
 
 // Code staging layout: code byte q at q + 16 (q >> (L - 1)), i.e. 16 pad
@@ -199,7 +235,7 @@ __device__ inline uint32_t bf16_sign_mask(bool neg, int half) {
 }
 
 template <int L, bool BF16, int QK>
-__global__ void __launch_bounds__(512)
+__global__ void __launch_bounds__(kMaxThreads<BF16>)
 rpbh_quant_kernel(RpbhArgs a) {
     using S = Src<BF16>;
     // MMA-layout fields: symmetric codes carried as q + 8, unsigned as they are
@@ -220,18 +256,20 @@ rpbh_quant_kernel(RpbhArgs a) {
     uint8_t *const cs0 = smem + (size_t)a.tpw * (K * S::XB + 4 * xw);
 
     // ---- prologue: gather offsets, source-side sign masks -----------------
+    // (the inverse permutation, K ints, is built at the start of the dynamic
+    // LDS; every token's threads write the same values)
     int gofs[kE];
 #pragma unroll
     for (int r = 0; r < kE; ++r) gofs[r] = a.perm[kE * tt + r] * S::XB;
     {
-        int *inv = reinterpret_cast<int *>(us);
+        int *inv = reinterpret_cast<int *>(smem);
 #pragma unroll
         for (int r = 0; r < kE; ++r) inv[a.perm[kE * tt + r]] = kE * tt + r;
     }
     __syncthreads();
     uint32_t smask[S::WORDS];
     {
-        const int *inv = reinterpret_cast<const int *>(us);
+        const int *inv = reinterpret_cast<const int *>(smem);
 #pragma unroll
         for (int q = 0; q < S::CHUNKS; ++q) {
             const int e0 = S::ELEMS_PER_CHUNK * (tt + q * a.tpt);
@@ -339,7 +377,7 @@ rpbh_quant_kernel(RpbhArgs a) {
                 v[r] = *reinterpret_cast<const float *>(xs + gofs[r]);
         }
         stages<L, 0>(v);
-        if constexpr (Plan<L>::NP > 1) put<L, 0>(us, tt, v);
+        if constexpr (Plan<L>::NP > 1) put<L, 0, 0>(us, tt, v);   // exchange round 0
         lds_barrier();  // B1: every gather of this token is done
         const int64_t next = first_tok(it + 1);
         if (next >= 0) {
@@ -351,13 +389,11 @@ rpbh_quant_kernel(RpbhArgs a) {
         if (grouped && it > 0 && (it & ipg_mask) == 0)
             flush(vb + (int64_t)((it - 1) >> a.ipg_log2) * gridDim.x);
         if constexpr (Plan<L>::NP > 1) {
-            get<L, 1>(us, tt, v);
+            exchange<L, 0, false>(us, tt, v);
             stages<L, 1>(v);
         }
         if constexpr (Plan<L>::NP > 2) {
-            put<L, 1>(us, tt, v);
-            lds_barrier();
-            get<L, 2>(us, tt, v);
+            exchange<L, 1, true>(us, tt, v);
             stages<L, 2>(v);
         }
         static_assert(Plan<L>::NP <= 3, "block too large");
@@ -532,27 +568,51 @@ hipError_t launch_L(RpbhArgs a, hipStream_t s) {
     const size_t slot = (L <= 5 && !grouped) ? 0 : slot_bytes;
     auto group_of = [&](int tpw) { return grouped && tpw < 4 ? 4 : tpw; };
     auto lds_of = [&](int tpw) { return per_tok * tpw + slot * group_of(tpw); };
-    // Tokens per workgroup: <= 512 threads and <= 159 KB of LDS; two
-    // workgroups per CU when each fits in 78 KB, else one.  Every workgroup
-    // stays resident and loops over groups, so the candidate with the fewest
-    // tokens on the busiest CU wins; ties go to more waves per CU, then to
-    // the larger workgroup (fewer barriers per token).
+    auto kern = rpbh_quant_kernel<L, BF16, QK>;
+    // waves one SIMD holds given the kernel's registers (512 per lane)
+    static int simd_waves = 0;
+    if (simd_waves == 0) {
+        hipFuncAttributes fa;
+        int w = 2;
+        if (hipFuncGetAttributes(&fa, (const void *)kern) == hipSuccess && fa.numRegs > 0) {
+            w = 512 / ((fa.numRegs + 7) & ~7);
+            w = w < 1 ? 1 : (w > 8 ? 8 : w);
+        }
+        simd_waves = w;
+    }
+    // Tokens per workgroup (<= 768 or 512 threads, <= 159 KB of LDS) and workgroups
+    // per CU (as many as LDS and registers allow, or fewer).  A workgroup of
+    // w waves puts ceil(w / 4) of them on some SIMD, and co-resident
+    // workgroups are counted as landing on the same SIMDs (a pair of six-wave
+    // workgroups at three waves per SIMD was measured not to co-reside).
+    // Every workgroup stays resident and loops over groups.  The candidate
+    // with the fewest tokens on the busiest CU wins, counting a CU that runs
+    // several workgroups at once as kOverlap times as fast per workgroup as
+    // one that runs a single one; ties go to more waves per CU, then to the
+    // larger workgroup (fewer barriers per token).
     const int cus = num_cus();
-    int best_tpw = 1;
-    int64_t best_load = -1;
-    int best_waves = 0;
+    int best_tpw = 1, best_occ = 1, best_waves = 0;
+    double best_cost = -1.0;
     for (int tpw = 1; tpw <= kMaxTpw; tpw *= 2) {
-        if (tpw > 1 && (tpw * a.tpt > 512 || lds_of(tpw) > kLdsMax)) break;
-        const int occ = lds_of(tpw) <= 78 * 1024 ? 2 : 1;
+        if (tpw > 1 && (tpw * a.tpt > kMaxThreads<BF16> || lds_of(tpw) > kLdsMax)) break;
+        const int wpw = (tpw * a.tpt + 63) / 64;
+        int occ_max = (int)((160 * 1024) / (lds_of(tpw) + 1024));
+        const int by_regs = simd_waves / ((wpw + 3) / 4);
+        if (occ_max > by_regs) occ_max = by_regs;
+        if (occ_max < 1) occ_max = 1;
         const int gs = group_of(tpw);
         const int64_t groups = (a.T + gs - 1) / gs;
-        const int64_t wgs = (int64_t)cus * occ;
-        const int64_t load = (int64_t)occ * ((groups + wgs - 1) / wgs) * gs;
-        const int waves = occ * ((tpw * a.tpt + 63) / 64);
-        if (best_load < 0 || load < best_load || (load == best_load && waves >= best_waves)) {
-            best_load = load;
-            best_waves = waves;
-            best_tpw = tpw;
+        for (int occ = 1; occ <= occ_max; ++occ) {
+            const int64_t wgs = (int64_t)cus * occ;
+            const int64_t load = (int64_t)occ * ((groups + wgs - 1) / wgs) * gs;
+            const double cost = (double)load * (occ > 1 ? kOverlap : 1.0);
+            const int waves = occ * wpw;
+            if (best_cost < 0 || cost < best_cost || (cost == best_cost && waves >= best_waves)) {
+                best_cost = cost;
+                best_waves = waves;
+                best_tpw = tpw;
+                best_occ = occ;
+            }
         }
     }
     a.tpw = best_tpw;
@@ -561,9 +621,8 @@ hipError_t launch_L(RpbhArgs a, hipStream_t s) {
     a.ipg_log2 = ilog2(gs / best_tpw);
     a.ngroups = (a.T + gs - 1) / gs;
     const size_t lds = lds_of(best_tpw);
-    const int64_t resident = (int64_t)cus * (lds <= 78 * 1024 ? 2 : 1);
+    const int64_t resident = (int64_t)cus * best_occ;
     const int grid = (int)(a.ngroups < resident ? a.ngroups : resident);
-    auto kern = rpbh_quant_kernel<L, BF16, QK>;
     // raise the dynamic-LDS limit once per instantiation (the call is not free)
     static size_t lds_set = 0;
     if (lds > 64 * 1024 && lds > lds_set) {

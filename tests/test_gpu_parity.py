@@ -84,9 +84,11 @@ SMALL = [
     ("tiny", dict(T=65, K=96, N=40, block=2)),
     ("tiny", dict(T=33, K=32, N=7, block=8)),
     ("flux_up", dict(T=40, K=16384, N=64, block=512)),
-    # fp32 input at the largest K: the MMA codes are stored per token (a group
-    # of four tokens' code slots does not fit in LDS beside the row)
+    # fp32 input at the largest K: a group of four tokens' code slots fits in
+    # LDS beside the row at block 512; at block 64 (more padding) it does
+    # not, and the MMA codes are stored per token
     ("tiny", dict(T=37, K=16384, N=64, block=512)),
+    ("tiny", dict(T=37, K=16384, N=64, block=64)),
     # asymmetric per-token activations (zero point)
     ("flux_up_asym", dict(T=257, K=3072, N=384)),
     ("flux_down_asym", dict(T=131, K=12288, N=136)),
