@@ -89,6 +89,8 @@ typedef enum rq_q_kind { RQ_Q_INT4_SYM = 0, RQ_Q_LLOYDMAX = 1, RQ_Q_INT4_ASYM = 
  *   r      DENSE: coordinates kept in bf16, 0 <= r < K, r % 32 == 0; RPBH: 0
  *   sign   RPBH: int8 [K], each -1 or +1
  *   perm   RPBH: int32 [K], a permutation of 0..K-1 (not checked on device)
+ *          (rq_rotate_quant reads both as 16-byte vectors: the device copies
+ *          must be 16-byte aligned, else RQ_ERR_ALIGN)
  *   R      DENSE: fp32 [K][K] row-major, column j is basis vector j
  */
 typedef struct rq_rotation {

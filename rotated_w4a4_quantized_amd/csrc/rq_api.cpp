@@ -111,6 +111,8 @@ rq_status rq_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void 
     if (!aligned16(X) || (codes && !aligned16(codes)) || !aligned16(scale) ||
         (top && !aligned16(top)) || (codes_mma && !aligned16(codes_mma)))
         return fail(RQ_ERR_ALIGN, "device buffers must be 16-byte aligned");
+    if (!dense && (!aligned16(rot->sign) || !aligned16(rot->perm)))
+        return fail(RQ_ERR_ALIGN, "RPBH sign and perm must be 16-byte aligned");
     const int xb = x_dtype == RQ_BF16 ? 1 : 0;
     if (!dense) {
         if (int4)

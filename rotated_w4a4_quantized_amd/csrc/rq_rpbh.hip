@@ -142,11 +142,10 @@ template <int L>
 __host__ __device__ constexpr int hslot(int m) {
     return L == 6 ? m + 8 * (m >> 4) + (m >> 6) : L == 7 ? m + 4 * (m >> 4) + (m >> 7) : m + (m >> 4);
 }
-// exchange words per token (blocks up to 32 need none, but the prologue's
-// inverse-permutation scratch needs the staging plus these words to hold K ints)
+// exchange words per token (blocks up to 32 need none)
 template <int L>
 __host__ __device__ constexpr int xwords(int K) {
-    return L <= 5 ? ((K / 2 + 3) & ~3) : ((hslot<L>(K / 2 - 1) + 1 + 3) & ~3);
+    return L <= 5 ? 0 : ((hslot<L>(K / 2 - 1) + 1 + 3) & ~3);
 }
 
 template <int L, int P, int H>
@@ -230,10 +229,6 @@ struct Src {
     static constexpr int XB = BF16 ? 2 : 4;
 };
 
-__device__ inline uint32_t bf16_sign_mask(bool neg, int half) {
-    return neg ? (half ? 0x80000000u : 0x00008000u) : 0u;
-}
-
 template <int L, bool BF16, int QK>
 __global__ void __launch_bounds__(kMaxThreads<BF16>)
 rpbh_quant_kernel(RpbhArgs a) {
@@ -256,34 +251,52 @@ rpbh_quant_kernel(RpbhArgs a) {
     uint8_t *const cs0 = smem + (size_t)a.tpw * (K * S::XB + 4 * xw);
 
     // ---- prologue: gather offsets, source-side sign masks -----------------
-    // (the inverse permutation, K ints, is built at the start of the dynamic
-    // LDS; every token's threads write the same values)
+    // Thread tt owns destination coordinates j = 32 tt + r: it reads perm[j]
+    // and sign[j] contiguously, and writes the sign bit that source element
+    // perm[j] must carry into a table in the first token's staging row (one
+    // element per staging element, so the 16 bytes of the table that cover a
+    // staged 16-byte chunk are that chunk's XOR mask).  Only the first
+    // token's threads write it; every thread then reads its chunks' masks.
     int gofs[kE];
-#pragma unroll
-    for (int r = 0; r < kE; ++r) gofs[r] = a.perm[kE * tt + r] * S::XB;
     {
-        int *inv = reinterpret_cast<int *>(smem);
+        int pj[kE];
+        int8_t sj[kE];
 #pragma unroll
-        for (int r = 0; r < kE; ++r) inv[a.perm[kE * tt + r]] = kE * tt + r;
+        for (int r = 0; r < kE; r += 4) {
+            const int4 p4 = *reinterpret_cast<const int4 *>(a.perm + kE * tt + r);
+            pj[r] = p4.x;
+            pj[r + 1] = p4.y;
+            pj[r + 2] = p4.z;
+            pj[r + 3] = p4.w;
+        }
+#pragma unroll
+        for (int r = 0; r < kE; r += 16) {
+            const int4 s4 = *reinterpret_cast<const int4 *>(a.sign + kE * tt + r);
+            const int w[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sj[r + e] = (int8_t)(w[e >> 2] >> (8 * (e & 3)));
+        }
+#pragma unroll
+        for (int r = 0; r < kE; ++r) gofs[r] = pj[r] * S::XB;
+        if (tl == 0) {
+#pragma unroll
+            for (int r = 0; r < kE; ++r) {
+                if constexpr (BF16)
+                    *reinterpret_cast<uint16_t *>(smem + 2 * pj[r]) = sj[r] < 0 ? 0x8000u : 0u;
+                else
+                    *reinterpret_cast<uint32_t *>(smem + 4 * pj[r]) = sj[r] < 0 ? 0x80000000u : 0u;
+            }
+        }
     }
     __syncthreads();
     uint32_t smask[S::WORDS];
-    {
-        const int *inv = reinterpret_cast<const int *>(smem);
 #pragma unroll
-        for (int q = 0; q < S::CHUNKS; ++q) {
-            const int e0 = S::ELEMS_PER_CHUNK * (tt + q * a.tpt);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                if constexpr (BF16) {
-                    const int e = e0 + 2 * w;
-                    smask[4 * q + w] = bf16_sign_mask(a.sign[inv[e]] < 0, 0) |
-                                       bf16_sign_mask(a.sign[inv[e + 1]] < 0, 1);
-                } else {
-                    smask[4 * q + w] = a.sign[inv[e0 + w]] < 0 ? 0x80000000u : 0u;
-                }
-            }
-        }
+    for (int q = 0; q < S::CHUNKS; ++q) {
+        const uint4 m = *reinterpret_cast<const uint4 *>(smem + (size_t)16 * (tt + q * a.tpt));
+        smask[4 * q] = m.x;
+        smask[4 * q + 1] = m.y;
+        smask[4 * q + 2] = m.z;
+        smask[4 * q + 3] = m.w;
     }
     __syncthreads();
 

@@ -77,6 +77,10 @@ def test_rotate_quant_validation_errors():
     assert _rq_call(_rpbh(), q, X=0) == -1
     assert _rq_call(_rpbh(), q, codes=(1 << 20) + 8) == -4
     assert "aligned" in rq.load().rq_last_error().decode()
+    # the kernel reads sign and perm as 16-byte vectors
+    assert _rq_call(rq.c_rotation(rq.RQ_ROT_RPBH, 256, 64, 0, (1 << 20) + 4, 1 << 21, None), q) == -4
+    assert _rq_call(rq.c_rotation(rq.RQ_ROT_RPBH, 256, 64, 0, 1 << 20, (1 << 21) + 4, None), q) == -4
+    assert "sign and perm" in rq.load().rq_last_error().decode()
     # dense: r must be a multiple of 32 below K; workspace required; top required
     dense = rq.c_rotation(rq.RQ_ROT_DENSE, 256, 0, 16, None, None, 1 << 22)
     assert _rq_call(dense, q) == -2
