@@ -250,6 +250,31 @@ rpbh_quant_kernel(RpbhArgs a) {
     // code staging: one slot per token of the group
     uint8_t *const cs0 = smem + (size_t)a.tpw * (K * S::XB + 4 * xw);
 
+    // Workgroup b runs on XCD b % 8: number the workgroups XCD-major so that
+    // each XCD works on a contiguous range of tokens, whose 32-token tiles of
+    // the MMA-layout codes are then written from one L2.
+    int vb = blockIdx.x;
+    if (gridDim.x % 8 == 0) vb = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
+    // Iteration k of this workgroup takes group vb + (k / ipg) * grid, and in
+    // it tokens (k % ipg) tpw .. (k % ipg) tpw + tpw - 1; -1 past the end.
+    const int ipg_mask = (1 << a.ipg_log2) - 1;
+    auto first_tok = [&](int k) -> int64_t {
+        const int64_t g = vb + (int64_t)(k >> a.ipg_log2) * gridDim.x;
+        return g < a.ngroups ? (g << a.gsz_log2) + (int64_t)(k & ipg_mask) * a.tpw : -1;
+    };
+    int64_t base = first_tok(0);
+    uint4 pre[S::CHUNKS];
+    auto fetch = [&](int64_t b) {
+        int64_t tok = b + tl;
+        if (tok >= a.T) tok = a.T - 1;
+        const uint8_t *row = static_cast<const uint8_t *>(a.X) + tok * (int64_t)K * S::XB;
+#pragma unroll
+        for (int q = 0; q < S::CHUNKS; ++q)
+            pre[q] = *reinterpret_cast<const uint4 *>(row + (size_t)16 * (tt + q * a.tpt));
+    };
+    // the first token's row is in flight while the prologue runs
+    if (base >= 0) fetch(base);
+
     // ---- prologue: gather offsets, source-side sign masks -----------------
     // Thread tt owns destination coordinates j = 32 tt + r: it reads perm[j]
     // and sign[j] contiguously, and writes the sign bit that source element
@@ -300,28 +325,6 @@ rpbh_quant_kernel(RpbhArgs a) {
     }
     __syncthreads();
 
-    // Workgroup b runs on XCD b % 8: number the workgroups XCD-major so that
-    // each XCD works on a contiguous range of tokens, whose 32-token tiles of
-    // the MMA-layout codes are then written from one L2.
-    int vb = blockIdx.x;
-    if (gridDim.x % 8 == 0) vb = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
-    // Iteration k of this workgroup takes group vb + (k / ipg) * grid, and in
-    // it tokens (k % ipg) tpw .. (k % ipg) tpw + tpw - 1; -1 past the end.
-    const int ipg_mask = (1 << a.ipg_log2) - 1;
-    auto first_tok = [&](int k) -> int64_t {
-        const int64_t g = vb + (int64_t)(k >> a.ipg_log2) * gridDim.x;
-        return g < a.ngroups ? (g << a.gsz_log2) + (int64_t)(k & ipg_mask) * a.tpw : -1;
-    };
-    int64_t base = first_tok(0);
-    uint4 pre[S::CHUNKS];
-    auto fetch = [&](int64_t b) {
-        int64_t tok = b + tl;
-        if (tok >= a.T) tok = a.T - 1;
-        const uint8_t *row = static_cast<const uint8_t *>(a.X) + tok * (int64_t)K * S::XB;
-#pragma unroll
-        for (int q = 0; q < S::CHUNKS; ++q)
-            pre[q] = *reinterpret_cast<const uint4 *>(row + (size_t)16 * (tt + q * a.tpt));
-    };
     auto stage = [&]() {
 #pragma unroll
         for (int q = 0; q < S::CHUNKS; ++q) {
@@ -334,7 +337,6 @@ rpbh_quant_kernel(RpbhArgs a) {
         }
     };
     if (base >= 0) {
-        fetch(base);
         stage();
         const int64_t b1 = first_tok(1);
         if (b1 >= 0) fetch(b1);
