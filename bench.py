@@ -49,6 +49,7 @@ WORKLOADS = {
     "tiny": ["tiny"],
     "pixart": ["pixart"],
     "video": ["video"],
+    "video_w4": ["video_w4"],
 }
 
 

@@ -88,7 +88,7 @@ def _declare(L):
     L.orc_asym_gemm_pairs.argtypes = [_P, _I, _P, _P, _P, _I64, _P]
     L.orc_int_gemm.argtypes = [_P, _I, _I, _P, _I, _I, _I, _P]
     L.orc_lowrank_pairs.argtypes = [_P, _I, _P, _I, _P, _P, _I64, _P]
-    L.orc_codebook_dot_pairs.argtypes = [_P, _P, _I, _P, _P, _P, _P, _I64, _P]
+    L.orc_codebook_dot_pairs.argtypes = [_P, _P, _I, _I, _P, _P, _P, _P, _I64, _P]
     L.orc_num_threads.restype = _I
 
 
@@ -323,7 +323,8 @@ def weight_rows(W, *, rot_kind, b=0, sign=None, perm=None, R=None, q_kind=0, lev
     quantize (see orc_weight_rows).  Returns dict(codes, scale, q)."""
     W = np.ascontiguousarray(W, np.float32)
     N, K = W.shape
-    ncode = K // 2 if q_kind == 0 else K // 4
+    # INT4 and 16-level codebooks: nibbles; 4-level codebooks: crumbs
+    ncode = K // 2 if (q_kind == 0 or (levels is not None and len(levels) == 16)) else K // 4
     codes = np.zeros((N, ncode), np.uint8)
     scale = np.zeros(N, np.float32)
     q = np.zeros((N, K), np.int8)
@@ -379,11 +380,14 @@ def lowrank_pairs(top, r, codes_w, Kw, ta, nw):
 
 
 def codebook_dot_pairs(codes_a, codes_w, K, a_lv, w_lv, ta, nw):
+    """fp64 sum_k a_lv[ia] w_lv[iw] for listed pairs; the weight index width
+    (2 or 4 bits) follows the size of w_lv (4 or 16 levels)."""
     ta = np.ascontiguousarray(ta, np.int64)
     nw = np.ascontiguousarray(nw, np.int64)
     dot = np.zeros(ta.size, np.float64)
+    w_bits = {4: 2, 16: 4}[len(w_lv)]
     lib().orc_codebook_dot_pairs(_ptr(np.ascontiguousarray(codes_a, np.uint8)),
-                                 _ptr(np.ascontiguousarray(codes_w, np.uint8)), K,
+                                 _ptr(np.ascontiguousarray(codes_w, np.uint8)), K, w_bits,
                                  _ptr(np.ascontiguousarray(a_lv, np.float32)),
                                  _ptr(np.ascontiguousarray(w_lv, np.float32)),
                                  _ptr(ta), _ptr(nw), ta.size, _ptr(dot))

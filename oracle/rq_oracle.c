@@ -462,7 +462,8 @@ void orc_act_rows(const void *X, int xdtype, int K, const int64_t *rows,
  * in fp64, then quantize.
  *   q_kind 0: INT4 symmetric over all K -> codes [N][K/2], scale s_w[N];
  *             qvals (optional) [N][K] int8 signed codes
- *   q_kind 1: Lloyd-Max (levels, L=4) -> codes [N][K/4] crumbs, scale tau[N];
+ *   q_kind 1: Lloyd-Max (levels, L = 4 or 16) -> codes [N][K/4] crumbs
+ *             (L = 4) or [N][K/2] nibbles (L = 16), scale tau[N];
  *             qvals (optional) [N][K] indices
  */
 void orc_weight_rows(const float *W, int N, int K, int rot_kind, int b,
@@ -491,7 +492,10 @@ void orc_weight_rows(const float *W, int N, int K, int rot_kind, int b,
                     memcpy(qvals + (size_t)n * K, q, (size_t)K);
             } else {
                 orc_quant_lloydmax_wrow(v, K, levels, L, ix, &scale[n]);
-                orc_pack_crumbs(ix, K, codes + (size_t)n * (K / 4));
+                if (L == 16)
+                    orc_pack_nibbles((const int8_t *)ix, K, codes + (size_t)n * (K / 2));
+                else
+                    orc_pack_crumbs(ix, K, codes + (size_t)n * (K / 4));
                 if (qvals)
                     memcpy(qvals + (size_t)n * K, ix, (size_t)K);
             }
@@ -592,21 +596,24 @@ void orc_lowrank_pairs(const uint16_t *top, int r, const uint8_t *codes_w, int K
 /*
  * Codebook dot product of the Lloyd-Max variant for listed pairs, fp64:
  *   dot[p] = sum_k a_lv[idx_a[t][k]] * w_lv[idx_w[n][k]]
- * codes_a: [*][K/2] nibbles (4-bit index), codes_w: [N][K/4] crumbs.
+ * codes_a: [*][K/2] nibbles (4-bit index); codes_w: [N][K/4] crumbs
+ * (w_bits 2) or [N][K/2] nibbles (w_bits 4).
  */
-void orc_codebook_dot_pairs(const uint8_t *codes_a, const uint8_t *codes_w, int K,
+void orc_codebook_dot_pairs(const uint8_t *codes_a, const uint8_t *codes_w, int K, int w_bits,
                             const float *a_lv, const float *w_lv,
                             const int64_t *ta, const int64_t *nw, int64_t npairs,
                             double *dot)
 {
+    const int per_byte = 8 / w_bits;
+    const int mask = (1 << w_bits) - 1;
 #pragma omp parallel for schedule(static)
     for (int64_t p = 0; p < npairs; p++) {
         const uint8_t *ra = codes_a + (size_t)ta[p] * (K / 2);
-        const uint8_t *rw = codes_w + (size_t)nw[p] * (K / 4);
+        const uint8_t *rw = codes_w + (size_t)nw[p] * (K / per_byte);
         double s = 0.0;
         for (int k = 0; k < K; k++) {
             int ia = (ra[k >> 1] >> ((k & 1) * 4)) & 0xF;
-            int iw = (rw[k >> 2] >> ((k & 3) * 2)) & 0x3;
+            int iw = (rw[k / per_byte] >> ((k % per_byte) * w_bits)) & mask;
             s += (double)a_lv[ia] * (double)w_lv[iw];
         }
         dot[p] = s;

@@ -61,7 +61,8 @@ gemm_codebook_kernel(CodebookArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t As[BM * CLDS];
     __shared__ __attribute__((aligned(16))) uint8_t Bs[BN * CLDS];
     __shared__ uint32_t lutA[256];   // packed byte of two 4-bit indices -> two bf16
-    __shared__ uint2 lutB[256];      // packed byte of four 2-bit indices -> four bf16
+    __shared__ uint2 lutB[256];      // packed byte of four 2-bit indices -> four bf16, or
+                                     // of two 4-bit indices -> two bf16 (x)
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -78,7 +79,9 @@ gemm_codebook_kernel(CodebookArgs a) {
             for (int e = 0; e < 4; ++e) h[e] = __float_as_uint(a.w_levels[(tid >> (2 * e)) & 3]) >> 16;
             lutB[tid] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
         } else {
-            lutB[tid] = make_uint2(0, 0);
+            const uint32_t wl = __float_as_uint(a.w_levels[tid & 15]) >> 16;
+            const uint32_t wh = __float_as_uint(a.w_levels[tid >> 4]) >> 16;
+            lutB[tid] = make_uint2(wl | (wh << 16), 0u);
         }
     }
     __syncthreads();
@@ -132,12 +135,7 @@ gemm_codebook_kernel(CodebookArgs a) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
 #pragma unroll
-                for (int by = 0; by < 4; ++by) {
-                    const uint32_t bt = (w[q] >> (8 * by)) & 0xFFu;
-                    const uint32_t lo = __float_as_uint(a.w_levels[bt & 15]) >> 16;
-                    const uint32_t hi = __float_as_uint(a.w_levels[bt >> 4]) >> 16;
-                    d[4 * q + by] = lo | (hi << 16);
-                }
+                for (int by = 0; by < 4; ++by) d[4 * q + by] = lutB[(w[q] >> (8 * by)) & 0xFFu].x;
             uint4 *dst = reinterpret_cast<uint4 *>(Bs + row * CLDS + cb * 4);
 #pragma unroll
             for (int q = 0; q < 4; ++q) dst[q] = make_uint4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]);

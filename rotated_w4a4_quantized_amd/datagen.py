@@ -56,10 +56,11 @@ class Workload:
         """Algorithmic GEMM operations 2*T*Kq*N (multiply-add counted as 2)."""
         return 2 * self.T * self.Kq * self.N
 
-    def with_shape(self, T=None, K=None, N=None, block=None) -> "Workload":
+    def with_shape(self, T=None, K=None, N=None, block=None, w_bits=None) -> "Workload":
         return replace(self, T=self.T if T is None else T, K=self.K if K is None else K,
                        N=self.N if N is None else N,
-                       block=self.block if block is None else block)
+                       block=self.block if block is None else block,
+                       w_bits=self.w_bits if w_bits is None else w_bits)
 
 
 WORKLOADS = {
@@ -79,6 +80,10 @@ WORKLOADS = {
                                "bf16", "bf16", "gelu"),
     "video": Workload("video", 4, 32760, 1536, 8960, "rpbh", 256, 0, "lloydmax", "bf16", "bf16",
                       "gauss", a_bits=4, w_bits=2),
+    # OrbitQuant's W4A4 setting on the same layer (same seeds as video): a
+    # 16-level weight book instead of the 4-level one
+    "video_w4": Workload("video_w4", 4, 32760, 1536, 8960, "rpbh", 256, 0, "lloydmax", "bf16", "bf16",
+                         "gauss", a_bits=4, w_bits=4),
 }
 
 

@@ -284,6 +284,19 @@ def test_pack_lloydmax_matches_oracle():
     assert np.array_equal(np.array(pw.header.a_levels[:16], np.float32), a_lv)
 
 
+def test_pack_lloydmax_16_level_weights_matches_oracle():
+    # OrbitQuant W4A4: a 16-level weight book, 4-bit indices (nibbles)
+    w = datagen.WORKLOADS["video"].with_shape(T=4, K=512, N=24, block=256, w_bits=4)
+    inp = datagen.make_inputs(w)
+    a_lv, w_lv = rq.lloydmax_gaussian(16), rq.lloydmax_gaussian(16)
+    pw = rq.pack_weights(rq.Rotation.rpbh(inp["sign"], inp["perm"], 256),
+                         rq.Quant.lloydmax(a_lv, w_lv), inp["W"])
+    ref = _oracle_weights(w, inp, q_kind=1, levels=orc.codebook_bf16(16))
+    assert pw.header.row_bytes == w.K // 2 and pw.header.w_bits == 4
+    assert np.array_equal(pw.codes(), ref["codes"])
+    assert np.array_equal(pw.scales(), ref["scale"])
+
+
 def test_pack_rejects_bad_tables():
     sign, perm = datagen.random_rpbh(256, 1)
     perm = perm.copy()

@@ -93,6 +93,8 @@ SMALL = [
     ("flux_up_asym", dict(T=257, K=3072, N=384)),
     ("flux_down_asym", dict(T=131, K=12288, N=136)),
     ("flux_up_asym", dict(T=33, K=96, N=40, block=2)),
+    # OrbitQuant W4A4: a 16-level weight book
+    ("video_w4", dict(T=190, N=264)),
 ]
 
 
@@ -137,7 +139,7 @@ def test_small_full_parity(name, shape):
     assert ok
 
 
-FULL = ["tiny", "flux_up", "flux_down", "video", "pixart", "flux_up_asym", "flux_down_asym"]
+FULL = ["tiny", "flux_up", "flux_down", "video", "pixart", "flux_up_asym", "flux_down_asym", "video_w4"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -283,3 +285,42 @@ def test_mma_bf16_output_matches_converting_kernel():
     L.linear(Yb, use_mma=False)
     torch.cuda.synchronize()
     assert torch.equal(Ya.view(torch.int16), Yb.view(torch.int16))
+
+
+# The codebook GEMM at mid-size shapes (many tiles, ragged token and channel
+# edges, another K), against the oracle at sampled pairs plus the first and
+# last token rows and channel columns.
+CODEBOOK_BIG = [
+    ("video", dict(T=4000, N=4100)),
+    ("video", dict(T=4104, N=4000, K=1024)),
+    ("video_w4", dict(T=4000, N=4100)),
+]
+
+
+@pytest.mark.parametrize("name,shape", CODEBOOK_BIG,
+                         ids=[f"{n}-{'-'.join(f'{k}{v}' for k, v in s.items())}" for n, s in CODEBOOK_BIG])
+def test_codebook_mid_size(name, shape):
+    w = datagen.WORKLOADS[name].with_shape(**shape)
+    say(f"[codebook mid] {w}")
+    inp = datagen.make_inputs(w)
+    L = H.GpuLayer(w, inp, y_dtype="f32")
+    L.run()
+    torch.cuda.synchronize()
+    g = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([g.choice(w.T, 256, replace=False), [0, w.T - 1]]))
+    act = H.oracle_act(w, inp, rows)
+    wts = H.oracle_weights(w, inp)
+    assert np.array_equal(L.packed.codes(), wts["codes"])
+    ta = np.concatenate([g.choice(rows, 8192), np.repeat(rows[[0, -1]], w.N), np.repeat(rows, 2)])
+    nw = np.concatenate([g.integers(0, w.N, 8192), np.tile(np.arange(w.N), 2),
+                         np.tile(np.array([0, w.N - 1]), rows.size)])
+    yhat = H.oracle_yhat_pairs(w, act, wts, ta, nw, act_rows=rows)
+    idx = torch.from_numpy(ta).to("cuda") * w.N + torch.from_numpy(nw).to("cuda")
+    err = H.rel_err(L.Y.view(-1)[idx].cpu().numpy(), yhat)
+    say(f"  fp32 max floored rel err {err:.3e}")
+    assert err <= H.REL_TOL
+    Yb = torch.empty((w.T, w.N), dtype=torch.bfloat16, device="cuda")
+    L.linear(Yb)
+    dist, ok = H.bf16_check(H.to_np_bf16_bits(Yb.view(-1)[idx]), yhat)
+    say(f"  bf16 max ulp distance {dist}")
+    assert ok

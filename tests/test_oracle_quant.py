@@ -206,10 +206,11 @@ def test_codebook_ties_go_to_lower_level():
     assert list(idx) == [3, 1, 1, 1]                   # 0 is the midpoint of (-0.5, 0.5)
 
 
-def test_codebook_weight_row():
+@pytest.mark.parametrize("L", [4, 16])
+def test_codebook_weight_row(L):
     g = np.random.default_rng(9)
     K = 128
-    levels = orc.codebook_bf16(4)
+    levels = orc.codebook_bf16(L)
     v = g.standard_normal(K) * 0.05
     idx, tau = orc.quant_lloydmax_wrow(v, levels)
     nrm = np.sqrt(np.sum(v * v))
@@ -313,3 +314,30 @@ def test_asym_gemm_and_output_identity():
     y = orc.yhat_int4_asym(s_a[ta], z_a[ta], s_w[nw], acc, qw.sum(1)[nw], b)
     direct = ((s_a[:, None] * (ua - z_a[:, None])) @ (s_w[:, None] * qw).T) / b
     assert np.allclose(y.reshape(T, N), direct, rtol=1e-12, atol=1e-12)
+
+
+def test_codebook_weight_book_of_16_levels_packs_nibbles():
+    # a 16-level weight book (OrbitQuant's W4A4 setting) stores one 4-bit
+    # index per coordinate, two per byte, low nibble = even coordinate; the
+    # codebook dot product reads it back: checked against a direct sum over
+    # the nearest-level indices of each row
+    g = np.random.default_rng(21)
+    N, K = 6, 64
+    W = g.standard_normal((N, K)).astype(np.float32)
+    sign = np.ones(K, np.int8)
+    perm = np.arange(K, dtype=np.int32)
+    lv16 = orc.codebook_bf16(16)
+    out = orc.weight_rows(W, rot_kind=0, b=2, sign=sign, perm=perm, q_kind=1, levels=lv16)
+    assert out["codes"].shape == (N, K // 2)
+    idx = out["q"].astype(np.int64)
+    assert idx.min() >= 0 and idx.max() <= 15
+    assert np.array_equal(out["codes"], (idx[:, 0::2] | (idx[:, 1::2] << 4)).astype(np.uint8))
+    # activations: one row of 4-bit indices
+    ia = g.integers(0, 16, (3, K))
+    codes_a = (ia[:, 0::2] | (ia[:, 1::2] << 4)).astype(np.uint8)
+    a_lv = orc.codebook_bf16(16)
+    ta, nw = np.meshgrid(np.arange(3), np.arange(N), indexing="ij")
+    dot = orc.codebook_dot_pairs(codes_a, out["codes"], K, a_lv, lv16, ta.ravel(), nw.ravel())
+    ref = [sum(float(a_lv[ia[t, k]]) * float(lv16[idx[n, k]]) for k in range(K))
+           for t, n in zip(ta.ravel(), nw.ravel())]
+    assert np.allclose(dot, ref, rtol=0, atol=1e-12)
