@@ -93,14 +93,33 @@ gemm_codebook_kernel(CodebookArgs a) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+    // This thread's rows of the tile (clamped past the edges; those outputs
+    // are not stored): token row tid / 2 (16 bytes of indices per stage) and
+    // weight row tid / 2 (8 or 16 bytes).  The next stage's indices are
+    // loaded into registers before the current stage's MFMAs.
+    const int row = tid >> 1;
+    int64_t ar = m0 + row;
+    if (ar >= a.T) ar = a.T - 1;
+    int br = n0 + row;
+    if (br >= a.N) br = a.N - 1;
+    const uint8_t *ap = a.A + ar * (a.K / 2) + (tid & 1) * 16;
+    const uint8_t *bp = a.B + (int64_t)br * a.ldb + (a.w_bits == 2 ? (tid & 1) * 8 : (tid & 1) * 16);
+    uint4 ra, rb;
+    auto load = [&](int k0) {
+        ra = *reinterpret_cast<const uint4 *>(ap + k0 / 2);
+        if (a.w_bits == 2) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(bp + k0 / 4);
+            rb = make_uint4(v.x, v.y, 0u, 0u);
+        } else {
+            rb = *reinterpret_cast<const uint4 *>(bp + k0 / 2);
+        }
+    };
+    load(0);
     for (int k0 = 0; k0 < a.K; k0 += CBK) {
         // A: 128 rows x 32 bytes; thread -> row tid / 2, 16 bytes at (tid & 1) * 16
         {
-            const int row = tid >> 1, cb = (tid & 1) * 16;
-            int64_t ar = m0 + row;
-            if (ar >= a.T) ar = a.T - 1;
-            const uint4 v = *reinterpret_cast<const uint4 *>(a.A + ar * (a.K / 2) + k0 / 2 + cb);
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            const int cb = (tid & 1) * 16;
+            const uint32_t w[4] = {ra.x, ra.y, ra.z, ra.w};
             uint32_t d[16];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -112,11 +131,8 @@ gemm_codebook_kernel(CodebookArgs a) {
         }
         // B: 128 rows x 64 k
         if (a.w_bits == 2) {
-            const int row = tid >> 1, cb = (tid & 1) * 8;   // 8 bytes = 32 k
-            int br = n0 + row;
-            if (br >= a.N) br = a.N - 1;
-            const uint2 v = *reinterpret_cast<const uint2 *>(a.B + (int64_t)br * a.ldb + k0 / 4 + cb);
-            const uint32_t w[2] = {v.x, v.y};
+            const int cb = (tid & 1) * 8;   // 8 bytes = 32 k
+            const uint32_t w[2] = {rb.x, rb.y};
             uint2 d[8];
 #pragma unroll
             for (int q = 0; q < 2; ++q)
@@ -126,11 +142,8 @@ gemm_codebook_kernel(CodebookArgs a) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) dst[q] = make_uint4(d[2 * q].x, d[2 * q].y, d[2 * q + 1].x, d[2 * q + 1].y);
         } else {
-            const int row = tid >> 1, cb = (tid & 1) * 16;  // 16 bytes = 32 k (4-bit weights)
-            int br = n0 + row;
-            if (br >= a.N) br = a.N - 1;
-            const uint4 v = *reinterpret_cast<const uint4 *>(a.B + (int64_t)br * a.ldb + k0 / 2 + cb);
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            const int cb = (tid & 1) * 16;  // 16 bytes = 32 k (4-bit weights)
+            const uint32_t w[4] = {rb.x, rb.y, rb.z, rb.w};
             uint32_t d[16];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -140,6 +153,7 @@ gemm_codebook_kernel(CodebookArgs a) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) dst[q] = make_uint4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]);
         }
+        if (k0 + CBK < a.K) load(k0 + CBK);
         __syncthreads();
 #pragma unroll
         for (int ks = 0; ks < CBK / 16; ++ks) {
