@@ -19,7 +19,8 @@
 //            and the row is written to LDS in its natural order;
 //   gather   each thread reads its 32 permuted inputs from LDS;
 //   pass 0   stages on bits 0..4 of the block index, in registers;
-//   pass p   one LDS exchange, then up to four more stages in registers; the
+//   pass p   one exchange inside the wave (two rounds through LDS, see
+//            exchange()), then up to four more stages in registers; the
 //            register set of every pass after the first also carries index
 //            bit 0, so the final values of each nibble pair sit in one thread;
 //   stat     per-token absmax (asymmetric: min and max; for the codebook
@@ -34,7 +35,9 @@
 //            them so that the four tokens' 16-byte slots of one piece -- 64
 //            contiguous bytes -- come from four adjacent lanes: whole-request
 //            stores instead of sixteen-byte writes to scattered lines.
-// Two workgroup barriers per token (three for the codebook).
+// Two workgroup barriers per iteration of `tpw` tokens (three for the
+// codebook).  A per-workgroup prologue reads perm and sign and builds the
+// source-side sign masks in LDS.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
