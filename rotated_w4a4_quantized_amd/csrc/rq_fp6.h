@@ -48,8 +48,9 @@ __device__ __forceinline__ void to_fp6(uint32_t a, uint32_t b, uint32_t &d0, uin
     d2 = (a & 0x00F00F00u) | (b2 & 0x3C03C03Cu);
 }
 
-// Stores the 32 canonical codes of chunk c (coordinates 32 c .. 32 c + 31,
-// sixteen bytes w) of token t into the MMA-layout buffer of S stages.
+// Stores the 32 nibble codes of chunk c (coordinates 32 c .. 32 c + 31,
+// sixteen bytes w, each nibble XOR flip giving the field) of token t into the
+// MMA-layout buffer of S stages.
 __device__ __forceinline__ void store_chunk_mma(uint8_t *mma, int64_t t, int S, int c, uint4 w,
                                                 uint32_t flip) {
     uint32_t d[6];
@@ -68,20 +69,22 @@ __device__ __forceinline__ void store_chunk_mma(uint8_t *mma, int64_t t, int S, 
     }
 }
 
-// Stores the MMA-layout codes of token t for stage s and half h: the canonical
-// chunks c0 = 4 s + h (k-step 0) and c1 = 4 s + 2 + h (k-step 1), sixteen
-// bytes each, become the token's three 16-byte lane slots (lane t % 32 + 32 h)
-// of the stage block's pieces 0, 1 and 2 (only k-step 0's 24 bytes when has1
-// is false: chunk c1 lies past the last coordinate).  Tokens t .. t + 3 of
-// one tile write one contiguous 64-byte run per piece.
-__device__ __forceinline__ void store_pair_mma(uint8_t *mma, int64_t t, int S, int s, int h, uint4 w0,
-                                               uint4 w1, bool has1, uint32_t flip) {
+// Stores the MMA-layout codes of the token at position t32 (0..31) of the
+// 32-token tile whose S stage blocks start at `tile` (= mma + (t / 32) S
+// kMmaTileStageBytes), for stage s and half h: the chunks c0 = 4 s + h
+// (k-step 0) and c1 = 4 s + 2 + h (k-step 1), sixteen bytes each, become the
+// token's three 16-byte lane slots (lane t32 + 32 h) of the stage block's
+// pieces 0, 1 and 2 (only k-step 0's 24 bytes when has1 is false: chunk c1
+// lies past the last coordinate).  Four consecutive tokens of one tile write
+// one contiguous 64-byte run per piece.
+__device__ __forceinline__ void store_pair_mma_in_tile(uint8_t *tile, int s, int t32, int h, uint4 w0,
+                                                       uint4 w1, bool has1, uint32_t flip) {
     uint32_t d[12];
     to_fp6(w0.x, w0.y, d[0], d[1], d[2], flip);
     to_fp6(w0.z, w0.w, d[3], d[4], d[5], flip);
     to_fp6(w1.x, w1.y, d[6], d[7], d[8], flip);
     to_fp6(w1.z, w1.w, d[9], d[10], d[11], flip);
-    uint8_t *blk = mma + ((t >> 5) * S + s) * (int64_t)kMmaTileStageBytes + (((int)t & 31) + 32 * h) * 16;
+    uint8_t *blk = tile + s * kMmaTileStageBytes + (t32 + 32 * h) * 16;
     *reinterpret_cast<uint4 *>(blk) = make_uint4(d[0], d[1], d[2], d[3]);
     if (!has1) {
         *reinterpret_cast<uint2 *>(blk + 1024) = make_uint2(d[4], d[5]);

@@ -204,6 +204,26 @@ __device__ inline float fkey_inv(unsigned k) {
     return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
 }
 
+// x of the lane that the data-parallel-primitive control CTRL selects inside
+// x's row of 16 lanes (0 where that lane is inactive; the runs reduced below
+// are all active or all inactive).
+template <int CTRL>
+__device__ inline unsigned dpp_peer(unsigned x) {
+    return (unsigned)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
+}
+// Max (MAX) or min of x over every aligned run of g lanes (g = 1, 2, 4, 8 or
+// 16): swaps inside each quad, then the half-row and row mirrors.  Every lane
+// of a run ends with the run's result.
+template <bool MAX>
+__device__ inline unsigned run_reduce(unsigned x, int g) {
+    auto op = [](unsigned p, unsigned q) { return MAX ? (p > q ? p : q) : (p < q ? p : q); };
+    if (g >= 2) x = op(x, dpp_peer<0xB1>(x));    // quad lanes 1 0 3 2
+    if (g >= 4) x = op(x, dpp_peer<0x4E>(x));    // quad lanes 2 3 0 1
+    if (g >= 8) x = op(x, dpp_peer<0x141>(x));   // mirror inside each half row
+    if (g >= 16) x = op(x, dpp_peer<0x140>(x));  // mirror inside the row
+    return x;
+}
+
 struct RpbhArgs {
     const void *X;
     int64_t T;
@@ -236,8 +256,11 @@ template <int L, bool BF16, int QK>
 __global__ void __launch_bounds__(kMaxThreads<BF16>)
 rpbh_quant_kernel(RpbhArgs a) {
     using S = Src<BF16>;
-    // MMA-layout fields: symmetric codes carried as q + 8, unsigned as they are
-    constexpr uint32_t kFlip = QK == 2 ? 0u : 0x88888888u;
+    // Staged nibbles are the MMA-layout fields: a symmetric code is held as
+    // q + 8, an unsigned one (asymmetric, codebook) as it is.  The canonical
+    // layout holds a symmetric q in two's complement: the nibble's top bit
+    // flipped.
+    constexpr uint32_t kCanonFlip = QK == 0 ? 0x88888888u : 0u;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ unsigned red_max[2][kMaxTpw];
     __shared__ unsigned red_min[2][kMaxTpw];   // asymmetric INT4 (keys)
@@ -349,16 +372,20 @@ rpbh_quant_kernel(RpbhArgs a) {
     // MMA-layout codes of group g (complete in the slots, LDS writes ordered
     // by a barrier): item i is (stage s, half h) = (i >> gsz_log2) and token
     // j = i % group size, so four adjacent lanes write one 64-byte run.
+    // A group (at most 16 tokens, aligned) lies inside one 32-token tile.
     auto flush = [&](int64_t g) {
         const int items = a.mma_stages * 2 << a.gsz_log2;
         const int nth = a.tpw * a.tpt;
         const int nch = K / kE;
-        const int gmask = (1 << a.gsz_log2) - 1;
+        const int gsz = 1 << a.gsz_log2;
+        const int64_t t0 = g << a.gsz_log2;
+        const int nvalid = a.T - t0 < gsz ? (int)(a.T - t0) : gsz;
+        uint8_t *const tile = a.codes_mma + (t0 >> 5) * (int64_t)a.mma_stages * kMmaTileStageBytes;
+        const int t32 = (int)(t0 & 31);
         for (int i = tid; i < items; i += nth) {
-            const int j = i & gmask;
+            const int j = i & (gsz - 1);
             const int sh = i >> a.gsz_log2;
-            const int64_t t = (g << a.gsz_log2) + j;
-            if (t >= a.T) continue;
+            if (j >= nvalid) continue;
             const uint8_t *slot = cs0 + (size_t)j * cb;
             // chunks c0 (k-step 0) and c1 (k-step 1); those past the last
             // coordinate are not written
@@ -367,7 +394,7 @@ rpbh_quant_kernel(RpbhArgs a) {
             const uint4 w0 = *reinterpret_cast<const uint4 *>(slot + chunk_off<L>(c0));
             const uint4 w1 = c1 < nch ? *reinterpret_cast<const uint4 *>(slot + chunk_off<L>(c1))
                                       : make_uint4(0u, 0u, 0u, 0u);
-            store_pair_mma(a.codes_mma, t, a.mma_stages, sh >> 1, sh & 1, w0, w1, c1 < nch, kFlip);
+            store_pair_mma_in_tile(tile, sh >> 1, t32 + j, sh & 1, w0, w1, c1 < nch, 0u);
         }
     };
     const bool grouped = QK != 1 && a.grouped;
@@ -375,6 +402,8 @@ rpbh_quant_kernel(RpbhArgs a) {
     // lane groups of one token for the shuffle reductions
     int grp = 64;
     while (a.tpt % grp) grp >>= 1;
+    // the same runs cut to one row of 16 lanes (max / min reductions)
+    const int rg = grp < 16 ? grp : 16;
 
     int it = 0;
     for (; base >= 0; ++it) {
@@ -424,20 +453,19 @@ rpbh_quant_kernel(RpbhArgs a) {
                 lo = fminf(lo, v[r]);
                 hi = fmaxf(hi, v[r]);
             }
-            for (int off = 1; off < grp; off <<= 1) {
-                lo = fminf(lo, __shfl_xor(lo, off, 64));
-                hi = fmaxf(hi, __shfl_xor(hi, off, 64));
-            }
-            if ((tid & (grp - 1)) == 0) {
-                atomicMin(&red_min[it & 1][tl], fkey(lo));
-                atomicMax(&red_max[it & 1][tl], fkey(hi));
+            const unsigned klo = run_reduce<false>(fkey(lo), rg);
+            const unsigned khi = run_reduce<true>(fkey(hi), rg);
+            if ((tid & (rg - 1)) == 0) {
+                atomicMin(&red_min[it & 1][tl], klo);
+                atomicMax(&red_max[it & 1][tl], khi);
             }
         } else {
             float m = 0.0f;
 #pragma unroll
             for (int r = 0; r < kE; ++r) m = fmaxf(m, fabsf(v[r]));
-            for (int off = 1; off < grp; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-            if ((tid & (grp - 1)) == 0) atomicMax(&red_max[it & 1][tl], __float_as_uint(m));
+            // m >= 0: its bits order as unsigned integers
+            const unsigned km = run_reduce<true>(__float_as_uint(m), rg);
+            if ((tid & (rg - 1)) == 0) atomicMax(&red_max[it & 1][tl], km);
         }
         lds_barrier();  // B2: statistic complete, next token staged
         const float amax = __uint_as_float(red_max[it & 1][tl]);
@@ -467,13 +495,14 @@ rpbh_quant_kernel(RpbhArgs a) {
             }
         } else if constexpr (QK == 0) {
             // q = rne(fl32(u * inv)) lands in [-7, 7]: |u * inv| <= fl32(7 (1 + 2^-24)) = 7,
-            // so no clamp is needed.  Adding 1.5 * 2^23 rounds to an integer
-            // (nearest-even) and leaves q in the low bits, two's complement.
+            // so no clamp is needed.  Adding 1.5 * 2^23 + 8 (even) rounds to
+            // an integer, nearest-even, and leaves q + 8 in bits 0..3 with
+            // bits 4..21 clear.
             const float inv = amax > 0.0f ? 7.0f / amax : 0.0f;
 #pragma unroll
             for (int r = 0; r < kE; ++r) {
                 const float mq = v[r] * inv;
-                nib[r] = __float_as_uint(mq + 12582912.0f);   // code in bits 0..3
+                nib[r] = __float_as_uint(mq + 12582920.0f);   // q + 8 in bits 0..3
             }
             sc = amax > 0.0f ? amax / 7.0f : 0.0f;
         } else {
@@ -510,7 +539,7 @@ rpbh_quant_kernel(RpbhArgs a) {
         }
 
         // pack: register bit 0 carries index bit 0, so registers (2m, 2m + 1)
-        // hold a nibble pair
+        // hold a nibble pair; bits 4..7 of every code word are clear
         uint4 chunk = make_uint4(0u, 0u, 0u, 0u);
         if constexpr (Plan<L>::NP == 1) {
             uint32_t w[4];
@@ -527,7 +556,7 @@ rpbh_quant_kernel(RpbhArgs a) {
             uint8_t *p = cs + cpad<L>(pbase<L, PL>(tt) >> 1);
 #pragma unroll
             for (int mm = 0; mm < kE / 2; ++mm)
-                p[Plan<L>::roff(PL, 2 * mm) >> 1] = (uint8_t)((nib[2 * mm] & 0xFu) | (nib[2 * mm + 1] << 4));
+                p[Plan<L>::roff(PL, 2 * mm) >> 1] = (uint8_t)(nib[2 * mm] | (nib[2 * mm + 1] << 4));
             if (a.codes || (a.codes_mma && !grouped)) {
                 // the 16 bytes this thread stores were written by lanes of its
                 // own wave (its RPBH block): order the LDS writes before the read
@@ -538,11 +567,12 @@ rpbh_quant_kernel(RpbhArgs a) {
             }
         }
         if (valid) {
-            if (a.codes) *reinterpret_cast<uint4 *>(a.codes + tok * (int64_t)(K / 2) + 16 * tt) = chunk;
-            if constexpr (QK == 0)
-                if (a.codes_mma && !grouped) store_chunk_mma(a.codes_mma, tok, a.mma_stages, tt, chunk, kFlip);
-            if constexpr (QK == 2)
-                if (a.codes_mma && !grouped) store_chunk_mma(a.codes_mma, tok, a.mma_stages, tt, chunk, kFlip);
+            if (a.codes)
+                *reinterpret_cast<uint4 *>(a.codes + tok * (int64_t)(K / 2) + 16 * tt) =
+                    make_uint4(chunk.x ^ kCanonFlip, chunk.y ^ kCanonFlip, chunk.z ^ kCanonFlip,
+                               chunk.w ^ kCanonFlip);
+            if constexpr (QK != 1)
+                if (a.codes_mma && !grouped) store_chunk_mma(a.codes_mma, tok, a.mma_stages, tt, chunk, 0u);
             if (tt == 0) {
                 a.scale[tok] = sc;
                 if constexpr (QK == 2) a.scale[a.T + tok] = zp;
