@@ -569,11 +569,10 @@ struct MmaCfg {
     static constexpr int NA = BT / 32 * 3 / NW;   // activation loads per wave per stage
     static constexpr int NB = BN / 32 * 3 / NW;   // weight loads per wave per stage
     static constexpr int IPW = NA + NB;
-    static constexpr int OUT_STRIDE = BN * 2 + 16;
-    // after the stage buffers / output staging: the epilogue's per-token
-    // scales, per-channel scales, code sums and per-token zero points of the
-    // tile, 1 KB each
-    static constexpr int EPI_OFF = 3 * LDS_STAGE > BT * OUT_STRIDE ? 3 * LDS_STAGE : BT * OUT_STRIDE;
+    // after the stage buffers (which the epilogue reuses for its output
+    // slabs): the tile's per-token scales, per-channel scales, code sums and
+    // per-token zero points, 1 KB each
+    static constexpr int EPI_OFF = 3 * LDS_STAGE;
     static constexpr int LDS_BYTES = EPI_OFF + 4 * 1024;
     static_assert(BT == 256 && BN == 256, "one 1 KB direct-to-LDS load per epilogue array");
     static_assert(NW >= 4, "four waves load the epilogue arrays");
@@ -756,11 +755,20 @@ gemm_fp6_mma_kernel(Fp6Args a) {
     if (nstage >= 2) stage(nstage - 2, F_{}, F_{});
     stage(nstage - 1, F_{}, F_{});
 
-    // epilogue: full bf16 tiles staged through LDS (free after the last
-    // barrier once this wave's reads have landed), else the general path
-    constexpr int kOutStride = C::OUT_STRIDE;
+    // Epilogue.  Full bf16 tiles: each wave scales its 64 tokens x 128
+    // channels into a private slab of the stage buffers (every fragment read
+    // of the last stage completed before that stage's barrier; the reads
+    // issued after it are stale and unused), then copies the slab out as
+    // 256-byte row segments.  No workgroup barrier.  Other tiles take the
+    // general path.
     if (fast) {
-        lds_barrier();
+        // keep the epilogue below the main loop's last MFMAs (register pressure)
+        __builtin_amdgcn_sched_barrier(0);
+        constexpr int kRowBytes = C::BN / C::WN * 2;      // one token's channels
+        constexpr int kSlabStride = kRowBytes + 16;       // padded LDS row
+        constexpr int kRows = C::FT * 32;
+        static_assert(C::NW * kRows * kSlabStride <= 3 * C::LDS_STAGE, "slabs fit the stage buffers");
+        uint8_t *slab = lds + wave * kRows * kSlabStride;
         const float *e_sa = reinterpret_cast<const float *>(lds + C::EPI_OFF);
         const float *e_sw = reinterpret_cast<const float *>(lds + C::EPI_OFF + 1024);
         const int32_t *e_ws = reinterpret_cast<const int32_t *>(lds + C::EPI_OFF + 2048);
@@ -780,19 +788,19 @@ gemm_fp6_mma_kernel(Fp6Args a) {
                 constexpr int i = decltype(ic)::value;
                 static_for<4>([&](auto qc) {
                     constexpr int q = decltype(qc)::value;
-                    const int nl = wn * C::FN * 32 + i * 32 + 8 * q + 4 * lg;
+                    const int nw = i * 32 + 8 * q + 4 * lg;   // channel within the wave's 128
+                    const int nl = wn * C::FN * 32 + nw;
                     const float4 sw4 = *reinterpret_cast<const float4 *>(e_sw + nl);
                     const int4 ws4 = *reinterpret_cast<const int4 *>(e_ws + nl);
                     const float w0 = (float)ws4.x, w1 = (float)ws4.y, w2 = (float)ws4.z, w3 = (float)ws4.w;
                     const float o0 = 8.0f * w0, o1 = 8.0f * w1, o2 = 8.0f * w2, o3 = 8.0f * w3;
                     static_for<C::FT>([&](auto jc) {
                         constexpr int j = decltype(jc)::value;
-                        const int tl = wt * C::FT * 32 + j * 32 + li;
                         const float y0 = (acc[i][j][4 * q + 0] - (ASYM ? zt[j] * w0 : o0)) * (sat[j] * sw4.x);
                         const float y1 = (acc[i][j][4 * q + 1] - (ASYM ? zt[j] * w1 : o1)) * (sat[j] * sw4.y);
                         const float y2 = (acc[i][j][4 * q + 2] - (ASYM ? zt[j] * w2 : o2)) * (sat[j] * sw4.z);
                         const float y3 = (acc[i][j][4 * q + 3] - (ASYM ? zt[j] * w3 : o3)) * (sat[j] * sw4.w);
-                        *reinterpret_cast<uint2 *>(lds + tl * kOutStride + 2 * nl) =
+                        *reinterpret_cast<uint2 *>(slab + (j * 32 + li) * kSlabStride + 2 * nw) =
                             make_uint2(bf16x2_rne(y0, y1), bf16x2_rne(y2, y3));
                     });
                 });
@@ -800,25 +808,36 @@ gemm_fp6_mma_kernel(Fp6Args a) {
         };
         if (a.za) scale_tile(std::true_type());
         else scale_tile(std::false_type());
-        lds_barrier();
-        constexpr int kChunksPerRow = C::BN * 2 / 16;
-        constexpr int kChunks = C::BT * kChunksPerRow;
-        static_assert(kChunks % (8 * C::NTH) == 0, "whole batches of eight chunks per thread");
-        // eight LDS reads in flight, then their eight stores
-        for (int c0 = tid; c0 < kChunks; c0 += 8 * C::NTH) {
-            uint4 v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int c = c0 + u * C::NTH;
-                v[u] = *reinterpret_cast<const uint4 *>(lds + (c / kChunksPerRow) * kOutStride +
-                                                        16 * (c % kChunksPerRow));
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int c = c0 + u * C::NTH;
-                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.Y) + (t0 + c / kChunksPerRow) * a.N +
-                                           n0 + 8 * (c % kChunksPerRow)) = v[u];
-            }
+        // the slab's writes come from this wave only: order them before the reads
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // copy-out: one instruction moves 64 / kChunksPerRow rows of 16-byte
+        // chunks; lane l takes chunk l % kChunksPerRow of row l / kChunksPerRow
+        constexpr int kChunksPerRow = kRowBytes / 16;
+        constexpr int kRowsPerInst = 64 / kChunksPerRow;
+        static_assert(kRows % (8 * kRowsPerInst) == 0, "whole batches of eight instructions");
+        const int lr = lane / kChunksPerRow, lc = lane % kChunksPerRow;
+        const uint8_t *src = slab + lr * kSlabStride + 16 * lc;
+        uint16_t *dst = static_cast<uint16_t *>(a.Y) + (t0 + wt * kRows + lr) * a.N + n0 +
+                        wn * (kRowBytes / 2) + 8 * lc;
+        // eight LDS reads in flight, then their eight stores (named values: an
+        // array here was kept in scratch memory)
+        auto ld = [&](int r) { return *reinterpret_cast<const uint4 *>(src + r * kSlabStride); };
+        auto st = [&](int r, const uint4 &v) { *reinterpret_cast<uint4 *>(dst + (int64_t)r * a.N) = v; };
+        constexpr int R = kRowsPerInst;
+#pragma unroll 1
+        for (int r0 = 0; r0 < kRows; r0 += 8 * R) {
+            const uint4 v0 = ld(r0), v1 = ld(r0 + R), v2 = ld(r0 + 2 * R), v3 = ld(r0 + 3 * R);
+            const uint4 v4 = ld(r0 + 4 * R), v5 = ld(r0 + 5 * R), v6 = ld(r0 + 6 * R), v7 = ld(r0 + 7 * R);
+            st(r0, v0);
+            st(r0 + R, v1);
+            st(r0 + 2 * R, v2);
+            st(r0 + 3 * R, v3);
+            st(r0 + 4 * R, v4);
+            st(r0 + 5 * R, v5);
+            st(r0 + 6 * R, v6);
+            st(r0 + 7 * R, v7);
         }
         return;
     }
