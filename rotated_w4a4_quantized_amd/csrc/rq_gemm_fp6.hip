@@ -716,6 +716,32 @@ gemm_fp6_mma_kernel(Fp6Args a) {
     else if (npre == 2) wait_vm(std::integral_constant<int, C::IPW>());
     else wait_vm(std::integral_constant<int, 0>());
     lds_barrier();
+    // Full bf16 tiles start the accumulators at -zt wsum[n] (zt = 8, or the
+    // token's zero point): the MFMAs then leave acc - zt wsum, and every
+    // partial sum is an integer of magnitude below 2^24, so this is exact and
+    // the epilogue only rescales.
+    if (fast) {
+        const int32_t *e_ws = reinterpret_cast<const int32_t *>(lds + C::EPI_OFF + 2048);
+        const float *e_za = reinterpret_cast<const float *>(lds + C::EPI_OFF + 3072);
+        float zt[C::FT];
+#pragma unroll
+        for (int j = 0; j < C::FT; ++j) {
+            const int tl = wt * C::FT * 32 + j * 32 + li;
+            zt[j] = !a.za ? 8.0f : za_lds ? e_za[tl] : a.za[t0 + tl];
+        }
+        static_for<C::FN>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            static_for<4>([&](auto qc) {
+                constexpr int q = decltype(qc)::value;
+                const int4 ws4 = *reinterpret_cast<const int4 *>(e_ws + wn * C::FN * 32 + i * 32 + 8 * q + 4 * lg);
+                const float w[4] = {(float)ws4.x, (float)ws4.y, (float)ws4.z, (float)ws4.w};
+#pragma unroll
+                for (int j = 0; j < C::FT; ++j)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) acc[i][j][4 * q + c] = -(zt[j] * w[c]);
+            });
+        });
+    }
     Frag A[C::FT], W0, W1;
 #pragma unroll
     for (int j = 0; j < C::FT; ++j) A[j] = rd_act(0, j);
@@ -771,43 +797,27 @@ gemm_fp6_mma_kernel(Fp6Args a) {
         uint8_t *slab = lds + wave * kRows * kSlabStride;
         const float *e_sa = reinterpret_cast<const float *>(lds + C::EPI_OFF);
         const float *e_sw = reinterpret_cast<const float *>(lds + C::EPI_OFF + 1024);
-        const int32_t *e_ws = reinterpret_cast<const int32_t *>(lds + C::EPI_OFF + 2048);
-        const float *e_za = reinterpret_cast<const float *>(lds + C::EPI_OFF + 3072);
-        float sat[C::FT], zt[C::FT];
+        float sat[C::FT];
 #pragma unroll
-        for (int j = 0; j < C::FT; ++j) {
-            const int tl = wt * C::FT * 32 + j * 32 + li;
-            sat[j] = e_sa[tl] * a.post;
-            zt[j] = !a.za ? 8.0f : za_lds ? e_za[tl] : a.za[t0 + tl];
-        }
-        // y = (acc - zt wsum[n]) (s_a post s_w): zt wsum is an exact integer
-        // below 2^24 (zt = 8 for symmetric codes: one offset per channel)
-        auto scale_tile = [&](auto asym_c) {
-            constexpr bool ASYM = decltype(asym_c)::value;
-            static_for<C::FN>([&](auto ic) {
-                constexpr int i = decltype(ic)::value;
-                static_for<4>([&](auto qc) {
-                    constexpr int q = decltype(qc)::value;
-                    const int nw = i * 32 + 8 * q + 4 * lg;   // channel within the wave's 128
-                    const int nl = wn * C::FN * 32 + nw;
-                    const float4 sw4 = *reinterpret_cast<const float4 *>(e_sw + nl);
-                    const int4 ws4 = *reinterpret_cast<const int4 *>(e_ws + nl);
-                    const float w0 = (float)ws4.x, w1 = (float)ws4.y, w2 = (float)ws4.z, w3 = (float)ws4.w;
-                    const float o0 = 8.0f * w0, o1 = 8.0f * w1, o2 = 8.0f * w2, o3 = 8.0f * w3;
-                    static_for<C::FT>([&](auto jc) {
-                        constexpr int j = decltype(jc)::value;
-                        const float y0 = (acc[i][j][4 * q + 0] - (ASYM ? zt[j] * w0 : o0)) * (sat[j] * sw4.x);
-                        const float y1 = (acc[i][j][4 * q + 1] - (ASYM ? zt[j] * w1 : o1)) * (sat[j] * sw4.y);
-                        const float y2 = (acc[i][j][4 * q + 2] - (ASYM ? zt[j] * w2 : o2)) * (sat[j] * sw4.z);
-                        const float y3 = (acc[i][j][4 * q + 3] - (ASYM ? zt[j] * w3 : o3)) * (sat[j] * sw4.w);
-                        *reinterpret_cast<uint2 *>(slab + (j * 32 + li) * kSlabStride + 2 * nw) =
-                            make_uint2(bf16x2_rne(y0, y1), bf16x2_rne(y2, y3));
-                    });
+        for (int j = 0; j < C::FT; ++j) sat[j] = e_sa[wt * C::FT * 32 + j * 32 + li] * a.post;
+        // y = (acc - zt wsum[n]) (s_a post s_w); the offset is already in acc
+        static_for<C::FN>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            static_for<4>([&](auto qc) {
+                constexpr int q = decltype(qc)::value;
+                const int nw = i * 32 + 8 * q + 4 * lg;   // channel within the wave's 128
+                const float4 sw4 = *reinterpret_cast<const float4 *>(e_sw + wn * C::FN * 32 + nw);
+                static_for<C::FT>([&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    const float y0 = acc[i][j][4 * q + 0] * (sat[j] * sw4.x);
+                    const float y1 = acc[i][j][4 * q + 1] * (sat[j] * sw4.y);
+                    const float y2 = acc[i][j][4 * q + 2] * (sat[j] * sw4.z);
+                    const float y3 = acc[i][j][4 * q + 3] * (sat[j] * sw4.w);
+                    *reinterpret_cast<uint2 *>(slab + (j * 32 + li) * kSlabStride + 2 * nw) =
+                        make_uint2(bf16x2_rne(y0, y1), bf16x2_rne(y2, y3));
                 });
             });
-        };
-        if (a.za) scale_tile(std::true_type());
-        else scale_tile(std::false_type());
+        });
         // the slab's writes come from this wave only: order them before the reads
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
