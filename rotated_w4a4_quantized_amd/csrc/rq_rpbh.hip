@@ -241,6 +241,7 @@ struct RpbhArgs {
     int64_t ngroups;
     float *scale;         // s or sigma [T]; asymmetric INT4: s [T] then z [T]
     float th[15];         // codebook thresholds (Lloyd-Max)
+    int th_sym;           // th[7] == 0 and th[i] == -th[14 - i] exactly
 };
 
 template <bool BF16>
@@ -528,8 +529,21 @@ rpbh_quant_kernel(RpbhArgs a) {
                 for (int r = 0; r < kE; ++r) {
                     const float x = v[r] * g;
                     uint32_t idx = 0;
+                    if (a.th_sym) {
+                        // Symmetric book: for x > 0 the eight thresholds up to
+                        // th[7] = 0 lie below x; for x <= 0, th[i] < x exactly
+                        // when th[14 - i] > |x|, and th[j] <= |x| exactly when
+                        // th[j] < nextup(|x|).  Seven compares either way.
+                        const float ax = fabsf(x);
+                        const float vv = x > 0.0f ? ax : __uint_as_float(__float_as_uint(ax) + 1u);
+                        uint32_t c = 0;
 #pragma unroll
-                    for (int i = 0; i < 15; ++i) idx += (x > a.th[i]) ? 1u : 0u;
+                        for (int j = 8; j < 15; ++j) c += (vv > a.th[j]) ? 1u : 0u;
+                        idx = x > 0.0f ? 8u + c : 7u - c;
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 15; ++i) idx += (x > a.th[i]) ? 1u : 0u;
+                    }
                     nib[r] = idx;
                 }
             } else {
@@ -718,6 +732,7 @@ RpbhArgs make_args(const void *X, int64_t T, int K, const int8_t *sign, const in
     a.ngroups = 0;
     a.scale = scale;
     for (int i = 0; i < 15; ++i) a.th[i] = 0.0f;
+    a.th_sym = 0;
     return a;
 }
 
@@ -739,6 +754,10 @@ int launch_rpbh_lloydmax(const void *X, int x_bf16, int64_t T, int K, int block,
     if (n_thresholds != 15) return (int)hipErrorInvalidValue;
     RpbhArgs a = make_args(X, T, K, sign, perm, codes, nullptr, sigma);
     for (int i = 0; i < 15; ++i) a.th[i] = thresholds[i];
+    // ascending thresholds of a book symmetric about 0 (exact float equality)
+    a.th_sym = a.th[7] == 0.0f ? 1 : 0;
+    for (int i = 0; i < 15; ++i)
+        if (a.th[i] != -a.th[14 - i] || (i > 0 && a.th[i] < a.th[i - 1])) a.th_sym = 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int L = ilog2(block);
     return (int)(x_bf16 ? dispatch<true, 1>(L, a, s) : dispatch<false, 1>(L, a, s));

@@ -297,6 +297,29 @@ CODEBOOK_BIG = [
 ]
 
 
+def test_codebook_asymmetric_activation_book():
+    """An activation book that is not symmetric about 0 (the Lloyd-Max levels
+    shifted by 1/16, rounded to bf16) takes the general fifteen-threshold
+    index count in rq_rotate_quant; codes and sigma match the oracle given the
+    same levels bit for bit."""
+    from oracle import oracle as orc
+    w = datagen.WORKLOADS["video"].with_shape(T=190, N=264)
+    say(f"[codebook asymmetric book] {w}")
+    inp = datagen.make_inputs(w)
+    L = H.GpuLayer(w, inp, y_dtype="f32")
+    lv = np.array([orc.round_to_bf16(float(v) + 0.0625) for v in orc.codebook_bf16(16)], np.float32)
+    assert np.all(np.diff(lv) > 0) and (lv[7] + lv[8]) != 0.0
+    L.q = H.rq.Quant.lloydmax(lv, H.rq.lloydmax_gaussian(4))
+    L.rotate_quant()
+    torch.cuda.synchronize()
+    act = orc.act_rows(inp["X"], 1, w.K, np.arange(w.T), rot_kind=0, b=w.block, sign=inp["sign"],
+                       perm=inp["perm"], q_kind=1, levels=lv)
+    check_act(w, L, act)
+    # both ends of the book are in use (indices are unsigned nibbles)
+    nib = np.concatenate([act["codes"] & 15, act["codes"] >> 4])
+    assert nib.min() == 0 and nib.max() == 15
+
+
 @pytest.mark.parametrize("name,shape", CODEBOOK_BIG,
                          ids=[f"{n}-{'-'.join(f'{k}{v}' for k, v in s.items())}" for n, s in CODEBOOK_BIG])
 def test_codebook_mid_size(name, shape):
