@@ -21,20 +21,20 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int BM = 128, BN = 128;
 
-// Output element e of a 32x32 MFMA accumulator held by lane l:
-// column l % 32, row 8 * (e / 4) + 4 * (l / 32) + e % 4.
-__device__ inline int acc_row(int e, int lane) { return 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); }
+// Output element e of a 32x32 MFMA accumulator held by lane l: column
+// l % 32, row 8 * (e / 4) + 4 * (l / 32) + e % 4.  The weight fragment is the
+// MFMA's A operand and the token fragment its B operand, so a lane owns one
+// token and runs of four consecutive output channels.
 
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
-__device__ inline uint16_t f32_to_bf16_rne(float x) {
-    const uint32_t b = __float_as_uint(x);
-    const uint32_t lower = b & 0xFFFFu, upper = b >> 16;
-    return (uint16_t)(upper + ((lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) ? 1u : 0u));
+// two floats -> packed bf16 (round to nearest even), one instruction
+__device__ inline uint32_t bf16x2_rne(float lo, float hi) {
+    const f2v v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
 }
 
-__device__ inline __bf16 bits_to_bf16(uint16_t h) {
-    return __builtin_bit_cast(__bf16, h);
-}
 
 // ---------------------------------------------------------------------------
 // Codebook GEMM (W2A4 / W4A4 Lloyd-Max)
@@ -169,28 +169,47 @@ gemm_codebook_kernel(CodebookArgs a) {
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
         }
         __syncthreads();
     }
+    // acc[i][j]: tokens wm 64 + 32 i + (lane % 32), channels
+    // wn 64 + 32 j + 8 g + 4 (lane / 32) + c for element 4 g + c
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
+        const int64_t t = m0 + wm * 64 + i * 32 + li;
+        if (t >= a.T) continue;
+        const float st = a.sigma[t];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int col = n0 + wn * 64 + j * 32 + li;
-            if (col >= a.N) continue;
-            const float tn = a.tau[col] * a.post;
-            const float bn = a.bias ? a.bias[col] : 0.0f;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t row = m0 + wm * 64 + i * 32 + acc_row(e, lane);
-                if (row >= a.T) continue;
-                const float y = acc[i][j][e] * (a.sigma[row] * tn) + bn;
-                const int64_t o = row * a.N + col;
-                if (a.ydt == RQ_F32)
-                    static_cast<float *>(a.Y)[o] = y;
-                else
-                    static_cast<uint16_t *>(a.Y)[o] = f32_to_bf16_rne(y);
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * 64 + j * 32 + 8 * g + 4 * lg;
+                float y[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int nc = n + c < a.N ? n + c : a.N - 1;
+                    const float tn = a.tau[nc] * a.post;
+                    const float bn = a.bias ? a.bias[nc] : 0.0f;
+                    y[c] = acc[i][j][4 * g + c] * (st * tn) + bn;
+                }
+                const int64_t o = t * a.N + n;
+                if (n + 3 < a.N && (a.N % 4) == 0) {
+                    if (a.ydt == RQ_F32)
+                        *reinterpret_cast<float4 *>(static_cast<float *>(a.Y) + o) = make_float4(y[0], y[1], y[2], y[3]);
+                    else
+                        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.Y) + o) =
+                            make_uint2(bf16x2_rne(y[0], y[1]), bf16x2_rne(y[2], y[3]));
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        if (n + c >= a.N) break;
+                        if (a.ydt == RQ_F32)
+                            static_cast<float *>(a.Y)[o + c] = y[c];
+                        else
+                            static_cast<uint16_t *>(a.Y)[o + c] = (uint16_t)(bf16x2_rne(y[c], 0.0f) & 0xFFFFu);
+                    }
+                }
             }
         }
     }
