@@ -673,7 +673,7 @@ gemm_fp6_mma_kernel(Fp6Args a) {
     };
     auto rd_act = [&](int buf, int j) { return rd(LA + buf * C::LDS_STAGE + j * 3 * 1024); };
     auto rd_w = [&](int buf, int i) { return rd(LW + buf * C::LDS_STAGE + i * 3 * 1024); };
-    // the eight MFMAs of weight fragment i: both k-steps, all token fragments
+    // the MFMAs of weight fragment i: both k-steps, all token fragments
     auto mfma_frag = [&](auto ic, const Frag &w, const Frag (&act)[C::FT]) {
         constexpr int i = decltype(ic)::value;
         const v8i w0 = frag_k0(w), w1 = frag_k1(w);
