@@ -95,6 +95,10 @@ SMALL = [
     ("flux_up_asym", dict(T=33, K=96, N=40, block=2)),
     # OrbitQuant W4A4: a 16-level weight book
     ("video_w4", dict(T=190, N=264)),
+    # two and six threads per token: per-token reductions over runs of two lanes
+    ("tiny", dict(T=45, K=64, N=48, block=64)),
+    ("tiny", dict(T=21, K=192, N=40, block=64)),
+    ("flux_up_asym", dict(T=33, K=64, N=40, block=64)),
 ]
 
 
