@@ -883,9 +883,12 @@ hipError_t launch_cfg(Fp6Args a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// 256 x 256 tiles, four waves of 64 tokens x 256 channels, one workgroup per
-// CU: each token fragment is converted to FP6 by exactly one wave.
-using CfgBig = Cfg<256, 256, 4, 1, 3, 1>;
+// 256 x 256 tiles, eight waves of 64 tokens x 128 channels, one workgroup per
+// CU: two waves per SIMD (128 accumulators each) hide each other's waits.
+// Each token fragment is converted by the two waves that use it; four
+// waves of 64 x 256 (one conversion per fragment, 256 accumulators, one
+// wave per SIMD) were 11% slower.
+using CfgBig = Cfg<256, 256, 4, 2, 3, 1>;
 // 128 x 128 tiles, four waves of 64 x 64, two workgroups per CU: small
 // shapes and the low-rank path (which needs registers for its own sums).
 using CfgMid = Cfg<128, 128, 2, 2, 3, 2>;
