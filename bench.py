@@ -215,6 +215,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="flux", choices=sorted(WORKLOADS))
+    ap.add_argument("--engine", default="auto", choices=["auto", "fp6", "int8"],
+                    help="matrix cores of the INT4 GEMM (int8: the int8-MFMA engine on canonical codes)")
     ap.add_argument("--ring", type=int, default=2, help="independent layer instances cycled")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -248,7 +250,7 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     rq.load()
-    int8_gemm = os.environ.get("RQ_W4A4_MFMA") == "int8"
+    int8_gemm = args.engine == "int8"
     names = WORKLOADS[args.workload]
     wls = [datagen.WORKLOADS[n] for n in names]
 
@@ -276,7 +278,7 @@ def main():
             L.rotate_quant()
             if ev is not None:
                 ev[j][1].record(stream)
-            L.linear()
+            L.linear(engine=args.engine)
             if ev is not None:
                 ev[j][2].record(stream)
 

@@ -41,7 +41,9 @@
  *     device (torch tensors are fine); "host" pointers are CPU memory.
  *   - The caller owns and allocates every buffer; the library allocates no
  *     memory on the runtime path and keeps no state besides a thread-local
- *     error message and its loaded kernels.  Calls are re-entrant.
+ *     error message, its loaded kernels and per-device launch facts (compute-unit
+ *     count, raised LDS limits) that it caches under a lock.  Host threads may
+ *     call in concurrently; calls on one stream run in issue order.
  *   - Runtime calls are asynchronous on `stream` (a hipStream_t; NULL is the
  *     default stream).  Inputs are read only; outputs must not alias inputs.
  *   - Every call validates its arguments before touching the GPU and returns
@@ -76,6 +78,15 @@ typedef enum rq_dtype {
     RQ_BF16 = 1,  /* bfloat16 bit patterns (uint16) */
     RQ_I32 = 2    /* raw int32 accumulators (rq_w4a4_linear output only) */
 } rq_dtype;
+
+/* Matrix cores that run an INT4 GEMM (rq_w4a4_linear_engine).
+ *   AUTO  the library's choice: FP6 for INT4 weights, the codebook kernel
+ *         for Lloyd-Max weights
+ *   FP6   E2M3 operands on v_mfma_scale_f32_32x32x64_f8f6f4: codes carried
+ *         exactly, fp32 accumulation exact, twice the int8 rate
+ *   INT8  v_mfma_i32_32x32x32_i8 with the nibbles widened to int8 in
+ *         registers, int32 accumulation (INT4_SYM weights, canonical codes) */
+typedef enum rq_engine { RQ_ENGINE_AUTO = 0, RQ_ENGINE_FP6 = 1, RQ_ENGINE_INT8 = 2 } rq_engine;
 
 typedef enum rq_rot_kind { RQ_ROT_RPBH = 0, RQ_ROT_DENSE = 1 } rq_rot_kind;
 typedef enum rq_q_kind { RQ_Q_INT4_SYM = 0, RQ_Q_LLOYDMAX = 1, RQ_Q_INT4_ASYM = 2 } rq_q_kind;
@@ -316,9 +327,8 @@ rq_status rq_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void 
  * INT4 weights run on the FP6 (E2M3) matrix cores: activation codes become
  * q + 8, weight codes q, both exact in E2M3, and the per-channel sum of the
  * weight codes (in the blob) removes the offset; every partial sum is an
- * integer below 2^24, so the fp32 accumulation is exact.  With
- * RQ_W4A4_MFMA=int8 in the environment the int8 matrix cores run instead
- * (codes must then be given; INT4_SYM only).
+ * integer below 2^24, so the fp32 accumulation is exact.
+ * rq_w4a4_linear_engine() selects the matrix cores explicitly.
  * Arguments:
  *   hdr     host pointer to the blob's header (its first 256 bytes)
  *   blob    device copy of the whole blob, 16-byte aligned
@@ -339,6 +349,21 @@ rq_status rq_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void 
 rq_status rq_w4a4_linear(const rq_weight_header *hdr, const void *blob, const uint8_t *codes,
                          const float *scale, const uint16_t *top, const uint8_t *codes_mma,
                          int64_t T, const float *bias, void *Y, int32_t y_dtype, void *stream);
+
+/*
+ * rq_w4a4_linear with an explicit choice of matrix cores (same passages and
+ * arguments as rq_w4a4_linear, which is this call with RQ_ENGINE_AUTO).
+ *   engine  rq_engine.  RQ_ENGINE_INT8 takes INT4_SYM weights (any r) and
+ *           the canonical codes (codes_mma must be NULL); the accumulators
+ *           and outputs equal the FP6 engine's bit for bit.  The Lloyd-Max
+ *           format takes RQ_ENGINE_AUTO only.
+ * Errors: as rq_w4a4_linear; RQ_ERR_UNSUPPORTED for an engine that cannot
+ *         run the blob's format or for codes_mma with RQ_ENGINE_INT8.
+ */
+rq_status rq_w4a4_linear_engine(const rq_weight_header *hdr, const void *blob,
+                                const uint8_t *codes, const float *scale, const uint16_t *top,
+                                const uint8_t *codes_mma, int64_t T, const float *bias, void *Y,
+                                int32_t y_dtype, int32_t engine, void *stream);
 
 #ifdef __cplusplus
 }

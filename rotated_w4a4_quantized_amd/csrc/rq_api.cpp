@@ -4,7 +4,6 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
-#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -47,17 +46,6 @@ rq_status check_header(const rq_weight_header *hdr) {
             return fail(RQ_ERR_FORMAT, "weight header FP6 section offsets are inconsistent");
     }
     return RQ_OK;
-}
-
-// Which matrix cores run the INT4 GEMM: FP6 (default; exact, twice the int8
-// rate on gfx950) or, with RQ_W4A4_MFMA=int8 in the environment, the int8
-// kernel that widens the nibbles in registers.  Read once per process.
-bool use_int8_gemm() {
-    static const bool v = [] {
-        const char *e = std::getenv("RQ_W4A4_MFMA");
-        return e && std::strcmp(e, "int8") == 0;
-    }();
-    return v;
 }
 
 }  // namespace
@@ -138,28 +126,35 @@ rq_status rq_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void 
                       "dense quant launch");
 }
 
-rq_status rq_w4a4_linear(const rq_weight_header *hdr, const void *blob, const uint8_t *codes,
-                         const float *scale, const uint16_t *top, const uint8_t *codes_mma,
-                         int64_t T, const float *bias, void *Y, int32_t y_dtype, void *stream) {
+rq_status rq_w4a4_linear_engine(const rq_weight_header *hdr, const void *blob,
+                                const uint8_t *codes, const float *scale, const uint16_t *top,
+                                const uint8_t *codes_mma, int64_t T, const float *bias, void *Y,
+                                int32_t y_dtype, int32_t engine, void *stream) {
     clear_error();
     rq_status st = check_header(hdr);
     if (st != RQ_OK) return st;
     if (y_dtype != RQ_F32 && y_dtype != RQ_BF16 && y_dtype != RQ_I32)
         return fail(RQ_ERR_DTYPE, "Y must be RQ_F32, RQ_BF16 or RQ_I32");
+    if (engine != RQ_ENGINE_AUTO && engine != RQ_ENGINE_FP6 && engine != RQ_ENGINE_INT8)
+        return fail(RQ_ERR_UNSUPPORTED, "unknown engine " + std::to_string(engine));
     const bool int4 = hdr->format != RQ_Q_LLOYDMAX;
     const bool asym = hdr->format == RQ_Q_INT4_ASYM;
     if (y_dtype == RQ_I32 && !int4)
         return fail(RQ_ERR_UNSUPPORTED, "raw accumulators exist for INT4 weights only");
     if (codes_mma && (!int4 || hdr->r != 0))
         return fail(RQ_ERR_UNSUPPORTED, "codes_mma is read for INT4 weights with r == 0 only");
-    if (asym && use_int8_gemm())
-        return fail(RQ_ERR_UNSUPPORTED, "the int8 GEMM (RQ_W4A4_MFMA=int8) takes INT4_SYM only");
+    if (engine != RQ_ENGINE_AUTO && !int4)
+        return fail(RQ_ERR_UNSUPPORTED, "the Lloyd-Max format has one engine (RQ_ENGINE_AUTO)");
+    const bool int8 = engine == RQ_ENGINE_INT8;
+    if (int8 && asym)
+        return fail(RQ_ERR_UNSUPPORTED, "the int8 engine takes INT4_SYM weights only");
+    if (int8 && codes_mma)
+        return fail(RQ_ERR_UNSUPPORTED, "the int8 engine reads the canonical codes (codes_mma must be NULL)");
     if (T < 0 || T >= (int64_t(1) << 31)) return fail(RQ_ERR_SHAPE, "T out of range");
     if (T == 0) return RQ_OK;
-    const bool int8 = hdr->format == RQ_Q_INT4_SYM && use_int8_gemm();
-    if (!blob || !scale || !Y || (!codes && !codes_mma) || (int8 && !codes))
+    if (!blob || !scale || !Y || (!codes && !codes_mma))
         return fail(RQ_ERR_NULL, "blob, scale, Y and the activation codes must not be NULL");
-    if (!int4 && !codes) return fail(RQ_ERR_NULL, "LLOYDMAX needs codes");
+    if ((!int4 || int8) && !codes) return fail(RQ_ERR_NULL, "this engine needs codes");
     if (hdr->r > 0 && !top) return fail(RQ_ERR_NULL, "weights with r > 0 need top");
     if (!aligned16(blob) || (codes && !aligned16(codes)) || !aligned16(scale) || !aligned16(Y) ||
         (top && !aligned16(top)) || (bias && !aligned16(bias)) ||
@@ -176,6 +171,13 @@ rq_status rq_w4a4_linear(const rq_weight_header *hdr, const void *blob, const ui
     }
     return hip_status(launch_gemm_codebook(codes, scale, T, hdr, blob, bias, Y, y_dtype, stream),
                       "codebook gemm launch");
+}
+
+rq_status rq_w4a4_linear(const rq_weight_header *hdr, const void *blob, const uint8_t *codes,
+                         const float *scale, const uint16_t *top, const uint8_t *codes_mma,
+                         int64_t T, const float *bias, void *Y, int32_t y_dtype, void *stream) {
+    return rq_w4a4_linear_engine(hdr, blob, codes, scale, top, codes_mma, T, bias, Y, y_dtype,
+                                 RQ_ENGINE_AUTO, stream);
 }
 
 }  // extern "C"

@@ -7,9 +7,9 @@
 //   RPBH:  Y = s_a[t] s_w[n] acc / b
 //   DENSE: Y = s_w[n] (lr[t][n] + s_a[t] acc),  lr = sum_{j<r} bf16(u)[t][j] qw[n][j]
 //
-// This is the int8 baseline of the INT4 GEMM (selected with
-// RQ_W4A4_MFMA=int8); the default runs on the FP6 matrix cores
-// (rq_gemm_fp6.hip) at twice the rate.
+// This is the int8 engine of the INT4 GEMM (rq_w4a4_linear_engine with
+// RQ_ENGINE_INT8); the default runs on the FP6 matrix cores
+// (rq_gemm_fp6.hip) at twice the rate, with the same accumulators.
 //
 // Widening: gfx950 has no 4-bit MFMA.  For a packed word p (eight nibbles,
 // low nibble = even k), (p << 4) & 0xF0F0F0F0 holds 16 q for the even k and

@@ -26,6 +26,13 @@ inline int64_t mma_codes_bytes(int64_t T, int Kq) {
     return ((T + 31) / 32) * (int64_t)((Kq + 127) / 128) * 3 * 1024;
 }
 
+// Launch facts of the current HIP device, cached per device and safe to call
+// from several host threads: compute units, and raising a kernel's dynamic-LDS
+// limit to `bytes` (once per kernel and device; a no-op up to 64 KB).  The
+// second returns a hipError_t as int.
+int device_cus();
+int ensure_dyn_lds(const void *kernel, size_t bytes);
+
 // Kernel launchers (rq_rpbh.hip, rq_dense.hip, rq_gemm_*.hip).  Arguments are validated
 // by the caller; these only launch.  They return a hipError_t as int.
 // asym: per-token zero point (INT4_ASYM), written to scale[T .. 2T)

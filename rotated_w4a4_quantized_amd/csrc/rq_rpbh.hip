@@ -483,8 +483,11 @@ rpbh_quant_kernel(RpbhArgs a) {
             if (d != 0.0f) {
                 const float inv = 15.0f / d;
                 sc = d / 15.0f;
+                // z is the integer -rne(lo inv) clamped to [0, 15], as a float;
+                // rne(lo inv) = -0 or +0 (a row whose minimum is at most s / 2
+                // from zero) gives z = +0
                 const float zr = rintf(lo * inv);
-                zp = zr > 0.0f ? 0.0f : (zr < -15.0f ? 15.0f : -zr);
+                zp = zr >= 0.0f ? 0.0f : (zr < -15.0f ? 15.0f : -zr);
 #pragma unroll
                 for (int r = 0; r < kE; ++r) {
                     const float t = fminf(fmaxf(rintf(v[r] * inv) + zp, 0.0f), 15.0f);
@@ -600,20 +603,6 @@ rpbh_quant_kernel(RpbhArgs a) {
     }
 }
 
-int g_num_cus = 0;
-
-int num_cus() {
-    if (g_num_cus == 0) {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-            g_num_cus = n;
-        else
-            g_num_cus = 256;
-    }
-    return g_num_cus;
-}
-
 template <int L, bool BF16, int QK>
 hipError_t launch_L(RpbhArgs a, hipStream_t s) {
     const int xb = BF16 ? 2 : 4;
@@ -631,17 +620,17 @@ hipError_t launch_L(RpbhArgs a, hipStream_t s) {
     auto group_of = [&](int tpw) { return grouped && tpw < 4 ? 4 : tpw; };
     auto lds_of = [&](int tpw) { return per_tok * tpw + slot * group_of(tpw); };
     auto kern = rpbh_quant_kernel<L, BF16, QK>;
-    // waves one SIMD holds given the kernel's registers (512 per lane)
-    static int simd_waves = 0;
-    if (simd_waves == 0) {
+    // waves one SIMD holds given the kernel's registers (512 per lane); the
+    // same on every gfx950 device, read once (thread-safe static init)
+    static const int simd_waves = [kern] {
         hipFuncAttributes fa;
         int w = 2;
         if (hipFuncGetAttributes(&fa, (const void *)kern) == hipSuccess && fa.numRegs > 0) {
             w = 512 / ((fa.numRegs + 7) & ~7);
             w = w < 1 ? 1 : (w > 8 ? 8 : w);
         }
-        simd_waves = w;
-    }
+        return w;
+    }();
     // Tokens per workgroup (<= 768 or 512 threads, <= 159 KB of LDS) and workgroups
     // per CU (as many as LDS and registers allow, or fewer).  A workgroup of
     // w waves puts ceil(w / 4) of them on some SIMD, and co-resident
@@ -652,7 +641,7 @@ hipError_t launch_L(RpbhArgs a, hipStream_t s) {
     // several workgroups at once as kOverlap times as fast per workgroup as
     // one that runs a single one; ties go to more waves per CU, then to the
     // larger workgroup (fewer barriers per token).
-    const int cus = num_cus();
+    const int cus = device_cus();
     int best_tpw = 1, best_occ = 1, best_waves = 0;
     double best_cost = -1.0;
     for (int tpw = 1; tpw <= kMaxTpw; tpw *= 2) {
@@ -685,13 +674,10 @@ hipError_t launch_L(RpbhArgs a, hipStream_t s) {
     const size_t lds = lds_of(best_tpw);
     const int64_t resident = (int64_t)cus * best_occ;
     const int grid = (int)(a.ngroups < resident ? a.ngroups : resident);
-    // raise the dynamic-LDS limit once per instantiation (the call is not free)
-    static size_t lds_set = 0;
-    if (lds > 64 * 1024 && lds > lds_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    // raise the dynamic-LDS limit once per kernel and device (the call is not free)
+    {
+        const hipError_t e = (hipError_t)ensure_dyn_lds((const void *)kern, lds);
         if (e != hipSuccess) return e;
-        lds_set = lds;
     }
     hipLaunchKernelGGL(kern, dim3(grid), dim3(a.tpw * a.tpt), lds, s, a);
     return hipGetLastError();

@@ -78,19 +78,19 @@ class QuantLinear:
         rq.rotate_quant(self.drot, self.q, self.X, self.codes, self.scale, self.top, self.ws,
                         stream=stream, codes_mma=self.codes_mma)
 
-    def linear(self, Y=None, stream=None, use_mma=True):
+    def linear(self, Y=None, stream=None, use_mma=True, engine="auto"):
         rq.w4a4_linear(self.dw, self.codes, self.scale, self.Y if Y is None else Y, top=self.top,
                        stream=stream, T=self.w.T,
-                       codes_mma=self.codes_mma if use_mma else None)
+                       codes_mma=self.codes_mma if use_mma else None, engine=engine)
 
     def run(self):
         self.rotate_quant()
         self.linear()
 
-    def raw_acc(self, use_mma=True):
+    def raw_acc(self, use_mma=True, engine="auto"):
         torch = torch_mod()
         acc = torch.empty((self.w.T, self.w.N), dtype=torch.int32, device=self.device)
-        self.linear(acc, use_mma=use_mma)
+        self.linear(acc, use_mma=use_mma, engine=engine)
         return acc
 
 

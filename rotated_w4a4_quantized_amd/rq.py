@@ -22,6 +22,8 @@ RQ_OK = 0
 RQ_F32, RQ_BF16, RQ_I32 = 0, 1, 2
 RQ_ROT_RPBH, RQ_ROT_DENSE = 0, 1
 RQ_Q_INT4_SYM, RQ_Q_LLOYDMAX, RQ_Q_INT4_ASYM = 0, 1, 2
+RQ_ENGINE_AUTO, RQ_ENGINE_FP6, RQ_ENGINE_INT8 = 0, 1, 2
+ENGINES = {"auto": RQ_ENGINE_AUTO, "fp6": RQ_ENGINE_FP6, "int8": RQ_ENGINE_INT8}
 RQ_WEIGHT_MAGIC = 0x31575152
 STATUS_NAMES = {0: "RQ_OK", -1: "RQ_ERR_NULL", -2: "RQ_ERR_SHAPE", -3: "RQ_ERR_DTYPE",
                 -4: "RQ_ERR_ALIGN", -5: "RQ_ERR_FORMAT", -6: "RQ_ERR_UNSUPPORTED",
@@ -63,7 +65,7 @@ assert ctypes.sizeof(c_weight_header) == 256
 # every symbol include/rq.h declares
 EXPORTS = ("rq_version", "rq_last_error", "rq_lloydmax_gaussian", "rq_packed_weight_bytes",
            "rq_pack_weights", "rq_rotate_quant_workspace_bytes", "rq_codes_mma_bytes",
-           "rq_rotate_quant", "rq_w4a4_linear")
+           "rq_rotate_quant", "rq_w4a4_linear", "rq_w4a4_linear_engine")
 
 _lib = None
 
@@ -88,9 +90,10 @@ def load() -> ctypes.CDLL:
     L.rq_codes_mma_bytes.argtypes = [P, I64, ctypes.POINTER(SZ)]
     L.rq_rotate_quant.argtypes = [P, P, P, I32, I64, P, P, P, P, P, SZ, P]
     L.rq_w4a4_linear.argtypes = [P, P, P, P, P, P, I64, P, P, I32, P]
+    L.rq_w4a4_linear_engine.argtypes = [P, P, P, P, P, P, I64, P, P, I32, I32, P]
     for name in ("rq_lloydmax_gaussian", "rq_packed_weight_bytes", "rq_pack_weights",
                  "rq_rotate_quant_workspace_bytes", "rq_codes_mma_bytes", "rq_rotate_quant",
-                 "rq_w4a4_linear"):
+                 "rq_w4a4_linear", "rq_w4a4_linear_engine"):
         getattr(L, name).restype = I32
     _lib = L
     return L
@@ -343,13 +346,17 @@ def rotate_quant(drot: DeviceRotation, q: Quant, X, codes, scale, top=None, work
 
 
 def w4a4_linear(dw: DeviceWeights, codes, scale, Y, top=None, bias=None, T=None, stream=None,
-                codes_mma=None):
+                codes_mma=None, engine="auto"):
     """Launch the low-bit GEMM; Y dtype picks the output (f32, bf16, raw int32).
-    When codes_mma is given it is read instead of codes (which may be None)."""
+    When codes_mma is given it is read instead of codes (which may be None).
+    engine: "auto" (rq_w4a4_linear), or "fp6" / "int8" (rq_w4a4_linear_engine)."""
     if T is None:
         if codes is None:
             raise ValueError("T must be given when codes is None")
         T = int(codes.shape[0])
-    _check(load().rq_w4a4_linear(ctypes.byref(dw.header), _t_ptr(dw.blob), _t_ptr(codes),
-                                 _t_ptr(scale), _t_ptr(top), _t_ptr(codes_mma), T, _t_ptr(bias),
-                                 _t_ptr(Y), dtype_code(Y), _stream(stream)))
+    args = (ctypes.byref(dw.header), _t_ptr(dw.blob), _t_ptr(codes), _t_ptr(scale), _t_ptr(top),
+            _t_ptr(codes_mma), T, _t_ptr(bias), _t_ptr(Y), dtype_code(Y))
+    if engine == "auto":
+        _check(load().rq_w4a4_linear(*args, _stream(stream)))
+    else:
+        _check(load().rq_w4a4_linear_engine(*args, ENGINES[engine], _stream(stream)))

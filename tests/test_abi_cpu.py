@@ -163,6 +163,39 @@ def test_linear_validation_errors():
     assert L.rq_w4a4_linear(*args(dh, mma=1 << 23)) == -6
 
 
+def test_engine_validation_errors():
+    """rq_w4a4_linear_engine rejects what its engine cannot run, before any
+    GPU call."""
+    L = rq.load()
+    hdr = _small_header()
+
+    def call(h, engine, codes=1 << 21, mma=None):
+        return L.rq_w4a4_linear_engine(ctypes.byref(h), ctypes.c_void_p(1 << 20),
+                                       None if codes is None else ctypes.c_void_p(codes),
+                                       ctypes.c_void_p(1 << 22), None,
+                                       None if mma is None else ctypes.c_void_p(mma), 4, None,
+                                       ctypes.c_void_p(1 << 24), rq.RQ_F32, engine, None)
+    assert call(hdr, 7) == -6                                  # unknown engine
+    assert call(hdr, rq.RQ_ENGINE_INT8, mma=1 << 23) == -6     # int8 reads canonical codes
+    assert call(hdr, rq.RQ_ENGINE_INT8, codes=None) == -1
+    w = datagen.WORKLOADS["flux_up_asym"].with_shape(T=4, K=256, N=40, block=64)
+    inp = datagen.make_inputs(w)
+    ah = rq.pack_weights(rq.Rotation.rpbh(inp["sign"], inp["perm"], 64), rq.Quant.int4_asym(),
+                         inp["W"]).header
+    assert call(ah, rq.RQ_ENGINE_INT8) == -6                   # int8 engine: INT4_SYM only
+    w = datagen.WORKLOADS["video"].with_shape(T=4, K=256, N=40)
+    inp = datagen.make_inputs(w)
+    lh = rq.pack_weights(rq.Rotation.rpbh(inp["sign"], inp["perm"], 256),
+                         rq.Quant.lloydmax(rq.lloydmax_gaussian(16), rq.lloydmax_gaussian(4)),
+                         inp["W"]).header
+    assert call(lh, rq.RQ_ENGINE_FP6) == -6                    # codebook: AUTO only
+    assert call(hdr, rq.RQ_ENGINE_INT8, codes=None) == -1
+    # T == 0 is a no-op for every engine
+    for e in (rq.RQ_ENGINE_AUTO, rq.RQ_ENGINE_FP6, rq.RQ_ENGINE_INT8):
+        assert L.rq_w4a4_linear_engine(ctypes.byref(hdr), None, None, None, None, None, 0, None,
+                                       None, rq.RQ_F32, e, None) == 0
+
+
 def test_lloydmax_codebook_matches_oracle():
     for L in (2, 4, 8, 16):
         assert np.array_equal(rq.lloydmax_gaussian(L), orc.codebook_bf16(L)), L

@@ -107,7 +107,12 @@ SMALL = [
 def test_small_full_parity(name, shape):
     w = datagen.WORKLOADS[name].with_shape(**shape)
     say(f"[parity small] {w}")
-    inp = datagen.make_inputs(w)
+    small_parity(w, datagen.make_inputs(w))
+
+
+def small_parity(w, inp):
+    """Every code, scale, accumulator and output of one small layer against
+    the oracle (both code layouts for RPBH INT4, both output dtypes)."""
     L = H.GpuLayer(w, inp, y_dtype="f32", codes=mma_mode(w))
     L.run()
     torch.cuda.synchronize()
@@ -177,6 +182,14 @@ def test_full_workload_parity(name):
     Y = L.Y
     idx = torch.from_numpy(ta).to("cuda") * w.N + torch.from_numpy(nw).to("cuda")
     ys = Y.view(-1)[idx]
+    if w.quant == "int4" and w.r == 0:
+        # the exact int32 accumulators of the same launch configuration at
+        # the sampled pairs
+        acc = L.raw_acc().view(-1)[idx].cpu().numpy().astype(np.int64)
+        ia = ta if rows is None else np.searchsorted(rows, ta)
+        ref = H.orc.int_gemm_pairs(act["codes"], w.Kq, wts["codes"], w.K, ia, nw, koff=w.r)
+        assert np.array_equal(acc, ref), f"accumulators differ at {int(np.sum(acc != ref))} pairs"
+        say(f"  int32 accumulators bit-exact at {ta.size} pairs")
     if w.ydtype == "f32":
         err = H.rel_err(ys.cpu().numpy(), yhat)
         say(f"  fp32 max floored rel err {err:.3e}")
@@ -351,3 +364,103 @@ def test_codebook_mid_size(name, shape):
     dist, ok = H.bf16_check(H.to_np_bf16_bits(Yb.view(-1)[idx]), yhat)
     say(f"  bf16 max ulp distance {dist}")
     assert ok
+
+
+def test_asym_nonnegative_rows():
+    """Asymmetric activations whose rotated row has a non-negative minimum:
+    rne(min / s) is +0 or positive, and the zero point must be +0.0 exactly
+    (bits 0), as the oracle stores it.  K = block, identity permutation and
+    +1 signs, so x = a e0 + c e1 rotates to u = (a + c, a - c, a + c, ...);
+    with 0 < c < a every coordinate is positive.  Also: rows whose minimum
+    is a tiny positive or negative number, a constant rotated row (x = e0,
+    d = 0) and ordinary Gaussian rows."""
+    base = datagen.WORKLOADS["flux_up_asym"].with_shape(T=96, K=256, N=72, block=256)
+    inp = datagen.make_inputs(base)
+    X = np.zeros((base.T, base.K), np.float32)
+    pairs = [(1.0, 0.97), (1.0, 0.999), (2.0, 1.5), (3.0, 0.5), (1.0, 1.0 - 2.0 ** -10),
+             (0.75, 0.25), (1.0, 1.001), (1.0, 1.02), (0.5, 0.5)]
+    for i, (a, c) in enumerate(pairs):
+        X[i, 0], X[i, 1] = a, c
+    X[len(pairs), 0] = 1.0                    # constant rotated row: d = 0
+    g = np.random.default_rng(11)
+    X[len(pairs) + 1:] = g.standard_normal((base.T - len(pairs) - 1, base.K)).astype(np.float32)
+    xb = datagen.f32_to_bf16_bits(X)
+    inp = dict(inp, X=xb, Xf=datagen.bf16_bits_to_f32(xb),
+               sign=np.ones(base.K, np.int8), perm=np.arange(base.K, dtype=np.int32))
+    act = H.oracle_act(base, inp)
+    z = act["zero"][:len(pairs)]
+    assert np.any(z.view(np.uint32) == 0), "no row reaches the +0 zero point"
+    say(f"[asym non-negative rows] zero points {z.tolist()}")
+    small_parity(base, inp)
+
+
+# The int8-MFMA engine (rq_w4a4_linear_engine, RQ_ENGINE_INT8) on canonical
+# codes: exact accumulators against the oracle, outputs within tolerance and
+# equal to the FP6 engine's bit for bit (same accumulators, same fp32
+# epilogue operations).
+INT8_ENGINE = [
+    ("tiny", dict(T=300, N=200)),
+    ("flux_up", dict(T=257, K=3072, N=384)),
+    ("flux_down", dict(T=131, K=12288, N=136)),
+    ("pixart", dict(T=200, N=170)),
+    ("tiny", dict(T=65, K=96, N=40, block=2)),
+    ("flux_up", dict(T=600, K=1024, N=800, block=256)),
+]
+
+
+@pytest.mark.parametrize("name,shape", INT8_ENGINE,
+                         ids=[f"{n}-{'-'.join(f'{k}{v}' for k, v in s.items())}" for n, s in INT8_ENGINE])
+def test_int8_engine_parity(name, shape):
+    w = datagen.WORKLOADS[name].with_shape(**shape)
+    say(f"[int8 engine] {w}")
+    inp = datagen.make_inputs(w)
+    L = H.GpuLayer(w, inp, y_dtype="f32")
+    L.rotate_quant()
+    torch.cuda.synchronize()
+    act = H.oracle_act(w, inp)
+    wts = H.oracle_weights(w, inp)
+    acc = L.raw_acc(engine="int8").cpu().numpy().astype(np.int64)
+    assert np.array_equal(acc, H.oracle_raw_acc(w, act, wts))
+    Yi = torch.empty((w.T, w.N), dtype=torch.float32, device="cuda")
+    L.linear(Yi, engine="int8")
+    ta, nw = np.meshgrid(np.arange(w.T), np.arange(w.N), indexing="ij")
+    yhat = H.oracle_yhat_pairs(w, act, wts, ta.ravel(), nw.ravel())
+    err = H.rel_err(Yi.cpu().numpy().ravel(), yhat)
+    say(f"  fp32 max floored rel err {err:.3e}")
+    assert err <= H.REL_TOL
+    Yf = torch.empty_like(Yi)
+    L.linear(Yf, engine="fp6")
+    assert torch.equal(Yi, Yf)
+    Bi = torch.empty((w.T, w.N), dtype=torch.bfloat16, device="cuda")
+    Bf = torch.empty_like(Bi)
+    L.linear(Bi, engine="int8")
+    L.linear(Bf, engine="fp6")
+    torch.cuda.synchronize()
+    assert torch.equal(Bi.view(torch.int16), Bf.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["flux_up", "flux_down"])
+def test_int8_engine_full_workload(name):
+    """The int8 engine at the full FLUX shapes (the bench's --engine int8
+    configuration): accumulators at sampled pairs against the oracle, and
+    the bf16 output equal to the FP6 engine's bit for bit."""
+    w = datagen.WORKLOADS[name]
+    say(f"[int8 engine full] {w}")
+    inp = datagen.make_inputs(w)
+    L = H.GpuLayer(w, inp)
+    L.rotate_quant()
+    Bi = torch.empty((w.T, w.N), dtype=torch.bfloat16, device="cuda")
+    L.linear(Bi, engine="int8")
+    L.linear(engine="fp6")
+    torch.cuda.synchronize()
+    assert torch.equal(Bi.view(torch.int16), L.Y.view(torch.int16))
+    g = np.random.default_rng(3)
+    ta = g.integers(0, w.T, 4096)
+    nw = g.integers(0, w.N, 4096)
+    rows = np.unique(ta)
+    act = H.oracle_act(w, inp, rows)
+    wts = H.oracle_weights(w, inp)
+    idx = torch.from_numpy(ta).to("cuda") * w.N + torch.from_numpy(nw).to("cuda")
+    acc = L.raw_acc(engine="int8").view(-1)[idx].cpu().numpy().astype(np.int64)
+    ref = H.orc.int_gemm_pairs(act["codes"], w.Kq, wts["codes"], w.K, np.searchsorted(rows, ta), nw)
+    assert np.array_equal(acc, ref)
