@@ -311,6 +311,24 @@ rq_status rq_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void 
                           size_t workspace_bytes, void *stream);
 
 /*
+ * rq_rotate_quant for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments without the workspace, the same kernels and the same
+ * results bit for bit.  DENSE stages its fp32 rotated tokens in a scratch
+ * array inside the library (one per device, 64 MiB, held from the module's
+ * load until the process ends; its address is looked up once per device at
+ * the first call there); RPBH uses none.  The call allocates nothing and
+ * calls no allocating routine.  Every call on a device shares that device's
+ * scratch: DENSE calls that overlap on one device (other streams, other host
+ * threads) race and must be serialized by the caller.
+ * Errors: as rq_rotate_quant; RQ_ERR_SHAPE when DENSE needs more than
+ *         64 MiB (T * K * 4 bytes) -- use rq_rotate_quant with a workspace.
+ */
+rq_status rq_rotate_quant_noalloc(const rq_rotation *rot, const rq_quant *q, const void *X,
+                                  int32_t x_dtype, int64_t T, uint8_t *codes, float *scale,
+                                  uint16_t *top, uint8_t *codes_mma, void *stream);
+
+/*
  * Runtime low-bit GEMM with the per-token x per-channel rescale
  * (TR-DQ section 3.1: Y = X W with per-token activation and per-channel
  * weight scales; DiRotQ abstract: the top principal coefficients add a

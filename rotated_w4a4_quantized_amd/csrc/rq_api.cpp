@@ -48,6 +48,33 @@ rq_status check_header(const rq_weight_header *hdr) {
     return RQ_OK;
 }
 
+// Argument checks of the runtime activation call that follow the descriptor
+// checks (everything but the workspace).
+rq_status validate_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void *X,
+                                int32_t x_dtype, int64_t T, const uint8_t *codes,
+                                const float *scale, const uint16_t *top,
+                                const uint8_t *codes_mma) {
+    if (x_dtype != RQ_F32 && x_dtype != RQ_BF16)
+        return fail(RQ_ERR_DTYPE, "X must be RQ_F32 or RQ_BF16");
+    if (T < 0 || T >= (int64_t(1) << 31)) return fail(RQ_ERR_SHAPE, "T out of range");
+    const bool dense = rot->kind == RQ_ROT_DENSE;
+    const bool int4 = q->kind == RQ_Q_INT4_SYM || q->kind == RQ_Q_INT4_ASYM;
+    if (codes_mma && (dense || !int4))
+        return fail(RQ_ERR_UNSUPPORTED, "codes_mma is written for RPBH with INT4 only");
+    if (T == 0) return RQ_OK;
+    if (!X || !scale || (!codes && !codes_mma))
+        return fail(RQ_ERR_NULL, "X, scale and at least one of codes / codes_mma must not be NULL");
+    if (dense && !codes) return fail(RQ_ERR_NULL, "DENSE needs codes");
+    if (!int4 && !codes) return fail(RQ_ERR_NULL, "LLOYDMAX needs codes");
+    if (dense && rot->r > 0 && !top) return fail(RQ_ERR_NULL, "DENSE with r > 0 needs top");
+    if (!aligned16(X) || (codes && !aligned16(codes)) || !aligned16(scale) ||
+        (top && !aligned16(top)) || (codes_mma && !aligned16(codes_mma)))
+        return fail(RQ_ERR_ALIGN, "device buffers must be 16-byte aligned");
+    if (!dense && (!aligned16(rot->sign) || !aligned16(rot->perm)))
+        return fail(RQ_ERR_ALIGN, "RPBH sign and perm must be 16-byte aligned");
+    return RQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -82,25 +109,12 @@ rq_status rq_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void 
     rq_status st = check_rotation(rot, true);
     if (st != RQ_OK) return st;
     if ((st = check_quant(rot, q)) != RQ_OK) return st;
-    if (x_dtype != RQ_F32 && x_dtype != RQ_BF16)
-        return fail(RQ_ERR_DTYPE, "X must be RQ_F32 or RQ_BF16");
-    if (T < 0 || T >= (int64_t(1) << 31)) return fail(RQ_ERR_SHAPE, "T out of range");
+    if ((st = validate_rotate_quant(rot, q, X, x_dtype, T, codes, scale, top, codes_mma)) != RQ_OK)
+        return st;
+    if (T == 0) return RQ_OK;
     const int K = rot->K;
     const bool dense = rot->kind == RQ_ROT_DENSE;
     const bool int4 = q->kind == RQ_Q_INT4_SYM || q->kind == RQ_Q_INT4_ASYM;
-    if (codes_mma && (dense || !int4))
-        return fail(RQ_ERR_UNSUPPORTED, "codes_mma is written for RPBH with INT4 only");
-    if (T == 0) return RQ_OK;
-    if (!X || !scale || (!codes && !codes_mma))
-        return fail(RQ_ERR_NULL, "X, scale and at least one of codes / codes_mma must not be NULL");
-    if (dense && !codes) return fail(RQ_ERR_NULL, "DENSE needs codes");
-    if (!int4 && !codes) return fail(RQ_ERR_NULL, "LLOYDMAX needs codes");
-    if (dense && rot->r > 0 && !top) return fail(RQ_ERR_NULL, "DENSE with r > 0 needs top");
-    if (!aligned16(X) || (codes && !aligned16(codes)) || !aligned16(scale) ||
-        (top && !aligned16(top)) || (codes_mma && !aligned16(codes_mma)))
-        return fail(RQ_ERR_ALIGN, "device buffers must be 16-byte aligned");
-    if (!dense && (!aligned16(rot->sign) || !aligned16(rot->perm)))
-        return fail(RQ_ERR_ALIGN, "RPBH sign and perm must be 16-byte aligned");
     const int xb = x_dtype == RQ_BF16 ? 1 : 0;
     if (!dense) {
         if (int4)
@@ -124,6 +138,34 @@ rq_status rq_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void 
     if (st != RQ_OK) return st;
     return hip_status(launch_dense_quant(U, T, K, rot->r, codes, scale, top, stream),
                       "dense quant launch");
+}
+
+rq_status rq_rotate_quant_noalloc(const rq_rotation *rot, const rq_quant *q, const void *X,
+                                  int32_t x_dtype, int64_t T, uint8_t *codes, float *scale,
+                                  uint16_t *top, uint8_t *codes_mma, void *stream) {
+    clear_error();
+    rq_status st = check_rotation(rot, true);
+    if (st != RQ_OK) return st;
+    if ((st = check_quant(rot, q)) != RQ_OK) return st;
+    if (rot->kind != RQ_ROT_DENSE)   // RPBH kernels use no scratch
+        return rq_rotate_quant(rot, q, X, x_dtype, T, codes, scale, top, codes_mma, nullptr, 0,
+                               stream);
+    if (T < 0 || T >= (int64_t(1) << 31)) return fail(RQ_ERR_SHAPE, "T out of range");
+    const size_t need = (size_t)T * (size_t)rot->K * sizeof(float);
+    if (need > kDenseScratchBytes)
+        return fail(RQ_ERR_SHAPE, "rq_rotate_quant_noalloc: DENSE needs T * K * 4 = " +
+                                      std::to_string(need) + " bytes of scratch, above its " +
+                                      std::to_string(kDenseScratchBytes) +
+                                      "-byte limit; use rq_rotate_quant with a workspace");
+    if (T == 0) return rq_rotate_quant(rot, q, X, x_dtype, 0, codes, scale, top, codes_mma,
+                                       nullptr, 0, stream);
+    // every argument check runs before the scratch lookup touches the GPU
+    st = validate_rotate_quant(rot, q, X, x_dtype, T, codes, scale, top, codes_mma);
+    if (st != RQ_OK) return st;
+    float *ws = nullptr;
+    st = hip_status(dense_scratch(&ws), "scratch lookup");
+    if (st != RQ_OK) return st;
+    return rq_rotate_quant(rot, q, X, x_dtype, T, codes, scale, top, codes_mma, ws, need, stream);
 }
 
 rq_status rq_w4a4_linear_engine(const rq_weight_header *hdr, const void *blob,

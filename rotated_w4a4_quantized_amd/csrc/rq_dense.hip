@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "rq_internal.h"
 
 namespace rq {
@@ -130,7 +132,34 @@ dense_quant_kernel(const float *__restrict__ U, int64_t T, int K, int r,
     if (lane == 0) scale[tok] = m > 0.0f ? m / 7.0f : 0.0f;
 }
 
+// Device scratch of the allocation-free entry point (rq_rotate_quant_noalloc):
+// the fp32 rotated tokens of a DENSE call, kDenseScratchBytes at most.  One
+// copy per device, held from the module's load until the process ends.  In
+// host code the name is only a stand-in: kernels get the address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) float scratch[kDenseScratchBytes / sizeof(float)];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+float *g_scratch_ptr[kMaxScratchDevices];   // per device, null until looked up
+
 }  // namespace
+
+int dense_scratch(float **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return (int)hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return (int)e;
+        g_scratch_ptr[dev] = static_cast<float *>(p);
+    }
+    *ptr = g_scratch_ptr[dev];
+    return (int)hipSuccess;
+}
 
 int launch_dense_rotate(const void *X, int x_bf16, int64_t T, int K, const float *R, float *U,
                         void *stream) {

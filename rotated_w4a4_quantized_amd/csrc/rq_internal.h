@@ -44,6 +44,11 @@ int launch_rpbh_lloydmax(const void *X, int x_bf16, int64_t T, int K, int block,
                          int n_thresholds, uint8_t *codes, float *sigma, void *stream);
 int launch_dense_rotate(const void *X, int x_bf16, int64_t T, int K, const float *R,
                         float *U, void *stream);
+// Largest fp32 staging of rq_rotate_quant_noalloc (T * K * 4 bytes, DENSE).
+constexpr size_t kDenseScratchBytes = size_t(64) << 20;
+// The calling thread's current device's copy of that scratch (looked up once
+// per device with hipGetSymbolAddress); returns a hipError_t as int.
+int dense_scratch(float **ptr);
 int launch_dense_quant(const float *U, int64_t T, int K, int r, uint8_t *codes,
                        float *scale, uint16_t *top, void *stream);
 int launch_gemm_w4a4(const uint8_t *codes, const float *scale, const uint16_t *top,

@@ -65,7 +65,8 @@ assert ctypes.sizeof(c_weight_header) == 256
 # every symbol include/rq.h declares
 EXPORTS = ("rq_version", "rq_last_error", "rq_lloydmax_gaussian", "rq_packed_weight_bytes",
            "rq_pack_weights", "rq_rotate_quant_workspace_bytes", "rq_codes_mma_bytes",
-           "rq_rotate_quant", "rq_w4a4_linear", "rq_w4a4_linear_engine")
+           "rq_rotate_quant", "rq_w4a4_linear", "rq_w4a4_linear_engine",
+           "rq_rotate_quant_noalloc")
 
 _lib = None
 
@@ -91,9 +92,10 @@ def load() -> ctypes.CDLL:
     L.rq_rotate_quant.argtypes = [P, P, P, I32, I64, P, P, P, P, P, SZ, P]
     L.rq_w4a4_linear.argtypes = [P, P, P, P, P, P, I64, P, P, I32, P]
     L.rq_w4a4_linear_engine.argtypes = [P, P, P, P, P, P, I64, P, P, I32, I32, P]
+    L.rq_rotate_quant_noalloc.argtypes = [P, P, P, I32, I64, P, P, P, P, P]
     for name in ("rq_lloydmax_gaussian", "rq_packed_weight_bytes", "rq_pack_weights",
                  "rq_rotate_quant_workspace_bytes", "rq_codes_mma_bytes", "rq_rotate_quant",
-                 "rq_w4a4_linear", "rq_w4a4_linear_engine"):
+                 "rq_w4a4_linear", "rq_w4a4_linear_engine", "rq_rotate_quant_noalloc"):
         getattr(L, name).restype = I32
     _lib = L
     return L
@@ -343,6 +345,17 @@ def rotate_quant(drot: DeviceRotation, q: Quant, X, codes, scale, top=None, work
     _check(load().rq_rotate_quant(ctypes.byref(cr), ctypes.byref(cq), _t_ptr(X), dtype_code(X), T,
                                   _t_ptr(codes), _t_ptr(scale), _t_ptr(top), _t_ptr(codes_mma),
                                   _t_ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def rotate_quant_noalloc(drot: DeviceRotation, q: Quant, X, codes, scale, top=None, stream=None,
+                         codes_mma=None):
+    """rq_rotate_quant_noalloc: rotate_quant without a workspace (the library's
+    per-device scratch serves DENSE)."""
+    cr, cq = drot.c_dev(), q.c()
+    T = int(X.shape[0])
+    _check(load().rq_rotate_quant_noalloc(ctypes.byref(cr), ctypes.byref(cq), _t_ptr(X),
+                                          dtype_code(X), T, _t_ptr(codes), _t_ptr(scale),
+                                          _t_ptr(top), _t_ptr(codes_mma), _stream(stream)))
 
 
 def w4a4_linear(dw: DeviceWeights, codes, scale, Y, top=None, bias=None, T=None, stream=None,
