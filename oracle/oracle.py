@@ -80,16 +80,46 @@ def _declare(L):
     L.orc_norm2_grid.restype = ctypes.c_double
     L.orc_quant_lloydmax_row.argtypes = [_P, _I, _P, _I, _P, _P]
     L.orc_quant_lloydmax_wrow.argtypes = [_P, _I, _P, _I, _P, _P]
-    L.orc_act_rows.argtypes = [_P, _I, _I, _P, _I64, _I, _I, _P, _P, _P, _I, _I,
-                               _P, _I, _P, _P, _P, _P, _P]
-    L.orc_weight_rows.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _I, _P,
-                                  _P, _P]
+    L.orc_quant_sym_row.argtypes = [_P, _I, _I, _I, _P, _P]
+    L.orc_quant_asym_row.argtypes = [_P, _I, _I, _P, _P, _P]
+    L.orc_quant_sym_wrow.argtypes = [_P, _I, _I, _P, _P]
+    L.orc_e2m1_value.argtypes = [_I]
+    L.orc_e2m1_value.restype = ctypes.c_double
+    L.orc_e2m1_encode.argtypes = [ctypes.c_double]
+    L.orc_e2m1_encode.restype = _I
+    L.orc_mx_scale_code.argtypes = [ctypes.c_double]
+    L.orc_mx_scale_code.restype = _I
+    L.orc_quant_mxfp4_f64.argtypes = [_P, _I, _P, _P]
+    L.orc_quant_mxfp4_row.argtypes = [_P, _I, _P, _P]
+    L.orc_trdq_row_f32.argtypes = [_P, _I, _I, _P, _P, _P, _P, _P]
+    L.orc_trdq_row_f64.argtypes = [_P, _I, _I, _P, _P, _P, _P, _P]
+    L.orc_act_rows.argtypes = [_P, _I, _I, _P, _I64, _P, _I, _I, _I, _P, _I,
+                               _P, _P, _P, _P, _P, _P]
+    L.orc_weight_rows.argtypes = [_P, _I, _I, _P, _I, _I, _P, _I, _P, _P, _P, _P]
+    L.orc_gemm_codes_pairs.argtypes = [_P, _I, _I, _I, _P, _I, _I, _I, _P, _P, _I64, _P]
+    L.orc_mx_dot_pairs.argtypes = [_P, _P, _P, _P, _I, _P, _P, _I64, _P]
     L.orc_int_gemm_pairs.argtypes = [_P, _I, _P, _I, _I, _P, _P, _I64, _P]
     L.orc_asym_gemm_pairs.argtypes = [_P, _I, _P, _P, _P, _I64, _P]
     L.orc_int_gemm.argtypes = [_P, _I, _I, _P, _I, _I, _I, _P]
     L.orc_lowrank_pairs.argtypes = [_P, _I, _P, _I, _P, _P, _I64, _P]
     L.orc_codebook_dot_pairs.argtypes = [_P, _P, _I, _I, _P, _P, _P, _P, _I64, _P]
     L.orc_num_threads.restype = _I
+
+
+class _Rot(ctypes.Structure):
+    """orc_rot: the rotation the row drivers apply."""
+    _fields_ = [("kind", ctypes.c_int), ("b", ctypes.c_int), ("sign", _P), ("perm", _P),
+                ("R", _P), ("m", _P), ("R2", _P)]
+
+
+def _rot(rot_kind, b=0, sign=None, perm=None, R=None, m=None, R2=None):
+    """A _Rot plus the contiguous arrays it points into (kept alive by the caller)."""
+    keep = [None if sign is None else np.ascontiguousarray(sign, np.int8),
+            None if perm is None else np.ascontiguousarray(perm, np.int32),
+            None if R is None else np.ascontiguousarray(R, np.float32),
+            None if m is None else np.ascontiguousarray(m, np.float32),
+            None if R2 is None else np.ascontiguousarray(R2, np.float32)]
+    return _Rot(rot_kind, b, *(_ptr(a) for a in keep)), keep
 
 
 def _ptr(a):
@@ -163,6 +193,79 @@ def quant_int4_wrow(v):
     s = np.zeros(1, np.float32)
     lib().orc_quant_int4_wrow(_ptr(v), v.size, _ptr(q), _ptr(s))
     return q, np.float32(s[0])
+
+
+def quant_sym_row(u, r=0, qmax=7):
+    """Symmetric per-token quantizer with qmax 7 (INT4) or 127 (INT8)."""
+    u = np.ascontiguousarray(u, np.float32)
+    q = np.zeros(u.size - r, np.int16)
+    s = ctypes.c_float(0)
+    lib().orc_quant_sym_row(_ptr(u), u.size, r, qmax, _ptr(q), ctypes.byref(s))
+    return q, s.value
+
+
+def quant_asym_row(u, levels=15):
+    """Asymmetric per-token quantizer with 15 (4-bit) or 255 (8-bit) levels."""
+    u = np.ascontiguousarray(u, np.float32)
+    q = np.zeros(u.size, np.uint16)
+    s, z = ctypes.c_float(0), ctypes.c_float(0)
+    lib().orc_quant_asym_row(_ptr(u), u.size, levels, _ptr(q), ctypes.byref(s), ctypes.byref(z))
+    return q, s.value, z.value
+
+
+def quant_sym_wrow(v, qmax=7):
+    v = np.ascontiguousarray(v, np.float64)
+    q = np.zeros(v.size, np.int16)
+    s = ctypes.c_float(0)
+    lib().orc_quant_sym_wrow(_ptr(v), v.size, qmax, _ptr(q), ctypes.byref(s))
+    return q, s.value
+
+
+def e2m1_value(code: int) -> float:
+    return lib().orc_e2m1_value(int(code))
+
+
+def e2m1_encode(x: float) -> int:
+    return lib().orc_e2m1_encode(float(x))
+
+
+def mx_scale_code(amax: float) -> int:
+    return lib().orc_mx_scale_code(float(amax))
+
+
+def quant_mxfp4_row(u):
+    """MXFP4 of an fp32 row: (codes [K/2] nibbles, E8M0 scale codes [K/32])."""
+    u = np.ascontiguousarray(u, np.float32)
+    codes = np.zeros(u.size // 2, np.uint8)
+    sc = np.zeros(u.size // 32, np.uint8)
+    lib().orc_quant_mxfp4_row(_ptr(u), u.size, _ptr(codes), _ptr(sc))
+    return codes, sc
+
+
+def quant_mxfp4_f64(x):
+    x = np.ascontiguousarray(x, np.float64)
+    codes = np.zeros(x.size // 2, np.uint8)
+    sc = np.zeros(x.size // 32, np.uint8)
+    lib().orc_quant_mxfp4_f64(_ptr(x), x.size, _ptr(codes), _ptr(sc))
+    return codes, sc
+
+
+def trdq_row_f32(x, b, m, R1, perm, R2):
+    x = np.ascontiguousarray(x, np.float32)
+    u = np.empty_like(x)
+    keep = [np.ascontiguousarray(a, t) for a, t in ((m, np.float32), (R1, np.float32),
+                                                     (perm, np.int32), (R2, np.float32))]
+    lib().orc_trdq_row_f32(_ptr(x), x.size, b, *(_ptr(a) for a in keep), _ptr(u))
+    return u
+
+
+def trdq_row_f64(w, b, m, R1, perm, R2):
+    w = np.ascontiguousarray(w, np.float64)
+    v = np.empty_like(w)
+    keep = [np.ascontiguousarray(a, t) for a, t in ((m, np.float32), (R1, np.float32),
+                                                     (perm, np.int32), (R2, np.float32))]
+    lib().orc_trdq_row_f64(_ptr(w), w.size, b, *(_ptr(a) for a in keep), _ptr(v))
+    return v
 
 
 def pack_nibbles(q):
@@ -292,50 +395,61 @@ def codebook_bf16(L: int) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def act_rows(X, xdtype, K, rows, *, rot_kind, b=0, sign=None, perm=None, R=None,
-             r=0, q_kind=0, levels=None, want_u=False):
+             m=None, R2=None, r=0, q_kind=0, a_bits=4, levels=None, want_u=False):
     """Activation side for the listed rows of X (see orc_act_rows).
 
     X: np.float32 [T][K] (xdtype 0) or np.uint16 bf16 bits [T][K] (xdtype 1).
-    q_kind 2 (asymmetric INT4, r = 0) also returns the zero points.
-    Returns dict(codes, scale, zero, top, u)."""
+    rot_kind 0 RPBH (b, sign, perm), 1 dense (R, r), 2 TR-DQ (b, m, R = the
+    first block rotation, perm, R2).  q_kind 0 symmetric integer, 1
+    Lloyd-Max, 2 asymmetric integer (also returns the zero points), 3 MXFP4
+    (also returns the E8M0 block scales); a_bits 4 or 8 for the integer kinds.
+    Returns dict(codes, scale, zero, top, u, mx_scales)."""
     rows = np.ascontiguousarray(rows, np.int64)
     n = rows.size
     X = np.ascontiguousarray(X)
     Kq = K - r
-    ncode = (Kq // 2) if q_kind == 0 else (K // 2)
+    if q_kind in (1, 3):
+        ncode = K // 2
+    else:
+        ncode = Kq * a_bits // 8
     codes = np.zeros((n, ncode), np.uint8)
     scale = np.zeros(n, np.float32)
     zero = np.zeros(n, np.float32) if q_kind == 2 else None
     top = np.zeros((n, r), np.uint16) if r > 0 else None
+    mx = np.zeros((n, K // 32), np.uint8) if q_kind == 3 else None
     u = np.zeros((n, K), np.float32) if want_u else None
     lv = None if levels is None else np.ascontiguousarray(levels, np.float32)
-    lib().orc_act_rows(_ptr(X), xdtype, K, _ptr(rows), n, rot_kind, b,
-                       _ptr(None if sign is None else np.ascontiguousarray(sign, np.int8)),
-                       _ptr(None if perm is None else np.ascontiguousarray(perm, np.int32)),
-                       _ptr(None if R is None else np.ascontiguousarray(R, np.float32)),
-                       r, q_kind, _ptr(lv), 0 if lv is None else lv.size,
-                       _ptr(codes), _ptr(scale), _ptr(zero), _ptr(top), _ptr(u))
-    return dict(codes=codes, scale=scale, zero=zero, top=top, u=u)
+    rot, keep = _rot(rot_kind, b, sign, perm, R, m, R2)
+    lib().orc_act_rows(_ptr(X), xdtype, K, _ptr(rows), n, ctypes.byref(rot), r, q_kind, a_bits,
+                       _ptr(lv), 0 if lv is None else lv.size, _ptr(codes), _ptr(scale),
+                       _ptr(zero), _ptr(top), _ptr(mx), _ptr(u))
+    del keep
+    return dict(codes=codes, scale=scale, zero=zero, top=top, u=u, mx_scales=mx)
 
 
-def weight_rows(W, *, rot_kind, b=0, sign=None, perm=None, R=None, q_kind=0, levels=None):
+def weight_rows(W, *, rot_kind, b=0, sign=None, perm=None, R=None, m=None, R2=None, q_kind=0,
+                w_bits=4, levels=None):
     """Offline weight side: fold every row of W [N][K] (fp32) in fp64 and
-    quantize (see orc_weight_rows).  Returns dict(codes, scale, q)."""
+    quantize (see orc_weight_rows).  Returns dict(codes, scale, q, mx_scales)."""
     W = np.ascontiguousarray(W, np.float32)
     N, K = W.shape
-    # INT4 and 16-level codebooks: nibbles; 4-level codebooks: crumbs
-    ncode = K // 2 if (q_kind == 0 or (levels is not None and len(levels) == 16)) else K // 4
+    if q_kind == 1:
+        # 16-level codebooks: nibbles; 4-level codebooks: crumbs
+        ncode = K // 2 if len(levels) == 16 else K // 4
+    elif q_kind == 3:
+        ncode = K // 2
+    else:
+        ncode = K * w_bits // 8
     codes = np.zeros((N, ncode), np.uint8)
     scale = np.zeros(N, np.float32)
-    q = np.zeros((N, K), np.int8)
+    mx = np.zeros((N, K // 32), np.uint8) if q_kind == 3 else None
+    q = np.zeros((N, K), np.int16)
     lv = None if levels is None else np.ascontiguousarray(levels, np.float32)
-    lib().orc_weight_rows(_ptr(W), N, K, rot_kind, b,
-                          _ptr(None if sign is None else np.ascontiguousarray(sign, np.int8)),
-                          _ptr(None if perm is None else np.ascontiguousarray(perm, np.int32)),
-                          _ptr(None if R is None else np.ascontiguousarray(R, np.float32)),
-                          q_kind, _ptr(lv), 0 if lv is None else lv.size,
-                          _ptr(codes), _ptr(scale), _ptr(q))
-    return dict(codes=codes, scale=scale, q=q)
+    rot, keep = _rot(rot_kind, b, sign, perm, R, m, R2)
+    lib().orc_weight_rows(_ptr(W), N, K, ctypes.byref(rot), q_kind, w_bits, _ptr(lv),
+                          0 if lv is None else lv.size, _ptr(codes), _ptr(scale), _ptr(mx), _ptr(q))
+    del keep
+    return dict(codes=codes, scale=scale, q=q, mx_scales=mx)
 
 
 def int_gemm(codes_a, Kq, codes_w, Kw, koff=0):
@@ -367,6 +481,31 @@ def asym_gemm_pairs(codes_a, codes_w, K, ta, nw):
                               _ptr(np.ascontiguousarray(codes_w, np.uint8)),
                               _ptr(ta), _ptr(nw), ta.size, _ptr(acc))
     return acc
+
+
+def gemm_codes_pairs(codes_a, a_bits, a_signed, Kq, codes_w, w_bits, Kw, ta, nw, koff=0):
+    """acc[p] = sum_k a[t_p][k] w[n_p][koff + k] for 4- or 8-bit codes, int64."""
+    ta = np.ascontiguousarray(ta, np.int64)
+    nw = np.ascontiguousarray(nw, np.int64)
+    acc = np.zeros(ta.size, np.int64)
+    lib().orc_gemm_codes_pairs(_ptr(np.ascontiguousarray(codes_a, np.uint8)), a_bits,
+                               1 if a_signed else 0, Kq,
+                               _ptr(np.ascontiguousarray(codes_w, np.uint8)), w_bits, Kw, koff,
+                               _ptr(ta), _ptr(nw), ta.size, _ptr(acc))
+    return acc
+
+
+def mx_dot_pairs(codes_a, sc_a, codes_w, sc_w, K, ta, nw):
+    """fp64 MXFP4 dot products for listed pairs (see orc_mx_dot_pairs)."""
+    ta = np.ascontiguousarray(ta, np.int64)
+    nw = np.ascontiguousarray(nw, np.int64)
+    dot = np.zeros(ta.size, np.float64)
+    lib().orc_mx_dot_pairs(_ptr(np.ascontiguousarray(codes_a, np.uint8)),
+                           _ptr(np.ascontiguousarray(sc_a, np.uint8)),
+                           _ptr(np.ascontiguousarray(codes_w, np.uint8)),
+                           _ptr(np.ascontiguousarray(sc_w, np.uint8)), K,
+                           _ptr(ta), _ptr(nw), ta.size, _ptr(dot))
+    return dot
 
 
 def lowrank_pairs(top, r, codes_w, Kw, ta, nw):
@@ -417,3 +556,9 @@ def yhat_codebook(sigma, tau, dot, b):
     """fp64 output of the Lloyd-Max path: sigma tau / b * codebook dot."""
     return (np.asarray(sigma, np.float64) * np.asarray(tau, np.float64) *
             np.asarray(dot, np.float64) / float(b))
+
+
+def yhat_mx(dot, b):
+    """fp64 output of the MXFP4 path: the block-scaled dot product / b (the
+    unnormalized block Hadamard scales dot products by b)."""
+    return np.asarray(dot, np.float64) / float(b)

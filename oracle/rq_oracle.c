@@ -164,7 +164,28 @@ void orc_dense_row_f64(const double *w, const float *R, int K, double *v)
  *              q[j] = clamp(rne(fl32(u[j] * inv)), -7, 7)
  * q has K - r entries.
  */
+void orc_quant_sym_row(const float *u, int K, int r, int qmax, int16_t *q, float *s_out);
+
 void orc_quant_int4_row(const float *u, int K, int r, int8_t *q, float *s_out)
+{
+    int16_t *w = (int16_t *)malloc((size_t)(K - r) * sizeof(int16_t));
+    orc_quant_sym_row(u, K, r, 7, w, s_out);
+    for (int j = 0; j < K - r; j++)
+        q[j] = (int8_t)w[j];
+    free(w);
+}
+
+/*
+ * Per-token symmetric b-bit quantizer of a rotated row, qmax = 2^(b-1) - 1
+ * (7 for INT4, 127 for INT8 -- TR-DQ's W8A8 / W4A8 settings), over the
+ * coordinates u[r..K-1]:
+ *   amax = max |u[j]|
+ *   amax == 0  ->  all codes 0, scale 0
+ *   else       s = fl32(amax / qmax), inv = fl32(qmax / amax)  (correctly rounded)
+ *              q[j] = clamp(rne(fl32(u[j] * inv)), -qmax, qmax)
+ * q has K - r entries.
+ */
+void orc_quant_sym_row(const float *u, int K, int r, int qmax, int16_t *q, float *s_out)
 {
     float amax = 0.0f;
     for (int j = r; j < K; j++) {
@@ -178,36 +199,55 @@ void orc_quant_int4_row(const float *u, int K, int r, int8_t *q, float *s_out)
         *s_out = 0.0f;
         return;
     }
-    float s = amax / 7.0f;
-    float inv = 7.0f / amax;
+    float fq = (float)qmax;
+    float s = amax / fq;
+    float inv = fq / amax;
     for (int j = r; j < K; j++) {
         float m = u[j] * inv;
         float t = rintf(m);
-        if (t > 7.0f) t = 7.0f;
-        if (t < -7.0f) t = -7.0f;
-        q[j - r] = (int8_t)t;
+        if (t > fq) t = fq;
+        if (t < -fq) t = -fq;
+        q[j - r] = (int16_t)t;
     }
     *s_out = s;
 }
 
+void orc_quant_asym_row(const float *u, int K, int levels, uint16_t *q, float *s_out,
+                        float *z_out);
+
 /*
  * Per-token asymmetric INT4 of a rotated row ([TRDQ] section 3.1: Eq.(1)
  * X_int = clamp(round(X / s) + z, 0, 2^b - 1), Eq.(2) s = (max X - min X) /
- * (2^b - 1), Eq.(3) the zero point z), b = 4, over all K coordinates.
- * Readings where the pages are open or garbled:
+ * (2^b - 1), Eq.(3) the zero point z), b = 4, over all K coordinates; the
+ * general b-bit form is orc_quant_asym_row below.
+ */
+void orc_quant_int4_asym_row(const float *u, int K, uint8_t *q, float *s_out, float *z_out)
+{
+    uint16_t *w = (uint16_t *)malloc((size_t)K * sizeof(uint16_t));
+    orc_quant_asym_row(u, K, 15, w, s_out, z_out);
+    for (int j = 0; j < K; j++)
+        q[j] = (uint8_t)w[j];
+    free(w);
+}
+
+/*
+ * Per-token asymmetric b-bit quantizer, levels = 2^b - 1 (15 or 255), over
+ * all K coordinates ([TRDQ] Eq.(1)-(3)).  Readings where the pages are open
+ * or garbled:
  *   - Eq.(3) prints z = round(min X / s); with Eq.(1)'s "+ z" the minimum
  *     must land on code 0, so z = -round(min X / s);
- *   - z is kept in [0, 15] (it already is whenever min <= 0 <= max);
+ *   - z is kept in [0, levels] (it already is whenever min <= 0 <= max);
  *   - one fp32 rounding per operation, the division by s taken as a
  *     multiplication by its reciprocal computed directly:
  *       lo = min u, hi = max u, d = fl32(hi - lo)
  *       d == 0  ->  all codes 0, s = 0, z = 0
- *       else    s = fl32(d / 15), inv = fl32(15 / d)
- *               z = clamp(-rne(fl32(lo * inv)), 0, 15)
- *               q[j] = clamp(rne(fl32(u[j] * inv)) + z, 0, 15)
- * Codes are unsigned, 0..15.
+ *       else    s = fl32(d / levels), inv = fl32(levels / d)
+ *               z = clamp(-rne(fl32(lo * inv)), 0, levels)   (an integer, +0 for zero)
+ *               q[j] = clamp(rne(fl32(u[j] * inv)) + z, 0, levels)
+ * Codes are unsigned, 0..levels.
  */
-void orc_quant_int4_asym_row(const float *u, int K, uint8_t *q, float *s_out, float *z_out)
+void orc_quant_asym_row(const float *u, int K, int levels, uint16_t *q, float *s_out,
+                        float *z_out)
 {
     float lo = u[0], hi = u[0];
     for (int j = 1; j < K; j++) {
@@ -222,27 +262,29 @@ void orc_quant_int4_asym_row(const float *u, int K, uint8_t *q, float *s_out, fl
         *z_out = 0.0f;
         return;
     }
-    float s = d / 15.0f;
-    float inv = 15.0f / d;
+    float fl = (float)levels;
+    float s = d / fl;
+    float inv = fl / d;
     float zl = lo * inv;
     float zr = rintf(zl);
-    int zi = zr > 0.0f ? 0 : (zr < -15.0f ? 15 : -(int)zr);
-    float z = (float)zi;        /* an integer in [0, 15]; +0 for zero */
+    int zi = zr > 0.0f ? 0 : (zr < -fl ? levels : -(int)zr);
+    float z = (float)zi;        /* an integer in [0, levels]; +0 for zero */
     for (int j = 0; j < K; j++) {
         float m = u[j] * inv;
         float t = rintf(m) + z;   /* integers below 2^24: exact */
         if (t < 0.0f) t = 0.0f;
-        if (t > 15.0f) t = 15.0f;
-        q[j] = (uint8_t)t;
+        if (t > fl) t = fl;
+        q[j] = (uint16_t)t;
     }
     *s_out = s;
     *z_out = z;
 }
 
-/* Per-output-channel symmetric INT4 of a folded fp64 weight row (all K).
+/* Per-output-channel symmetric b-bit quantizer of a folded fp64 weight row
+ * (all K), qmax = 7 (INT4) or 127 (INT8):
  *   amax == 0 -> codes 0, scale 0
- *   s_w = (float)(amax / 7), inv = 7 / amax (fp64), q = clamp(rne(v*inv)). */
-void orc_quant_int4_wrow(const double *v, int K, int8_t *q, float *s_out)
+ *   s_w = (float)(amax / qmax), inv = qmax / amax (fp64), q = clamp(rne(v*inv)). */
+void orc_quant_sym_wrow(const double *v, int K, int qmax, int16_t *q, float *s_out)
 {
     double amax = 0.0;
     for (int j = 0; j < K; j++) {
@@ -256,14 +298,196 @@ void orc_quant_int4_wrow(const double *v, int K, int8_t *q, float *s_out)
         *s_out = 0.0f;
         return;
     }
-    double inv = 7.0 / amax;
+    double dq = (double)qmax;
+    double inv = dq / amax;
     for (int j = 0; j < K; j++) {
         double t = rint(v[j] * inv);
-        if (t > 7.0) t = 7.0;
-        if (t < -7.0) t = -7.0;
-        q[j] = (int8_t)t;
+        if (t > dq) t = dq;
+        if (t < -dq) t = -dq;
+        q[j] = (int16_t)t;
     }
-    *s_out = (float)(amax / 7.0);
+    *s_out = (float)(amax / dq);
+}
+
+void orc_quant_int4_wrow(const double *v, int K, int8_t *q, float *s_out)
+{
+    int16_t *w = (int16_t *)malloc((size_t)K * sizeof(int16_t));
+    orc_quant_sym_wrow(v, K, 7, w, s_out);
+    for (int j = 0; j < K; j++)
+        q[j] = (int8_t)w[j];
+    free(w);
+}
+
+/* ------------------------------------------------------------------ */
+/* MXFP4: E2M1 elements with one E8M0 scale per 32 coordinates          */
+/* ------------------------------------------------------------------ */
+
+/*
+ * The FP4 format variant ("DiRotQ" abstract, later version: the same method
+ * run with NVFP4 on a Blackwell GPU).  The pages name the format and define
+ * nothing more; the reading here is the OCP Microscaling (MX) v1.0 MXFP4
+ * format, the one gfx950's scaled matrix cores take:
+ *   element  E2M1: sign, 2 exponent bits (bias 1), 1 mantissa bit;
+ *            magnitudes by 3-bit code 0..7: 0, 0.5, 1, 1.5, 2, 3, 4, 6
+ *            (code 1 is the subnormal 0.5); the sign is bit 3
+ *   block    32 consecutive coordinates share an E8M0 scale 2^e
+ *            (code e + 127, e in [-127, 127])
+ *   scale    e = floor(log2(max |x| of the block)) - 2  (2 = the exponent of
+ *            E2M1's largest value), clamped to [-127, 127]; a block of
+ *            zeros takes e = -127
+ *   element  nearest E2M1 value to x / 2^e, ties to the even code (mantissa
+ *            bit 0), magnitudes above 6 saturate to 6; a zero is code 0
+ *            (positive) whatever the sign of x
+ * The value of a block element is e2m1(code) * 2^e.
+ */
+static const double orc_e2m1_mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double orc_e2m1_value(int code)
+{
+    double m = orc_e2m1_mag[code & 7];
+    return (code & 8) ? -m : m;
+}
+
+/* Nearest E2M1 code to x (brute force over the eight magnitudes). */
+int orc_e2m1_encode(double x)
+{
+    double a = fabs(x);
+    int best = 0;
+    double bd = a;
+    for (int c = 1; c < 8; c++) {
+        double d = fabs(a - orc_e2m1_mag[c]);
+        if (d < bd || (d == bd && (c & 1) == 0)) {
+            best = c;
+            bd = d;
+        }
+    }
+    if (best == 0)
+        return 0;
+    return (x < 0.0 ? 8 : 0) | best;
+}
+
+/* E8M0 code of the scale of a block whose largest magnitude is amax. */
+int orc_mx_scale_code(double amax)
+{
+    if (amax == 0.0)
+        return 0;
+    int e = ilogb(amax) - 2;
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e + 127;
+}
+
+/* MXFP4 of a vector of K coordinates (K % 32 == 0), given in fp64 (the
+ * fp32 activations convert exactly): codes [K/2] nibbles (low nibble = even
+ * coordinate), scales [K/32] E8M0 codes.  x / 2^e is exact in fp64. */
+void orc_quant_mxfp4_f64(const double *x, int K, uint8_t *codes, uint8_t *scales)
+{
+    for (int c = 0; c < K / 32; c++) {
+        double amax = 0.0;
+        for (int j = 32 * c; j < 32 * c + 32; j++)
+            if (fabs(x[j]) > amax)
+                amax = fabs(x[j]);
+        int sc = orc_mx_scale_code(amax);
+        scales[c] = (uint8_t)sc;
+        for (int j = 32 * c; j < 32 * c + 32; j += 2) {
+            int lo = orc_e2m1_encode(ldexp(x[j], 127 - sc));
+            int hi = orc_e2m1_encode(ldexp(x[j + 1], 127 - sc));
+            codes[j / 2] = (uint8_t)(lo | (hi << 4));
+        }
+    }
+}
+
+void orc_quant_mxfp4_row(const float *u, int K, uint8_t *codes, uint8_t *scales)
+{
+    double *x = (double *)malloc((size_t)K * sizeof(double));
+    for (int j = 0; j < K; j++)
+        x[j] = (double)u[j];
+    orc_quant_mxfp4_f64(x, K, codes, scales);
+    free(x);
+}
+
+/* ------------------------------------------------------------------ */
+/* TR-DQ runtime rotation: smoothing, block rotation, zigzag            */
+/* permutation, block rotation                                          */
+/* ------------------------------------------------------------------ */
+
+/*
+ * [TRDQ] Eq.(9)-(10): G(X) = (X . Delta) R1 P R2, with Delta a per-channel
+ * scale (Eq.(4)-(5), SmoothQuant's migration), R1 and R2 block-diagonal
+ * rotations (Eq.(8): b x b blocks) and P the zigzag permutation.  Readings:
+ *   - m[K] is the per-channel multiplier the activations receive (Eq.(9)'s
+ *     Delta; Eq.(4) writes the same migration as X diag(Delta)^-1), the
+ *     weights receive its inverse;
+ *   - R1, R2 are [K/b][b][b], block c mapping coordinates cb..cb+b-1 to
+ *     themselves: z[cb + j] = sum_i y[cb + i] R1[c][i][j];
+ *   - P as a gather: p[j] = z[perm[j]] (the same convention as RPBH's);
+ *   - arithmetic as the dense path's: one fp32 multiply per smoothed
+ *     coordinate, then per output one fp32 fused multiply-add chain over i
+ *     ascending from +0, for each of the two block rotations.
+ */
+void orc_trdq_row_f32(const float *x, int K, int b, const float *m, const float *R1,
+                      const int32_t *perm, const float *R2, float *u)
+{
+    float *y = (float *)malloc((size_t)K * sizeof(float));
+    float *z = (float *)malloc((size_t)K * sizeof(float));
+    for (int j = 0; j < K; j++)
+        y[j] = x[j] * m[j];
+    for (int c = 0; c < K / b; c++) {
+        const float *Rc = R1 + (size_t)c * b * b;
+        for (int j = 0; j < b; j++) {
+            float acc = 0.0f;
+            for (int i = 0; i < b; i++)
+                acc = fmaf(y[c * b + i], Rc[(size_t)i * b + j], acc);
+            z[c * b + j] = acc;
+        }
+    }
+    for (int j = 0; j < K; j++)
+        y[j] = z[perm[j]];
+    for (int c = 0; c < K / b; c++) {
+        const float *Rc = R2 + (size_t)c * b * b;
+        for (int j = 0; j < b; j++) {
+            float acc = 0.0f;
+            for (int i = 0; i < b; i++)
+                acc = fmaf(y[c * b + i], Rc[(size_t)i * b + j], acc);
+            u[c * b + j] = acc;
+        }
+    }
+    free(y);
+    free(z);
+}
+
+/* The weight fold of [TRDQ] Eq.(9)-(10), H(W) = R2^T P^T R1^T Delta^-1 W:
+ * with W stored [N][K], row w becomes ((w / m) R1) P R2, in fp64 (division
+ * correctly rounded, fp64 fma chains over i ascending). */
+void orc_trdq_row_f64(const double *w, int K, int b, const float *m, const float *R1,
+                      const int32_t *perm, const float *R2, double *v)
+{
+    double *y = (double *)malloc((size_t)K * sizeof(double));
+    double *z = (double *)malloc((size_t)K * sizeof(double));
+    for (int j = 0; j < K; j++)
+        y[j] = w[j] / (double)m[j];
+    for (int c = 0; c < K / b; c++) {
+        const float *Rc = R1 + (size_t)c * b * b;
+        for (int j = 0; j < b; j++) {
+            double acc = 0.0;
+            for (int i = 0; i < b; i++)
+                acc = fma(y[c * b + i], (double)Rc[(size_t)i * b + j], acc);
+            z[c * b + j] = acc;
+        }
+    }
+    for (int j = 0; j < K; j++)
+        y[j] = z[perm[j]];
+    for (int c = 0; c < K / b; c++) {
+        const float *Rc = R2 + (size_t)c * b * b;
+        for (int j = 0; j < b; j++) {
+            double acc = 0.0;
+            for (int i = 0; i < b; i++)
+                acc = fma(y[c * b + i], (double)Rc[(size_t)i * b + j], acc);
+            v[c * b + j] = acc;
+        }
+    }
+    free(y);
+    free(z);
 }
 
 /* Two 4-bit two's-complement codes per byte, low nibble = even index. */
@@ -402,105 +626,161 @@ static void widen_row(const void *X, int xdtype, size_t row, int K, float *out)
     }
 }
 
+/* A rotation as the row drivers take it. */
+typedef struct {
+    int kind;             /* 0: RPBH, 1: dense, 2: TR-DQ */
+    int b;                /* RPBH / TR-DQ block */
+    const int8_t *sign;   /* RPBH signs [K] */
+    const int32_t *perm;  /* RPBH / TR-DQ permutation [K] */
+    const float *R;       /* dense basis [K][K]; TR-DQ first block rotation [K/b][b][b] */
+    const float *m;       /* TR-DQ per-channel multiplier [K] */
+    const float *R2;      /* TR-DQ second block rotation [K/b][b][b] */
+} orc_rot;
+
+static void rotate_row_f32(const orc_rot *rot, const float *x, int K, float *u)
+{
+    if (rot->kind == 0)
+        orc_rpbh_row_f32(x, K, rot->b, rot->sign, rot->perm, u);
+    else if (rot->kind == 1)
+        orc_dense_row_f32(x, rot->R, K, u);
+    else
+        orc_trdq_row_f32(x, K, rot->b, rot->m, rot->R, rot->perm, rot->R2, u);
+}
+
+static void rotate_row_f64(const orc_rot *rot, const double *w, int K, double *v)
+{
+    if (rot->kind == 0)
+        orc_rpbh_row_f64(w, K, rot->b, rot->sign, rot->perm, v);
+    else if (rot->kind == 1)
+        orc_dense_row_f64(w, rot->R, K, v);
+    else
+        orc_trdq_row_f64(w, K, rot->b, rot->m, rot->R, rot->perm, rot->R2, v);
+}
+
 /*
  * Activation side of the layer for a list of rows.
- *   rot_kind 0: RPBH (b, sign, perm);  1: dense R with top-r bf16.
- *   q_kind   0: INT4 symmetric -> codes [nrows][(K-r)/2] nibbles, scale[nrows]
+ *   rot      the rotation (RPBH, dense R with top-r bf16, or TR-DQ)
+ *   q_kind   0: symmetric integer, a_bits 4 or 8 -> codes [nrows][K-r]
+ *               as nibbles (4) or int8 bytes (8), scale[nrows]
  *            1: Lloyd-Max (levels, L=16) -> codes [nrows][K/2] nibbles of the
  *               4-bit index, scale[nrows] = sigma
- *            2: INT4 asymmetric (r = 0) -> codes [nrows][K/2] unsigned
- *               nibbles, scale[nrows] = s, zero[nrows] = z
+ *            2: asymmetric integer, a_bits 4 or 8 (r = 0) -> unsigned nibbles
+ *               or bytes [nrows][K], scale[nrows] = s, zero[nrows] = z
+ *            3: MXFP4 (r = 0) -> codes [nrows][K/2] E2M1 nibbles,
+ *               mx_scales [nrows][K/32] E8M0 codes
  *   top: bf16 [nrows][r] (dense only), may be NULL when r == 0.
  *   u_out: optional fp32 [nrows][K] copy of the rotated rows.
- * rows: indices into X (nrows of them).
+ * rows: indices into X (nrows of them).  Codes pack low nibble = even index.
  */
-void orc_act_rows(const void *X, int xdtype, int K, const int64_t *rows,
-                  int64_t nrows, int rot_kind, int b, const int8_t *sign,
-                  const int32_t *perm, const float *R, int r, int q_kind,
-                  const float *levels, int L, uint8_t *codes, float *scale,
-                  float *zero, uint16_t *top, float *u_out)
+void orc_act_rows(const void *X, int xdtype, int K, const int64_t *rows, int64_t nrows,
+                  const orc_rot *rot, int r, int q_kind, int a_bits, const float *levels,
+                  int L, uint8_t *codes, float *scale, float *zero, uint16_t *top,
+                  uint8_t *mx_scales, float *u_out)
 {
     int Kq = K - r;
+    int row_bytes = q_kind == 3 || q_kind == 1 ? K / 2 : (Kq * a_bits) / 8;
 #pragma omp parallel
     {
         float *x = (float *)malloc((size_t)K * 4);
         float *u = (float *)malloc((size_t)K * 4);
-        int8_t *q = (int8_t *)malloc((size_t)K);
-        uint8_t *ix = (uint8_t *)malloc((size_t)K);
+        int16_t *q = (int16_t *)malloc((size_t)K * sizeof(int16_t));
+        uint16_t *ix = (uint16_t *)malloc((size_t)K * sizeof(uint16_t));
+        uint8_t *b8 = (uint8_t *)malloc((size_t)K);
 #pragma omp for schedule(static)
         for (int64_t i = 0; i < nrows; i++) {
+            uint8_t *crow = codes + (size_t)i * row_bytes;
             widen_row(X, xdtype, (size_t)rows[i], K, x);
-            if (rot_kind == 0)
-                orc_rpbh_row_f32(x, K, b, sign, perm, u);
-            else
-                orc_dense_row_f32(x, R, K, u);
+            rotate_row_f32(rot, x, K, u);
             if (u_out)
                 memcpy(u_out + (size_t)i * K, u, (size_t)K * 4);
             if (q_kind == 0) {
-                orc_quant_int4_row(u, K, r, q, &scale[i]);
-                orc_pack_nibbles(q, Kq, codes + (size_t)i * (Kq / 2));
+                orc_quant_sym_row(u, K, r, a_bits == 8 ? 127 : 7, q, &scale[i]);
+                if (a_bits == 8) {
+                    for (int j = 0; j < Kq; j++)
+                        crow[j] = (uint8_t)(int8_t)q[j];
+                } else {
+                    for (int j = 0; j < Kq; j++)
+                        b8[j] = (uint8_t)(int8_t)q[j];
+                    orc_pack_nibbles((const int8_t *)b8, Kq, crow);
+                }
                 for (int j = 0; j < r; j++)
                     top[(size_t)i * r + j] = orc_f32_to_bf16(u[j]);
             } else if (q_kind == 2) {
-                orc_quant_int4_asym_row(u, K, ix, &scale[i], &zero[i]);
-                for (int j = 0; j < K / 2; j++)
-                    codes[(size_t)i * (K / 2) + j] =
-                        (uint8_t)((ix[2 * j] & 0x0Fu) | ((ix[2 * j + 1] & 0x0Fu) << 4));
+                orc_quant_asym_row(u, K, a_bits == 8 ? 255 : 15, ix, &scale[i], &zero[i]);
+                if (a_bits == 8) {
+                    for (int j = 0; j < K; j++)
+                        crow[j] = (uint8_t)ix[j];
+                } else {
+                    for (int j = 0; j < K / 2; j++)
+                        crow[j] = (uint8_t)((ix[2 * j] & 0x0Fu) | ((ix[2 * j + 1] & 0x0Fu) << 4));
+                }
+            } else if (q_kind == 3) {
+                orc_quant_mxfp4_row(u, K, crow, mx_scales + (size_t)i * (K / 32));
             } else {
-                orc_quant_lloydmax_row(u, K, levels, L, ix, &scale[i]);
+                orc_quant_lloydmax_row(u, K, levels, L, b8, &scale[i]);
                 for (int j = 0; j < K / 2; j++)
-                    codes[(size_t)i * (K / 2) + j] =
-                        (uint8_t)((ix[2 * j] & 0x0Fu) | ((ix[2 * j + 1] & 0x0Fu) << 4));
+                    crow[j] = (uint8_t)((b8[2 * j] & 0x0Fu) | ((b8[2 * j + 1] & 0x0Fu) << 4));
             }
         }
-        free(x); free(u); free(q); free(ix);
+        free(x); free(u); free(q); free(ix); free(b8);
     }
 }
 
 /*
  * Weight side (offline): fold every row of W [N][K] (fp32) with the rotation
  * in fp64, then quantize.
- *   q_kind 0: INT4 symmetric over all K -> codes [N][K/2], scale s_w[N];
- *             qvals (optional) [N][K] int8 signed codes
+ *   q_kind 0, 2: symmetric integer over all K, w_bits 4 or 8 -> codes
+ *             [N][K/2] nibbles or [N][K] int8 bytes, scale s_w[N]; qvals
+ *             (optional) [N][K] signed codes
  *   q_kind 1: Lloyd-Max (levels, L = 4 or 16) -> codes [N][K/4] crumbs
  *             (L = 4) or [N][K/2] nibbles (L = 16), scale tau[N];
  *             qvals (optional) [N][K] indices
+ *   q_kind 3: MXFP4 -> codes [N][K/2] E2M1 nibbles, mx_scales [N][K/32];
+ *             qvals (optional) [N][K] E2M1 codes
  */
-void orc_weight_rows(const float *W, int N, int K, int rot_kind, int b,
-                     const int8_t *sign, const int32_t *perm, const float *R,
-                     int q_kind, const float *levels, int L, uint8_t *codes,
-                     float *scale, int8_t *qvals)
+void orc_weight_rows(const float *W, int N, int K, const orc_rot *rot, int q_kind, int w_bits,
+                     const float *levels, int L, uint8_t *codes, float *scale,
+                     uint8_t *mx_scales, int16_t *qvals)
 {
 #pragma omp parallel
     {
         double *w = (double *)malloc((size_t)K * 8);
         double *v = (double *)malloc((size_t)K * 8);
-        int8_t *q = (int8_t *)malloc((size_t)K);
-        uint8_t *ix = (uint8_t *)malloc((size_t)K);
+        int16_t *q = (int16_t *)malloc((size_t)K * sizeof(int16_t));
+        uint8_t *b8 = (uint8_t *)malloc((size_t)K);
 #pragma omp for schedule(static)
         for (int n = 0; n < N; n++) {
             for (int k = 0; k < K; k++)
                 w[k] = (double)W[(size_t)n * K + k];
-            if (rot_kind == 0)
-                orc_rpbh_row_f64(w, K, b, sign, perm, v);
-            else
-                orc_dense_row_f64(w, R, K, v);
-            if (q_kind == 0) {
-                orc_quant_int4_wrow(v, K, q, &scale[n]);
-                orc_pack_nibbles(q, K, codes + (size_t)n * (K / 2));
-                if (qvals)
-                    memcpy(qvals + (size_t)n * K, q, (size_t)K);
-            } else {
-                orc_quant_lloydmax_wrow(v, K, levels, L, ix, &scale[n]);
-                if (L == 16)
-                    orc_pack_nibbles((const int8_t *)ix, K, codes + (size_t)n * (K / 2));
+            rotate_row_f64(rot, w, K, v);
+            if (q_kind == 0 || q_kind == 2) {
+                orc_quant_sym_wrow(v, K, w_bits == 8 ? 127 : 7, q, &scale[n]);
+                for (int k = 0; k < K; k++)
+                    b8[k] = (uint8_t)(int8_t)q[k];
+                if (w_bits == 8)
+                    memcpy(codes + (size_t)n * K, b8, (size_t)K);
                 else
-                    orc_pack_crumbs(ix, K, codes + (size_t)n * (K / 4));
+                    orc_pack_nibbles((const int8_t *)b8, K, codes + (size_t)n * (K / 2));
                 if (qvals)
-                    memcpy(qvals + (size_t)n * K, ix, (size_t)K);
+                    memcpy(qvals + (size_t)n * K, q, (size_t)K * sizeof(int16_t));
+            } else if (q_kind == 3) {
+                uint8_t *crow = codes + (size_t)n * (K / 2);
+                orc_quant_mxfp4_f64(v, K, crow, mx_scales + (size_t)n * (K / 32));
+                if (qvals)
+                    for (int k = 0; k < K; k++)
+                        qvals[(size_t)n * K + k] = (int16_t)((crow[k >> 1] >> ((k & 1) * 4)) & 0xF);
+            } else {
+                orc_quant_lloydmax_wrow(v, K, levels, L, b8, &scale[n]);
+                if (L == 16)
+                    orc_pack_nibbles((const int8_t *)b8, K, codes + (size_t)n * (K / 2));
+                else
+                    orc_pack_crumbs(b8, K, codes + (size_t)n * (K / 4));
+                if (qvals)
+                    for (int k = 0; k < K; k++)
+                        qvals[(size_t)n * K + k] = (int16_t)b8[k];
             }
         }
-        free(w); free(v); free(q); free(ix);
+        free(w); free(v); free(q); free(b8);
     }
 }
 
@@ -615,6 +895,69 @@ void orc_codebook_dot_pairs(const uint8_t *codes_a, const uint8_t *codes_w, int 
             int ia = (ra[k >> 1] >> ((k & 1) * 4)) & 0xF;
             int iw = (rw[k / per_byte] >> ((k % per_byte) * w_bits)) & mask;
             s += (double)a_lv[ia] * (double)w_lv[iw];
+        }
+        dot[p] = s;
+    }
+}
+
+/* Code i of a packed row of `bits`-bit codes (4: nibbles, low nibble = even
+ * index; 8: bytes), two's complement when is_signed, else unsigned. */
+static int code_at(const uint8_t *row, int bits, int is_signed, int i)
+{
+    int v = bits == 8 ? row[i] : (row[i >> 1] >> ((i & 1) * 4)) & 0xF;
+    if (is_signed) {
+        int half = 1 << (bits - 1);
+        if (v >= half)
+            v -= 2 * half;
+    }
+    return v;
+}
+
+/*
+ * Integer GEMM of 4- or 8-bit codes for listed pairs, int64:
+ *   acc[p] = sum_{k < Kq} a[t_p][k] * w[n_p][koff + k]
+ * a: rows of Kq codes of a_bits (signed or unsigned); w: rows of Kw signed
+ * codes of w_bits.  (W4A4, W4A8 and W8A8 of [TRDQ]'s settings.)
+ */
+void orc_gemm_codes_pairs(const uint8_t *codes_a, int a_bits, int a_signed, int Kq,
+                          const uint8_t *codes_w, int w_bits, int Kw, int koff,
+                          const int64_t *ta, const int64_t *nw, int64_t npairs, int64_t *acc)
+{
+    size_t arow = (size_t)Kq * a_bits / 8, wrow = (size_t)Kw * w_bits / 8;
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < npairs; p++) {
+        const uint8_t *ra = codes_a + (size_t)ta[p] * arow;
+        const uint8_t *rw = codes_w + (size_t)nw[p] * wrow;
+        int64_t s = 0;
+        for (int k = 0; k < Kq; k++)
+            s += (int64_t)code_at(ra, a_bits, a_signed, k) *
+                 (int64_t)code_at(rw, w_bits, 1, koff + k);
+        acc[p] = s;
+    }
+}
+
+/*
+ * MXFP4 dot products for listed pairs, fp64:
+ *   dot[p] = sum_c 2^(ea[t][c] + ew[n][c]) sum_{k in block c} e2m1(a[t][k]) e2m1(w[n][k])
+ * Every block's inner sum is exact in fp64 (multiples of 1/4 below 2^11).
+ */
+void orc_mx_dot_pairs(const uint8_t *codes_a, const uint8_t *sc_a, const uint8_t *codes_w,
+                      const uint8_t *sc_w, int K, const int64_t *ta, const int64_t *nw,
+                      int64_t npairs, double *dot)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < npairs; p++) {
+        const uint8_t *ra = codes_a + (size_t)ta[p] * (K / 2);
+        const uint8_t *rw = codes_w + (size_t)nw[p] * (K / 2);
+        const uint8_t *sa = sc_a + (size_t)ta[p] * (K / 32);
+        const uint8_t *sw = sc_w + (size_t)nw[p] * (K / 32);
+        double s = 0.0;
+        for (int c = 0; c < K / 32; c++) {
+            double blk = 0.0;
+            for (int k = 32 * c; k < 32 * c + 32; k++)
+                blk += orc_e2m1_value((ra[k >> 1] >> ((k & 1) * 4)) & 0xF) *
+                       orc_e2m1_value((rw[k >> 1] >> ((k & 1) * 4)) & 0xF);
+            s += ldexp(blk, (int)sa[c] + (int)sw[c] - 254);
         }
         dot[p] = s;
     }

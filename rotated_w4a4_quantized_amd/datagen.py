@@ -15,6 +15,10 @@ stacked into one batch):
   flux_down 9216 x 12288 -> 3072, bf16 (GELU-shaped), RPBH block 512, INT4
   video  32760 x 1536 -> 8960, bf16, RPBH block 256, Lloyd-Max A4 / W2
 
+and variants of the FLUX up-projection for the other formats: MXFP4
+(E2M1 + E8M0 per 32), INT8 activations (W4A8, W8A8), and TR-DQ's runtime
+rotation (smoothing, block rotation, zigzag permutation, block rotation).
+
 Random streams: numpy PCG64 seeded from SeedSequence(1000 + i) for workload
 i, with spawned child streams for X, W, sign, perm and the calibration
 sample, so every tensor is reproducible on its own.
@@ -34,10 +38,10 @@ class Workload:
     T: int
     K: int
     N: int
-    rot: str            # "rpbh" | "dense"
-    block: int          # RPBH block (0 for dense)
+    rot: str            # "rpbh" | "dense" | "trdq"
+    block: int          # RPBH / TR-DQ block (0 for dense)
     r: int              # top-r kept in bf16 (dense only)
-    quant: str          # "int4" | "int4_asym" | "lloydmax"
+    quant: str          # "int4" | "int4_asym" | "lloydmax" | "mxfp4"; int4* with a_bits 8 = INT8 activations
     xdtype: str         # "f32" | "bf16"
     ydtype: str         # "f32" | "bf16"
     x_kind: str         # distribution recipe of X
@@ -52,15 +56,21 @@ class Workload:
     def b_eff(self) -> int:
         return self.block if self.rot == "rpbh" else 1
 
+    @property
+    def code_bytes(self) -> int:
+        """Bytes of activation codes per token (canonical layout)."""
+        return self.Kq * self.a_bits // 8
+
     def ops(self) -> int:
         """Algorithmic GEMM operations 2*T*Kq*N (multiply-add counted as 2)."""
         return 2 * self.T * self.Kq * self.N
 
-    def with_shape(self, T=None, K=None, N=None, block=None, w_bits=None) -> "Workload":
+    def with_shape(self, T=None, K=None, N=None, block=None, w_bits=None, a_bits=None) -> "Workload":
         return replace(self, T=self.T if T is None else T, K=self.K if K is None else K,
                        N=self.N if N is None else N,
                        block=self.block if block is None else block,
-                       w_bits=self.w_bits if w_bits is None else w_bits)
+                       w_bits=self.w_bits if w_bits is None else w_bits,
+                       a_bits=self.a_bits if a_bits is None else a_bits)
 
 
 WORKLOADS = {
@@ -84,6 +94,21 @@ WORKLOADS = {
     # 16-level weight book instead of the 4-level one
     "video_w4": Workload("video_w4", 4, 32760, 1536, 8960, "rpbh", 256, 0, "lloydmax", "bf16", "bf16",
                          "gauss", a_bits=4, w_bits=4),
+    # the FP4 format variant (MXFP4: E2M1 elements, one E8M0 scale per 32
+    # coordinates) on the FLUX layers, same seeds as flux_up / flux_down
+    "flux_up_mxfp4": Workload("flux_up_mxfp4", 2, 9216, 3072, 12288, "rpbh", 256, 0, "mxfp4",
+                              "bf16", "bf16", "gauss_outlier16x30"),
+    "flux_down_mxfp4": Workload("flux_down_mxfp4", 3, 9216, 12288, 3072, "rpbh", 512, 0, "mxfp4",
+                                "bf16", "bf16", "gelu"),
+    # INT8 activations (TR-DQ's W4A8 and W8A8 settings) on the FLUX up-projection
+    "flux_up_w4a8": Workload("flux_up_w4a8", 2, 9216, 3072, 12288, "rpbh", 256, 0, "int4", "bf16",
+                             "bf16", "gauss_outlier16x30", a_bits=8, w_bits=4),
+    "flux_up_w8a8": Workload("flux_up_w8a8", 2, 9216, 3072, 12288, "rpbh", 256, 0, "int4", "bf16",
+                             "bf16", "gauss_outlier16x30", a_bits=8, w_bits=8),
+    # TR-DQ's runtime rotation (smoothing, block rotation 128, zigzag
+    # permutation, block rotation 128) with its W4A8 setting
+    "flux_up_trdq": Workload("flux_up_trdq", 2, 9216, 3072, 12288, "trdq", 128, 0, "int4", "bf16",
+                             "bf16", "gauss_outlier16x30", a_bits=8, w_bits=4),
 }
 
 
@@ -169,6 +194,12 @@ def make_inputs(w: Workload, seed_offset: int = 0) -> dict:
         out["sign"] = np.where(s["sign"].integers(0, 2, size=K) == 1, 1, -1).astype(np.int8)
         out["perm"] = s["perm"].permutation(K).astype(np.int32)
         out["R"] = None
+    elif w.rot == "trdq":
+        calib = _draw_x(w, s["calib"], 1024, K, cols)
+        if w.xdtype == "bf16":
+            calib = bf16_bits_to_f32(f32_to_bf16_bits(calib))
+        out.update(trdq_rotation(calib, out["W"], w.block, s["perm"]))
+        out["sign"] = None
     else:
         out["sign"] = None
         out["perm"] = None
@@ -199,3 +230,93 @@ def random_rpbh(K: int, seed: int):
     sign = np.where(g.integers(0, 2, size=K) == 1, 1, -1).astype(np.int8)
     perm = g.permutation(K).astype(np.int32)
     return sign, perm
+
+
+# ---------------------------------------------------------------------------
+# TR-DQ's runtime rotation, built from a calibration sample (harness only:
+# the library takes the smoothing vector, the two block rotations and the
+# permutation as inputs, like the dense path's PCA basis)
+# ---------------------------------------------------------------------------
+
+def smoothing_multiplier(calib: np.ndarray, W: np.ndarray, alpha: float = 0.5) -> np.ndarray:
+    """Per-channel multiplier m = 1 / Delta of the SmoothQuant-style migration
+    ("TR-DQ" Eq.(4)-(5)): Delta_j = max|X_j|^alpha / max|W_j|^(1 - alpha), the
+    activations divided by Delta and the weights multiplied by it.  W is
+    [N][K], so W_j is column j.  fp64, stored fp32."""
+    ax = np.max(np.abs(calib.astype(np.float64)), axis=0)
+    aw = np.max(np.abs(W.astype(np.float64)), axis=0)
+    ax = np.where(ax > 0, ax, 1.0)
+    aw = np.where(aw > 0, aw, 1.0)
+    delta = ax ** alpha / aw ** (1.0 - alpha)
+    return (1.0 / delta).astype(np.float32)
+
+
+def _uniform_first_row_orthogonal(b: int, g: np.random.Generator) -> np.ndarray:
+    """A random b x b orthogonal matrix whose first row is uniform (every
+    entry 1 / sqrt(b)), fp64: QR of a Gaussian matrix whose first column is
+    all ones, transposed."""
+    A = g.standard_normal((b, b))
+    A[:, 0] = 1.0
+    Q, Rr = np.linalg.qr(A)
+    Q = Q * np.sign(np.diag(Rr))[None, :]
+    return Q.T
+
+
+def greedy_block_rotation(Xb: np.ndarray, g: np.random.Generator, steps: int = 4) -> np.ndarray:
+    """One block of TR-DQ's rotation ("TR-DQ" Eq.(6)-(7)): R^k = C1 Q C2,
+    where C1 swaps column 0 with the column holding the largest |value| of
+    the current activations, Q is a random orthogonal matrix with a uniform
+    first row, and C2 swaps the two columns back; R = R^1 ... R^n with n the
+    step count that minimizes the largest |value|.  fp64."""
+    b = Xb.shape[1]
+    R = np.eye(b)
+    cur = Xb.astype(np.float64)
+    best, best_R = np.max(np.abs(cur)), R.copy()
+    for _ in range(steps):
+        col = int(np.argmax(np.max(np.abs(cur), axis=0)))
+        C = np.eye(b)
+        C[[0, col]] = C[[col, 0]]
+        Rk = C @ _uniform_first_row_orthogonal(b, g) @ C
+        R = R @ Rk
+        cur = cur @ Rk
+        m = np.max(np.abs(cur))
+        if m < best:
+            best, best_R = m, R.copy()
+    return best_R
+
+
+def zigzag_permutation(chan_max: np.ndarray, b: int) -> np.ndarray:
+    """TR-DQ's zigzag permutation (section 3.2): channels ranked by
+    descending largest |activation| are dealt to blocks 0, 1, ..., nb - 1,
+    then nb - 1, ..., 0, and so on, each block filling its slots in arrival
+    order.  Returned as a gather: p[j] = z[perm[j]]."""
+    K = chan_max.size
+    nb = K // b
+    order = np.lexsort((np.arange(K), -chan_max.astype(np.float64)))
+    fill = np.zeros(nb, np.int64)
+    perm = np.zeros(K, np.int32)
+    for rank, ch in enumerate(order):
+        lap, pos = divmod(rank, nb)
+        blk = pos if lap % 2 == 0 else nb - 1 - pos
+        perm[blk * b + fill[blk]] = ch
+        fill[blk] += 1
+    return perm
+
+
+def trdq_rotation(calib: np.ndarray, W: np.ndarray, b: int, g: np.random.Generator) -> dict:
+    """Smoothing multiplier m [K], block rotations R1, R2 [K/b][b][b] (fp32)
+    and the zigzag permutation [K] for one layer, from a calibration sample
+    [Tc][K] (fp32): m from Eq.(5); R1 block by block on the smoothed sample;
+    the zigzag order from the channel maxima after R1; R2 block by block on
+    the permuted sample."""
+    K = calib.shape[1]
+    nb = K // b
+    m = smoothing_multiplier(calib, W)
+    y = calib.astype(np.float64) * m.astype(np.float64)[None, :]
+    R1 = np.stack([greedy_block_rotation(y[:, c * b:(c + 1) * b], g) for c in range(nb)])
+    R1 = R1.astype(np.float32)
+    z = np.concatenate([y[:, c * b:(c + 1) * b] @ R1[c].astype(np.float64) for c in range(nb)], axis=1)
+    perm = zigzag_permutation(np.max(np.abs(z), axis=0), b)
+    p = z[:, perm]
+    R2 = np.stack([greedy_block_rotation(p[:, c * b:(c + 1) * b], g) for c in range(nb)])
+    return {"m": m, "R1": R1, "perm": perm, "R2": R2.astype(np.float32), "R": None}
