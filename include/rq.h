@@ -12,7 +12,7 @@
  * offline (rq_pack_weights); at runtime only the forward rotation of the
  * activations, their per-token 4-bit quantization (rq_rotate_quant) and the
  * low-bit GEMM with the per-token x per-channel rescale (rq_w4a4_linear)
- * remain.  Two rotations are supported:
+ * remain.  Three rotations are supported:
  *
  *   RPBH   randomized permuted block-Hadamard (OrbitQuant abstract):
  *          y[j] = sign[j] * x[perm[j]], then an unnormalized Sylvester
@@ -23,18 +23,29 @@
  *   DENSE  an orthogonal basis R [K][K] (DiRotQ abstract: PCA basis from
  *          calibration); the first r rotated coordinates of every token are
  *          kept in bf16, the remaining K - r quantized to 4 bits.
+ *   TRDQ   TR-DQ's runtime rotation (section 3.2, Eq.(9)-(10)): a
+ *          per-channel smoothing multiplier, a block rotation R1, the
+ *          zigzag permutation, a block rotation R2.
  *
- * and two quantizers:
+ * and three quantizer families:
  *
- *   INT4_SYM   symmetric round-to-nearest-even INT4 in [-7, 7], one fp32
- *              scale per token (activations) / per output channel (weights)
- *              (TR-DQ Eq.(1)-(2) with a zero point of 0; granularity from
- *              TR-DQ section 3.1).
+ *   INT (RQ_Q_INT4_SYM / RQ_Q_INT4_ASYM, a_bits 4 or 8, w_bits 4 or 8)
+ *              round-to-nearest-even integers, one fp32 scale per token
+ *              (activations, symmetric in [-qmax, qmax] or asymmetric in
+ *              [0, 2^b - 1] with a zero point) and per output channel
+ *              (weights, symmetric) (TR-DQ Eq.(1)-(3); granularity from
+ *              TR-DQ section 3.1; its W4A8 / W8A8 settings).
  *   LLOYDMAX   OrbitQuant's normalized-basis quantizer: a token is scaled to
  *              norm sqrt(K) and every coordinate is coded by the nearest of
  *              2^a_bits fixed levels (a Lloyd-Max codebook of N(0,1)); weight
  *              rows likewise with 2^w_bits levels.  The token norm sigma and
  *              the row norm tau (both divided by sqrt(K)) rescale the output.
+ *   MXFP4      the FP4 variant (DiRotQ abstract, later version: NVFP4 on a
+ *              Blackwell GPU), read as OCP MX v1.0 MXFP4: E2M1 elements, one
+ *              E8M0 power-of-two scale per 32 consecutive coordinates,
+ *              e = floor(log2 max|x|) - 2, elements rounded to nearest with
+ *              ties to even and saturated at 6 -- the format gfx950's scaled
+ *              matrix cores take.
  *
  * Conventions for every entry point:
  *   - Pointers documented "device" must be device memory of the current HIP
@@ -80,29 +91,48 @@ typedef enum rq_dtype {
 } rq_dtype;
 
 /* Matrix cores that run an INT4 GEMM (rq_w4a4_linear_engine).
- *   AUTO  the library's choice: FP6 for INT4 weights, the codebook kernel
- *         for Lloyd-Max weights
+ *   AUTO  the library's choice: FP6 for INT weights with 4-bit activations,
+ *         int8 for 8-bit activations, the scaled FP4 cores for MXFP4, the
+ *         codebook kernel for Lloyd-Max weights
  *   FP6   E2M3 operands on v_mfma_scale_f32_32x32x64_f8f6f4: codes carried
  *         exactly, fp32 accumulation exact, twice the int8 rate
  *   INT8  v_mfma_i32_32x32x32_i8 with the nibbles widened to int8 in
  *         registers, int32 accumulation (INT4_SYM weights, canonical codes) */
 typedef enum rq_engine { RQ_ENGINE_AUTO = 0, RQ_ENGINE_FP6 = 1, RQ_ENGINE_INT8 = 2 } rq_engine;
 
-typedef enum rq_rot_kind { RQ_ROT_RPBH = 0, RQ_ROT_DENSE = 1 } rq_rot_kind;
-typedef enum rq_q_kind { RQ_Q_INT4_SYM = 0, RQ_Q_LLOYDMAX = 1, RQ_Q_INT4_ASYM = 2 } rq_q_kind;
+typedef enum rq_rot_kind { RQ_ROT_RPBH = 0, RQ_ROT_DENSE = 1, RQ_ROT_TRDQ = 2 } rq_rot_kind;
+/* RQ_Q_INT4_SYM / RQ_Q_INT4_ASYM are the integer family at any a_bits / w_bits
+ * (RQ_Q_INT_SYM / RQ_Q_INT_ASYM name the same values). */
+typedef enum rq_q_kind {
+    RQ_Q_INT4_SYM = 0,
+    RQ_Q_LLOYDMAX = 1,
+    RQ_Q_INT4_ASYM = 2,
+    RQ_Q_MXFP4 = 3,
+    RQ_Q_INT_SYM = 0,
+    RQ_Q_INT_ASYM = 2
+} rq_q_kind;
 
 /*
  * Rotation descriptor.  Pointer members are host pointers for
  * rq_pack_weights and device pointers for rq_rotate_quant.
  *   kind   rq_rot_kind
  *   K      input features; 32 <= K <= 16384, K % 32 == 0
- *   block  RPBH: b, a power of two, 2 <= b <= 1024, K % b == 0
- *   r      DENSE: coordinates kept in bf16, 0 <= r < K, r % 32 == 0; RPBH: 0
+ *   block  RPBH: b, a power of two, 2 <= b <= 1024, K % b == 0;
+ *          TRDQ: b, a power of two, 16 <= b <= 256, K % b == 0
+ *   r      DENSE: coordinates kept in bf16, 0 <= r < K, r % 32 == 0; else 0
  *   sign   RPBH: int8 [K], each -1 or +1
- *   perm   RPBH: int32 [K], a permutation of 0..K-1 (not checked on device)
- *          (rq_rotate_quant reads both as 16-byte vectors: the device copies
- *          must be 16-byte aligned, else RQ_ERR_ALIGN)
- *   R      DENSE: fp32 [K][K] row-major, column j is basis vector j
+ *   perm   RPBH: int32 [K], a permutation of 0..K-1 (not checked on device);
+ *          TRDQ: the zigzag permutation as a gather, p[j] = z[perm[j]]
+ *          (rq_rotate_quant reads sign and perm as 16-byte vectors: the
+ *          device copies must be 16-byte aligned, else RQ_ERR_ALIGN)
+ *   R      DENSE: fp32 [K][K] row-major, column j is basis vector j;
+ *          TRDQ: R1, fp32 [K/b][b][b]; block c maps coordinates cb..cb+b-1:
+ *          z[cb + j] = sum_i y[cb + i] R1[c][i][j]
+ *   smooth TRDQ: fp32 [K], the per-channel multiplier the activations
+ *          receive (y = x * smooth; TR-DQ Eq.(4)-(5): 1 / Delta); the weights
+ *          are divided by it.  NULL otherwise.
+ *   R2     TRDQ: fp32 [K/b][b][b], the second block rotation (as R1).
+ *          NULL otherwise.
  */
 typedef struct rq_rotation {
     int32_t kind;
@@ -112,16 +142,20 @@ typedef struct rq_rotation {
     const int8_t *sign;
     const int32_t *perm;
     const float *R;
+    const float *smooth;
+    const float *R2;
 } rq_rotation;
 
 /*
  * Quantizer descriptor (plain values, no pointers).
  *   kind      rq_q_kind.  INT4_ASYM: activations per token with a zero point
- *             (TR-DQ section 3.1 Eq.(1)-(3)), weights as INT4_SYM; RPBH only
- *   a_bits    4
- *   w_bits    INT4_SYM, INT4_ASYM: 4;  LLOYDMAX: 2 or 4
+ *             (TR-DQ section 3.1 Eq.(1)-(3)), weights symmetric; RPBH or TRDQ
+ *   a_bits    INT kinds: 4 or 8 (8: RPBH or TRDQ, symmetric weights of
+ *             w_bits 4 or 8; 4: w_bits 4);  LLOYDMAX, MXFP4: 4
+ *   w_bits    INT kinds: 4 or 8;  LLOYDMAX: 2 or 4;  MXFP4: 4
  *   a_levels  LLOYDMAX: 2^a_bits strictly ascending, bf16-representable
  *   w_levels  LLOYDMAX: 2^w_bits strictly ascending, bf16-representable
+ * MXFP4 runs with the RPBH rotation.
  */
 typedef struct rq_quant {
     int32_t kind;
@@ -133,7 +167,7 @@ typedef struct rq_quant {
 } rq_quant;
 
 #define RQ_WEIGHT_MAGIC 0x31575152u /* "RQW1" */
-#define RQ_WEIGHT_VERSION 2u
+#define RQ_WEIGHT_VERSION 3u
 
 /*
  * Header at the start of every packed-weight blob (256 bytes).  The blob is
@@ -143,23 +177,35 @@ typedef struct rq_quant {
  *   format        rq_q_kind of the weights
  *   K, N          input / output features
  *   r             DENSE top-r (0 otherwise)
- *   b_div         epilogue divisor: the RPBH block, 1 for DENSE
- *   row_bytes     bytes per packed weight row (K/2 for INT4, K/4 for 2-bit)
- *   scale_offset  byte offset of fp32 [N] (INT4: s_w; LLOYDMAX: tau)
+ *   b_div         epilogue divisor: the RPBH block, 1 otherwise
+ *   a_bits, w_bits  as in rq_quant
+ *   row_bytes     bytes per packed weight row (K/2 for 4-bit codes, K for
+ *                 8-bit, K/4 for 2-bit)
+ *   scale_offset  byte offset of the weight scales: fp32 [N] (INT: s_w;
+ *                 LLOYDMAX: tau) or, MXFP4, the E8M0 codes uint8 [N][K/32]
  *   codes_offset  byte offset of the packed codes [N][row_bytes]
- *                 INT4: two's-complement nibbles, low nibble = even k;
- *                 LLOYDMAX 2-bit: four level indices per byte, lowest k in
- *                 the lowest bits
+ *                 INT 4-bit: two's-complement nibbles, low nibble = even k;
+ *                 INT 8-bit: int8; MXFP4: E2M1 nibbles (sign in bit 3), low
+ *                 nibble = even k; LLOYDMAX 2-bit: four level indices per
+ *                 byte, lowest k in the lowest bits
  *   total_bytes   size of the whole blob
- *   a_levels, w_levels  the LLOYDMAX decode levels (zeros for INT4)
- *   INT4 only, the GEMM's private copy of the codes of the quantized
- *   coordinates k in [r, K) (zeros for LLOYDMAX):
- *   wsum_offset   byte offset of int32 [N]: sum over k in [r, K) of q_w[n][k]
- *   mma_offset    byte offset of the FP6 matrix-core fragments,
+ *   a_levels, w_levels  the LLOYDMAX decode levels (zeros otherwise)
+ *   The GEMMs' private copies (zero when absent):
+ *   wsum_offset   INT: int32 [N], sum over k in [r, K) of q_w[n][k]
+ *   mma_offset    INT with a_bits 4: the FP6 matrix-core fragments of the
+ *                 quantized coordinates k in [r, K),
  *                 [mma_ntiles][mma_stages][3][64][16] bytes: 32 output rows
- *                 by 128 coordinates per 3 KB tile, zero-padded past N and K
+ *                 by 128 coordinates per 3 KB tile, zero-padded past N and K;
+ *                 MXFP4: the E2M1 codes tiled [mma_ntiles][K/32][32][16]:
+ *                 rows in tiles of 32, each row's 16 bytes of coordinates
+ *                 32 c .. 32 c + 31 (zero rows past N)
  *   mma_stages    ceil((K - r) / 128)
  *   mma_ntiles    ceil(N / 32)
+ *   i8_offset     INT with a_bits 8: int8 [N][K] weight codes (the canonical
+ *                 codes when w_bits is 8, their widened copy when 4)
+ *   mxs_offset    MXFP4: the E8M0 codes tiled [mma_stages][mma_ntiles][64][2]:
+ *                 byte ks of lane 32 h + i is the scale of row 32 tile + i,
+ *                 coordinates 128 s + 64 ks + 32 h .. + 31
  */
 typedef struct rq_weight_header {
     uint32_t magic;
@@ -181,7 +227,9 @@ typedef struct rq_weight_header {
     int64_t mma_offset;
     int32_t mma_stages;
     int32_t mma_ntiles;
-    uint8_t reserved[256 - 64 - 128 - 24];
+    int64_t i8_offset;
+    int64_t mxs_offset;
+    uint8_t reserved[256 - 64 - 128 - 40];
 } rq_weight_header;
 
 /* Library version (major * 10000 + minor * 100 + patch). */
@@ -235,8 +283,8 @@ rq_status rq_pack_weights(const rq_rotation *rot, const rq_quant *q, const void 
                           int32_t w_dtype, int32_t N, void *blob, size_t blob_bytes);
 
 /*
- * Bytes of device workspace rq_rotate_quant needs (0 for RPBH; T*K*4 for
- * DENSE, which stages the rotated tokens in fp32).
+ * Bytes of device workspace rq_rotate_quant needs (0 for RPBH and TRDQ;
+ * T*K*4 for DENSE, which stages the rotated tokens in fp32).
  */
 rq_status rq_rotate_quant_workspace_bytes(const rq_rotation *rot, const rq_quant *q,
                                           int64_t T, size_t *bytes);
@@ -250,6 +298,21 @@ rq_status rq_rotate_quant_workspace_bytes(const rq_rotation *rot, const rq_quant
 rq_status rq_codes_mma_bytes(const rq_rotation *rot, int64_t T, size_t *bytes);
 
 /*
+ * Bytes of every activation buffer of T tokens under a quantizer:
+ *   codes      the canonical codes: T * (K - r) * a_bits / 8 (LLOYDMAX,
+ *              MXFP4: T * K / 2)
+ *   scale      T * 4 (INT symmetric, LLOYDMAX), T * 8 (INT asymmetric: s
+ *              then z), T * K / 32 (MXFP4: E8M0 codes)
+ *   codes_mma  the GEMM-layout copy rq_rotate_quant can write: INT with
+ *              a_bits 4 (RPBH): rq_codes_mma_bytes(); MXFP4: the tiled codes
+ *              and tiled scales (see rq_rotate_quant); 0 where none exists
+ * Any output pointer may be NULL.
+ * Errors: descriptor errors, RQ_ERR_SHAPE (T out of range).
+ */
+rq_status rq_activation_bytes(const rq_rotation *rot, const rq_quant *q, int64_t T,
+                              size_t *codes, size_t *scale, size_t *codes_mma);
+
+/*
  * Runtime activation path: rotate and quantize T tokens.
  * ("OrbitQuant" abstract: only a forward rotation of the activations
  * remains at runtime; TR-DQ section 3.2: quantization parameters are
@@ -259,34 +322,47 @@ rq_status rq_codes_mma_bytes(const rq_rotation *rot, int64_t T, size_t *bytes);
  *          stages h = 1, 2, 4, ..., block/2 in that order.
  *   DENSE: u[j] = fp32 fused multiply-add chain over k ascending of
  *          x[k] * R[k][j], starting from +0.
- *   INT4_SYM: over the quantized coordinates j in [r, K):
- *          amax = max |u[j]|; s = fl32(amax / 7); inv = fl32(7 / amax)
- *          q[j] = clamp(rne(fl32(u[j] * inv)), -7, 7); amax == 0 -> 0, s = 0.
+ *   TRDQ:  y[j] = fl32(x[j] * smooth[j]); z = y BlockDiag(R1) and then
+ *          u = p BlockDiag(R2) with p[j] = z[perm[j]], every output one fp32
+ *          fused multiply-add chain over its block's inputs ascending, from +0.
+ *   INT symmetric (qmax = 7 for a_bits 4, 127 for 8), over the quantized
+ *          coordinates j in [r, K):
+ *          amax = max |u[j]|; s = fl32(amax / qmax); inv = fl32(qmax / amax)
+ *          q[j] = clamp(rne(fl32(u[j] * inv)), -qmax, qmax); amax == 0 -> 0, s = 0.
  *          DENSE also writes top[t][j] = bf16_rne(u[j]) for j < r.
- *   INT4_ASYM (RPBH): lo = min u, hi = max u, d = fl32(hi - lo);
- *          s = fl32(d / 15); inv = fl32(15 / d);
- *          z = clamp(-rne(fl32(lo * inv)), 0, 15) (an integer);
- *          q[j] = clamp(rne(fl32(u[j] * inv)) + z, 0, 15); d == 0 -> 0, s = z = 0.
+ *   INT asymmetric (L = 15 or 255): lo = min u, hi = max u, d = fl32(hi - lo);
+ *          s = fl32(d / L); inv = fl32(L / d);
+ *          z = clamp(-rne(fl32(lo * inv)), 0, L) (an integer, +0 for zero);
+ *          q[j] = clamp(rne(fl32(u[j] * inv)) + z, 0, L); d == 0 -> 0, s = z = 0.
  *   LLOYDMAX: d = |u|^2 on an exact integer grid (order independent),
  *          g = (float)sqrt(K / d); index[j] = number of midpoints of adjacent
  *          a_levels strictly below fl32(u[j] * g); sigma = (float)sqrt(d / K).
+ *   MXFP4: per 32 coordinates c: e = floor(log2(max |u|)) - 2 (clamped to
+ *          [-127, 127]; -127 for a zero block), E8M0 code e + 127; element
+ *          code = the E2M1 value nearest to u / 2^e, ties to the even code,
+ *          magnitudes above 6 saturating to 6, zero always code 0.
  * Arguments:
- *   rot     host descriptor with device sign/perm (RPBH) or R (DENSE)
- *   q       quantizer (INT4_SYM with RPBH or DENSE; INT4_ASYM and LLOYDMAX
- *           with RPBH)
+ *   rot     host descriptor with device sign/perm (RPBH), R (DENSE) or
+ *           smooth/R/perm/R2 (TRDQ)
+ *   q       quantizer: INT with RPBH, TRDQ, or DENSE (symmetric, a_bits 4);
+ *           LLOYDMAX and MXFP4 with RPBH
  *   X       device [T][K] tokens, row-major, dtype x_dtype (RQ_F32/RQ_BF16),
  *           16-byte aligned
  *   T       tokens, 0 <= T < 2^31
- *   codes   device uint8 [T][(K - r) / 2]: INT4_SYM nibbles (two's complement,
- *           low nibble = even coordinate), INT4_ASYM unsigned nibbles, or
- *           LLOYDMAX 4-bit indices, same packing.  May be NULL for RPBH
- *           INT4 when codes_mma is given.
- *   scale   device fp32 [T]: s (INT4_SYM) or sigma (LLOYDMAX); INT4_ASYM:
- *           fp32 [2][T], s[t] then the zero point z[t]
+ *   codes   device uint8 [T][...] of rq_activation_bytes(): INT 4-bit
+ *           nibbles (two's complement when symmetric, unsigned when
+ *           asymmetric; low nibble = even coordinate), INT 8-bit bytes
+ *           (int8 / uint8), LLOYDMAX 4-bit indices or MXFP4 E2M1 codes as
+ *           nibbles.  May be NULL for RPBH INT 4-bit and MXFP4 when
+ *           codes_mma is given.
+ *   scale   device: fp32 [T] s (INT symmetric) or sigma (LLOYDMAX); INT
+ *           asymmetric: fp32 [2][T], s[t] then the zero point z[t]; MXFP4:
+ *           uint8 [T][K/32] E8M0 codes (the pointer is read as bytes).  May
+ *           be NULL for MXFP4 when codes_mma is given.
  *   top     device bf16 [T][r] for DENSE with r > 0, else NULL
- *   codes_mma  RPBH INT4 only, optional: device buffer of
- *           rq_codes_mma_bytes() receiving the same codes in the low-bit
- *           GEMM's matrix-core layout (NULL: not written).  Tokens come in
+ *   codes_mma  optional (NULL: not written), RPBH only:
+ *           INT 4-bit: a device buffer of rq_codes_mma_bytes() receiving the
+ *           same codes in the FP6 GEMM's matrix-core layout.  Tokens come in
  *           tiles of 32 and coordinates in stages of 128; the buffer is
  *           [tile][stage][piece 0..2][lane 0..63][16 bytes], 3 KB per tile
  *           and stage.  Token t of a tile owns lanes t and t + 32 (half h);
@@ -297,6 +373,11 @@ rq_status rq_codes_mma_bytes(const rq_rotation *rot, int64_t T, size_t *bytes);
  *           u (value u / 8, top two bits clear; u = q + 8 for INT4_SYM, the
  *           unsigned code for INT4_ASYM) of coordinate offset
  *           {0,1,3,4,6,7,9,10,12,13,15,8,2,11,5,14}[e % 16] + 16 (e / 16).
+ *           MXFP4: a device buffer of rq_activation_bytes()'s codes_mma:
+ *           the E2M1 codes tiled [ceil(T/32)][K/32][32][16 bytes] (token t
+ *           of a tile, its 16 bytes of coordinates 32 c .. 32 c + 31),
+ *           followed by the E8M0 codes tiled [ceil(K/128)][ceil(T/32)][64][2]
+ *           (byte ks of lane 32 h + t: coordinates 128 s + 64 ks + 32 h ..).
  *           Bytes of tokens past T and coordinates past K - r are left
  *           unwritten.
  *   workspace, workspace_bytes  device scratch of at least
@@ -333,33 +414,41 @@ rq_status rq_rotate_quant_noalloc(const rq_rotation *rot, const rq_quant *q, con
  * (TR-DQ section 3.1: Y = X W with per-token activation and per-channel
  * weight scales; DiRotQ abstract: the top principal coefficients add a
  * higher-precision term).
- *   INT4:  acc[t][n] = sum_{k < K-r} q_a[t][k] * q_w[n][r + k]  (exact, int32);
- *          INT4_ASYM: q_a[t][k] = u_a[t][k] - z[t] (codes minus zero point)
+ *   INT:   acc[t][n] = sum_{k < K-r} q_a[t][k] * q_w[n][r + k]  (exact, int32);
+ *          asymmetric: q_a[t][k] = u_a[t][k] - z[t] (codes minus zero point)
  *          RPBH:  Y = s_a[t] s_w[n] acc / b_div
+ *          TRDQ:  Y = s_a[t] s_w[n] acc
  *          DENSE: Y = s_w[n] (lr[t][n] + s_a[t] acc), with
  *                 lr = sum_{j < r} top[t][j] * q_w[n][j] (bf16 x int4 products,
  *                 fp32 accumulation)
  *   LLOYDMAX: Y = sigma[t] tau[n] / b_div * sum_k a_levels[idx_a] * w_levels[idx_w]
  *          (bf16 products, fp32 accumulation)
+ *   MXFP4: Y = 1 / b_div * sum over 32-coordinate blocks c of
+ *          2^(e_a[t][c] + e_w[n][c]) sum_{k in c} e2m1(a[t][k]) e2m1(w[n][k])
+ *          (exact products, fp32 accumulation in the matrix cores)
  *   + bias[n] when bias is not NULL.
- * INT4 weights run on the FP6 (E2M3) matrix cores: activation codes become
- * q + 8, weight codes q, both exact in E2M3, and the per-channel sum of the
- * weight codes (in the blob) removes the offset; every partial sum is an
- * integer below 2^24, so the fp32 accumulation is exact.
+ * INT weights with 4-bit activations run on the FP6 (E2M3) matrix cores:
+ * activation codes become q + 8, weight codes q, both exact in E2M3, and the
+ * per-channel sum of the weight codes (in the blob) removes the offset;
+ * every partial sum is an integer below 2^24, so the fp32 accumulation is
+ * exact.  8-bit activations run on the int8 matrix cores (int32
+ * accumulation), MXFP4 on the scaled FP4 matrix cores with the E8M0 block
+ * scales as the instruction's per-lane scales.
  * rq_w4a4_linear_engine() selects the matrix cores explicitly.
  * Arguments:
  *   hdr     host pointer to the blob's header (its first 256 bytes)
  *   blob    device copy of the whole blob, 16-byte aligned
  *   codes, scale, top  as written by rq_rotate_quant (device); the weights'
- *           format (INT4_SYM / INT4_ASYM) must match the activations' quantizer
- *   codes_mma  optional (INT4 weights with r == 0): the codes_mma output of
- *           rq_rotate_quant for the same tokens; when given it is read
- *           instead of codes (which may then be NULL)
+ *           format (kind, a_bits) must match the activations' quantizer
+ *   codes_mma  optional (INT with a_bits 4 and r == 0, or MXFP4): the
+ *           codes_mma output of rq_rotate_quant for the same tokens; when
+ *           given it is read instead of codes (and, MXFP4, scale), which may
+ *           then be NULL
  *   T       tokens, 0 <= T < 2^31
  *   bias    device fp32 [N] or NULL
  *   Y       device [T][N], dtype y_dtype: RQ_F32, RQ_BF16 (nearest-even), or
- *           RQ_I32 = the exact INT4 accumulators acc (INT4 formats only;
- *           the low-rank term and bias are left out)
+ *           RQ_I32 = the exact accumulators acc (INT formats only; the
+ *           low-rank term and bias are left out)
  *   stream  hipStream_t
  * Errors: RQ_ERR_NULL, RQ_ERR_FORMAT, RQ_ERR_SHAPE, RQ_ERR_DTYPE,
  *         RQ_ERR_ALIGN, RQ_ERR_UNSUPPORTED, RQ_ERR_HIP.
@@ -371,10 +460,11 @@ rq_status rq_w4a4_linear(const rq_weight_header *hdr, const void *blob, const ui
 /*
  * rq_w4a4_linear with an explicit choice of matrix cores (same passages and
  * arguments as rq_w4a4_linear, which is this call with RQ_ENGINE_AUTO).
- *   engine  rq_engine.  RQ_ENGINE_INT8 takes INT4_SYM weights (any r) and
- *           the canonical codes (codes_mma must be NULL); the accumulators
- *           and outputs equal the FP6 engine's bit for bit.  The Lloyd-Max
- *           format takes RQ_ENGINE_AUTO only.
+ *   engine  rq_engine.  RQ_ENGINE_INT8 takes INT4_SYM weights with 4-bit
+ *           activations (any r) and the canonical codes (codes_mma must be
+ *           NULL); the accumulators and outputs equal the FP6 engine's bit
+ *           for bit.  8-bit activations run on the int8 engine only (AUTO or
+ *           INT8); Lloyd-Max and MXFP4 take RQ_ENGINE_AUTO only.
  * Errors: as rq_w4a4_linear; RQ_ERR_UNSUPPORTED for an engine that cannot
  *         run the blob's format or for codes_mma with RQ_ENGINE_INT8.
  */

@@ -24,26 +24,49 @@ rq_status check_header(const rq_weight_header *hdr) {
     if (hdr->version != RQ_WEIGHT_VERSION)
         return fail(RQ_ERR_FORMAT, "weight header version " + std::to_string(hdr->version) +
                                        " is not " + std::to_string(RQ_WEIGHT_VERSION));
-    if (hdr->format != RQ_Q_INT4_SYM && hdr->format != RQ_Q_LLOYDMAX && hdr->format != RQ_Q_INT4_ASYM)
+    const int f = hdr->format;
+    if (f != RQ_Q_INT4_SYM && f != RQ_Q_LLOYDMAX && f != RQ_Q_INT4_ASYM && f != RQ_Q_MXFP4)
         return fail(RQ_ERR_FORMAT, "unknown weight format");
-    const bool int4 = hdr->format != RQ_Q_LLOYDMAX;
+    const bool intq = f == RQ_Q_INT4_SYM || f == RQ_Q_INT4_ASYM;
     if (hdr->K < 32 || hdr->K > 16384 || hdr->K % 32 != 0 || hdr->N < 1 || hdr->N > (1 << 20) ||
         hdr->r < 0 || hdr->r >= hdr->K || hdr->r % 32 != 0 || hdr->b_div < 1)
         return fail(RQ_ERR_FORMAT, "weight header shape fields are inconsistent");
-    const int want_rb = (int4 || hdr->w_bits == 4) ? hdr->K / 2 : hdr->K / 4;
+    if (intq && !((hdr->a_bits == 4 && hdr->w_bits == 4) ||
+                  (hdr->a_bits == 8 && (hdr->w_bits == 4 || hdr->w_bits == 8) && hdr->r == 0)))
+        return fail(RQ_ERR_FORMAT, "weight header bit widths are inconsistent");
+    int want_rb;
+    if (f == RQ_Q_LLOYDMAX)
+        want_rb = hdr->w_bits == 4 ? hdr->K / 2 : hdr->K / 4;
+    else if (f == RQ_Q_MXFP4)
+        want_rb = hdr->K / 2;
+    else
+        want_rb = hdr->K * hdr->w_bits / 8;
     if (hdr->row_bytes != want_rb) return fail(RQ_ERR_FORMAT, "weight header row_bytes mismatch");
-    if (hdr->format == RQ_Q_LLOYDMAX && hdr->K % 64 != 0)
+    if (f == RQ_Q_LLOYDMAX && hdr->K % 64 != 0)
         return fail(RQ_ERR_SHAPE, "the codebook GEMM needs K % 64 == 0");
     if (hdr->scale_offset % 16 != 0 || hdr->codes_offset % 16 != 0)
         return fail(RQ_ERR_FORMAT, "weight header offsets are not 16-byte aligned");
-    if (hdr->format == RQ_Q_INT4_ASYM && hdr->r != 0)
-        return fail(RQ_ERR_FORMAT, "INT4_ASYM weights have r == 0 (RPBH)");
-    if (int4) {
+    if (f == RQ_Q_INT4_ASYM && hdr->r != 0)
+        return fail(RQ_ERR_FORMAT, "INT4_ASYM weights have r == 0");
+    if (intq && hdr->a_bits == 4) {
         if (hdr->mma_stages != (hdr->K - hdr->r + 127) / 128 || hdr->mma_ntiles != (hdr->N + 31) / 32)
             return fail(RQ_ERR_FORMAT, "weight header FP6 tile counts are inconsistent");
         if (hdr->wsum_offset % 16 != 0 || hdr->mma_offset % 16 != 0 || hdr->wsum_offset <= 0 ||
             hdr->mma_offset + (int64_t)hdr->mma_ntiles * hdr->mma_stages * 3 * 1024 > hdr->total_bytes)
             return fail(RQ_ERR_FORMAT, "weight header FP6 section offsets are inconsistent");
+    }
+    if (intq && hdr->a_bits == 8) {
+        if (hdr->wsum_offset <= 0 || hdr->wsum_offset % 16 != 0 || hdr->i8_offset <= 0 ||
+            hdr->i8_offset % 16 != 0 || hdr->i8_offset + (int64_t)hdr->N * hdr->K > hdr->total_bytes)
+            return fail(RQ_ERR_FORMAT, "weight header int8 section offsets are inconsistent");
+    }
+    if (f == RQ_Q_MXFP4) {
+        if (hdr->K % 128 != 0) return fail(RQ_ERR_FORMAT, "MXFP4 weights need K % 128 == 0");
+        if (hdr->mma_stages != hdr->K / 128 || hdr->mma_ntiles != (hdr->N + 31) / 32 ||
+            hdr->mma_offset <= 0 || hdr->mma_offset % 16 != 0 || hdr->mxs_offset % 16 != 0 ||
+            hdr->mxs_offset < hdr->mma_offset + (int64_t)hdr->mma_ntiles * (hdr->K / 32) * 512 ||
+            hdr->mxs_offset + (int64_t)hdr->mma_stages * hdr->mma_ntiles * 128 > hdr->total_bytes)
+            return fail(RQ_ERR_FORMAT, "weight header MXFP4 sections are inconsistent");
     }
     return RQ_OK;
 }
@@ -57,17 +80,20 @@ rq_status validate_rotate_quant(const rq_rotation *rot, const rq_quant *q, const
     if (x_dtype != RQ_F32 && x_dtype != RQ_BF16)
         return fail(RQ_ERR_DTYPE, "X must be RQ_F32 or RQ_BF16");
     if (T < 0 || T >= (int64_t(1) << 31)) return fail(RQ_ERR_SHAPE, "T out of range");
+    const bool rpbh = rot->kind == RQ_ROT_RPBH;
     const bool dense = rot->kind == RQ_ROT_DENSE;
-    const bool int4 = q->kind == RQ_Q_INT4_SYM || q->kind == RQ_Q_INT4_ASYM;
-    if (codes_mma && (dense || !int4))
-        return fail(RQ_ERR_UNSUPPORTED, "codes_mma is written for RPBH with INT4 only");
+    const bool mx = q->kind == RQ_Q_MXFP4;
+    const bool int4 = (q->kind == RQ_Q_INT4_SYM || q->kind == RQ_Q_INT4_ASYM) && q->a_bits == 4;
+    if (codes_mma && !(rpbh && (int4 || mx)))
+        return fail(RQ_ERR_UNSUPPORTED,
+                    "codes_mma is written for RPBH with 4-bit integer codes or MXFP4 only");
     if (T == 0) return RQ_OK;
-    if (!X || !scale || (!codes && !codes_mma))
+    if (!X || (!codes && !codes_mma) || (!scale && !(mx && codes_mma)))
         return fail(RQ_ERR_NULL, "X, scale and at least one of codes / codes_mma must not be NULL");
-    if (dense && !codes) return fail(RQ_ERR_NULL, "DENSE needs codes");
-    if (!int4 && !codes) return fail(RQ_ERR_NULL, "LLOYDMAX needs codes");
+    if (!codes && !(rpbh && (int4 || mx)))
+        return fail(RQ_ERR_NULL, "this rotation and quantizer write the canonical codes: codes is NULL");
     if (dense && rot->r > 0 && !top) return fail(RQ_ERR_NULL, "DENSE with r > 0 needs top");
-    if (!aligned16(X) || (codes && !aligned16(codes)) || !aligned16(scale) ||
+    if (!aligned16(X) || (codes && !aligned16(codes)) || (scale && !aligned16(scale)) ||
         (top && !aligned16(top)) || (codes_mma && !aligned16(codes_mma)))
         return fail(RQ_ERR_ALIGN, "device buffers must be 16-byte aligned");
     if (!dense && (!aligned16(rot->sign) || !aligned16(rot->perm)))
@@ -88,6 +114,30 @@ rq_status rq_rotate_quant_workspace_bytes(const rq_rotation *rot, const rq_quant
     if (!bytes) return fail(RQ_ERR_NULL, "bytes is NULL");
     if (T < 0 || T >= (int64_t(1) << 31)) return fail(RQ_ERR_SHAPE, "T out of range");
     *bytes = rot->kind == RQ_ROT_DENSE ? (size_t)T * (size_t)rot->K * sizeof(float) : 0;
+    return RQ_OK;
+}
+
+rq_status rq_activation_bytes(const rq_rotation *rot, const rq_quant *q, int64_t T,
+                              size_t *codes, size_t *scale, size_t *codes_mma) {
+    clear_error();
+    rq_status st = check_rotation(rot, false);
+    if (st != RQ_OK) return st;
+    if ((st = check_quant(rot, q)) != RQ_OK) return st;
+    if (T < 0 || T >= (int64_t(1) << 31)) return fail(RQ_ERR_SHAPE, "T out of range");
+    const int K = rot->K, Kq = K - rot->r;
+    const bool intq = q->kind == RQ_Q_INT4_SYM || q->kind == RQ_Q_INT4_ASYM;
+    const bool mx = q->kind == RQ_Q_MXFP4;
+    if (codes) *codes = (size_t)T * (size_t)(intq ? Kq * q->a_bits / 8 : K / 2);
+    if (scale)
+        *scale = mx ? (size_t)T * (K / 32)
+                    : (size_t)T * (q->kind == RQ_Q_INT4_ASYM ? 8 : 4);
+    if (codes_mma) {
+        *codes_mma = 0;
+        if (rot->kind == RQ_ROT_RPBH && intq && q->a_bits == 4)
+            *codes_mma = (size_t)mma_codes_bytes(T, Kq);
+        else if (rot->kind == RQ_ROT_RPBH && mx)
+            *codes_mma = (size_t)mx_mma_bytes(T, K);
+    }
     return RQ_OK;
 }
 
@@ -116,11 +166,15 @@ rq_status rq_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void 
     const bool dense = rot->kind == RQ_ROT_DENSE;
     const bool int4 = q->kind == RQ_Q_INT4_SYM || q->kind == RQ_Q_INT4_ASYM;
     const int xb = x_dtype == RQ_BF16 ? 1 : 0;
-    if (!dense) {
-        if (int4)
+    if (rot->kind == RQ_ROT_RPBH) {
+        if (q->kind == RQ_Q_MXFP4)
+            return hip_status(launch_rpbh_mxfp4(X, xb, T, K, rot->block, rot->sign, rot->perm, codes,
+                                                reinterpret_cast<uint8_t *>(scale), codes_mma, stream),
+                              "rotate_quant launch");
+        if (q->kind == RQ_Q_INT4_SYM || q->kind == RQ_Q_INT4_ASYM)
             return hip_status(launch_rpbh_int4(X, xb, T, K, rot->block, rot->sign, rot->perm, codes,
                                                codes_mma, scale, q->kind == RQ_Q_INT4_ASYM ? 1 : 0,
-                                               stream),
+                                               q->a_bits, stream),
                               "rotate_quant launch");
         float th[15];
         const int La = 1 << q->a_bits;
@@ -129,6 +183,11 @@ rq_status rq_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void 
                                                La - 1, codes, scale, stream),
                           "rotate_quant launch");
     }
+    if (rot->kind == RQ_ROT_TRDQ)
+        return hip_status(launch_trdq(X, xb, T, K, rot->block, rot->smooth, rot->R, rot->perm, rot->R2,
+                                      codes, scale, q->kind == RQ_Q_INT4_ASYM ? 1 : 0, q->a_bits,
+                                      stream),
+                          "rotate_quant launch");
     const size_t need = (size_t)T * (size_t)K * sizeof(float);
     if (!workspace || workspace_bytes < need)
         return fail(RQ_ERR_SHAPE, "DENSE needs a workspace of " + std::to_string(need) + " bytes");
@@ -179,33 +238,51 @@ rq_status rq_w4a4_linear_engine(const rq_weight_header *hdr, const void *blob,
         return fail(RQ_ERR_DTYPE, "Y must be RQ_F32, RQ_BF16 or RQ_I32");
     if (engine != RQ_ENGINE_AUTO && engine != RQ_ENGINE_FP6 && engine != RQ_ENGINE_INT8)
         return fail(RQ_ERR_UNSUPPORTED, "unknown engine " + std::to_string(engine));
-    const bool int4 = hdr->format != RQ_Q_LLOYDMAX;
-    const bool asym = hdr->format == RQ_Q_INT4_ASYM;
-    if (y_dtype == RQ_I32 && !int4)
-        return fail(RQ_ERR_UNSUPPORTED, "raw accumulators exist for INT4 weights only");
-    if (codes_mma && (!int4 || hdr->r != 0))
-        return fail(RQ_ERR_UNSUPPORTED, "codes_mma is read for INT4 weights with r == 0 only");
-    if (engine != RQ_ENGINE_AUTO && !int4)
-        return fail(RQ_ERR_UNSUPPORTED, "the Lloyd-Max format has one engine (RQ_ENGINE_AUTO)");
-    const bool int8 = engine == RQ_ENGINE_INT8;
-    if (int8 && asym)
-        return fail(RQ_ERR_UNSUPPORTED, "the int8 engine takes INT4_SYM weights only");
+    const int f = hdr->format;
+    const bool intq = f == RQ_Q_INT4_SYM || f == RQ_Q_INT4_ASYM;
+    const bool asym = f == RQ_Q_INT4_ASYM;
+    const bool a8 = intq && hdr->a_bits == 8;
+    const bool mx = f == RQ_Q_MXFP4;
+    if (y_dtype == RQ_I32 && !intq)
+        return fail(RQ_ERR_UNSUPPORTED, "raw accumulators exist for integer weights only");
+    if (codes_mma && !((intq && !a8 && hdr->r == 0) || mx))
+        return fail(RQ_ERR_UNSUPPORTED,
+                    "codes_mma is read for 4-bit integer weights with r == 0 and for MXFP4 only");
+    if (engine != RQ_ENGINE_AUTO && !intq)
+        return fail(RQ_ERR_UNSUPPORTED, "the Lloyd-Max and MXFP4 formats have one engine (RQ_ENGINE_AUTO)");
+    if (a8 && engine == RQ_ENGINE_FP6)
+        return fail(RQ_ERR_UNSUPPORTED, "8-bit activations run on the int8 engine");
+    const bool int8 = a8 || engine == RQ_ENGINE_INT8;
+    if (int8 && !a8 && asym)
+        return fail(RQ_ERR_UNSUPPORTED, "the int8 engine takes INT4_SYM weights with 4-bit activations");
     if (int8 && codes_mma)
         return fail(RQ_ERR_UNSUPPORTED, "the int8 engine reads the canonical codes (codes_mma must be NULL)");
     if (T < 0 || T >= (int64_t(1) << 31)) return fail(RQ_ERR_SHAPE, "T out of range");
     if (T == 0) return RQ_OK;
-    if (!blob || !scale || !Y || (!codes && !codes_mma))
-        return fail(RQ_ERR_NULL, "blob, scale, Y and the activation codes must not be NULL");
-    if ((!int4 || int8) && !codes) return fail(RQ_ERR_NULL, "this engine needs codes");
+    if (!blob || !Y) return fail(RQ_ERR_NULL, "blob and Y must not be NULL");
+    if (mx) {
+        if (!codes_mma)
+            return fail(RQ_ERR_UNSUPPORTED, "the MXFP4 GEMM reads the tiled codes_mma of rq_rotate_quant");
+    } else {
+        if (!scale || (!codes && !codes_mma))
+            return fail(RQ_ERR_NULL, "scale and the activation codes must not be NULL");
+        if ((!intq || int8) && !codes) return fail(RQ_ERR_NULL, "this engine needs codes");
+    }
     if (hdr->r > 0 && !top) return fail(RQ_ERR_NULL, "weights with r > 0 need top");
-    if (!aligned16(blob) || (codes && !aligned16(codes)) || !aligned16(scale) || !aligned16(Y) ||
-        (top && !aligned16(top)) || (bias && !aligned16(bias)) ||
+    if (!aligned16(blob) || (codes && !aligned16(codes)) || (scale && !aligned16(scale)) ||
+        !aligned16(Y) || (top && !aligned16(top)) || (bias && !aligned16(bias)) ||
         (codes_mma && !aligned16(codes_mma)))
         return fail(RQ_ERR_ALIGN, "device buffers must be 16-byte aligned");
-    if (int4) {
+    if (mx) {
+        if (y_dtype == RQ_I32) return fail(RQ_ERR_UNSUPPORTED, "MXFP4 has no integer accumulators");
+        return hip_status(launch_gemm_mx(codes_mma, T, hdr, blob, bias, Y, y_dtype, stream),
+                          "mxfp4 gemm launch");
+    }
+    if (intq) {
         if (int8)
-            return hip_status(launch_gemm_w4a4(codes, scale, top, T, hdr, blob, bias, Y, y_dtype, stream),
-                              "w4a4 int8 gemm launch");
+            return hip_status(launch_gemm_w4a4(codes, scale, asym ? scale + T : nullptr, top, T, hdr,
+                                               blob, bias, Y, y_dtype, stream),
+                              "int8 gemm launch");
         return hip_status(launch_gemm_fp6(codes_mma ? nullptr : codes, codes_mma, scale,
                                           asym ? scale + T : nullptr, top, T, hdr, blob, bias, Y,
                                           y_dtype, stream),

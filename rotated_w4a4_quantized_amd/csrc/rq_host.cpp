@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <functional>
 #include <string>
 #include <thread>
 #include <vector>
@@ -41,6 +42,17 @@ rq_status check_rotation(const rq_rotation *rot, bool need_tables) {
         if (rot->r != 0) return fail(RQ_ERR_SHAPE, "RPBH takes r == 0");
         if (need_tables && (!rot->sign || !rot->perm))
             return fail(RQ_ERR_NULL, "RPBH needs sign and perm tables");
+    } else if (rot->kind == RQ_ROT_TRDQ) {
+        const int b = rot->block;
+        if (!is_pow2(b) || b < 16 || b > 256)
+            return fail(RQ_ERR_SHAPE, "TRDQ block must be a power of two in [16, 256], got " +
+                                          std::to_string(b));
+        if (K % b != 0)
+            return fail(RQ_ERR_SHAPE, "TRDQ block " + std::to_string(b) + " does not divide K " +
+                                          std::to_string(K));
+        if (rot->r != 0) return fail(RQ_ERR_SHAPE, "TRDQ takes r == 0");
+        if (need_tables && (!rot->smooth || !rot->R || !rot->perm || !rot->R2))
+            return fail(RQ_ERR_NULL, "TRDQ needs smooth, R (R1), perm and R2");
     } else if (rot->kind == RQ_ROT_DENSE) {
         if (rot->r < 0 || rot->r >= K || rot->r % 32 != 0)
             return fail(RQ_ERR_SHAPE, "DENSE r must satisfy 0 <= r < K and r % 32 == 0, got " +
@@ -54,12 +66,25 @@ rq_status check_rotation(const rq_rotation *rot, bool need_tables) {
 
 rq_status check_quant(const rq_rotation *rot, const rq_quant *q) {
     if (!q) return fail(RQ_ERR_NULL, "quantizer descriptor is NULL");
-    if (q->a_bits != 4) return fail(RQ_ERR_UNSUPPORTED, "a_bits must be 4");
     if (q->kind == RQ_Q_INT4_SYM || q->kind == RQ_Q_INT4_ASYM) {
-        if (q->w_bits != 4) return fail(RQ_ERR_UNSUPPORTED, "INT4 needs w_bits == 4");
-        if (q->kind == RQ_Q_INT4_ASYM && rot->kind != RQ_ROT_RPBH)
-            return fail(RQ_ERR_UNSUPPORTED, "INT4_ASYM is built for the RPBH rotation only");
+        if (q->a_bits != 4 && q->a_bits != 8)
+            return fail(RQ_ERR_UNSUPPORTED, "integer activations take a_bits 4 or 8");
+        if (q->w_bits != 4 && q->w_bits != 8)
+            return fail(RQ_ERR_UNSUPPORTED, "integer weights take w_bits 4 or 8");
+        if (q->a_bits == 4 && q->w_bits != 4)
+            return fail(RQ_ERR_UNSUPPORTED, "4-bit activations take w_bits 4");
+        if ((q->a_bits == 8 || q->kind == RQ_Q_INT4_ASYM) && rot->kind == RQ_ROT_DENSE)
+            return fail(RQ_ERR_UNSUPPORTED,
+                        "the dense rotation takes symmetric 4-bit activations (with top-r bf16)");
+    } else if (q->kind == RQ_Q_MXFP4) {
+        if (q->a_bits != 4 || q->w_bits != 4)
+            return fail(RQ_ERR_UNSUPPORTED, "MXFP4 takes a_bits 4 and w_bits 4");
+        if (rot->kind != RQ_ROT_RPBH)
+            return fail(RQ_ERR_UNSUPPORTED, "MXFP4 is built for the RPBH rotation only");
+        if (rot->K % 128 != 0)
+            return fail(RQ_ERR_SHAPE, "MXFP4 needs K % 128 == 0 (whole 128-coordinate GEMM stages)");
     } else if (q->kind == RQ_Q_LLOYDMAX) {
+        if (q->a_bits != 4) return fail(RQ_ERR_UNSUPPORTED, "LLOYDMAX takes a_bits 4");
         if (q->w_bits != 2 && q->w_bits != 4)
             return fail(RQ_ERR_UNSUPPORTED, "LLOYDMAX needs w_bits 2 or 4");
         if (rot->kind != RQ_ROT_RPBH)
@@ -109,6 +134,60 @@ static void fold_rpbh(const double *w, int K, int b, const int8_t *sign, const i
                 }
 }
 
+// TR-DQ (Eq.(9)-(10), H(W) = R2^T P^T R1^T Delta^-1 W): each weight row
+// divided by the activations' smoothing multiplier, then the two block
+// rotations around the zigzag gather, fp64 fma chains over i ascending.
+static void fold_trdq(const double *w, int K, int b, const float *smooth, const float *R1,
+                      const int32_t *perm, const float *R2, double *v) {
+    std::vector<double> y(K), z(K);
+    for (int j = 0; j < K; ++j) y[j] = w[j] / (double)smooth[j];
+    for (int c = 0; c < K / b; ++c)
+        for (int j = 0; j < b; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < b; ++i)
+                acc = std::fma(y[c * b + i], (double)R1[((size_t)c * b + i) * b + j], acc);
+            z[c * b + j] = acc;
+        }
+    for (int j = 0; j < K; ++j) y[j] = z[perm[j]];
+    for (int c = 0; c < K / b; ++c)
+        for (int j = 0; j < b; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < b; ++i)
+                acc = std::fma(y[c * b + i], (double)R2[((size_t)c * b + i) * b + j], acc);
+            v[c * b + j] = acc;
+        }
+}
+
+// MXFP4 element: the E2M1 code (sign in bit 3) of the value nearest to x,
+// ties to the even mantissa, magnitudes above 6 saturating.  Below 1 the
+// grid is the multiples of 1/2; in [2^e, 2^(e+1)) the multiples of 2^(e-1).
+static int e2m1_code(double x) {
+    const double a = std::fabs(x);
+    int c;
+    if (a < 1.0) {
+        c = (int)std::nearbyint(2.0 * a);   // 0, 1 (0.5) or 2 (1.0)
+    } else {
+        int e;
+        std::frexp(a, &e);                  // a = f 2^e, 0.5 <= f < 1: binade 2^(e-1)
+        const double step = std::ldexp(1.0, e - 2);
+        const double v = std::min(6.0, std::nearbyint(a / step) * step);
+        // v in {1, 1.5, 2, 3, 4, 6}: code = 2 (exponent field) + mantissa bit
+        int ve;
+        const double vf = std::frexp(v, &ve);   // v = vf 2^ve
+        c = 2 * ve + (vf > 0.5 ? 1 : 0);        // 1 -> 2, 1.5 -> 3, 2 -> 4, 3 -> 5, 4 -> 6, 6 -> 7
+    }
+    if (c == 0) return 0;
+    return (x < 0.0 ? 8 : 0) | c;
+}
+
+// E8M0 code of a 32-coordinate block whose largest magnitude is amax:
+// e = floor(log2 amax) - 2 (E2M1's largest exponent), clamped to [-127, 127].
+static int e8m0_code(double amax) {
+    if (amax == 0.0) return 0;
+    const int e = std::max(-127, std::min(127, std::ilogb(amax) - 2));
+    return e + 127;
+}
+
 // Dense: v[j] = fp64 fma chain over k ascending of w[k] * R[k][j], from +0.
 static void fold_dense(const double *w, int K, const float *R, double *v) {
     std::fill(v, v + K, 0.0);
@@ -128,7 +207,7 @@ static inline double bf16_bits_to_double(uint16_t h) {
 
 struct BlobLayout {
     int32_t row_bytes;
-    int64_t scale_off, codes_off, wsum_off, mma_off, total;
+    int64_t scale_off, codes_off, wsum_off, mma_off, i8_off, mxs_off, total;
     int32_t mma_stages, mma_ntiles;
 };
 
@@ -137,22 +216,36 @@ static inline int64_t round256(int64_t v) { return (v + 255) / 256 * 256; }
 static BlobLayout blob_layout(const rq_rotation *rot, const rq_quant *q, int32_t N) {
     const int K = rot->K;
     const int r = rot->kind == RQ_ROT_DENSE ? rot->r : 0;
+    const bool mx = q->kind == RQ_Q_MXFP4, lm = q->kind == RQ_Q_LLOYDMAX;
     BlobLayout L;
-    L.row_bytes = (q->kind != RQ_Q_LLOYDMAX || q->w_bits == 4) ? K / 2 : K / 4;
+    L.row_bytes = lm ? (q->w_bits == 4 ? K / 2 : K / 4) : (mx ? K / 2 : K * q->w_bits / 8);
     L.scale_off = (int64_t)sizeof(rq_weight_header);
-    L.codes_off = L.scale_off + round256((int64_t)N * 4);
-    const int64_t end = L.codes_off + round256((int64_t)N * L.row_bytes);
-    if (q->kind != RQ_Q_LLOYDMAX) {   // INT4 weights (either activation quantizer)
-        L.mma_stages = (K - r + 127) / 128;
+    L.codes_off = L.scale_off + round256(mx ? (int64_t)N * (K / 32) : (int64_t)N * 4);
+    int64_t end = L.codes_off + round256((int64_t)N * L.row_bytes);
+    L.mma_stages = L.mma_ntiles = 0;
+    L.wsum_off = L.mma_off = L.i8_off = L.mxs_off = 0;
+    if (mx) {
+        L.mma_stages = (K + 127) / 128;
         L.mma_ntiles = (N + 31) / 32;
+        L.mma_off = end;
+        L.mxs_off = L.mma_off + (int64_t)L.mma_ntiles * (K / 32) * 512;
+        end = L.mxs_off + round256((int64_t)L.mma_stages * L.mma_ntiles * 128);
+    } else if (!lm) {                    // integer weights
         L.wsum_off = end;
-        L.mma_off = L.wsum_off + round256((int64_t)N * 4);
-        L.total = L.mma_off + (int64_t)L.mma_ntiles * L.mma_stages * 3 * 1024;
-    } else {
-        L.mma_stages = L.mma_ntiles = 0;
-        L.wsum_off = L.mma_off = 0;
-        L.total = end;
+        end = L.wsum_off + round256((int64_t)N * 4);
+        if (q->a_bits == 4) {            // FP6 fragments of the quantized coordinates
+            L.mma_stages = (K - r + 127) / 128;
+            L.mma_ntiles = (N + 31) / 32;
+            L.mma_off = end;
+            end = L.mma_off + (int64_t)L.mma_ntiles * L.mma_stages * 3 * 1024;
+        } else if (q->w_bits == 8) {     // the canonical int8 codes serve the GEMM
+            L.i8_off = L.codes_off;
+        } else {                         // int8 copy of the 4-bit codes
+            L.i8_off = end;
+            end = L.i8_off + round256((int64_t)N * K);
+        }
     }
+    L.total = end;
     return L;
 }
 
@@ -201,7 +294,7 @@ using namespace rq;
 
 extern "C" {
 
-int32_t rq_version(void) { return 100; }
+int32_t rq_version(void) { return 200; }
 
 const char *rq_last_error(void) { return g_err.c_str(); }
 
@@ -228,14 +321,16 @@ rq_status rq_pack_weights(const rq_rotation *rot, const rq_quant *q, const void 
         return fail(RQ_ERR_DTYPE, "W must be RQ_F32 or RQ_BF16");
     if (N < 1 || N > (1 << 20)) return fail(RQ_ERR_SHAPE, "N must be in [1, 2^20]");
     const int K = rot->K;
-    if (rot->kind == RQ_ROT_RPBH) {
+    if (rot->kind == RQ_ROT_RPBH || rot->kind == RQ_ROT_TRDQ) {
         std::vector<char> seen(K, 0);
         for (int j = 0; j < K; ++j) {
             const int p = rot->perm[j];
             if (p < 0 || p >= K || seen[p]) return fail(RQ_ERR_SHAPE, "perm is not a permutation");
             seen[p] = 1;
-            if (rot->sign[j] != 1 && rot->sign[j] != -1)
+            if (rot->kind == RQ_ROT_RPBH && rot->sign[j] != 1 && rot->sign[j] != -1)
                 return fail(RQ_ERR_SHAPE, "sign entries must be -1 or +1");
+            if (rot->kind == RQ_ROT_TRDQ && (!std::isfinite(rot->smooth[j]) || rot->smooth[j] == 0.0f))
+                return fail(RQ_ERR_SHAPE, "smooth entries must be finite and nonzero");
         }
     }
     const BlobLayout BL = blob_layout(rot, q, N);
@@ -255,7 +350,7 @@ rq_status rq_pack_weights(const rq_rotation *rot, const rq_quant *q, const void 
     hdr.K = K;
     hdr.N = N;
     hdr.r = rot->kind == RQ_ROT_DENSE ? rot->r : 0;
-    hdr.b_div = rot->kind == RQ_ROT_RPBH ? rot->block : 1;
+    hdr.b_div = rot->kind == RQ_ROT_RPBH ? rot->block : 1;   // DENSE, TRDQ: orthonormal
     hdr.a_bits = q->a_bits;
     hdr.w_bits = q->w_bits;
     hdr.row_bytes = rb;
@@ -266,6 +361,8 @@ rq_status rq_pack_weights(const rq_rotation *rot, const rq_quant *q, const void 
     hdr.mma_offset = BL.mma_off;
     hdr.mma_stages = BL.mma_stages;
     hdr.mma_ntiles = BL.mma_ntiles;
+    hdr.i8_offset = BL.i8_off;
+    hdr.mxs_offset = BL.mxs_off;
     if (q->kind == RQ_Q_LLOYDMAX) {
         std::memcpy(hdr.a_levels, q->a_levels, sizeof hdr.a_levels);
         std::memcpy(hdr.w_levels, q->w_levels, sizeof hdr.w_levels);
@@ -274,9 +371,9 @@ rq_status rq_pack_weights(const rq_rotation *rot, const rq_quant *q, const void 
     float *scales = reinterpret_cast<float *>(out + so);
     uint8_t *codes = out + co;
 
-    // midpoints of adjacent weight levels (exact for bf16 levels)
-    const int Lw = 1 << q->w_bits;
-    double wth[15];
+    // Lloyd-Max: midpoints of adjacent weight levels (exact for bf16 levels)
+    const int Lw = q->kind == RQ_Q_LLOYDMAX ? 1 << q->w_bits : 0;
+    double wth[15] = {0};
     for (int i = 0; i + 1 < Lw; ++i)
         wth[i] = ((double)q->w_levels[i] + (double)q->w_levels[i + 1]) / 2.0;
 
@@ -292,27 +389,46 @@ rq_status rq_pack_weights(const rq_rotation *rot, const rq_quant *q, const void 
             }
             if (rot->kind == RQ_ROT_RPBH)
                 fold_rpbh(w.data(), K, rot->block, rot->sign, rot->perm, v.data());
+            else if (rot->kind == RQ_ROT_TRDQ)
+                fold_trdq(w.data(), K, rot->block, rot->smooth, rot->R, rot->perm, rot->R2, v.data());
             else
                 fold_dense(w.data(), K, rot->R, v.data());
             uint8_t *row = codes + (size_t)n * rb;
-            if (q->kind != RQ_Q_LLOYDMAX) {   // symmetric INT4 weights (both INT4 kinds)
+            if (q->kind == RQ_Q_MXFP4) {
+                uint8_t *e8 = out + so + (size_t)n * (K / 32);
+                for (int c = 0; c < K / 32; ++c) {
+                    double amax = 0.0;
+                    for (int k = 32 * c; k < 32 * c + 32; ++k) amax = std::max(amax, std::fabs(v[k]));
+                    const int sc = e8m0_code(amax);
+                    e8[c] = (uint8_t)sc;
+                    for (int k = 32 * c; k < 32 * c + 32; k += 2)
+                        row[k / 2] = (uint8_t)(e2m1_code(std::ldexp(v[k], 127 - sc)) |
+                                               (e2m1_code(std::ldexp(v[k + 1], 127 - sc)) << 4));
+                }
+            } else if (q->kind != RQ_Q_LLOYDMAX) {   // symmetric integer weights
+                const int qmax = q->w_bits == 8 ? 127 : 7;
                 double amax = 0.0;
                 for (int k = 0; k < K; ++k) amax = std::max(amax, std::fabs(v[k]));
                 if (amax == 0.0) {
                     scales[n] = 0.0f;
                     continue;  // codes already zero
                 }
-                const double inv = 7.0 / amax;
+                const double inv = (double)qmax / amax;
                 for (int k = 0; k < K; k += 2) {
                     int c[2];
                     for (int e = 0; e < 2; ++e) {
                         double t = std::nearbyint(v[k + e] * inv);
-                        t = std::min(7.0, std::max(-7.0, t));
+                        t = std::min((double)qmax, std::max(-(double)qmax, t));
                         c[e] = (int)t;
                     }
-                    row[k / 2] = (uint8_t)((c[0] & 0xF) | ((c[1] & 0xF) << 4));
+                    if (q->w_bits == 8) {
+                        row[k] = (uint8_t)(int8_t)c[0];
+                        row[k + 1] = (uint8_t)(int8_t)c[1];
+                    } else {
+                        row[k / 2] = (uint8_t)((c[0] & 0xF) | ((c[1] & 0xF) << 4));
+                    }
                 }
-                scales[n] = (float)(amax / 7.0);
+                scales[n] = (float)(amax / (double)qmax);
             } else {
                 double ss = 0.0;
                 for (int k = 0; k < K; ++k) ss += v[k] * v[k];
@@ -342,35 +458,63 @@ rq_status rq_pack_weights(const rq_rotation *rot, const rq_quant *q, const void 
         if (n0 < n1) pool.emplace_back(work, n0, n1);
     }
     for (auto &th : pool) th.join();
-    if (q->kind != RQ_Q_LLOYDMAX) {
-        // the GEMM's copy of the quantized coordinates [r, K): row sums and
-        // FP6 fragments (see pack_mma_tile)
+    auto parallel = [&](int count, const std::function<void(int, int)> &fn) {
+        std::vector<std::thread> tp;
+        const unsigned nth = std::max(1u, std::min<unsigned>(nt, (unsigned)count));
+        const int ch = (count + (int)nth - 1) / (int)nth;
+        for (unsigned t = 0; t < nth; ++t) {
+            const int a0 = (int)t * ch, a1 = std::min(count, a0 + ch);
+            if (a0 < a1) tp.emplace_back(fn, a0, a1);
+        }
+        for (auto &th : tp) th.join();
+    };
+    if (q->kind == RQ_Q_INT4_SYM || q->kind == RQ_Q_INT4_ASYM) {
+        // the GEMMs' copies of the quantized coordinates [r, K): row sums, and
+        // FP6 fragments (4-bit activations, see pack_mma_tile) or int8 codes
         const int r = hdr.r, Kq = K - r;
+        const bool w8 = q->w_bits == 8;
+        auto wcode = [&](int n, int k) -> int {
+            if (w8) return (int)(int8_t)codes[(size_t)n * rb + k];
+            const uint8_t byte = codes[(size_t)n * rb + k / 2];
+            const int nib = (k & 1) ? (byte >> 4) : (byte & 15);
+            return nib >= 8 ? nib - 16 : nib;
+        };
         int32_t *wsum = reinterpret_cast<int32_t *>(out + BL.wsum_off);
         for (int n = 0; n < N; ++n) {
             int32_t sum = 0;
-            for (int k = r; k < K; ++k) {
-                const uint8_t byte = codes[(size_t)n * rb + k / 2];
-                const int nib = (k & 1) ? (byte >> 4) : (byte & 15);
-                sum += nib >= 8 ? nib - 16 : nib;
-            }
+            for (int k = r; k < K; ++k) sum += wcode(n, k);
             wsum[n] = sum;
         }
-        const int ntiles = BL.mma_ntiles, S = BL.mma_stages;
-        auto tiles = [&](int t0, int t1) {
-            for (int tile = t0; tile < t1; ++tile)
-                for (int s = 0; s < S; ++s)
-                    pack_mma_tile(codes, N, rb, r, Kq, tile, s,
-                                  out + BL.mma_off + ((int64_t)tile * S + s) * 3 * 1024);
-        };
-        std::vector<std::thread> tp;
-        const unsigned nth = std::max(1u, std::min<unsigned>(nt, (unsigned)ntiles));
-        const int tchunk = (ntiles + (int)nth - 1) / (int)nth;
-        for (unsigned t = 0; t < nth; ++t) {
-            const int a0 = (int)t * tchunk, a1 = std::min(ntiles, a0 + tchunk);
-            if (a0 < a1) tp.emplace_back(tiles, a0, a1);
+        if (q->a_bits == 4) {
+            const int ntiles = BL.mma_ntiles, S = BL.mma_stages;
+            parallel(ntiles, [&](int t0, int t1) {
+                for (int tile = t0; tile < t1; ++tile)
+                    for (int s = 0; s < S; ++s)
+                        pack_mma_tile(codes, N, rb, r, Kq, tile, s,
+                                      out + BL.mma_off + ((int64_t)tile * S + s) * 3 * 1024);
+            });
+        } else if (!w8) {
+            int8_t *i8 = reinterpret_cast<int8_t *>(out + BL.i8_off);
+            for (int n = 0; n < N; ++n)
+                for (int k = 0; k < K; ++k) i8[(size_t)n * K + k] = (int8_t)wcode(n, k);
         }
-        for (auto &th : tp) th.join();
+    } else if (q->kind == RQ_Q_MXFP4) {
+        // tiled copies for the scaled FP4 GEMM: codes [tile][K/32][32][16],
+        // scales [stage][tile][64][2] (byte ks of lane 32 h + i: row
+        // 32 tile + i, coordinates 128 s + 64 ks + 32 h ..)
+        const int ntiles = BL.mma_ntiles, S = BL.mma_stages, nch = K / 32;
+        const uint8_t *e8 = out + so;
+        for (int tile = 0; tile < ntiles; ++tile)
+            for (int c = 0; c < nch; ++c)
+                for (int i = 0; i < 32; ++i) {
+                    const int n = 32 * tile + i;
+                    if (n >= N) continue;
+                    std::memcpy(out + BL.mma_off + (((int64_t)tile * nch + c) * 32 + i) * 16,
+                                codes + (size_t)n * rb + 16 * c, 16);
+                    const int s = c / 4, ks = (c / 2) & 1, h = c & 1;
+                    out[BL.mxs_off + (((int64_t)s * ntiles + tile) * 64 + 32 * h + i) * 2 + ks] =
+                        e8[(size_t)n * nch + c];
+                }
     }
     return RQ_OK;
 }

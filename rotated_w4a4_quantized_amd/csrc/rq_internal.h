@@ -36,9 +36,15 @@ int ensure_dyn_lds(const void *kernel, size_t bytes);
 // Kernel launchers (rq_rpbh.hip, rq_dense.hip, rq_gemm_*.hip).  Arguments are validated
 // by the caller; these only launch.  They return a hipError_t as int.
 // asym: per-token zero point (INT4_ASYM), written to scale[T .. 2T)
+// a_bits 4 or 8 (8: canonical codes only)
 int launch_rpbh_int4(const void *X, int x_bf16, int64_t T, int K, int block,
                      const int8_t *sign, const int32_t *perm, uint8_t *codes,
-                     uint8_t *codes_mma, float *scale, int asym, void *stream);
+                     uint8_t *codes_mma, float *scale, int asym, int a_bits, void *stream);
+// MXFP4: codes [T][K/2] and E8M0 scales [T][K/32] (either may be null), and/or
+// the tiled copies in codes_mma
+int launch_rpbh_mxfp4(const void *X, int x_bf16, int64_t T, int K, int block,
+                      const int8_t *sign, const int32_t *perm, uint8_t *codes,
+                      uint8_t *scales, uint8_t *codes_mma, void *stream);
 int launch_rpbh_lloydmax(const void *X, int x_bf16, int64_t T, int K, int block,
                          const int8_t *sign, const int32_t *perm, const float *thresholds,
                          int n_thresholds, uint8_t *codes, float *sigma, void *stream);
@@ -51,14 +57,30 @@ constexpr size_t kDenseScratchBytes = size_t(64) << 20;
 int dense_scratch(float **ptr);
 int launch_dense_quant(const float *U, int64_t T, int K, int r, uint8_t *codes,
                        float *scale, uint16_t *top, void *stream);
-int launch_gemm_w4a4(const uint8_t *codes, const float *scale, const uint16_t *top,
-                     int64_t T, const rq_weight_header *hdr, const void *blob,
-                     const float *bias, void *Y, int y_dtype, void *stream);
+// the int8-MFMA GEMM: 4-bit codes widened in registers (a_bits 4), or int8
+// activation codes against the blob's int8 weight copy (a_bits 8); zero: the
+// per-token zero points of asymmetric 8-bit activations, or null
+int launch_gemm_w4a4(const uint8_t *codes, const float *scale, const float *zero,
+                     const uint16_t *top, int64_t T, const rq_weight_header *hdr,
+                     const void *blob, const float *bias, void *Y, int y_dtype, void *stream);
+// TR-DQ runtime rotation (smoothing, block rotation, zigzag gather, block
+// rotation) and per-token integer quantization (a_bits 4 or 8, asym or not)
+int launch_trdq(const void *X, int x_bf16, int64_t T, int K, int block, const float *smooth,
+                const float *R1, const int32_t *perm, const float *R2, uint8_t *codes,
+                float *scale, int asym, int a_bits, void *stream);
 // zero: per-token zero points of INT4_ASYM activations, or null (symmetric)
 int launch_gemm_fp6(const uint8_t *codes, const uint8_t *codes_mma, const float *scale,
                     const float *zero, const uint16_t *top, int64_t T,
                     const rq_weight_header *hdr, const void *blob, const float *bias, void *Y,
                     int y_dtype, void *stream);
+// MXFP4 GEMM on the tiled codes and scales of rq_rotate_quant's codes_mma
+int launch_gemm_mx(const uint8_t *codes_mma, int64_t T, const rq_weight_header *hdr,
+                   const void *blob, const float *bias, void *Y, int y_dtype, void *stream);
+// bytes of an MXFP4 codes_mma buffer: tiled codes, then tiled scales
+inline int64_t mx_mma_bytes(int64_t T, int K) {
+    const int64_t tiles = (T + 31) / 32;
+    return tiles * (K / 32) * 512 + (int64_t)((K + 127) / 128) * tiles * 128;
+}
 int launch_gemm_codebook(const uint8_t *codes, const float *sigma, int64_t T,
                          const rq_weight_header *hdr, const void *blob,
                          const float *bias, void *Y, int y_dtype, void *stream);

@@ -182,17 +182,50 @@ __device__ inline void exchange(float *us, int tt, float (&v)[kE]) {
     get<L, P + 1, 1>(us, tt, v);
 }
 
-// Code staging layout: code byte q at q + 16 (q >> (L - 1)), i.e. 16 pad
-// bytes after every block (b / 2 bytes), which spreads the byte writes of one
-// instruction over the banks and keeps every 16-byte chunk aligned.
-template <int L>
-__host__ __device__ constexpr int cpad(int q) { return q + 16 * (q >> (L - 1)); }
-template <int L>
-__host__ __device__ constexpr int cbytes(int K) { return L <= 5 ? K / 2 : K / 2 + 16 * (K >> L) + 16; }
-// byte offset of the 16-byte code chunk c (coordinates 32 c .. 32 c + 31)
+// Pass P -> natural order (pass 0's sets, thread tt holding coordinates
+// 32 tt .. 32 tt + 31), through the same two half-token rounds.
+template <int L, int P>
+__device__ inline void to_natural(float *us, int tt, float (&v)[kE]) {
+    put<L, P, 0>(us, tt, v);
+    wave_lds_order();
+    get<L, 0, 0>(us, tt, v);
+    wave_lds_order();
+    put<L, P, 1>(us, tt, v);
+    wave_lds_order();
+    get<L, 0, 1>(us, tt, v);
+}
+
+// Code staging layout: code byte q (coordinate q << CSH; CSH = 1 for 4-bit
+// codes, 0 for 8-bit) at q + 16 (q >> (L - CSH)), i.e. 16 pad bytes after
+// every block's codes, which spreads the byte writes of one instruction over
+// the banks and keeps every 16-byte chunk aligned.
+template <int L, int CSH = 1>
+__host__ __device__ constexpr int cpad(int q) { return q + 16 * (q >> (L - CSH)); }
+template <int L, int CSH = 1>
+__host__ __device__ constexpr int cbytes(int K) {
+    return L <= 5 ? (K >> CSH) : (K >> CSH) + 16 * (K >> L) + 16;
+}
+// byte offset of the 16-byte code chunk c (4-bit coordinates 32 c .. 32 c + 31)
 // in a token's staging slot
 template <int L>
 __host__ __device__ constexpr int chunk_off(int c) { return L <= 5 ? 16 * c : cpad<L>(16 * c); }
+
+// MXFP4 element: the E2M1 code of x / 2^e (x times inv = 2^-e, exact but for
+// values far below E2M1's smallest step, which round to code 0 either way):
+// below 1 the nearest multiple of 1/2 (rne(2 a): codes 0, 1, 2); from 1 up the
+// fp32 mantissa rounded to one bit, nearest-even (add 2^21 - 1 plus the kept
+// bit, clear the low 22), capped at 6; the code is then 2 (fp32 exponent -
+// 126) plus the mantissa bit.  The sign goes to bit 3 unless the code is 0.
+__device__ inline uint32_t e2m1_code(float x, float inv) {
+    const float a = fabsf(x) * inv;
+    const uint32_t small = (uint32_t)rintf(a + a);
+    uint32_t b = __float_as_uint(a);
+    b = (b + 0x1FFFFFu + ((b >> 22) & 1u)) & 0xFFC00000u;
+    const uint32_t r = __float_as_uint(fminf(__uint_as_float(b), 6.0f));
+    const uint32_t big = (((r >> 23) - 126u) << 1) | ((r >> 22) & 1u);
+    const uint32_t c = a < 1.0f ? small : big;
+    return (c != 0u && x < 0.0f) ? (c | 8u) : c;
+}
 
 // Order-preserving 32-bit key of a float (for LDS atomic min / max over
 // values of either sign) and its inverse.
@@ -239,7 +272,9 @@ struct RpbhArgs {
     int gsz_log2;         // tokens per group: a workgroup's unit of work
     int ipg_log2;         // iterations per group (group size / tpw)
     int64_t ngroups;
-    float *scale;         // s or sigma [T]; asymmetric INT4: s [T] then z [T]
+    float *scale;         // s or sigma [T]; asymmetric: s [T] then z [T];
+                          // MXFP4: E8M0 codes uint8 [T][K/32] (or null)
+    int mx_tiles;         // MXFP4: ceil(T / 32) (tiled codes_mma layout)
     float th[15];         // codebook thresholds (Lloyd-Max)
     int th_sym;           // th[7] == 0 and th[i] == -th[14 - i] exactly
 };
@@ -261,6 +296,16 @@ rpbh_quant_kernel(RpbhArgs a) {
     // q + 8, an unsigned one (asymmetric, codebook) as it is.  The canonical
     // layout holds a symmetric q in two's complement: the nibble's top bit
     // flipped.
+    // QK: 0 symmetric 4-bit, 1 Lloyd-Max, 2 asymmetric 4-bit, 3 MXFP4,
+    //     4 symmetric 8-bit, 5 asymmetric 8-bit
+    constexpr bool ASYM = QK == 2 || QK == 5;
+    constexpr bool MX = QK == 3;
+    constexpr bool B8 = QK == 4 || QK == 5;
+    constexpr int CSH = B8 ? 0 : 1;   // code byte = coordinate >> CSH
+    constexpr float kLevels = QK == 5 ? 255.0f : 15.0f;   // asymmetric top code
+    // final codes in natural coordinate order per thread (32 per thread):
+    // the register layout of pass 0, or MXFP4 after its regrouping exchange
+    constexpr bool NATURAL = Plan<L>::NP == 1 || MX;
     constexpr uint32_t kCanonFlip = QK == 0 ? 0x88888888u : 0u;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ unsigned red_max[2][kMaxTpw];
@@ -272,7 +317,7 @@ rpbh_quant_kernel(RpbhArgs a) {
     const int tt = tid - tl * a.tpt;
     uint8_t *xs = smem + (size_t)tl * K * S::XB;
     const int xw = xwords<L>(K);
-    const int cb = (cbytes<L>(K) + 15) & ~15;
+    const int cb = (cbytes<L, CSH>(K) + 15) & ~15;
     float *us = reinterpret_cast<float *>(smem + (size_t)a.tpw * K * S::XB) + (size_t)tl * xw;
     // code staging: one slot per token of the group
     uint8_t *const cs0 = smem + (size_t)a.tpw * (K * S::XB + 4 * xw);
@@ -398,7 +443,7 @@ rpbh_quant_kernel(RpbhArgs a) {
             store_pair_mma_in_tile(tile, sh >> 1, t32 + j, sh & 1, w0, w1, c1 < nch, 0u);
         }
     };
-    const bool grouped = QK != 1 && a.grouped;
+    const bool grouped = (QK == 0 || QK == 2) && a.grouped;
 
     // lane groups of one token for the shuffle reductions
     int grp = 64;
@@ -414,7 +459,7 @@ rpbh_quant_kernel(RpbhArgs a) {
         if (tt == 0) {
             red_max[it & 1][tl] = 0u;
             if constexpr (QK == 1) red_sum[it & 1][tl] = 0ull;
-            if constexpr (QK == 2) red_min[it & 1][tl] = 0xFFFFFFFFu;
+            if constexpr (ASYM) red_min[it & 1][tl] = 0xFFFFFFFFu;
         }
         float v[kE];
 #pragma unroll
@@ -447,7 +492,14 @@ rpbh_quant_kernel(RpbhArgs a) {
         static_assert(Plan<L>::NP <= 3, "block too large");
         constexpr int PL = Plan<L>::NP - 1;
 
-        if constexpr (QK == 2) {
+        if constexpr (MX && Plan<L>::NP > 1) {
+            // regroup into natural order (thread tt: coordinates 32 tt ..
+            // 32 tt + 31, one MX block), through the exchange buffer: an MX
+            // block lies inside one RPBH block, so inside one wave
+            wave_lds_order();
+            to_natural<L, PL>(us, tt, v);
+        }
+        if constexpr (ASYM) {
             float lo = v[0], hi = v[0];
 #pragma unroll
             for (int r = 1; r < kE; ++r) {
@@ -460,7 +512,7 @@ rpbh_quant_kernel(RpbhArgs a) {
                 atomicMin(&red_min[it & 1][tl], klo);
                 atomicMax(&red_max[it & 1][tl], khi);
             }
-        } else {
+        } else if constexpr (!MX) {
             float m = 0.0f;
 #pragma unroll
             for (int r = 0; r < kE; ++r) m = fmaxf(m, fabsf(v[r]));
@@ -471,26 +523,27 @@ rpbh_quant_kernel(RpbhArgs a) {
         lds_barrier();  // B2: statistic complete, next token staged
         const float amax = __uint_as_float(red_max[it & 1][tl]);
 
-        uint32_t nib[kE];
+        uint32_t nib[kE];   // the codes: nibbles, or bytes for 8-bit codes
         float sc = 0.0f, zp = 0.0f;
-        if constexpr (QK == 2) {
-            // s = fl32(d / 15), inv = fl32(15 / d), z = clamp(-rne(fl32(lo inv)), 0, 15),
-            // q = clamp(rne(fl32(u inv)) + z, 0, 15); the float sum is exact
-            // wherever the clamp does not bind
+        uint32_t mxsc = 0u;  // MXFP4: E8M0 code of this thread's block
+        if constexpr (ASYM) {
+            // L = 15 or 255: s = fl32(d / L), inv = fl32(L / d),
+            // z = clamp(-rne(fl32(lo inv)), 0, L), q = clamp(rne(fl32(u inv)) + z, 0, L);
+            // the float sum is exact wherever the clamp does not bind
             const float lo = fkey_inv(red_min[it & 1][tl]);
             const float hi = fkey_inv(red_max[it & 1][tl]);
             const float d = hi - lo;
             if (d != 0.0f) {
-                const float inv = 15.0f / d;
-                sc = d / 15.0f;
-                // z is the integer -rne(lo inv) clamped to [0, 15], as a float;
+                const float inv = kLevels / d;
+                sc = d / kLevels;
+                // z is the integer -rne(lo inv) clamped to [0, L], as a float;
                 // rne(lo inv) = -0 or +0 (a row whose minimum is at most s / 2
                 // from zero) gives z = +0
                 const float zr = rintf(lo * inv);
-                zp = zr >= 0.0f ? 0.0f : (zr < -15.0f ? 15.0f : -zr);
+                zp = zr >= 0.0f ? 0.0f : (zr < -kLevels ? kLevels : -zr);
 #pragma unroll
                 for (int r = 0; r < kE; ++r) {
-                    const float t = fminf(fmaxf(rintf(v[r] * inv) + zp, 0.0f), 15.0f);
+                    const float t = fminf(fmaxf(rintf(v[r] * inv) + zp, 0.0f), kLevels);
                     nib[r] = (uint32_t)t;
                 }
             } else {
@@ -509,6 +562,25 @@ rpbh_quant_kernel(RpbhArgs a) {
                 nib[r] = __float_as_uint(mq + 12582920.0f);   // q + 8 in bits 0..3
             }
             sc = amax > 0.0f ? amax / 7.0f : 0.0f;
+        } else if constexpr (QK == 4) {
+            // q = rne(fl32(u * inv)) in [-127, 127] (|u * inv| <= fl32(127 (1 + 2^-24))
+            // rounds to at most 127); adding 1.5 * 2^23 leaves q in the low
+            // mantissa bits, whose low byte is q in two's complement
+            const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+#pragma unroll
+            for (int r = 0; r < kE; ++r) nib[r] = __float_as_uint(v[r] * inv + 12582912.0f) & 0xFFu;
+            sc = amax > 0.0f ? amax / 127.0f : 0.0f;
+        } else if constexpr (MX) {
+            // this thread's 32 coordinates are one block: e = floor(log2 max|u|) - 2
+            float m = 0.0f;
+#pragma unroll
+            for (int r = 0; r < kE; ++r) m = fmaxf(m, fabsf(v[r]));
+            int e = m > 0.0f ? ilogbf(m) - 2 : -127;
+            e = e < -127 ? -127 : e;
+            mxsc = (uint32_t)(e + 127);
+            const float inv = ldexpf(1.0f, -e);   // 2^-e: 2^-125 .. 2^127, exact
+#pragma unroll
+            for (int r = 0; r < kE; ++r) nib[r] = e2m1_code(v[r], inv);
         } else {
             // exact squared norm on the grid 2^(2E - 36), E = ilogb(max |u|)
             const int E = amax > 0.0f ? ilogbf(amax) : 0;
@@ -556,43 +628,85 @@ rpbh_quant_kernel(RpbhArgs a) {
         }
 
         // pack: register bit 0 carries index bit 0, so registers (2m, 2m + 1)
-        // hold a nibble pair; bits 4..7 of every code word are clear
-        uint4 chunk = make_uint4(0u, 0u, 0u, 0u);
-        if constexpr (Plan<L>::NP == 1) {
-            uint32_t w[4];
+        // hold a nibble (byte) pair; bits 4..7 (8..31) of every code word are clear
+        uint4 chunk = make_uint4(0u, 0u, 0u, 0u), chunk1 = make_uint4(0u, 0u, 0u, 0u);
+        if constexpr (NATURAL) {
+            if constexpr (B8) {
+                uint32_t w[8];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                uint32_t x = 0;
+                for (int q = 0; q < 8; ++q)
+                    w[q] = nib[4 * q] | (nib[4 * q + 1] << 8) | (nib[4 * q + 2] << 16) | (nib[4 * q + 3] << 24);
+                chunk = make_uint4(w[0], w[1], w[2], w[3]);
+                chunk1 = make_uint4(w[4], w[5], w[6], w[7]);
+            } else {
+                uint32_t w[4];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x |= (nib[8 * q + e] & 0xFu) << (4 * e);
-                w[q] = x;
+                for (int q = 0; q < 4; ++q) {
+                    uint32_t x = 0;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x |= (nib[8 * q + e] & 0xFu) << (4 * e);
+                    w[q] = x;
+                }
+                chunk = make_uint4(w[0], w[1], w[2], w[3]);
+                if (grouped) *reinterpret_cast<uint4 *>(cs + 16 * tt) = chunk;
             }
-            chunk = make_uint4(w[0], w[1], w[2], w[3]);
-            if (grouped) *reinterpret_cast<uint4 *>(cs + 16 * tt) = chunk;
         } else {
-            uint8_t *p = cs + cpad<L>(pbase<L, PL>(tt) >> 1);
+            uint8_t *p = cs + cpad<L, CSH>(pbase<L, PL>(tt) >> CSH);
+            if constexpr (B8) {
 #pragma unroll
-            for (int mm = 0; mm < kE / 2; ++mm)
-                p[Plan<L>::roff(PL, 2 * mm) >> 1] = (uint8_t)(nib[2 * mm] | (nib[2 * mm + 1] << 4));
+                for (int mm = 0; mm < kE / 2; ++mm)
+                    *reinterpret_cast<uint16_t *>(p + Plan<L>::roff(PL, 2 * mm)) =
+                        (uint16_t)(nib[2 * mm] | (nib[2 * mm + 1] << 8));
+            } else {
+#pragma unroll
+                for (int mm = 0; mm < kE / 2; ++mm)
+                    p[Plan<L>::roff(PL, 2 * mm) >> 1] = (uint8_t)(nib[2 * mm] | (nib[2 * mm + 1] << 4));
+            }
             if (a.codes || (a.codes_mma && !grouped)) {
-                // the 16 bytes this thread stores were written by lanes of its
+                // the bytes this thread stores were written by lanes of its
                 // own wave (its RPBH block): order the LDS writes before the read
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                chunk = *reinterpret_cast<const uint4 *>(cs + cpad<L>(16 * tt));
+                if constexpr (B8) {
+                    chunk = *reinterpret_cast<const uint4 *>(cs + cpad<L, 0>(32 * tt));
+                    chunk1 = *reinterpret_cast<const uint4 *>(cs + cpad<L, 0>(32 * tt) + 16);
+                } else {
+                    chunk = *reinterpret_cast<const uint4 *>(cs + cpad<L>(16 * tt));
+                }
             }
         }
         if (valid) {
-            if (a.codes)
-                *reinterpret_cast<uint4 *>(a.codes + tok * (int64_t)(K / 2) + 16 * tt) =
-                    make_uint4(chunk.x ^ kCanonFlip, chunk.y ^ kCanonFlip, chunk.z ^ kCanonFlip,
-                               chunk.w ^ kCanonFlip);
-            if constexpr (QK != 1)
+            if (a.codes) {
+                if constexpr (B8) {
+                    uint4 *dst = reinterpret_cast<uint4 *>(a.codes + tok * (int64_t)K + 32 * tt);
+                    dst[0] = chunk;
+                    dst[1] = chunk1;
+                } else {
+                    *reinterpret_cast<uint4 *>(a.codes + tok * (int64_t)(K / 2) + 16 * tt) =
+                        make_uint4(chunk.x ^ kCanonFlip, chunk.y ^ kCanonFlip, chunk.z ^ kCanonFlip,
+                                   chunk.w ^ kCanonFlip);
+                }
+            }
+            if constexpr (QK == 0 || QK == 2)
                 if (a.codes_mma && !grouped) store_chunk_mma(a.codes_mma, tok, a.mma_stages, tt, chunk, 0u);
-            if (tt == 0) {
+            if constexpr (MX) {
+                // E8M0 code of block tt: canonical [T][K/32], and the tiled
+                // copies [tile][K/32][32][16] (codes) and
+                // [stage][tile][64][2] (scales) of the scaled FP4 GEMM
+                const int nch = K / kE;
+                if (a.scale) reinterpret_cast<uint8_t *>(a.scale)[tok * nch + tt] = (uint8_t)mxsc;
+                if (a.codes_mma) {
+                    const int64_t tile = tok >> 5;
+                    const int row = (int)(tok & 31);
+                    *reinterpret_cast<uint4 *>(a.codes_mma + ((tile * nch + tt) * 32 + row) * 16) = chunk;
+                    uint8_t *mxs = a.codes_mma + (int64_t)a.mx_tiles * nch * 512;
+                    mxs[(((int64_t)(tt >> 2) * a.mx_tiles + tile) * 64 + 32 * (tt & 1) + row) * 2 +
+                        ((tt >> 1) & 1)] = (uint8_t)mxsc;
+                }
+            } else if (tt == 0) {
                 a.scale[tok] = sc;
-                if constexpr (QK == 2) a.scale[a.T + tok] = zp;
+                if constexpr (ASYM) a.scale[a.T + tok] = zp;
             }
         }
         base = next;
@@ -607,16 +721,18 @@ template <int L, bool BF16, int QK>
 hipError_t launch_L(RpbhArgs a, hipStream_t s) {
     const int xb = BF16 ? 2 : 4;
     const size_t per_tok = (size_t)a.K * xb + 4 * (size_t)xwords<L>(a.K);
-    const size_t slot_bytes = (size_t)((cbytes<L>(a.K) + 15) & ~15);
+    constexpr int CSH = (QK == 4 || QK == 5) ? 0 : 1;
+    const size_t slot_bytes = (size_t)((cbytes<L, CSH>(a.K) + 15) & ~15);
     // the dynamic LDS a workgroup may take (160 KB less the static arrays)
     constexpr size_t kLdsMax = 159 * 1024;
     // MMA-layout codes are written per group of >= 4 consecutive tokens when
     // the group's code slots fit, else per token
-    const bool grouped = QK != 1 && a.codes_mma != nullptr && per_tok + 4 * slot_bytes <= kLdsMax;
+    const bool grouped = (QK == 0 || QK == 2) && a.codes_mma != nullptr && per_tok + 4 * slot_bytes <= kLdsMax;
     a.grouped = grouped ? 1 : 0;
     // per-token code staging: the regrouping exchange (blocks > 32), or the
     // group's slots
-    const size_t slot = (L <= 5 && !grouped) ? 0 : slot_bytes;
+    // (MXFP4 regroups its values in the exchange buffer instead)
+    const size_t slot = ((L <= 5 && !grouped) || QK == 3) ? 0 : slot_bytes;
     auto group_of = [&](int tpw) { return grouped && tpw < 4 ? 4 : tpw; };
     auto lds_of = [&](int tpw) { return per_tok * tpw + slot * group_of(tpw); };
     auto kern = rpbh_quant_kernel<L, BF16, QK>;
@@ -717,6 +833,7 @@ RpbhArgs make_args(const void *X, int64_t T, int K, const int8_t *sign, const in
     a.gsz_log2 = a.ipg_log2 = 0;
     a.ngroups = 0;
     a.scale = scale;
+    a.mx_tiles = (int)((T + 31) / 32);
     for (int i = 0; i < 15; ++i) a.th[i] = 0.0f;
     a.th_sym = 0;
     return a;
@@ -726,12 +843,25 @@ RpbhArgs make_args(const void *X, int64_t T, int K, const int8_t *sign, const in
 
 int launch_rpbh_int4(const void *X, int x_bf16, int64_t T, int K, int block, const int8_t *sign,
                      const int32_t *perm, uint8_t *codes, uint8_t *codes_mma, float *scale,
-                     int asym, void *stream) {
+                     int asym, int a_bits, void *stream) {
     RpbhArgs a = make_args(X, T, K, sign, perm, codes, codes_mma, scale);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int L = ilog2(block);
+    if (a_bits == 8) {
+        if (asym) return (int)(x_bf16 ? dispatch<true, 5>(L, a, s) : dispatch<false, 5>(L, a, s));
+        return (int)(x_bf16 ? dispatch<true, 4>(L, a, s) : dispatch<false, 4>(L, a, s));
+    }
     if (asym) return (int)(x_bf16 ? dispatch<true, 2>(L, a, s) : dispatch<false, 2>(L, a, s));
     return (int)(x_bf16 ? dispatch<true, 0>(L, a, s) : dispatch<false, 0>(L, a, s));
+}
+
+int launch_rpbh_mxfp4(const void *X, int x_bf16, int64_t T, int K, int block, const int8_t *sign,
+                      const int32_t *perm, uint8_t *codes, uint8_t *scales, uint8_t *codes_mma,
+                      void *stream) {
+    RpbhArgs a = make_args(X, T, K, sign, perm, codes, codes_mma, reinterpret_cast<float *>(scales));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int L = ilog2(block);
+    return (int)(x_bf16 ? dispatch<true, 3>(L, a, s) : dispatch<false, 3>(L, a, s));
 }
 
 int launch_rpbh_lloydmax(const void *X, int x_bf16, int64_t T, int K, int block,

@@ -26,14 +26,16 @@ def device_x(inp, device):
 def rotation_for(w, inp) -> rq.Rotation:
     if w.rot == "rpbh":
         return rq.Rotation.rpbh(inp["sign"], inp["perm"], w.block)
+    if w.rot == "trdq":
+        return rq.Rotation.trdq(inp["m"], inp["R1"], inp["perm"], inp["R2"], w.block)
     return rq.Rotation.dense(inp["R"], w.r)
 
 
 def quant_for(w) -> rq.Quant:
-    if w.quant == "int4":
-        return rq.Quant.int4()
-    if w.quant == "int4_asym":
-        return rq.Quant.int4_asym()
+    if w.quant in ("int4", "int4_asym"):
+        return rq.Quant.integer(w.a_bits, w.w_bits, asym=w.quant == "int4_asym")
+    if w.quant == "mxfp4":
+        return rq.Quant.mxfp4()
     return rq.Quant.lloydmax(rq.lloydmax_gaussian(16), rq.lloydmax_gaussian(1 << w.w_bits))
 
 
@@ -42,9 +44,10 @@ class QuantLinear:
     inputs): rotation, packed weights, buffers.
 
     codes: which activation-code layouts rq_rotate_quant writes and
-    rq_w4a4_linear reads -- "canonical" (nibbles), "mma" (the GEMM's FP6
-    fragment layout only; RPBH INT4 layers) or "both" (writes both, the GEMM
-    reads the MMA copy)."""
+    rq_w4a4_linear reads -- "canonical" (nibbles or bytes), "mma" (the GEMM's
+    matrix-core layout only; RPBH layers with 4-bit integer codes or MXFP4)
+    or "both" (writes both, the GEMM reads the MMA copy).  MXFP4 layers
+    always write the MMA copy, which their GEMM reads."""
 
     def __init__(self, w, inp: dict, device="cuda", y_dtype=None, codes="canonical"):
         torch = torch_mod()
@@ -56,18 +59,23 @@ class QuantLinear:
         self.drot = self.rot.to_device(device)
         self.X = device_x(inp, device)
         T = w.T
-        ncode = (w.Kq // 2)
-        mma_ok = w.rot == "rpbh" and w.quant in ("int4", "int4_asym")
+        mma_ok = w.rot == "rpbh" and ((w.quant in ("int4", "int4_asym") and w.a_bits == 4) or
+                                      w.quant == "mxfp4")
         if codes not in ("canonical", "mma", "both") or (codes != "canonical" and not mma_ok):
             raise ValueError(f"codes={codes!r} is not available for {w.name}")
-        self.codes = (torch.empty((T, ncode), dtype=torch.uint8, device=device)
+        if w.quant == "mxfp4" and codes == "canonical":
+            codes = "both"
+        ncode, nscale, nmma = rq.activation_bytes(self.rot, self.q, T)
+        self.codes = (torch.empty((T, ncode // max(T, 1)), dtype=torch.uint8, device=device)
                       if codes != "mma" else None)
         self.codes_mma = None
         if codes != "canonical":
-            nb = rq.codes_mma_bytes(self.rot, T)
-            self.codes_mma = torch.empty((max(nb, 16),), dtype=torch.uint8, device=device)
-        # INT4_ASYM: s [T] then the zero points [T]
-        self.scale = torch.empty((self.q.scale_rows * T,), dtype=torch.float32, device=device)
+            self.codes_mma = torch.empty((max(nmma, 16),), dtype=torch.uint8, device=device)
+        if w.quant == "mxfp4":   # E8M0 codes [T][K/32]
+            self.scale = (torch.empty((T, w.K // 32), dtype=torch.uint8, device=device)
+                          if codes != "mma" else None)
+        else:                    # fp32 s [T] (and z [T] for asymmetric codes)
+            self.scale = torch.empty((self.q.scale_rows * T,), dtype=torch.float32, device=device)
         self.top = torch.empty((T, w.r), dtype=torch.int16, device=device) if w.r else None
         wsb = rq.rotate_quant_workspace_bytes(self.rot, self.q, T)
         self.ws = torch.empty((max(wsb, 16) // 4,), dtype=torch.float32, device=device) if wsb else None

@@ -20,8 +20,8 @@ LIB_PATH = os.path.join(_HERE, "librq.so")
 
 RQ_OK = 0
 RQ_F32, RQ_BF16, RQ_I32 = 0, 1, 2
-RQ_ROT_RPBH, RQ_ROT_DENSE = 0, 1
-RQ_Q_INT4_SYM, RQ_Q_LLOYDMAX, RQ_Q_INT4_ASYM = 0, 1, 2
+RQ_ROT_RPBH, RQ_ROT_DENSE, RQ_ROT_TRDQ = 0, 1, 2
+RQ_Q_INT4_SYM, RQ_Q_LLOYDMAX, RQ_Q_INT4_ASYM, RQ_Q_MXFP4 = 0, 1, 2, 3
 RQ_ENGINE_AUTO, RQ_ENGINE_FP6, RQ_ENGINE_INT8 = 0, 1, 2
 ENGINES = {"auto": RQ_ENGINE_AUTO, "fp6": RQ_ENGINE_FP6, "int8": RQ_ENGINE_INT8}
 RQ_WEIGHT_MAGIC = 0x31575152
@@ -39,7 +39,7 @@ class RQError(RuntimeError):
 class c_rotation(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("K", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("r", ctypes.c_int32), ("sign", ctypes.c_void_p), ("perm", ctypes.c_void_p),
-                ("R", ctypes.c_void_p)]
+                ("R", ctypes.c_void_p), ("smooth", ctypes.c_void_p), ("R2", ctypes.c_void_p)]
 
 
 class c_quant(ctypes.Structure):
@@ -57,7 +57,8 @@ class c_weight_header(ctypes.Structure):
                 ("total_bytes", ctypes.c_int64), ("a_levels", ctypes.c_float * 16),
                 ("w_levels", ctypes.c_float * 16), ("wsum_offset", ctypes.c_int64),
                 ("mma_offset", ctypes.c_int64), ("mma_stages", ctypes.c_int32),
-                ("mma_ntiles", ctypes.c_int32), ("reserved", ctypes.c_uint8 * 40)]
+                ("mma_ntiles", ctypes.c_int32), ("i8_offset", ctypes.c_int64),
+                ("mxs_offset", ctypes.c_int64), ("reserved", ctypes.c_uint8 * 24)]
 
 
 assert ctypes.sizeof(c_weight_header) == 256
@@ -66,7 +67,7 @@ assert ctypes.sizeof(c_weight_header) == 256
 EXPORTS = ("rq_version", "rq_last_error", "rq_lloydmax_gaussian", "rq_packed_weight_bytes",
            "rq_pack_weights", "rq_rotate_quant_workspace_bytes", "rq_codes_mma_bytes",
            "rq_rotate_quant", "rq_w4a4_linear", "rq_w4a4_linear_engine",
-           "rq_rotate_quant_noalloc")
+           "rq_rotate_quant_noalloc", "rq_activation_bytes")
 
 _lib = None
 
@@ -93,9 +94,12 @@ def load() -> ctypes.CDLL:
     L.rq_w4a4_linear.argtypes = [P, P, P, P, P, P, I64, P, P, I32, P]
     L.rq_w4a4_linear_engine.argtypes = [P, P, P, P, P, P, I64, P, P, I32, I32, P]
     L.rq_rotate_quant_noalloc.argtypes = [P, P, P, I32, I64, P, P, P, P, P]
+    L.rq_activation_bytes.argtypes = [P, P, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ),
+                                      ctypes.POINTER(SZ)]
     for name in ("rq_lloydmax_gaussian", "rq_packed_weight_bytes", "rq_pack_weights",
                  "rq_rotate_quant_workspace_bytes", "rq_codes_mma_bytes", "rq_rotate_quant",
-                 "rq_w4a4_linear", "rq_w4a4_linear_engine", "rq_rotate_quant_noalloc"):
+                 "rq_w4a4_linear", "rq_w4a4_linear_engine", "rq_rotate_quant_noalloc",
+                 "rq_activation_bytes"):
         getattr(L, name).restype = I32
     _lib = L
     return L
@@ -143,6 +147,8 @@ class Rotation:
     sign: Optional[np.ndarray] = None
     perm: Optional[np.ndarray] = None
     R: Optional[np.ndarray] = None
+    smooth: Optional[np.ndarray] = None
+    R2: Optional[np.ndarray] = None
 
     @staticmethod
     def rpbh(sign, perm, block):
@@ -155,20 +161,27 @@ class Rotation:
         R = np.ascontiguousarray(R, np.float32)
         return Rotation(RQ_ROT_DENSE, int(R.shape[0]), 0, int(r), None, None, R)
 
+    @staticmethod
+    def trdq(smooth, R1, perm, R2, block):
+        """TR-DQ: smoothing multiplier [K], block rotations R1, R2 [K/b][b][b],
+        zigzag permutation [K] (a gather)."""
+        smooth = np.ascontiguousarray(smooth, np.float32)
+        return Rotation(RQ_ROT_TRDQ, int(smooth.size), int(block), 0, None,
+                        np.ascontiguousarray(perm, np.int32), np.ascontiguousarray(R1, np.float32),
+                        smooth, np.ascontiguousarray(R2, np.float32))
+
     def c_host(self) -> c_rotation:
-        return c_rotation(self.kind, self.K, self.block, self.r,
-                          None if self.sign is None else self.sign.ctypes.data,
-                          None if self.perm is None else self.perm.ctypes.data,
-                          None if self.R is None else self.R.ctypes.data)
+        ptr = (lambda a: None if a is None else a.ctypes.data)
+        return c_rotation(self.kind, self.K, self.block, self.r, ptr(self.sign), ptr(self.perm),
+                          ptr(self.R), ptr(self.smooth), ptr(self.R2))
 
     def to_device(self, device="cuda") -> "DeviceRotation":
         import torch
         d = DeviceRotation(self)
-        if self.sign is not None:
-            d.sign = torch.from_numpy(self.sign).to(device)
-            d.perm = torch.from_numpy(self.perm).to(device)
-        if self.R is not None:
-            d.R = torch.from_numpy(self.R).to(device)
+        for name in ("sign", "perm", "R", "smooth", "R2"):
+            a = getattr(self, name)
+            if a is not None:
+                setattr(d, name, torch.from_numpy(a).to(device))
         return d
 
 
@@ -178,13 +191,14 @@ class DeviceRotation:
     sign: object = None
     perm: object = None
     R: object = None
+    smooth: object = None
+    R2: object = None
 
     def c_dev(self) -> c_rotation:
         h = self.host
-        return c_rotation(h.kind, h.K, h.block, h.r,
-                          None if self.sign is None else self.sign.data_ptr(),
-                          None if self.perm is None else self.perm.data_ptr(),
-                          None if self.R is None else self.R.data_ptr())
+        ptr = (lambda t: None if t is None else t.data_ptr())
+        return c_rotation(h.kind, h.K, h.block, h.r, ptr(self.sign), ptr(self.perm), ptr(self.R),
+                          ptr(self.smooth), ptr(self.R2))
 
 
 @dataclass
@@ -203,6 +217,17 @@ class Quant:
     def int4_asym():
         """Asymmetric per-token INT4 activations (zero point), INT4 weights."""
         return Quant(RQ_Q_INT4_ASYM, 4, 4)
+
+    @staticmethod
+    def integer(a_bits, w_bits, asym=False):
+        """Integer activations of a_bits (4 or 8, zero point if asym) and
+        symmetric weights of w_bits (W4A4, W4A8, W8A8)."""
+        return Quant(RQ_Q_INT4_ASYM if asym else RQ_Q_INT4_SYM, a_bits, w_bits)
+
+    @staticmethod
+    def mxfp4():
+        """MXFP4: E2M1 elements, one E8M0 scale per 32 coordinates."""
+        return Quant(RQ_Q_MXFP4, 4, 4)
 
     @property
     def scale_rows(self) -> int:
@@ -273,6 +298,16 @@ class PackedWeights:
         h = self.header
         return self.blob[h.wsum_offset:h.wsum_offset + 4 * h.N].view(np.int32)
 
+    def mx_scales(self) -> np.ndarray:
+        """MXFP4: the E8M0 codes, uint8 [N][K/32]."""
+        h = self.header
+        return self.blob[h.scale_offset:h.scale_offset + h.N * (h.K // 32)].reshape(h.N, h.K // 32)
+
+    def i8_codes(self) -> np.ndarray:
+        """INT with 8-bit activations: the int8 weight codes [N][K]."""
+        h = self.header
+        return self.blob[h.i8_offset:h.i8_offset + h.N * h.K].view(np.int8).reshape(h.N, h.K)
+
     def mma_tiles(self) -> np.ndarray:
         """INT4: the GEMM's FP6 fragments, uint8 [ntiles][stages][3][64][16]."""
         h = self.header
@@ -321,6 +356,15 @@ def rotate_quant_workspace_bytes(rot: Rotation, q: Quant, T: int) -> int:
     return n.value
 
 
+def activation_bytes(rot: Rotation, q: Quant, T: int):
+    """(codes, scale, codes_mma) byte counts of the activation buffers."""
+    c, sc, m = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+    cr, cq = rot.c_host(), q.c()
+    _check(load().rq_activation_bytes(ctypes.byref(cr), ctypes.byref(cq), T, ctypes.byref(c),
+                                      ctypes.byref(sc), ctypes.byref(m)))
+    return c.value, sc.value, m.value
+
+
 def dtype_code(t) -> int:
     import torch
     return {torch.float32: RQ_F32, torch.bfloat16: RQ_BF16, torch.int16: RQ_BF16,
@@ -342,6 +386,7 @@ def rotate_quant(drot: DeviceRotation, q: Quant, X, codes, scale, top=None, work
     cr, cq = drot.c_dev(), q.c()
     T = int(X.shape[0])
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    # (MXFP4: scale is a uint8 tensor of E8M0 codes, passed as a pointer)
     _check(load().rq_rotate_quant(ctypes.byref(cr), ctypes.byref(cq), _t_ptr(X), dtype_code(X), T,
                                   _t_ptr(codes), _t_ptr(scale), _t_ptr(top), _t_ptr(codes_mma),
                                   _t_ptr(workspace), ws_bytes, _stream(stream)))

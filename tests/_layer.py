@@ -19,28 +19,41 @@ from rotated_w4a4_quantized_amd.layer import (QuantLinear as GpuLayer, device_x,
 REL_TOL = 1e-3
 
 
+def _rot_args(w, inp):
+    if w.rot == "rpbh":
+        return dict(rot_kind=0, b=w.block, sign=inp["sign"], perm=inp["perm"])
+    if w.rot == "trdq":
+        return dict(rot_kind=2, b=w.block, m=inp["m"], R=inp["R1"], perm=inp["perm"], R2=inp["R2"])
+    return dict(rot_kind=1, R=inp["R"])
+
+
 def oracle_act(w, inp, rows=None):
     rows = np.arange(w.T) if rows is None else np.asarray(rows)
     xd = 0 if w.xdtype == "f32" else 1
-    if w.rot == "rpbh":
-        if w.quant == "int4":
-            return orc.act_rows(inp["X"], xd, w.K, rows, rot_kind=0, b=w.block, sign=inp["sign"],
-                                perm=inp["perm"])
-        if w.quant == "int4_asym":
-            return orc.act_rows(inp["X"], xd, w.K, rows, rot_kind=0, b=w.block, sign=inp["sign"],
-                                perm=inp["perm"], q_kind=2)
-        return orc.act_rows(inp["X"], xd, w.K, rows, rot_kind=0, b=w.block, sign=inp["sign"],
-                            perm=inp["perm"], q_kind=1, levels=orc.codebook_bf16(16))
-    return orc.act_rows(inp["X"], xd, w.K, rows, rot_kind=1, R=inp["R"], r=w.r)
+    ra = _rot_args(w, inp)
+    if w.quant == "int4":
+        return orc.act_rows(inp["X"], xd, w.K, rows, r=w.r, a_bits=w.a_bits, **ra)
+    if w.quant == "int4_asym":
+        return orc.act_rows(inp["X"], xd, w.K, rows, q_kind=2, a_bits=w.a_bits, **ra)
+    if w.quant == "mxfp4":
+        return orc.act_rows(inp["X"], xd, w.K, rows, q_kind=3, **ra)
+    return orc.act_rows(inp["X"], xd, w.K, rows, q_kind=1, levels=orc.codebook_bf16(16), **ra)
 
 
 def oracle_weights(w, inp):
-    if w.rot == "rpbh":
-        if w.quant in ("int4", "int4_asym"):   # INT4 weights are symmetric either way
-            return orc.weight_rows(inp["W"], rot_kind=0, b=w.block, sign=inp["sign"], perm=inp["perm"])
-        return orc.weight_rows(inp["W"], rot_kind=0, b=w.block, sign=inp["sign"], perm=inp["perm"],
-                               q_kind=1, levels=orc.codebook_bf16(1 << w.w_bits))
-    return orc.weight_rows(inp["W"], rot_kind=1, R=inp["R"])
+    ra = _rot_args(w, inp)
+    if w.quant in ("int4", "int4_asym"):   # integer weights are symmetric either way
+        return orc.weight_rows(inp["W"], w_bits=w.w_bits, **ra)
+    if w.quant == "mxfp4":
+        return orc.weight_rows(inp["W"], q_kind=3, **ra)
+    return orc.weight_rows(inp["W"], q_kind=1, levels=orc.codebook_bf16(1 << w.w_bits), **ra)
+
+
+def _acc_pairs(w, act, wts, ia, nw):
+    """Exact integer accumulators sum_k code_a code_w at pairs (codes as stored:
+    asymmetric activation codes unsigned)."""
+    return orc.gemm_codes_pairs(act["codes"], w.a_bits, w.quant == "int4", w.Kq, wts["codes"],
+                                w.w_bits, w.K, ia, nw, koff=w.r)
 
 
 def oracle_yhat_pairs(w, act, wts, ta, nw, act_rows=None):
@@ -51,12 +64,16 @@ def oracle_yhat_pairs(w, act, wts, ta, nw, act_rows=None):
         dot = orc.codebook_dot_pairs(act["codes"], wts["codes"], w.K, orc.codebook_bf16(16),
                                      orc.codebook_bf16(1 << w.w_bits), ia, nw)
         return orc.yhat_codebook(act["scale"][ia], wts["scale"][nw], dot, w.block)
+    if w.quant == "mxfp4":
+        dot = orc.mx_dot_pairs(act["codes"], act["mx_scales"], wts["codes"], wts["mx_scales"], w.K,
+                               ia, nw)
+        return orc.yhat_mx(dot, w.b_eff)
     if w.quant == "int4_asym":
-        acc_u = orc.asym_gemm_pairs(act["codes"], wts["codes"], w.K, ia, nw)
+        acc_u = _acc_pairs(w, act, wts, ia, nw)
         wsum = wts["q"].astype(np.int64).sum(axis=1)
         return orc.yhat_int4_asym(act["scale"][ia], act["zero"][ia], wts["scale"][nw], acc_u,
                                   wsum[nw], w.b_eff)
-    acc = orc.int_gemm_pairs(act["codes"], w.Kq, wts["codes"], w.K, ia, nw, koff=w.r)
+    acc = _acc_pairs(w, act, wts, ia, nw)
     lr = None
     if w.r:
         lr = orc.lowrank_pairs(act["top"], w.r, wts["codes"], w.K, ia, nw)
@@ -66,13 +83,13 @@ def oracle_yhat_pairs(w, act, wts, ta, nw, act_rows=None):
 def oracle_raw_acc(w, act, wts):
     """Exact int64 accumulators [T][N] that RQ_I32 output returns:
     sum_k q_a q_w, with q_a = u - z for asymmetric activations."""
+    T, N = act["codes"].shape[0], wts["codes"].shape[0]
+    ta, nw = np.meshgrid(np.arange(T), np.arange(N), indexing="ij")
+    acc = _acc_pairs(w, act, wts, ta.ravel(), nw.ravel()).reshape(T, N)
     if w.quant == "int4_asym":
-        T, N = act["codes"].shape[0], wts["codes"].shape[0]
-        ta, nw = np.meshgrid(np.arange(T), np.arange(N), indexing="ij")
-        acc_u = orc.asym_gemm_pairs(act["codes"], wts["codes"], w.K, ta.ravel(), nw.ravel())
         wsum = wts["q"].astype(np.int64).sum(axis=1)
-        return acc_u.reshape(T, N) - act["zero"].astype(np.int64)[:, None] * wsum[None, :]
-    return orc.int_gemm(act["codes"], w.Kq, wts["codes"], w.K, koff=w.r)
+        return acc - act["zero"].astype(np.int64)[:, None] * wsum[None, :]
+    return acc
 
 
 def rel_err(y, yhat):

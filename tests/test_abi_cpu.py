@@ -37,10 +37,28 @@ def test_library_exports_every_declared_symbol():
     assert rq.version() >= 100
 
 
-def test_struct_sizes_match_header():
+def test_struct_sizes_match_header(tmp_path):
+    """The binding's ctypes structs lay out exactly as the C compiler lays out
+    include/rq.h's (sizes and every field offset, from a compiled probe)."""
     assert ctypes.sizeof(rq.c_weight_header) == 256
-    assert ctypes.sizeof(rq.c_quant) == 16 + 128
-    assert ctypes.sizeof(rq.c_rotation) == 16 + 24
+    structs = {"rq_rotation": rq.c_rotation, "rq_quant": rq.c_quant,
+               "rq_weight_header": rq.c_weight_header}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "rq.h"', 'int main(void) {']
+    for cname, ct in structs.items():
+        lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
+        for fname, _ in ct._fields_:
+            lines.append(f'printf("{cname}.{fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ["return 0;", "}"]
+    src = tmp_path / "probe.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "probe"
+    import subprocess
+    subprocess.check_call(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    got = dict(l.split() for l in subprocess.check_output([str(exe)]).decode().splitlines())
+    for cname, ct in structs.items():
+        assert int(got[cname]) == ctypes.sizeof(ct), cname
+        for fname, _ in ct._fields_:
+            assert int(got[f"{cname}.{fname}"]) == getattr(ct, fname).offset, (cname, fname)
 
 
 def _status(fn, *args):
@@ -61,7 +79,7 @@ def _rq_call(rot: rq.c_rotation, q: rq.c_quant, X=1 << 20, xdt=rq.RQ_BF16, T=4, 
 def _rpbh(K=256, b=64):
     # pointer values only: every call below is rejected (or returns for T == 0)
     # before any pointer is dereferenced or any HIP call is made
-    return rq.c_rotation(rq.RQ_ROT_RPBH, K, b, 0, 1 << 20, 1 << 21, None)
+    return rq.c_rotation(rq.RQ_ROT_RPBH, K, b, 0, 1 << 20, 1 << 21, None, None, None)
 
 
 def test_rotate_quant_validation_errors():
@@ -366,3 +384,91 @@ def test_int4_asym_descriptor_and_blob():
     rd = rq.Rotation.dense(np.eye(512, dtype=np.float32), 0)
     assert rq.load().rq_packed_weight_bytes(ctypes.byref(rd.c_host()), ctypes.byref(qa), 40,
                                             ctypes.byref(n)) == -6
+
+
+# ---------------------------------------------------------------------------
+# the further formats: MXFP4, 8-bit integer weights, the TR-DQ fold
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,shape", [("flux_up_mxfp4", dict(K=1024, N=70)),
+                                        ("flux_down_mxfp4", dict(K=2048, N=33)),
+                                        ("tiny", dict(K=256, N=40, block=64))])
+def test_pack_mxfp4_matches_oracle(name, shape):
+    """Weight fold + MXFP4 (E2M1 codes, E8M0 block scales) equal the oracle
+    bit for bit; the GEMM's tiled copies hold the same codes and scales."""
+    w = datagen.WORKLOADS[name].with_shape(T=4, **shape)
+    inp = datagen.make_inputs(w)
+    pw = rq.pack_weights(rq.Rotation.rpbh(inp["sign"], inp["perm"], w.block), rq.Quant.mxfp4(),
+                         inp["W"])
+    ref = orc.weight_rows(inp["W"], rot_kind=0, b=w.block, sign=inp["sign"], perm=inp["perm"],
+                          q_kind=3)
+    assert np.array_equal(pw.codes(), ref["codes"])
+    assert np.array_equal(pw.mx_scales(), ref["mx_scales"])
+    h = pw.header
+    assert (h.format, h.b_div, h.row_bytes, h.mma_stages, h.mma_ntiles) == (
+        rq.RQ_Q_MXFP4, w.block, w.K // 2, w.K // 128, -(-w.N // 32))
+    nch = w.K // 32
+    tiles = pw.blob[h.mma_offset:h.mma_offset + h.mma_ntiles * nch * 512].reshape(h.mma_ntiles, nch, 32, 16)
+    codes = tiles.transpose(0, 2, 1, 3).reshape(h.mma_ntiles * 32, nch * 16)[:w.N]
+    assert np.array_equal(codes, ref["codes"])
+    sc = pw.blob[h.mxs_offset:h.mxs_offset + h.mma_stages * h.mma_ntiles * 128]
+    sc = sc.reshape(h.mma_stages, h.mma_ntiles, 2, 32, 2)           # [s][tile][h][row][ks]
+    full = sc.transpose(1, 3, 0, 4, 2).reshape(h.mma_ntiles * 32, nch)   # chunk 4 s + 2 ks + h
+    assert np.array_equal(full[:w.N], ref["mx_scales"])
+
+
+@pytest.mark.parametrize("name,shape", [("flux_up_w4a8", dict(K=512, N=40)),
+                                        ("flux_up_w8a8", dict(K=512, N=40)),
+                                        ("flux_up_trdq", dict(K=512, N=40)),
+                                        ("flux_up_trdq", dict(K=256, N=24, w_bits=8))])
+def test_pack_int8_paths_match_oracle(name, shape):
+    """8-bit weights and the int8 copy of 4-bit weights that the int8 GEMM
+    reads; the TR-DQ fold (smoothing, R1, zigzag, R2 in fp64)."""
+    w = datagen.WORKLOADS[name].with_shape(T=4, **shape)
+    inp = datagen.make_inputs(w)
+    from rotated_w4a4_quantized_amd.layer import quant_for, rotation_for
+    pw = rq.pack_weights(rotation_for(w, inp), quant_for(w), inp["W"])
+    from tests import _layer as H
+    ref = H.oracle_weights(w, inp)
+    assert np.array_equal(pw.codes(), ref["codes"])
+    assert np.array_equal(pw.scales().view(np.uint32), ref["scale"].view(np.uint32))
+    h = pw.header
+    assert (h.a_bits, h.w_bits, h.b_div) == (w.a_bits, w.w_bits, w.b_eff)
+    assert np.array_equal(pw.i8_codes().astype(np.int16), ref["q"])
+    assert np.array_equal(pw.wsum(), ref["q"].astype(np.int64).sum(axis=1))
+
+
+def test_new_format_validation_errors():
+    L = rq.load()
+    K = 256
+    mx = rq.Quant.mxfp4().c()
+    # MXFP4 needs K % 128 == 0 and the RPBH rotation
+    assert _rq_call(rq.c_rotation(rq.RQ_ROT_RPBH, 160, 32, 0, 1 << 20, 1 << 21, None), mx) == -2
+    dense = rq.c_rotation(rq.RQ_ROT_DENSE, K, 0, 0, None, None, 1 << 22)
+    assert _rq_call(dense, mx) == -6
+    # 8-bit activations: not with the dense path; a_bits / w_bits values
+    assert _rq_call(dense, rq.Quant.integer(8, 4).c()) == -6
+    assert _rq_call(_rpbh(), rq.c_quant(0, 6, 4, 0)) == -6
+    assert _rq_call(_rpbh(), rq.c_quant(0, 4, 8, 0)) == -6
+    # TR-DQ: block range, tables
+    td = rq.c_rotation(rq.RQ_ROT_TRDQ, K, 8, 0, None, 1 << 21, 1 << 22, 1 << 23, 1 << 24)
+    assert _rq_call(td, rq.Quant.integer(8, 4).c()) == -2
+    td = rq.c_rotation(rq.RQ_ROT_TRDQ, K, 64, 0, None, 1 << 21, 1 << 22, None, 1 << 24)
+    assert _rq_call(td, rq.Quant.integer(8, 4).c()) == -1
+    td = rq.c_rotation(rq.RQ_ROT_TRDQ, K, 64, 0, None, 1 << 21, 1 << 22, 1 << 23, 1 << 24)
+    assert _rq_call(td, mx) == -6
+    # activation sizes
+    rot = rq.Rotation.rpbh(np.ones(K, np.int8), np.arange(K, dtype=np.int32), 64)
+    assert rq.activation_bytes(rot, rq.Quant.mxfp4(), 40) == (40 * K // 2, 40 * K // 32,
+                                                             2 * (K // 32) * 512 + (K // 128) * 2 * 128)
+    assert rq.activation_bytes(rot, rq.Quant.integer(8, 4, asym=True), 40) == (40 * K, 80 * 4, 0)
+    # the MXFP4 GEMM reads the tiled codes: canonical codes alone are refused
+    w = datagen.WORKLOADS["flux_up_mxfp4"].with_shape(T=4, K=K, N=40, block=64)
+    inp = datagen.make_inputs(w)
+    h = rq.pack_weights(rq.Rotation.rpbh(inp["sign"], inp["perm"], 64), rq.Quant.mxfp4(), inp["W"]).header
+    assert L.rq_w4a4_linear(ctypes.byref(h), ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 21),
+                            ctypes.c_void_p(1 << 22), None, None, 4, None, ctypes.c_void_p(1 << 24),
+                            rq.RQ_F32, None) == -6
+    assert L.rq_w4a4_linear(ctypes.byref(h), ctypes.c_void_p(1 << 20), None, None, None,
+                            ctypes.c_void_p(1 << 23), 4, None, ctypes.c_void_p(1 << 24),
+                            rq.RQ_I32, None) == -6

@@ -34,12 +34,39 @@ def say(msg):
 
 
 def mma_mode(w):
-    """Layer mode for the parity runs: RPBH INT4 layers write both code
-    layouts and the GEMM reads the MMA copy."""
-    return "both" if (w.rot == "rpbh" and w.quant in ("int4", "int4_asym")) else "canonical"
+    """Layer mode for the parity runs: RPBH layers with 4-bit integer codes or
+    MXFP4 write both code layouts and the GEMM reads the MMA copy."""
+    mma = w.rot == "rpbh" and ((w.quant in ("int4", "int4_asym") and w.a_bits == 4) or
+                               w.quant == "mxfp4")
+    return "both" if mma else "canonical"
+
+
+def check_act_mx(w, L, act, rows=None):
+    """MXFP4: canonical E2M1 codes and E8M0 scales, and the tiled copies the
+    GEMM reads, bit for bit."""
+    codes = L.codes.cpu().numpy()
+    sc = L.scale.cpu().numpy()
+    nch = w.K // 32
+    tiles = -(-w.T // 32)
+    buf = L.codes_mma.cpu().numpy()
+    tc = buf[:tiles * nch * 512].reshape(tiles, nch, 32, 16).transpose(0, 2, 1, 3)
+    tc = tc.reshape(tiles * 32, nch * 16)[:w.T]
+    S = w.K // 128
+    ts = buf[tiles * nch * 512:tiles * nch * 512 + S * tiles * 128].reshape(S, tiles, 2, 32, 2)
+    ts = ts.transpose(1, 3, 0, 4, 2).reshape(tiles * 32, nch)[:w.T]
+    if rows is not None:
+        codes, sc, tc, ts = codes[rows], sc[rows], tc[rows], ts[rows]
+    for name, got in (("codes", codes), ("tiled codes", tc)):
+        bad = np.nonzero(np.any(got != act["codes"], axis=1))[0]
+        assert bad.size == 0, f"MXFP4 {name} differ in {bad.size} tokens, first {bad[:5]}"
+    for name, got in (("scales", sc), ("tiled scales", ts)):
+        bad = np.nonzero(np.any(got != act["mx_scales"], axis=1))[0]
+        assert bad.size == 0, f"MXFP4 {name} differ in {bad.size} tokens, first {bad[:5]}"
 
 
 def check_act(w, L, act, rows=None):
+    if w.quant == "mxfp4":
+        return check_act_mx(w, L, act, rows)
     codes = L.codes.cpu().numpy()
     scale = L.scale.cpu().numpy()
     asym = w.quant == "int4_asym"
@@ -74,6 +101,23 @@ def check_act(w, L, act, rows=None):
 
 
 SMALL = [
+    # MXFP4 (E2M1 + E8M0 per 32), 8-bit activations (W4A8, W8A8, asymmetric),
+    # and the TR-DQ rotation
+    ("flux_up_mxfp4", dict(T=257, K=3072, N=384)),
+    ("flux_down_mxfp4", dict(T=131, K=12288, N=136)),
+    ("flux_up_mxfp4", dict(T=40, K=256, N=300, block=64)),
+    ("flux_up_mxfp4", dict(T=70, K=1024, N=128, block=1024)),
+    ("flux_up_mxfp4", dict(T=33, K=128, N=40, block=2)),
+    ("flux_up_mxfp4", dict(T=65, K=512, N=64, block=32)),
+    ("flux_up_w4a8", dict(T=257, K=3072, N=384)),
+    ("flux_up_w8a8", dict(T=257, K=3072, N=384)),
+    ("flux_up_w4a8", dict(T=33, K=96, N=40, block=2)),
+    ("flux_up_w8a8", dict(T=45, K=64, N=48, block=64)),
+    ("flux_up_trdq", dict(T=70, K=1024, N=136)),
+    ("flux_up_trdq", dict(T=33, K=512, N=40, block=16)),
+    ("flux_up_trdq", dict(T=20, K=8192, N=64, block=256)),
+    ("flux_up_trdq", dict(T=9, K=16384, N=40, block=64)),
+
     ("tiny", dict(T=300, N=200)),
     ("tiny", dict(T=1, N=130, K=256, block=256)),
     ("flux_up", dict(T=257, K=3072, N=384)),
@@ -131,7 +175,7 @@ def small_parity(w, inp):
         ref = H.oracle_raw_acc(w, act, wts)
         acc = L.raw_acc().cpu().numpy().astype(np.int64)
         assert np.array_equal(acc, ref)
-        if L.codes_mma is not None:
+        if L.codes_mma is not None and L.codes is not None:
             # the same accumulators from the canonical codes (converted in the GEMM)
             acc = L.raw_acc(use_mma=False).cpu().numpy().astype(np.int64)
             assert np.array_equal(acc, ref)
@@ -148,7 +192,8 @@ def small_parity(w, inp):
     assert ok
 
 
-FULL = ["tiny", "flux_up", "flux_down", "video", "pixart", "flux_up_asym", "flux_down_asym", "video_w4"]
+FULL = ["tiny", "flux_up", "flux_down", "video", "pixart", "flux_up_asym", "flux_down_asym", "video_w4",
+        "flux_up_mxfp4", "flux_down_mxfp4", "flux_up_w4a8", "flux_up_w8a8", "flux_up_trdq"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -161,7 +206,7 @@ def test_full_workload_parity(name):
     torch.cuda.synchronize()
     g = np.random.default_rng(7)
     # every code and scale for the RPBH paths; a token sample for the dense
-    # path, whose oracle rotation is a K x K fp32 chain per token
+    # and TR-DQ paths, whose oracle rotations are fp32 chains per coordinate
     rows = None if w.rot == "rpbh" else np.sort(g.choice(w.T, 512, replace=False))
     act = H.oracle_act(w, inp, rows)
     check_act(w, L, act, rows)
@@ -187,7 +232,7 @@ def test_full_workload_parity(name):
         # the sampled pairs
         acc = L.raw_acc().view(-1)[idx].cpu().numpy().astype(np.int64)
         ia = ta if rows is None else np.searchsorted(rows, ta)
-        ref = H.orc.int_gemm_pairs(act["codes"], w.Kq, wts["codes"], w.K, ia, nw, koff=w.r)
+        ref = H._acc_pairs(w, act, wts, ia, nw)
         assert np.array_equal(acc, ref), f"accumulators differ at {int(np.sum(acc != ref))} pairs"
         say(f"  int32 accumulators bit-exact at {ta.size} pairs")
     if w.ydtype == "f32":
