@@ -19,8 +19,18 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
   ms_per_step    wall time per step (host clock around K synchronized steps)
   roofline       the dominant kernel (the GEMM), from HIP events on the
                  launch stream: algorithmic ops per launch / mean duration,
-                 against the int8 MFMA peak
-  cpu_baseline   the CPU oracle on a bounded sample of the same workload
+                 against the peak of the matrix cores it runs on (FP6 / FP4:
+                 10.1 POP/s, int8: 5.0, bf16: 2.5 PFLOP/s)
+  roofline_rotate_quant  the activation kernel: algorithmic bytes / time
+                 against HBM (RPBH), or fp32 FMA flops against the
+                 non-packed fp32 rate (dense and TR-DQ rotations)
+  sclk_mhz       shader clock sampled with rocm-smi while the steps run
+  cpu_baseline   the CPU oracle on a bounded sample of the same workload,
+                 on all host threads and on one
+
+Other workloads (--workload): tiny, pixart, video, video_w4, flux_asym,
+flux_mxfp4 (the FP4 variant), flux_up_w4a8 / flux_up_w8a8 (8-bit
+activations), flux_up_trdq (TR-DQ's rotation, W4A8).
 """
 from __future__ import annotations
 
@@ -44,13 +54,20 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 WORKLOADS = {
     "flux": ["flux_up", "flux_down"],
     "flux_asym": ["flux_up_asym", "flux_down_asym"],
+    "flux_mxfp4": ["flux_up_mxfp4", "flux_down_mxfp4"],
     "flux_up": ["flux_up"],
     "flux_down": ["flux_down"],
+    "flux_up_w4a8": ["flux_up_w4a8"],
+    "flux_up_w8a8": ["flux_up_w8a8"],
+    "flux_up_trdq": ["flux_up_trdq"],
     "tiny": ["tiny"],
     "pixart": ["pixart"],
     "video": ["video"],
     "video_w4": ["video_w4"],
 }
+# non-packed fp32 fused multiply-add rate: 256 CUs x 64 lanes x 2 flops x 2.4 GHz
+# (the chip's 157.3 TFLOP/s counts packed fp32, which this build does not emit)
+PEAK_FP32_FMA_TFLOPS = 78.6
 
 
 def log(*a):
@@ -83,7 +100,9 @@ PMC_KERNELS = {
     "gemm": ("rq_gemm_fp6.hip", "gemm_fp6_mma_kernel"),
     "gemm_int8": ("rq_gemm_w4a4.hip", "gemm_w4a4_kernel"),
     "gemm_codebook": ("rq_gemm_codebook.hip", "gemm_codebook_kernel"),
+    "gemm_mx": ("rq_gemm_mx.hip", "gemm_mx_kernel"),
     "rotate": ("rq_rpbh.hip", "rpbh_quant_kernel"),
+    "trdq": ("rq_trdq.hip", "trdq_quant_kernel"),
     "dense": ("rq_dense.hip", "dense_rotate_kernel"),
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
@@ -163,9 +182,14 @@ def summarize_stats(stats_csv, workload, command):
 
 def rotate_bytes(w) -> int:
     """Algorithmic HBM bytes of one rotate+quant launch: X read, codes,
-    scales (and top) written."""
+    scales (and top) written, in the method's minimal encoding."""
     xb = 4 if w.xdtype == "f32" else 2
-    b = w.T * w.K * xb + w.T * (w.Kq // 2) + 4 * w.T
+    b = w.T * w.K * xb
+    if w.quant == "mxfp4":
+        return b + w.T * (w.K // 2) + w.T * (w.K // 32)     # E2M1 codes, E8M0 per 32
+    if w.quant == "lloydmax":
+        return b + w.T * (w.K // 2) + 4 * w.T
+    b += w.T * w.code_bytes + 4 * w.T
     if w.quant == "int4_asym":
         b += 4 * w.T   # zero points
     if w.r:
@@ -173,39 +197,81 @@ def rotate_bytes(w) -> int:
     return b
 
 
-def cpu_baseline(names, budget_s: float):
+def rotate_flops(w) -> int:
+    """Algorithmic fp32 flops of a rotation that runs as fused multiply-add
+    chains (dense: 2 T K^2; TR-DQ: two block rotations, 4 T K b)."""
+    if w.rot == "dense":
+        return 2 * w.T * w.K * w.K
+    if w.rot == "trdq":
+        return 4 * w.T * w.K * w.block
+    return 0
+
+
+def pct(a, q):
+    return float(np.percentile(a, q))
+
+
+def sample_sclk():
+    """Current shader clock (MHz) as rocm-smi reports it, or None."""
+    import re
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
+                             timeout=20).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    m = re.search(r"sclk[^\n]*?\((\d+)\s*Mhz\)", out, re.I)
+    return int(m.group(1)) if m else None
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(names, budget_s: float, threads=None):
     """Oracle layer (rotate + quantize + integer GEMM + fp64 output) on a
-    bounded token sample of each layer, scaled to TOPS."""
+    bounded token sample of each layer, scaled to TOPS.  threads: OpenMP
+    threads (None: all)."""
     from oracle import oracle as orc
     from rotated_w4a4_quantized_amd import datagen
     from tests import _layer as H
 
-    threads = orc.num_threads()
-    total_ops, total_t, parts = 0, 0.0, []
-    for name in names:
-        w = datagen.WORKLOADS[name]
-        inp = datagen.make_inputs(w)
-        t0 = time.perf_counter()
-        wts = H.oracle_weights(w, inp)        # offline fold, not part of the rate
-        log(f"[cpu_baseline] {name}: oracle weight fold {time.perf_counter() - t0:.1f}s")
-        ntok = 8
-        while True:
-            rows = np.arange(ntok)
-            t0 = time.perf_counter()
-            act = H.oracle_act(w, inp, rows)
-            ta = np.repeat(rows, w.N)
-            nw = np.tile(np.arange(w.N), ntok)
-            H.oracle_yhat_pairs(w, act, wts, ta, nw, act_rows=rows)
-            dt = time.perf_counter() - t0
-            if dt > budget_s / (4 * len(names)) or ntok >= w.T:
-                break
-            ntok = min(w.T, ntok * 4)
-        ops = 2 * ntok * w.Kq * w.N
-        total_ops += ops
-        total_t += dt
-        parts.append(f"{name}: first {ntok} tokens x all {w.N} outputs ({dt:.1f}s)")
-        log(f"[cpu_baseline] {parts[-1]}")
-    return {"value": total_ops / total_t / 1e12, "unit": "TOPS", "cores": threads,
+    prev = orc.num_threads()
+    if threads:
+        orc.set_threads(threads)
+    used = orc.num_threads()
+    try:
+        total_ops, total_t, parts = 0, 0.0, []
+        for name in names:
+            w = datagen.WORKLOADS[name]
+            inp = datagen.make_inputs(w)
+            wts = H.oracle_weights(w, inp)        # offline fold, not part of the rate
+            ntok = 2
+            while True:
+                rows = np.arange(ntok)
+                t0 = time.perf_counter()
+                act = H.oracle_act(w, inp, rows)
+                ta = np.repeat(rows, w.N)
+                nw = np.tile(np.arange(w.N), ntok)
+                H.oracle_yhat_pairs(w, act, wts, ta, nw, act_rows=rows)
+                dt = time.perf_counter() - t0
+                if dt > budget_s / (4 * len(names)) or ntok >= w.T:
+                    break
+                ntok = min(w.T, ntok * 4)
+            ops = 2 * ntok * w.Kq * w.N
+            total_ops += ops
+            total_t += dt
+            parts.append(f"{name}: first {ntok} tokens x all {w.N} outputs ({dt:.1f}s)")
+            log(f"[cpu_baseline] {used} threads, {parts[-1]}")
+    finally:
+        orc.set_threads(prev)
+    return {"value": total_ops / total_t / 1e12, "unit": "TOPS", "cores": used,
             "kind": "oracle", "sample": "; ".join(parts)}
 
 
@@ -220,6 +286,7 @@ def main():
     ap.add_argument("--ring", type=int, default=2, help="independent layer instances cycled")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sclk", action="store_true", help="skip the rocm-smi clock sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after timing, run a plain device copy of BYTES (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -250,9 +317,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     rq.load()
-    int8_gemm = args.engine == "int8"
     names = WORKLOADS[args.workload]
     wls = [datagen.WORKLOADS[n] for n in names]
+    int8_gemm = args.engine == "int8" or any(w.a_bits == 8 for w in wls)
 
     # ring of independent instances (distinct seeds), all resident in HBM
     ring = []
@@ -260,10 +327,11 @@ def main():
         layers = []
         for w in wls:
             inp = datagen.make_inputs(w, seed_offset=100 * i)
-            # RPBH INT4 layers hand the GEMM its codes in the matrix-core layout
-            mode = ("mma" if (w.rot == "rpbh" and w.quant in ("int4", "int4_asym") and not int8_gemm)
-                    else "canonical")
-            layers.append(QuantLinear(w, inp, codes=mode))
+            # RPBH layers with 4-bit integer codes or MXFP4 hand the GEMM its
+            # codes in the matrix-core layout only
+            mma = w.rot == "rpbh" and ((w.quant in ("int4", "int4_asym") and w.a_bits == 4 and
+                                        args.engine != "int8") or w.quant == "mxfp4")
+            layers.append(QuantLinear(w, inp, codes="mma" if mma else "canonical"))
             log(f"[bench] instance {i} layer {w.name}: T={w.T} K={w.K} N={w.N} ready")
         ring.append(layers)
     torch.cuda.synchronize()
@@ -296,6 +364,7 @@ def main():
     ms_step = wall * 1e3 / args.steps
 
     # per-kernel durations: a second pass of K steps bracketed by HIP events
+    # on the launch stream
     evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nl)]
            for _ in range(args.steps)]
     for i in range(args.steps):
@@ -305,6 +374,35 @@ def main():
                        for i in range(args.steps)])
     gemm_ms = np.array([[evs[i][j][1].elapsed_time(evs[i][j][2]) for j in range(nl)]
                         for i in range(args.steps)])
+
+    # shader clock under this load: the step loop keeps running while
+    # rocm-smi is sampled
+    sclk = None
+    if not args.no_sclk:
+        import threading
+        samples = []
+        stop = threading.Event()
+
+        def sampler():
+            while not stop.is_set() and len(samples) < 3:
+                v = sample_sclk()
+                if v is None:
+                    break
+                samples.append(v)
+
+        th = threading.Thread(target=sampler)
+        th.start()
+        t_end = time.perf_counter() + 3.0
+        i = 0
+        while th.is_alive() and time.perf_counter() < t_end:
+            step(i)
+            i += 1
+            if i % 20 == 0:
+                torch.cuda.synchronize()
+        stop.set()
+        torch.cuda.synchronize()
+        th.join()
+        sclk = int(np.median(samples)) if samples else None
 
     if args.copy_calibration:
         n = args.copy_calibration
@@ -319,45 +417,65 @@ def main():
     value = sum(ops) / (ms_step * 1e-3) / 1e12
     layers = []
     for j, w in enumerate(wls):
-        rm, gm = float(np.mean(rot_ms[:, j])), float(np.mean(gemm_ms[:, j]))
-        layers.append({
+        r, g = rot_ms[:, j] * 1e3, gemm_ms[:, j] * 1e3       # us
+        entry = {
             "layer": w.name, "T": w.T, "K": w.K, "N": w.N, "rotation": w.rot,
-            "block": w.block, "quant": w.quant,
-            "rotate_quant_us": round(rm * 1e3, 2),
-            "rotate_quant_GBps": round(rotate_bytes(w) / (rm * 1e-3) / 1e9, 1),
-            "gemm_us": round(gm * 1e3, 2),
-            "gemm_TOPS": round(w.ops() / (gm * 1e-3) / 1e12, 1),
-            "layer_ms": round(rm + gm, 4),
-            "layer_TOPS": round(w.ops() / ((rm + gm) * 1e-3) / 1e12, 1),
-        })
-        log(f"[bench] {json.dumps(layers[-1])}")
+            "block": w.block, "quant": w.quant, "a_bits": w.a_bits, "w_bits": w.w_bits,
+            "rotate_quant_us": {"mean": round(float(r.mean()), 2), "median": round(pct(r, 50), 2),
+                                "p10": round(pct(r, 10), 2), "p90": round(pct(r, 90), 2)},
+            "rotate_quant_GBps": round(rotate_bytes(w) / (r.mean() * 1e-6) / 1e9, 1),
+            "gemm_us": {"mean": round(float(g.mean()), 2), "median": round(pct(g, 50), 2),
+                        "p10": round(pct(g, 10), 2), "p90": round(pct(g, 90), 2)},
+            "gemm_TOPS": round(w.ops() / (g.mean() * 1e-6) / 1e12, 1),
+            "layer_us": round(float((r + g).mean()), 2),
+        }
+        if rotate_flops(w):
+            entry["rotate_TFLOPs"] = round(rotate_flops(w) / (r.mean() * 1e-6) / 1e12, 2)
+        layers.append(entry)
+        log(f"[bench] {json.dumps(entry)}")
 
-    is_codebook = all(w.quant == "lloydmax" for w in wls)
-    if is_codebook:
-        peak, gsrc, gkey, gname = PEAK_BF16_TFLOPS, "rq_gemm_codebook.hip", "gemm_codebook", "gemm_codebook_kernel"
+    w0 = wls[0]
+    if w0.quant == "lloydmax":
+        peak, gsrc, gkey, gname, dtype = PEAK_BF16_TFLOPS, "rq_gemm_codebook.hip", "gemm_codebook", \
+            "gemm_codebook_kernel", "bf16"
+    elif w0.quant == "mxfp4":
+        peak, gsrc, gkey, gname, dtype = PEAK_FP6_TOPS, "rq_gemm_mx.hip", "gemm_mx", "gemm_mx_kernel", "fp4"
     elif int8_gemm:
-        peak, gsrc, gkey, gname = PEAK_INT8_TOPS, "rq_gemm_w4a4.hip", "gemm_int8", "gemm_w4a4_kernel"
+        peak, gsrc, gkey, gname, dtype = PEAK_INT8_TOPS, "rq_gemm_w4a4.hip", "gemm_int8", \
+            "gemm_w4a4_kernel", "i8"
     else:
         # the INT4 GEMM computes on the FP6 matrix cores: its own dtype's peak
-        peak, gsrc, gkey, gname = PEAK_FP6_TOPS, "rq_gemm_fp6.hip", "gemm", "gemm_fp6_mma_kernel"
+        peak, gsrc, gkey, gname, dtype = PEAK_FP6_TOPS, "rq_gemm_fp6.hip", "gemm", \
+            ("gemm_fp6_mma_kernel" if w0.rot == "rpbh" else "gemm_fp6_kernel"), "fp6"
     gemm_mean_ms = float(np.mean(gemm_ms))
     achieved = float(np.mean(ops)) / (gemm_mean_ms * 1e-3) / 1e12
     traffic = profiled_traffic(gsrc, f"{gkey}_{args.workload}_counters.json")
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
-                "unit": "TFLOP/s" if is_codebook else "TOP/s",
-                "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": gname}
+                "unit": "TFLOP/s" if w0.quant == "lloydmax" else "TOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": gname,
+                "timing": "mean of per-launch HIP-event durations on the launch stream"}
+    if sclk:
+        roofline["frac_at_measured_sclk"] = round(achieved / (peak * sclk / 2400.0), 4)
     rot_mean_ms = float(np.mean(rot_ms))
-    rot_bytes = float(np.mean([rotate_bytes(w) for w in wls]))
-    rot_gbs = rot_bytes / (rot_mean_ms * 1e-3) / 1e9
-    roofline_rot = {"bound": "hbm", "achieved": round(rot_gbs, 1), "peak": PEAK_HBM_GBS,
-                    "unit": "GB/s", "frac": round(rot_gbs / PEAK_HBM_GBS, 4),
-                    "traffic": profiled_traffic("rq_rpbh.hip",
-                                                f"rotate_{args.workload}_counters.json"),
-                    "kernel": "rotate_quant"}
+    if w0.rot == "rpbh":
+        rot_bytes = float(np.mean([rotate_bytes(w) for w in wls]))
+        rot_gbs = rot_bytes / (rot_mean_ms * 1e-3) / 1e9
+        roofline_rot = {"bound": "hbm", "achieved": round(rot_gbs, 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(rot_gbs / PEAK_HBM_GBS, 4),
+                        "traffic": profiled_traffic("rq_rpbh.hip", f"rotate_{args.workload}_counters.json"),
+                        "kernel": "rpbh_quant_kernel"}
+    else:
+        fl = float(np.mean([rotate_flops(w) for w in wls])) / (rot_mean_ms * 1e-3) / 1e12
+        roofline_rot = {"bound": "alu", "achieved": round(fl, 2), "peak": PEAK_FP32_FMA_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(fl / PEAK_FP32_FMA_TFLOPS, 4), "traffic": None,
+                        "kernel": "dense_rotate_kernel" if w0.rot == "dense" else "trdq_quant_kernel"}
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(names, args.cpu_budget)
+        cpu["cpu_model"] = cpu_model()
+        one = cpu_baseline(names, args.cpu_budget / 4, threads=1)
+        cpu["one_thread"] = {"value": one["value"], "unit": one["unit"], "sample": one["sample"]}
 
     out = {
         "metric": "fused rotate+quant+W4A4 linear TOPS & ms/layer at FLUX-scale; % int8 MFMA peak",
@@ -369,15 +487,18 @@ def main():
         "ms_per_step": round(ms_step, 4),
         "ms_per_layer": round(ms_step / nl, 4),
         "pct_int8_peak": round(100 * value / PEAK_INT8_TOPS, 2),
+        "pct_fp6_peak": round(100 * value / PEAK_FP6_TOPS, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if is_codebook else ("i8" if int8_gemm else "fp6"),
+        "dtype": dtype,
         "data": "synthetic",
         "config": {"workload": args.workload, "layers": [
             {"name": w.name, "T": w.T, "K": w.K, "N": w.N, "rotation": w.rot, "block": w.block,
-             "r": w.r, "quant": w.quant, "x": w.xdtype, "y": w.ydtype} for w in wls],
-            "ring_instances": args.ring},
+             "r": w.r, "quant": w.quant, "a_bits": w.a_bits, "w_bits": w.w_bits, "x": w.xdtype,
+             "y": w.ydtype} for w in wls],
+            "ring_instances": args.ring, "engine": args.engine},
+        "sclk_mhz": sclk,
         "layers": layers,
         "roofline": roofline,
         "roofline_rotate_quant": roofline_rot,

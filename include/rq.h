@@ -232,6 +232,32 @@ typedef struct rq_weight_header {
     uint8_t reserved[256 - 64 - 128 - 40];
 } rq_weight_header;
 
+/*
+ * Time-step rotation sets (TR-DQ section 3.2, Eq.(10)): instead of one
+ * rotation and one packed weight for every denoising step, step t selects a
+ * group g = step_group[t] with its own rotation (smoothing multiplier,
+ * rotations, permutation -- or any rotation kind) and its own weights folded
+ * with that rotation.  A set blob is this header followed by one ordinary
+ * packed-weight blob per group (memory grows with the groups).
+ *   groups        G, 1 <= G <= RQ_SET_MAX_GROUPS
+ *   steps         number of steps mapped, 1 <= steps <= RQ_SET_MAX_STEPS
+ *   member_offset byte offset of group g's blob (256-byte aligned)
+ *   step_group    group of step t, in [0, G)
+ */
+#define RQ_SET_MAGIC 0x53545152u /* "RQTS" */
+#define RQ_SET_VERSION 1u
+#define RQ_SET_MAX_GROUPS 64
+#define RQ_SET_MAX_STEPS 1024
+typedef struct rq_set_header {
+    uint32_t magic;
+    uint32_t version;
+    int32_t groups;
+    int32_t steps;
+    int64_t member_offset[RQ_SET_MAX_GROUPS];
+    int32_t step_group[RQ_SET_MAX_STEPS];
+    uint8_t reserved[4864 - 16 - 8 * RQ_SET_MAX_GROUPS - 4 * RQ_SET_MAX_STEPS];
+} rq_set_header;
+
 /* Library version (major * 10000 + minor * 100 + patch). */
 int32_t rq_version(void);
 
@@ -281,6 +307,40 @@ rq_status rq_packed_weight_bytes(const rq_rotation *rot, const rq_quant *q, int3
  */
 rq_status rq_pack_weights(const rq_rotation *rot, const rq_quant *q, const void *W,
                           int32_t w_dtype, int32_t N, void *blob, size_t blob_bytes);
+
+/*
+ * Bytes of a time-step set blob for `groups` rotations (host descriptors;
+ * all of one K and kind family accepted by rq_pack_weights) and N outputs.
+ * Errors: as rq_packed_weight_bytes; RQ_ERR_SHAPE for a group count out of
+ *         range or rotations of different K.
+ */
+rq_status rq_weight_set_bytes(const rq_rotation *rots, int32_t groups, const rq_quant *q,
+                              int32_t N, size_t *bytes);
+
+/*
+ * Offline packing of a time-step set: rq_pack_weights of W for each group's
+ * rotation, behind an rq_set_header holding step_group[0 .. steps).
+ *   rots        host descriptors [groups]
+ *   step_group  host int32 [steps], each in [0, groups)
+ *   q, W, w_dtype, N  as rq_pack_weights
+ *   blob        host buffer of blob_bytes >= rq_weight_set_bytes()
+ * Errors: as rq_pack_weights; RQ_ERR_SHAPE for a step mapped outside the
+ *         groups or counts out of range.
+ */
+rq_status rq_pack_weight_set(const rq_rotation *rots, int32_t groups, const int32_t *step_group,
+                             int32_t steps, const rq_quant *q, const void *W, int32_t w_dtype,
+                             int32_t N, void *blob, size_t blob_bytes);
+
+/*
+ * The member of a set that step `step` uses: its group (the index of the
+ * rotation descriptor to pass to rq_rotate_quant), a pointer to its weight
+ * header inside the host copy of the set, and the byte offset of its blob
+ * (add it to the device copy's address for rq_w4a4_linear).  Host only.
+ * Errors: RQ_ERR_NULL, RQ_ERR_FORMAT (not a set), RQ_ERR_SHAPE (step out of
+ *         range).
+ */
+rq_status rq_weight_set_member(const void *set_host, int32_t step, int32_t *group,
+                               const rq_weight_header **hdr, int64_t *offset);
 
 /*
  * Bytes of device workspace rq_rotate_quant needs (0 for RPBH and TRDQ;

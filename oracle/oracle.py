@@ -104,6 +104,7 @@ def _declare(L):
     L.orc_lowrank_pairs.argtypes = [_P, _I, _P, _I, _P, _P, _I64, _P]
     L.orc_codebook_dot_pairs.argtypes = [_P, _P, _I, _I, _P, _P, _P, _P, _I64, _P]
     L.orc_num_threads.restype = _I
+    L.orc_set_threads.argtypes = [_I]
 
 
 class _Rot(ctypes.Structure):
@@ -131,6 +132,11 @@ def _ptr(a):
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads of the oracle's parallel row loops."""
+    lib().orc_set_threads(int(n))
 
 
 # ---------------------------------------------------------------------------

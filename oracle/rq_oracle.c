@@ -979,3 +979,15 @@ int orc_num_threads(void)
     }
     return n;
 }
+
+/* Set the OpenMP thread count of the parallel regions above. */
+void orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

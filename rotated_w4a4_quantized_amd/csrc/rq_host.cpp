@@ -519,6 +519,83 @@ rq_status rq_pack_weights(const rq_rotation *rot, const rq_quant *q, const void 
     return RQ_OK;
 }
 
+static_assert(sizeof(rq_set_header) == 4864, "set header size");
+
+rq_status rq_weight_set_bytes(const rq_rotation *rots, int32_t groups, const rq_quant *q,
+                              int32_t N, size_t *bytes) {
+    clear_error();
+    if (!rots || !bytes) return fail(RQ_ERR_NULL, "rots and bytes must not be NULL");
+    if (groups < 1 || groups > RQ_SET_MAX_GROUPS)
+        return fail(RQ_ERR_SHAPE, "groups must be in [1, " + std::to_string(RQ_SET_MAX_GROUPS) + "]");
+    size_t total = sizeof(rq_set_header);
+    for (int g = 0; g < groups; ++g) {
+        if (rots[g].K != rots[0].K) return fail(RQ_ERR_SHAPE, "the set's rotations differ in K");
+        size_t b = 0;
+        const rq_status st = rq_packed_weight_bytes(&rots[g], q, N, &b);
+        if (st != RQ_OK) return st;
+        total += (b + 255) / 256 * 256;
+    }
+    *bytes = total;
+    return RQ_OK;
+}
+
+rq_status rq_pack_weight_set(const rq_rotation *rots, int32_t groups, const int32_t *step_group,
+                             int32_t steps, const rq_quant *q, const void *W, int32_t w_dtype,
+                             int32_t N, void *blob, size_t blob_bytes) {
+    size_t need = 0;
+    rq_status st = rq_weight_set_bytes(rots, groups, q, N, &need);
+    if (st != RQ_OK) return st;
+    if (!step_group || !blob || !W) return fail(RQ_ERR_NULL, "step_group, W and blob must not be NULL");
+    if (steps < 1 || steps > RQ_SET_MAX_STEPS)
+        return fail(RQ_ERR_SHAPE, "steps must be in [1, " + std::to_string(RQ_SET_MAX_STEPS) + "]");
+    for (int t = 0; t < steps; ++t)
+        if (step_group[t] < 0 || step_group[t] >= groups)
+            return fail(RQ_ERR_SHAPE, "step " + std::to_string(t) + " maps outside the groups");
+    if (blob_bytes < need)
+        return fail(RQ_ERR_SHAPE, "blob_bytes " + std::to_string(blob_bytes) + " < required " +
+                                      std::to_string(need));
+    uint8_t *out = static_cast<uint8_t *>(blob);
+    rq_set_header sh;
+    std::memset(&sh, 0, sizeof sh);
+    sh.magic = RQ_SET_MAGIC;
+    sh.version = RQ_SET_VERSION;
+    sh.groups = groups;
+    sh.steps = steps;
+    for (int t = 0; t < steps; ++t) sh.step_group[t] = step_group[t];
+    size_t off = sizeof(rq_set_header);
+    for (int g = 0; g < groups; ++g) {
+        size_t b = 0;
+        rq_packed_weight_bytes(&rots[g], q, N, &b);
+        sh.member_offset[g] = (int64_t)off;
+        st = rq_pack_weights(&rots[g], q, W, w_dtype, N, out + off, b);
+        if (st != RQ_OK) return st;
+        off += (b + 255) / 256 * 256;
+    }
+    std::memcpy(out, &sh, sizeof sh);
+    return RQ_OK;
+}
+
+rq_status rq_weight_set_member(const void *set_host, int32_t step, int32_t *group,
+                               const rq_weight_header **hdr, int64_t *offset) {
+    clear_error();
+    if (!set_host || !group || !hdr || !offset)
+        return fail(RQ_ERR_NULL, "set, group, hdr and offset must not be NULL");
+    const rq_set_header *sh = static_cast<const rq_set_header *>(set_host);
+    if (sh->magic != RQ_SET_MAGIC || sh->version != RQ_SET_VERSION || sh->groups < 1 ||
+        sh->groups > RQ_SET_MAX_GROUPS || sh->steps < 1 || sh->steps > RQ_SET_MAX_STEPS)
+        return fail(RQ_ERR_FORMAT, "not a time-step set blob");
+    if (step < 0 || step >= sh->steps)
+        return fail(RQ_ERR_SHAPE, "step " + std::to_string(step) + " outside the set's " +
+                                      std::to_string(sh->steps) + " steps");
+    const int g = sh->step_group[step];
+    if (g < 0 || g >= sh->groups) return fail(RQ_ERR_FORMAT, "set step table is corrupt");
+    *group = g;
+    *offset = sh->member_offset[g];
+    *hdr = reinterpret_cast<const rq_weight_header *>(static_cast<const uint8_t *>(set_host) +
+                                                      sh->member_offset[g]);
+    return RQ_OK;
+}
+
 // Lloyd's iteration for N(0,1) in fp64, then bf16 rounding of the levels.
 rq_status rq_lloydmax_gaussian(int32_t L, float *levels) {
     clear_error();

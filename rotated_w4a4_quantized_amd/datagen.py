@@ -160,7 +160,7 @@ def _draw_x(w: Workload, g: np.random.Generator, T: int, K: int, outlier_cols=No
     return x
 
 
-def make_inputs(w: Workload, seed_offset: int = 0) -> dict:
+def make_inputs(w: Workload, seed_offset: int = 0, W=None) -> dict:
     """All inputs of one workload instance.
 
     Returns dict with:
@@ -190,6 +190,8 @@ def make_inputs(w: Workload, seed_offset: int = 0) -> dict:
         out["X"] = xf
         out["Xf"] = xf
     out["W"] = (s["w"].standard_normal((N, K), dtype=np.float32) * np.float32(0.02)).astype(np.float32)
+    if W is not None:   # a given layer (time-step sets: one W, several rotations)
+        out["W"] = np.ascontiguousarray(W, np.float32)
     if w.rot == "rpbh":
         out["sign"] = np.where(s["sign"].integers(0, 2, size=K) == 1, 1, -1).astype(np.int8)
         out["perm"] = s["perm"].permutation(K).astype(np.int32)
@@ -320,3 +322,12 @@ def trdq_rotation(calib: np.ndarray, W: np.ndarray, b: int, g: np.random.Generat
     p = z[:, perm]
     R2 = np.stack([greedy_block_rotation(p[:, c * b:(c + 1) * b], g) for c in range(nb)])
     return {"m": m, "R1": R1, "perm": perm, "R2": R2.astype(np.float32), "R": None}
+
+
+def make_timestep_inputs(w: Workload, groups: int) -> list:
+    """One layer seen at `groups` groups of denoising steps ("TR-DQ" Eq.(10)):
+    the weights are the layer's, fixed; the activations -- their outlier
+    channels and calibration statistics -- and so the rotation differ per
+    group.  Returns one make_inputs dict per group, all with the same W."""
+    W = make_inputs(w)["W"]
+    return [make_inputs(w, seed_offset=50 + g, W=W) for g in range(groups)]

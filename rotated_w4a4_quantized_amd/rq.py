@@ -63,11 +63,22 @@ class c_weight_header(ctypes.Structure):
 
 assert ctypes.sizeof(c_weight_header) == 256
 
+
+class c_set_header(ctypes.Structure):
+    _fields_ = [("magic", ctypes.c_uint32), ("version", ctypes.c_uint32),
+                ("groups", ctypes.c_int32), ("steps", ctypes.c_int32),
+                ("member_offset", ctypes.c_int64 * 64), ("step_group", ctypes.c_int32 * 1024),
+                ("reserved", ctypes.c_uint8 * (4864 - 16 - 8 * 64 - 4 * 1024))]
+
+
+assert ctypes.sizeof(c_set_header) == 4864
+
 # every symbol include/rq.h declares
 EXPORTS = ("rq_version", "rq_last_error", "rq_lloydmax_gaussian", "rq_packed_weight_bytes",
            "rq_pack_weights", "rq_rotate_quant_workspace_bytes", "rq_codes_mma_bytes",
            "rq_rotate_quant", "rq_w4a4_linear", "rq_w4a4_linear_engine",
-           "rq_rotate_quant_noalloc", "rq_activation_bytes")
+           "rq_rotate_quant_noalloc", "rq_activation_bytes", "rq_weight_set_bytes",
+           "rq_pack_weight_set", "rq_weight_set_member")
 
 _lib = None
 
@@ -96,10 +107,15 @@ def load() -> ctypes.CDLL:
     L.rq_rotate_quant_noalloc.argtypes = [P, P, P, I32, I64, P, P, P, P, P]
     L.rq_activation_bytes.argtypes = [P, P, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ),
                                       ctypes.POINTER(SZ)]
+    L.rq_weight_set_bytes.argtypes = [P, I32, P, I32, ctypes.POINTER(SZ)]
+    L.rq_pack_weight_set.argtypes = [P, I32, P, I32, P, P, I32, I32, P, SZ]
+    L.rq_weight_set_member.argtypes = [P, I32, ctypes.POINTER(I32), ctypes.POINTER(P),
+                                       ctypes.POINTER(I64)]
     for name in ("rq_lloydmax_gaussian", "rq_packed_weight_bytes", "rq_pack_weights",
                  "rq_rotate_quant_workspace_bytes", "rq_codes_mma_bytes", "rq_rotate_quant",
                  "rq_w4a4_linear", "rq_w4a4_linear_engine", "rq_rotate_quant_noalloc",
-                 "rq_activation_bytes"):
+                 "rq_activation_bytes", "rq_weight_set_bytes", "rq_pack_weight_set",
+                 "rq_weight_set_member"):
         getattr(L, name).restype = I32
     _lib = L
     return L
@@ -346,6 +362,50 @@ def pack_weights(rot: Rotation, q: Quant, W: np.ndarray) -> PackedWeights:
                                   _np_ptr(blob), nbytes))
     hdr = c_weight_header.from_buffer_copy(blob[:256].tobytes())
     return PackedWeights(blob, hdr)
+
+
+class WeightSet:
+    """A time-step set (host blob): per group the weights folded with that
+    group's rotation, and the step -> group table."""
+
+    def __init__(self, blob: np.ndarray):
+        self.blob = blob
+        self.device_blob = None
+
+    def member(self, step: int):
+        """(group, header, byte offset) of the blob that step uses."""
+        g = ctypes.c_int32(0)
+        h = ctypes.c_void_p(0)
+        off = ctypes.c_int64(0)
+        _check(load().rq_weight_set_member(_np_ptr(self.blob), step, ctypes.byref(g),
+                                           ctypes.byref(h), ctypes.byref(off)))
+        hdr = c_weight_header.from_buffer_copy(self.blob[off.value:off.value + 256].tobytes())
+        return g.value, hdr, off.value
+
+    def to_device(self, device="cuda"):
+        import torch
+        self.device_blob = torch.from_numpy(self.blob).to(device)
+        return self
+
+    def device_member(self, step: int) -> "DeviceWeights":
+        """The DeviceWeights of the step's member: a view into the device set."""
+        g, hdr, off = self.member(step)
+        return DeviceWeights(hdr, self.device_blob[off:off + hdr.total_bytes])
+
+
+def pack_weight_set(rots, step_group, q: Quant, W: np.ndarray) -> WeightSet:
+    """Offline packing of a time-step set (rq_pack_weight_set)."""
+    W = np.ascontiguousarray(W, np.float32)
+    N = int(W.shape[0])
+    arr = (c_rotation * len(rots))(*[r.c_host() for r in rots])
+    cq = q.c()
+    n = ctypes.c_size_t(0)
+    _check(load().rq_weight_set_bytes(arr, len(rots), ctypes.byref(cq), N, ctypes.byref(n)))
+    blob = np.zeros(n.value, np.uint8)
+    sg = np.ascontiguousarray(step_group, np.int32)
+    _check(load().rq_pack_weight_set(arr, len(rots), _np_ptr(sg), sg.size, ctypes.byref(cq),
+                                     _np_ptr(W), RQ_F32, N, _np_ptr(blob), n.value))
+    return WeightSet(blob)
 
 
 def rotate_quant_workspace_bytes(rot: Rotation, q: Quant, T: int) -> int:

@@ -42,7 +42,7 @@ def test_struct_sizes_match_header(tmp_path):
     include/rq.h's (sizes and every field offset, from a compiled probe)."""
     assert ctypes.sizeof(rq.c_weight_header) == 256
     structs = {"rq_rotation": rq.c_rotation, "rq_quant": rq.c_quant,
-               "rq_weight_header": rq.c_weight_header}
+               "rq_weight_header": rq.c_weight_header, "rq_set_header": rq.c_set_header}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "rq.h"', 'int main(void) {']
     for cname, ct in structs.items():
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
@@ -472,3 +472,30 @@ def test_new_format_validation_errors():
     assert L.rq_w4a4_linear(ctypes.byref(h), ctypes.c_void_p(1 << 20), None, None, None,
                             ctypes.c_void_p(1 << 23), 4, None, ctypes.c_void_p(1 << 24),
                             rq.RQ_I32, None) == -6
+
+
+def test_weight_set_members():
+    """Time-step sets ("TR-DQ" Eq.(10)): each group's member is exactly
+    rq_pack_weights with that group's rotation; steps map to their group."""
+    w = datagen.WORKLOADS["flux_up_trdq"].with_shape(T=4, K=256, N=40, block=64)
+    ins = datagen.make_timestep_inputs(w, 3)
+    assert all(np.array_equal(i["W"], ins[0]["W"]) for i in ins)
+    assert not np.array_equal(ins[0]["perm"], ins[1]["perm"])
+    from rotated_w4a4_quantized_amd.layer import quant_for, rotation_for
+    rots = [rotation_for(w, i) for i in ins]
+    steps = [0, 0, 1, 1, 1, 2, 2, 0]
+    ws = rq.pack_weight_set(rots, steps, quant_for(w), ins[0]["W"])
+    for t, g_want in enumerate(steps):
+        g, hdr, off = ws.member(t)
+        assert g == g_want and off % 256 == 0
+        one = rq.pack_weights(rots[g], quant_for(w), ins[0]["W"])
+        assert np.array_equal(ws.blob[off:off + one.blob.size], one.blob)
+    with pytest.raises(rq.RQError) as e:
+        ws.member(len(steps))
+    assert e.value.status == -2
+    bad = rq.WeightSet(np.zeros(8192, np.uint8))
+    with pytest.raises(rq.RQError) as e:
+        bad.member(0)
+    assert e.value.status == -5
+    with pytest.raises(rq.RQError):
+        rq.pack_weight_set(rots, [0, 3], quant_for(w), ins[0]["W"])   # step maps past the groups

@@ -509,3 +509,38 @@ def test_int8_engine_full_workload(name):
     acc = L.raw_acc(engine="int8").view(-1)[idx].cpu().numpy().astype(np.int64)
     ref = H.orc.int_gemm_pairs(act["codes"], w.Kq, wts["codes"], w.K, np.searchsorted(rows, ta), nw)
     assert np.array_equal(acc, ref)
+
+
+@pytest.mark.parametrize("name,shape", [("flux_up_trdq", dict(T=70, K=1024, N=136)),
+                                        ("flux_up", dict(T=100, K=1024, N=200, block=256))])
+def test_timestep_set_parity(name, shape):
+    """Time-step rotation sets ("TR-DQ" Eq.(10)): eight denoising steps in
+    three groups, each group with its own rotation and its own folded
+    weights (one layer W).  Every step's codes and outputs match the oracle
+    with that step's rotation; the wrong group's weights would not."""
+    w = datagen.WORKLOADS[name].with_shape(**shape)
+    ins = datagen.make_timestep_inputs(w, 3)
+    rots = [H.rotation_for(w, i) for i in ins]
+    q = H.quant_for(w)
+    steps = [0, 0, 1, 1, 1, 2, 2, 0]
+    ws = H.rq.pack_weight_set(rots, steps, q, ins[0]["W"]).to_device("cuda")
+    drots = [r.to_device("cuda") for r in rots]
+    for t, g in enumerate(steps):
+        inp = ins[g]
+        say(f"[timestep set] {w.name} step {t} group {g}")
+        L = H.GpuLayer(w, inp, y_dtype="f32")
+        L.drot = drots[g]
+        L.dw = ws.device_member(t)
+        L.run()
+        torch.cuda.synchronize()
+        act = H.oracle_act(w, inp)
+        check_act(w, L, act)
+        wts = H.oracle_weights(w, inp)
+        ta, nw = np.meshgrid(np.arange(w.T), np.arange(w.N), indexing="ij")
+        yhat = H.oracle_yhat_pairs(w, act, wts, ta.ravel(), nw.ravel())
+        err = H.rel_err(L.Y.cpu().numpy().ravel(), yhat)
+        assert err <= H.REL_TOL, (t, err)
+        if t == 2:   # another group's member does not reproduce this step
+            L.dw = ws.device_member(0)
+            L.linear()
+            assert H.rel_err(L.Y.cpu().numpy().ravel(), yhat) > 1e-2
