@@ -180,6 +180,42 @@ def summarize_stats(stats_csv, workload, command):
     return path
 
 
+def summarize_trace(trace_csv, workload, command, warmup=3):
+    """Where a step's time goes, from a rocprofv3 --kernel-trace csv of a
+    bench run: per kernel and grid, the mean duration of all launches and of
+    those after the warmup steps; and the idle time between consecutive
+    kernels of this library that follow each other within 100 us (gaps
+    above that are the bench's host synchronizations between its phases)."""
+    import csv
+    rows = [r for r in csv.DictReader(open(trace_csv)) if "rq::" in r["Kernel_Name"]]
+
+    def short(name):
+        name = name.replace("void rq::(anonymous namespace)::", "").replace("rq::(anonymous namespace)::", "")
+        return name.split("(")[0]
+
+    ks = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), short(r["Kernel_Name"]),
+                 int(r["Grid_Size_X"])) for r in rows)
+    per = {}
+    for b, e, n, g in ks:
+        per.setdefault((n, g), []).append(e - b)
+    lines = [f"# Kernel timeline, workload {workload}", "",
+             "Command (from the repository root on the GPU host):", "", "    " + command, "",
+             f"Durations per kernel and grid (the first {warmup} launches of each are the warmup steps):", "",
+             "| kernel | grid | launches | mean, all (us) | mean after warmup (us) | min (us) |",
+             "|---|---|---|---|---|---|"]
+    for (n, g), d in sorted(per.items()):
+        d = np.array(d) / 1e3
+        lines.append(f"| `{n}` | {g} | {d.size} | {d.mean():.2f} | {d[warmup:].mean() if d.size > warmup else d.mean():.2f} | {d.min():.2f} |")
+    gaps = [b1 - e0 for (b0, e0, _, _), (b1, e1, _, _) in zip(ks, ks[1:]) if b1 - e0 < 100_000]
+    busy = sum(e - b for b, e, _, _ in ks)
+    lines += ["", f"Idle gaps between back-to-back kernels (under 100 us): {len(gaps)} gaps, mean "
+              f"{np.mean(gaps) / 1e3:.2f} us, median {np.median(gaps) / 1e3:.2f} us, max "
+              f"{np.max(gaps) / 1e3:.2f} us; kernels busy {busy / 1e3:.1f} us in all."]
+    path = os.path.join(ROOT, "profiles", f"kernel_timeline_{workload}.md")
+    open(path, "w").write("\n".join(lines) + "\n")
+    return path
+
+
 def rotate_bytes(w) -> int:
     """Algorithmic HBM bytes of one rotate+quant launch: X read, codes,
     scales (and top) written, in the method's minimal encoding."""
@@ -293,9 +329,13 @@ def main():
                     help="offline: summarize two rocprofv3 --pmc runs into profiles/")
     ap.add_argument("--summarize-stats", metavar="STATS_CSV",
                     help="offline: summarize a rocprofv3 --stats csv into profiles/")
+    ap.add_argument("--summarize-trace", metavar="TRACE_CSV",
+                    help="offline: kernel gaps from a rocprofv3 --kernel-trace csv into profiles/")
     ap.add_argument("--command", default="", help="command recorded in the summaries")
     args = ap.parse_args()
 
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.workload, args.command))
     if args.summarize_pmc or args.summarize_stats:
         if args.summarize_pmc:
             res = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
@@ -303,6 +343,8 @@ def main():
             print(json.dumps({k: v["hbm_bytes_per_launch"] for k, v in res.items()}))
         if args.summarize_stats:
             print(summarize_stats(args.summarize_stats, args.workload, args.command))
+        return
+    if args.summarize_trace:
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
