@@ -355,7 +355,7 @@ def main():
 
     import torch
     from rotated_w4a4_quantized_amd import datagen, rq
-    from rotated_w4a4_quantized_amd.layer import QuantLinear
+    from rotated_w4a4_quantized_amd.layer import QuantLinear, mma_capable
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     rq.load()
@@ -369,10 +369,9 @@ def main():
         layers = []
         for w in wls:
             inp = datagen.make_inputs(w, seed_offset=100 * i)
-            # RPBH layers with 4-bit integer codes or MXFP4 hand the GEMM its
-            # codes in the matrix-core layout only
-            mma = w.rot == "rpbh" and ((w.quant in ("int4", "int4_asym") and w.a_bits == 4 and
-                                        args.engine != "int8") or w.quant == "mxfp4")
+            # layers with 4-bit integer codes (RPBH, DENSE) or MXFP4 hand the
+            # GEMM its codes in the matrix-core layout only
+            mma = mma_capable(w) and not (args.engine == "int8" and w.quant != "mxfp4")
             layers.append(QuantLinear(w, inp, codes="mma" if mma else "canonical"))
             log(f"[bench] instance {i} layer {w.name}: T={w.T} K={w.K} N={w.N} ready")
         ring.append(layers)

@@ -364,7 +364,7 @@ rq_status rq_codes_mma_bytes(const rq_rotation *rot, int64_t T, size_t *bytes);
  *   scale      T * 4 (INT symmetric, LLOYDMAX), T * 8 (INT asymmetric: s
  *              then z), T * K / 32 (MXFP4: E8M0 codes)
  *   codes_mma  the GEMM-layout copy rq_rotate_quant can write: INT with
- *              a_bits 4 (RPBH): rq_codes_mma_bytes(); MXFP4: the tiled codes
+ *              a_bits 4 (RPBH, DENSE): rq_codes_mma_bytes(); MXFP4: the tiled codes
  *              and tiled scales (see rq_rotate_quant); 0 where none exists
  * Any output pointer may be NULL.
  * Errors: descriptor errors, RQ_ERR_SHAPE (T out of range).
@@ -413,19 +413,21 @@ rq_status rq_activation_bytes(const rq_rotation *rot, const rq_quant *q, int64_t
  *           nibbles (two's complement when symmetric, unsigned when
  *           asymmetric; low nibble = even coordinate), INT 8-bit bytes
  *           (int8 / uint8), LLOYDMAX 4-bit indices or MXFP4 E2M1 codes as
- *           nibbles.  May be NULL for RPBH INT 4-bit and MXFP4 when
- *           codes_mma is given.
+ *           nibbles.  May be NULL for INT 4-bit (RPBH, DENSE) and MXFP4
+ *           when codes_mma is given.
  *   scale   device: fp32 [T] s (INT symmetric) or sigma (LLOYDMAX); INT
  *           asymmetric: fp32 [2][T], s[t] then the zero point z[t]; MXFP4:
  *           uint8 [T][K/32] E8M0 codes (the pointer is read as bytes).  May
  *           be NULL for MXFP4 when codes_mma is given.
  *   top     device bf16 [T][r] for DENSE with r > 0, else NULL
- *   codes_mma  optional (NULL: not written), RPBH only:
+ *   codes_mma  optional (NULL: not written), RPBH or DENSE:
  *           INT 4-bit: a device buffer of rq_codes_mma_bytes() receiving the
  *           same codes in the FP6 GEMM's matrix-core layout.  Tokens come in
  *           tiles of 32 and coordinates in stages of 128; the buffer is
  *           [tile][stage][piece 0..2][lane 0..63][16 bytes], 3 KB per tile
- *           and stage.  Token t of a tile owns lanes t and t + 32 (half h);
+ *           and stage (DENSE: the K - r quantized coordinates; fields of
+ *           coordinates past K - r and of token slots past T are left
+ *           unwritten).  Token t of a tile owns lanes t and t + 32 (half h);
  *           its twelve dwords f[0..11] for half h of a stage are dword d % 4
  *           of its lane in piece d / 4.  f[0..5] and f[6..11] are the 192-bit
  *           fragments of coordinates 128 s + 64 ks + 32 h + (0..31) for
@@ -500,7 +502,7 @@ rq_status rq_rotate_quant_noalloc(const rq_rotation *rot, const rq_quant *q, con
  *   blob    device copy of the whole blob, 16-byte aligned
  *   codes, scale, top  as written by rq_rotate_quant (device); the weights'
  *           format (kind, a_bits) must match the activations' quantizer
- *   codes_mma  optional (INT with a_bits 4 and r == 0, or MXFP4): the
+ *   codes_mma  optional (INT with a_bits 4, or MXFP4): the
  *           codes_mma output of rq_rotate_quant for the same tokens; when
  *           given it is read instead of codes (and, MXFP4, scale), which may
  *           then be NULL

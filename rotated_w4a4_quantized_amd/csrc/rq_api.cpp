@@ -84,13 +84,14 @@ rq_status validate_rotate_quant(const rq_rotation *rot, const rq_quant *q, const
     const bool dense = rot->kind == RQ_ROT_DENSE;
     const bool mx = q->kind == RQ_Q_MXFP4;
     const bool int4 = (q->kind == RQ_Q_INT4_SYM || q->kind == RQ_Q_INT4_ASYM) && q->a_bits == 4;
-    if (codes_mma && !(rpbh && (int4 || mx)))
+    if (codes_mma && !((rpbh && (int4 || mx)) || (dense && int4)))
         return fail(RQ_ERR_UNSUPPORTED,
-                    "codes_mma is written for RPBH with 4-bit integer codes or MXFP4 only");
+                    "codes_mma is written for RPBH or DENSE with 4-bit integer codes and for RPBH "
+                    "with MXFP4 only");
     if (T == 0) return RQ_OK;
     if (!X || (!codes && !codes_mma) || (!scale && !(mx && codes_mma)))
         return fail(RQ_ERR_NULL, "X, scale and at least one of codes / codes_mma must not be NULL");
-    if (!codes && !(rpbh && (int4 || mx)))
+    if (!codes && !((rpbh && (int4 || mx)) || (dense && int4)))
         return fail(RQ_ERR_NULL, "this rotation and quantizer write the canonical codes: codes is NULL");
     if (dense && rot->r > 0 && !top) return fail(RQ_ERR_NULL, "DENSE with r > 0 needs top");
     if (!aligned16(X) || (codes && !aligned16(codes)) || (scale && !aligned16(scale)) ||
@@ -133,7 +134,7 @@ rq_status rq_activation_bytes(const rq_rotation *rot, const rq_quant *q, int64_t
                     : (size_t)T * (q->kind == RQ_Q_INT4_ASYM ? 8 : 4);
     if (codes_mma) {
         *codes_mma = 0;
-        if (rot->kind == RQ_ROT_RPBH && intq && q->a_bits == 4)
+        if ((rot->kind == RQ_ROT_RPBH || rot->kind == RQ_ROT_DENSE) && intq && q->a_bits == 4)
             *codes_mma = (size_t)mma_codes_bytes(T, Kq);
         else if (rot->kind == RQ_ROT_RPBH && mx)
             *codes_mma = (size_t)mx_mma_bytes(T, K);
@@ -195,7 +196,7 @@ rq_status rq_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void 
     float *U = static_cast<float *>(workspace);
     st = hip_status(launch_dense_rotate(X, xb, T, K, rot->R, U, stream), "dense rotate launch");
     if (st != RQ_OK) return st;
-    return hip_status(launch_dense_quant(U, T, K, rot->r, codes, scale, top, stream),
+    return hip_status(launch_dense_quant(U, T, K, rot->r, codes, scale, top, codes_mma, stream),
                       "dense quant launch");
 }
 
@@ -245,9 +246,9 @@ rq_status rq_w4a4_linear_engine(const rq_weight_header *hdr, const void *blob,
     const bool mx = f == RQ_Q_MXFP4;
     if (y_dtype == RQ_I32 && !intq)
         return fail(RQ_ERR_UNSUPPORTED, "raw accumulators exist for integer weights only");
-    if (codes_mma && !((intq && !a8 && hdr->r == 0) || mx))
+    if (codes_mma && !((intq && !a8) || mx))
         return fail(RQ_ERR_UNSUPPORTED,
-                    "codes_mma is read for 4-bit integer weights with r == 0 and for MXFP4 only");
+                    "codes_mma is read for 4-bit integer activations and for MXFP4 only");
     if (engine != RQ_ENGINE_AUTO && !intq)
         return fail(RQ_ERR_UNSUPPORTED, "the Lloyd-Max and MXFP4 formats have one engine (RQ_ENGINE_AUTO)");
     if (a8 && engine == RQ_ENGINE_FP6)

@@ -15,6 +15,7 @@
 
 #include <mutex>
 
+#include "rq_fp6.h"
 #include "rq_internal.h"
 
 namespace rq {
@@ -100,11 +101,14 @@ __device__ inline uint16_t f32_to_bf16_rne(float x) {
     return (uint16_t)(upper + ((lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) ? 1u : 0u));
 }
 
-// One 64-lane wave per token.
+// One 64-lane wave per token.  Lane l quantizes the 32-coordinate chunks
+// c = l, l + 64, ... of the token's Kq = K - r quantized coordinates and
+// writes them as sixteen canonical nibble bytes and/or in the GEMM's FP6
+// fragment layout (rq_fp6.h; signed codes, carried as q + 8).
 __global__ void __launch_bounds__(256)
 dense_quant_kernel(const float *__restrict__ U, int64_t T, int K, int r,
                    uint8_t *__restrict__ codes, float *__restrict__ scale,
-                   uint16_t *__restrict__ top) {
+                   uint16_t *__restrict__ top, uint8_t *__restrict__ codes_mma) {
     const int lane = threadIdx.x & 63;
     const int64_t tok = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (tok >= T) return;
@@ -114,20 +118,29 @@ dense_quant_kernel(const float *__restrict__ U, int64_t T, int K, int r,
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
     for (int j = lane; j < r; j += 64) top[tok * r + j] = f32_to_bf16_rne(u[j]);
-    const int Kq = K - r;
-    uint8_t *crow = codes + tok * (int64_t)(Kq / 2);
+    const int Kq = K - r, nch = Kq / 32, S = (Kq + 127) / 128;
     const float inv = m > 0.0f ? 7.0f / m : 0.0f;
-    for (int p = lane; p < Kq / 2; p += 64) {
-        uint32_t b = 0;
-        if (m > 0.0f) {
+    for (int c = lane; c < nch; c += 64) {
+        const float4 *src = reinterpret_cast<const float4 *>(u + r + 32 * c);
+        uint32_t w[4];
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                float q = rintf(u[r + 2 * p + e] * inv);
-                q = fminf(7.0f, fmaxf(-7.0f, q));
-                b |= ((uint32_t)(int)q & 0xFu) << (4 * e);
+        for (int d = 0; d < 4; ++d) {
+            const float4 v0 = src[2 * d], v1 = src[2 * d + 1];
+            const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            uint32_t b = 0;
+            if (m > 0.0f) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float q = rintf(v[e] * inv);
+                    q = fminf(7.0f, fmaxf(-7.0f, q));
+                    b |= ((uint32_t)(int)q & 0xFu) << (4 * e);   // low nibble = even coordinate
+                }
             }
+            w[d] = b;
         }
-        crow[p] = (uint8_t)b;
+        const uint4 w4 = make_uint4(w[0], w[1], w[2], w[3]);
+        if (codes) *reinterpret_cast<uint4 *>(codes + tok * (int64_t)(Kq / 2) + 16 * c) = w4;
+        if (codes_mma) store_chunk_mma(codes_mma, tok, S, c, w4, 0x88888888u);
     }
     if (lane == 0) scale[tok] = m > 0.0f ? m / 7.0f : 0.0f;
 }
@@ -173,10 +186,10 @@ int launch_dense_rotate(const void *X, int x_bf16, int64_t T, int K, const float
 }
 
 int launch_dense_quant(const float *U, int64_t T, int K, int r, uint8_t *codes, float *scale,
-                       uint16_t *top, void *stream) {
+                       uint16_t *top, uint8_t *codes_mma, void *stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipLaunchKernelGGL(dense_quant_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, U, T,
-                       K, r, codes, scale, top);
+                       K, r, codes, scale, top, codes_mma);
     return (int)hipGetLastError();
 }
 

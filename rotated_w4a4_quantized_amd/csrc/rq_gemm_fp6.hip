@@ -609,7 +609,7 @@ __device__ __forceinline__ void pin(Frag &f) {
     asm volatile("" : "+v"(f.p[0]), "+v"(f.p[1]), "+v"(f.p[2]));
 }
 
-template <class C>
+template <class C, bool HAS_LR>
 __global__ void __launch_bounds__(C::NTH, 1)
 gemm_fp6_mma_kernel(Fp6Args a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_BYTES];
@@ -703,6 +703,41 @@ gemm_fp6_mma_kernel(Fp6Args a) {
     // zero points follow the scales ([2][T]): a 16-byte aligned start only
     // when T % 4 == 0, else they are read from global memory at the end
     const bool za_lds = a.za != nullptr && (reinterpret_cast<uintptr_t>(a.za) & 15) == 0;
+    // Low-rank operands of the first 32 coordinates (every DENSE blob has
+    // r >= 32), loaded ahead of the stage loads so that the prologue's wait
+    // covers them: per weight fragment i and k-step kk the lane's eight
+    // nibbles of channel row ..+ li, coordinates 16 kk + 8 lg .. + 7; per
+    // token fragment j its eight bf16 top coefficients.
+    uint32_t lrw[HAS_LR ? C::FN : 1][2];
+    uint4 lrt[HAS_LR ? C::FT : 1][2];
+    auto lr_load = [&](int k0, uint32_t (&w)[HAS_LR ? C::FN : 1], uint4 (&tv)[HAS_LR ? C::FT : 1]) {
+#pragma unroll
+        for (int i = 0; i < C::FN; ++i) {
+            int n = n0 + wn * C::FN * 32 + i * 32 + li;
+            if (n >= a.N) n = a.N - 1;
+            w[i] = *reinterpret_cast<const uint32_t *>(a.Bcan + (int64_t)n * a.ldb + (k0 + 8 * lg) / 2);
+        }
+#pragma unroll
+        for (int j = 0; j < C::FT; ++j) {
+            int64_t t = t0 + wt * C::FT * 32 + j * 32 + li;
+            if (t >= a.T) t = a.T - 1;
+            tv[j] = *reinterpret_cast<const uint4 *>(a.top + t * a.r + k0 + 8 * lg);
+        }
+    };
+    if constexpr (HAS_LR) {
+        if (a.ydt != RQ_I32) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                uint32_t w[C::FN];
+                uint4 tv[C::FT];
+                lr_load(16 * kk, w, tv);
+#pragma unroll
+                for (int i = 0; i < C::FN; ++i) lrw[i][kk] = w[i];
+#pragma unroll
+                for (int j = 0; j < C::FT; ++j) lrt[j][kk] = tv[j];
+            }
+        }
+    }
     if (fast && (wave < 3 || (wave == 3 && za_lds))) {
         const void *src = wave == 0   ? static_cast<const void *>(a.sa + t0)
                           : wave == 1 ? static_cast<const void *>(a.sw + n0)
@@ -781,6 +816,75 @@ gemm_fp6_mma_kernel(Fp6Args a) {
     if (nstage >= 2) stage(nstage - 2, F_{}, F_{});
     stage(nstage - 1, F_{}, F_{});
 
+    // keep the epilogue below the main loop's last MFMAs (register pressure)
+    __builtin_amdgcn_sched_barrier(0);
+    // Low-rank term (DENSE weights, float outputs):
+    //   Y = s_w[n] (s_a[t] acc + sum_{j < r} bf16(u)[t][j] qw[n][j])
+    // The accumulators are first rescaled in place to s_a[t] (acc - zt
+    // wsum[n]) (on full bf16 tiles the offset is already in them); the
+    // bf16 matrix core then adds the products of the top coefficients and
+    // the weights' leading r codes (exact in bf16: |q| <= 8) into the same
+    // registers -- its 32x32 output layout is the FP6 one.  Raw int32
+    // accumulators skip this.
+    const bool lr_on = HAS_LR && a.ydt != RQ_I32;
+    if constexpr (HAS_LR) {
+        if (lr_on) {
+            const float *e_sa = reinterpret_cast<const float *>(lds + C::EPI_OFF);
+            static_for<C::FT>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                const int tl = wt * C::FT * 32 + j * 32 + li;
+                const int64_t t = t0 + tl < a.T ? t0 + tl : a.T - 1;
+                const float sat = fast ? e_sa[tl] : a.sa[t];
+                const float zt = a.za ? a.za[t] : 8.0f;
+                static_for<C::FN>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    static_for<4>([&](auto qc) {
+                        constexpr int q = decltype(qc)::value;
+                        const int nb = n0 + wn * C::FN * 32 + i * 32 + 8 * q + 4 * lg;
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const int n = nb + c < a.N ? nb + c : a.N - 1;
+                            const float off = fast ? 0.0f : zt * (float)a.wsum[n];   // exact
+                            acc[i][j][4 * q + c] = (acc[i][j][4 * q + c] - off) * sat;
+                        }
+                    });
+                });
+            });
+            auto lr_mfma = [&](const uint32_t (&w)[C::FN], const uint4 (&tv)[C::FT]) {
+                v8bf wa[C::FN];
+#pragma unroll
+                for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int q = ((int)(w[i] << (28 - 4 * e))) >> 28;   // sign-extended nibble
+                        wa[i][e] = (__bf16)(float)q;
+                    }
+#pragma unroll
+                for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::FT; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            wa[i], __builtin_bit_cast(v8bf, tv[j]), acc[i][j], 0, 0, 0);
+            };
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                uint32_t w[C::FN];
+                uint4 tv[C::FT];
+#pragma unroll
+                for (int i = 0; i < C::FN; ++i) w[i] = lrw[i][kk];
+#pragma unroll
+                for (int j = 0; j < C::FT; ++j) tv[j] = lrt[j][kk];
+                lr_mfma(w, tv);
+            }
+            for (int k0 = 32; k0 < a.r; k0 += 16) {
+                uint32_t w[C::FN];
+                uint4 tv[C::FT];
+                lr_load(k0, w, tv);
+                lr_mfma(w, tv);
+            }
+        }
+    }
+
     // Epilogue.  Full bf16 tiles: each wave scales its 64 tokens x 128
     // channels into a private slab of the stage buffers (every fragment read
     // of the last stage completed before that stage's barrier; the reads
@@ -788,8 +892,6 @@ gemm_fp6_mma_kernel(Fp6Args a) {
     // 256-byte row segments.  No workgroup barrier.  Other tiles take the
     // general path.
     if (fast) {
-        // keep the epilogue below the main loop's last MFMAs (register pressure)
-        __builtin_amdgcn_sched_barrier(0);
         constexpr int kRowBytes = C::BN / C::WN * 2;      // one token's channels
         constexpr int kSlabStride = kRowBytes + 16;       // padded LDS row
         constexpr int kRows = C::FT * 32;
@@ -797,10 +899,11 @@ gemm_fp6_mma_kernel(Fp6Args a) {
         uint8_t *slab = lds + wave * kRows * kSlabStride;
         const float *e_sa = reinterpret_cast<const float *>(lds + C::EPI_OFF);
         const float *e_sw = reinterpret_cast<const float *>(lds + C::EPI_OFF + 1024);
+        // y = (acc - zt wsum[n]) (s_a post s_w); the offset is already in
+        // acc (with the low-rank term: y = acc s_w, acc already final)
         float sat[C::FT];
 #pragma unroll
-        for (int j = 0; j < C::FT; ++j) sat[j] = e_sa[wt * C::FT * 32 + j * 32 + li] * a.post;
-        // y = (acc - zt wsum[n]) (s_a post s_w); the offset is already in acc
+        for (int j = 0; j < C::FT; ++j) sat[j] = HAS_LR ? 1.0f : e_sa[wt * C::FT * 32 + j * 32 + li] * a.post;
         static_for<C::FN>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
             static_for<4>([&](auto qc) {
@@ -851,12 +954,14 @@ gemm_fp6_mma_kernel(Fp6Args a) {
         }
         return;
     }
+    // general epilogue (with the low-rank term the accumulators are already
+    // s_a (acc - zt wsum) + lr: only s_w remains, post is 1 for DENSE)
     static_for<C::FT>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
         const int64_t t = t0 + wt * C::FT * 32 + j * 32 + li;
         const bool t_ok = t < a.T;
-        const float sat = a.sa[t_ok ? t : a.T - 1];
-        const float zt = a.za ? a.za[t_ok ? t : a.T - 1] : 8.0f;
+        const float sat = lr_on ? 1.0f : a.sa[t_ok ? t : a.T - 1];
+        const float zt = lr_on ? 0.0f : a.za ? a.za[t_ok ? t : a.T - 1] : 8.0f;
         static_for<C::FN>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
             static_for<4>([&](auto qc) {
@@ -924,7 +1029,8 @@ int launch_gemm_fp6(const uint8_t *codes, const uint8_t *codes_mma, const float 
     a.post = 1.0f / (float)hdr->b_div;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (codes_mma) {
-        // Activations already in the FP6 fragment layout (RPBH, r == 0).
+        // Activations already in the FP6 fragment layout (RPBH, or DENSE
+        // with the low-rank term in the epilogue).
         // 256 x 256 tiles on eight waves of 64 tokens x 128 channels: 128
         // accumulators and about 200 registers per lane, so two waves share
         // each SIMD and one wave's LDS and barrier waits overlap the other's
@@ -933,7 +1039,10 @@ int launch_gemm_fp6(const uint8_t *codes, const uint8_t *codes_mma, const float 
         using C = MmaCfg<256, 256, 4, 2>;
         a.tiles_t = (int)((T + C::BT - 1) / C::BT);
         a.tiles_n = (a.N + C::BN - 1) / C::BN;
-        hipLaunchKernelGGL((gemm_fp6_mma_kernel<C>), dim3(a.tiles_t * a.tiles_n), dim3(C::NTH), 0, s, a);
+        if (a.r > 0)
+            hipLaunchKernelGGL((gemm_fp6_mma_kernel<C, true>), dim3(a.tiles_t * a.tiles_n), dim3(C::NTH), 0, s, a);
+        else
+            hipLaunchKernelGGL((gemm_fp6_mma_kernel<C, false>), dim3(a.tiles_t * a.tiles_n), dim3(C::NTH), 0, s, a);
         return (int)hipGetLastError();
     }
     if (a.r > 0) return (int)launch_cfg<CfgMid, true>(a, s);

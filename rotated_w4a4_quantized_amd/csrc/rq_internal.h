@@ -55,8 +55,8 @@ constexpr size_t kDenseScratchBytes = size_t(64) << 20;
 // The calling thread's current device's copy of that scratch (looked up once
 // per device with hipGetSymbolAddress); returns a hipError_t as int.
 int dense_scratch(float **ptr);
-int launch_dense_quant(const float *U, int64_t T, int K, int r, uint8_t *codes,
-                       float *scale, uint16_t *top, void *stream);
+int launch_dense_quant(const float *U, int64_t T, int K, int r, uint8_t *codes, float *scale,
+                       uint16_t *top, uint8_t *codes_mma, void *stream);
 // the int8-MFMA GEMM: 4-bit codes widened in registers (a_bits 4), or int8
 // activation codes against the blob's int8 weight copy (a_bits 8); zero: the
 // per-token zero points of asymmetric 8-bit activations, or null

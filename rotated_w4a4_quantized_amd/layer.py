@@ -39,13 +39,20 @@ def quant_for(w) -> rq.Quant:
     return rq.Quant.lloydmax(rq.lloydmax_gaussian(16), rq.lloydmax_gaussian(1 << w.w_bits))
 
 
+def mma_capable(w) -> bool:
+    """Whether rq_rotate_quant can hand this workload's GEMM its codes in the
+    matrix-core layout: 4-bit integer codes under RPBH or DENSE, and MXFP4."""
+    int4 = w.quant in ("int4", "int4_asym") and w.a_bits == 4
+    return (w.rot in ("rpbh", "dense") and int4) or (w.rot == "rpbh" and w.quant == "mxfp4")
+
+
 class QuantLinear:
     """Device state of one layer instance (w: a datagen.Workload, inp: its
     inputs): rotation, packed weights, buffers.
 
     codes: which activation-code layouts rq_rotate_quant writes and
     rq_w4a4_linear reads -- "canonical" (nibbles or bytes), "mma" (the GEMM's
-    matrix-core layout only; RPBH layers with 4-bit integer codes or MXFP4)
+    matrix-core layout only; see mma_capable)
     or "both" (writes both, the GEMM reads the MMA copy).  MXFP4 layers
     always write the MMA copy, which their GEMM reads."""
 
@@ -59,9 +66,7 @@ class QuantLinear:
         self.drot = self.rot.to_device(device)
         self.X = device_x(inp, device)
         T = w.T
-        mma_ok = w.rot == "rpbh" and ((w.quant in ("int4", "int4_asym") and w.a_bits == 4) or
-                                      w.quant == "mxfp4")
-        if codes not in ("canonical", "mma", "both") or (codes != "canonical" and not mma_ok):
+        if codes not in ("canonical", "mma", "both") or (codes != "canonical" and not mma_capable(w)):
             raise ValueError(f"codes={codes!r} is not available for {w.name}")
         if w.quant == "mxfp4" and codes == "canonical":
             codes = "both"

@@ -112,13 +112,18 @@ def test_rotate_quant_validation_errors():
     assert _rq_call(_rpbh(), lm) == -2      # levels not ascending
     lm = rq.Quant.lloydmax(np.linspace(-2, 2, 16).astype(np.float32), np.arange(4, dtype=np.float32)).c()
     assert _rq_call(_rpbh(), lm) == -2      # levels not bf16-representable
-    # the MMA-layout copy of the codes: RPBH INT4 only, aligned, one of the two outputs
+    # the MMA-layout copy of the codes: INT4 under RPBH or DENSE, aligned, one
+    # of the two outputs
     assert _rq_call(_rpbh(), q, codes=None, mma=None) == -1
     assert _rq_call(_rpbh(), q, codes=None, mma=(1 << 22) + 8) == -4
     dense = rq.c_rotation(rq.RQ_ROT_DENSE, 256, 0, 32, None, None, 1 << 22)
-    assert _rq_call(dense, q, top=1 << 23, ws=1 << 24, wsb=1 << 30, mma=1 << 22) == -6
+    assert _rq_call(dense, q, top=1 << 23, ws=1 << 24, wsb=1 << 30, codes=None, mma=None) == -1
+    assert _rq_call(dense, q, top=1 << 23, ws=1 << 24, wsb=1 << 30, codes=None,
+                    mma=(1 << 22) + 8) == -4
     lm = rq.Quant.lloydmax(rq.lloydmax_gaussian(16), rq.lloydmax_gaussian(4)).c()
     assert _rq_call(_rpbh(), lm, mma=1 << 22) == -6
+    td = rq.c_rotation(rq.RQ_ROT_TRDQ, 256, 64, 0, None, 1 << 21, 1 << 22, 1 << 23, 1 << 24)
+    assert _rq_call(td, q, mma=1 << 22) == -6
 
 
 def test_codes_mma_bytes():
@@ -174,11 +179,19 @@ def test_linear_validation_errors():
     assert L.rq_w4a4_linear(None, None, None, None, None, None, 1, None, None, 0, None) == -1
     assert L.rq_w4a4_linear(*args(hdr, codes=None)) == -1
     assert L.rq_w4a4_linear(*args(hdr, codes=None, mma=(1 << 23) + 4)) == -4
-    # the MMA-layout codes are read for r == 0 only
-    w = datagen.WORKLOADS["pixart"].with_shape(T=4, K=256, N=40)
+    # the MMA-layout codes are read for 4-bit integer activations and MXFP4
+    # only: not with 8-bit activations, nor for the codebook format
+    w = datagen.WORKLOADS["flux_up_w4a8"].with_shape(T=4, K=256, N=40, block=64)
     inp = datagen.make_inputs(w)
-    dh = rq.pack_weights(rq.Rotation.dense(inp["R"], w.r), rq.Quant.int4(), inp["W"]).header
-    assert L.rq_w4a4_linear(*args(dh, mma=1 << 23)) == -6
+    h8 = rq.pack_weights(rq.Rotation.rpbh(inp["sign"], inp["perm"], 64), rq.Quant.integer(8, 4),
+                         inp["W"]).header
+    assert L.rq_w4a4_linear(*args(h8, mma=1 << 23)) == -6
+    w = datagen.WORKLOADS["video"].with_shape(T=4, K=256, N=40)
+    inp = datagen.make_inputs(w)
+    lh = rq.pack_weights(rq.Rotation.rpbh(inp["sign"], inp["perm"], 256),
+                         rq.Quant.lloydmax(rq.lloydmax_gaussian(16), rq.lloydmax_gaussian(4)),
+                         inp["W"]).header
+    assert L.rq_w4a4_linear(*args(lh, mma=1 << 23)) == -6
 
 
 def test_engine_validation_errors():

@@ -16,6 +16,7 @@ import pytest
 
 from rotated_w4a4_quantized_amd import datagen
 from tests import _layer as H
+from rotated_w4a4_quantized_amd.layer import mma_capable
 
 pytestmark = pytest.mark.gpu
 
@@ -34,11 +35,10 @@ def say(msg):
 
 
 def mma_mode(w):
-    """Layer mode for the parity runs: RPBH layers with 4-bit integer codes or
-    MXFP4 write both code layouts and the GEMM reads the MMA copy."""
-    mma = w.rot == "rpbh" and ((w.quant in ("int4", "int4_asym") and w.a_bits == 4) or
-                               w.quant == "mxfp4")
-    return "both" if mma else "canonical"
+    """Layer mode for the parity runs: layers whose codes have a matrix-core
+    layout (4-bit integer codes under RPBH or DENSE, MXFP4) write both code
+    layouts and the GEMM reads the MMA copy."""
+    return "both" if mma_capable(w) else "canonical"
 
 
 def check_act_mx(w, L, act, rows=None):
