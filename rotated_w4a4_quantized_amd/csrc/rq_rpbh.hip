@@ -582,17 +582,22 @@ rpbh_quant_kernel(RpbhArgs a) {
 #pragma unroll
             for (int r = 0; r < kE; ++r) nib[r] = e2m1_code(v[r], inv);
         } else {
-            // exact squared norm on the grid 2^(2E - 36), E = ilogb(max |u|)
+            // exact squared norm on the grid 2^(2E - 36), E = ilogb(max |u|):
+            // each term rint(u^2 2^(36 - 2E)) = rint((u 2^(18 - E))^2) (both
+            // the scaling and the square are exact in fp64) is an integer
+            // below 2^38, so the fp64 sums of at most 16384 of them (below
+            // 2^52) are exact integers in any order
             const int E = amax > 0.0f ? ilogbf(amax) : 0;
-            unsigned long long s = 0;
+            double sd = 0.0;
             if (amax > 0.0f) {
 #pragma unroll
                 for (int r = 0; r < kE; ++r) {
-                    const double sq = (double)v[r] * (double)v[r];
-                    s += (unsigned long long)rint(ldexp(sq, 36 - 2 * E));
+                    const double xs = ldexp((double)v[r], 18 - E);
+                    sd += rint(xs * xs);
                 }
             }
-            for (int off = 1; off < grp; off <<= 1) s += __shfl_xor(s, off, 64);
+            for (int off = 1; off < grp; off <<= 1) sd += __shfl_xor(sd, off, 64);
+            const unsigned long long s = (unsigned long long)sd;
             if ((tid & (grp - 1)) == 0 && s) atomicAdd(&red_sum[it & 1][tl], s);
             lds_barrier();  // B3
             const unsigned long long S = red_sum[it & 1][tl];
