@@ -365,7 +365,9 @@ rq_status rq_codes_mma_bytes(const rq_rotation *rot, int64_t T, size_t *bytes);
  *              then z), T * K / 32 (MXFP4: E8M0 codes)
  *   codes_mma  the GEMM-layout copy rq_rotate_quant can write: INT with
  *              a_bits 4 (RPBH, DENSE): rq_codes_mma_bytes(); MXFP4: the tiled codes
- *              and tiled scales (see rq_rotate_quant); 0 where none exists
+ *              and tiled scales; LLOYDMAX (RPBH): the bf16 levels,
+ *              ceil(T / 32) * (K / 16) * 1024 (see rq_rotate_quant); 0 where
+ *              none exists
  * Any output pointer may be NULL.
  * Errors: descriptor errors, RQ_ERR_SHAPE (T out of range).
  */
@@ -413,14 +415,20 @@ rq_status rq_activation_bytes(const rq_rotation *rot, const rq_quant *q, int64_t
  *           nibbles (two's complement when symmetric, unsigned when
  *           asymmetric; low nibble = even coordinate), INT 8-bit bytes
  *           (int8 / uint8), LLOYDMAX 4-bit indices or MXFP4 E2M1 codes as
- *           nibbles.  May be NULL for INT 4-bit (RPBH, DENSE) and MXFP4
- *           when codes_mma is given.
+ *           nibbles.  May be NULL for INT 4-bit (RPBH, DENSE), MXFP4 and
+ *           LLOYDMAX (RPBH) when codes_mma is given.
  *   scale   device: fp32 [T] s (INT symmetric) or sigma (LLOYDMAX); INT
  *           asymmetric: fp32 [2][T], s[t] then the zero point z[t]; MXFP4:
  *           uint8 [T][K/32] E8M0 codes (the pointer is read as bytes).  May
  *           be NULL for MXFP4 when codes_mma is given.
  *   top     device bf16 [T][r] for DENSE with r > 0, else NULL
  *   codes_mma  optional (NULL: not written), RPBH or DENSE:
+ *           LLOYDMAX (RPBH): a device buffer of rq_activation_bytes()'s
+ *           codes_mma receiving the levels a_levels[code] as bf16 in the
+ *           codebook GEMM's matrix-core order [ceil(T/32)][K/16][64 lanes]
+ *           [8 bf16]: coordinates 16 ks + 8 h .. 16 ks + 8 h + 7 of token t
+ *           are lane t % 32 + 32 h of k-step ks of tile t / 32 (slots of
+ *           tokens past T are left unwritten).
  *           INT 4-bit: a device buffer of rq_codes_mma_bytes() receiving the
  *           same codes in the FP6 GEMM's matrix-core layout.  Tokens come in
  *           tiles of 32 and coordinates in stages of 128; the buffer is
@@ -502,7 +510,7 @@ rq_status rq_rotate_quant_noalloc(const rq_rotation *rot, const rq_quant *q, con
  *   blob    device copy of the whole blob, 16-byte aligned
  *   codes, scale, top  as written by rq_rotate_quant (device); the weights'
  *           format (kind, a_bits) must match the activations' quantizer
- *   codes_mma  optional (INT with a_bits 4, or MXFP4): the
+ *   codes_mma  optional (INT with a_bits 4, MXFP4 or LLOYDMAX): the
  *           codes_mma output of rq_rotate_quant for the same tokens; when
  *           given it is read instead of codes (and, MXFP4, scale), which may
  *           then be NULL

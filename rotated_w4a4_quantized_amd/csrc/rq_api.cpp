@@ -84,14 +84,15 @@ rq_status validate_rotate_quant(const rq_rotation *rot, const rq_quant *q, const
     const bool dense = rot->kind == RQ_ROT_DENSE;
     const bool mx = q->kind == RQ_Q_MXFP4;
     const bool int4 = (q->kind == RQ_Q_INT4_SYM || q->kind == RQ_Q_INT4_ASYM) && q->a_bits == 4;
-    if (codes_mma && !((rpbh && (int4 || mx)) || (dense && int4)))
+    const bool lm = q->kind == RQ_Q_LLOYDMAX;
+    if (codes_mma && !((rpbh && (int4 || mx || lm)) || (dense && int4)))
         return fail(RQ_ERR_UNSUPPORTED,
                     "codes_mma is written for RPBH or DENSE with 4-bit integer codes and for RPBH "
-                    "with MXFP4 only");
+                    "with MXFP4 or LLOYDMAX only");
     if (T == 0) return RQ_OK;
     if (!X || (!codes && !codes_mma) || (!scale && !(mx && codes_mma)))
         return fail(RQ_ERR_NULL, "X, scale and at least one of codes / codes_mma must not be NULL");
-    if (!codes && !((rpbh && (int4 || mx)) || (dense && int4)))
+    if (!codes && !((rpbh && (int4 || mx || lm)) || (dense && int4)))
         return fail(RQ_ERR_NULL, "this rotation and quantizer write the canonical codes: codes is NULL");
     if (dense && rot->r > 0 && !top) return fail(RQ_ERR_NULL, "DENSE with r > 0 needs top");
     if (!aligned16(X) || (codes && !aligned16(codes)) || (scale && !aligned16(scale)) ||
@@ -138,6 +139,8 @@ rq_status rq_activation_bytes(const rq_rotation *rot, const rq_quant *q, int64_t
             *codes_mma = (size_t)mma_codes_bytes(T, Kq);
         else if (rot->kind == RQ_ROT_RPBH && mx)
             *codes_mma = (size_t)mx_mma_bytes(T, K);
+        else if (rot->kind == RQ_ROT_RPBH && q->kind == RQ_Q_LLOYDMAX)
+            *codes_mma = (size_t)cb_mma_bytes(T, K);
     }
     return RQ_OK;
 }
@@ -181,7 +184,7 @@ rq_status rq_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void 
         const int La = 1 << q->a_bits;
         for (int i = 0; i + 1 < La; ++i) th[i] = (q->a_levels[i] + q->a_levels[i + 1]) / 2.0f;
         return hip_status(launch_rpbh_lloydmax(X, xb, T, K, rot->block, rot->sign, rot->perm, th,
-                                               La - 1, codes, scale, stream),
+                                               La - 1, q->a_levels, codes, scale, codes_mma, stream),
                           "rotate_quant launch");
     }
     if (rot->kind == RQ_ROT_TRDQ)
@@ -246,9 +249,8 @@ rq_status rq_w4a4_linear_engine(const rq_weight_header *hdr, const void *blob,
     const bool mx = f == RQ_Q_MXFP4;
     if (y_dtype == RQ_I32 && !intq)
         return fail(RQ_ERR_UNSUPPORTED, "raw accumulators exist for integer weights only");
-    if (codes_mma && !((intq && !a8) || mx))
-        return fail(RQ_ERR_UNSUPPORTED,
-                    "codes_mma is read for 4-bit integer activations and for MXFP4 only");
+    if (codes_mma && intq && a8)
+        return fail(RQ_ERR_UNSUPPORTED, "codes_mma is not read with 8-bit activations");
     if (engine != RQ_ENGINE_AUTO && !intq)
         return fail(RQ_ERR_UNSUPPORTED, "the Lloyd-Max and MXFP4 formats have one engine (RQ_ENGINE_AUTO)");
     if (a8 && engine == RQ_ENGINE_FP6)
@@ -267,7 +269,7 @@ rq_status rq_w4a4_linear_engine(const rq_weight_header *hdr, const void *blob,
     } else {
         if (!scale || (!codes && !codes_mma))
             return fail(RQ_ERR_NULL, "scale and the activation codes must not be NULL");
-        if ((!intq || int8) && !codes) return fail(RQ_ERR_NULL, "this engine needs codes");
+        if (int8 && !codes) return fail(RQ_ERR_NULL, "this engine needs codes");
     }
     if (hdr->r > 0 && !top) return fail(RQ_ERR_NULL, "weights with r > 0 need top");
     if (!aligned16(blob) || (codes && !aligned16(codes)) || (scale && !aligned16(scale)) ||
@@ -289,7 +291,7 @@ rq_status rq_w4a4_linear_engine(const rq_weight_header *hdr, const void *blob,
                                           y_dtype, stream),
                           "w4a4 fp6 gemm launch");
     }
-    return hip_status(launch_gemm_codebook(codes, scale, T, hdr, blob, bias, Y, y_dtype, stream),
+    return hip_status(launch_gemm_codebook(codes, codes_mma, scale, T, hdr, blob, bias, Y, y_dtype, stream),
                       "codebook gemm launch");
 }
 

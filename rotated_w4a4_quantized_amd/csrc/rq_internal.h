@@ -47,7 +47,11 @@ int launch_rpbh_mxfp4(const void *X, int x_bf16, int64_t T, int K, int block,
                       uint8_t *scales, uint8_t *codes_mma, void *stream);
 int launch_rpbh_lloydmax(const void *X, int x_bf16, int64_t T, int K, int block,
                          const int8_t *sign, const int32_t *perm, const float *thresholds,
-                         int n_thresholds, uint8_t *codes, float *sigma, void *stream);
+                         int n_thresholds, const float *levels, uint8_t *codes, float *sigma,
+                         uint8_t *codes_mma, void *stream);
+// bytes of the Lloyd-Max activations in the codebook GEMM's bf16 fragment
+// layout: [ceil(T / 32)][K / 16][64 lanes][16 bytes]
+inline int64_t cb_mma_bytes(int64_t T, int K) { return (T + 31) / 32 * (int64_t)(K / 16) * 1024; }
 int launch_dense_rotate(const void *X, int x_bf16, int64_t T, int K, const float *R,
                         float *U, void *stream);
 // Largest fp32 staging of rq_rotate_quant_noalloc (T * K * 4 bytes, DENSE).
@@ -81,8 +85,8 @@ inline int64_t mx_mma_bytes(int64_t T, int K) {
     const int64_t tiles = (T + 31) / 32;
     return tiles * (K / 32) * 512 + (int64_t)((K + 127) / 128) * tiles * 128;
 }
-int launch_gemm_codebook(const uint8_t *codes, const float *sigma, int64_t T,
-                         const rq_weight_header *hdr, const void *blob,
-                         const float *bias, void *Y, int y_dtype, void *stream);
+int launch_gemm_codebook(const uint8_t *codes, const uint8_t *codes_mma, const float *sigma, int64_t T,
+                         const rq_weight_header *hdr, const void *blob, const float *bias,
+                         void *Y, int y_dtype, void *stream);
 
 }  // namespace rq

@@ -42,6 +42,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstring>
+
 #include "rq_fp6.h"
 #include "rq_internal.h"
 
@@ -277,6 +279,7 @@ struct RpbhArgs {
     int mx_tiles;         // MXFP4: ceil(T / 32) (tiled codes_mma layout)
     float th[15];         // codebook thresholds (Lloyd-Max)
     int th_sym;           // th[7] == 0 and th[i] == -th[14 - i] exactly
+    uint32_t lev[16];     // Lloyd-Max: bf16 bits of the 16 levels (codes_mma)
 };
 
 template <bool BF16>
@@ -311,6 +314,8 @@ rpbh_quant_kernel(RpbhArgs a) {
     __shared__ unsigned red_max[2][kMaxTpw];
     __shared__ unsigned red_min[2][kMaxTpw];   // asymmetric INT4 (keys)
     __shared__ unsigned long long red_sum[2][kMaxTpw];
+    // Lloyd-Max with codes_mma: packed byte of two indices -> their two bf16 levels
+    __shared__ uint32_t lev_pair[QK == 1 ? 256 : 1];
     const int K = a.K;
     const int tid = threadIdx.x;
     const int tl = tid / a.tpt;
@@ -346,6 +351,10 @@ rpbh_quant_kernel(RpbhArgs a) {
     };
     // the first token's row is in flight while the prologue runs
     if (base >= 0) fetch(base);
+    if constexpr (QK == 1) {
+        // (visible to every thread after the prologue's barriers)
+        for (int i = tid; i < 256; i += blockDim.x) lev_pair[i] = a.lev[i & 15] | (a.lev[i >> 4] << 16);
+    }
 
     // ---- prologue: gather offsets, source-side sign masks -----------------
     // Thread tt owns destination coordinates j = 32 tt + r: it reads perm[j]
@@ -695,6 +704,23 @@ rpbh_quant_kernel(RpbhArgs a) {
             }
             if constexpr (QK == 0 || QK == 2)
                 if (a.codes_mma && !grouped) store_chunk_mma(a.codes_mma, tok, a.mma_stages, tt, chunk, 0u);
+            if constexpr (QK == 1) {
+                // the levels in bf16, in the codebook GEMM's fragment order
+                // [32-token tile][16-coordinate k-step][lane][16 bytes]:
+                // coordinates 16 ks + 8 h .. + 7 of token t sit in lane
+                // t % 32 + 32 h of k-step ks
+                if (a.codes_mma) {
+                    const uint32_t wq[4] = {chunk.x, chunk.y, chunk.z, chunk.w};
+                    uint8_t *tile = a.codes_mma + (tok >> 5) * (int64_t)(K / 16) * 1024 + (tok & 31) * 16;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const uint32_t w = wq[c];
+                        const uint4 v = make_uint4(lev_pair[w & 0xFFu], lev_pair[(w >> 8) & 0xFFu],
+                                                   lev_pair[(w >> 16) & 0xFFu], lev_pair[w >> 24]);
+                        *reinterpret_cast<uint4 *>(tile + (2 * tt + (c >> 1)) * 1024 + 512 * (c & 1)) = v;
+                    }
+                }
+            }
             if constexpr (MX) {
                 // E8M0 code of block tt: canonical [T][K/32], and the tiled
                 // copies [tile][K/32][32][16] (codes) and
@@ -841,6 +867,7 @@ RpbhArgs make_args(const void *X, int64_t T, int K, const int8_t *sign, const in
     a.mx_tiles = (int)((T + 31) / 32);
     for (int i = 0; i < 15; ++i) a.th[i] = 0.0f;
     a.th_sym = 0;
+    for (int i = 0; i < 16; ++i) a.lev[i] = 0u;
     return a;
 }
 
@@ -871,10 +898,14 @@ int launch_rpbh_mxfp4(const void *X, int x_bf16, int64_t T, int K, int block, co
 
 int launch_rpbh_lloydmax(const void *X, int x_bf16, int64_t T, int K, int block,
                          const int8_t *sign, const int32_t *perm, const float *thresholds,
-                         int n_thresholds, uint8_t *codes, float *sigma, void *stream) {
+                         int n_thresholds, const float *levels, uint8_t *codes, float *sigma,
+                         uint8_t *codes_mma, void *stream) {
     if (n_thresholds != 15) return (int)hipErrorInvalidValue;
-    RpbhArgs a = make_args(X, T, K, sign, perm, codes, nullptr, sigma);
+    RpbhArgs a = make_args(X, T, K, sign, perm, codes, codes_mma, sigma);
     for (int i = 0; i < 15; ++i) a.th[i] = thresholds[i];
+    uint32_t lb[16];
+    std::memcpy(lb, levels, sizeof lb);   // bf16-representable: the top halves
+    for (int i = 0; i < 16; ++i) a.lev[i] = lb[i] >> 16;
     // ascending thresholds of a book symmetric about 0 (exact float equality)
     a.th_sym = a.th[7] == 0.0f ? 1 : 0;
     for (int i = 0; i < 15; ++i)

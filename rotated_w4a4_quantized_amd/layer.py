@@ -41,9 +41,10 @@ def quant_for(w) -> rq.Quant:
 
 def mma_capable(w) -> bool:
     """Whether rq_rotate_quant can hand this workload's GEMM its codes in the
-    matrix-core layout: 4-bit integer codes under RPBH or DENSE, and MXFP4."""
+    matrix-core layout: 4-bit integer codes under RPBH or DENSE, and MXFP4
+    and Lloyd-Max codes (as their bf16 levels) under RPBH."""
     int4 = w.quant in ("int4", "int4_asym") and w.a_bits == 4
-    return (w.rot in ("rpbh", "dense") and int4) or (w.rot == "rpbh" and w.quant == "mxfp4")
+    return (w.rot in ("rpbh", "dense") and int4) or (w.rot == "rpbh" and w.quant in ("mxfp4", "lloydmax"))
 
 
 class QuantLinear:

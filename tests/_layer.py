@@ -168,6 +168,12 @@ def decode_codes_mma(buf, T, Kq):
     return out[:T, :Kq], not tops[:T, :Kq].any()
 
 
+def unpack_nibbles(codes):
+    """Canonical unsigned nibbles [T][K/2] -> indices [T][K] (low nibble first)."""
+    codes = np.asarray(codes, np.uint8)
+    return np.stack([codes & 15, codes >> 4], -1).reshape(codes.shape[0], -1).astype(np.int64)
+
+
 def unpack_codes(codes):
     """Canonical nibbles [T][Kq/2] -> INT4 codes [T][Kq]."""
     codes = np.asarray(codes, np.uint8)
@@ -176,3 +182,13 @@ def unpack_codes(codes):
     q = np.stack([lo, hi], -1).reshape(codes.shape[0], -1)
     return np.where(q >= 8, q - 16, q)
 
+
+def decode_cb_mma(buf, T, K):
+    """bf16 bits [T][K] from the Lloyd-Max codes_mma output, read as rq.h
+    documents it: [32-token tile][16-coordinate k-step][lane 0..63][8 bf16];
+    coordinate 16 ks + 8 h + e of token t is element e of lane t % 32 + 32 h."""
+    tiles = -(-T // 32)
+    v = np.ascontiguousarray(buf, np.uint8)[:tiles * (K // 16) * 1024].view(np.uint16)
+    v = v.reshape(tiles, K // 16, 2, 32, 8)            # [tile][ks][h][t32][e]
+    v = v.transpose(0, 3, 1, 2, 4).reshape(tiles * 32, K)
+    return v[:T]

@@ -121,7 +121,8 @@ def test_rotate_quant_validation_errors():
     assert _rq_call(dense, q, top=1 << 23, ws=1 << 24, wsb=1 << 30, codes=None,
                     mma=(1 << 22) + 8) == -4
     lm = rq.Quant.lloydmax(rq.lloydmax_gaussian(16), rq.lloydmax_gaussian(4)).c()
-    assert _rq_call(_rpbh(), lm, mma=1 << 22) == -6
+    assert _rq_call(_rpbh(), lm, codes=None, mma=None) == -1
+    assert _rq_call(_rpbh(), lm, codes=None, mma=(1 << 22) + 8) == -4
     td = rq.c_rotation(rq.RQ_ROT_TRDQ, 256, 64, 0, None, 1 << 21, 1 << 22, 1 << 23, 1 << 24)
     assert _rq_call(td, q, mma=1 << 22) == -6
 
@@ -179,8 +180,8 @@ def test_linear_validation_errors():
     assert L.rq_w4a4_linear(None, None, None, None, None, None, 1, None, None, 0, None) == -1
     assert L.rq_w4a4_linear(*args(hdr, codes=None)) == -1
     assert L.rq_w4a4_linear(*args(hdr, codes=None, mma=(1 << 23) + 4)) == -4
-    # the MMA-layout codes are read for 4-bit integer activations and MXFP4
-    # only: not with 8-bit activations, nor for the codebook format
+    # the MMA-layout codes are not read with 8-bit activations; the codebook
+    # format reads its bf16 level fragments (16-byte aligned)
     w = datagen.WORKLOADS["flux_up_w4a8"].with_shape(T=4, K=256, N=40, block=64)
     inp = datagen.make_inputs(w)
     h8 = rq.pack_weights(rq.Rotation.rpbh(inp["sign"], inp["perm"], 64), rq.Quant.integer(8, 4),
@@ -191,7 +192,8 @@ def test_linear_validation_errors():
     lh = rq.pack_weights(rq.Rotation.rpbh(inp["sign"], inp["perm"], 256),
                          rq.Quant.lloydmax(rq.lloydmax_gaussian(16), rq.lloydmax_gaussian(4)),
                          inp["W"]).header
-    assert L.rq_w4a4_linear(*args(lh, mma=1 << 23)) == -6
+    assert L.rq_w4a4_linear(*args(lh, mma=(1 << 23) + 4)) == -4
+    assert L.rq_w4a4_linear(*args(lh, codes=None)) == -1
 
 
 def test_engine_validation_errors():

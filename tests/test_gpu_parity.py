@@ -83,7 +83,7 @@ def check_act(w, L, act, rows=None):
         f"scale mismatch in {int(np.sum(scale != act['scale']))} tokens"
     bad = np.nonzero(np.any(codes != act["codes"], axis=1))[0]
     assert bad.size == 0, f"codes differ in {bad.size} tokens, first {bad[:5]}"
-    if L.codes_mma is not None:
+    if L.codes_mma is not None and w.quant in ("int4", "int4_asym"):
         dec, top_clear = H.decode_codes_mma(L.codes_mma.cpu().numpy(), w.T, w.Kq)
         if rows is not None:
             dec = dec[rows]
@@ -93,6 +93,15 @@ def check_act(w, L, act, rows=None):
             ref = (ref & 15) - 8
         bad = np.nonzero(np.any(dec != ref, axis=1))[0]
         assert bad.size == 0, f"codes_mma differs in {bad.size} tokens, first {bad[:5]}"
+    if w.quant == "lloydmax" and L.codes_mma is not None:
+        # the bf16 levels of the codes, in the codebook GEMM's fragment order
+        dec = H.decode_cb_mma(L.codes_mma.cpu().numpy(), w.T, w.K)
+        if rows is not None:
+            dec = dec[rows]
+        lev = datagen.f32_to_bf16_bits(H.orc.codebook_bf16(16).astype(np.float32))
+        ref = lev[H.unpack_nibbles(act["codes"])]
+        bad = np.nonzero(np.any(dec != ref, axis=1))[0]
+        assert bad.size == 0, f"bf16 level fragments differ in {bad.size} tokens, first {bad[:5]}"
     if w.r:
         top = L.top.cpu().numpy().view(np.uint16)
         if rows is not None:
@@ -171,6 +180,13 @@ def small_parity(w, inp):
     err = H.rel_err(y, yhat)
     say(f"  fp32 output max floored rel err {err:.3e}")
     assert err <= H.REL_TOL
+    if w.quant == "lloydmax" and L.codes_mma is not None and L.codes is not None:
+        # the same GEMM decoding the canonical indices itself
+        Yc = torch.empty((w.T, w.N), dtype=torch.float32, device="cuda")
+        L.linear(Yc, use_mma=False)
+        err = H.rel_err(Yc.cpu().numpy().ravel(), yhat)
+        say(f"  fp32 output (index-decoding GEMM) max floored rel err {err:.3e}")
+        assert err <= H.REL_TOL
     if w.quant in ("int4", "int4_asym"):
         ref = H.oracle_raw_acc(w, act, wts)
         acc = L.raw_acc().cpu().numpy().astype(np.int64)
