@@ -23,75 +23,162 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // DENSE ("DiRotQ" abstract): u = x R as one fp32 fma chain per output over k
-// ascending (register-tiled: each thread owns an 8 x 8 block of (token,
+// ascending (register-tiled: each thread owns an 8 x CW block of (token,
 // column) outputs and walks k in order), then per-token quantization of the
 // coordinates [r, K) with the top r kept in bf16.
+//
+// A workgroup computes 128 tokens x 16 CW columns in chunks of 16 k: the
+// chunk's x tile (transposed, [k][token]) and R tile ([k][column]) sit in one
+// of two LDS buffers while the next chunk's tiles are loaded into registers
+// (16-byte global loads) and written to the other, so each chunk takes one
+// barrier.  The column-tile width (CW = 8, 6 or 4 columns per thread) is
+// chosen per shape so that the workgroups spread evenly over the CUs: every
+// workgroup is resident at once and a CU holding one more than the others
+// sets the time.
 // ---------------------------------------------------------------------------
 constexpr int kDT = 128;   // tokens per tile
-constexpr int kDJ = 128;   // output columns per tile
-constexpr int kDK = 16;    // k per LDS stage
+constexpr int kDK = 16;    // k per LDS chunk
 
-template <bool BF16>
-__global__ void __launch_bounds__(256)
+// an empty asm that takes and returns a row of sums: code before it must
+// have produced them
+template <int CW>
+__device__ __forceinline__ void pin_row(float (&r)[CW]) {
+    if constexpr (CW == 8)
+        asm volatile("" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7]));
+    else if constexpr (CW == 6)
+        asm volatile("" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]));
+    else
+        asm volatile("" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
+}
+
+template <bool BF16, int CW>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 dense_rotate_kernel(const void *__restrict__ X, int64_t T, int K, const float *__restrict__ R,
                     float *__restrict__ U) {
-    __shared__ float xs[kDK][kDT + 4];  // x^T tile: [k][token]
-    __shared__ float rs[kDK][kDJ + 4];  // R tile:   [k][column]
+    constexpr int DJ = 16 * CW;                 // columns per tile
+    constexpr int XL = BF16 ? 1 : 2;            // 16-byte x loads per thread per chunk
+    constexpr int RL = (kDK * DJ / 4 + 255) / 256;   // 16-byte R loads per thread per chunk
+    __shared__ __attribute__((aligned(16))) float xs[2][kDK][kDT + 4];  // x^T: [k][token]
+    __shared__ __attribute__((aligned(16))) float rs[2][kDK][DJ + 4];   // R:   [k][column]
     const int tid = threadIdx.x;
-    const int tx = tid & 15, ty = tid >> 4;  // 16 x 16 threads, 8 x 8 outputs each
+    const int tx = tid & 15, ty = tid >> 4;    // 16 x 16 threads, 8 x CW outputs each
     const int64_t t0 = (int64_t)blockIdx.y * kDT;
-    const int j0 = blockIdx.x * kDJ;
-    float acc[8][8];
+    const int j0 = blockIdx.x * DJ;
+    float acc[8][CW];
 #pragma unroll
     for (int a = 0; a < 8; ++a)
 #pragma unroll
-        for (int b = 0; b < 8; ++b) acc[a][b] = 0.0f;
-    for (int k0 = 0; k0 < K; k0 += kDK) {
-        // x tile: 128 tokens x 16 k; thread loads 8 values
+        for (int b = 0; b < CW; ++b) acc[a][b] = 0.0f;
+
+    // x: load i of thread tid covers token (tid + 256 i) / Q, k-quarter
+    // (tid + 256 i) % Q of the chunk (Q = 2 for bf16: 8 values per 16 bytes;
+    // 4 for fp32); R: load i covers row q / (DJ / 4), columns 4 (q % (DJ / 4))
+    // of the chunk, q = tid + 256 i (loads past the tile or the matrix are
+    // skipped; their slots hold zeros that no output reads)
+    constexpr int Q = BF16 ? 2 : 4;
+    uint4 xr[XL];
+    float4 rr[RL];
+    auto load = [&](int k0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int li = tid + 256 * e;   // 0..2047
-            const int tt = li / kDK, kk = li % kDK;
-            int64_t tok = t0 + tt;
+        for (int i = 0; i < XL; ++i) {
+            const int q = tid + 256 * i;
+            int64_t tok = t0 + q / Q;
             if (tok >= T) tok = T - 1;
-            float xv;
-            if constexpr (BF16)
-                xv = __uint_as_float((uint32_t)static_cast<const uint16_t *>(X)[tok * K + k0 + kk] << 16);
-            else
-                xv = static_cast<const float *>(X)[tok * K + k0 + kk];
-            xs[kk][tt] = xv;
+            const int kq = (q % Q) * (16 / (BF16 ? 2 : 4));   // first k of this load
+            const uint8_t *src = static_cast<const uint8_t *>(X) + (tok * K + k0 + kq) * (BF16 ? 2 : 4);
+            xr[i] = *reinterpret_cast<const uint4 *>(src);
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int li = tid + 256 * e;
-            const int kk = li / kDJ, jj = li % kDJ;
-            const int j = j0 + jj;
-            rs[kk][jj] = j < K ? R[(int64_t)(k0 + kk) * K + j] : 0.0f;
+        for (int i = 0; i < RL; ++i) {
+            const int q = tid + 256 * i;
+            const int kk = q / (DJ / 4), jj = 4 * (q % (DJ / 4));
+            rr[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (kk < kDK && j0 + jj < K)
+                rr[i] = *reinterpret_cast<const float4 *>(R + (int64_t)(k0 + kk) * K + j0 + jj);
         }
-        __syncthreads();
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < XL; ++i) {
+            const int q = tid + 256 * i;
+            const int tt = q / Q;
+            const int kq = (q % Q) * (16 / (BF16 ? 2 : 4));
+            const uint32_t w[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+            if constexpr (BF16) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    xs[buf][kq + e][tt] = __uint_as_float(e & 1 ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xs[buf][kq + e][tt] = __uint_as_float(w[e]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < RL; ++i) {
+            const int q = tid + 256 * i;
+            const int kk = q / (DJ / 4), jj = 4 * (q % (DJ / 4));
+            if (kk < kDK) *reinterpret_cast<float4 *>(&rs[buf][kk][jj]) = rr[i];
+        }
+    };
+
+    const int nchunk = K / kDK;
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int c = 0; c < nchunk; ++c) {
+        const int buf = c & 1;
+        if (c + 1 < nchunk) load((c + 1) * kDK);   // in flight during the FMAs
+        // operands of step kk + 1 are read while step kk's FMAs run (two
+        // register sets; the empty asm statements, which the compiler may not
+        // move memory accesses across, keep it from hoisting every read of
+        // the chunk, which would cost occupancy)
+        float xa[2][8], rb[2][CW];
+        auto rd = [&](int kk, int p) {
+#pragma unroll
+            for (int a = 0; a < 8; ++a) xa[p][a] = xs[buf][kk][ty * 8 + a];
+#pragma unroll
+            for (int b = 0; b < CW; ++b) rb[p][b] = rs[buf][kk][tx * CW + b];
+        };
+        rd(0, 0);
 #pragma unroll
         for (int kk = 0; kk < kDK; ++kk) {
-            float xa[8], rb[8];
-#pragma unroll
-            for (int a = 0; a < 8; ++a) xa[a] = xs[kk][ty * 8 + a];
-#pragma unroll
-            for (int b = 0; b < 8; ++b) rb[b] = rs[kk][tx * 8 + b];
+            if (kk + 1 < kDK) rd(kk + 1, (kk + 1) & 1);
+            asm volatile("" ::: "memory");
 #pragma unroll
             for (int a = 0; a < 8; ++a)
 #pragma unroll
-                for (int b = 0; b < 8; ++b) acc[a][b] = fmaf(xa[a], rb[b], acc[a][b]);
+                for (int b = 0; b < CW; ++b) acc[a][b] = fmaf(xa[kk & 1][a], rb[kk & 1][b], acc[a][b]);
+            // the step's sums are due here (else the compiler sinks every FMA
+            // of the chunk below its last read)
+#pragma unroll
+            for (int a = 0; a < 8; ++a) pin_row(acc[a]);
         }
+        // the other buffer was last read before the previous barrier
+        if (c + 1 < nchunk) store(buf ^ 1);
         __syncthreads();
     }
+    // this thread's columns jb .. jb + CW - 1 (those below K), rows t0 + 8 ty + a
+    const int jb = j0 + tx * CW;
+    const bool full = jb + CW <= K;
+    float *u = U + (t0 + ty * 8) * K + jb;
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
-        const int64_t tok = t0 + ty * 8 + a;
-        if (tok >= T) continue;
+        if (t0 + ty * 8 + a >= T) break;
+        if (full) {
+            if constexpr (CW % 4 == 0) {
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const int j = j0 + tx * 8 + b;
-            if (j < K) U[tok * K + j] = acc[a][b];
+                for (int b = 0; b < CW; b += 4)
+                    *reinterpret_cast<float4 *>(u + b) = make_float4(acc[a][b], acc[a][b + 1], acc[a][b + 2], acc[a][b + 3]);
+            } else {
+#pragma unroll
+                for (int b = 0; b < CW; b += 2) *reinterpret_cast<float2 *>(u + b) = make_float2(acc[a][b], acc[a][b + 1]);
+            }
+        } else {
+#pragma unroll
+            for (int b = 0; b < CW; ++b)
+                if (jb + b < K) u[b] = acc[a][b];
         }
+        u += K;
     }
 }
 
@@ -177,11 +264,31 @@ int dense_scratch(float **ptr) {
 int launch_dense_rotate(const void *X, int x_bf16, int64_t T, int K, const float *R, float *U,
                         void *stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    dim3 grid((K + kDJ - 1) / kDJ, (unsigned)((T + kDT - 1) / kDT));
-    if (x_bf16)
-        hipLaunchKernelGGL(dense_rotate_kernel<true>, grid, dim3(256), 0, s, X, T, K, R, U);
-    else
-        hipLaunchKernelGGL(dense_rotate_kernel<false>, grid, dim3(256), 0, s, X, T, K, R, U);
+    // columns per thread: the width whose workgroup count spreads most evenly
+    // over the CUs (every workgroup is resident at once), ties to the wider
+    const int64_t ttiles = (T + kDT - 1) / kDT;
+    const int64_t cus = device_cus();
+    int cw = 8;
+    double best = -1.0;
+    for (int c : {8, 6, 4}) {
+        const int64_t n = ttiles * ((K + 16 * c - 1) / (16 * c));
+        const double eff = (double)n / (double)(((n + cus - 1) / cus) * cus);
+        if (eff > best + 1e-9) {
+            best = eff;
+            cw = c;
+        }
+    }
+    const dim3 grid((unsigned)((K + 16 * cw - 1) / (16 * cw)), (unsigned)ttiles);
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, X, T, K, R, U); };
+    if (x_bf16) {
+        if (cw == 8) go(dense_rotate_kernel<true, 8>);
+        else if (cw == 6) go(dense_rotate_kernel<true, 6>);
+        else go(dense_rotate_kernel<true, 4>);
+    } else {
+        if (cw == 8) go(dense_rotate_kernel<false, 8>);
+        else if (cw == 6) go(dense_rotate_kernel<false, 6>);
+        else go(dense_rotate_kernel<false, 4>);
+    }
     return (int)hipGetLastError();
 }
 

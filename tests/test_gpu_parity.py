@@ -133,6 +133,9 @@ SMALL = [
     ("flux_down", dict(T=131, K=12288, N=136)),
     ("video", dict(T=190, N=264)),
     ("pixart", dict(T=200, N=170)),
+    # dense rotation tiles with ragged column and token edges
+    ("pixart", dict(T=77, K=160, N=40)),
+    ("pixart", dict(T=260, K=416, N=96)),
     ("tiny", dict(T=70, K=1024, N=128, block=1024)),
     ("tiny", dict(T=65, K=96, N=40, block=2)),
     ("tiny", dict(T=33, K=32, N=7, block=8)),
@@ -464,6 +467,9 @@ INT8_ENGINE = [
     ("flux_up", dict(T=257, K=3072, N=384)),
     ("flux_down", dict(T=131, K=12288, N=136)),
     ("pixart", dict(T=200, N=170)),
+    # dense rotation tiles with ragged column and token edges
+    ("pixart", dict(T=77, K=160, N=40)),
+    ("pixart", dict(T=260, K=416, N=96)),
     ("tiny", dict(T=65, K=96, N=40, block=2)),
     ("flux_up", dict(T=600, K=1024, N=800, block=256)),
 ]
