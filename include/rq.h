@@ -343,8 +343,12 @@ rq_status rq_weight_set_member(const void *set_host, int32_t step, int32_t *grou
                                const rq_weight_header **hdr, int64_t *offset);
 
 /*
- * Bytes of device workspace rq_rotate_quant needs (0 for RPBH and TRDQ;
- * T*K*4 for DENSE, which stages the rotated tokens in fp32).
+ * Bytes of device workspace rq_rotate_quant takes: 0 for RPBH; T*K*4 for
+ * DENSE, which stages the rotated tokens in fp32 (required); T*K*8 + T*8
+ * for TRDQ (optional: with it the two block rotations run as tiled launches
+ * through fp32 buffers, each rotation matrix read once per 128 tokens; without
+ * it one pass per few tokens holds the rows in LDS; the codes are the same
+ * bit for bit).
  */
 rq_status rq_rotate_quant_workspace_bytes(const rq_rotation *rot, const rq_quant *q,
                                           int64_t T, size_t *bytes);
@@ -451,7 +455,8 @@ rq_status rq_activation_bytes(const rq_rotation *rot, const rq_quant *q, int64_t
  *           Bytes of tokens past T and coordinates past K - r are left
  *           unwritten.
  *   workspace, workspace_bytes  device scratch of at least
- *           rq_rotate_quant_workspace_bytes() (NULL/0 when that is 0)
+ *           rq_rotate_quant_workspace_bytes() (NULL/0 when that is 0; TRDQ:
+ *           NULL or at least that size), 16-byte aligned
  *   stream  hipStream_t
  * Errors: RQ_ERR_NULL, RQ_ERR_SHAPE, RQ_ERR_DTYPE, RQ_ERR_ALIGN,
  *         RQ_ERR_UNSUPPORTED, RQ_ERR_HIP.
@@ -468,7 +473,8 @@ rq_status rq_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void 
  * results bit for bit.  DENSE stages its fp32 rotated tokens in a scratch
  * array inside the library (one per device, 64 MiB, held from the module's
  * load until the process ends; its address is looked up once per device at
- * the first call there); RPBH uses none.  The call allocates nothing and
+ * the first call there); RPBH uses none and TRDQ runs its workspace-free
+ * one-pass form.  The call allocates nothing and
  * calls no allocating routine.  Every call on a device shares that device's
  * scratch: DENSE calls that overlap on one device (other streams, other host
  * threads) race and must be serialized by the caller.

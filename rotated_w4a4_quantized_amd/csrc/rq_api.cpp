@@ -115,7 +115,9 @@ rq_status rq_rotate_quant_workspace_bytes(const rq_rotation *rot, const rq_quant
     if ((st = check_quant(rot, q)) != RQ_OK) return st;
     if (!bytes) return fail(RQ_ERR_NULL, "bytes is NULL");
     if (T < 0 || T >= (int64_t(1) << 31)) return fail(RQ_ERR_SHAPE, "T out of range");
-    *bytes = rot->kind == RQ_ROT_DENSE ? (size_t)T * (size_t)rot->K * sizeof(float) : 0;
+    *bytes = rot->kind == RQ_ROT_DENSE  ? (size_t)T * (size_t)rot->K * sizeof(float)
+             : rot->kind == RQ_ROT_TRDQ ? trdq_workspace_bytes(T, rot->K)
+                                        : 0;
     return RQ_OK;
 }
 
@@ -185,6 +187,16 @@ rq_status rq_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void 
         for (int i = 0; i + 1 < La; ++i) th[i] = (q->a_levels[i] + q->a_levels[i + 1]) / 2.0f;
         return hip_status(launch_rpbh_lloydmax(X, xb, T, K, rot->block, rot->sign, rot->perm, th,
                                                La - 1, q->a_levels, codes, scale, codes_mma, stream),
+                          "rotate_quant launch");
+    }
+    if (rot->kind == RQ_ROT_TRDQ && workspace) {
+        const size_t need = trdq_workspace_bytes(T, K);
+        if (workspace_bytes < need)
+            return fail(RQ_ERR_SHAPE, "TRDQ: a workspace, when given, needs " + std::to_string(need) + " bytes");
+        if (!aligned16(workspace)) return fail(RQ_ERR_ALIGN, "workspace must be 16-byte aligned");
+        return hip_status(launch_trdq_tiled(X, xb, T, K, rot->block, rot->smooth, rot->R, rot->perm,
+                                            rot->R2, codes, scale, q->kind == RQ_Q_INT4_ASYM ? 1 : 0,
+                                            q->a_bits, workspace, stream),
                           "rotate_quant launch");
     }
     if (rot->kind == RQ_ROT_TRDQ)

@@ -72,6 +72,13 @@ int launch_gemm_w4a4(const uint8_t *codes, const float *scale, const float *zero
 int launch_trdq(const void *X, int x_bf16, int64_t T, int K, int block, const float *smooth,
                 const float *R1, const int32_t *perm, const float *R2, uint8_t *codes,
                 float *scale, int asym, int a_bits, void *stream);
+// TR-DQ with a workspace: two tiled block-rotation launches through fp32
+// buffers and a quantize launch (bit-identical codes); the workspace holds
+// Z and U, fp32 [T][K] each, then the per-token extremes, uint32 [2][T]
+size_t trdq_workspace_bytes(int64_t T, int K);
+int launch_trdq_tiled(const void *X, int x_bf16, int64_t T, int K, int block, const float *smooth,
+                      const float *R1, const int32_t *perm, const float *R2, uint8_t *codes,
+                      float *scale, int asym, int a_bits, void *workspace, void *stream);
 // zero: per-token zero points of INT4_ASYM activations, or null (symmetric)
 int launch_gemm_fp6(const uint8_t *codes, const uint8_t *codes_mma, const float *scale,
                     const float *zero, const uint16_t *top, int64_t T,

@@ -260,6 +260,298 @@ hipError_t launch_tok(const TrdqArgs &a, int asym, int a_bits, hipStream_t s) {
                 : go(trdq_quant_kernel<TOK, NBMAX, BF16, 4, false>);
 }
 
+// ---------------------------------------------------------------------------
+// Tiled form (a workspace is given): three launches.
+//   rot 1   z = (x * smooth) BlockDiag(R1)          -> Zt, fp32 [K][Tp], token
+//           index fastest (Tp = T rounded up to 128), so that rot 2 gathers
+//           whole 512-byte column runs
+//   rot 2   u = z[perm] BlockDiag(R2)               -> U, fp32 [T][K], and the
+//           per-token extremes (atomics on [2][T] keys)
+//   quant   codes and scales from U and the extremes
+// A rotation workgroup owns 128 tokens x DJ = 16 CW columns of one block and
+// walks that block's b inputs in chunks of 16: the chunk's input tile
+// (transposed, [k][token]) and R tile sit in one of two LDS buffers while the
+// next chunk is loaded into registers and written to the other (one barrier
+// per chunk); each thread keeps 8 tokens x CW columns of sums.  Every output
+// is the same FMA chain as in the one-pass kernel (the block's inputs
+// ascending from +0), so the codes agree bit for bit; R is read once per 128
+// tokens instead of once per workgroup of 2 or 4 tokens.
+// ---------------------------------------------------------------------------
+constexpr int kTT = 128;   // tokens per rotation tile
+constexpr int kTK = 16;    // k per chunk
+
+struct TileArgs {
+    const void *X;          // STEP 1: x [T][K] (bf16 or fp32); STEP 2: Zt
+    float *Out;             // STEP 1: Zt; STEP 2: U
+    const float *smooth;    // STEP 1
+    const int32_t *perm;    // STEP 2
+    const float *R;         // [K/b][b][b]
+    unsigned *stat;         // [2][T]: max key, then min key (asymmetric)
+    int64_t T;
+    int64_t Tp;             // Zt row stride (T rounded up to 128)
+    int K, b;
+};
+
+template <int CW>
+__device__ __forceinline__ void pin_sums(float (&r)[CW]) {
+    if constexpr (CW == 8)
+        asm volatile("" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7]));
+    else if constexpr (CW == 4)
+        asm volatile("" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
+    else if constexpr (CW == 2)
+        asm volatile("" : "+v"(r[0]), "+v"(r[1]));
+    else
+        asm volatile("" : "+v"(r[0]));
+}
+
+// STEP 1: inputs x * smooth (BF16: x is bf16); STEP 2: inputs Z[perm[k]],
+// per-token extremes of the outputs (ASYM: min and max, else max |u|).
+template <int STEP, bool BF16, int CW, bool ASYM>
+__global__ void __launch_bounds__(256)
+trdq_tile_kernel(TileArgs a) {
+    constexpr int DJ = 16 * CW;
+    constexpr int RL = (kTK * DJ / 4 + 255) / 256;   // 16-byte R loads per thread per chunk
+    __shared__ __attribute__((aligned(16))) float xs[2][kTK][kTT + 4];
+    __shared__ __attribute__((aligned(16))) float rs[2][kTK][DJ + 4];
+    const int tid = threadIdx.x;
+    const int tx = tid & 15, ty = tid >> 4;
+    const int64_t t0 = (int64_t)blockIdx.y * kTT;
+    const int K = a.K, b = a.b;
+    const int j0 = blockIdx.x * DJ;           // first output column
+    const int c = j0 / b;                     // its block (DJ divides b)
+    const int kb = c * b;                     // the block's first input
+    const float *Rc = a.R + (size_t)c * b * b + (j0 - kb);
+
+    if constexpr (STEP == 1) {
+        // the extremes of rot 2 start from the atomics' identities
+        if (blockIdx.x == 0 && tid < kTT && t0 + tid < a.T) {
+            a.stat[t0 + tid] = 0u;
+            a.stat[a.T + t0 + tid] = 0xFFFFFFFFu;
+        }
+    }
+
+    // input loads: STEP 1 x as 16-byte pieces (thread -> token tid / 2, k
+    // 8 (tid % 2) .. + 7: one piece of bf16, two of fp32); STEP 2 the
+    // gathered columns of Zt (thread -> k tid / 16, tokens 8 (tid % 16) .. + 7:
+    // two pieces)
+    constexpr int XW = STEP == 1 ? (BF16 ? 4 : 8) : 8;   // 32-bit words per thread
+    uint32_t xr[XW];
+    float4 rr[RL];
+    const int lt = tid >> 1, lh = tid & 1;
+    int64_t ltok = t0 + lt;
+    if (ltok >= a.T) ltok = a.T - 1;
+    auto load = [&](int k0) {
+        if constexpr (STEP == 1) {
+            if constexpr (BF16) {
+                const uint4 w = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.X) + ltok * K + k0 + 8 * lh);
+                xr[0] = w.x; xr[1] = w.y; xr[2] = w.z; xr[3] = w.w;
+            } else {
+                const float *src = static_cast<const float *>(a.X) + ltok * K + k0 + 8 * lh;
+                const uint4 w0 = *reinterpret_cast<const uint4 *>(src);
+                const uint4 w1 = *reinterpret_cast<const uint4 *>(src + 4);
+                xr[0] = w0.x; xr[1] = w0.y; xr[2] = w0.z; xr[3] = w0.w;
+                xr[4] = w1.x; xr[5] = w1.y; xr[6] = w1.z; xr[7] = w1.w;
+            }
+        } else {
+            const float *col = static_cast<const float *>(a.X) + (int64_t)a.perm[k0 + (tid >> 4)] * a.Tp + t0 +
+                               8 * (tid & 15);
+            const uint4 w0 = *reinterpret_cast<const uint4 *>(col);
+            const uint4 w1 = *reinterpret_cast<const uint4 *>(col + 4);
+            xr[0] = w0.x; xr[1] = w0.y; xr[2] = w0.z; xr[3] = w0.w;
+            xr[4] = w1.x; xr[5] = w1.y; xr[6] = w1.z; xr[7] = w1.w;
+        }
+#pragma unroll
+        for (int i = 0; i < RL; ++i) {
+            const int q = tid + 256 * i;
+            const int kk = q / (DJ / 4), jj = 4 * (q % (DJ / 4));
+            if (kk < kTK) rr[i] = *reinterpret_cast<const float4 *>(Rc + (size_t)(k0 - kb + kk) * b + jj);
+        }
+    };
+    auto store = [&](int buf, int k0) {
+        const int kq = 8 * lh;
+        if constexpr (STEP == 1) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float x;
+                if constexpr (BF16)
+                    x = __uint_as_float(e & 1 ? (xr[e >> 1] & 0xFFFF0000u) : (xr[e >> 1] << 16));
+                else
+                    x = __uint_as_float(xr[e]);
+                xs[buf][kq + e][lt] = x * a.smooth[k0 + kq + e];
+            }
+        } else {
+            float *d = &xs[buf][tid >> 4][8 * (tid & 15)];
+            *reinterpret_cast<uint4 *>(d) = make_uint4(xr[0], xr[1], xr[2], xr[3]);
+            *reinterpret_cast<uint4 *>(d + 4) = make_uint4(xr[4], xr[5], xr[6], xr[7]);
+        }
+#pragma unroll
+        for (int i = 0; i < RL; ++i) {
+            const int q = tid + 256 * i;
+            const int kk = q / (DJ / 4), jj = 4 * (q % (DJ / 4));
+            if (kk < kTK) *reinterpret_cast<float4 *>(&rs[buf][kk][jj]) = rr[i];
+        }
+    };
+
+    float acc[8][CW];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int e = 0; e < CW; ++e) acc[t][e] = 0.0f;
+    const int nchunk = b / kTK;
+    load(kb);
+    store(0, kb);
+    __syncthreads();
+    for (int ch = 0; ch < nchunk; ++ch) {
+        const int buf = ch & 1;
+        const int k0 = kb + ch * kTK;
+        if (ch + 1 < nchunk) load(k0 + kTK);
+        float xa[2][8], rb[2][CW];
+        auto rd = [&](int kk, int p) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) xa[p][t] = xs[buf][kk][ty * 8 + t];
+#pragma unroll
+            for (int e = 0; e < CW; ++e) rb[p][e] = rs[buf][kk][tx * CW + e];
+        };
+        rd(0, 0);
+#pragma unroll
+        for (int kk = 0; kk < kTK; ++kk) {
+            if (kk + 1 < kTK) rd(kk + 1, (kk + 1) & 1);
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int e = 0; e < CW; ++e) acc[t][e] = fmaf(xa[kk & 1][t], rb[kk & 1][e], acc[t][e]);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) pin_sums(acc[t]);
+        }
+        if (ch + 1 < nchunk) store(buf ^ 1, k0 + kTK);
+        __syncthreads();
+    }
+
+    // outputs: tokens t0 + 8 ty + t, columns j0 + CW tx .. + CW - 1
+    if constexpr (STEP == 1) {
+        // Zt: per column, the thread's eight tokens are 32 contiguous bytes
+        // (the padding rows past T are written too; nothing reads them for
+        // a real token)
+#pragma unroll
+        for (int e = 0; e < CW; ++e) {
+            float *d = a.Out + (int64_t)(j0 + tx * CW + e) * a.Tp + t0 + ty * 8;
+            *reinterpret_cast<float4 *>(d) = make_float4(acc[0][e], acc[1][e], acc[2][e], acc[3][e]);
+            *reinterpret_cast<float4 *>(d + 4) = make_float4(acc[4][e], acc[5][e], acc[6][e], acc[7][e]);
+        }
+        return;
+    }
+    float *o = a.Out + (t0 + ty * 8) * K + j0 + tx * CW;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int64_t tok = t0 + ty * 8 + t;
+        const bool ok = tok < a.T;
+        if (ok) {
+            if constexpr (CW % 4 == 0) {
+#pragma unroll
+                for (int e = 0; e < CW; e += 4)
+                    *reinterpret_cast<float4 *>(o + e) = make_float4(acc[t][e], acc[t][e + 1], acc[t][e + 2], acc[t][e + 3]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < CW; ++e) o[e] = acc[t][e];
+            }
+        }
+        o += K;
+        if constexpr (STEP == 2) {
+            // this token's extremes over the tile: the thread's CW columns,
+            // then the 16 threads (lanes) of its row group
+            float hi = ASYM ? -INFINITY : 0.0f, lo = INFINITY;
+#pragma unroll
+            for (int e = 0; e < CW; ++e) {
+                if constexpr (ASYM) {
+                    hi = fmaxf(hi, acc[t][e]);
+                    lo = fminf(lo, acc[t][e]);
+                } else {
+                    hi = fmaxf(hi, fabsf(acc[t][e]));
+                }
+            }
+            unsigned khi = ASYM ? fkey(hi) : __float_as_uint(hi);
+            unsigned klo = fkey(lo);
+            for (int off = 1; off < 16; off <<= 1) {
+                khi = max(khi, (unsigned)__shfl_xor((int)khi, off, 64));
+                if constexpr (ASYM) klo = min(klo, (unsigned)__shfl_xor((int)klo, off, 64));
+            }
+            if (tx == 0 && ok) {
+                atomicMax(&a.stat[tok], khi);
+                if constexpr (ASYM) atomicMin(&a.stat[a.T + tok], klo);
+            }
+        }
+    }
+}
+
+// codes and scales of U: one wave per token, four consecutive coordinates per
+// lane and step (the one-pass kernel's quantizer, formula for formula)
+template <int QB, bool ASYM>
+__global__ void __launch_bounds__(256)
+trdq_quant_tiled_kernel(const float *__restrict__ U, const unsigned *__restrict__ stat, int64_t T, int K,
+                        uint8_t *__restrict__ codes, float *__restrict__ scale) {
+    const int lane = threadIdx.x & 63;
+    const int64_t tok = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (tok >= T) return;
+    constexpr float kQ = ASYM ? (QB == 8 ? 255.0f : 15.0f) : (QB == 8 ? 127.0f : 7.0f);
+    float inv = 0.0f, sc = 0.0f, zp = 0.0f;
+    bool zero_row;
+    if constexpr (ASYM) {
+        const float lo = fkey_inv(stat[T + tok]), hi = fkey_inv(stat[tok]);
+        const float d = hi - lo;
+        zero_row = d == 0.0f;
+        if (!zero_row) {
+            inv = kQ / d;
+            sc = d / kQ;
+            const float zr = rintf(lo * inv);
+            zp = zr >= 0.0f ? 0.0f : (zr < -kQ ? kQ : -zr);
+        }
+    } else {
+        const float amax = __uint_as_float(stat[tok]);
+        zero_row = amax == 0.0f;
+        if (!zero_row) {
+            inv = kQ / amax;
+            sc = amax / kQ;
+        }
+    }
+    if (lane == 0) {
+        scale[tok] = sc;
+        if constexpr (ASYM) scale[T + tok] = zp;
+    }
+    const float *u = U + tok * K;
+    for (int k = 4 * lane; k < K; k += 256) {
+        const float4 v4 = *reinterpret_cast<const float4 *>(u + k);
+        const float v[4] = {v4.x, v4.y, v4.z, v4.w};
+        uint32_t q[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float r = rintf(v[e] * inv);
+            if constexpr (ASYM) r = fminf(fmaxf(r + zp, 0.0f), kQ);
+            else r = fminf(fmaxf(r, -kQ), kQ);
+            q[e] = zero_row ? 0u : ((uint32_t)(int)r & (QB == 8 ? 0xFFu : 0xFu));
+        }
+        if constexpr (QB == 8)
+            *reinterpret_cast<uint32_t *>(codes + tok * K + k) = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+        else
+            *reinterpret_cast<uint16_t *>(codes + tok * (K / 2) + k / 2) =
+                (uint16_t)(q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12));
+    }
+}
+
+template <int STEP, bool BF16, bool ASYM>
+hipError_t launch_tile_step(const TileArgs &a, hipStream_t s) {
+    // widest column tile that divides the block
+    const int cw = a.b >= 128 ? 8 : a.b / 16;
+    const dim3 grid((unsigned)(a.K / (16 * cw)), (unsigned)((a.T + kTT - 1) / kTT));
+    switch (cw) {
+        case 8: hipLaunchKernelGGL((trdq_tile_kernel<STEP, BF16, 8, ASYM>), grid, dim3(256), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((trdq_tile_kernel<STEP, BF16, 4, ASYM>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((trdq_tile_kernel<STEP, BF16, 2, ASYM>), grid, dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((trdq_tile_kernel<STEP, BF16, 1, ASYM>), grid, dim3(256), 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 int launch_trdq(const void *X, int x_bf16, int64_t T, int K, int block, const float *smooth,
@@ -276,6 +568,38 @@ int launch_trdq(const void *X, int x_bf16, int64_t T, int K, int block, const fl
                             : launch_tok<4, 8, false>(a, asym, a_bits, s));
     return (int)(x_bf16 ? launch_tok<2, 16, true>(a, asym, a_bits, s)
                         : launch_tok<2, 16, false>(a, asym, a_bits, s));
+}
+
+size_t trdq_workspace_bytes(int64_t T, int K) {
+    const size_t Tp = (size_t)((T + kTT - 1) / kTT) * kTT;
+    return Tp * (size_t)K * 4 + (size_t)T * (size_t)K * 4 + (size_t)T * 8;
+}
+
+int launch_trdq_tiled(const void *X, int x_bf16, int64_t T, int K, int block, const float *smooth,
+                      const float *R1, const int32_t *perm, const float *R2, uint8_t *codes,
+                      float *scale, int asym, int a_bits, void *workspace, void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t Tp = (T + kTT - 1) / kTT * kTT;
+    float *Zt = static_cast<float *>(workspace);
+    float *U = Zt + (size_t)Tp * K;
+    unsigned *stat = reinterpret_cast<unsigned *>(U + (size_t)T * K);
+    TileArgs a1{X, Zt, smooth, perm, R1, stat, T, Tp, K, block};
+    TileArgs a2{Zt, U, smooth, perm, R2, stat, T, Tp, K, block};
+    hipError_t e;
+    if (x_bf16) e = asym ? launch_tile_step<1, true, true>(a1, s) : launch_tile_step<1, true, false>(a1, s);
+    else e = asym ? launch_tile_step<1, false, true>(a1, s) : launch_tile_step<1, false, false>(a1, s);
+    if (e != hipSuccess) return (int)e;
+    e = asym ? launch_tile_step<2, false, true>(a2, s) : launch_tile_step<2, false, false>(a2, s);
+    if (e != hipSuccess) return (int)e;
+    const dim3 grid((unsigned)((T + 3) / 4));
+    if (a_bits == 8) {
+        if (asym) hipLaunchKernelGGL((trdq_quant_tiled_kernel<8, true>), grid, dim3(256), 0, s, U, stat, T, K, codes, scale);
+        else hipLaunchKernelGGL((trdq_quant_tiled_kernel<8, false>), grid, dim3(256), 0, s, U, stat, T, K, codes, scale);
+    } else {
+        if (asym) hipLaunchKernelGGL((trdq_quant_tiled_kernel<4, true>), grid, dim3(256), 0, s, U, stat, T, K, codes, scale);
+        else hipLaunchKernelGGL((trdq_quant_tiled_kernel<4, false>), grid, dim3(256), 0, s, U, stat, T, K, codes, scale);
+    }
+    return (int)hipGetLastError();
 }
 
 }  // namespace rq

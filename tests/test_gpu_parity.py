@@ -9,6 +9,7 @@ dense, flux_up 9216x3072->12288, flux_down 9216x12288->3072, video
 times, with every code and scale compared and the outputs compared at
 sampled (token, channel) pairs.
 """
+import dataclasses
 import sys
 
 import numpy as np
@@ -566,3 +567,37 @@ def test_timestep_set_parity(name, shape):
             L.dw = ws.device_member(0)
             L.linear()
             assert H.rel_err(L.Y.cpu().numpy().ravel(), yhat) > 1e-2
+
+
+# TR-DQ's rotation with a workspace (tiled launches through fp32 buffers) and
+# without (one pass, rows in LDS): the same codes and scales bit for bit, and
+# the oracle's; symmetric and asymmetric, 4- and 8-bit, blocks 16 .. 256,
+# ragged token counts
+TRDQ_FORMS = [
+    ("flux_up_trdq", dict(T=300, K=1024, N=40), "int4"),
+    ("flux_up_trdq", dict(T=129, K=512, N=40, block=16, a_bits=4), "int4"),
+    ("flux_up_trdq", dict(T=70, K=2048, N=40, block=32), "int4_asym"),
+    ("flux_up_trdq", dict(T=257, K=1024, N=40, block=64, a_bits=4), "int4_asym"),
+    ("flux_up_trdq", dict(T=9, K=16384, N=40, block=256), "int4"),
+]
+
+
+@pytest.mark.parametrize("name,shape,quant", TRDQ_FORMS,
+                         ids=[f"{q}-{'-'.join(f'{k}{v}' for k, v in s.items())}" for _, s, q in TRDQ_FORMS])
+def test_trdq_tiled_matches_one_pass(name, shape, quant):
+    w = dataclasses.replace(datagen.WORKLOADS[name].with_shape(**shape), quant=quant)
+    say(f"[trdq forms] {w}")
+    inp = datagen.make_inputs(w)
+    L = H.GpuLayer(w, inp, y_dtype="f32")
+    assert L.ws is not None, "TR-DQ takes a workspace"
+    L.rotate_quant()
+    torch.cuda.synchronize()
+    c_tiled, s_tiled = L.codes.clone(), L.scale.clone()
+    check_act(w, L, H.oracle_act(w, inp))
+    L.codes.fill_(0xA5)
+    L.scale.fill_(-1.0)
+    L.ws = None
+    L.rotate_quant()
+    torch.cuda.synchronize()
+    assert torch.equal(L.codes, c_tiled), "one-pass and tiled codes differ"
+    assert torch.equal(L.scale.view(torch.int32), s_tiled.view(torch.int32)), "scales differ"
