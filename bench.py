@@ -99,10 +99,10 @@ def profiled_traffic(kernel_file: str, summary: str):
 PMC_KERNELS = {
     "gemm": ("rq_gemm_fp6.hip", "gemm_fp6_mma_kernel"),
     "gemm_int8": ("rq_gemm_w4a4.hip", "gemm_w4a4_kernel"),
-    "gemm_codebook": ("rq_gemm_codebook.hip", "gemm_codebook_kernel"),
+    "gemm_codebook": ("rq_gemm_codebook.hip", "gemm_cb_kernel"),
     "gemm_mx": ("rq_gemm_mx.hip", "gemm_mx_kernel"),
     "rotate": ("rq_rpbh.hip", "rpbh_quant_kernel"),
-    "trdq": ("rq_trdq.hip", "trdq_quant_kernel"),
+    "trdq": ("rq_trdq.hip", "trdq_tile_kernel"),
     "dense": ("rq_dense.hip", "dense_rotate_kernel"),
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
@@ -478,7 +478,7 @@ def main():
     w0 = wls[0]
     if w0.quant == "lloydmax":
         peak, gsrc, gkey, gname, dtype = PEAK_BF16_TFLOPS, "rq_gemm_codebook.hip", "gemm_codebook", \
-            "gemm_codebook_kernel", "bf16"
+            "gemm_cb_kernel", "bf16"
     elif w0.quant == "mxfp4":
         peak, gsrc, gkey, gname, dtype = PEAK_FP6_TOPS, "rq_gemm_mx.hip", "gemm_mx", "gemm_mx_kernel", "fp4"
     elif int8_gemm:
@@ -487,7 +487,7 @@ def main():
     else:
         # the INT4 GEMM computes on the FP6 matrix cores: its own dtype's peak
         peak, gsrc, gkey, gname, dtype = PEAK_FP6_TOPS, "rq_gemm_fp6.hip", "gemm", \
-            ("gemm_fp6_mma_kernel" if w0.rot == "rpbh" else "gemm_fp6_kernel"), "fp6"
+            ("gemm_fp6_mma_kernel" if mma_capable(w0) else "gemm_fp6_kernel"), "fp6"
     gemm_mean_ms = float(np.mean(gemm_ms))
     achieved = float(np.mean(ops)) / (gemm_mean_ms * 1e-3) / 1e12
     traffic = profiled_traffic(gsrc, f"{gkey}_{args.workload}_counters.json")
@@ -509,7 +509,7 @@ def main():
         fl = float(np.mean([rotate_flops(w) for w in wls])) / (rot_mean_ms * 1e-3) / 1e12
         roofline_rot = {"bound": "alu", "achieved": round(fl, 2), "peak": PEAK_FP32_FMA_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(fl / PEAK_FP32_FMA_TFLOPS, 4), "traffic": None,
-                        "kernel": "dense_rotate_kernel" if w0.rot == "dense" else "trdq_quant_kernel"}
+                        "kernel": "dense_rotate_kernel" if w0.rot == "dense" else "trdq_tile_kernel"}
 
     cpu = None
     if not args.no_cpu_baseline:
