@@ -167,7 +167,7 @@ typedef struct rq_quant {
 } rq_quant;
 
 #define RQ_WEIGHT_MAGIC 0x31575152u /* "RQW1" */
-#define RQ_WEIGHT_VERSION 3u
+#define RQ_WEIGHT_VERSION 4u
 
 /*
  * Header at the start of every packed-weight blob (256 bytes).  The blob is
@@ -201,8 +201,12 @@ typedef struct rq_quant {
  *                 32 c .. 32 c + 31 (zero rows past N)
  *   mma_stages    ceil((K - r) / 128)
  *   mma_ntiles    ceil(N / 32)
- *   i8_offset     INT with a_bits 8: int8 [N][K] weight codes (the canonical
- *                 codes when w_bits is 8, their widened copy when 4)
+ *   i8_offset     INT with a_bits 8: the int8 weight codes (the canonical
+ *                 codes when w_bits is 8, their widened copy when 4) in the
+ *                 int8 matrix cores' fragment order
+ *                 [mma_ntiles][K/32][64 lanes][16 bytes]: lane 32 h + i of
+ *                 k-step c holds coordinates 32 c + 16 h .. + 15 of row
+ *                 32 tile + i (zero rows past N)
  *   mxs_offset    MXFP4: the E8M0 codes tiled [mma_stages][mma_ntiles][64][2]:
  *                 byte ks of lane 32 h + i is the scale of row 32 tile + i,
  *                 coordinates 128 s + 64 ks + 32 h .. + 31
@@ -370,8 +374,9 @@ rq_status rq_codes_mma_bytes(const rq_rotation *rot, int64_t T, size_t *bytes);
  *   codes_mma  the GEMM-layout copy rq_rotate_quant can write: INT with
  *              a_bits 4 (RPBH, DENSE): rq_codes_mma_bytes(); MXFP4: the tiled codes
  *              and tiled scales; LLOYDMAX (RPBH): the bf16 levels,
- *              ceil(T / 32) * (K / 16) * 1024 (see rq_rotate_quant); 0 where
- *              none exists
+ *              ceil(T / 32) * (K / 16) * 1024; INT with a_bits 8 (RPBH,
+ *              TRDQ): the int8 fragments, ceil(T / 32) * 32 * K (see
+ *              rq_rotate_quant); 0 where none exists
  * Any output pointer may be NULL.
  * Errors: descriptor errors, RQ_ERR_SHAPE (T out of range).
  */
@@ -419,8 +424,8 @@ rq_status rq_activation_bytes(const rq_rotation *rot, const rq_quant *q, int64_t
  *           nibbles (two's complement when symmetric, unsigned when
  *           asymmetric; low nibble = even coordinate), INT 8-bit bytes
  *           (int8 / uint8), LLOYDMAX 4-bit indices or MXFP4 E2M1 codes as
- *           nibbles.  May be NULL for INT 4-bit (RPBH, DENSE), MXFP4 and
- *           LLOYDMAX (RPBH) when codes_mma is given.
+ *           nibbles.  May be NULL for INT 4-bit (RPBH, DENSE), INT 8-bit
+ *           (RPBH, TRDQ), MXFP4 and LLOYDMAX (RPBH) when codes_mma is given.
  *   scale   device: fp32 [T] s (INT symmetric) or sigma (LLOYDMAX); INT
  *           asymmetric: fp32 [2][T], s[t] then the zero point z[t]; MXFP4:
  *           uint8 [T][K/32] E8M0 codes (the pointer is read as bytes).  May
@@ -433,6 +438,11 @@ rq_status rq_activation_bytes(const rq_rotation *rot, const rq_quant *q, int64_t
  *           [8 bf16]: coordinates 16 ks + 8 h .. 16 ks + 8 h + 7 of token t
  *           are lane t % 32 + 32 h of k-step ks of tile t / 32 (slots of
  *           tokens past T are left unwritten).
+ *           INT 8-bit (RPBH, TRDQ): a device buffer of rq_activation_bytes()'s
+ *           codes_mma receiving the code bytes in the int8 GEMM's fragment
+ *           order [ceil(T/32)][K/32][64 lanes][16 bytes]: coordinates
+ *           32 c + 16 h .. + 15 of token t are lane t % 32 + 32 h of k-step c
+ *           of tile t / 32 (slots of tokens past T are left unwritten).
  *           INT 4-bit: a device buffer of rq_codes_mma_bytes() receiving the
  *           same codes in the FP6 GEMM's matrix-core layout.  Tokens come in
  *           tiles of 32 and coordinates in stages of 128; the buffer is
@@ -516,7 +526,7 @@ rq_status rq_rotate_quant_noalloc(const rq_rotation *rot, const rq_quant *q, con
  *   blob    device copy of the whole blob, 16-byte aligned
  *   codes, scale, top  as written by rq_rotate_quant (device); the weights'
  *           format (kind, a_bits) must match the activations' quantizer
- *   codes_mma  optional (INT with a_bits 4, MXFP4 or LLOYDMAX): the
+ *   codes_mma  optional (INT, MXFP4 or LLOYDMAX): the
  *           codes_mma output of rq_rotate_quant for the same tokens; when
  *           given it is read instead of codes (and, MXFP4, scale), which may
  *           then be NULL
@@ -537,12 +547,13 @@ rq_status rq_w4a4_linear(const rq_weight_header *hdr, const void *blob, const ui
  * rq_w4a4_linear with an explicit choice of matrix cores (same passages and
  * arguments as rq_w4a4_linear, which is this call with RQ_ENGINE_AUTO).
  *   engine  rq_engine.  RQ_ENGINE_INT8 takes INT4_SYM weights with 4-bit
- *           activations (any r) and the canonical codes (codes_mma must be
- *           NULL); the accumulators and outputs equal the FP6 engine's bit
+ *           activations (any r) and their canonical codes (codes_mma must
+ *           be NULL for 4-bit activations); the accumulators and outputs equal the FP6 engine's bit
  *           for bit.  8-bit activations run on the int8 engine only (AUTO or
  *           INT8); Lloyd-Max and MXFP4 take RQ_ENGINE_AUTO only.
  * Errors: as rq_w4a4_linear; RQ_ERR_UNSUPPORTED for an engine that cannot
- *         run the blob's format or for codes_mma with RQ_ENGINE_INT8.
+ *         run the blob's format or for codes_mma of 4-bit activations with
+ *         RQ_ENGINE_INT8.
  */
 rq_status rq_w4a4_linear_engine(const rq_weight_header *hdr, const void *blob,
                                 const uint8_t *codes, const float *scale, const uint16_t *top,

@@ -17,8 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librq.so")
 SOURCES = ["rq_host.cpp", "rq_api.cpp", "rq_device.cpp", "rq_rpbh.hip", "rq_dense.hip",
-           "rq_gemm_w4a4.hip", "rq_gemm_fp6.hip", "rq_gemm_codebook.hip", "rq_gemm_mx.hip",
-           "rq_trdq.hip"]
+           "rq_gemm_w4a4.hip", "rq_gemm_i8.hip", "rq_gemm_fp6.hip", "rq_gemm_codebook.hip",
+           "rq_gemm_mx.hip", "rq_trdq.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

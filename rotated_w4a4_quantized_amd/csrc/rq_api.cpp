@@ -57,7 +57,8 @@ rq_status check_header(const rq_weight_header *hdr) {
     }
     if (intq && hdr->a_bits == 8) {
         if (hdr->wsum_offset <= 0 || hdr->wsum_offset % 16 != 0 || hdr->i8_offset <= 0 ||
-            hdr->i8_offset % 16 != 0 || hdr->i8_offset + (int64_t)hdr->N * hdr->K > hdr->total_bytes)
+            hdr->i8_offset % 16 != 0 ||
+            hdr->i8_offset + (int64_t)(hdr->N + 31) / 32 * 32 * hdr->K > hdr->total_bytes)
             return fail(RQ_ERR_FORMAT, "weight header int8 section offsets are inconsistent");
     }
     if (f == RQ_Q_MXFP4) {
@@ -84,15 +85,18 @@ rq_status validate_rotate_quant(const rq_rotation *rot, const rq_quant *q, const
     const bool dense = rot->kind == RQ_ROT_DENSE;
     const bool mx = q->kind == RQ_Q_MXFP4;
     const bool int4 = (q->kind == RQ_Q_INT4_SYM || q->kind == RQ_Q_INT4_ASYM) && q->a_bits == 4;
+    const bool int8 = (q->kind == RQ_Q_INT4_SYM || q->kind == RQ_Q_INT4_ASYM) && q->a_bits == 8;
     const bool lm = q->kind == RQ_Q_LLOYDMAX;
-    if (codes_mma && !((rpbh && (int4 || mx || lm)) || (dense && int4)))
+    const bool trdq = rot->kind == RQ_ROT_TRDQ;
+    const bool mma_ok = (rpbh && (int4 || int8 || mx || lm)) || (dense && int4) || (trdq && int8);
+    if (codes_mma && !mma_ok)
         return fail(RQ_ERR_UNSUPPORTED,
-                    "codes_mma is written for RPBH or DENSE with 4-bit integer codes and for RPBH "
-                    "with MXFP4 or LLOYDMAX only");
+                    "codes_mma is written for 4-bit integer codes (RPBH, DENSE), 8-bit integer "
+                    "codes (RPBH, TRDQ), and MXFP4 or LLOYDMAX (RPBH) only");
     if (T == 0) return RQ_OK;
     if (!X || (!codes && !codes_mma) || (!scale && !(mx && codes_mma)))
         return fail(RQ_ERR_NULL, "X, scale and at least one of codes / codes_mma must not be NULL");
-    if (!codes && !((rpbh && (int4 || mx || lm)) || (dense && int4)))
+    if (!codes && !mma_ok)
         return fail(RQ_ERR_NULL, "this rotation and quantizer write the canonical codes: codes is NULL");
     if (dense && rot->r > 0 && !top) return fail(RQ_ERR_NULL, "DENSE with r > 0 needs top");
     if (!aligned16(X) || (codes && !aligned16(codes)) || (scale && !aligned16(scale)) ||
@@ -139,6 +143,8 @@ rq_status rq_activation_bytes(const rq_rotation *rot, const rq_quant *q, int64_t
         *codes_mma = 0;
         if ((rot->kind == RQ_ROT_RPBH || rot->kind == RQ_ROT_DENSE) && intq && q->a_bits == 4)
             *codes_mma = (size_t)mma_codes_bytes(T, Kq);
+        else if ((rot->kind == RQ_ROT_RPBH || rot->kind == RQ_ROT_TRDQ) && intq && q->a_bits == 8)
+            *codes_mma = (size_t)i8_mma_bytes(T, K);
         else if (rot->kind == RQ_ROT_RPBH && mx)
             *codes_mma = (size_t)mx_mma_bytes(T, K);
         else if (rot->kind == RQ_ROT_RPBH && q->kind == RQ_Q_LLOYDMAX)
@@ -195,14 +201,15 @@ rq_status rq_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void 
             return fail(RQ_ERR_SHAPE, "TRDQ: a workspace, when given, needs " + std::to_string(need) + " bytes");
         if (!aligned16(workspace)) return fail(RQ_ERR_ALIGN, "workspace must be 16-byte aligned");
         return hip_status(launch_trdq_tiled(X, xb, T, K, rot->block, rot->smooth, rot->R, rot->perm,
-                                            rot->R2, codes, scale, q->kind == RQ_Q_INT4_ASYM ? 1 : 0,
-                                            q->a_bits, workspace, stream),
+                                            rot->R2, codes, codes_mma, scale,
+                                            q->kind == RQ_Q_INT4_ASYM ? 1 : 0, q->a_bits, workspace,
+                                            stream),
                           "rotate_quant launch");
     }
     if (rot->kind == RQ_ROT_TRDQ)
         return hip_status(launch_trdq(X, xb, T, K, rot->block, rot->smooth, rot->R, rot->perm, rot->R2,
-                                      codes, scale, q->kind == RQ_Q_INT4_ASYM ? 1 : 0, q->a_bits,
-                                      stream),
+                                      codes, codes_mma, scale, q->kind == RQ_Q_INT4_ASYM ? 1 : 0,
+                                      q->a_bits, stream),
                           "rotate_quant launch");
     const size_t need = (size_t)T * (size_t)K * sizeof(float);
     if (!workspace || workspace_bytes < need)
@@ -261,8 +268,7 @@ rq_status rq_w4a4_linear_engine(const rq_weight_header *hdr, const void *blob,
     const bool mx = f == RQ_Q_MXFP4;
     if (y_dtype == RQ_I32 && !intq)
         return fail(RQ_ERR_UNSUPPORTED, "raw accumulators exist for integer weights only");
-    if (codes_mma && intq && a8)
-        return fail(RQ_ERR_UNSUPPORTED, "codes_mma is not read with 8-bit activations");
+
     if (engine != RQ_ENGINE_AUTO && !intq)
         return fail(RQ_ERR_UNSUPPORTED, "the Lloyd-Max and MXFP4 formats have one engine (RQ_ENGINE_AUTO)");
     if (a8 && engine == RQ_ENGINE_FP6)
@@ -270,8 +276,9 @@ rq_status rq_w4a4_linear_engine(const rq_weight_header *hdr, const void *blob,
     const bool int8 = a8 || engine == RQ_ENGINE_INT8;
     if (int8 && !a8 && asym)
         return fail(RQ_ERR_UNSUPPORTED, "the int8 engine takes INT4_SYM weights with 4-bit activations");
-    if (int8 && codes_mma)
-        return fail(RQ_ERR_UNSUPPORTED, "the int8 engine reads the canonical codes (codes_mma must be NULL)");
+    if (int8 && !a8 && codes_mma)
+        return fail(RQ_ERR_UNSUPPORTED,
+                    "the int8 engine reads the canonical codes of 4-bit activations (codes_mma must be NULL)");
     if (T < 0 || T >= (int64_t(1) << 31)) return fail(RQ_ERR_SHAPE, "T out of range");
     if (T == 0) return RQ_OK;
     if (!blob || !Y) return fail(RQ_ERR_NULL, "blob and Y must not be NULL");
@@ -281,7 +288,7 @@ rq_status rq_w4a4_linear_engine(const rq_weight_header *hdr, const void *blob,
     } else {
         if (!scale || (!codes && !codes_mma))
             return fail(RQ_ERR_NULL, "scale and the activation codes must not be NULL");
-        if (int8 && !codes) return fail(RQ_ERR_NULL, "this engine needs codes");
+        if (int8 && !a8 && !codes) return fail(RQ_ERR_NULL, "this engine needs codes");
     }
     if (hdr->r > 0 && !top) return fail(RQ_ERR_NULL, "weights with r > 0 need top");
     if (!aligned16(blob) || (codes && !aligned16(codes)) || (scale && !aligned16(scale)) ||
@@ -294,6 +301,11 @@ rq_status rq_w4a4_linear_engine(const rq_weight_header *hdr, const void *blob,
                           "mxfp4 gemm launch");
     }
     if (intq) {
+        if (a8)
+            return hip_status(launch_gemm_i8(codes_mma ? nullptr : codes, codes_mma, scale,
+                                             asym ? scale + T : nullptr, T, hdr, blob, bias, Y,
+                                             y_dtype, stream),
+                              "int8 gemm launch");
         if (int8)
             return hip_status(launch_gemm_w4a4(codes, scale, asym ? scale + T : nullptr, top, T, hdr,
                                                blob, bias, Y, y_dtype, stream),

@@ -511,14 +511,7 @@ int launch_gemm_w4a4(const uint8_t *codes, const float *scale, const float *zero
     a.za = zero;
     a.wsum = reinterpret_cast<const int32_t *>(base + hdr->wsum_offset);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (a8) {
-        if (zero) {
-            if (T >= 256) return (int)launch_cfg<CfgBig, false, 2>(a, s);
-            return (int)launch_cfg<CfgMid, false, 2>(a, s);
-        }
-        if (T >= 256) return (int)launch_cfg<CfgBig, false, 1>(a, s);
-        return (int)launch_cfg<CfgMid, false, 1>(a, s);
-    }
+    if (a8) return launch_gemm_i8(codes, nullptr, scale, zero, T, hdr, blob, bias, Y, y_dtype, stream);
     // the low-rank term needs registers for its own accumulators: mid tile
     if (a.r > 0) return (int)launch_cfg<CfgMid, true, 0>(a, s);
     if (T >= 256) return (int)launch_cfg<CfgBig, false, 0>(a, s);

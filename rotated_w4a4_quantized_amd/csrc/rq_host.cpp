@@ -238,11 +238,9 @@ static BlobLayout blob_layout(const rq_rotation *rot, const rq_quant *q, int32_t
             L.mma_ntiles = (N + 31) / 32;
             L.mma_off = end;
             end = L.mma_off + (int64_t)L.mma_ntiles * L.mma_stages * 3 * 1024;
-        } else if (q->w_bits == 8) {     // the canonical int8 codes serve the GEMM
-            L.i8_off = L.codes_off;
-        } else {                         // int8 copy of the 4-bit codes
+        } else {                         // int8 codes in the int8 GEMM's fragment order
             L.i8_off = end;
-            end = L.i8_off + round256((int64_t)N * K);
+            end = L.i8_off + round256((int64_t)(N + 31) / 32 * 32 * K);
         }
     }
     L.total = end;
@@ -493,10 +491,17 @@ rq_status rq_pack_weights(const rq_rotation *rot, const rq_quant *q, const void 
                         pack_mma_tile(codes, N, rb, r, Kq, tile, s,
                                       out + BL.mma_off + ((int64_t)tile * S + s) * 3 * 1024);
             });
-        } else if (!w8) {
+        } else {
+            // [ceil(N/32)][K/32][64 lanes][16 B]: lane l of k-step kb holds row
+            // 32 tile + l % 32, coordinates 32 kb + 16 (l / 32) .. + 15
+            // (rows past N stay zero)
             int8_t *i8 = reinterpret_cast<int8_t *>(out + BL.i8_off);
+            const int nkb = K / 32;
             for (int n = 0; n < N; ++n)
-                for (int k = 0; k < K; ++k) i8[(size_t)n * K + k] = (int8_t)wcode(n, k);
+                for (int k = 0; k < K; ++k) {
+                    const size_t lane = (size_t)(n % 32) + 32 * ((k % 32) / 16);
+                    i8[(((size_t)(n / 32) * nkb + k / 32) * 64 + lane) * 16 + k % 16] = (int8_t)wcode(n, k);
+                }
         }
     } else if (q->kind == RQ_Q_MXFP4) {
         // tiled copies for the scaled FP4 GEMM: codes [tile][K/32][32][16],

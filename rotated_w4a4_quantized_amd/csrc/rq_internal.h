@@ -67,18 +67,27 @@ int launch_dense_quant(const float *U, int64_t T, int K, int r, uint8_t *codes, 
 int launch_gemm_w4a4(const uint8_t *codes, const float *scale, const float *zero,
                      const uint16_t *top, int64_t T, const rq_weight_header *hdr,
                      const void *blob, const float *bias, void *Y, int y_dtype, void *stream);
+// 8-bit activations on the int8 matrix cores (operands copied straight from
+// the row-major int8 matrices; blob's int8 weight copy)
+int launch_gemm_i8(const uint8_t *codes, const uint8_t *codes_mma, const float *scale,
+                   const float *zero, int64_t T, const rq_weight_header *hdr, const void *blob,
+                   const float *bias, void *Y, int y_dtype, void *stream);
+// bytes of 8-bit activation codes in the int8 GEMM's fragment order:
+// [ceil(T / 32)][K / 32][64 lanes][16 bytes]
+inline int64_t i8_mma_bytes(int64_t T, int K) { return (T + 31) / 32 * 32 * (int64_t)K; }
 // TR-DQ runtime rotation (smoothing, block rotation, zigzag gather, block
 // rotation) and per-token integer quantization (a_bits 4 or 8, asym or not)
 int launch_trdq(const void *X, int x_bf16, int64_t T, int K, int block, const float *smooth,
                 const float *R1, const int32_t *perm, const float *R2, uint8_t *codes,
-                float *scale, int asym, int a_bits, void *stream);
+                uint8_t *codes_mma, float *scale, int asym, int a_bits, void *stream);
 // TR-DQ with a workspace: two tiled block-rotation launches through fp32
 // buffers and a quantize launch (bit-identical codes); the workspace holds
 // Z and U, fp32 [T][K] each, then the per-token extremes, uint32 [2][T]
 size_t trdq_workspace_bytes(int64_t T, int K);
 int launch_trdq_tiled(const void *X, int x_bf16, int64_t T, int K, int block, const float *smooth,
                       const float *R1, const int32_t *perm, const float *R2, uint8_t *codes,
-                      float *scale, int asym, int a_bits, void *workspace, void *stream);
+                      uint8_t *codes_mma, float *scale, int asym, int a_bits, void *workspace,
+                      void *stream);
 // zero: per-token zero points of INT4_ASYM activations, or null (symmetric)
 int launch_gemm_fp6(const uint8_t *codes, const uint8_t *codes_mma, const float *scale,
                     const float *zero, const uint16_t *top, int64_t T,

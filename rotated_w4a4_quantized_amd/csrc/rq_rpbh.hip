@@ -704,6 +704,15 @@ rpbh_quant_kernel(RpbhArgs a) {
             }
             if constexpr (QK == 0 || QK == 2)
                 if (a.codes_mma && !grouped) store_chunk_mma(a.codes_mma, tok, a.mma_stages, tt, chunk, 0u);
+            if constexpr (B8) {
+                // the int8 GEMM's fragment order [t / 32][k-step][lane][16 B]: the
+                // thread's 32 codes are k-step tt, lanes t % 32 and t % 32 + 32
+                if (a.codes_mma) {
+                    uint8_t *d = a.codes_mma + (((tok >> 5) * (K / 32) + tt) * 64 + (tok & 31)) * 16;
+                    *reinterpret_cast<uint4 *>(d) = chunk;
+                    *reinterpret_cast<uint4 *>(d + 512) = chunk1;
+                }
+            }
             if constexpr (QK == 1) {
                 // the levels in bf16, in the codebook GEMM's fragment order
                 // [32-token tile][16-coordinate k-step][lane][16 bytes]:

@@ -58,9 +58,16 @@ struct TrdqArgs {
     const float *R1;       // [K/b][b][b]
     const int32_t *perm;   // [K]
     const float *R2;       // [K/b][b][b]
-    uint8_t *codes;        // [T][K a_bits / 8]
+    uint8_t *codes;        // [T][K a_bits / 8], or null
+    uint8_t *codes_mma;    // 8-bit codes in the int8 GEMM's fragment order, or null
     float *scale;          // [T] (asymmetric: s [T] then z [T])
 };
+
+// 8-bit code of (token t, coordinate k) in the int8 GEMM's fragment order
+// [t / 32][k / 32][lane t % 32 + 32 (k % 32 / 16)][k % 16]
+__device__ __forceinline__ int64_t i8_frag_offset(int64_t t, int k, int K) {
+    return (((t >> 5) * (K / 32) + (k >> 5)) * 64 + (t & 31) + 32 * ((k & 31) >> 4)) * 16 + (k & 15);
+}
 
 // TOK tokens per workgroup, NBMAX = the most blocks one thread handles,
 // QB code bits (4 or 8), ASYM zero point.
@@ -233,12 +240,14 @@ trdq_quant_kernel(TrdqArgs a) {
                 q[e] = zero_row ? 0u : ((uint32_t)(int)r & (QB == 8 ? 0xFFu : 0xFu));
             }
             const int k = c * b + 4 * g;
-            if constexpr (QB == 8)
-                *reinterpret_cast<uint32_t *>(a.codes + tok * K + k) =
-                    q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-            else
+            if constexpr (QB == 8) {
+                const uint32_t w = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+                if (a.codes) *reinterpret_cast<uint32_t *>(a.codes + tok * K + k) = w;
+                if (a.codes_mma) *reinterpret_cast<uint32_t *>(a.codes_mma + i8_frag_offset(tok, k, K)) = w;
+            } else {
                 *reinterpret_cast<uint16_t *>(a.codes + tok * (K / 2) + k / 2) =
                     (uint16_t)(q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12));
+            }
         }
     }
 }
@@ -489,7 +498,8 @@ trdq_tile_kernel(TileArgs a) {
 template <int QB, bool ASYM>
 __global__ void __launch_bounds__(256)
 trdq_quant_tiled_kernel(const float *__restrict__ U, const unsigned *__restrict__ stat, int64_t T, int K,
-                        uint8_t *__restrict__ codes, float *__restrict__ scale) {
+                        uint8_t *__restrict__ codes, uint8_t *__restrict__ codes_mma,
+                        float *__restrict__ scale) {
     const int lane = threadIdx.x & 63;
     const int64_t tok = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (tok >= T) return;
@@ -530,9 +540,11 @@ trdq_quant_tiled_kernel(const float *__restrict__ U, const unsigned *__restrict_
             else r = fminf(fmaxf(r, -kQ), kQ);
             q[e] = zero_row ? 0u : ((uint32_t)(int)r & (QB == 8 ? 0xFFu : 0xFu));
         }
-        if constexpr (QB == 8)
-            *reinterpret_cast<uint32_t *>(codes + tok * K + k) = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-        else
+        if constexpr (QB == 8) {
+            const uint32_t w = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+            if (codes) *reinterpret_cast<uint32_t *>(codes + tok * K + k) = w;
+            if (codes_mma) *reinterpret_cast<uint32_t *>(codes_mma + i8_frag_offset(tok, k, K)) = w;
+        } else
             *reinterpret_cast<uint16_t *>(codes + tok * (K / 2) + k / 2) =
                 (uint16_t)(q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12));
     }
@@ -556,8 +568,8 @@ hipError_t launch_tile_step(const TileArgs &a, hipStream_t s) {
 
 int launch_trdq(const void *X, int x_bf16, int64_t T, int K, int block, const float *smooth,
                 const float *R1, const int32_t *perm, const float *R2, uint8_t *codes,
-                float *scale, int asym, int a_bits, void *stream) {
-    TrdqArgs a{X, T, K, block, smooth, R1, perm, R2, codes, scale};
+                uint8_t *codes_mma, float *scale, int asym, int a_bits, void *stream) {
+    TrdqArgs a{X, T, K, block, smooth, R1, perm, R2, codes, codes_mma, scale};
     hipStream_t s = static_cast<hipStream_t>(stream);
     // a thread holds ceil(K / 1024) blocks x TOK tokens x 4 columns
     if (K <= 4096)
@@ -577,7 +589,8 @@ size_t trdq_workspace_bytes(int64_t T, int K) {
 
 int launch_trdq_tiled(const void *X, int x_bf16, int64_t T, int K, int block, const float *smooth,
                       const float *R1, const int32_t *perm, const float *R2, uint8_t *codes,
-                      float *scale, int asym, int a_bits, void *workspace, void *stream) {
+                      uint8_t *codes_mma, float *scale, int asym, int a_bits, void *workspace,
+                      void *stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t Tp = (T + kTT - 1) / kTT * kTT;
     float *Zt = static_cast<float *>(workspace);
@@ -593,11 +606,11 @@ int launch_trdq_tiled(const void *X, int x_bf16, int64_t T, int K, int block, co
     if (e != hipSuccess) return (int)e;
     const dim3 grid((unsigned)((T + 3) / 4));
     if (a_bits == 8) {
-        if (asym) hipLaunchKernelGGL((trdq_quant_tiled_kernel<8, true>), grid, dim3(256), 0, s, U, stat, T, K, codes, scale);
-        else hipLaunchKernelGGL((trdq_quant_tiled_kernel<8, false>), grid, dim3(256), 0, s, U, stat, T, K, codes, scale);
+        if (asym) hipLaunchKernelGGL((trdq_quant_tiled_kernel<8, true>), grid, dim3(256), 0, s, U, stat, T, K, codes, codes_mma, scale);
+        else hipLaunchKernelGGL((trdq_quant_tiled_kernel<8, false>), grid, dim3(256), 0, s, U, stat, T, K, codes, codes_mma, scale);
     } else {
-        if (asym) hipLaunchKernelGGL((trdq_quant_tiled_kernel<4, true>), grid, dim3(256), 0, s, U, stat, T, K, codes, scale);
-        else hipLaunchKernelGGL((trdq_quant_tiled_kernel<4, false>), grid, dim3(256), 0, s, U, stat, T, K, codes, scale);
+        if (asym) hipLaunchKernelGGL((trdq_quant_tiled_kernel<4, true>), grid, dim3(256), 0, s, U, stat, T, K, codes, codes_mma, scale);
+        else hipLaunchKernelGGL((trdq_quant_tiled_kernel<4, false>), grid, dim3(256), 0, s, U, stat, T, K, codes, codes_mma, scale);
     }
     return (int)hipGetLastError();
 }

@@ -320,9 +320,14 @@ class PackedWeights:
         return self.blob[h.scale_offset:h.scale_offset + h.N * (h.K // 32)].reshape(h.N, h.K // 32)
 
     def i8_codes(self) -> np.ndarray:
-        """INT with 8-bit activations: the int8 weight codes [N][K]."""
+        """INT with 8-bit activations: the int8 weight codes [N][K], read back
+        from the blob's fragment order [N/32][K/32][64 lanes][16 bytes] (lane
+        l: row 32 tile + l % 32, coordinates 32 kb + 16 (l / 32) .. + 15)."""
         h = self.header
-        return self.blob[h.i8_offset:h.i8_offset + h.N * h.K].view(np.int8).reshape(h.N, h.K)
+        tiles = -(-h.N // 32)
+        raw = self.blob[h.i8_offset:h.i8_offset + tiles * 32 * h.K].view(np.int8)
+        v = raw.reshape(tiles, h.K // 32, 2, 32, 16).transpose(0, 3, 1, 2, 4).reshape(tiles * 32, h.K)
+        return v[:h.N]
 
     def mma_tiles(self) -> np.ndarray:
         """INT4: the GEMM's FP6 fragments, uint8 [ntiles][stages][3][64][16]."""
@@ -441,8 +446,10 @@ def codes_mma_bytes(rot: Rotation, T: int) -> int:
 def rotate_quant(drot: DeviceRotation, q: Quant, X, codes, scale, top=None, workspace=None,
                  stream=None, codes_mma=None):
     """Launch the activation kernels on `stream` (default: torch's current).
-    codes and/or codes_mma (the GEMM's FP6 fragment layout) receive the codes;
-    scale holds T floats, or 2T (s then z) for INT4_ASYM."""
+    codes and/or codes_mma (the GEMM's matrix-core layout of this format:
+    FP6 fragments for INT 4-bit, int8 fragments for INT 8-bit, tiled codes
+    and scales for MXFP4, bf16 level fragments for Lloyd-Max) receive the
+    codes; scale holds T floats, or 2T (s then z) for INT4_ASYM."""
     cr, cq = drot.c_dev(), q.c()
     T = int(X.shape[0])
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -192,3 +192,13 @@ def decode_cb_mma(buf, T, K):
     v = v.reshape(tiles, K // 16, 2, 32, 8)            # [tile][ks][h][t32][e]
     v = v.transpose(0, 3, 1, 2, 4).reshape(tiles * 32, K)
     return v[:T]
+
+
+def decode_i8_mma(buf, T, K):
+    """uint8 codes [T][K] from the 8-bit codes_mma output, read as rq.h
+    documents it: [32-token tile][32-coordinate k-step][lane 0..63][16 bytes];
+    coordinate 32 kb + 16 h + e of token t is byte e of lane t % 32 + 32 h."""
+    tiles = -(-T // 32)
+    v = np.ascontiguousarray(buf, np.uint8)[:tiles * 32 * K]
+    v = v.reshape(tiles, K // 32, 2, 32, 16).transpose(0, 3, 1, 2, 4).reshape(tiles * 32, K)
+    return v[:T]

@@ -180,13 +180,13 @@ def test_linear_validation_errors():
     assert L.rq_w4a4_linear(None, None, None, None, None, None, 1, None, None, 0, None) == -1
     assert L.rq_w4a4_linear(*args(hdr, codes=None)) == -1
     assert L.rq_w4a4_linear(*args(hdr, codes=None, mma=(1 << 23) + 4)) == -4
-    # the MMA-layout codes are not read with 8-bit activations; the codebook
-    # format reads its bf16 level fragments (16-byte aligned)
+    # 8-bit activations read their int8 fragment copy and the codebook format
+    # its bf16 level fragments, both 16-byte aligned
     w = datagen.WORKLOADS["flux_up_w4a8"].with_shape(T=4, K=256, N=40, block=64)
     inp = datagen.make_inputs(w)
     h8 = rq.pack_weights(rq.Rotation.rpbh(inp["sign"], inp["perm"], 64), rq.Quant.integer(8, 4),
                          inp["W"]).header
-    assert L.rq_w4a4_linear(*args(h8, mma=1 << 23)) == -6
+    assert L.rq_w4a4_linear(*args(h8, mma=(1 << 23) + 4)) == -4
     w = datagen.WORKLOADS["video"].with_shape(T=4, K=256, N=40)
     inp = datagen.make_inputs(w)
     lh = rq.pack_weights(rq.Rotation.rpbh(inp["sign"], inp["perm"], 256),
@@ -476,7 +476,7 @@ def test_new_format_validation_errors():
     rot = rq.Rotation.rpbh(np.ones(K, np.int8), np.arange(K, dtype=np.int32), 64)
     assert rq.activation_bytes(rot, rq.Quant.mxfp4(), 40) == (40 * K // 2, 40 * K // 32,
                                                              2 * (K // 32) * 512 + (K // 128) * 2 * 128)
-    assert rq.activation_bytes(rot, rq.Quant.integer(8, 4, asym=True), 40) == (40 * K, 80 * 4, 0)
+    assert rq.activation_bytes(rot, rq.Quant.integer(8, 4, asym=True), 40) == (40 * K, 80 * 4, 64 * K)
     # the MXFP4 GEMM reads the tiled codes: canonical codes alone are refused
     w = datagen.WORKLOADS["flux_up_mxfp4"].with_shape(T=4, K=K, N=40, block=64)
     inp = datagen.make_inputs(w)

@@ -84,7 +84,7 @@ def check_act(w, L, act, rows=None):
         f"scale mismatch in {int(np.sum(scale != act['scale']))} tokens"
     bad = np.nonzero(np.any(codes != act["codes"], axis=1))[0]
     assert bad.size == 0, f"codes differ in {bad.size} tokens, first {bad[:5]}"
-    if L.codes_mma is not None and w.quant in ("int4", "int4_asym"):
+    if L.codes_mma is not None and w.quant in ("int4", "int4_asym") and w.a_bits == 4:
         dec, top_clear = H.decode_codes_mma(L.codes_mma.cpu().numpy(), w.T, w.Kq)
         if rows is not None:
             dec = dec[rows]
@@ -94,6 +94,13 @@ def check_act(w, L, act, rows=None):
             ref = (ref & 15) - 8
         bad = np.nonzero(np.any(dec != ref, axis=1))[0]
         assert bad.size == 0, f"codes_mma differs in {bad.size} tokens, first {bad[:5]}"
+    if w.quant in ("int4", "int4_asym") and w.a_bits == 8 and L.codes_mma is not None:
+        # the same bytes in the int8 GEMM's fragment order
+        dec = H.decode_i8_mma(L.codes_mma.cpu().numpy(), w.T, w.K)
+        if rows is not None:
+            dec = dec[rows]
+        bad = np.nonzero(np.any(dec != np.asarray(act["codes"], np.uint8), axis=1))[0]
+        assert bad.size == 0, f"int8 fragment codes differ in {bad.size} tokens, first {bad[:5]}"
     if w.quant == "lloydmax" and L.codes_mma is not None:
         # the bf16 levels of the codes, in the codebook GEMM's fragment order
         dec = H.decode_cb_mma(L.codes_mma.cpu().numpy(), w.T, w.K)
@@ -334,10 +341,22 @@ def test_runs_on_a_side_stream():
     assert torch.equal(ref, L.Y)
 
 
-def test_mma_codes_only_path():
+CODES_ONLY = [
+    ("flux_down", dict(T=300, K=2048, N=520, block=512)),
+    ("pixart", dict(T=300, K=1152, N=520)),
+    ("flux_up_w4a8", dict(T=300, K=1024, N=520, block=256)),
+    ("flux_up_w8a8", dict(T=300, K=1024, N=520, block=256)),
+    ("flux_up_trdq", dict(T=300, K=1024, N=520, block=128)),
+]
+
+
+@pytest.mark.parametrize("name,shape", CODES_ONLY, ids=[c[0] for c in CODES_ONLY])
+def test_mma_codes_only_path(name, shape):
     # the bench configuration: rq_rotate_quant writes only the MMA-layout
-    # codes and the GEMM reads them; compared with a canonical-code run
-    w = datagen.WORKLOADS["flux_down"].with_shape(T=300, K=2048, N=520, block=512)
+    # codes (canonical codes NULL) and the GEMM reads them; compared with a
+    # canonical-code run
+    w = datagen.WORKLOADS[name].with_shape(**shape)
+    say(f"[codes only] {w}")
     inp = datagen.make_inputs(w)
     A = H.GpuLayer(w, inp, y_dtype="f32", codes="mma")
     B = H.GpuLayer(w, inp, y_dtype="f32", codes="canonical")
@@ -347,7 +366,16 @@ def test_mma_codes_only_path():
     accB = B.raw_acc().cpu().numpy()
     torch.cuda.synchronize()
     assert A.codes is None and np.array_equal(accA, accB)
-    assert torch.equal(A.scale, B.scale) and torch.equal(A.Y, B.Y)
+    assert torch.equal(A.scale, B.scale)
+    if w.r == 0:
+        assert torch.equal(A.Y, B.Y)
+    else:
+        # the MMA-layout GEMM adds the bf16 low-rank term on the matrix cores,
+        # the canonical-code GEMM with fp32 FMAs: the same exact products
+        # summed in another order
+        assert torch.equal(A.top, B.top)
+        d = (A.Y - B.Y).abs().max().item()
+        assert d <= 1e-5 * B.Y.abs().max().item(), d
 
 
 
