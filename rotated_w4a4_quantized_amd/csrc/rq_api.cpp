@@ -175,8 +175,6 @@ rq_status rq_rotate_quant(const rq_rotation *rot, const rq_quant *q, const void 
         return st;
     if (T == 0) return RQ_OK;
     const int K = rot->K;
-    const bool dense = rot->kind == RQ_ROT_DENSE;
-    const bool int4 = q->kind == RQ_Q_INT4_SYM || q->kind == RQ_Q_INT4_ASYM;
     const int xb = x_dtype == RQ_BF16 ? 1 : 0;
     if (rot->kind == RQ_ROT_RPBH) {
         if (q->kind == RQ_Q_MXFP4)
@@ -307,8 +305,7 @@ rq_status rq_w4a4_linear_engine(const rq_weight_header *hdr, const void *blob,
                                              y_dtype, stream),
                               "int8 gemm launch");
         if (int8)
-            return hip_status(launch_gemm_w4a4(codes, scale, asym ? scale + T : nullptr, top, T, hdr,
-                                               blob, bias, Y, y_dtype, stream),
+            return hip_status(launch_gemm_w4a4(codes, scale, top, T, hdr, blob, bias, Y, y_dtype, stream),
                               "int8 gemm launch");
         return hip_status(launch_gemm_fp6(codes_mma ? nullptr : codes, codes_mma, scale,
                                           asym ? scale + T : nullptr, top, T, hdr, blob, bias, Y,

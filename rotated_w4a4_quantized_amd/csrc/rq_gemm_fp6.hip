@@ -173,20 +173,6 @@ __device__ inline const uint8_t *uniform_ptr(const uint8_t *p) {
     return reinterpret_cast<const uint8_t *>((uintptr_t)(((uint64_t)hi << 32) | lo));
 }
 
-// The same load with M0 declared clobbered instead of saved and restored:
-// three instructions.  Every operand is wave-uniform by construction (kernel
-// arguments, the scalar wave index and loop counters), so the scalar
-// constraints need no readfirstlane.
-__device__ inline void dma16_m0(const void *sbase, uint32_t voff, uint32_t lds_addr) {
-    asm volatile(
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %0, %1"
-        :
-        : "v"(voff), "s"(sbase), "s"(lds_addr)
-        : "memory", "m0");
-}
-
 // sixteen zero bytes: the source of activation chunks past the end of a row
 __device__ __attribute__((aligned(16))) uint8_t g_zero16_fp6[16];
 
@@ -640,14 +626,14 @@ gemm_fp6_mma_kernel(Fp6Args a) {
             const int q = wave * C::NA + i;
             int tt = (int)(t0 / 32) + q / 3;
             if (tt >= atiles) tt = atiles - 1;
-            dma16_m0(a.Amma + (((int64_t)tt * a.S + s) * 3 + q % 3) * 1024, loff, lb + q * 1024);
+            dma16_s(a.Amma + (((int64_t)tt * a.S + s) * 3 + q % 3) * 1024, loff, lb + q * 1024);
         }
 #pragma unroll
         for (int i = 0; i < C::NB; ++i) {
             const int q = wave * C::NB + i;
             int nt = n0 / 32 + q / 3;
             if (nt >= a.ntiles) nt = a.ntiles - 1;
-            dma16_m0(a.Bmma + (((int64_t)nt * a.S + s) * 3 + q % 3) * 1024, loff, lb + C::ACT_STAGE + q * 1024);
+            dma16_s(a.Bmma + (((int64_t)nt * a.S + s) * 3 + q % 3) * 1024, loff, lb + C::ACT_STAGE + q * 1024);
         }
     };
     auto wait_vm = [](auto nc) {
@@ -743,7 +729,7 @@ gemm_fp6_mma_kernel(Fp6Args a) {
                           : wave == 1 ? static_cast<const void *>(a.sw + n0)
                           : wave == 2 ? static_cast<const void *>(a.wsum + n0)
                                       : static_cast<const void *>(a.za + t0);
-        dma16_m0(src, loff, lds_base + C::EPI_OFF + wave * 1024);
+        dma16_s(src, loff, lds_base + C::EPI_OFF + wave * 1024);
     }
     const int npre = nstage < 3 ? nstage : 3;
     for (int p = 0; p < npre; ++p) issue(p, p);

@@ -36,18 +36,21 @@ __device__ __forceinline__ void static_for(F &&f) {
 
 // One direct-to-LDS load of 16 bytes per active lane
 // (global_load_lds_dwordx4): lane l's bytes, from sbase + voff, land at LDS
-// byte lds_addr + 16 l.  M0 holds the LDS address (declared clobbered; one
-// wait state after writing it); the load has no VGPR result, so its
-// completion is counted by hand with wait_vm.  Every scalar operand must be
-// wave-uniform.
+// byte lds_addr + 16 l.  M0 holds the LDS address (saved and restored: the
+// compiler reserves M0 and does not expect it to change; one wait state
+// after writing it); the load has no VGPR result, so its completion is
+// counted by hand with wait_vm.  Every scalar operand must be wave-uniform.
 __device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t lds_addr) {
+    uint32_t saved;
     asm volatile(
-        "s_mov_b32 m0, %2\n\t"
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
         "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %0, %1"
-        :
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
         : "v"(voff), "s"(sbase), "s"(lds_addr)
-        : "memory", "m0");
+        : "memory");
 }
 
 // Tile id for workgroup `bid`: contiguous id ranges per XCD (workgroup id

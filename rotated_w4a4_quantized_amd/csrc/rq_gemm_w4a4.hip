@@ -11,11 +11,8 @@
 // RQ_ENGINE_INT8); the default runs on the FP6 matrix cores
 // (rq_gemm_fp6.hip) at twice the rate, with the same accumulators.
 //
-// 8-bit activations (TR-DQ's W4A8 and W8A8 settings): the same kernel on
-// int8 bytes, 64 coordinates per stage, against the blob's int8 copy of the
-// weight codes; v_mfma_i32_32x32x32_i8 returns acc itself.  Asymmetric 8-bit
-// codes u in [0, 255] enter as u - 128 (the top bit flipped), and the
-// epilogue adds (128 - z[t]) wsum[n] back: every value stays an int32.
+// 8-bit activations have their own kernel on fragment-ordered operands
+// (rq_gemm_i8.hip).
 //
 // Widening: gfx950 has no 4-bit MFMA.  For a packed word p (eight nibbles,
 // low nibble = even k), (p << 4) & 0xF0F0F0F0 holds 16 q for the even k and
@@ -68,8 +65,6 @@ struct W4A4Args {
     int lda;               // bytes per activation row (Kq / 2)
     int ldb;               // bytes per weight row (K / 2)
     int koff;              // byte offset of the quantized part in a weight row (r / 2)
-    const float *za;       // asymmetric 8-bit activations: zero points [T], else null
-    const int32_t *wsum;   // [N] sums of the weight codes (asymmetric 8-bit activations)
     int r;                 // low-rank width (multiple of 32) or 0
     int ydt;               // rq_dtype
     int tiles_t, tiles_n;
@@ -161,14 +156,11 @@ __device__ inline void tile_of(int bid, int nblk, int tiles_t, int tiles_n, int 
     tn = in / gsize;
 }
 
-// MODE: 0 nibbles widened in registers (W4A4), 1 int8 activations, 2 unsigned
-// 8-bit activations (zero point)
-template <class C, bool HAS_LR, bool TAIL, int MODE>
+template <class C, bool HAS_LR, bool TAIL>
 __global__ void __launch_bounds__(C::NTH, C::OCC)
 gemm_w4a4_kernel(W4A4Args a) {
-    constexpr bool A8 = MODE != 0;
-    // the accumulator holds 256 acc (nibbles widened to 16 q) or acc itself
-    constexpr int kAccShift = A8 ? 0 : 8;
+    // the accumulator holds 256 acc (nibbles widened to 16 q)
+    constexpr int kAccShift = 8;
     __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_BYTES];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -267,39 +259,20 @@ gemm_w4a4_kernel(W4A4Args a) {
         }
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-            if constexpr (A8) {
-                // sixteen int8 coordinates per lane: one MFMA per half
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
                 v4i xn[C::FN], xt[C::FT];
 #pragma unroll
                 for (int i = 0; i < C::FN; ++i)
-                    xn[i] = v4i{(int)fn_[half][i].x, (int)fn_[half][i].y, (int)fn_[half][i].z,
-                                (int)fn_[half][i].w};
-                constexpr uint32_t F = MODE == 2 ? 0x80808080u : 0u;   // u -> u - 128
+                    xn[i] = k ? widen(fn_[half][i].z, fn_[half][i].w) : widen(fn_[half][i].x, fn_[half][i].y);
 #pragma unroll
                 for (int j = 0; j < C::FT; ++j)
-                    xt[j] = v4i{(int)(ft_[half][j].x ^ F), (int)(ft_[half][j].y ^ F),
-                                (int)(ft_[half][j].z ^ F), (int)(ft_[half][j].w ^ F)};
+                    xt[j] = k ? widen(ft_[half][j].z, ft_[half][j].w) : widen(ft_[half][j].x, ft_[half][j].y);
 #pragma unroll
                 for (int i = 0; i < C::FN; ++i)
 #pragma unroll
                     for (int j = 0; j < C::FT; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xn[i], xt[j], acc[i][j], 0, 0, 0);
-            } else {
-#pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    v4i xn[C::FN], xt[C::FT];
-#pragma unroll
-                    for (int i = 0; i < C::FN; ++i)
-                        xn[i] = k ? widen(fn_[half][i].z, fn_[half][i].w) : widen(fn_[half][i].x, fn_[half][i].y);
-#pragma unroll
-                    for (int j = 0; j < C::FT; ++j)
-                        xt[j] = k ? widen(ft_[half][j].z, ft_[half][j].w) : widen(ft_[half][j].x, ft_[half][j].y);
-#pragma unroll
-                    for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-                        for (int j = 0; j < C::FT; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xn[i], xt[j], acc[i][j], 0, 0, 0);
-                }
             }
         }
         // stage s + 1 has landed; stages s + 2 .. may still be in flight
@@ -309,26 +282,6 @@ gemm_w4a4_kernel(W4A4Args a) {
         }
         lds_barrier();
         buf = buf == D ? 0 : buf + 1;
-    }
-
-    if constexpr (MODE == 2) {
-        // acc = sum (u - 128) qw; the output needs sum (u - z) qw = acc + (128 - z) wsum
-#pragma unroll
-        for (int j = 0; j < C::FT; ++j) {
-            int64_t t = t0 + wt * C::FT * 32 + j * 32 + li;
-            if (t >= a.T) t = a.T - 1;
-            const int dz = 128 - (int)a.za[t];
-#pragma unroll
-            for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        int n = n0 + wn * C::FN * 32 + i * 32 + 8 * q + 4 * lg + e;
-                        if (n >= a.N) n = a.N - 1;
-                        acc[i][j][4 * q + e] += dz * a.wsum[n];
-                    }
-        }
     }
 
     // low-rank term (DENSE weights): lr[n][t] = sum_{j < r} qw[n][j] * bf16(top[t][j])
@@ -467,15 +420,15 @@ gemm_w4a4_kernel(W4A4Args a) {
     }
 }
 
-template <class C, bool HAS_LR, int MODE>
+template <class C, bool HAS_LR>
 hipError_t launch_cfg(W4A4Args a, hipStream_t s) {
     a.tiles_t = (int)((a.T + C::BT - 1) / C::BT);
     a.tiles_n = (a.N + C::BN - 1) / C::BN;
     const int nblk = a.tiles_t * a.tiles_n;
     if (a.lda % kStageBytes)
-        hipLaunchKernelGGL((gemm_w4a4_kernel<C, HAS_LR, true, MODE>), dim3(nblk), dim3(C::NTH), 0, s, a);
+        hipLaunchKernelGGL((gemm_w4a4_kernel<C, HAS_LR, true>), dim3(nblk), dim3(C::NTH), 0, s, a);
     else
-        hipLaunchKernelGGL((gemm_w4a4_kernel<C, HAS_LR, false, MODE>), dim3(nblk), dim3(C::NTH), 0, s, a);
+        hipLaunchKernelGGL((gemm_w4a4_kernel<C, HAS_LR, false>), dim3(nblk), dim3(C::NTH), 0, s, a);
     return hipGetLastError();
 }
 
@@ -487,14 +440,14 @@ using CfgMid = Cfg<128, 128, 2, 2, 3>;    // 4 waves of 64 x 64
 
 }  // namespace
 
-int launch_gemm_w4a4(const uint8_t *codes, const float *scale, const float *zero,
-                     const uint16_t *top, int64_t T, const rq_weight_header *hdr, const void *blob,
-                     const float *bias, void *Y, int y_dtype, void *stream) {
+int launch_gemm_w4a4(const uint8_t *codes, const float *scale, const uint16_t *top, int64_t T,
+                     const rq_weight_header *hdr, const void *blob, const float *bias, void *Y,
+                     int y_dtype, void *stream) {
     W4A4Args a;
     const uint8_t *base = static_cast<const uint8_t *>(blob);
-    const bool a8 = hdr->a_bits == 8;
+    if (hdr->a_bits != 4) return (int)hipErrorInvalidValue;   // 8-bit activations: rq_gemm_i8.hip
     a.A = codes;
-    a.B = base + (a8 ? hdr->i8_offset : hdr->codes_offset);
+    a.B = base + hdr->codes_offset;
     a.sa = scale;
     a.sw = reinterpret_cast<const float *>(base + hdr->scale_offset);
     a.top = top;
@@ -503,19 +456,16 @@ int launch_gemm_w4a4(const uint8_t *codes, const float *scale, const float *zero
     a.T = T;
     a.N = hdr->N;
     a.r = hdr->r;
-    a.lda = a8 ? hdr->K : (hdr->K - hdr->r) / 2;
-    a.ldb = a8 ? hdr->K : hdr->row_bytes;
+    a.lda = (hdr->K - hdr->r) / 2;
+    a.ldb = hdr->row_bytes;
     a.koff = hdr->r / 2;
     a.ydt = y_dtype;
     a.post = 1.0f / (float)hdr->b_div;
-    a.za = zero;
-    a.wsum = reinterpret_cast<const int32_t *>(base + hdr->wsum_offset);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (a8) return launch_gemm_i8(codes, nullptr, scale, zero, T, hdr, blob, bias, Y, y_dtype, stream);
     // the low-rank term needs registers for its own accumulators: mid tile
-    if (a.r > 0) return (int)launch_cfg<CfgMid, true, 0>(a, s);
-    if (T >= 256) return (int)launch_cfg<CfgBig, false, 0>(a, s);
-    return (int)launch_cfg<CfgMid, false, 0>(a, s);
+    if (a.r > 0) return (int)launch_cfg<CfgMid, true>(a, s);
+    if (T >= 256) return (int)launch_cfg<CfgBig, false>(a, s);
+    return (int)launch_cfg<CfgMid, false>(a, s);
 }
 
 }  // namespace rq

@@ -507,7 +507,7 @@ rq_status rq_pack_weights(const rq_rotation *rot, const rq_quant *q, const void 
         // tiled copies for the scaled FP4 GEMM: codes [tile][K/32][32][16],
         // scales [stage][tile][64][2] (byte ks of lane 32 h + i: row
         // 32 tile + i, coordinates 128 s + 64 ks + 32 h ..)
-        const int ntiles = BL.mma_ntiles, S = BL.mma_stages, nch = K / 32;
+        const int ntiles = BL.mma_ntiles, nch = K / 32;
         const uint8_t *e8 = out + so;
         for (int tile = 0; tile < ntiles; ++tile)
             for (int c = 0; c < nch; ++c)

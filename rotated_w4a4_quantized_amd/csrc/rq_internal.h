@@ -61,12 +61,11 @@ constexpr size_t kDenseScratchBytes = size_t(64) << 20;
 int dense_scratch(float **ptr);
 int launch_dense_quant(const float *U, int64_t T, int K, int r, uint8_t *codes, float *scale,
                        uint16_t *top, uint8_t *codes_mma, void *stream);
-// the int8-MFMA GEMM: 4-bit codes widened in registers (a_bits 4), or int8
-// activation codes against the blob's int8 weight copy (a_bits 8); zero: the
-// per-token zero points of asymmetric 8-bit activations, or null
-int launch_gemm_w4a4(const uint8_t *codes, const float *scale, const float *zero,
-                     const uint16_t *top, int64_t T, const rq_weight_header *hdr,
-                     const void *blob, const float *bias, void *Y, int y_dtype, void *stream);
+// the int8-MFMA engine of the INT4_SYM GEMM (4-bit activation codes widened
+// in registers; a_bits 4 only)
+int launch_gemm_w4a4(const uint8_t *codes, const float *scale, const uint16_t *top, int64_t T,
+                     const rq_weight_header *hdr, const void *blob, const float *bias, void *Y,
+                     int y_dtype, void *stream);
 // 8-bit activations on the int8 matrix cores (operands copied straight from
 // the row-major int8 matrices; blob's int8 weight copy)
 int launch_gemm_i8(const uint8_t *codes, const uint8_t *codes_mma, const float *scale,
