@@ -99,6 +99,7 @@ def profiled_traffic(kernel_file: str, summary: str):
 PMC_KERNELS = {
     "gemm": ("rq_gemm_fp6.hip", "gemm_fp6_mma_kernel"),
     "gemm_int8": ("rq_gemm_w4a4.hip", "gemm_w4a4_kernel"),
+    "gemm_i8": ("rq_gemm_i8.hip", "gemm_i8_kernel"),
     "gemm_codebook": ("rq_gemm_codebook.hip", "gemm_cb_kernel"),
     "gemm_mx": ("rq_gemm_mx.hip", "gemm_mx_kernel"),
     "rotate": ("rq_rpbh.hip", "rpbh_quant_kernel"),
@@ -481,6 +482,9 @@ def main():
             "gemm_cb_kernel", "bf16"
     elif w0.quant == "mxfp4":
         peak, gsrc, gkey, gname, dtype = PEAK_FP6_TOPS, "rq_gemm_mx.hip", "gemm_mx", "gemm_mx_kernel", "fp4"
+    elif w0.a_bits == 8:
+        peak, gsrc, gkey, gname, dtype = PEAK_INT8_TOPS, "rq_gemm_i8.hip", "gemm_i8", \
+            "gemm_i8_kernel", "i8"
     elif int8_gemm:
         peak, gsrc, gkey, gname, dtype = PEAK_INT8_TOPS, "rq_gemm_w4a4.hip", "gemm_int8", \
             "gemm_w4a4_kernel", "i8"
