@@ -17,18 +17,18 @@
 //            loads into registers), the sign of the coordinate each source
 //            element will land on is applied with one XOR per 32-bit word,
 //            and the row is written to LDS in its natural order;
-//   gather   each thread reads its 32 permuted inputs from LDS;
-//   pass 0   stages on bits 0..4 of the block index, in registers;
-//   pass p   one exchange inside the wave (two rounds through LDS, see
-//            exchange()), then up to four more stages in registers; the
-//            register set of every pass after the first also carries index
-//            bit 0, so the final values of each nibble pair sit in one thread;
+//   gather   each thread reads its 32 permuted inputs from LDS: 32
+//            consecutive coordinates of one block (see lane_hbits);
+//   stages   index bits 0..4 of the block in registers, bits 5 .. L - 1
+//            across the block's adjacent lanes, one fused multiply-add per
+//            value with the partner lane's register as a DPP operand (no LDS
+//            exchange); those lanes end with their values negated, which the
+//            quantizer folds into its scale;
 //   stat     per-token absmax (asymmetric: min and max; for the codebook
 //            also the exact integer-grid squared norm) by shuffles and one
 //            LDS atomic per lane group;
-//   codes    nibbles are packed from registers and regrouped through LDS
-//            into 16 contiguous bytes per 32 coordinates; the canonical
-//            layout is stored with one 16-byte store per thread.  For the
+//   codes    packed from registers, 16 bytes per 32 coordinates; the
+//            canonical layout is stored with one 16-byte store per thread.  For the
 //            GEMM's FP6 fragment layout (rq_fp6.h) a workgroup takes its
 //            tokens in groups of at least four consecutive ones, keeps the
 //            group's codes in LDS, and once the group is complete spreads
@@ -68,59 +68,44 @@ __device__ inline void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Layout of a block in a thread's registers.  The block's 2^L coordinates
+// are split over 2^NB adjacent lanes (NB = L - 5 lane bits, none for L <= 5)
+// and 32 registers: index bits 0..4 are the register index r, and the high
+// bits h = index bits 5 .. L - 1 sit on the lane.  Index bit 5 + t maps to
+// the lane mask m_t = 1, 2, 7, 8, 16 (t = 0 .. 4): the lane of h within the
+// block is the XOR of m_t over the set bits h_t.  The two butterfly partners
+// of index bit 5 + t then sit in the same register of lanes l and l ^ m_t,
+// which a data-parallel-primitive operand reaches inside a row of 16 lanes
+// (quad swaps for 1 and 2, the half-row mirror for 7, a rotation by 8 for 8)
+// and a swizzle for 16.  Every thread thus holds 32 consecutive coordinates
+// of its block, chunk 32 h .. 32 h + 31.
 template <int L>
-struct Plan {
-    static constexpr int NP = L <= 5 ? 1 : 1 + (L - 5 + 3) / 4;
-    __host__ __device__ static constexpr int lo(int p) { return p == 0 ? 0 : 5 + 4 * (p - 1); }
-    __host__ __device__ static constexpr int hi(int p) {
-        return p == 0 ? (L < 5 ? L : 5) : (5 + 4 * p < L ? 5 + 4 * p : L);
-    }
-    // index bit carried by register bit k in pass p
-    __host__ __device__ static constexpr int vbit(int p, int k) {
-        return p == 0 ? k : (k < 5 - (hi(p) - lo(p)) ? k : lo(p) + k - (5 - (hi(p) - lo(p))));
-    }
-    __host__ __device__ static constexpr int roff(int p, int r) {
-        int o = 0;
-        for (int k = 0; k < 5; ++k)
-            if ((r >> k) & 1) o |= 1 << vbit(p, k);
-        return o;
-    }
-    __host__ __device__ static constexpr bool isv(int p, int pos) {
-        for (int k = 0; k < 5; ++k)
-            if (vbit(p, k) == pos) return true;
-        return false;
-    }
-    __host__ __device__ static constexpr int rbit(int p, int s) {
-        for (int k = 0; k < 5; ++k)
-            if (vbit(p, k) == s) return k;
-        return -1;
-    }
-};
+constexpr int kLaneBits = L > 5 ? L - 5 : 0;
 
-// First coordinate of thread tt's set in pass P (the set is base + roff(P, r)).
-template <int L, int P>
-__device__ inline int pbase(int tt) {
-    if constexpr (P == 0) {
-        return kE * tt;
+// h of lane position l (0 .. 2^NB - 1) inside the block: the inverse of the
+// mask map (only m_2 = 7 has bit 2 set; bits 0 and 1 of l mix h_0, h_1 with it)
+__host__ __device__ constexpr int lane_hbits(int l) {
+    const int h2 = (l >> 2) & 1;
+    return (l & ~7) | (h2 << 2) | ((((l >> 1) & 1) ^ h2) << 1) | ((l & 1) ^ h2);
+}
+
+// the token-relative 32-coordinate chunk that thread tt holds
+template <int L>
+__device__ inline int chunk_of(int tt) {
+    constexpr int NB = kLaneBits<L>;
+    if constexpr (NB == 0) {
+        return tt;
     } else {
-        const int c = tt >> (L - 5);
-        int f = tt & ((1 << (L - 5)) - 1);
-        int i = 0;
-#pragma unroll
-        for (int pos = 0; pos < L; ++pos) {
-            if (Plan<L>::isv(P, pos)) continue;
-            i |= (f & 1) << pos;
-            f >>= 1;
-        }
-        return (c << L) + i;
+        const int l = tt & ((1 << NB) - 1);
+        return (tt - l) | lane_hbits(l);
     }
 }
 
-template <int L, int P>
-__device__ inline void stages(float (&v)[kE]) {
+// Butterfly stages on index bits 0 .. min(L, 5) - 1, inside the registers.
+template <int L>
+__device__ inline void reg_stages(float (&v)[kE]) {
 #pragma unroll
-    for (int s = Plan<L>::lo(P); s < Plan<L>::hi(P); ++s) {
-        const int kb = Plan<L>::rbit(P, s);
+    for (int kb = 0; kb < (L < 5 ? L : 5); ++kb) {
 #pragma unroll
         for (int r = 0; r < kE; ++r) {
             if (r & (1 << kb)) continue;
@@ -131,94 +116,82 @@ __device__ inline void stages(float (&v)[kE]) {
     }
 }
 
-// Exchanges.  A block's 2^(L-5) threads are adjacent lanes of one wave, so
-// every exchange stays inside a wave and needs only wave-level ordering (LDS
-// operations of one wave complete in issue order).  It runs in two rounds:
-// round h moves the coordinates with index bit 0 = h, which sit in the
-// registers of parity h in every pass, so one round needs a buffer of half a
-// token.  Half-coordinate m = j >> 1 lives at hslot(m).  In every pass a
-// thread's coordinates are base | roff(r) with disjoint bit fields, so the
-// slot splits into a per-thread base plus a per-register constant (an
-// immediate offset of the LDS instruction).  The pads put the 64 lanes of one
-// instruction on distinct banks in both access patterns for b >= 512, with at
-// most a two-way conflict for b = 64..256 (checked for 32 and 64 four-byte
-// banks).
-template <int L>
-__host__ __device__ constexpr int hslot(int m) {
-    return L == 6 ? m + 8 * (m >> 4) + (m >> 6) : L == 7 ? m + 4 * (m >> 4) + (m >> 7) : m + (m >> 4);
-}
-// exchange words per token (blocks up to 32 need none)
-template <int L>
-__host__ __device__ constexpr int xwords(int K) {
-    return L <= 5 ? 0 : ((hslot<L>(K / 2 - 1) + 1 + 3) & ~3);
-}
+// One butterfly stage across lanes, on every register: v = partner * c + v
+// with one v_fmac_f32 whose first operand is the partner lane's register
+// (a DPP operand).  c = +1 on the lane that holds the lower coordinate (its
+// index bit is 0), which gets fl(lo + hi) exactly as the pinned butterfly;
+// c = -1 on the other lane, which gets fl(hi - lo) = -fl(lo - hi), the
+// butterfly's result negated (the product by -1 is exact and the sum is
+// rounded once).  The negations are tracked per lane (see lane_sign): a
+// partner pair always carries the same accumulated sign, so every stage takes
+// the same form.  Hazard: two wait states between a VALU write of a register
+// and a DPP read of it (s_nop 1); the register operands are consumed in the
+// order they were last written.
+#define RQ_FMAC_DPP(n, ctrl) "v_fmac_f32_dpp %" #n ", %" #n ", %32 " ctrl " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+#define RQ_FMAC_DPP8(a, b, c, d, e, f, g, h, ctrl)                                                     \
+    RQ_FMAC_DPP(a, ctrl) RQ_FMAC_DPP(b, ctrl) RQ_FMAC_DPP(c, ctrl) RQ_FMAC_DPP(d, ctrl) RQ_FMAC_DPP(e, ctrl) \
+        RQ_FMAC_DPP(f, ctrl) RQ_FMAC_DPP(g, ctrl) RQ_FMAC_DPP(h, ctrl)
+#define RQ_FMAC_DPP32(ctrl)                                                                          \
+    "s_nop 1\n\t" RQ_FMAC_DPP8(0, 1, 2, 3, 4, 5, 6, 7, ctrl) RQ_FMAC_DPP8(8, 9, 10, 11, 12, 13, 14, 15, ctrl) \
+        RQ_FMAC_DPP8(16, 17, 18, 19, 20, 21, 22, 23, ctrl) RQ_FMAC_DPP8(24, 25, 26, 27, 28, 29, 30, 31, ctrl)
+#define RQ_V32                                                                                        \
+    "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]),     \
+        "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]),     \
+        "+v"(v[15]), "+v"(v[16]), "+v"(v[17]), "+v"(v[18]), "+v"(v[19]), "+v"(v[20]), "+v"(v[21]),   \
+        "+v"(v[22]), "+v"(v[23]), "+v"(v[24]), "+v"(v[25]), "+v"(v[26]), "+v"(v[27]), "+v"(v[28]),   \
+        "+v"(v[29]), "+v"(v[30]), "+v"(v[31])
+static_assert(kE == 32, "the lane stages are written for 32 registers");
 
-template <int L, int P, int H>
-__device__ inline void put(float *us, int tt, const float (&v)[kE]) {
-    float *p = us + hslot<L>(pbase<L, P>(tt) >> 1);
+template <int T>
+__device__ inline void lane_stage(float (&v)[kE], float c) {
+    if constexpr (T == 0) {
+        asm volatile(RQ_FMAC_DPP32("quad_perm:[1,0,3,2]") : RQ_V32 : "v"(c));
+    } else if constexpr (T == 1) {
+        asm volatile(RQ_FMAC_DPP32("quad_perm:[2,3,0,1]") : RQ_V32 : "v"(c));
+    } else if constexpr (T == 2) {
+        asm volatile(RQ_FMAC_DPP32("row_half_mirror") : RQ_V32 : "v"(c));
+    } else if constexpr (T == 3) {
+        asm volatile(RQ_FMAC_DPP32("row_ror:8") : RQ_V32 : "v"(c));
+    } else {
+        // lane ^ 16 inside each 32-lane half: swizzle, bit mode (and 0x1F, xor 0x10)
 #pragma unroll
-    for (int r = H; r < kE; r += 2) p[hslot<L>(Plan<L>::roff(P, r) >> 1)] = v[r];
+        for (int r = 0; r < kE; ++r) {
+            const float p = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v[r]), 0x401F));
+            v[r] = __builtin_fmaf(p, c, v[r]);
+        }
+    }
 }
-template <int L, int P, int H>
-__device__ inline void get(const float *us, int tt, float (&v)[kE]) {
-    const float *p = us + hslot<L>(pbase<L, P>(tt) >> 1);
-#pragma unroll
-    for (int r = H; r < kE; r += 2) v[r] = p[hslot<L>(Plan<L>::roff(P, r) >> 1)];
-}
-// orders this wave's LDS accesses at the compiler level (the hardware keeps
-// one wave's LDS operations in order)
-__device__ inline void wave_lds_order() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-// pass P -> pass P + 1; round 0's put may already have been issued
-template <int L, int P, bool PUT0>
-__device__ inline void exchange(float *us, int tt, float (&v)[kE]) {
-    if constexpr (PUT0) put<L, P, 0>(us, tt, v);
-    wave_lds_order();
-    get<L, P + 1, 0>(us, tt, v);
-    wave_lds_order();
-    put<L, P, 1>(us, tt, v);
-    wave_lds_order();
-    get<L, P + 1, 1>(us, tt, v);
-}
+#undef RQ_V32
+#undef RQ_FMAC_DPP32
+#undef RQ_FMAC_DPP8
+#undef RQ_FMAC_DPP
 
-// Pass P -> natural order (pass 0's sets, thread tt holding coordinates
-// 32 tt .. 32 tt + 31), through the same two half-token rounds.
-template <int L, int P>
-__device__ inline void to_natural(float *us, int tt, float (&v)[kE]) {
-    put<L, P, 0>(us, tt, v);
-    wave_lds_order();
-    get<L, 0, 0>(us, tt, v);
-    wave_lds_order();
-    put<L, P, 1>(us, tt, v);
-    wave_lds_order();
-    get<L, 0, 1>(us, tt, v);
-}
-
-// Code staging layout: code byte q (coordinate q << CSH; CSH = 1 for 4-bit
-// codes, 0 for 8-bit) at q + 16 (q >> (L - CSH)), i.e. 16 pad bytes after
-// every block's codes, which spreads the byte writes of one instruction over
-// the banks and keeps every 16-byte chunk aligned.
-template <int L, int CSH = 1>
-__host__ __device__ constexpr int cpad(int q) { return q + 16 * (q >> (L - CSH)); }
-template <int L, int CSH = 1>
-__host__ __device__ constexpr int cbytes(int K) {
-    return L <= 5 ? (K >> CSH) : (K >> CSH) + 16 * (K >> L) + 16;
-}
-// byte offset of the 16-byte code chunk c (4-bit coordinates 32 c .. 32 c + 31)
-// in a token's staging slot
+// the stages on index bits 5 .. L - 1, in order; coef[t] = -1 on the lane
+// whose h_t is set, else +1
 template <int L>
-__host__ __device__ constexpr int chunk_off(int c) { return L <= 5 ? 16 * c : cpad<L>(16 * c); }
+__device__ inline void lane_stages(float (&v)[kE], const float (&coef)[5]) {
+    constexpr int NB = kLaneBits<L>;
+    static_assert(NB <= 5, "block too large");
+    if constexpr (NB > 0) lane_stage<0>(v, coef[0]);
+    if constexpr (NB > 1) lane_stage<1>(v, coef[1]);
+    if constexpr (NB > 2) lane_stage<2>(v, coef[2]);
+    if constexpr (NB > 3) lane_stage<3>(v, coef[3]);
+    if constexpr (NB > 4) lane_stage<4>(v, coef[4]);
+}
+
+// After the lane stages a lane holds sign * u: -1 when an odd number of h
+// bits is set (each set bit negated the lane's values once).
+__device__ inline float lane_sign(int h) { return (__popc((unsigned)h) & 1) ? -1.0f : 1.0f; }
 
 // MXFP4 element: the E2M1 code of x / 2^e (x times inv = 2^-e, exact but for
 // values far below E2M1's smallest step, which round to code 0 either way):
 // below 1 the nearest multiple of 1/2 (rne(2 a): codes 0, 1, 2); from 1 up the
 // fp32 mantissa rounded to one bit, nearest-even (add 2^21 - 1 plus the kept
 // bit, clear the low 22), capped at 6; the code is then 2 (fp32 exponent -
-// 126) plus the mantissa bit.  The sign goes to bit 3 unless the code is 0.
-__device__ inline uint32_t e2m1_code(float x, float inv) {
+// 126) plus the mantissa bit.  The sign goes to bit 3 unless the code is 0;
+// neg (0 or 1): x is the coordinate negated (a lane's sign after the lane
+// stages).  A nonzero code has x != 0, whose sign bit is then x < 0.
+__device__ inline uint32_t e2m1_code(float x, float inv, uint32_t neg) {
     const float a = fabsf(x) * inv;
     const uint32_t small = (uint32_t)rintf(a + a);
     uint32_t b = __float_as_uint(a);
@@ -226,7 +199,8 @@ __device__ inline uint32_t e2m1_code(float x, float inv) {
     const uint32_t r = __float_as_uint(fminf(__uint_as_float(b), 6.0f));
     const uint32_t big = (((r >> 23) - 126u) << 1) | ((r >> 22) & 1u);
     const uint32_t c = a < 1.0f ? small : big;
-    return (c != 0u && x < 0.0f) ? (c | 8u) : c;
+    const uint32_t s = ((__float_as_uint(x) >> 31) ^ neg) & (c != 0u ? 1u : 0u);
+    return c | (s << 3);
 }
 
 // Order-preserving 32-bit key of a float (for LDS atomic min / max over
@@ -306,9 +280,6 @@ rpbh_quant_kernel(RpbhArgs a) {
     constexpr bool B8 = QK == 4 || QK == 5;
     constexpr int CSH = B8 ? 0 : 1;   // code byte = coordinate >> CSH
     constexpr float kLevels = QK == 5 ? 255.0f : 15.0f;   // asymmetric top code
-    // final codes in natural coordinate order per thread (32 per thread):
-    // the register layout of pass 0, or MXFP4 after its regrouping exchange
-    constexpr bool NATURAL = Plan<L>::NP == 1 || MX;
     constexpr uint32_t kCanonFlip = QK == 0 ? 0x88888888u : 0u;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ unsigned red_max[2][kMaxTpw];
@@ -321,11 +292,18 @@ rpbh_quant_kernel(RpbhArgs a) {
     const int tl = tid / a.tpt;
     const int tt = tid - tl * a.tpt;
     uint8_t *xs = smem + (size_t)tl * K * S::XB;
-    const int xw = xwords<L>(K);
-    const int cb = (cbytes<L, CSH>(K) + 15) & ~15;
-    float *us = reinterpret_cast<float *>(smem + (size_t)a.tpw * K * S::XB) + (size_t)tl * xw;
-    // code staging: one slot per token of the group
-    uint8_t *const cs0 = smem + (size_t)a.tpw * (K * S::XB + 4 * xw);
+    const int cb = ((K >> CSH) + 15) & ~15;
+    // code staging (MMA layout, grouped): one slot per token of the group
+    uint8_t *const cs0 = smem + (size_t)a.tpw * K * S::XB;
+    // the 32-coordinate chunk this thread holds, its lane's high index bits,
+    // the lane stages' coefficients and the lane's final sign
+    const int qc = chunk_of<L>(tt);
+    constexpr int NB = kLaneBits<L>;
+    const int hb = NB ? (qc & ((1 << NB) - 1)) : 0;
+    float coef[5];
+#pragma unroll
+    for (int t = 0; t < 5; ++t) coef[t] = ((hb >> t) & 1) ? -1.0f : 1.0f;
+    const float lsign = lane_sign(hb);
 
     // Workgroup b runs on XCD b % 8: number the workgroups XCD-major so that
     // each XCD works on a contiguous range of tokens, whose 32-token tiles of
@@ -357,7 +335,7 @@ rpbh_quant_kernel(RpbhArgs a) {
     }
 
     // ---- prologue: gather offsets, source-side sign masks -----------------
-    // Thread tt owns destination coordinates j = 32 tt + r: it reads perm[j]
+    // Thread tt owns destination coordinates j = 32 qc + r: it reads perm[j]
     // and sign[j] contiguously, and writes the sign bit that source element
     // perm[j] must carry into a table in the first token's staging row (one
     // element per staging element, so the 16 bytes of the table that cover a
@@ -369,7 +347,7 @@ rpbh_quant_kernel(RpbhArgs a) {
         int8_t sj[kE];
 #pragma unroll
         for (int r = 0; r < kE; r += 4) {
-            const int4 p4 = *reinterpret_cast<const int4 *>(a.perm + kE * tt + r);
+            const int4 p4 = *reinterpret_cast<const int4 *>(a.perm + kE * qc + r);
             pj[r] = p4.x;
             pj[r + 1] = p4.y;
             pj[r + 2] = p4.z;
@@ -377,7 +355,7 @@ rpbh_quant_kernel(RpbhArgs a) {
         }
 #pragma unroll
         for (int r = 0; r < kE; r += 16) {
-            const int4 s4 = *reinterpret_cast<const int4 *>(a.sign + kE * tt + r);
+            const int4 s4 = *reinterpret_cast<const int4 *>(a.sign + kE * qc + r);
             const int w[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
             for (int e = 0; e < 16; ++e) sj[r + e] = (int8_t)(w[e >> 2] >> (8 * (e & 3)));
@@ -446,8 +424,8 @@ rpbh_quant_kernel(RpbhArgs a) {
             // coordinate are not written
             const int c0 = 2 * (sh & ~1) + (sh & 1), c1 = c0 + 2;
             if (c0 >= nch) continue;
-            const uint4 w0 = *reinterpret_cast<const uint4 *>(slot + chunk_off<L>(c0));
-            const uint4 w1 = c1 < nch ? *reinterpret_cast<const uint4 *>(slot + chunk_off<L>(c1))
+            const uint4 w0 = *reinterpret_cast<const uint4 *>(slot + 16 * c0);
+            const uint4 w1 = c1 < nch ? *reinterpret_cast<const uint4 *>(slot + 16 * c1)
                                       : make_uint4(0u, 0u, 0u, 0u);
             store_pair_mma_in_tile(tile, sh >> 1, t32 + j, sh & 1, w0, w1, c1 < nch, 0u);
         }
@@ -478,8 +456,7 @@ rpbh_quant_kernel(RpbhArgs a) {
             else
                 v[r] = *reinterpret_cast<const float *>(xs + gofs[r]);
         }
-        stages<L, 0>(v);
-        if constexpr (Plan<L>::NP > 1) put<L, 0, 0>(us, tt, v);   // exchange round 0
+        reg_stages<L>(v);
         lds_barrier();  // B1: every gather of this token is done
         const int64_t next = first_tok(it + 1);
         if (next >= 0) {
@@ -490,30 +467,19 @@ rpbh_quant_kernel(RpbhArgs a) {
         // the previous group is complete: its packs are ordered by B1
         if (grouped && it > 0 && (it & ipg_mask) == 0)
             flush(vb + (int64_t)((it - 1) >> a.ipg_log2) * gridDim.x);
-        if constexpr (Plan<L>::NP > 1) {
-            exchange<L, 0, false>(us, tt, v);
-            stages<L, 1>(v);
-        }
-        if constexpr (Plan<L>::NP > 2) {
-            exchange<L, 1, true>(us, tt, v);
-            stages<L, 2>(v);
-        }
-        static_assert(Plan<L>::NP <= 3, "block too large");
-        constexpr int PL = Plan<L>::NP - 1;
-
-        if constexpr (MX && Plan<L>::NP > 1) {
-            // regroup into natural order (thread tt: coordinates 32 tt ..
-            // 32 tt + 31, one MX block), through the exchange buffer: an MX
-            // block lies inside one RPBH block, so inside one wave
-            wave_lds_order();
-            to_natural<L, PL>(us, tt, v);
-        }
+        // v = lsign * u from here on (coordinates 32 qc .. 32 qc + 31)
+        lane_stages<L>(v, coef);
         if constexpr (ASYM) {
             float lo = v[0], hi = v[0];
 #pragma unroll
             for (int r = 1; r < kE; ++r) {
                 lo = fminf(lo, v[r]);
                 hi = fmaxf(hi, v[r]);
+            }
+            if (lsign < 0.0f) {
+                const float t = lo;
+                lo = -hi;
+                hi = -t;
             }
             const unsigned klo = run_reduce<false>(fkey(lo), rg);
             const unsigned khi = run_reduce<true>(fkey(hi), rg);
@@ -550,9 +516,11 @@ rpbh_quant_kernel(RpbhArgs a) {
                 // from zero) gives z = +0
                 const float zr = rintf(lo * inv);
                 zp = zr >= 0.0f ? 0.0f : (zr < -kLevels ? kLevels : -zr);
+                // v = lsign u, so v (lsign inv) = fl32(u inv) (the sign flip is exact)
+                const float sinv = lsign * inv;
 #pragma unroll
                 for (int r = 0; r < kE; ++r) {
-                    const float t = fminf(fmaxf(rintf(v[r] * inv) + zp, 0.0f), kLevels);
+                    const float t = fminf(fmaxf(rintf(v[r] * sinv) + zp, 0.0f), kLevels);
                     nib[r] = (uint32_t)t;
                 }
             } else {
@@ -565,9 +533,10 @@ rpbh_quant_kernel(RpbhArgs a) {
             // an integer, nearest-even, and leaves q + 8 in bits 0..3 with
             // bits 4..21 clear.
             const float inv = amax > 0.0f ? 7.0f / amax : 0.0f;
+            const float sinv = lsign * inv;   // v = lsign u
 #pragma unroll
             for (int r = 0; r < kE; ++r) {
-                const float mq = v[r] * inv;
+                const float mq = v[r] * sinv;
                 nib[r] = __float_as_uint(mq + 12582920.0f);   // q + 8 in bits 0..3
             }
             sc = amax > 0.0f ? amax / 7.0f : 0.0f;
@@ -576,8 +545,9 @@ rpbh_quant_kernel(RpbhArgs a) {
             // rounds to at most 127); adding 1.5 * 2^23 leaves q in the low
             // mantissa bits, whose low byte is q in two's complement
             const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+            const float sinv = lsign * inv;   // v = lsign u
 #pragma unroll
-            for (int r = 0; r < kE; ++r) nib[r] = __float_as_uint(v[r] * inv + 12582912.0f) & 0xFFu;
+            for (int r = 0; r < kE; ++r) nib[r] = __float_as_uint(v[r] * sinv + 12582912.0f) & 0xFFu;
             sc = amax > 0.0f ? amax / 127.0f : 0.0f;
         } else if constexpr (MX) {
             // this thread's 32 coordinates are one block: e = floor(log2 max|u|) - 2
@@ -589,7 +559,7 @@ rpbh_quant_kernel(RpbhArgs a) {
             mxsc = (uint32_t)(e + 127);
             const float inv = ldexpf(1.0f, -e);   // 2^-e: 2^-125 .. 2^127, exact
 #pragma unroll
-            for (int r = 0; r < kE; ++r) nib[r] = e2m1_code(v[r], inv);
+            for (int r = 0; r < kE; ++r) nib[r] = e2m1_code(v[r], inv, lsign < 0.0f ? 1u : 0u);
         } else {
             // exact squared norm on the grid 2^(2E - 36), E = ilogb(max |u|):
             // each term rint(u^2 2^(36 - 2E)) = rint((u 2^(18 - E))^2) (both
@@ -614,9 +584,10 @@ rpbh_quant_kernel(RpbhArgs a) {
                 const double d = ldexp((double)S, 2 * E - 36);
                 const float g = (float)sqrt((double)K / d);
                 sc = (float)sqrt(d / (double)K);
+                const float sg = lsign * g;   // v = lsign u: x = fl32(u g)
 #pragma unroll
                 for (int r = 0; r < kE; ++r) {
-                    const float x = v[r] * g;
+                    const float x = v[r] * sg;
                     uint32_t idx = 0;
                     if (a.th_sym) {
                         // Symmetric book: for x > 0 the eight thresholds up to
@@ -641,74 +612,49 @@ rpbh_quant_kernel(RpbhArgs a) {
             }
         }
 
-        // pack: register bit 0 carries index bit 0, so registers (2m, 2m + 1)
-        // hold a nibble (byte) pair; bits 4..7 (8..31) of every code word are clear
-        uint4 chunk = make_uint4(0u, 0u, 0u, 0u), chunk1 = make_uint4(0u, 0u, 0u, 0u);
-        if constexpr (NATURAL) {
-            if constexpr (B8) {
-                uint32_t w[8];
+        // pack: the thread's 32 codes are coordinates 32 qc .. 32 qc + 31 in
+        // register order; bits 4..7 (8..31) of every code word are clear
+        uint4 chunk, chunk1 = make_uint4(0u, 0u, 0u, 0u);
+        if constexpr (B8) {
+            uint32_t w[8];
 #pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    w[q] = nib[4 * q] | (nib[4 * q + 1] << 8) | (nib[4 * q + 2] << 16) | (nib[4 * q + 3] << 24);
-                chunk = make_uint4(w[0], w[1], w[2], w[3]);
-                chunk1 = make_uint4(w[4], w[5], w[6], w[7]);
-            } else {
-                uint32_t w[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    uint32_t x = 0;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) x |= (nib[8 * q + e] & 0xFu) << (4 * e);
-                    w[q] = x;
-                }
-                chunk = make_uint4(w[0], w[1], w[2], w[3]);
-                if (grouped) *reinterpret_cast<uint4 *>(cs + 16 * tt) = chunk;
-            }
+            for (int m = 0; m < 8; ++m)
+                w[m] = nib[4 * m] | (nib[4 * m + 1] << 8) | (nib[4 * m + 2] << 16) | (nib[4 * m + 3] << 24);
+            chunk = make_uint4(w[0], w[1], w[2], w[3]);
+            chunk1 = make_uint4(w[4], w[5], w[6], w[7]);
         } else {
-            uint8_t *p = cs + cpad<L, CSH>(pbase<L, PL>(tt) >> CSH);
-            if constexpr (B8) {
+            // byte m = code 2m | code 2m + 1 << 4 (one shift-or: only bits
+            // 0..3 of a code word and 4..7 of the shifted one reach byte 0),
+            // then byte selects: two bytes per halfword, two halfwords per word
+            uint32_t by[16], hw[8], w[4];
 #pragma unroll
-                for (int mm = 0; mm < kE / 2; ++mm)
-                    *reinterpret_cast<uint16_t *>(p + Plan<L>::roff(PL, 2 * mm)) =
-                        (uint16_t)(nib[2 * mm] | (nib[2 * mm + 1] << 8));
-            } else {
+            for (int m = 0; m < 16; ++m) by[m] = (nib[2 * m + 1] << 4) | nib[2 * m];
 #pragma unroll
-                for (int mm = 0; mm < kE / 2; ++mm)
-                    p[Plan<L>::roff(PL, 2 * mm) >> 1] = (uint8_t)(nib[2 * mm] | (nib[2 * mm + 1] << 4));
-            }
-            if (a.codes || (a.codes_mma && !grouped)) {
-                // the bytes this thread stores were written by lanes of its
-                // own wave (its RPBH block): order the LDS writes before the read
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                if constexpr (B8) {
-                    chunk = *reinterpret_cast<const uint4 *>(cs + cpad<L, 0>(32 * tt));
-                    chunk1 = *reinterpret_cast<const uint4 *>(cs + cpad<L, 0>(32 * tt) + 16);
-                } else {
-                    chunk = *reinterpret_cast<const uint4 *>(cs + cpad<L>(16 * tt));
-                }
-            }
+            for (int m = 0; m < 8; ++m) hw[m] = __builtin_amdgcn_perm(by[2 * m + 1], by[2 * m], 0x0c0c0400u);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) w[m] = __builtin_amdgcn_perm(hw[2 * m + 1], hw[2 * m], 0x05040100u);
+            chunk = make_uint4(w[0], w[1], w[2], w[3]);
+            if (grouped) *reinterpret_cast<uint4 *>(cs + 16 * qc) = chunk;
         }
         if (valid) {
             if (a.codes) {
                 if constexpr (B8) {
-                    uint4 *dst = reinterpret_cast<uint4 *>(a.codes + tok * (int64_t)K + 32 * tt);
+                    uint4 *dst = reinterpret_cast<uint4 *>(a.codes + tok * (int64_t)K + 32 * qc);
                     dst[0] = chunk;
                     dst[1] = chunk1;
                 } else {
-                    *reinterpret_cast<uint4 *>(a.codes + tok * (int64_t)(K / 2) + 16 * tt) =
+                    *reinterpret_cast<uint4 *>(a.codes + tok * (int64_t)(K / 2) + 16 * qc) =
                         make_uint4(chunk.x ^ kCanonFlip, chunk.y ^ kCanonFlip, chunk.z ^ kCanonFlip,
                                    chunk.w ^ kCanonFlip);
                 }
             }
             if constexpr (QK == 0 || QK == 2)
-                if (a.codes_mma && !grouped) store_chunk_mma(a.codes_mma, tok, a.mma_stages, tt, chunk, 0u);
+                if (a.codes_mma && !grouped) store_chunk_mma(a.codes_mma, tok, a.mma_stages, qc, chunk, 0u);
             if constexpr (B8) {
                 // the int8 GEMM's fragment order [t / 32][k-step][lane][16 B]: the
-                // thread's 32 codes are k-step tt, lanes t % 32 and t % 32 + 32
+                // thread's 32 codes are k-step qc, lanes t % 32 and t % 32 + 32
                 if (a.codes_mma) {
-                    uint8_t *d = a.codes_mma + (((tok >> 5) * (K / 32) + tt) * 64 + (tok & 31)) * 16;
+                    uint8_t *d = a.codes_mma + (((tok >> 5) * (K / 32) + qc) * 64 + (tok & 31)) * 16;
                     *reinterpret_cast<uint4 *>(d) = chunk;
                     *reinterpret_cast<uint4 *>(d + 512) = chunk1;
                 }
@@ -726,23 +672,23 @@ rpbh_quant_kernel(RpbhArgs a) {
                         const uint32_t w = wq[c];
                         const uint4 v = make_uint4(lev_pair[w & 0xFFu], lev_pair[(w >> 8) & 0xFFu],
                                                    lev_pair[(w >> 16) & 0xFFu], lev_pair[w >> 24]);
-                        *reinterpret_cast<uint4 *>(tile + (2 * tt + (c >> 1)) * 1024 + 512 * (c & 1)) = v;
+                        *reinterpret_cast<uint4 *>(tile + (2 * qc + (c >> 1)) * 1024 + 512 * (c & 1)) = v;
                     }
                 }
             }
             if constexpr (MX) {
-                // E8M0 code of block tt: canonical [T][K/32], and the tiled
+                // E8M0 code of block qc: canonical [T][K/32], and the tiled
                 // copies [tile][K/32][32][16] (codes) and
                 // [stage][tile][64][2] (scales) of the scaled FP4 GEMM
                 const int nch = K / kE;
-                if (a.scale) reinterpret_cast<uint8_t *>(a.scale)[tok * nch + tt] = (uint8_t)mxsc;
+                if (a.scale) reinterpret_cast<uint8_t *>(a.scale)[tok * nch + qc] = (uint8_t)mxsc;
                 if (a.codes_mma) {
                     const int64_t tile = tok >> 5;
                     const int row = (int)(tok & 31);
-                    *reinterpret_cast<uint4 *>(a.codes_mma + ((tile * nch + tt) * 32 + row) * 16) = chunk;
+                    *reinterpret_cast<uint4 *>(a.codes_mma + ((tile * nch + qc) * 32 + row) * 16) = chunk;
                     uint8_t *mxs = a.codes_mma + (int64_t)a.mx_tiles * nch * 512;
-                    mxs[(((int64_t)(tt >> 2) * a.mx_tiles + tile) * 64 + 32 * (tt & 1) + row) * 2 +
-                        ((tt >> 1) & 1)] = (uint8_t)mxsc;
+                    mxs[(((int64_t)(qc >> 2) * a.mx_tiles + tile) * 64 + 32 * (qc & 1) + row) * 2 +
+                        ((qc >> 1) & 1)] = (uint8_t)mxsc;
                 }
             } else if (tt == 0) {
                 a.scale[tok] = sc;
@@ -760,19 +706,17 @@ rpbh_quant_kernel(RpbhArgs a) {
 template <int L, bool BF16, int QK>
 hipError_t launch_L(RpbhArgs a, hipStream_t s) {
     const int xb = BF16 ? 2 : 4;
-    const size_t per_tok = (size_t)a.K * xb + 4 * (size_t)xwords<L>(a.K);
+    const size_t per_tok = (size_t)a.K * xb;
     constexpr int CSH = (QK == 4 || QK == 5) ? 0 : 1;
-    const size_t slot_bytes = (size_t)((cbytes<L, CSH>(a.K) + 15) & ~15);
+    const size_t slot_bytes = (size_t)((((size_t)a.K >> CSH) + 15) & ~(size_t)15);
     // the dynamic LDS a workgroup may take (160 KB less the static arrays)
     constexpr size_t kLdsMax = 159 * 1024;
     // MMA-layout codes are written per group of >= 4 consecutive tokens when
     // the group's code slots fit, else per token
     const bool grouped = (QK == 0 || QK == 2) && a.codes_mma != nullptr && per_tok + 4 * slot_bytes <= kLdsMax;
     a.grouped = grouped ? 1 : 0;
-    // per-token code staging: the regrouping exchange (blocks > 32), or the
-    // group's slots
-    // (MXFP4 regroups its values in the exchange buffer instead)
-    const size_t slot = ((L <= 5 && !grouped) || QK == 3) ? 0 : slot_bytes;
+    // per-token code staging: the group's slots (grouped MMA-layout codes only)
+    const size_t slot = grouped ? slot_bytes : 0;
     auto group_of = [&](int tpw) { return grouped && tpw < 4 ? 4 : tpw; };
     auto lds_of = [&](int tpw) { return per_tok * tpw + slot * group_of(tpw); };
     auto kern = rpbh_quant_kernel<L, BF16, QK>;
