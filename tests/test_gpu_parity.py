@@ -163,6 +163,14 @@ SMALL = [
     ("tiny", dict(T=45, K=64, N=48, block=64)),
     ("tiny", dict(T=21, K=192, N=40, block=64)),
     ("flux_up_asym", dict(T=33, K=64, N=40, block=64)),
+    # the block's high index bits across 16 and 32 lanes (the lane stages'
+    # last mask is a swizzle at block 1024) under every quantizer that folds
+    # the lanes' sign: zero point, codebook, 8-bit codes
+    ("flux_up_asym", dict(T=70, K=2048, N=96, block=1024)),
+    ("video", dict(T=70, K=2048, N=96, block=1024)),
+    ("video_w4", dict(T=45, K=1024, N=64, block=512)),
+    ("flux_up_w8a8", dict(T=70, K=2048, N=96, block=1024)),
+    ("flux_up_w4a8", dict(T=33, K=1024, N=40, block=512)),
 ]
 
 
