@@ -202,7 +202,7 @@ def quant_int4_wrow(v):
 
 
 def quant_sym_row(u, r=0, qmax=7):
-    """Symmetric per-token quantizer with qmax 7 (INT4) or 127 (INT8)."""
+    """Symmetric per-token quantizer with qmax 7 (INT4), 31 (6-bit) or 127 (INT8)."""
     u = np.ascontiguousarray(u, np.float32)
     q = np.zeros(u.size - r, np.int16)
     s = ctypes.c_float(0)
@@ -211,7 +211,7 @@ def quant_sym_row(u, r=0, qmax=7):
 
 
 def quant_asym_row(u, levels=15):
-    """Asymmetric per-token quantizer with 15 (4-bit) or 255 (8-bit) levels."""
+    """Asymmetric per-token quantizer with 15 (4-bit), 63 (6-bit) or 255 (8-bit) levels."""
     u = np.ascontiguousarray(u, np.float32)
     q = np.zeros(u.size, np.uint16)
     s, z = ctypes.c_float(0), ctypes.c_float(0)
@@ -408,7 +408,8 @@ def act_rows(X, xdtype, K, rows, *, rot_kind, b=0, sign=None, perm=None, R=None,
     rot_kind 0 RPBH (b, sign, perm), 1 dense (R, r), 2 TR-DQ (b, m, R = the
     first block rotation, perm, R2).  q_kind 0 symmetric integer, 1
     Lloyd-Max, 2 asymmetric integer (also returns the zero points), 3 MXFP4
-    (also returns the E8M0 block scales); a_bits 4 or 8 for the integer kinds.
+    (also returns the E8M0 block scales); a_bits 4, 6 or 8 for the integer
+    kinds (4-bit codes two per byte, 6- and 8-bit codes one per byte).
     Returns dict(codes, scale, zero, top, u, mx_scales)."""
     rows = np.ascontiguousarray(rows, np.int64)
     n = rows.size
@@ -417,7 +418,7 @@ def act_rows(X, xdtype, K, rows, *, rot_kind, b=0, sign=None, perm=None, R=None,
     if q_kind in (1, 3):
         ncode = K // 2
     else:
-        ncode = Kq * a_bits // 8
+        ncode = Kq // 2 if a_bits == 4 else Kq
     codes = np.zeros((n, ncode), np.uint8)
     scale = np.zeros(n, np.float32)
     zero = np.zeros(n, np.float32) if q_kind == 2 else None
@@ -445,7 +446,7 @@ def weight_rows(W, *, rot_kind, b=0, sign=None, perm=None, R=None, m=None, R2=No
     elif q_kind == 3:
         ncode = K // 2
     else:
-        ncode = K * w_bits // 8
+        ncode = K // 2 if w_bits == 4 else K
     codes = np.zeros((N, ncode), np.uint8)
     scale = np.zeros(N, np.float32)
     mx = np.zeros((N, K // 32), np.uint8) if q_kind == 3 else None
@@ -490,7 +491,8 @@ def asym_gemm_pairs(codes_a, codes_w, K, ta, nw):
 
 
 def gemm_codes_pairs(codes_a, a_bits, a_signed, Kq, codes_w, w_bits, Kw, ta, nw, koff=0):
-    """acc[p] = sum_k a[t_p][k] w[n_p][koff + k] for 4- or 8-bit codes, int64."""
+    """acc[p] = sum_k a[t_p][k] w[n_p][koff + k] for 4-, 6- or 8-bit codes
+    (6-bit codes one per byte), int64."""
     ta = np.ascontiguousarray(ta, np.int64)
     nw = np.ascontiguousarray(nw, np.int64)
     acc = np.zeros(ta.size, np.int64)

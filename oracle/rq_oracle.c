@@ -177,7 +177,8 @@ void orc_quant_int4_row(const float *u, int K, int r, int8_t *q, float *s_out)
 
 /*
  * Per-token symmetric b-bit quantizer of a rotated row, qmax = 2^(b-1) - 1
- * (7 for INT4, 127 for INT8 -- TR-DQ's W8A8 / W4A8 settings), over the
+ * (7 for INT4, 31 for 6-bit, 127 for INT8 -- TR-DQ's W6A6, W8A8 and W4A8
+ * settings), over the
  * coordinates u[r..K-1]:
  *   amax = max |u[j]|
  *   amax == 0  ->  all codes 0, scale 0
@@ -231,7 +232,7 @@ void orc_quant_int4_asym_row(const float *u, int K, uint8_t *q, float *s_out, fl
 }
 
 /*
- * Per-token asymmetric b-bit quantizer, levels = 2^b - 1 (15 or 255), over
+ * Per-token asymmetric b-bit quantizer, levels = 2^b - 1 (15, 63 or 255), over
  * all K coordinates ([TRDQ] Eq.(1)-(3)).  Readings where the pages are open
  * or garbled:
  *   - Eq.(3) prints z = round(min X / s); with Eq.(1)'s "+ z" the minimum
@@ -281,7 +282,7 @@ void orc_quant_asym_row(const float *u, int K, int levels, uint16_t *q, float *s
 }
 
 /* Per-output-channel symmetric b-bit quantizer of a folded fp64 weight row
- * (all K), qmax = 7 (INT4) or 127 (INT8):
+ * (all K), qmax = 7 (INT4), 31 (6-bit) or 127 (INT8):
  *   amax == 0 -> codes 0, scale 0
  *   s_w = (float)(amax / qmax), inv = qmax / amax (fp64), q = clamp(rne(v*inv)). */
 void orc_quant_sym_wrow(const double *v, int K, int qmax, int16_t *q, float *s_out)
@@ -660,12 +661,14 @@ static void rotate_row_f64(const orc_rot *rot, const double *w, int K, double *v
 /*
  * Activation side of the layer for a list of rows.
  *   rot      the rotation (RPBH, dense R with top-r bf16, or TR-DQ)
- *   q_kind   0: symmetric integer, a_bits 4 or 8 -> codes [nrows][K-r]
- *               as nibbles (4) or int8 bytes (8), scale[nrows]
+ *   q_kind   0: symmetric integer, a_bits 4, 6 or 8 (qmax 7, 31, 127) ->
+ *               codes [nrows][K-r] as nibbles (4) or int8 bytes (6, 8),
+ *               scale[nrows]
  *            1: Lloyd-Max (levels, L=16) -> codes [nrows][K/2] nibbles of the
  *               4-bit index, scale[nrows] = sigma
- *            2: asymmetric integer, a_bits 4 or 8 (r = 0) -> unsigned nibbles
- *               or bytes [nrows][K], scale[nrows] = s, zero[nrows] = z
+ *            2: asymmetric integer, a_bits 4, 6 or 8 (r = 0; 15, 63, 255
+ *               levels) -> unsigned nibbles (4) or bytes (6, 8) [nrows][K],
+ *               scale[nrows] = s, zero[nrows] = z
  *            3: MXFP4 (r = 0) -> codes [nrows][K/2] E2M1 nibbles,
  *               mx_scales [nrows][K/32] E8M0 codes
  *   top: bf16 [nrows][r] (dense only), may be NULL when r == 0.
@@ -678,7 +681,9 @@ void orc_act_rows(const void *X, int xdtype, int K, const int64_t *rows, int64_t
                   uint8_t *mx_scales, float *u_out)
 {
     int Kq = K - r;
-    int row_bytes = q_kind == 3 || q_kind == 1 ? K / 2 : (Kq * a_bits) / 8;
+    /* 4-bit codes two per byte, 6- and 8-bit codes one per byte */
+    const int a_bytes = a_bits != 4;
+    int row_bytes = q_kind == 3 || q_kind == 1 ? K / 2 : (a_bytes ? Kq : Kq / 2);
 #pragma omp parallel
     {
         float *x = (float *)malloc((size_t)K * 4);
@@ -694,8 +699,8 @@ void orc_act_rows(const void *X, int xdtype, int K, const int64_t *rows, int64_t
             if (u_out)
                 memcpy(u_out + (size_t)i * K, u, (size_t)K * 4);
             if (q_kind == 0) {
-                orc_quant_sym_row(u, K, r, a_bits == 8 ? 127 : 7, q, &scale[i]);
-                if (a_bits == 8) {
+                orc_quant_sym_row(u, K, r, (1 << (a_bits - 1)) - 1, q, &scale[i]);
+                if (a_bytes) {
                     for (int j = 0; j < Kq; j++)
                         crow[j] = (uint8_t)(int8_t)q[j];
                 } else {
@@ -706,8 +711,8 @@ void orc_act_rows(const void *X, int xdtype, int K, const int64_t *rows, int64_t
                 for (int j = 0; j < r; j++)
                     top[(size_t)i * r + j] = orc_f32_to_bf16(u[j]);
             } else if (q_kind == 2) {
-                orc_quant_asym_row(u, K, a_bits == 8 ? 255 : 15, ix, &scale[i], &zero[i]);
-                if (a_bits == 8) {
+                orc_quant_asym_row(u, K, (1 << a_bits) - 1, ix, &scale[i], &zero[i]);
+                if (a_bytes) {
                     for (int j = 0; j < K; j++)
                         crow[j] = (uint8_t)ix[j];
                 } else {
@@ -729,8 +734,9 @@ void orc_act_rows(const void *X, int xdtype, int K, const int64_t *rows, int64_t
 /*
  * Weight side (offline): fold every row of W [N][K] (fp32) with the rotation
  * in fp64, then quantize.
- *   q_kind 0, 2: symmetric integer over all K, w_bits 4 or 8 -> codes
- *             [N][K/2] nibbles or [N][K] int8 bytes, scale s_w[N]; qvals
+ *   q_kind 0, 2: symmetric integer over all K, w_bits 4, 6 or 8 (qmax 7,
+ *             31, 127) -> codes [N][K/2] nibbles (4) or [N][K] int8 bytes
+ *             (6, 8), scale s_w[N]; qvals
  *             (optional) [N][K] signed codes
  *   q_kind 1: Lloyd-Max (levels, L = 4 or 16) -> codes [N][K/4] crumbs
  *             (L = 4) or [N][K/2] nibbles (L = 16), scale tau[N];
@@ -754,10 +760,10 @@ void orc_weight_rows(const float *W, int N, int K, const orc_rot *rot, int q_kin
                 w[k] = (double)W[(size_t)n * K + k];
             rotate_row_f64(rot, w, K, v);
             if (q_kind == 0 || q_kind == 2) {
-                orc_quant_sym_wrow(v, K, w_bits == 8 ? 127 : 7, q, &scale[n]);
+                orc_quant_sym_wrow(v, K, (1 << (w_bits - 1)) - 1, q, &scale[n]);
                 for (int k = 0; k < K; k++)
                     b8[k] = (uint8_t)(int8_t)q[k];
-                if (w_bits == 8)
+                if (w_bits != 4)
                     memcpy(codes + (size_t)n * K, b8, (size_t)K);
                 else
                     orc_pack_nibbles((const int8_t *)b8, K, codes + (size_t)n * (K / 2));
@@ -900,13 +906,15 @@ void orc_codebook_dot_pairs(const uint8_t *codes_a, const uint8_t *codes_w, int 
     }
 }
 
-/* Code i of a packed row of `bits`-bit codes (4: nibbles, low nibble = even
- * index; 8: bytes), two's complement when is_signed, else unsigned. */
+/* Code i of a row of `bits`-bit codes (4: nibbles, low nibble = even index;
+ * 6 and 8: one per byte), two's complement in its container (nibble or
+ * byte) when is_signed, else unsigned. */
 static int code_at(const uint8_t *row, int bits, int is_signed, int i)
 {
-    int v = bits == 8 ? row[i] : (row[i >> 1] >> ((i & 1) * 4)) & 0xF;
+    const int cont = bits == 4 ? 4 : 8;
+    int v = cont == 8 ? row[i] : (row[i >> 1] >> ((i & 1) * 4)) & 0xF;
     if (is_signed) {
-        int half = 1 << (bits - 1);
+        int half = 1 << (cont - 1);
         if (v >= half)
             v -= 2 * half;
     }
@@ -914,16 +922,17 @@ static int code_at(const uint8_t *row, int bits, int is_signed, int i)
 }
 
 /*
- * Integer GEMM of 4- or 8-bit codes for listed pairs, int64:
+ * Integer GEMM of 4-, 6- or 8-bit codes for listed pairs, int64:
  *   acc[p] = sum_{k < Kq} a[t_p][k] * w[n_p][koff + k]
  * a: rows of Kq codes of a_bits (signed or unsigned); w: rows of Kw signed
- * codes of w_bits.  (W4A4, W4A8 and W8A8 of [TRDQ]'s settings.)
+ * codes of w_bits.  (W4A4, and the W4A8, W8A8 and W6A6 settings of the
+ * "TR-DQ" page's tables.)
  */
 void orc_gemm_codes_pairs(const uint8_t *codes_a, int a_bits, int a_signed, int Kq,
                           const uint8_t *codes_w, int w_bits, int Kw, int koff,
                           const int64_t *ta, const int64_t *nw, int64_t npairs, int64_t *acc)
 {
-    size_t arow = (size_t)Kq * a_bits / 8, wrow = (size_t)Kw * w_bits / 8;
+    size_t arow = a_bits == 4 ? (size_t)Kq / 2 : (size_t)Kq, wrow = w_bits == 4 ? (size_t)Kw / 2 : (size_t)Kw;
 #pragma omp parallel for schedule(static)
     for (int64_t p = 0; p < npairs; p++) {
         const uint8_t *ra = codes_a + (size_t)ta[p] * arow;

@@ -173,19 +173,21 @@ def is_nearest_f32(s, exact):
     return d <= abs(Fraction(float(dn)) - exact) and d <= abs(Fraction(float(up)) - exact)
 
 
+@pytest.mark.parametrize("qmax", [31, 127])
 @pytest.mark.parametrize("seed", range(4))
-def test_int8_activation_brute_force(seed):
+def test_int8_activation_brute_force(seed, qmax):
+    # qmax 127: 8-bit codes (W8A8, W4A8); 31: 6-bit codes (W6A6)
     g = np.random.default_rng(10 + seed)
     K = 64
     u = (g.standard_normal(K) * g.choice([1e-3, 1.0, 37.0])).astype(np.float32)
-    q, s = orc.quant_sym_row(u, qmax=127)
+    q, s = orc.quant_sym_row(u, qmax=qmax)
     amax = Fraction(float(np.max(np.abs(u))))
-    assert is_nearest_f32(s, amax / 127)
-    inv = np.float32(127.0) / np.float32(float(amax))
-    assert is_nearest_f32(inv, Fraction(127) / amax)
+    assert is_nearest_f32(s, amax / qmax)
+    inv = np.float32(qmax) / np.float32(float(amax))
+    assert is_nearest_f32(inv, Fraction(qmax) / amax)
     for j in range(K):
-        assert q[j] == rne_argmin(np.float32(u[j]) * inv, -127, 127), j
-    assert abs(int(q[int(np.argmax(np.abs(u)))])) == 127
+        assert q[j] == rne_argmin(np.float32(u[j]) * inv, -qmax, qmax), j
+    assert abs(int(q[int(np.argmax(np.abs(u)))])) == qmax
 
 
 def test_sym_quantizer_reduces_to_int4():
@@ -204,33 +206,36 @@ def test_sym_quantizer_reduces_to_int4():
     assert np.array_equal(qw, q4.astype(np.int16)) and sw == s4
 
 
+@pytest.mark.parametrize("levels", [63, 255])
 @pytest.mark.parametrize("seed", range(3))
-def test_asym8_activation_brute_force(seed):
+def test_asym8_activation_brute_force(seed, levels):
+    # 255 levels: 8-bit codes; 63: 6-bit codes
     g = np.random.default_rng(30 + seed)
     K = 64
     u = (g.standard_normal(K) + g.choice([0.0, 2.5])).astype(np.float32)
-    q, s, z = orc.quant_asym_row(u, levels=255)
+    q, s, z = orc.quant_asym_row(u, levels=levels)
     lo, hi = np.float32(u.min()), np.float32(u.max())
     d = np.float32(hi - lo)
-    assert is_nearest_f32(s, Fraction(float(d)) / 255)
-    inv = np.float32(255.0) / d
+    assert is_nearest_f32(s, Fraction(float(d)) / levels)
+    inv = np.float32(levels) / d
     zi = -round(Fraction(float(np.float32(lo * inv))))      # Fraction rounds half to even
-    assert z == float(min(max(zi, 0), 255)) and np.float32(z).view(np.uint32) == np.float32(abs(z)).view(np.uint32)
+    assert z == float(min(max(zi, 0), levels)) and np.float32(z).view(np.uint32) == np.float32(abs(z)).view(np.uint32)
     for j in range(K):
-        ref = min(max(round(Fraction(float(np.float32(u[j]) * inv))) + int(z), 0), 255)
+        ref = min(max(round(Fraction(float(np.float32(u[j]) * inv))) + int(z), 0), levels)
         assert q[j] == ref, j
     assert q.min() == 0 if zi >= 0 else True
 
 
-def test_int8_weight_row_brute_force():
+@pytest.mark.parametrize("qmax", [31, 127])
+def test_int8_weight_row_brute_force(qmax):
     g = np.random.default_rng(40)
     v = g.standard_normal(80) * 0.05
-    q, s = orc.quant_sym_wrow(v, qmax=127)
+    q, s = orc.quant_sym_wrow(v, qmax=qmax)
     amax = float(np.max(np.abs(v)))
-    assert s == np.float32(amax / 127)
-    inv = 127 / amax
+    assert s == np.float32(amax / qmax)
+    inv = qmax / amax
     for j in range(v.size):
-        assert q[j] == rne_argmin(v[j] * inv, -127, 127)
+        assert q[j] == rne_argmin(v[j] * inv, -qmax, qmax)
 
 
 def test_gemm_codes_against_numpy():
@@ -238,8 +243,11 @@ def test_gemm_codes_against_numpy():
     T, N, K = 7, 9, 96
     qa8 = g.integers(-127, 128, (T, K))
     ua8 = g.integers(0, 256, (T, K))
+    qa6 = g.integers(-31, 32, (T, K))
+    ua6 = g.integers(0, 64, (T, K))
     qa4 = g.integers(-7, 8, (T, K))
     qw8 = g.integers(-127, 128, (N, K))
+    qw6 = g.integers(-31, 32, (N, K))
     qw4 = g.integers(-7, 8, (N, K))
     ta, nw = np.meshgrid(np.arange(T), np.arange(N), indexing="ij")
     ta, nw = ta.ravel(), nw.ravel()
@@ -248,11 +256,15 @@ def test_gemm_codes_against_numpy():
         q = (q & 15).astype(np.uint8)
         return (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
 
+    # 6-bit codes sit one per byte, two's complement in the byte when signed
     cases = [(qa8.astype(np.int8).view(np.uint8), 8, True, qa8),
              (ua8.astype(np.uint8), 8, False, ua8),
+             (qa6.astype(np.int8).view(np.uint8), 6, True, qa6),
+             (ua6.astype(np.uint8), 6, False, ua6),
              (nib(qa4), 4, True, qa4)]
     for ca, ab, sg, qa in cases:
-        for cw, wb, qw in ((qw8.astype(np.int8).view(np.uint8), 8, qw8), (nib(qw4), 4, qw4)):
+        for cw, wb, qw in ((qw8.astype(np.int8).view(np.uint8), 8, qw8),
+                           (qw6.astype(np.int8).view(np.uint8), 6, qw6), (nib(qw4), 4, qw4)):
             acc = orc.gemm_codes_pairs(ca, ab, sg, K, cw, wb, K, ta, nw)
             assert np.array_equal(acc, (qa @ qw.T).ravel())
 

@@ -96,3 +96,36 @@ def test_rotated_coordinates_follow_one_marginal():
     ks = kstest(v, "norm").statistic
     print(f"KS distance of normalized RPBH coordinates to N(0,1): {ks:.4f}")
     assert ks < 0.02
+
+
+def test_w6a6_layer_codes_and_snr():
+    """TR-DQ's W6A6 setting (its Tables 1 and 4): Eq.(1)-(3) with b = 6, so
+    qmax = 31 per token and per channel, codes one per byte.  The layer
+    driver's codes are the standalone quantizer's on the same rotated rows,
+    and the layer's error sits between W4A4's and W8A8's."""
+    w = datagen.WORKLOADS["tiny"].with_shape(T=48, N=64)
+    inp = datagen.make_inputs(w)
+    X, W, K, T = inp["X"], inp["W"], w.K, w.T
+    rot = dict(rot_kind=0, b=w.block, sign=inp["sign"], perm=inp["perm"])
+    ref = inp["Xf"].astype(np.float64) @ W.astype(np.float64).T
+    ta, nw = np.meshgrid(np.arange(T), np.arange(w.N), indexing="ij")
+    snr = {}
+    for bits in (4, 6, 8):
+        a = orc.act_rows(X, 0, K, np.arange(T), a_bits=bits, want_u=True, **rot)
+        wt = orc.weight_rows(W, w_bits=bits, **rot)
+        qmax = (1 << (bits - 1)) - 1
+        if bits == 6:
+            assert a["codes"].shape == (T, K) and wt["codes"].shape == (w.N, K)
+            for i in range(T):
+                q, s = orc.quant_sym_row(a["u"][i], qmax=31)
+                assert np.array_equal(a["codes"][i].view(np.int8), q.astype(np.int8)) and a["scale"][i] == s
+            assert np.array_equal(wt["codes"].view(np.int8), wt["q"].astype(np.int8))
+            assert np.abs(wt["q"]).max() == 31
+        acc = orc.gemm_codes_pairs(a["codes"], bits, True, K, wt["codes"], bits, K, ta.ravel(), nw.ravel())
+        y = (a["scale"][ta.ravel()].astype(np.float64) * wt["scale"][nw.ravel()].astype(np.float64)
+             * acc / w.block).reshape(T, w.N)
+        assert np.abs(acc).max() <= K * qmax * qmax
+        snr[bits] = snr_db(y, ref)
+    print(f"tiny SNR by bits: {snr}")
+    # about 6 dB per bit of both operands
+    assert snr[4] + 6.0 < snr[6] < snr[8] - 6.0
