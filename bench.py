@@ -60,6 +60,8 @@ WORKLOADS = {
     "flux_up_w4a8": ["flux_up_w4a8"],
     "flux_up_w8a8": ["flux_up_w8a8"],
     "flux_up_trdq": ["flux_up_trdq"],
+    "flux_up_trdq_w6a6": ["flux_up_trdq_w6a6"],
+    "flux_up_w6a6": ["flux_up_w6a6"],
     "tiny": ["tiny"],
     "pixart": ["pixart"],
     "video": ["video"],
@@ -362,7 +364,7 @@ def main():
     rq.load()
     names = WORKLOADS[args.workload]
     wls = [datagen.WORKLOADS[n] for n in names]
-    int8_gemm = args.engine == "int8" or any(w.a_bits == 8 for w in wls)
+    int8_gemm = args.engine == "int8" or any(w.a_bits != 4 for w in wls)
 
     # ring of independent instances (distinct seeds), all resident in HBM
     ring = []
@@ -482,7 +484,7 @@ def main():
             "gemm_cb_kernel", "bf16"
     elif w0.quant == "mxfp4":
         peak, gsrc, gkey, gname, dtype = PEAK_FP6_TOPS, "rq_gemm_mx.hip", "gemm_mx", "gemm_mx_kernel", "fp4"
-    elif w0.a_bits == 8:
+    elif w0.a_bits != 4:
         peak, gsrc, gkey, gname, dtype = PEAK_INT8_TOPS, "rq_gemm_i8.hip", "gemm_i8", \
             "gemm_i8_kernel", "i8"
     elif int8_gemm:

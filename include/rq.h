@@ -29,7 +29,8 @@
  *
  * and three quantizer families:
  *
- *   INT (RQ_Q_INT4_SYM / RQ_Q_INT4_ASYM, a_bits 4 or 8, w_bits 4 or 8)
+ *   INT (RQ_Q_INT4_SYM / RQ_Q_INT4_ASYM, a_bits 4, 6 or 8, w_bits 4, 6
+ *        or 8; 6- and 8-bit codes are stored one per byte)
  *              round-to-nearest-even integers, one fp32 scale per token
  *              (activations, symmetric in [-qmax, qmax] or asymmetric in
  *              [0, 2^b - 1] with a zero point) and per output channel
@@ -92,7 +93,7 @@ typedef enum rq_dtype {
 
 /* Matrix cores that run an INT4 GEMM (rq_w4a4_linear_engine).
  *   AUTO  the library's choice: FP6 for INT weights with 4-bit activations,
- *         int8 for 8-bit activations, the scaled FP4 cores for MXFP4, the
+ *         int8 for 6- and 8-bit activations, the scaled FP4 cores for MXFP4, the
  *         codebook kernel for Lloyd-Max weights
  *   FP6   E2M3 operands on v_mfma_scale_f32_32x32x64_f8f6f4: codes carried
  *         exactly, fp32 accumulation exact, twice the int8 rate
@@ -150,9 +151,10 @@ typedef struct rq_rotation {
  * Quantizer descriptor (plain values, no pointers).
  *   kind      rq_q_kind.  INT4_ASYM: activations per token with a zero point
  *             (TR-DQ section 3.1 Eq.(1)-(3)), weights symmetric; RPBH or TRDQ
- *   a_bits    INT kinds: 4 or 8 (8: RPBH or TRDQ, symmetric weights of
- *             w_bits 4 or 8; 4: w_bits 4);  LLOYDMAX, MXFP4: 4
- *   w_bits    INT kinds: 4 or 8;  LLOYDMAX: 2 or 4;  MXFP4: 4
+ *   a_bits    INT kinds: 4, 6 or 8 (6, 8: RPBH or TRDQ, symmetric weights
+ *             of w_bits 4, 6 or 8 -- TR-DQ's W4A8, W8A8 and W6A6 settings;
+ *             4: w_bits 4);  LLOYDMAX, MXFP4: 4
+ *   w_bits    INT kinds: 4, 6 or 8;  LLOYDMAX: 2 or 4;  MXFP4: 4
  *   a_levels  LLOYDMAX: 2^a_bits strictly ascending, bf16-representable
  *   w_levels  LLOYDMAX: 2^w_bits strictly ascending, bf16-representable
  * MXFP4 runs with the RPBH rotation.
@@ -180,12 +182,12 @@ typedef struct rq_quant {
  *   b_div         epilogue divisor: the RPBH block, 1 otherwise
  *   a_bits, w_bits  as in rq_quant
  *   row_bytes     bytes per packed weight row (K/2 for 4-bit codes, K for
- *                 8-bit, K/4 for 2-bit)
+ *                 6- and 8-bit, K/4 for 2-bit)
  *   scale_offset  byte offset of the weight scales: fp32 [N] (INT: s_w;
  *                 LLOYDMAX: tau) or, MXFP4, the E8M0 codes uint8 [N][K/32]
  *   codes_offset  byte offset of the packed codes [N][row_bytes]
  *                 INT 4-bit: two's-complement nibbles, low nibble = even k;
- *                 INT 8-bit: int8; MXFP4: E2M1 nibbles (sign in bit 3), low
+ *                 INT 6- and 8-bit: int8; MXFP4: E2M1 nibbles (sign in bit 3), low
  *                 nibble = even k; LLOYDMAX 2-bit: four level indices per
  *                 byte, lowest k in the lowest bits
  *   total_bytes   size of the whole blob
@@ -201,8 +203,8 @@ typedef struct rq_quant {
  *                 32 c .. 32 c + 31 (zero rows past N)
  *   mma_stages    ceil((K - r) / 128)
  *   mma_ntiles    ceil(N / 32)
- *   i8_offset     INT with a_bits 8: the int8 weight codes (the canonical
- *                 codes when w_bits is 8, their widened copy when 4) in the
+ *   i8_offset     INT with a_bits 6 or 8: the int8 weight codes (the canonical
+ *                 codes when w_bits is 6 or 8, their widened copy when 4) in the
  *                 int8 matrix cores' fragment order
  *                 [mma_ntiles][K/32][64 lanes][16 bytes]: lane 32 h + i of
  *                 k-step c holds coordinates 32 c + 16 h .. + 15 of row
@@ -367,14 +369,14 @@ rq_status rq_codes_mma_bytes(const rq_rotation *rot, int64_t T, size_t *bytes);
 
 /*
  * Bytes of every activation buffer of T tokens under a quantizer:
- *   codes      the canonical codes: T * (K - r) * a_bits / 8 (LLOYDMAX,
- *              MXFP4: T * K / 2)
+ *   codes      the canonical codes: T * (K - r) / 2 (INT 4-bit), T * K (INT
+ *              6- and 8-bit, one code per byte), T * K / 2 (LLOYDMAX, MXFP4)
  *   scale      T * 4 (INT symmetric, LLOYDMAX), T * 8 (INT asymmetric: s
  *              then z), T * K / 32 (MXFP4: E8M0 codes)
  *   codes_mma  the GEMM-layout copy rq_rotate_quant can write: INT with
  *              a_bits 4 (RPBH, DENSE): rq_codes_mma_bytes(); MXFP4: the tiled codes
  *              and tiled scales; LLOYDMAX (RPBH): the bf16 levels,
- *              ceil(T / 32) * (K / 16) * 1024; INT with a_bits 8 (RPBH,
+ *              ceil(T / 32) * (K / 16) * 1024; INT with a_bits 6 or 8 (RPBH,
  *              TRDQ): the int8 fragments, ceil(T / 32) * 32 * K (see
  *              rq_rotate_quant); 0 where none exists
  * Any output pointer may be NULL.
@@ -396,12 +398,12 @@ rq_status rq_activation_bytes(const rq_rotation *rot, const rq_quant *q, int64_t
  *   TRDQ:  y[j] = fl32(x[j] * smooth[j]); z = y BlockDiag(R1) and then
  *          u = p BlockDiag(R2) with p[j] = z[perm[j]], every output one fp32
  *          fused multiply-add chain over its block's inputs ascending, from +0.
- *   INT symmetric (qmax = 7 for a_bits 4, 127 for 8), over the quantized
+ *   INT symmetric (qmax = 2^(a_bits - 1) - 1: 7, 31 or 127), over the quantized
  *          coordinates j in [r, K):
  *          amax = max |u[j]|; s = fl32(amax / qmax); inv = fl32(qmax / amax)
  *          q[j] = clamp(rne(fl32(u[j] * inv)), -qmax, qmax); amax == 0 -> 0, s = 0.
  *          DENSE also writes top[t][j] = bf16_rne(u[j]) for j < r.
- *   INT asymmetric (L = 15 or 255): lo = min u, hi = max u, d = fl32(hi - lo);
+ *   INT asymmetric (L = 2^a_bits - 1: 15, 63 or 255): lo = min u, hi = max u, d = fl32(hi - lo);
  *          s = fl32(d / L); inv = fl32(L / d);
  *          z = clamp(-rne(fl32(lo * inv)), 0, L) (an integer, +0 for zero);
  *          q[j] = clamp(rne(fl32(u[j] * inv)) + z, 0, L); d == 0 -> 0, s = z = 0.
@@ -422,10 +424,11 @@ rq_status rq_activation_bytes(const rq_rotation *rot, const rq_quant *q, int64_t
  *   T       tokens, 0 <= T < 2^31
  *   codes   device uint8 [T][...] of rq_activation_bytes(): INT 4-bit
  *           nibbles (two's complement when symmetric, unsigned when
- *           asymmetric; low nibble = even coordinate), INT 8-bit bytes
- *           (int8 / uint8), LLOYDMAX 4-bit indices or MXFP4 E2M1 codes as
- *           nibbles.  May be NULL for INT 4-bit (RPBH, DENSE), INT 8-bit
- *           (RPBH, TRDQ), MXFP4 and LLOYDMAX (RPBH) when codes_mma is given.
+ *           asymmetric; low nibble = even coordinate), INT 6- and 8-bit
+ *           bytes (int8 / uint8), LLOYDMAX 4-bit indices or MXFP4 E2M1 codes
+ *           as nibbles.  May be NULL for INT 4-bit (RPBH, DENSE), INT 6- and
+ *           8-bit (RPBH, TRDQ), MXFP4 and LLOYDMAX (RPBH) when codes_mma is
+ *           given.
  *   scale   device: fp32 [T] s (INT symmetric) or sigma (LLOYDMAX); INT
  *           asymmetric: fp32 [2][T], s[t] then the zero point z[t]; MXFP4:
  *           uint8 [T][K/32] E8M0 codes (the pointer is read as bytes).  May
@@ -438,7 +441,7 @@ rq_status rq_activation_bytes(const rq_rotation *rot, const rq_quant *q, int64_t
  *           [8 bf16]: coordinates 16 ks + 8 h .. 16 ks + 8 h + 7 of token t
  *           are lane t % 32 + 32 h of k-step ks of tile t / 32 (slots of
  *           tokens past T are left unwritten).
- *           INT 8-bit (RPBH, TRDQ): a device buffer of rq_activation_bytes()'s
+ *           INT 6- and 8-bit (RPBH, TRDQ): a device buffer of rq_activation_bytes()'s
  *           codes_mma receiving the code bytes in the int8 GEMM's fragment
  *           order [ceil(T/32)][K/32][64 lanes][16 bytes]: coordinates
  *           32 c + 16 h .. + 15 of token t are lane t % 32 + 32 h of k-step c
@@ -517,7 +520,7 @@ rq_status rq_rotate_quant_noalloc(const rq_rotation *rot, const rq_quant *q, con
  * activation codes become q + 8, weight codes q, both exact in E2M3, and the
  * per-channel sum of the weight codes (in the blob) removes the offset;
  * every partial sum is an integer below 2^24, so the fp32 accumulation is
- * exact.  8-bit activations run on the int8 matrix cores (int32
+ * exact.  6- and 8-bit activations run on the int8 matrix cores (int32
  * accumulation), MXFP4 on the scaled FP4 matrix cores with the E8M0 block
  * scales as the instruction's per-lane scales.
  * rq_w4a4_linear_engine() selects the matrix cores explicitly.
@@ -549,7 +552,7 @@ rq_status rq_w4a4_linear(const rq_weight_header *hdr, const void *blob, const ui
  *   engine  rq_engine.  RQ_ENGINE_INT8 takes INT4_SYM weights with 4-bit
  *           activations (any r) and their canonical codes (codes_mma must
  *           be NULL for 4-bit activations); the accumulators and outputs equal the FP6 engine's bit
- *           for bit.  8-bit activations run on the int8 engine only (AUTO or
+ *           for bit.  6- and 8-bit activations run on the int8 engine only (AUTO or
  *           INT8); Lloyd-Max and MXFP4 take RQ_ENGINE_AUTO only.
  * Errors: as rq_w4a4_linear; RQ_ERR_UNSUPPORTED for an engine that cannot
  *         run the blob's format or for codes_mma of 4-bit activations with

@@ -31,8 +31,11 @@ rq_status check_header(const rq_weight_header *hdr) {
     if (hdr->K < 32 || hdr->K > 16384 || hdr->K % 32 != 0 || hdr->N < 1 || hdr->N > (1 << 20) ||
         hdr->r < 0 || hdr->r >= hdr->K || hdr->r % 32 != 0 || hdr->b_div < 1)
         return fail(RQ_ERR_FORMAT, "weight header shape fields are inconsistent");
+    // 4-bit activations with 4-bit weights; 6- or 8-bit activations (one
+    // code per byte) with 4-, 6- or 8-bit weights
+    const bool wb_ok = hdr->w_bits == 4 || hdr->w_bits == 6 || hdr->w_bits == 8;
     if (intq && !((hdr->a_bits == 4 && hdr->w_bits == 4) ||
-                  (hdr->a_bits == 8 && (hdr->w_bits == 4 || hdr->w_bits == 8) && hdr->r == 0)))
+                  ((hdr->a_bits == 6 || hdr->a_bits == 8) && wb_ok && hdr->r == 0)))
         return fail(RQ_ERR_FORMAT, "weight header bit widths are inconsistent");
     int want_rb;
     if (f == RQ_Q_LLOYDMAX)
@@ -40,7 +43,7 @@ rq_status check_header(const rq_weight_header *hdr) {
     else if (f == RQ_Q_MXFP4)
         want_rb = hdr->K / 2;
     else
-        want_rb = hdr->K * hdr->w_bits / 8;
+        want_rb = hdr->w_bits == 4 ? hdr->K / 2 : hdr->K;
     if (hdr->row_bytes != want_rb) return fail(RQ_ERR_FORMAT, "weight header row_bytes mismatch");
     if (f == RQ_Q_LLOYDMAX && hdr->K % 64 != 0)
         return fail(RQ_ERR_SHAPE, "the codebook GEMM needs K % 64 == 0");
@@ -55,7 +58,7 @@ rq_status check_header(const rq_weight_header *hdr) {
             hdr->mma_offset + (int64_t)hdr->mma_ntiles * hdr->mma_stages * 3 * 1024 > hdr->total_bytes)
             return fail(RQ_ERR_FORMAT, "weight header FP6 section offsets are inconsistent");
     }
-    if (intq && hdr->a_bits == 8) {
+    if (intq && hdr->a_bits != 4) {
         if (hdr->wsum_offset <= 0 || hdr->wsum_offset % 16 != 0 || hdr->i8_offset <= 0 ||
             hdr->i8_offset % 16 != 0 ||
             hdr->i8_offset + (int64_t)(hdr->N + 31) / 32 * 32 * hdr->K > hdr->total_bytes)
@@ -85,13 +88,13 @@ rq_status validate_rotate_quant(const rq_rotation *rot, const rq_quant *q, const
     const bool dense = rot->kind == RQ_ROT_DENSE;
     const bool mx = q->kind == RQ_Q_MXFP4;
     const bool int4 = (q->kind == RQ_Q_INT4_SYM || q->kind == RQ_Q_INT4_ASYM) && q->a_bits == 4;
-    const bool int8 = (q->kind == RQ_Q_INT4_SYM || q->kind == RQ_Q_INT4_ASYM) && q->a_bits == 8;
+    const bool int8 = (q->kind == RQ_Q_INT4_SYM || q->kind == RQ_Q_INT4_ASYM) && q->a_bits != 4;
     const bool lm = q->kind == RQ_Q_LLOYDMAX;
     const bool trdq = rot->kind == RQ_ROT_TRDQ;
     const bool mma_ok = (rpbh && (int4 || int8 || mx || lm)) || (dense && int4) || (trdq && int8);
     if (codes_mma && !mma_ok)
         return fail(RQ_ERR_UNSUPPORTED,
-                    "codes_mma is written for 4-bit integer codes (RPBH, DENSE), 8-bit integer "
+                    "codes_mma is written for 4-bit integer codes (RPBH, DENSE), 6- and 8-bit integer "
                     "codes (RPBH, TRDQ), and MXFP4 or LLOYDMAX (RPBH) only");
     if (T == 0) return RQ_OK;
     if (!X || (!codes && !codes_mma) || (!scale && !(mx && codes_mma)))
@@ -135,7 +138,7 @@ rq_status rq_activation_bytes(const rq_rotation *rot, const rq_quant *q, int64_t
     const int K = rot->K, Kq = K - rot->r;
     const bool intq = q->kind == RQ_Q_INT4_SYM || q->kind == RQ_Q_INT4_ASYM;
     const bool mx = q->kind == RQ_Q_MXFP4;
-    if (codes) *codes = (size_t)T * (size_t)(intq ? Kq * q->a_bits / 8 : K / 2);
+    if (codes) *codes = (size_t)T * (size_t)(intq ? (q->a_bits == 4 ? Kq / 2 : Kq) : K / 2);
     if (scale)
         *scale = mx ? (size_t)T * (K / 32)
                     : (size_t)T * (q->kind == RQ_Q_INT4_ASYM ? 8 : 4);
@@ -143,7 +146,7 @@ rq_status rq_activation_bytes(const rq_rotation *rot, const rq_quant *q, int64_t
         *codes_mma = 0;
         if ((rot->kind == RQ_ROT_RPBH || rot->kind == RQ_ROT_DENSE) && intq && q->a_bits == 4)
             *codes_mma = (size_t)mma_codes_bytes(T, Kq);
-        else if ((rot->kind == RQ_ROT_RPBH || rot->kind == RQ_ROT_TRDQ) && intq && q->a_bits == 8)
+        else if ((rot->kind == RQ_ROT_RPBH || rot->kind == RQ_ROT_TRDQ) && intq && q->a_bits != 4)
             *codes_mma = (size_t)i8_mma_bytes(T, K);
         else if (rot->kind == RQ_ROT_RPBH && mx)
             *codes_mma = (size_t)mx_mma_bytes(T, K);
@@ -262,7 +265,7 @@ rq_status rq_w4a4_linear_engine(const rq_weight_header *hdr, const void *blob,
     const int f = hdr->format;
     const bool intq = f == RQ_Q_INT4_SYM || f == RQ_Q_INT4_ASYM;
     const bool asym = f == RQ_Q_INT4_ASYM;
-    const bool a8 = intq && hdr->a_bits == 8;
+    const bool a8 = intq && hdr->a_bits != 4;   // 6- or 8-bit codes, one per byte
     const bool mx = f == RQ_Q_MXFP4;
     if (y_dtype == RQ_I32 && !intq)
         return fail(RQ_ERR_UNSUPPORTED, "raw accumulators exist for integer weights only");
@@ -270,7 +273,7 @@ rq_status rq_w4a4_linear_engine(const rq_weight_header *hdr, const void *blob,
     if (engine != RQ_ENGINE_AUTO && !intq)
         return fail(RQ_ERR_UNSUPPORTED, "the Lloyd-Max and MXFP4 formats have one engine (RQ_ENGINE_AUTO)");
     if (a8 && engine == RQ_ENGINE_FP6)
-        return fail(RQ_ERR_UNSUPPORTED, "8-bit activations run on the int8 engine");
+        return fail(RQ_ERR_UNSUPPORTED, "6- and 8-bit activations run on the int8 engine");
     const bool int8 = a8 || engine == RQ_ENGINE_INT8;
     if (int8 && !a8 && asym)
         return fail(RQ_ERR_UNSUPPORTED, "the int8 engine takes INT4_SYM weights with 4-bit activations");

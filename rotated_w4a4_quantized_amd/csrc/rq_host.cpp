@@ -67,13 +67,13 @@ rq_status check_rotation(const rq_rotation *rot, bool need_tables) {
 rq_status check_quant(const rq_rotation *rot, const rq_quant *q) {
     if (!q) return fail(RQ_ERR_NULL, "quantizer descriptor is NULL");
     if (q->kind == RQ_Q_INT4_SYM || q->kind == RQ_Q_INT4_ASYM) {
-        if (q->a_bits != 4 && q->a_bits != 8)
-            return fail(RQ_ERR_UNSUPPORTED, "integer activations take a_bits 4 or 8");
-        if (q->w_bits != 4 && q->w_bits != 8)
-            return fail(RQ_ERR_UNSUPPORTED, "integer weights take w_bits 4 or 8");
+        if (q->a_bits != 4 && q->a_bits != 6 && q->a_bits != 8)
+            return fail(RQ_ERR_UNSUPPORTED, "integer activations take a_bits 4, 6 or 8");
+        if (q->w_bits != 4 && q->w_bits != 6 && q->w_bits != 8)
+            return fail(RQ_ERR_UNSUPPORTED, "integer weights take w_bits 4, 6 or 8");
         if (q->a_bits == 4 && q->w_bits != 4)
             return fail(RQ_ERR_UNSUPPORTED, "4-bit activations take w_bits 4");
-        if ((q->a_bits == 8 || q->kind == RQ_Q_INT4_ASYM) && rot->kind == RQ_ROT_DENSE)
+        if ((q->a_bits != 4 || q->kind == RQ_Q_INT4_ASYM) && rot->kind == RQ_ROT_DENSE)
             return fail(RQ_ERR_UNSUPPORTED,
                         "the dense rotation takes symmetric 4-bit activations (with top-r bf16)");
     } else if (q->kind == RQ_Q_MXFP4) {
@@ -218,7 +218,8 @@ static BlobLayout blob_layout(const rq_rotation *rot, const rq_quant *q, int32_t
     const int r = rot->kind == RQ_ROT_DENSE ? rot->r : 0;
     const bool mx = q->kind == RQ_Q_MXFP4, lm = q->kind == RQ_Q_LLOYDMAX;
     BlobLayout L;
-    L.row_bytes = lm ? (q->w_bits == 4 ? K / 2 : K / 4) : (mx ? K / 2 : K * q->w_bits / 8);
+    // integer codes: 4-bit two per byte, 6- and 8-bit one per byte
+    L.row_bytes = lm ? (q->w_bits == 4 ? K / 2 : K / 4) : (mx ? K / 2 : (q->w_bits == 4 ? K / 2 : K));
     L.scale_off = (int64_t)sizeof(rq_weight_header);
     L.codes_off = L.scale_off + round256(mx ? (int64_t)N * (K / 32) : (int64_t)N * 4);
     int64_t end = L.codes_off + round256((int64_t)N * L.row_bytes);
@@ -404,7 +405,7 @@ rq_status rq_pack_weights(const rq_rotation *rot, const rq_quant *q, const void 
                                                (e2m1_code(std::ldexp(v[k + 1], 127 - sc)) << 4));
                 }
             } else if (q->kind != RQ_Q_LLOYDMAX) {   // symmetric integer weights
-                const int qmax = q->w_bits == 8 ? 127 : 7;
+                const int qmax = (1 << (q->w_bits - 1)) - 1;   // 7, 31, 127
                 double amax = 0.0;
                 for (int k = 0; k < K; ++k) amax = std::max(amax, std::fabs(v[k]));
                 if (amax == 0.0) {
@@ -419,7 +420,7 @@ rq_status rq_pack_weights(const rq_rotation *rot, const rq_quant *q, const void 
                         t = std::min((double)qmax, std::max(-(double)qmax, t));
                         c[e] = (int)t;
                     }
-                    if (q->w_bits == 8) {
+                    if (q->w_bits != 4) {
                         row[k] = (uint8_t)(int8_t)c[0];
                         row[k + 1] = (uint8_t)(int8_t)c[1];
                     } else {
@@ -470,9 +471,9 @@ rq_status rq_pack_weights(const rq_rotation *rot, const rq_quant *q, const void 
         // the GEMMs' copies of the quantized coordinates [r, K): row sums, and
         // FP6 fragments (4-bit activations, see pack_mma_tile) or int8 codes
         const int r = hdr.r, Kq = K - r;
-        const bool w8 = q->w_bits == 8;
+        const bool wbytes = q->w_bits != 4;
         auto wcode = [&](int n, int k) -> int {
-            if (w8) return (int)(int8_t)codes[(size_t)n * rb + k];
+            if (wbytes) return (int)(int8_t)codes[(size_t)n * rb + k];
             const uint8_t byte = codes[(size_t)n * rb + k / 2];
             const int nib = (k & 1) ? (byte >> 4) : (byte & 15);
             return nib >= 8 ? nib - 16 : nib;

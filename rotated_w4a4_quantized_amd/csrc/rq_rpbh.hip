@@ -254,6 +254,8 @@ struct RpbhArgs {
     float th[15];         // codebook thresholds (Lloyd-Max)
     int th_sym;           // th[7] == 0 and th[i] == -th[14 - i] exactly
     uint32_t lev[16];     // Lloyd-Max: bf16 bits of the 16 levels (codes_mma)
+    float qbyte;          // byte codes: symmetric qmax (31 or 127) or asymmetric
+                          // top code (63 or 255) of 6- or 8-bit codes
 };
 
 template <bool BF16>
@@ -279,7 +281,7 @@ rpbh_quant_kernel(RpbhArgs a) {
     constexpr bool MX = QK == 3;
     constexpr bool B8 = QK == 4 || QK == 5;
     constexpr int CSH = B8 ? 0 : 1;   // code byte = coordinate >> CSH
-    constexpr float kLevels = QK == 5 ? 255.0f : 15.0f;   // asymmetric top code
+    const float kLevels = QK == 5 ? a.qbyte : 15.0f;   // asymmetric top code
     constexpr uint32_t kCanonFlip = QK == 0 ? 0x88888888u : 0u;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ unsigned red_max[2][kMaxTpw];
@@ -541,14 +543,15 @@ rpbh_quant_kernel(RpbhArgs a) {
             }
             sc = amax > 0.0f ? amax / 7.0f : 0.0f;
         } else if constexpr (QK == 4) {
-            // q = rne(fl32(u * inv)) in [-127, 127] (|u * inv| <= fl32(127 (1 + 2^-24))
-            // rounds to at most 127); adding 1.5 * 2^23 leaves q in the low
+            // q = rne(fl32(u * inv)) in [-qm, qm] (|u * inv| <= fl32(qm (1 + 2^-24))
+            // rounds to at most qm); adding 1.5 * 2^23 leaves q in the low
             // mantissa bits, whose low byte is q in two's complement
-            const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+            const float qm = a.qbyte;   // 127 (8-bit) or 31 (6-bit)
+            const float inv = amax > 0.0f ? qm / amax : 0.0f;
             const float sinv = lsign * inv;   // v = lsign u
 #pragma unroll
             for (int r = 0; r < kE; ++r) nib[r] = __float_as_uint(v[r] * sinv + 12582912.0f) & 0xFFu;
-            sc = amax > 0.0f ? amax / 127.0f : 0.0f;
+            sc = amax > 0.0f ? amax / qm : 0.0f;
         } else if constexpr (MX) {
             // this thread's 32 coordinates are one block: e = floor(log2 max|u|) - 2
             float m = 0.0f;
@@ -821,6 +824,7 @@ RpbhArgs make_args(const void *X, int64_t T, int K, const int8_t *sign, const in
     for (int i = 0; i < 15; ++i) a.th[i] = 0.0f;
     a.th_sym = 0;
     for (int i = 0; i < 16; ++i) a.lev[i] = 0u;
+    a.qbyte = 0.0f;
     return a;
 }
 
@@ -832,7 +836,9 @@ int launch_rpbh_int4(const void *X, int x_bf16, int64_t T, int K, int block, con
     RpbhArgs a = make_args(X, T, K, sign, perm, codes, codes_mma, scale);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int L = ilog2(block);
-    if (a_bits == 8) {
+    if (a_bits != 4) {
+        // 6- or 8-bit codes, one per byte
+        a.qbyte = asym ? (float)((1 << a_bits) - 1) : (float)((1 << (a_bits - 1)) - 1);
         if (asym) return (int)(x_bf16 ? dispatch<true, 5>(L, a, s) : dispatch<false, 5>(L, a, s));
         return (int)(x_bf16 ? dispatch<true, 4>(L, a, s) : dispatch<false, 4>(L, a, s));
     }

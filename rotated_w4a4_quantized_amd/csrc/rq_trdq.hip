@@ -58,9 +58,10 @@ struct TrdqArgs {
     const float *R1;       // [K/b][b][b]
     const int32_t *perm;   // [K]
     const float *R2;       // [K/b][b][b]
-    uint8_t *codes;        // [T][K a_bits / 8], or null
-    uint8_t *codes_mma;    // 8-bit codes in the int8 GEMM's fragment order, or null
+    uint8_t *codes;        // [T][K / 2] (4-bit) or [T][K] (6- and 8-bit), or null
+    uint8_t *codes_mma;    // byte codes in the int8 GEMM's fragment order, or null
     float *scale;          // [T] (asymmetric: s [T] then z [T])
+    float qbyte;           // byte codes: symmetric qmax 31 / 127 or asymmetric top code 63 / 255
 };
 
 // 8-bit code of (token t, coordinate k) in the int8 GEMM's fragment order
@@ -196,7 +197,8 @@ trdq_quant_kernel(TrdqArgs a) {
     }
     __syncthreads();
 
-    constexpr float kQ = ASYM ? (QB == 8 ? 255.0f : 15.0f) : (QB == 8 ? 127.0f : 7.0f);
+    // QB: code container (4: nibbles, 8: bytes holding 6- or 8-bit codes)
+    const float kQ = QB == 8 ? a.qbyte : (ASYM ? 15.0f : 7.0f);
 #pragma unroll
     for (int t = 0; t < TOK; ++t) {
         const int64_t tok = t0 + t;
@@ -262,7 +264,7 @@ hipError_t launch_tok(const TrdqArgs &a, int asym, int a_bits, hipStream_t s) {
         hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, a);
         return hipGetLastError();
     };
-    if (a_bits == 8)
+    if (a_bits != 4)   // 6- or 8-bit codes, one per byte
         return asym ? go(trdq_quant_kernel<TOK, NBMAX, BF16, 8, true>)
                     : go(trdq_quant_kernel<TOK, NBMAX, BF16, 8, false>);
     return asym ? go(trdq_quant_kernel<TOK, NBMAX, BF16, 4, true>)
@@ -499,11 +501,12 @@ template <int QB, bool ASYM>
 __global__ void __launch_bounds__(256)
 trdq_quant_tiled_kernel(const float *__restrict__ U, const unsigned *__restrict__ stat, int64_t T, int K,
                         uint8_t *__restrict__ codes, uint8_t *__restrict__ codes_mma,
-                        float *__restrict__ scale) {
+                        float *__restrict__ scale, float qbyte) {
     const int lane = threadIdx.x & 63;
     const int64_t tok = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (tok >= T) return;
-    constexpr float kQ = ASYM ? (QB == 8 ? 255.0f : 15.0f) : (QB == 8 ? 127.0f : 7.0f);
+    // QB: code container (4: nibbles, 8: bytes holding 6- or 8-bit codes)
+    const float kQ = QB == 8 ? qbyte : (ASYM ? 15.0f : 7.0f);
     float inv = 0.0f, sc = 0.0f, zp = 0.0f;
     bool zero_row;
     if constexpr (ASYM) {
@@ -569,7 +572,8 @@ hipError_t launch_tile_step(const TileArgs &a, hipStream_t s) {
 int launch_trdq(const void *X, int x_bf16, int64_t T, int K, int block, const float *smooth,
                 const float *R1, const int32_t *perm, const float *R2, uint8_t *codes,
                 uint8_t *codes_mma, float *scale, int asym, int a_bits, void *stream) {
-    TrdqArgs a{X, T, K, block, smooth, R1, perm, R2, codes, codes_mma, scale};
+    const float qbyte = asym ? (float)((1 << a_bits) - 1) : (float)((1 << (a_bits - 1)) - 1);
+    TrdqArgs a{X, T, K, block, smooth, R1, perm, R2, codes, codes_mma, scale, qbyte};
     hipStream_t s = static_cast<hipStream_t>(stream);
     // a thread holds ceil(K / 1024) blocks x TOK tokens x 4 columns
     if (K <= 4096)
@@ -605,12 +609,13 @@ int launch_trdq_tiled(const void *X, int x_bf16, int64_t T, int K, int block, co
     e = asym ? launch_tile_step<2, false, true>(a2, s) : launch_tile_step<2, false, false>(a2, s);
     if (e != hipSuccess) return (int)e;
     const dim3 grid((unsigned)((T + 3) / 4));
-    if (a_bits == 8) {
-        if (asym) hipLaunchKernelGGL((trdq_quant_tiled_kernel<8, true>), grid, dim3(256), 0, s, U, stat, T, K, codes, codes_mma, scale);
-        else hipLaunchKernelGGL((trdq_quant_tiled_kernel<8, false>), grid, dim3(256), 0, s, U, stat, T, K, codes, codes_mma, scale);
+    const float qb = asym ? (float)((1 << a_bits) - 1) : (float)((1 << (a_bits - 1)) - 1);
+    if (a_bits != 4) {   // 6- or 8-bit codes, one per byte
+        if (asym) hipLaunchKernelGGL((trdq_quant_tiled_kernel<8, true>), grid, dim3(256), 0, s, U, stat, T, K, codes, codes_mma, scale, qb);
+        else hipLaunchKernelGGL((trdq_quant_tiled_kernel<8, false>), grid, dim3(256), 0, s, U, stat, T, K, codes, codes_mma, scale, qb);
     } else {
-        if (asym) hipLaunchKernelGGL((trdq_quant_tiled_kernel<4, true>), grid, dim3(256), 0, s, U, stat, T, K, codes, codes_mma, scale);
-        else hipLaunchKernelGGL((trdq_quant_tiled_kernel<4, false>), grid, dim3(256), 0, s, U, stat, T, K, codes, codes_mma, scale);
+        if (asym) hipLaunchKernelGGL((trdq_quant_tiled_kernel<4, true>), grid, dim3(256), 0, s, U, stat, T, K, codes, codes_mma, scale, qb);
+        else hipLaunchKernelGGL((trdq_quant_tiled_kernel<4, false>), grid, dim3(256), 0, s, U, stat, T, K, codes, codes_mma, scale, qb);
     }
     return (int)hipGetLastError();
 }

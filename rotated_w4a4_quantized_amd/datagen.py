@@ -41,7 +41,7 @@ class Workload:
     rot: str            # "rpbh" | "dense" | "trdq"
     block: int          # RPBH / TR-DQ block (0 for dense)
     r: int              # top-r kept in bf16 (dense only)
-    quant: str          # "int4" | "int4_asym" | "lloydmax" | "mxfp4"; int4* with a_bits 8 = INT8 activations
+    quant: str          # "int4" | "int4_asym" | "lloydmax" | "mxfp4"; int4* with a_bits 6 or 8 = 6- or 8-bit activations
     xdtype: str         # "f32" | "bf16"
     ydtype: str         # "f32" | "bf16"
     x_kind: str         # distribution recipe of X
@@ -58,7 +58,8 @@ class Workload:
 
     @property
     def code_bytes(self) -> int:
-        """Bytes of activation codes per token (canonical layout)."""
+        """Bytes of activation codes per token at the method's minimal
+        encoding (the canonical layout stores 6-bit codes one per byte)."""
         return self.Kq * self.a_bits // 8
 
     def ops(self) -> int:
@@ -109,6 +110,12 @@ WORKLOADS = {
     # permutation, block rotation 128) with its W4A8 setting
     "flux_up_trdq": Workload("flux_up_trdq", 2, 9216, 3072, 12288, "trdq", 128, 0, "int4", "bf16",
                              "bf16", "gauss_outlier16x30", a_bits=8, w_bits=4),
+    # TR-DQ's W6A6 setting: 6-bit codes (one per byte) on the int8 matrix
+    # cores, with TR-DQ's rotation and with RPBH
+    "flux_up_trdq_w6a6": Workload("flux_up_trdq_w6a6", 2, 9216, 3072, 12288, "trdq", 128, 0, "int4",
+                                  "bf16", "bf16", "gauss_outlier16x30", a_bits=6, w_bits=6),
+    "flux_up_w6a6": Workload("flux_up_w6a6", 2, 9216, 3072, 12288, "rpbh", 256, 0, "int4", "bf16",
+                             "bf16", "gauss_outlier16x30", a_bits=6, w_bits=6),
 }
 
 

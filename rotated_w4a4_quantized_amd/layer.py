@@ -41,11 +41,11 @@ def quant_for(w) -> rq.Quant:
 
 def mma_capable(w) -> bool:
     """Whether rq_rotate_quant can hand this workload's GEMM its codes in the
-    matrix-core layout: 4-bit integer codes under RPBH or DENSE, 8-bit integer
-    codes under RPBH or TR-DQ, and MXFP4 and Lloyd-Max codes (as their bf16
-    levels) under RPBH."""
+    matrix-core layout: 4-bit integer codes under RPBH or DENSE, 6- and 8-bit
+    integer codes under RPBH or TR-DQ, and MXFP4 and Lloyd-Max codes (as their
+    bf16 levels) under RPBH."""
     intq = w.quant in ("int4", "int4_asym")
-    int4, int8 = intq and w.a_bits == 4, intq and w.a_bits == 8
+    int4, int8 = intq and w.a_bits == 4, intq and w.a_bits in (6, 8)
     return ((w.rot in ("rpbh", "dense") and int4) or (w.rot in ("rpbh", "trdq") and int8) or
             (w.rot == "rpbh" and w.quant in ("mxfp4", "lloydmax")))
 

@@ -236,8 +236,9 @@ class Quant:
 
     @staticmethod
     def integer(a_bits, w_bits, asym=False):
-        """Integer activations of a_bits (4 or 8, zero point if asym) and
-        symmetric weights of w_bits (W4A4, W4A8, W8A8)."""
+        """Integer activations of a_bits (4, 6 or 8, zero point if asym) and
+        symmetric weights of w_bits (W4A4, W4A8, W8A8, W6A6); 6- and 8-bit
+        codes are stored one per byte."""
         return Quant(RQ_Q_INT4_ASYM if asym else RQ_Q_INT4_SYM, a_bits, w_bits)
 
     @staticmethod

@@ -435,10 +435,14 @@ def test_pack_mxfp4_matches_oracle(name, shape):
 @pytest.mark.parametrize("name,shape", [("flux_up_w4a8", dict(K=512, N=40)),
                                         ("flux_up_w8a8", dict(K=512, N=40)),
                                         ("flux_up_trdq", dict(K=512, N=40)),
-                                        ("flux_up_trdq", dict(K=256, N=24, w_bits=8))])
+                                        ("flux_up_trdq", dict(K=256, N=24, w_bits=8)),
+                                        ("flux_up_w6a6", dict(K=512, N=40)),
+                                        ("flux_up_trdq_w6a6", dict(K=256, N=24)),
+                                        ("flux_up_w6a6", dict(K=256, N=40, w_bits=4))])
 def test_pack_int8_paths_match_oracle(name, shape):
-    """8-bit weights and the int8 copy of 4-bit weights that the int8 GEMM
-    reads; the TR-DQ fold (smoothing, R1, zigzag, R2 in fp64)."""
+    """8- and 6-bit weights (one code per byte) and the int8 copy of 4-bit
+    weights that the int8 GEMM reads; the TR-DQ fold (smoothing, R1, zigzag,
+    R2 in fp64)."""
     w = datagen.WORKLOADS[name].with_shape(T=4, **shape)
     inp = datagen.make_inputs(w)
     from rotated_w4a4_quantized_amd.layer import quant_for, rotation_for
@@ -461,10 +465,13 @@ def test_new_format_validation_errors():
     assert _rq_call(rq.c_rotation(rq.RQ_ROT_RPBH, 160, 32, 0, 1 << 20, 1 << 21, None), mx) == -2
     dense = rq.c_rotation(rq.RQ_ROT_DENSE, K, 0, 0, None, None, 1 << 22)
     assert _rq_call(dense, mx) == -6
-    # 8-bit activations: not with the dense path; a_bits / w_bits values
+    # 6- and 8-bit activations: not with the dense path; a_bits / w_bits values
     assert _rq_call(dense, rq.Quant.integer(8, 4).c()) == -6
-    assert _rq_call(_rpbh(), rq.c_quant(0, 6, 4, 0)) == -6
+    assert _rq_call(dense, rq.Quant.integer(6, 6).c()) == -6
+    assert _rq_call(_rpbh(), rq.c_quant(0, 5, 4, 0)) == -6
+    assert _rq_call(_rpbh(), rq.c_quant(0, 6, 7, 0)) == -6
     assert _rq_call(_rpbh(), rq.c_quant(0, 4, 8, 0)) == -6
+    assert _rq_call(_rpbh(), rq.c_quant(0, 4, 6, 0)) == -6
     # TR-DQ: block range, tables
     td = rq.c_rotation(rq.RQ_ROT_TRDQ, K, 8, 0, None, 1 << 21, 1 << 22, 1 << 23, 1 << 24)
     assert _rq_call(td, rq.Quant.integer(8, 4).c()) == -2
@@ -477,6 +484,8 @@ def test_new_format_validation_errors():
     assert rq.activation_bytes(rot, rq.Quant.mxfp4(), 40) == (40 * K // 2, 40 * K // 32,
                                                              2 * (K // 32) * 512 + (K // 128) * 2 * 128)
     assert rq.activation_bytes(rot, rq.Quant.integer(8, 4, asym=True), 40) == (40 * K, 80 * 4, 64 * K)
+    # 6-bit codes one per byte
+    assert rq.activation_bytes(rot, rq.Quant.integer(6, 6), 40) == (40 * K, 40 * 4, 64 * K)
     # the MXFP4 GEMM reads the tiled codes: canonical codes alone are refused
     w = datagen.WORKLOADS["flux_up_mxfp4"].with_shape(T=4, K=K, N=40, block=64)
     inp = datagen.make_inputs(w)

@@ -94,7 +94,7 @@ def check_act(w, L, act, rows=None):
             ref = (ref & 15) - 8
         bad = np.nonzero(np.any(dec != ref, axis=1))[0]
         assert bad.size == 0, f"codes_mma differs in {bad.size} tokens, first {bad[:5]}"
-    if w.quant in ("int4", "int4_asym") and w.a_bits == 8 and L.codes_mma is not None:
+    if w.quant in ("int4", "int4_asym") and w.a_bits in (6, 8) and L.codes_mma is not None:
         # the same bytes in the int8 GEMM's fragment order
         dec = H.decode_i8_mma(L.codes_mma.cpu().numpy(), w.T, w.K)
         if rows is not None:
@@ -171,6 +171,12 @@ SMALL = [
     ("video_w4", dict(T=45, K=1024, N=64, block=512)),
     ("flux_up_w8a8", dict(T=70, K=2048, N=96, block=1024)),
     ("flux_up_w4a8", dict(T=33, K=1024, N=40, block=512)),
+    # TR-DQ's W6A6 setting: 6-bit codes one per byte, int8 matrix cores
+    ("flux_up_w6a6", dict(T=257, K=3072, N=384)),
+    ("flux_up_w6a6", dict(T=33, K=96, N=40, block=2)),
+    ("flux_up_w6a6", dict(T=70, K=2048, N=96, block=1024)),
+    ("flux_up_trdq_w6a6", dict(T=70, K=1024, N=136)),
+    ("flux_up_trdq_w6a6", dict(T=9, K=16384, N=40, block=64)),
 ]
 
 
@@ -179,6 +185,21 @@ SMALL = [
 def test_small_full_parity(name, shape):
     w = datagen.WORKLOADS[name].with_shape(**shape)
     say(f"[parity small] {w}")
+    small_parity(w, datagen.make_inputs(w))
+
+
+# Asymmetric byte codes under RPBH: 8-bit (255 levels) and 6-bit (63 levels,
+# TR-DQ's W6A6), against the oracle like the small cases.
+BYTE_ASYM = [(8, dict(T=70, K=1024, N=64)), (6, dict(T=70, K=1024, N=64)),
+             (6, dict(T=33, K=2048, N=40, block=1024))]
+
+
+@pytest.mark.parametrize("bits,shape", BYTE_ASYM,
+                         ids=[f"a{b}-{'-'.join(f'{k}{v}' for k, v in s.items())}" for b, s in BYTE_ASYM])
+def test_asym_byte_codes_parity(bits, shape):
+    w = dataclasses.replace(datagen.WORKLOADS["flux_up_w6a6"].with_shape(a_bits=bits, w_bits=bits, **shape),
+                            quant="int4_asym")
+    say(f"[parity asym bytes] {w}")
     small_parity(w, datagen.make_inputs(w))
 
 
@@ -228,7 +249,8 @@ def small_parity(w, inp):
 
 
 FULL = ["tiny", "flux_up", "flux_down", "video", "pixart", "flux_up_asym", "flux_down_asym", "video_w4",
-        "flux_up_mxfp4", "flux_down_mxfp4", "flux_up_w4a8", "flux_up_w8a8", "flux_up_trdq"]
+        "flux_up_mxfp4", "flux_down_mxfp4", "flux_up_w4a8", "flux_up_w8a8", "flux_up_trdq",
+        "flux_up_w6a6", "flux_up_trdq_w6a6"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -615,11 +637,13 @@ TRDQ_FORMS = [
     ("flux_up_trdq", dict(T=70, K=2048, N=40, block=32), "int4_asym"),
     ("flux_up_trdq", dict(T=257, K=1024, N=40, block=64, a_bits=4), "int4_asym"),
     ("flux_up_trdq", dict(T=9, K=16384, N=40, block=256), "int4"),
+    ("flux_up_trdq_w6a6", dict(T=129, K=512, N=40, block=16), "int4"),
+    ("flux_up_trdq_w6a6", dict(T=70, K=2048, N=40, block=32), "int4_asym"),
 ]
 
 
 @pytest.mark.parametrize("name,shape,quant", TRDQ_FORMS,
-                         ids=[f"{q}-{'-'.join(f'{k}{v}' for k, v in s.items())}" for _, s, q in TRDQ_FORMS])
+                         ids=[f"{n}-{q}-{'-'.join(f'{k}{v}' for k, v in s.items())}" for n, s, q in TRDQ_FORMS])
 def test_trdq_tiled_matches_one_pass(name, shape, quant):
     w = dataclasses.replace(datagen.WORKLOADS[name].with_shape(**shape), quant=quant)
     say(f"[trdq forms] {w}")
