@@ -124,9 +124,11 @@ __device__ inline void reg_stages(float (&v)[kE]) {
 // butterfly's result negated (the product by -1 is exact and the sum is
 // rounded once).  The negations are tracked per lane (see lane_sign): a
 // partner pair always carries the same accumulated sign, so every stage takes
-// the same form.  Hazard: two wait states between a VALU write of a register
-// and a DPP read of it (s_nop 1); the register operands are consumed in the
-// order they were last written.
+// the same form.  Hazard: a DPP read needs two wait states after a VALU write
+// of its register.  s_nop 1 gives the block's first instruction two, and
+// instruction k of the block reads at least k + 2 wait states after anything
+// written before the block; inside the block every instruction reads a
+// register that no earlier instruction of the block wrote.
 #define RQ_FMAC_DPP(n, ctrl) "v_fmac_f32_dpp %" #n ", %" #n ", %32 " ctrl " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
 #define RQ_FMAC_DPP8(a, b, c, d, e, f, g, h, ctrl)                                                     \
     RQ_FMAC_DPP(a, ctrl) RQ_FMAC_DPP(b, ctrl) RQ_FMAC_DPP(c, ctrl) RQ_FMAC_DPP(d, ctrl) RQ_FMAC_DPP(e, ctrl) \
