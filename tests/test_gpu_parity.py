@@ -177,6 +177,8 @@ SMALL = [
     ("flux_up_w6a6", dict(T=70, K=2048, N=96, block=1024)),
     ("flux_up_trdq_w6a6", dict(T=70, K=1024, N=136)),
     ("flux_up_trdq_w6a6", dict(T=9, K=16384, N=40, block=64)),
+    ("flux_up_w6a6", dict(T=1, K=64, N=7, block=64)),
+    ("flux_up_w6a6", dict(T=5, K=16384, N=40, block=512)),
 ]
 
 
