@@ -16,9 +16,12 @@
 //   staging  the row is read from HBM one iteration ahead (coalesced 16-byte
 //            loads into registers), the sign of the coordinate each source
 //            element will land on is applied with one XOR per 32-bit word,
-//            and the row is written to LDS in its natural order;
-//   gather   each thread reads its 32 permuted inputs from LDS: 32
-//            consecutive coordinates of one block (see lane_hbits);
+//            and every element is written to LDS at its destination
+//            coordinate's slot (the permutation as a scatter of 2- or 4-byte
+//            stores, which the wave does not wait on);
+//   gather   each thread reads its 32 consecutive coordinates of one block
+//            (see lane_hbits) as 16-byte pieces, laid out so that adjacent
+//            lanes read adjacent pieces;
 //   stages   index bits 0..4 of the block in registers, bits 5 .. L - 1
 //            across the block's adjacent lanes, one fused multiply-add per
 //            value with the partner lane's register as a DPP operand (no LDS
@@ -36,8 +39,8 @@
 //            contiguous bytes -- come from four adjacent lanes: whole-request
 //            stores instead of sixteen-byte writes to scattered lines.
 // Two workgroup barriers per iteration of `tpw` tokens (three for the
-// codebook).  A per-workgroup prologue reads perm and sign and builds the
-// source-side sign masks in LDS.
+// codebook).  A per-workgroup prologue reads perm and sign and builds, in
+// LDS, each source element's destination slot and sign.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -338,65 +341,89 @@ rpbh_quant_kernel(RpbhArgs a) {
         for (int i = tid; i < 256; i += blockDim.x) lev_pair[i] = a.lev[i & 15] | (a.lev[i >> 4] << 16);
     }
 
-    // ---- prologue: gather offsets, source-side sign masks -----------------
+    // ---- prologue: scatter offsets, source-side sign masks ----------------
     // Thread tt owns destination coordinates j = 32 qc + r: it reads perm[j]
-    // and sign[j] contiguously, and writes the sign bit that source element
-    // perm[j] must carry into a table in the first token's staging row (one
-    // element per staging element, so the 16 bytes of the table that cover a
-    // staged 16-byte chunk are that chunk's XOR mask).  Only the first
-    // token's threads write it; every thread then reads its chunks' masks.
-    int gofs[kE];
+    // and sign[j] contiguously.  A table in the first token's staging row
+    // holds one entry per source element, so that the entries covering a
+    // staged 16-byte chunk are the 16 bytes at the chunk's own position: for
+    // source element perm[j], the LDS offset of coordinate j in the gather
+    // layout, and in the element's own sign bit (bf16 bit 15, fp32 bit 31)
+    // the sign that it must carry.  An offset is below K * XB (K <= 16384):
+    // bf16 offsets are even and below 32 KB, so 15 bits hold them halved;
+    // fp32 offsets take 16 bits.  Only the first token's threads write the
+    // table; every thread then reads its staged chunks' entries.
+    //
+    // Gather layout: the 16-byte piece c of chunk qc (coordinates 32 qc +
+    // E c .. + E - 1, E coordinates per piece) sits at piece slot c nch + qc,
+    // so piece c of all chunks is one contiguous array and the gather's
+    // 16-byte reads of adjacent lanes are adjacent.
+    constexpr int EPC = S::ELEMS_PER_CHUNK;
+    const int nch = a.tpt;   // 32-coordinate chunks per token
+    int dofs[kE];            // LDS offset of each staged element's destination
+    uint32_t smask[S::WORDS];
     {
-        int pj[kE];
-        int8_t sj[kE];
-#pragma unroll
-        for (int r = 0; r < kE; r += 4) {
-            const int4 p4 = *reinterpret_cast<const int4 *>(a.perm + kE * qc + r);
-            pj[r] = p4.x;
-            pj[r + 1] = p4.y;
-            pj[r + 2] = p4.z;
-            pj[r + 3] = p4.w;
-        }
-#pragma unroll
-        for (int r = 0; r < kE; r += 16) {
-            const int4 s4 = *reinterpret_cast<const int4 *>(a.sign + kE * qc + r);
-            const int w[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-            for (int e = 0; e < 16; ++e) sj[r + e] = (int8_t)(w[e >> 2] >> (8 * (e & 3)));
-        }
-#pragma unroll
-        for (int r = 0; r < kE; ++r) gofs[r] = pj[r] * S::XB;
         if (tl == 0) {
 #pragma unroll
-            for (int r = 0; r < kE; ++r) {
-                if constexpr (BF16)
-                    *reinterpret_cast<uint16_t *>(smem + 2 * pj[r]) = sj[r] < 0 ? 0x8000u : 0u;
-                else
-                    *reinterpret_cast<uint32_t *>(smem + 4 * pj[r]) = sj[r] < 0 ? 0x80000000u : 0u;
+            for (int r = 0; r < kE; r += 16) {
+                int pj[16];
+#pragma unroll
+                for (int e = 0; e < 16; e += 4) {
+                    const int4 p4 = *reinterpret_cast<const int4 *>(a.perm + kE * qc + r + e);
+                    pj[e] = p4.x;
+                    pj[e + 1] = p4.y;
+                    pj[e + 2] = p4.z;
+                    pj[e + 3] = p4.w;
+                }
+                const int4 s4 = *reinterpret_cast<const int4 *>(a.sign + kE * qc + r);
+                const int w[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const bool neg = (int8_t)(w[e >> 2] >> (8 * (e & 3))) < 0;
+                    const int rr = r + e;
+                    const uint32_t off = 16u * (uint32_t)((rr / EPC) * nch + qc) + S::XB * (rr % EPC);
+                    if constexpr (BF16)
+                        *reinterpret_cast<uint16_t *>(smem + 2 * pj[e]) = (uint16_t)((off >> 1) | (neg ? 0x8000u : 0u));
+                    else
+                        *reinterpret_cast<uint32_t *>(smem + 4 * pj[e]) = off | (neg ? 0x80000000u : 0u);
+                }
             }
         }
-    }
-    __syncthreads();
-    uint32_t smask[S::WORDS];
+        __syncthreads();
 #pragma unroll
-    for (int q = 0; q < S::CHUNKS; ++q) {
-        const uint4 m = *reinterpret_cast<const uint4 *>(smem + (size_t)16 * (tt + q * a.tpt));
-        smask[4 * q] = m.x;
-        smask[4 * q + 1] = m.y;
-        smask[4 * q + 2] = m.z;
-        smask[4 * q + 3] = m.w;
+        for (int q = 0; q < S::CHUNKS; ++q) {
+            const uint4 m = *reinterpret_cast<const uint4 *>(smem + (size_t)16 * (tt + q * a.tpt));
+            const uint32_t w[4] = {m.x, m.y, m.z, m.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if constexpr (BF16) {
+                    smask[4 * q + k] = w[k] & 0x80008000u;
+                    dofs[8 * q + 2 * k] = (int)((w[k] & 0x7FFFu) << 1);
+                    dofs[8 * q + 2 * k + 1] = (int)((w[k] >> 15) & 0xFFFEu);
+                } else {
+                    smask[4 * q + k] = w[k] & 0x80000000u;
+                    dofs[4 * q + k] = (int)(w[k] & 0xFFFFu);
+                }
+            }
+        }
+        __syncthreads();
     }
-    __syncthreads();
 
+    // the staged row: each element, its destination's sign applied (one XOR
+    // per 32-bit word), written to its destination's slot of the gather layout
     auto stage = [&]() {
 #pragma unroll
         for (int q = 0; q < S::CHUNKS; ++q) {
-            uint4 w = pre[q];
-            w.x ^= smask[4 * q];
-            w.y ^= smask[4 * q + 1];
-            w.z ^= smask[4 * q + 2];
-            w.w ^= smask[4 * q + 3];
-            *reinterpret_cast<uint4 *>(xs + (size_t)16 * (tt + q * a.tpt)) = w;
+            const uint32_t w[4] = {pre[q].x ^ smask[4 * q], pre[q].y ^ smask[4 * q + 1],
+                                   pre[q].z ^ smask[4 * q + 2], pre[q].w ^ smask[4 * q + 3]};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if constexpr (BF16) {
+                    *reinterpret_cast<uint16_t *>(xs + dofs[8 * q + 2 * k]) = (uint16_t)w[k];
+                    *reinterpret_cast<uint16_t *>(xs + dofs[8 * q + 2 * k + 1]) = (uint16_t)(w[k] >> 16);
+                } else {
+                    *reinterpret_cast<uint32_t *>(xs + dofs[4 * q + k]) = w[k];
+                }
+            }
         }
     };
     if (base >= 0) {
@@ -452,13 +479,21 @@ rpbh_quant_kernel(RpbhArgs a) {
             if constexpr (QK == 1) red_sum[it & 1][tl] = 0ull;
             if constexpr (ASYM) red_min[it & 1][tl] = 0xFFFFFFFFu;
         }
+        // gather: the thread's 32 coordinates, in 16-byte pieces
         float v[kE];
 #pragma unroll
-        for (int r = 0; r < kE; ++r) {
-            if constexpr (BF16)
-                v[r] = __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t *>(xs + gofs[r])) << 16);
-            else
-                v[r] = *reinterpret_cast<const float *>(xs + gofs[r]);
+        for (int c = 0; c < kE / EPC; ++c) {
+            const uint4 m = *reinterpret_cast<const uint4 *>(xs + (size_t)16 * (c * nch + qc));
+            const uint32_t w[4] = {m.x, m.y, m.z, m.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if constexpr (BF16) {
+                    v[8 * c + 2 * k] = __uint_as_float(w[k] << 16);
+                    v[8 * c + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+                } else {
+                    v[4 * c + k] = __uint_as_float(w[k]);
+                }
+            }
         }
         reg_stages<L>(v);
         lds_barrier();  // B1: every gather of this token is done
