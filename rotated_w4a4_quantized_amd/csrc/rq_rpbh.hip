@@ -38,8 +38,9 @@
 //            them so that the four tokens' 16-byte slots of one piece -- 64
 //            contiguous bytes -- come from four adjacent lanes: whole-request
 //            stores instead of sixteen-byte writes to scattered lines.
-// Two workgroup barriers per iteration of `tpw` tokens (three for the
-// codebook).  A per-workgroup prologue reads perm and sign and builds, in
+// One workgroup barrier per iteration of `tpw` tokens (two for the
+// codebook): each token has two staging rows, used by alternate
+// iterations.  A per-workgroup prologue reads perm and sign and builds, in
 // LDS, each source element's destination slot and sign.
 
 #include <hip/hip_runtime.h>
@@ -289,19 +290,25 @@ rpbh_quant_kernel(RpbhArgs a) {
     const float kLevels = QK == 5 ? a.qbyte : 15.0f;   // asymmetric top code
     constexpr uint32_t kCanonFlip = QK == 0 ? 0x88888888u : 0u;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    __shared__ unsigned red_max[2][kMaxTpw];
-    __shared__ unsigned red_min[2][kMaxTpw];   // asymmetric INT4 (keys)
-    __shared__ unsigned long long red_sum[2][kMaxTpw];
+    // per-token statistics, three slots in rotation: iteration it reduces into
+    // slot it % 3 and clears slot (it + 1) % 3, last read two barriers earlier
+    __shared__ unsigned red_max[3][kMaxTpw];
+    __shared__ unsigned red_min[3][kMaxTpw];   // asymmetric INT4 (keys)
+    __shared__ unsigned long long red_sum[3][kMaxTpw];
     // Lloyd-Max with codes_mma: packed byte of two indices -> their two bf16 levels
     __shared__ uint32_t lev_pair[QK == 1 ? 256 : 1];
     const int K = a.K;
     const int tid = threadIdx.x;
     const int tl = tid / a.tpt;
     const int tt = tid - tl * a.tpt;
-    uint8_t *xs = smem + (size_t)tl * K * S::XB;
+    // two staging rows per token, used by alternate iterations: the next
+    // token is staged while this one is gathered, without a barrier between
+    uint8_t *const xs0 = smem + (size_t)tl * K * S::XB;
+    uint8_t *const xs1 = xs0 + (size_t)a.tpw * K * S::XB;
     const int cb = ((K >> CSH) + 15) & ~15;
-    // code staging (MMA layout, grouped): one slot per token of the group
-    uint8_t *const cs0 = smem + (size_t)a.tpw * K * S::XB;
+    // code staging (MMA layout, grouped): one slot per token of the group,
+    // two sets used by alternate groups
+    uint8_t *const cs0 = smem + (size_t)2 * a.tpw * K * S::XB;
     // the 32-coordinate chunk this thread holds, its lane's high index bits,
     // the lane stages' coefficients and the lane's final sign
     const int qc = chunk_of<L>(tt);
@@ -410,7 +417,7 @@ rpbh_quant_kernel(RpbhArgs a) {
 
     // the staged row: each element, its destination's sign applied (one XOR
     // per 32-bit word), written to its destination's slot of the gather layout
-    auto stage = [&]() {
+    auto stage = [&](uint8_t *xs) {
 #pragma unroll
         for (int q = 0; q < S::CHUNKS; ++q) {
             const uint32_t w[4] = {pre[q].x ^ smask[4 * q], pre[q].y ^ smask[4 * q + 1],
@@ -427,17 +434,22 @@ rpbh_quant_kernel(RpbhArgs a) {
         }
     };
     if (base >= 0) {
-        stage();
+        stage(xs0);
         const int64_t b1 = first_tok(1);
         if (b1 >= 0) fetch(b1);
     }
+    if (tt == 0) {
+        red_max[0][tl] = 0u;
+        if constexpr (QK == 1) red_sum[0][tl] = 0ull;
+        if constexpr (ASYM) red_min[0][tl] = 0xFFFFFFFFu;
+    }
     __syncthreads();
 
-    // MMA-layout codes of group g (complete in the slots, LDS writes ordered
-    // by a barrier): item i is (stage s, half h) = (i >> gsz_log2) and token
-    // j = i % group size, so four adjacent lanes write one 64-byte run.
-    // A group (at most 16 tokens, aligned) lies inside one 32-token tile.
-    auto flush = [&](int64_t g) {
+    // MMA-layout codes of group g (complete in slot set `set`, LDS writes
+    // ordered by a barrier): item i is (stage s, half h) = (i >> gsz_log2)
+    // and token j = i % group size, so four adjacent lanes write one 64-byte
+    // run.  A group (at most 16 tokens, aligned) lies inside one 32-token tile.
+    auto flush = [&](int64_t g, int set) {
         const int items = a.mma_stages * 2 << a.gsz_log2;
         const int nth = a.tpw * a.tpt;
         const int nch = K / kE;
@@ -450,7 +462,7 @@ rpbh_quant_kernel(RpbhArgs a) {
             const int j = i & (gsz - 1);
             const int sh = i >> a.gsz_log2;
             if (j >= nvalid) continue;
-            const uint8_t *slot = cs0 + (size_t)j * cb;
+            const uint8_t *slot = cs0 + (size_t)((set << a.gsz_log2) + j) * cb;
             // chunks c0 (k-step 0) and c1 (k-step 1); those past the last
             // coordinate are not written
             const int c0 = 2 * (sh & ~1) + (sh & 1), c1 = c0 + 2;
@@ -469,21 +481,29 @@ rpbh_quant_kernel(RpbhArgs a) {
     // the same runs cut to one row of 16 lanes (max / min reductions)
     const int rg = grp < 16 ? grp : 16;
 
-    int it = 0;
+    // Per iteration one barrier (B, two for the codebook).  Iteration it
+    // gathers row it % 2, stages the next token into the other row (gathered
+    // at it + 1, after B; restaged at it + 2, after this iteration's B, so
+    // after every gather of this one), reduces into statistic slot it % 3,
+    // and after B quantizes and writes the codes.
+    int it = 0, rs = 0;   // rs = it % 3
     for (; base >= 0; ++it) {
         const int64_t tok = base + tl;
         const bool valid = tok < a.T;
-        uint8_t *const cs = cs0 + (size_t)(((it & ipg_mask) * a.tpw) + tl) * cb;
+        const int rn = rs == 2 ? 0 : rs + 1;
+        uint8_t *const xg = (it & 1) ? xs1 : xs0;
+        uint8_t *const cs =
+            cs0 + (size_t)((((it >> a.ipg_log2) & 1) << a.gsz_log2) + (it & ipg_mask) * a.tpw + tl) * cb;
         if (tt == 0) {
-            red_max[it & 1][tl] = 0u;
-            if constexpr (QK == 1) red_sum[it & 1][tl] = 0ull;
-            if constexpr (ASYM) red_min[it & 1][tl] = 0xFFFFFFFFu;
+            red_max[rn][tl] = 0u;
+            if constexpr (QK == 1) red_sum[rn][tl] = 0ull;
+            if constexpr (ASYM) red_min[rn][tl] = 0xFFFFFFFFu;
         }
         // gather: the thread's 32 coordinates, in 16-byte pieces
         float v[kE];
 #pragma unroll
         for (int c = 0; c < kE / EPC; ++c) {
-            const uint4 m = *reinterpret_cast<const uint4 *>(xs + (size_t)16 * (c * nch + qc));
+            const uint4 m = *reinterpret_cast<const uint4 *>(xg + (size_t)16 * (c * nch + qc));
             const uint32_t w[4] = {m.x, m.y, m.z, m.w};
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -496,16 +516,12 @@ rpbh_quant_kernel(RpbhArgs a) {
             }
         }
         reg_stages<L>(v);
-        lds_barrier();  // B1: every gather of this token is done
         const int64_t next = first_tok(it + 1);
         if (next >= 0) {
-            stage();                                        // next token -> LDS
+            stage((it & 1) ? xs0 : xs1);                    // next token -> LDS
             const int64_t b2 = first_tok(it + 2);
             if (b2 >= 0) fetch(b2);
         }
-        // the previous group is complete: its packs are ordered by B1
-        if (grouped && it > 0 && (it & ipg_mask) == 0)
-            flush(vb + (int64_t)((it - 1) >> a.ipg_log2) * gridDim.x);
         // v = lsign * u from here on (coordinates 32 qc .. 32 qc + 31)
         lane_stages<L>(v, coef);
         if constexpr (ASYM) {
@@ -523,8 +539,8 @@ rpbh_quant_kernel(RpbhArgs a) {
             const unsigned klo = run_reduce<false>(fkey(lo), rg);
             const unsigned khi = run_reduce<true>(fkey(hi), rg);
             if ((tid & (rg - 1)) == 0) {
-                atomicMin(&red_min[it & 1][tl], klo);
-                atomicMax(&red_max[it & 1][tl], khi);
+                atomicMin(&red_min[rs][tl], klo);
+                atomicMax(&red_max[rs][tl], khi);
             }
         } else if constexpr (!MX) {
             float m = 0.0f;
@@ -532,10 +548,16 @@ rpbh_quant_kernel(RpbhArgs a) {
             for (int r = 0; r < kE; ++r) m = fmaxf(m, fabsf(v[r]));
             // m >= 0: its bits order as unsigned integers
             const unsigned km = run_reduce<true>(__float_as_uint(m), rg);
-            if ((tid & (rg - 1)) == 0) atomicMax(&red_max[it & 1][tl], km);
+            if ((tid & (rg - 1)) == 0) atomicMax(&red_max[rs][tl], km);
         }
-        lds_barrier();  // B2: statistic complete, next token staged
-        const float amax = __uint_as_float(red_max[it & 1][tl]);
+        lds_barrier();  // B: statistic complete, next token staged
+        // the previous group is complete (its codes were written before B)
+        // and the codes written from here on go to the other slot set
+        if (grouped && it > 0 && (it & ipg_mask) == 0) {
+            const int gl = (it - 1) >> a.ipg_log2;
+            flush(vb + (int64_t)gl * gridDim.x, gl & 1);
+        }
+        const float amax = __uint_as_float(red_max[rs][tl]);
 
         uint32_t nib[kE];   // the codes: nibbles, or bytes for 8-bit codes
         float sc = 0.0f, zp = 0.0f;
@@ -544,8 +566,8 @@ rpbh_quant_kernel(RpbhArgs a) {
             // L = 15 or 255: s = fl32(d / L), inv = fl32(L / d),
             // z = clamp(-rne(fl32(lo inv)), 0, L), q = clamp(rne(fl32(u inv)) + z, 0, L);
             // the float sum is exact wherever the clamp does not bind
-            const float lo = fkey_inv(red_min[it & 1][tl]);
-            const float hi = fkey_inv(red_max[it & 1][tl]);
+            const float lo = fkey_inv(red_min[rs][tl]);
+            const float hi = fkey_inv(red_max[rs][tl]);
             const float d = hi - lo;
             if (d != 0.0f) {
                 const float inv = kLevels / d;
@@ -617,9 +639,9 @@ rpbh_quant_kernel(RpbhArgs a) {
             }
             for (int off = 1; off < grp; off <<= 1) sd += __shfl_xor(sd, off, 64);
             const unsigned long long s = (unsigned long long)sd;
-            if ((tid & (grp - 1)) == 0 && s) atomicAdd(&red_sum[it & 1][tl], s);
+            if ((tid & (grp - 1)) == 0 && s) atomicAdd(&red_sum[rs][tl], s);
             lds_barrier();  // B3
-            const unsigned long long S = red_sum[it & 1][tl];
+            const unsigned long long S = red_sum[rs][tl];
             if (amax > 0.0f) {
                 const double d = ldexp((double)S, 2 * E - 36);
                 const float g = (float)sqrt((double)K / d);
@@ -736,10 +758,12 @@ rpbh_quant_kernel(RpbhArgs a) {
             }
         }
         base = next;
+        rs = rn;
     }
     if (grouped && it > 0) {
         lds_barrier();
-        flush(vb + (int64_t)((it - 1) >> a.ipg_log2) * gridDim.x);
+        const int gl = (it - 1) >> a.ipg_log2;
+        flush(vb + (int64_t)gl * gridDim.x, gl & 1);
     }
 }
 
@@ -753,12 +777,13 @@ hipError_t launch_L(RpbhArgs a, hipStream_t s) {
     constexpr size_t kLdsMax = 159 * 1024;
     // MMA-layout codes are written per group of >= 4 consecutive tokens when
     // the group's code slots fit, else per token
-    const bool grouped = (QK == 0 || QK == 2) && a.codes_mma != nullptr && per_tok + 4 * slot_bytes <= kLdsMax;
+    const bool grouped = (QK == 0 || QK == 2) && a.codes_mma != nullptr && 2 * per_tok + 8 * slot_bytes <= kLdsMax;
     a.grouped = grouped ? 1 : 0;
     // per-token code staging: the group's slots (grouped MMA-layout codes only)
     const size_t slot = grouped ? slot_bytes : 0;
     auto group_of = [&](int tpw) { return grouped && tpw < 4 ? 4 : tpw; };
-    auto lds_of = [&](int tpw) { return per_tok * tpw + slot * group_of(tpw); };
+    // two staging rows per token and two sets of group slots
+    auto lds_of = [&](int tpw) { return 2 * (per_tok * tpw + slot * group_of(tpw)); };
     auto kern = rpbh_quant_kernel<L, BF16, QK>;
     // waves one SIMD holds given the kernel's registers (512 per lane); the
     // same on every gfx950 device, read once (thread-safe static init)
