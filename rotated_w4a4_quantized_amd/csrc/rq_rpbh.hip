@@ -46,6 +46,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
 #include <cstring>
 
 #include "rq_fp6.h"
@@ -61,9 +62,6 @@ constexpr int kMaxTpw = 16;
 // twice the words per thread and keeps the 256-register budget of eight.
 template <bool BF16>
 constexpr int kMaxThreads = BF16 ? 768 : 512;
-// relative time per token of a workgroup that shares its CU with others
-// (their LDS, memory and VALU phases overlap), against one alone on the CU
-constexpr double kOverlap = 0.75;
 
 // Workgroup barrier that orders LDS only: waits for this wave's LDS
 // operations, not for its global loads and stores (a __syncthreads() would
@@ -801,12 +799,13 @@ hipError_t launch_L(RpbhArgs a, hipStream_t s) {
     // w waves puts ceil(w / 4) of them on some SIMD, and co-resident
     // workgroups are counted as landing on the same SIMDs (a pair of six-wave
     // workgroups at three waves per SIMD was measured not to co-reside).
-    // Every workgroup stays resident and loops over groups.  The candidate
-    // with the fewest tokens on the busiest CU wins, counting a CU that runs
-    // several workgroups at once as kOverlap times as fast per workgroup as
-    // one that runs a single one; ties go to more waves per CU, then to the
-    // larger workgroup (fewer barriers per token).
+    // Every workgroup stays resident and loops over groups.  Cost: the tokens
+    // on the busiest CU, times a per-token time that falls with the waves
+    // the CU holds, as 1 / sqrt(waves / the registers' limit) (a fit to a
+    // sweep of launch shapes on the 3072-wide FLUX layer).  Ties go to more
+    // waves per CU, then to the larger workgroup (fewer barriers per token).
     const int cus = device_cus();
+    const int max_waves = 4 * simd_waves;
     int best_tpw = 1, best_occ = 1, best_waves = 0;
     double best_cost = -1.0;
     for (int tpw = 1; tpw <= kMaxTpw; tpw *= 2) {
@@ -821,8 +820,8 @@ hipError_t launch_L(RpbhArgs a, hipStream_t s) {
         for (int occ = 1; occ <= occ_max; ++occ) {
             const int64_t wgs = (int64_t)cus * occ;
             const int64_t load = (int64_t)occ * ((groups + wgs - 1) / wgs) * gs;
-            const double cost = (double)load * (occ > 1 ? kOverlap : 1.0);
             const int waves = occ * wpw;
+            const double cost = (double)load / std::sqrt((double)(waves < max_waves ? waves : max_waves) / max_waves);
             if (best_cost < 0 || cost < best_cost || (cost == best_cost && waves >= best_waves)) {
                 best_cost = cost;
                 best_waves = waves;
