@@ -163,8 +163,10 @@ def summarize_pmc(fetch_dir, write_dir, workload, copy_bytes, command):
     return out
 
 
-def summarize_stats(stats_csv, workload, command):
-    """Short text summary of a rocprofv3 --kernel-trace --stats csv."""
+def summarize_stats(stats_csv, workload, command, bench_json=None):
+    """Short text summary of a rocprofv3 --kernel-trace --stats csv; with
+    the JSON line that the profiled bench run printed, also the two timings
+    of the dominant kernel side by side."""
     import csv
     rows = list(csv.DictReader(open(stats_csv)))
     lines = [f"# rocprofv3 kernel statistics, workload {workload}", "",
@@ -178,6 +180,22 @@ def summarize_stats(stats_csv, workload, command):
         lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | "
                      f"{float(r['MinNs'])/1e3:.2f} | {float(r['MaxNs'])/1e3:.2f} | "
                      f"{float(r['Percentage']):.2f} |")
+    if bench_json:
+        line = json.loads(open(bench_json).read().strip().splitlines()[-1])
+        rf = line["roofline"]
+        kern = rf["kernel"]
+        prof = [r for r in rows if kern + "<" in r["Name"]]
+        calls = sum(int(r["Calls"]) for r in prof)
+        avg = sum(float(r["AverageNs"]) * int(r["Calls"]) for r in prof) / max(calls, 1) / 1e3
+        ev = [l["gemm_us"]["mean"] for l in line["layers"]]
+        lines += ["", f"The bench line this run printed: {line['ms_per_step']} ms per step, "
+                  f"{line['value']} {line['unit']}; `{kern}` {rf['achieved']} {rf['unit']} = "
+                  f"{rf['frac']} of peak from its HIP-event means "
+                  f"({', '.join(f'{x:.2f}' for x in ev)} us per layer, {np.mean(ev):.2f} us on average "
+                  f"over its {len(line['layers']) * line['steps']} timed launches). The profile's "
+                  f"average over all {calls} launches of the kernel (warmup, timed, event-timed and "
+                  f"clock-sampling steps) is {avg:.2f} us, "
+                  f"{100.0 * (avg / np.mean(ev) - 1.0):+.1f}% from the event mean."]
     path = os.path.join(ROOT, "profiles", f"kernel_stats_{workload}.md")
     open(path, "w").write("\n".join(lines) + "\n")
     return path
@@ -335,17 +353,19 @@ def main():
     ap.add_argument("--summarize-trace", metavar="TRACE_CSV",
                     help="offline: kernel gaps from a rocprofv3 --kernel-trace csv into profiles/")
     ap.add_argument("--command", default="", help="command recorded in the summaries")
+    ap.add_argument("--bench-json", default=None,
+                    help="with --summarize-stats: the JSON line the profiled run printed")
     args = ap.parse_args()
 
     if args.summarize_trace:
-        print(summarize_trace(args.summarize_trace, args.workload, args.command))
+        print(summarize_trace(args.summarize_trace, args.workload, args.command, warmup=args.warmup))
     if args.summarize_pmc or args.summarize_stats:
         if args.summarize_pmc:
             res = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
                                 args.copy_calibration, args.command)
             print(json.dumps({k: v["hbm_bytes_per_launch"] for k, v in res.items()}))
         if args.summarize_stats:
-            print(summarize_stats(args.summarize_stats, args.workload, args.command))
+            print(summarize_stats(args.summarize_stats, args.workload, args.command, args.bench_json))
         return
     if args.summarize_trace:
         return
