@@ -169,7 +169,7 @@ typedef struct rq_quant {
 } rq_quant;
 
 #define RQ_WEIGHT_MAGIC 0x31575152u /* "RQW1" */
-#define RQ_WEIGHT_VERSION 4u
+#define RQ_WEIGHT_VERSION 5u
 
 /*
  * Header at the start of every packed-weight blob (256 bytes).  The blob is
@@ -200,9 +200,17 @@ typedef struct rq_quant {
  *                 by 128 coordinates per 3 KB tile, zero-padded past N and K;
  *                 MXFP4: the E2M1 codes tiled [mma_ntiles][K/32][32][16]:
  *                 rows in tiles of 32, each row's 16 bytes of coordinates
- *                 32 c .. 32 c + 31 (zero rows past N)
- *   mma_stages    ceil((K - r) / 128)
- *   mma_ntiles    ceil(N / 32)
+ *                 32 c .. 32 c + 31 (zero rows past N);
+ *                 LLOYDMAX with w_bits 4: the weight levels as bf16 in the
+ *                 codebook GEMM's fragment order [mma_ntiles][K/16][64][8 x
+ *                 bf16]: lane i + 32 h of k-step c holds row 32 tile + i,
+ *                 coordinates 16 c + 8 h .. + 7 (zero rows past N), which
+ *                 the GEMM copies with direct-to-LDS loads instead of
+ *                 decoding the indices (2 bytes per weight, 4x the 4-bit
+ *                 codes, which stay in the blob); 2-bit weights have none
+ *                 (the GEMM decodes them)
+ *   mma_stages    INT, MXFP4: ceil((K - r) / 128); LLOYDMAX: 0
+ *   mma_ntiles    ceil(N / 32) (0 for 2-bit LLOYDMAX weights)
  *   i8_offset     INT with a_bits 6 or 8: the int8 weight codes (the canonical
  *                 codes when w_bits is 6 or 8, their widened copy when 4) in the
  *                 int8 matrix cores' fragment order

@@ -47,6 +47,12 @@ rq_status check_header(const rq_weight_header *hdr) {
     if (hdr->row_bytes != want_rb) return fail(RQ_ERR_FORMAT, "weight header row_bytes mismatch");
     if (f == RQ_Q_LLOYDMAX && hdr->K % 64 != 0)
         return fail(RQ_ERR_SHAPE, "the codebook GEMM needs K % 64 == 0");
+    if (f == RQ_Q_LLOYDMAX && hdr->w_bits == 4 &&
+        (hdr->mma_ntiles != (hdr->N + 31) / 32 || hdr->mma_offset <= 0 || hdr->mma_offset % 16 != 0 ||
+         hdr->mma_offset + (int64_t)hdr->mma_ntiles * (hdr->K / 16) * 1024 > hdr->total_bytes))
+        return fail(RQ_ERR_FORMAT, "weight header bf16 fragment section is inconsistent");
+    if (f == RQ_Q_LLOYDMAX && hdr->w_bits != 4 && hdr->mma_offset != 0)
+        return fail(RQ_ERR_FORMAT, "2-bit Lloyd-Max weights carry no bf16 fragment section");
     if (hdr->scale_offset % 16 != 0 || hdr->codes_offset % 16 != 0)
         return fail(RQ_ERR_FORMAT, "weight header offsets are not 16-byte aligned");
     if (f == RQ_Q_INT4_ASYM && hdr->r != 0)

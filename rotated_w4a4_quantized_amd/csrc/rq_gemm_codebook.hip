@@ -9,15 +9,16 @@
 // Tiling: a workgroup owns 256 tokens x 256 channels on eight waves of 64
 // tokens x 128 channels (two token fragments x four channel fragments, 128
 // accumulators per lane, two waves per SIMD).  K advances in stages of 64.
-// The packed indices of stage s + 2 are loaded into registers while stage s
-// is multiplied; the indices of stage s + 1 are decoded through LDS look-up
-// tables (one entry per packed byte: two 4-bit activation indices -> two
-// bf16, four 2-bit weight indices -> four bf16) straight into the matrix-core
-// fragment order of the other LDS buffer, [fragment][k-step][lane][16 bytes],
-// so every fragment read is one conflict-free 1 KB ds_read_b128 and each
-// stage needs one workgroup barrier.  Decoding each index once per workgroup
-// (rather than per wave that reads it) keeps the vector ALU work at a tenth
-// of the matrix-core time.
+// Operands that arrive as bf16 levels in the matrix-core fragment order
+// [fragment][k-step][lane][16 bytes] -- the activations from rq_rotate_quant's
+// codes_mma, the weights from the packed blob's copy -- are copied for stage
+// s + 1 with direct-to-LDS loads while stage s is multiplied.  Operands given
+// as packed indices are loaded into registers for stage s + 2 and decoded for
+// stage s + 1 through LDS look-up tables (one entry per packed byte: two
+// 4-bit activation indices -> two bf16, four 2-bit weight indices -> four
+// bf16) into the same fragment order of the other LDS buffer.  Every
+// fragment read is one conflict-free 1 KB ds_read_b128 and each stage needs
+// one workgroup barrier.
 //
 // Accumulator element e of the 32x32 MFMA held by lane l: column l % 32,
 // row 8 (e / 4) + 4 (l / 32) + e % 4.  The weight fragment is the A operand
@@ -44,6 +45,7 @@ struct CodebookArgs {
     const uint8_t *A;      // activation indices, 4-bit, [T][K/2]
     const uint8_t *Amma;   // or their bf16 levels in fragment order (rq_rotate_quant's codes_mma)
     const uint8_t *B;      // weight indices, w_bits, [N][ldb]
+    const uint8_t *Bmma;   // or their bf16 levels in fragment order (the blob's copy)
     const float *sigma;    // [T]
     const float *tau;      // [N]
     const float *bias;     // [N] or null
@@ -75,9 +77,12 @@ __device__ __forceinline__ uint32_t frag_slot(int f, int ks, int l) {
     return (uint32_t)(((f * NKS + ks) * 64 + l) * 16);
 }
 
-template <bool W4, bool AMMA>
+template <bool W4, bool AMMA, bool BMMA>
 __global__ void __launch_bounds__(NTH, 1)
 gemm_cb_kernel(CodebookArgs a) {
+    // index loads per load() call (activation and weight rows still packed)
+    constexpr int LDN = (AMMA ? 0 : 1) + (BMMA ? 0 : 1);
+    constexpr bool COPY = AMMA || BMMA;
     __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
     uint32_t *lutA = reinterpret_cast<uint32_t *>(lds + LUT_OFF);   // byte -> two bf16
     uint2 *lutB = reinterpret_cast<uint2 *>(lds + LUT_OFF + 1024);  // byte -> four (two) bf16
@@ -124,10 +129,11 @@ gemm_cb_kernel(CodebookArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) dslot[c] = frag_slot(r >> 5, 2 * h + (c >> 1), (r & 31) + 32 * (c & 1));
 
-    uint4 ra = make_uint4(0u, 0u, 0u, 0u), rb;
+    uint4 ra = make_uint4(0u, 0u, 0u, 0u), rb = make_uint4(0u, 0u, 0u, 0u);
     auto load = [&](int s) {
         if constexpr (!AMMA) ra = *reinterpret_cast<const uint4 *>(ap + (int64_t)s * (KS / 2));
-        if constexpr (W4) {
+        if constexpr (BMMA) {
+        } else if constexpr (W4) {
             rb = *reinterpret_cast<const uint4 *>(bp + (int64_t)s * (KS / 2));
         } else {
             const uint2 v = *reinterpret_cast<const uint2 *>(bp + (int64_t)s * (KS / 4));
@@ -147,7 +153,8 @@ gemm_cb_kernel(CodebookArgs a) {
                 *reinterpret_cast<uint4 *>(base + dslot[c]) = v;
             }
         }
-        if constexpr (W4) {
+        if constexpr (BMMA) {
+        } else if constexpr (W4) {
             const uint32_t wb[4] = {rb.x, rb.y, rb.z, rb.w};
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -192,13 +199,29 @@ gemm_cb_kernel(CodebookArgs a) {
             dma16(src, lane * 16, lds_base + buf * STAGE + frag_slot(q / 4, q & 3, 0));
         }
     };
+    // BMMA: the weight fragments likewise, piece q of the stage is k-step
+    // q % 4 of channel tile q / 4 (tiles past the last channel repeat it)
+    const int btiles = (a.N + 31) / 32;
+    auto dma_w = [&](int s, int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = wave * 4 + i;
+            int nt = n0 / 32 + q / 4;
+            if (nt >= btiles) nt = btiles - 1;
+            const uint8_t *src = a.Bmma + (((int64_t)nt * (a.K / 16) + s * NKS + (q & 3)) * 64) * 16;
+            dma16(src, lane * 16, lds_base + buf * STAGE + OPND + frag_slot(q / 4, q & 3, 0));
+        }
+    };
     if constexpr (AMMA) dma_act(0, 0);
+    if constexpr (BMMA) dma_w(0, 0);
     load(0);
     __syncthreads();   // tables ready
     decode(0);
     if (nstage > 1) load(1);
-    if constexpr (AMMA) {
-        if (nstage > 1) wait_vm<1>();   // the stage-0 copies have landed
+    if constexpr (COPY) {
+        // the stage-0 copies have landed (stage 1's index loads, issued
+        // after them, may still be in flight)
+        if (nstage > 1) wait_vm<LDN>();
         else wait_vm<0>();
     }
     lds_barrier();
@@ -206,16 +229,16 @@ gemm_cb_kernel(CodebookArgs a) {
     const uint8_t *LA = lds + lane * 16;
     const uint8_t *LW = lds + OPND + lane * 16;
     // One stage: four k-steps of eight MFMAs from buffer s % 2; between them
-    // the next stage's indices are decoded into the other buffer (every read
-    // of it finished before the previous stage's barrier; AMMA: its
-    // activation fragments are copied there) (DEC) and the indices of the
-    // stage after that are fetched (LD).
+    // the next stage's operands are copied or decoded into the other buffer
+    // (every read of it finished before the previous stage's barrier) (DEC)
+    // and the indices of the stage after that are fetched (LD).
     auto stage = [&](int s, auto dec_c, auto ld_c) {
         constexpr bool DEC = decltype(dec_c)::value;
         constexpr bool LD = decltype(ld_c)::value;
         const int cur = s & 1;
         const uint8_t *la = LA + cur * STAGE, *lw = LW + cur * STAGE;
         if constexpr (AMMA && DEC) dma_act(s + 1, cur ^ 1);
+        if constexpr (BMMA && DEC) dma_w(s + 1, cur ^ 1);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             v8bf tf[FT], wf[FN];
@@ -237,10 +260,10 @@ gemm_cb_kernel(CodebookArgs a) {
                 if (ks == 2) load(s + 2);
             }
         }
-        // AMMA: the copies of stage s + 1 have landed (the index load of
-        // stage s + 2, issued after them, may still be in flight)
-        if constexpr (AMMA && DEC) {
-            if constexpr (LD) wait_vm<1>();
+        // the copies of stage s + 1 have landed (the index loads of stage
+        // s + 2, issued after them, may still be in flight)
+        if constexpr (COPY && DEC) {
+            if constexpr (LD) wait_vm<LDN>();
             else wait_vm<0>();
         }
         lds_barrier();
@@ -344,6 +367,8 @@ int launch_gemm_codebook(const uint8_t *codes, const uint8_t *codes_mma, const f
     a.A = codes;
     a.Amma = codes_mma;
     a.B = base + hdr->codes_offset;
+    // the weights' bf16 fragments (blobs of 16-level weight books)
+    a.Bmma = hdr->mma_offset ? base + hdr->mma_offset : nullptr;
     a.sigma = sigma;
     a.tau = reinterpret_cast<const float *>(base + hdr->scale_offset);
     a.bias = bias;
@@ -360,16 +385,23 @@ int launch_gemm_codebook(const uint8_t *codes, const uint8_t *codes_mma, const f
     a.tiles_n = (hdr->N + BN - 1) / BN;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)(a.tiles_t * a.tiles_n));
-    if (codes_mma) {
-        if (hdr->w_bits == 4)
-            hipLaunchKernelGGL((gemm_cb_kernel<true, true>), grid, dim3(NTH), 0, s, a);
+    const bool w4 = hdr->w_bits == 4, am = codes_mma != nullptr, bm = a.Bmma != nullptr;
+    if (bm) {
+        // the weights' index width no longer matters
+        if (am)
+            hipLaunchKernelGGL((gemm_cb_kernel<true, true, true>), grid, dim3(NTH), 0, s, a);
         else
-            hipLaunchKernelGGL((gemm_cb_kernel<false, true>), grid, dim3(NTH), 0, s, a);
+            hipLaunchKernelGGL((gemm_cb_kernel<true, false, true>), grid, dim3(NTH), 0, s, a);
+    } else if (am) {
+        if (w4)
+            hipLaunchKernelGGL((gemm_cb_kernel<true, true, false>), grid, dim3(NTH), 0, s, a);
+        else
+            hipLaunchKernelGGL((gemm_cb_kernel<false, true, false>), grid, dim3(NTH), 0, s, a);
     } else {
-        if (hdr->w_bits == 4)
-            hipLaunchKernelGGL((gemm_cb_kernel<true, false>), grid, dim3(NTH), 0, s, a);
+        if (w4)
+            hipLaunchKernelGGL((gemm_cb_kernel<true, false, false>), grid, dim3(NTH), 0, s, a);
         else
-            hipLaunchKernelGGL((gemm_cb_kernel<false, false>), grid, dim3(NTH), 0, s, a);
+            hipLaunchKernelGGL((gemm_cb_kernel<false, false, false>), grid, dim3(NTH), 0, s, a);
     }
     return (int)hipGetLastError();
 }

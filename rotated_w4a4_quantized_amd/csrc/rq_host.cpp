@@ -231,7 +231,17 @@ static BlobLayout blob_layout(const rq_rotation *rot, const rq_quant *q, int32_t
         L.mma_off = end;
         L.mxs_off = L.mma_off + (int64_t)L.mma_ntiles * (K / 32) * 512;
         end = L.mxs_off + round256((int64_t)L.mma_stages * L.mma_ntiles * 128);
-    } else if (!lm) {                    // integer weights
+    } else if (lm) {
+        // 16-level weight books: the levels as bf16 in the codebook GEMM's
+        // fragment order (2-bit books are decoded in the GEMM: cheap enough)
+        if (q->w_bits != 4) {
+            L.total = end;
+            return L;
+        }
+        L.mma_ntiles = (N + 31) / 32;
+        L.mma_off = end;
+        end = L.mma_off + (int64_t)L.mma_ntiles * (K / 16) * 1024;
+    } else {                             // integer weights
         L.wsum_off = end;
         end = L.wsum_off + round256((int64_t)N * 4);
         if (q->a_bits == 4) {            // FP6 fragments of the quantized coordinates
@@ -521,6 +531,27 @@ rq_status rq_pack_weights(const rq_rotation *rot, const rq_quant *q, const void 
                     out[BL.mxs_off + (((int64_t)s * ntiles + tile) * 64 + 32 * h + i) * 2 + ks] =
                         e8[(size_t)n * nch + c];
                 }
+    } else if (q->kind == RQ_Q_LLOYDMAX && BL.mma_off) {
+        // the levels as bf16 in the codebook GEMM's fragment order
+        // [ceil(N/32)][K/16][64 lanes][8 x bf16]: lane i + 32 h of k-step c
+        // holds row 32 tile + i, coordinates 16 c + 8 h .. + 7 (rows past N
+        // stay zero); the levels are bf16 values, so the top halves are exact
+        const int per_byte = 8 / q->w_bits, nks = K / 16;
+        uint16_t lev16[16];
+        for (int i = 0; i < Lw; ++i) {
+            uint32_t bits;
+            std::memcpy(&bits, &q->w_levels[i], 4);
+            lev16[i] = (uint16_t)(bits >> 16);
+        }
+        uint16_t *frag = reinterpret_cast<uint16_t *>(out + BL.mma_off);
+        parallel(N, [&](int n0, int n1) {
+            for (int n = n0; n < n1; ++n)
+                for (int k = 0; k < K; ++k) {
+                    const int idx = (codes[(size_t)n * rb + k / per_byte] >> ((k % per_byte) * q->w_bits)) & (Lw - 1);
+                    const size_t lane = (size_t)(n % 32) + 32 * ((k % 16) / 8);
+                    frag[(((size_t)(n / 32) * nks + k / 16) * 64 + lane) * 8 + k % 8] = lev16[idx];
+                }
+        });
     }
     return RQ_OK;
 }

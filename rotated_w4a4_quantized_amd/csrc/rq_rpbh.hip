@@ -558,7 +558,11 @@ rpbh_quant_kernel(RpbhArgs a) {
         const float amax = __uint_as_float(red_max[rs][tl]);
 
         uint32_t nib[kE];   // the codes: nibbles, or bytes for 8-bit codes
-        float sc = 0.0f, zp = 0.0f;
+        // The token's scale is stored by its first thread only, so only that
+        // wave divides: s = snum / sden (0 when snum = 0), or for the
+        // codebook sigma = sqrt(dn / K).
+        float snum = 0.0f, sden = 1.0f, zp = 0.0f;
+        double dn = 0.0;
         uint32_t mxsc = 0u;  // MXFP4: E8M0 code of this thread's block
         if constexpr (ASYM) {
             // L = 15 or 255: s = fl32(d / L), inv = fl32(L / d),
@@ -569,7 +573,8 @@ rpbh_quant_kernel(RpbhArgs a) {
             const float d = hi - lo;
             if (d != 0.0f) {
                 const float inv = kLevels / d;
-                sc = d / kLevels;
+                snum = d;
+                sden = kLevels;
                 // z is the integer -rne(lo inv) clamped to [0, L], as a float;
                 // rne(lo inv) = -0 or +0 (a row whose minimum is at most s / 2
                 // from zero) gives z = +0
@@ -598,7 +603,8 @@ rpbh_quant_kernel(RpbhArgs a) {
                 const float mq = v[r] * sinv;
                 nib[r] = __float_as_uint(mq + 12582920.0f);   // q + 8 in bits 0..3
             }
-            sc = amax > 0.0f ? amax / 7.0f : 0.0f;
+            snum = amax;
+            sden = 7.0f;
         } else if constexpr (QK == 4) {
             // q = rne(fl32(u * inv)) in [-qm, qm] (|u * inv| <= fl32(qm (1 + 2^-24))
             // rounds to at most qm); adding 1.5 * 2^23 leaves q in the low
@@ -608,7 +614,8 @@ rpbh_quant_kernel(RpbhArgs a) {
             const float sinv = lsign * inv;   // v = lsign u
 #pragma unroll
             for (int r = 0; r < kE; ++r) nib[r] = __float_as_uint(v[r] * sinv + 12582912.0f) & 0xFFu;
-            sc = amax > 0.0f ? amax / qm : 0.0f;
+            snum = amax;
+            sden = qm;
         } else if constexpr (MX) {
             // this thread's 32 coordinates are one block: e = floor(log2 max|u|) - 2
             float m = 0.0f;
@@ -643,7 +650,7 @@ rpbh_quant_kernel(RpbhArgs a) {
             if (amax > 0.0f) {
                 const double d = ldexp((double)S, 2 * E - 36);
                 const float g = (float)sqrt((double)K / d);
-                sc = (float)sqrt(d / (double)K);
+                dn = d;
                 const float sg = lsign * g;   // v = lsign u: x = fl32(u g)
 #pragma unroll
                 for (int r = 0; r < kE; ++r) {
@@ -751,6 +758,11 @@ rpbh_quant_kernel(RpbhArgs a) {
                         ((qc >> 1) & 1)] = (uint8_t)mxsc;
                 }
             } else if (tt == 0) {
+                float sc;
+                if constexpr (QK == 1)
+                    sc = (float)sqrt(dn / (double)K);
+                else
+                    sc = snum != 0.0f ? snum / sden : 0.0f;
                 a.scale[tok] = sc;
                 if constexpr (ASYM) a.scale[a.T + tok] = zp;
             }

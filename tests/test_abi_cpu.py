@@ -363,6 +363,37 @@ def test_pack_lloydmax_16_level_weights_matches_oracle():
     assert np.array_equal(pw.scales(), ref["scale"])
 
 
+@pytest.mark.parametrize("w_bits,N", [(4, 24), (4, 40)])
+def test_pack_lloydmax_bf16_fragments(w_bits, N):
+    """The codebook GEMM's copy of 16-level weights: the level of every
+    oracle index as bf16, in the fragment order [N/32][K/16][64 lanes][8]
+    (lane i + 32 h of k-step c: row 32 tile + i, coordinates 16 c + 8 h ..),
+    rows past N zero.  2-bit weights have no copy."""
+    w = datagen.WORKLOADS["video"].with_shape(T=4, K=512, N=N, block=256, w_bits=w_bits)
+    inp = datagen.make_inputs(w)
+    a_lv, w_lv = rq.lloydmax_gaussian(16), rq.lloydmax_gaussian(1 << w_bits)
+    pw = rq.pack_weights(rq.Rotation.rpbh(inp["sign"], inp["perm"], 256),
+                         rq.Quant.lloydmax(a_lv, w_lv), inp["W"])
+    ref = _oracle_weights(w, inp, q_kind=1, levels=orc.codebook_bf16(1 << w_bits))
+    per = 8 // w_bits
+    packed = ref["codes"].astype(np.int64)
+    idx = np.stack([(packed >> (w_bits * j)) & ((1 << w_bits) - 1) for j in range(per)], axis=2)
+    idx = idx.reshape(N, w.K)
+    want = (w_lv.view(np.uint32) >> 16).astype(np.uint16)[idx]
+    h = pw.header
+    nt = -(-N // 32)
+    assert h.mma_ntiles == nt and h.mma_stages == 0 and h.mma_offset % 256 == 0
+    frag = pw.blob[h.mma_offset:h.mma_offset + nt * (w.K // 16) * 1024].view(np.uint16)
+    frag = frag.reshape(nt, w.K // 16, 2, 32, 8)                  # [tile][c][h][i][e]
+    rows = frag.transpose(0, 3, 1, 2, 4).reshape(nt * 32, w.K)    # k = 16 c + 8 h + e
+    assert np.array_equal(rows[:N], want)
+    assert not rows[N:].any()
+    w2 = datagen.WORKLOADS["video"].with_shape(T=4, K=512, N=N, block=256)
+    p2 = rq.pack_weights(rq.Rotation.rpbh(inp["sign"], inp["perm"], 256),
+                         rq.Quant.lloydmax(a_lv, rq.lloydmax_gaussian(4)), datagen.make_inputs(w2)["W"])
+    assert p2.header.mma_offset == 0 and p2.header.mma_ntiles == 0
+
+
 def test_pack_rejects_bad_tables():
     sign, perm = datagen.random_rpbh(256, 1)
     perm = perm.copy()
