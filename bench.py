@@ -100,6 +100,7 @@ def profiled_traffic(kernel_file: str, summary: str):
 # kernels summarized from rocprofv3 runs: (summary file, kernel source, name match)
 PMC_KERNELS = {
     "gemm": ("rq_gemm_fp6.hip", "gemm_fp6_mma_kernel"),
+    "gemm_conv": ("rq_gemm_fp6.hip", "gemm_fp6_kernel"),
     "gemm_int8": ("rq_gemm_w4a4.hip", "gemm_w4a4_kernel"),
     "gemm_i8": ("rq_gemm_i8.hip", "gemm_i8_kernel"),
     "gemm_codebook": ("rq_gemm_codebook.hip", "gemm_cb_kernel"),
@@ -386,16 +387,25 @@ def main():
     wls = [datagen.WORKLOADS[n] for n in names]
     int8_gemm = args.engine == "int8" or any(w.a_bits != 4 for w in wls)
 
+    # Code layout per layer: 4-bit integer codes (RPBH, DENSE) and MXFP4
+    # reach the GEMM in the matrix-core fragment layout, except a 4-bit
+    # integer layer with fewer 256 x 256 output tiles than a quarter of the
+    # CUs, which takes the canonical codes: their GEMM runs 128 x 128 tiles.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def use_mma(w):
+        if not mma_capable(w) or (args.engine == "int8" and w.quant != "mxfp4"):
+            return False
+        small = -(-w.T // 256) * -(-w.N // 256) < cus // 4
+        return not (w.quant in ("int4", "int4_asym") and w.a_bits == 4 and w.r == 0 and small)
+
     # ring of independent instances (distinct seeds), all resident in HBM
     ring = []
     for i in range(args.ring):
         layers = []
         for w in wls:
             inp = datagen.make_inputs(w, seed_offset=100 * i)
-            # layers with 4-bit integer codes (RPBH, DENSE) or MXFP4 hand the
-            # GEMM its codes in the matrix-core layout only
-            mma = mma_capable(w) and not (args.engine == "int8" and w.quant != "mxfp4")
-            layers.append(QuantLinear(w, inp, codes="mma" if mma else "canonical"))
+            layers.append(QuantLinear(w, inp, codes="mma" if use_mma(w) else "canonical"))
             log(f"[bench] instance {i} layer {w.name}: T={w.T} K={w.K} N={w.N} ready")
         ring.append(layers)
     torch.cuda.synchronize()
@@ -485,6 +495,7 @@ def main():
         entry = {
             "layer": w.name, "T": w.T, "K": w.K, "N": w.N, "rotation": w.rot,
             "block": w.block, "quant": w.quant, "a_bits": w.a_bits, "w_bits": w.w_bits,
+            "codes": "mma" if use_mma(w) else "canonical",
             "rotate_quant_us": {"mean": round(float(r.mean()), 2), "median": round(pct(r, 50), 2),
                                 "p10": round(pct(r, 10), 2), "p90": round(pct(r, 90), 2)},
             "rotate_quant_GBps": round(rotate_bytes(w) / (r.mean() * 1e-6) / 1e9, 1),
@@ -512,8 +523,9 @@ def main():
             "gemm_w4a4_kernel", "i8"
     else:
         # the INT4 GEMM computes on the FP6 matrix cores: its own dtype's peak
-        peak, gsrc, gkey, gname, dtype = PEAK_FP6_TOPS, "rq_gemm_fp6.hip", "gemm", \
-            ("gemm_fp6_mma_kernel" if mma_capable(w0) else "gemm_fp6_kernel"), "fp6"
+        peak, gsrc, gkey, gname, dtype = (PEAK_FP6_TOPS, "rq_gemm_fp6.hip", "gemm", "gemm_fp6_mma_kernel", "fp6")
+        if not use_mma(w0):
+            gkey, gname = "gemm_conv", "gemm_fp6_kernel"
     gemm_mean_ms = float(np.mean(gemm_ms))
     achieved = float(np.mean(ops)) / (gemm_mean_ms * 1e-3) / 1e12
     traffic = profiled_traffic(gsrc, f"{gkey}_{args.workload}_counters.json")

@@ -1032,7 +1032,10 @@ int launch_gemm_fp6(const uint8_t *codes, const uint8_t *codes_mma, const float 
         return (int)hipGetLastError();
     }
     if (a.r > 0) return (int)launch_cfg<CfgMid, true>(a, s);
-    if (T >= 256 && hdr->N >= 256) return (int)launch_cfg<CfgBig, false>(a, s);
+    // 256 x 256 tiles only when they fill at least half of the CUs; a
+    // smaller layer runs on four times as many 128 x 128 tiles
+    const int64_t big_tiles = ((T + 255) / 256) * (int64_t)((hdr->N + 255) / 256);
+    if (T >= 256 && hdr->N >= 256 && big_tiles >= device_cus() / 2) return (int)launch_cfg<CfgBig, false>(a, s);
     return (int)launch_cfg<CfgMid, false>(a, s);
 }
 

@@ -379,10 +379,14 @@ CODES_ONLY = [
     ("flux_up_w4a8", dict(T=300, K=1024, N=520, block=256)),
     ("flux_up_w8a8", dict(T=300, K=1024, N=520, block=256)),
     ("flux_up_trdq", dict(T=300, K=1024, N=520, block=128)),
+    # enough 256 x 256 output tiles (9 x 17) that the canonical-code GEMM
+    # takes its 256 x 256 kernel rather than 128 x 128 tiles; ragged edges
+    ("flux_up", dict(T=2200, K=1024, N=4100, block=256)),
 ]
 
 
-@pytest.mark.parametrize("name,shape", CODES_ONLY, ids=[c[0] for c in CODES_ONLY])
+@pytest.mark.parametrize("name,shape", CODES_ONLY,
+                         ids=[f"{n}-T{s['T']}-N{s['N']}" for n, s in CODES_ONLY])
 def test_mma_codes_only_path(name, shape):
     # the bench configuration: rq_rotate_quant writes only the MMA-layout
     # codes (canonical codes NULL) and the GEMM reads them; compared with a
