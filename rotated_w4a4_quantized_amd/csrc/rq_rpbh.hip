@@ -187,26 +187,6 @@ __device__ inline void lane_stages(float (&v)[kE], const float (&coef)[5]) {
 // bits is set (each set bit negated the lane's values once).
 __device__ inline float lane_sign(int h) { return (__popc((unsigned)h) & 1) ? -1.0f : 1.0f; }
 
-// MXFP4 element: the E2M1 code of x / 2^e (x times inv = 2^-e, exact but for
-// values far below E2M1's smallest step, which round to code 0 either way):
-// below 1 the nearest multiple of 1/2 (rne(2 a): codes 0, 1, 2); from 1 up the
-// fp32 mantissa rounded to one bit, nearest-even (add 2^21 - 1 plus the kept
-// bit, clear the low 22), capped at 6; the code is then 2 (fp32 exponent -
-// 126) plus the mantissa bit.  The sign goes to bit 3 unless the code is 0;
-// neg (0 or 1): x is the coordinate negated (a lane's sign after the lane
-// stages).  A nonzero code has x != 0, whose sign bit is then x < 0.
-__device__ inline uint32_t e2m1_code(float x, float inv, uint32_t neg) {
-    const float a = fabsf(x) * inv;
-    const uint32_t small = (uint32_t)rintf(a + a);
-    uint32_t b = __float_as_uint(a);
-    b = (b + 0x1FFFFFu + ((b >> 22) & 1u)) & 0xFFC00000u;
-    const uint32_t r = __float_as_uint(fminf(__uint_as_float(b), 6.0f));
-    const uint32_t big = (((r >> 23) - 126u) << 1) | ((r >> 22) & 1u);
-    const uint32_t c = a < 1.0f ? small : big;
-    const uint32_t s = ((__float_as_uint(x) >> 31) ^ neg) & (c != 0u ? 1u : 0u);
-    return c | (s << 3);
-}
-
 // Order-preserving 32-bit key of a float (for LDS atomic min / max over
 // values of either sign) and its inverse.
 __device__ inline unsigned fkey(float f) {
@@ -564,6 +544,7 @@ rpbh_quant_kernel(RpbhArgs a) {
         float snum = 0.0f, sden = 1.0f, zp = 0.0f;
         double dn = 0.0;
         uint32_t mxsc = 0u;  // MXFP4: E8M0 code of this thread's block
+        uint32_t mxw[4];     // MXFP4: the block's 32 codes, two per byte
         if constexpr (ASYM) {
             // L = 15 or 255: s = fl32(d / L), inv = fl32(L / d),
             // z = clamp(-rne(fl32(lo inv)), 0, L), q = clamp(rne(fl32(u inv)) + z, 0, L);
@@ -624,9 +605,28 @@ rpbh_quant_kernel(RpbhArgs a) {
             int e = m > 0.0f ? ilogbf(m) - 2 : -127;
             e = e < -127 ? -127 : e;
             mxsc = (uint32_t)(e + 127);
-            const float inv = ldexpf(1.0f, -e);   // 2^-e: 2^-125 .. 2^127, exact
+            // 2^-e (2^-125 .. 2^127, exact), times the lane's sign: v sinv =
+            // u 2^-e = a, exact but for values far below E2M1's smallest step
+            // (code 0 either way), and |a| < 8.  The element's E2M1 code is
+            // |a| rounded to the grid {0, 0.5, 1, 1.5, 2, 3, 4, 6}, nearest
+            // with ties to even, saturating at 6, with the sign of a in bit 3
+            // unless the magnitude is 0.  v_cvt_scalef32_pk_fp4_f32 (scale 1)
+            // rounds two values that way into byte b of a word, low nibble
+            // first (checked on the device against a software encoder of the
+            // rule for every fp32 value of either sign up to 16), except that
+            // a value rounding to 0 may keep its sign; that sign is cleared
+            // per nibble (m + 7 sets bit 3 exactly when m != 0).
+            const float sinv = lsign * ldexpf(1.0f, -e);
 #pragma unroll
-            for (int r = 0; r < kE; ++r) nib[r] = e2m1_code(v[r], inv, lsign < 0.0f ? 1u : 0u);
+            for (int q = 0; q < 4; ++q) {
+                uint32_t w = 0u;
+                w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * q + 0] * sinv, v[8 * q + 1] * sinv, 1.0f, 0);
+                w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * q + 2] * sinv, v[8 * q + 3] * sinv, 1.0f, 1);
+                w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * q + 4] * sinv, v[8 * q + 5] * sinv, 1.0f, 2);
+                w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * q + 6] * sinv, v[8 * q + 7] * sinv, 1.0f, 3);
+                const uint32_t mag = w & 0x77777777u;
+                mxw[q] = mag | (w & (mag + 0x77777777u) & 0x88888888u);
+            }
         } else {
             // exact squared norm on the grid 2^(2E - 36), E = ilogb(max |u|):
             // each term rint(u^2 2^(36 - 2E)) = rint((u 2^(18 - E))^2) (both
@@ -689,6 +689,8 @@ rpbh_quant_kernel(RpbhArgs a) {
                 w[m] = nib[4 * m] | (nib[4 * m + 1] << 8) | (nib[4 * m + 2] << 16) | (nib[4 * m + 3] << 24);
             chunk = make_uint4(w[0], w[1], w[2], w[3]);
             chunk1 = make_uint4(w[4], w[5], w[6], w[7]);
+        } else if constexpr (MX) {
+            chunk = make_uint4(mxw[0], mxw[1], mxw[2], mxw[3]);
         } else {
             // byte m = code 2m | code 2m + 1 << 4 (one shift-or: only bits
             // 0..3 of a code word and 4..7 of the shifted one reach byte 0),
