@@ -667,3 +667,37 @@ def test_trdq_tiled_matches_one_pass(name, shape, quant):
     torch.cuda.synchronize()
     assert torch.equal(L.codes, c_tiled), "one-pass and tiled codes differ"
     assert torch.equal(L.scale.view(torch.int32), s_tiled.view(torch.int32)), "scales differ"
+
+
+def test_mxfp4_rounding_boundaries():
+    """MXFP4 codes at the E2M1 grid's ties (to the even code), just off
+    them, at saturation, and for values of either sign that round to zero
+    (code 0, no sign): block 2, identity permutation, +1 signs, so each pair
+    x0 = x1 = v / 2 rotates exactly to u = (v, 0).  Every 32-coordinate block
+    holds +-6 2^k first, so its E8M0 exponent is k; rows use k = -3 .. 3."""
+    w = datagen.WORKLOADS["flux_up_mxfp4"].with_shape(T=56, K=128, N=64, block=2)
+    inp = datagen.make_inputs(w)
+    ties = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    vals = [0.0, 6.0, 7.0, 7.5, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0]
+    for t in ties:
+        d = 2.0 ** (np.floor(np.log2(t)) - 5)
+        vals += [t, t - d, t + d]
+    vals += [1.0 / 128, 1.0 / 16, 0.2421875]          # round to 0
+    vals = np.array(vals + [-v for v in vals], dtype=np.float64)
+    u = np.zeros((w.T, w.K // 2))
+    for t in range(w.T):
+        k = t % 7 - 3
+        row = np.roll(vals, t)[: w.K // 2]
+        row[::16] = 6.0 if t % 2 == 0 else -6.0       # block maxima (16 pairs = 32 coordinates)
+        u[t] = row * 2.0 ** k
+    x = np.repeat(u / 2, 2, axis=1).astype(np.float32)
+    assert np.array_equal(datagen.bf16_bits_to_f32(datagen.f32_to_bf16_bits(x)), x)
+    inp["X"] = datagen.f32_to_bf16_bits(x)
+    inp["sign"] = np.ones(w.K, dtype=np.int8)
+    inp["perm"] = np.arange(w.K, dtype=np.int32)
+    say(f"[mxfp4 boundaries] {w}")
+    L = H.GpuLayer(w, inp, codes="both")
+    L.rotate_quant()
+    torch.cuda.synchronize()
+    act = H.oracle_act(w, inp)
+    check_act(w, L, act)
